@@ -1,0 +1,268 @@
+"""Seeded synthetic graph inputs (out-edge CSR, int32), shared by every test
+and by the benchmark.
+
+Holds no PageRank arithmetic and no transpose: it only makes graphs.  The
+large generators are C (``graphgen.c``, OpenMP); small named graphs are built
+here with numpy.
+
+Workloads (the shapes of the pages' graphs; none of their data):
+
+* ``citation``   -- 28,042 papers, 2,204 of which cite nothing (page 1, "100
+  Days of GPU" Day 40, the real citation graph's counts); the others cite a
+  geometric number of papers with mean 12, each target drawn with probability
+  proportional to in-degree + 1.  Stands in for the page's citation graph,
+  which is not available here.
+* ``stencil100`` -- 27-point stencil on a 100^3 grid (page 2, the HPCCG
+  problem's 100^3 size): n = 10^6, m = 298^3 - 10^6 = 25,463,592.
+* ``rmatS``      -- R-MAT scale S, edge factor 32, (a, b, c, d) =
+  (0.57, 0.19, 0.19, 0.05), seed S, self-loops and duplicates removed
+  (page 4, "gpu-graph-study", scale study over 2^18 .. 2^23 vertices).
+
+Every CSR has rows sorted by target with no duplicates and no self-loops,
+except graphs built with ``from_edges(..., dedup=False)``.
+"""
+from __future__ import annotations
+
+import ctypes
+import functools
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "graphgen.c")
+_LIB = os.path.join(_HERE, "libgraphgen.so")
+
+RMAT_ABC = (0.57, 0.19, 0.19)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libgraphgen.so in place (gcc, OpenMP)."""
+    cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+           "-o", _LIB + ".tmp", _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+@functools.lru_cache(maxsize=1)
+def _lib() -> ctypes.CDLL:
+    if not os.path.exists(_LIB):
+        raise RuntimeError(f"{_LIB} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(_LIB)
+    p32 = ctypes.POINTER(ctypes.POINTER(ctypes.c_int32))
+    pm = ctypes.POINTER(ctypes.c_int64)
+    lib.gg_rmat.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_double,
+                            ctypes.c_double, ctypes.c_uint64, p32, p32, pm]
+    lib.gg_stencil27.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, p32, p32, pm]
+    lib.gg_citation.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_uint64,
+                                p32, p32, pm]
+    for f in (lib.gg_rmat, lib.gg_stencil27, lib.gg_citation):
+        f.restype = ctypes.c_int
+    lib.gg_free.argtypes = [ctypes.c_void_p]
+    lib.gg_free.restype = None
+    lib.gg_draw_u64.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+    lib.gg_draw_u64.restype = ctypes.c_uint64
+    lib.gg_num_threads.restype = ctypes.c_int
+    return lib
+
+
+class Graph:
+    """Out-edge CSR: ``row_ptr`` int32[n+1], ``col_idx`` int32[m]."""
+
+    __slots__ = ("name", "n", "row_ptr", "col_idx")
+
+    def __init__(self, name: str, row_ptr: np.ndarray, col_idx: np.ndarray):
+        self.name = name
+        self.row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+        self.col_idx = np.ascontiguousarray(col_idx, dtype=np.int32)
+        self.n = int(self.row_ptr.shape[0] - 1)
+
+    @property
+    def m(self) -> int:
+        return int(self.col_idx.shape[0])
+
+    def out_degree(self) -> np.ndarray:
+        return np.diff(self.row_ptr.astype(np.int64))
+
+    def n_dangling(self) -> int:
+        return int(np.count_nonzero(self.out_degree() == 0))
+
+    def edges(self):
+        src = np.repeat(np.arange(self.n, dtype=np.int32), self.out_degree())
+        return src, self.col_idx.copy()
+
+    def __repr__(self) -> str:
+        return f"Graph({self.name!r}, n={self.n}, m={self.m})"
+
+
+def _take(name: str, rc: int, rp, ci, m, n: int) -> Graph:
+    lib = _lib()
+    if rc != 0:
+        raise ValueError(f"graph generator {name} failed with code {rc}")
+    try:
+        row_ptr = np.ctypeslib.as_array(rp, shape=(n + 1,)).copy()
+        col_idx = (np.ctypeslib.as_array(ci, shape=(m.value,)).copy() if m.value > 0
+                   else np.zeros(0, dtype=np.int32))
+    finally:
+        lib.gg_free(ctypes.cast(rp, ctypes.c_void_p))
+        lib.gg_free(ctypes.cast(ci, ctypes.c_void_p))
+    return Graph(name, row_ptr, col_idx)
+
+
+def rmat(scale: int, edge_factor: int = 32, abc=RMAT_ABC, seed: int | None = None) -> Graph:
+    """R-MAT graph with 2**scale vertices and edge_factor * 2**scale draws."""
+    seed = scale if seed is None else seed
+    rp, ci, m = (ctypes.POINTER(ctypes.c_int32)(), ctypes.POINTER(ctypes.c_int32)(),
+                 ctypes.c_int64())
+    rc = _lib().gg_rmat(scale, edge_factor << scale, abc[0], abc[1], abc[2], seed,
+                        ctypes.byref(rp), ctypes.byref(ci), ctypes.byref(m))
+    return _take(f"rmat{scale}", rc, rp, ci, m, 1 << scale)
+
+
+def stencil27(nx: int, ny: int | None = None, nz: int | None = None) -> Graph:
+    ny = nx if ny is None else ny
+    nz = nx if nz is None else nz
+    rp, ci, m = (ctypes.POINTER(ctypes.c_int32)(), ctypes.POINTER(ctypes.c_int32)(),
+                 ctypes.c_int64())
+    rc = _lib().gg_stencil27(nx, ny, nz, ctypes.byref(rp), ctypes.byref(ci), ctypes.byref(m))
+    return _take(f"stencil{nx}x{ny}x{nz}", rc, rp, ci, m, nx * ny * nz)
+
+
+def citation(n: int = 28042, n_dangling: int = 2204, mean_outdeg: float = 12.0,
+             seed: int = 40) -> Graph:
+    rp, ci, m = (ctypes.POINTER(ctypes.c_int32)(), ctypes.POINTER(ctypes.c_int32)(),
+                 ctypes.c_int64())
+    rc = _lib().gg_citation(n, n_dangling, mean_outdeg, seed, ctypes.byref(rp),
+                            ctypes.byref(ci), ctypes.byref(m))
+    return _take("citation", rc, rp, ci, m, n)
+
+
+# ----------------------------------------------------------------- small graphs
+
+def splitmix_u64(seed: int, counters: np.ndarray) -> np.ndarray:
+    """Vectorised counter-based SplitMix64 draws (same stream as graphgen.c)."""
+    with np.errstate(over="ignore"):
+        def mix(z):
+            z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+            z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+            return z ^ (z >> np.uint64(31))
+        key = mix(np.array([seed], dtype=np.uint64))[0]
+        k = np.asarray(counters, dtype=np.uint64)
+        return mix(key + (k + np.uint64(1)) * np.uint64(0x9E3779B97F4A7C15))
+
+
+def from_edges(n: int, src, dst, dedup: bool = True, drop_self: bool = True,
+               name: str = "edges") -> Graph:
+    """Out-edge CSR from an edge list; rows sorted by target."""
+    src = np.asarray(src, dtype=np.int64).ravel()
+    dst = np.asarray(dst, dtype=np.int64).ravel()
+    if src.shape != dst.shape:
+        raise ValueError("src and dst differ in length")
+    if src.size and (src.min() < 0 or src.max() >= n or dst.min() < 0 or dst.max() >= n):
+        raise ValueError("vertex id out of range")
+    if drop_self:
+        keep = src != dst
+        src, dst = src[keep], dst[keep]
+    order = np.lexsort((dst, src))
+    src, dst = src[order], dst[order]
+    if dedup and src.size:
+        keep = np.ones(src.size, dtype=bool)
+        keep[1:] = (src[1:] != src[:-1]) | (dst[1:] != dst[:-1])
+        src, dst = src[keep], dst[keep]
+    row_ptr = np.zeros(n + 1, dtype=np.int64)
+    np.add.at(row_ptr, src + 1, 1)
+    row_ptr = np.cumsum(row_ptr)
+    return Graph(name, row_ptr.astype(np.int32), dst.astype(np.int32))
+
+
+def random_graph(n: int, m_draws: int, seed: int, name: str | None = None,
+                 dedup: bool = True, drop_self: bool = True) -> Graph:
+    """Uniform random digraph from m_draws seeded (u, v) draws."""
+    k = np.arange(2 * m_draws, dtype=np.uint64)
+    r = splitmix_u64(seed, k) % np.uint64(max(n, 1))
+    src, dst = r[0::2].astype(np.int64), r[1::2].astype(np.int64)
+    return from_edges(n, src, dst, dedup=dedup, drop_self=drop_self,
+                      name=name or f"random{n}_{m_draws}_{seed}")
+
+
+def empty(n: int) -> Graph:
+    return Graph(f"empty{n}", np.zeros(n + 1, dtype=np.int32), np.zeros(0, dtype=np.int32))
+
+
+def cycle(n: int) -> Graph:
+    u = np.arange(n)
+    return from_edges(n, u, (u + 1) % n, name=f"cycle{n}")
+
+
+def chain(n: int) -> Graph:
+    u = np.arange(n - 1)
+    return from_edges(n, u, u + 1, name=f"chain{n}")
+
+
+def complete(n: int) -> Graph:
+    u, v = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    return from_edges(n, u.ravel(), v.ravel(), name=f"complete{n}")
+
+
+def star(n: int, inward: bool = True) -> Graph:
+    """Hub 0 and n-1 leaves; inward: every leaf points at the hub."""
+    leaves = np.arange(1, n)
+    hub = np.zeros(n - 1, dtype=np.int64)
+    if inward:
+        return from_edges(n, leaves, hub, name=f"star{n}_in")
+    return from_edges(n, hub, leaves, name=f"star{n}_out")
+
+
+def tiny() -> Graph:
+    """6 vertices, 9 edges, vertex 5 dangling."""
+    src = [0, 0, 1, 1, 2, 3, 3, 4, 4]
+    dst = [1, 2, 2, 3, 0, 4, 5, 0, 5]
+    return from_edges(6, src, dst, name="tiny")
+
+
+def single() -> Graph:
+    return Graph("single", np.zeros(2, dtype=np.int32), np.zeros(0, dtype=np.int32))
+
+
+def two_out(n: int, seed: int, name: str) -> Graph:
+    """Every vertex has exactly two distinct out-neighbours other than itself."""
+    off = splitmix_u64(seed, np.arange(2 * n, dtype=np.uint64))
+    a = 1 + (off[0::2] % np.uint64(n - 1)).astype(np.int64)
+    b = 1 + (off[1::2] % np.uint64(n - 2)).astype(np.int64)
+    b = np.where(b >= a, b + 1, b)  # distinct from a, still in 1..n-1
+    u = np.arange(n, dtype=np.int64)
+    src = np.concatenate([u, u])
+    dst = np.concatenate([(u + a) % n, (u + b) % n])
+    return from_edges(n, src, dst, name=name)
+
+
+def nodangling(n: int = 4096, seed: int = 7) -> Graph:
+    return two_out(n, seed, "nodangling")
+
+
+def dangling(n: int = 4096, n_dangling: int = 400, seed: int = 7) -> Graph:
+    """``nodangling`` with the out-edges of a seeded sample of vertices removed."""
+    g = two_out(n, seed, "dangling")
+    keys = splitmix_u64(seed + 1, np.arange(n, dtype=np.uint64))
+    drop = np.argsort(keys, kind="stable")[:n_dangling]
+    src, dst = g.edges()
+    keep = ~np.isin(src, drop)
+    return from_edges(n, src[keep], dst[keep], name="dangling")
+
+
+def workload(name: str) -> Graph:
+    """The named benchmark workloads."""
+    if name == "citation":
+        return citation()
+    if name == "stencil100":
+        return stencil27(100)
+    if name.startswith("rmat"):
+        return rmat(int(name[4:]))
+    raise KeyError(name)
+
+
+WORKLOADS = ("citation", "stencil100", "rmat18", "rmat21", "rmat23")
