@@ -1,0 +1,222 @@
+"""Benchmark: PageRank power iteration on one MI355X.
+
+One step = the whole path on one synthetic graph already resident in device
+memory: pr_transpose (in-edge CSR by device counting sort), pr_plan_create
+(inverse out-degrees + degree buckets) and pr_run with 50 fixed iterations
+(tol = 0, the timed mode of the Day 40 page).  The default workload is R-MAT
+scale 23, edge factor 32, (a, b, c, d) = (.57, .19, .19, .05), seed 23,
+self-loops and duplicates removed.
+
+Printed (one JSON line): whole-step throughput in GTEPS (edges x iterations /
+step time), plus the per-iteration figures of the dominant kernel (the fused
+iteration, k_iterate) against the HBM roofline, and the CPU oracle's rate on a
+bounded sample of the same graph.
+
+    python bench.py [--steps K] [--warmup W] [--workload rmat23] [--iters 50]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_iterate_rmat23_counters.json")
+KERNEL_SOURCES = ["pagerank_power_iteration_amd/csrc/run.hip",
+                  "pagerank_power_iteration_amd/csrc/plan.hpp",
+                  "pagerank_power_iteration_amd/csrc/common.hpp"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def min_bytes_per_iteration(n: int, m: int) -> int:
+    """Bytes any pull iteration must move: per edge a 4-byte column index and a
+    4-byte gathered contribution; per vertex row_ptr, x read, x' write,
+    inverse out-degree and contrib' write (4 bytes each); plus row_ptr[n]."""
+    return 8 * m + 20 * n + 4
+
+
+def traffic_from_counters(n_launch_bytes: int):
+    """HBM bytes per k_iterate launch from the committed rocprofv3 counter
+    summary, when it was taken on the current kernel source."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None, None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None, c.get("kernel_source_hash")
+    return c.get("hbm_bytes_per_launch"), c.get("kernel_source_hash")
+
+
+def copy_row(torch, gib: float = 2.0, reps: int = 5) -> float:
+    """Device-to-device copy bandwidth (read + write bytes) of a buffer larger
+    than the 256 MB Infinity Cache."""
+    nbytes = int(gib * (1 << 30))
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(g, iters: int) -> dict:
+    import oracle
+    r = oracle.pagerank(g.row_ptr, g.col_idx, d=0.85, tol=0.0, max_iter=iters)
+    secs = r.loop_seconds
+    return {"value": round(g.m * iters / secs / 1e9, 4), "unit": "GTEPS", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{iters} of the 50 iterations on the same {g.name} graph "
+                      f"(fp64, single thread, iteration loop only: {secs:.2f} s)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="rmat23")
+    ap.add_argument("--iters", type=int, default=50)
+    ap.add_argument("--cpu-iters", type=int, default=8,
+                    help="iterations of the CPU oracle sample (0 skips it)")
+    ap.add_argument("--no-copy-row", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding paragraph of DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import graphgen
+    import pagerank_power_iteration_amd as prx
+
+    prx.lib()
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    g = graphgen.workload(args.workload)
+    n, m = g.n, g.m
+    log(f"{g.name}: n={n} m={m} generated in {time.time() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream()
+    dg = prx.DeviceGraph.from_csr(g.row_ptr, g.col_idx)
+    in_rp = torch.empty(n + 1, dtype=torch.int32, device="cuda")
+    in_ci = torch.empty(max(m, 1), dtype=torch.int32, device="cuda")[:m]
+    ws_t = torch.empty(prx.pr_transpose_workspace_bytes(n, m), dtype=torch.uint8, device="cuda")
+    ws_p = torch.empty(prx.pr_plan_workspace_bytes(n, m), dtype=torch.uint8, device="cuda")
+    x = torch.empty(n, dtype=torch.float32, device="cuda")
+    l1 = torch.empty(args.iters, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step():
+        ev[0].record(stream)
+        prx.pr_transpose(n, m, dg.row_ptr, dg.col_idx, in_rp, in_ci, ws_t, 0, stream)
+        ev[1].record(stream)
+        plan = prx.pr_plan_create(n, m, dg.row_ptr, in_rp, in_ci, ws_p, 0, stream)
+        ev[2].record(stream)
+        it = prx.pr_run(plan, 0.85, 0.0, args.iters, x, l1, None, prx.PR_RECORD_EVENTS, stream)
+        ev[3].record(stream)
+        iter_ms = prx.pr_plan_iteration_ms(plan)  # waits for the last iteration
+        prx.pr_plan_destroy(plan)
+        return it, iter_ms
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    parts = {"transpose": [], "plan": [], "run": [], "iter": []}
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        it, iter_ms = step()
+        parts["transpose"].append(ev[0].elapsed_time(ev[1]))
+        parts["plan"].append(ev[1].elapsed_time(ev[2]))
+        parts["run"].append(ev[2].elapsed_time(ev[3]))
+        parts["iter"].append(iter_ms / it)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+
+    med = {k: statistics.median(v) for k, v in parts.items()}
+    iter_ms = med["iter"]
+    bytes_iter = min_bytes_per_iteration(n, m)
+    achieved = bytes_iter / (iter_ms * 1e-3) / 1e9
+    traffic, _ = traffic_from_counters(bytes_iter)
+    log(f"step {ms_per_step:.3f} ms: transpose {med['transpose']:.3f} ms, plan {med['plan']:.3f} ms, "
+        f"run {med['run']:.3f} ms ({iter_ms * 1e3:.1f} us/iteration)")
+
+    plan = prx.pr_plan_create(n, m, dg.row_ptr, in_rp, in_ci, ws_p, 0, stream)
+    buckets = prx.pr_plan_buckets(plan)
+    prx.pr_plan_destroy(plan)
+
+    copy_gbps = None if args.no_copy_row else round(copy_row(torch), 1)
+    del ws_t
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if args.cpu_iters > 0:
+        log(f"timing the CPU oracle on {args.cpu_iters} iterations ...")
+        cpu = cpu_baseline(g, args.cpu_iters)
+
+    iter_cv = (statistics.pstdev(parts["iter"]) / statistics.mean(parts["iter"])
+               if len(parts["iter"]) > 1 else 0.0)
+    out = {
+        "metric": "GTEPS per PageRank iteration + achieved HBM GB/s (% peak), RMAT scale 23",
+        "value": round(m * args.iters / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "GTEPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": g.name, "n": n, "m": m, "iterations": args.iters, "d": 0.85,
+                   "tol": 0.0, "index": "int32", "step": "pr_transpose + pr_plan_create + pr_run"},
+        "iteration": {"ms": round(iter_ms, 5), "gteps": round(m / (iter_ms * 1e-3) / 1e9, 2),
+                      "cv": round(iter_cv, 4), "algorithmic_bytes": bytes_iter},
+        "transpose_ms": round(med["transpose"], 4),
+        "plan_ms": round(med["plan"], 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "k_iterate"},
+        "copy_row_gbps": copy_gbps,
+        "buckets": buckets,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,184 @@
+/*
+ * pr.h -- C ABI of libpr, PageRank power iteration with dangling-node
+ * redistribution on one AMD Instinct MI355X (gfx950).
+ *
+ * The method ("100 Days of GPU", Day 40 "PageRank on a real graph in CUDA",
+ * section "One iteration, three shapes of work"):
+ *
+ *     x'[v] = (1 - d)/n + d * ( sum over in-neighbours u of x[u]/outdeg[u] + D/n )
+ *
+ * where D is the rank held by vertices with no out-edge (dangling vertices) in
+ * the vector the iteration starts from.  One iteration is a pull-style sparse
+ * matrix-vector product over the in-edge (transposed) graph plus two
+ * full-array reductions: the dangling mass and the L1 distance between
+ * successive vectors, which decides convergence.  The same page builds the
+ * in-edge graph once with a counting sort (histogram, prefix sum, scatter).
+ *
+ * Conventions for every entry point:
+ *   - Graphs are CSR with int32 indices: row_ptr[n+1], col_idx[nnz], and
+ *     nnz <= INT32_MAX.  "Out-edge CSR" rows list the targets of each vertex;
+ *     "in-edge CSR" rows list the sources pointing at each vertex.
+ *   - Pointers named *_dev are device pointers (hipMalloc'd or torch CUDA
+ *     tensors); the caller owns them and keeps them alive while any work that
+ *     uses them is in flight.  Host pointers are named *_host.
+ *   - Workspaces are caller-allocated device memory of at least the size the
+ *     matching *_workspace_bytes() call returns, 256-byte aligned.  The
+ *     library never allocates device memory and never uses the null stream.
+ *   - `stream` is a hipStream_t (passed as void*); all device work is enqueued
+ *     on it.  An entry point returns once its work is enqueued unless its
+ *     description says it synchronizes.
+ *   - Every entry point returns PR_OK (0) or a negative pr_status; no C++
+ *     exception crosses the ABI.  pr_last_error() gives the calling thread's
+ *     most recent error message.
+ */
+#ifndef PR_H
+#define PR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pr_status {
+    PR_OK = 0,
+    PR_ERR_ARG = -1,       /* null pointer, n < 1, nnz < 0 or > INT32_MAX, d outside [0,1],
+                              max_iter < 1, unknown flag bits */
+    PR_ERR_WORKSPACE = -2, /* workspace too small or not 256-byte aligned */
+    PR_ERR_GRAPH = -3,     /* malformed CSR found by PR_VALIDATE */
+    PR_ERR_HIP = -4        /* a HIP runtime call or kernel launch failed */
+} pr_status;
+
+/* Flags for pr_transpose and pr_plan_create. */
+#define PR_VALIDATE 0x1u /* check the input CSR on the device (row_ptr[0] == 0,
+                            non-decreasing, row_ptr[n] == nnz, 0 <= col < n); this
+                            synchronizes `stream` once to read the verdict.  Without
+                            it malformed input cannot fault the GPU (every device
+                            index is clamped) but the output is unspecified. */
+
+/* Flags for pr_run. */
+#define PR_X0_GIVEN 0x1u      /* x holds the start vector on entry (warm start, or a
+                                 resume from a saved vector); otherwise 1/n */
+#define PR_RECORD_EVENTS 0x2u /* record the plan's timing events around the
+                                 iteration launches (see pr_plan_iteration_ms) */
+
+/* Device bytes pr_transpose needs as workspace.  Host-only, no device work. */
+size_t pr_transpose_workspace_bytes(int32_t n, int64_t nnz);
+
+/*
+ * In-edge CSR of an out-edge CSR (Day 40, "One iteration, three shapes of
+ * work": the counting-sort transpose).  Built on the device as a stable
+ * least-significant-digit radix sort of the (target, source) pairs by target:
+ * each 8-bit pass is a histogram, an exclusive scan and a scatter; the
+ * in-degree histogram, exclusive-scanned, is in_row_ptr.
+ *
+ *   n, nnz                     vertices and edges
+ *   out_row_ptr_dev[n+1]       out-edge CSR (read only)
+ *   out_col_idx_dev[nnz]
+ *   in_row_ptr_dev[n+1]        written: in_row_ptr[v+1]-in_row_ptr[v] = in-degree of v
+ *   in_col_idx_dev[nnz]        written: the sources of each in-row in ascending id
+ *                              order, parallel edges kept adjacent; bit-identical to
+ *                              a sequential counting sort over sources in order
+ *   ws_dev, ws_bytes           workspace, >= pr_transpose_workspace_bytes(n, nnz)
+ *   flags                      0 or PR_VALIDATE
+ *
+ * Asynchronous on `stream` unless PR_VALIDATE is given.
+ */
+int pr_transpose(int32_t n, int64_t nnz, const int32_t* out_row_ptr_dev,
+                 const int32_t* out_col_idx_dev, int32_t* in_row_ptr_dev,
+                 int32_t* in_col_idx_dev, void* ws_dev, size_t ws_bytes, uint32_t flags,
+                 void* stream);
+
+/* Opaque iteration plan. */
+typedef struct pr_plan pr_plan;
+
+/* Device bytes pr_plan_create needs as workspace.  Host-only. */
+size_t pr_plan_workspace_bytes(int32_t n, int64_t nnz);
+
+/*
+ * Build an iteration plan for one graph: the inverse out-degrees
+ * (1/outdeg[u], or 0 for a dangling vertex -- Meerkat's PageRank section
+ * caches the per-vertex contribution ratio for the same reason), the
+ * in-rows partitioned into degree buckets (lane, sub-wave group, wavefront and
+ * workgroup per row; "gpu-graph-study", PageRank T4 degree-bucketed load
+ * balancing), and the per-run scratch vectors, all inside ws_dev.
+ *
+ *   plan_out                   receives the plan (host memory owned by the
+ *                              library; release with pr_plan_destroy)
+ *   out_row_ptr_dev[n+1]       out-edge CSR row pointers (out-degrees)
+ *   in_row_ptr_dev[n+1]        in-edge CSR from pr_transpose
+ *   in_col_idx_dev[nnz]
+ *   ws_dev, ws_bytes           workspace, >= pr_plan_workspace_bytes(n, nnz); must
+ *                              stay allocated and untouched while the plan lives
+ *   flags                      0 or PR_VALIDATE
+ *
+ * The plan keeps the three graph pointers (not copies): they must stay valid
+ * and unchanged while the plan lives.  Synchronizes `stream` once (the bucket
+ * sizes are read back to size the launch).  The plan belongs to the device
+ * that was current when it was created.
+ */
+int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_row_ptr_dev,
+                   const int32_t* in_row_ptr_dev, const int32_t* in_col_idx_dev, void* ws_dev,
+                   size_t ws_bytes, uint32_t flags, void* stream);
+
+/* Release a plan (host state and its events); NULL is allowed.  The caller
+ * must make sure no pr_run on it is still in flight. */
+int pr_plan_destroy(pr_plan* plan);
+
+/*
+ * Power iteration (Day 40 update; Meerkat's PageRank section gives the same
+ * loop with max_iter and an L1 error margin).
+ *
+ *   d              damping factor in [0, 1] (0.85 on the pages); the device
+ *                  arithmetic uses it rounded to float, the constant term
+ *                  (1-d)/n + d*D/n is formed in double
+ *   tol            tol > 0: stop after the first iteration t whose L1 distance
+ *                  sum_v |x_t[v] - x_{t-1}[v]| is below tol (that iteration
+ *                  counts and its vector is returned); tol <= 0: run exactly
+ *                  max_iter iterations (the timed mode)
+ *   max_iter       >= 1
+ *   x_dev[n]       float; start vector on entry if PR_X0_GIVEN (else ignored and
+ *                  1/n is used), ranks after the last iteration on exit
+ *   l1_trace_dev   float[max_iter]; entry t-1 = L1 distance of iteration t;
+ *                  entries after the stopping iteration are left untouched
+ *   sum_trace_dev  float[max_iter] or NULL; entry t-1 = sum of x after iteration t
+ *                  (the page's conserved quantity, which should stay 1)
+ *   iterations_host  receives the number of iterations performed
+ *   flags          PR_X0_GIVEN | PR_RECORD_EVENTS
+ *
+ * The dangling mass and the stop test stay on the device: no iteration waits
+ * for the host.  With tol <= 0 the call only enqueues work and does not
+ * synchronize.  With tol > 0 it enqueues iterations in chunks, reads the
+ * device stop flag after each chunk while the next chunk runs, and
+ * synchronizes `stream` before returning.  Calls on one plan must not
+ * overlap in time (they share the plan's scratch).
+ */
+int pr_run(pr_plan* plan, double d, double tol, int32_t max_iter, float* x_dev,
+           float* l1_trace_dev, float* sum_trace_dev, int32_t* iterations_host, uint32_t flags,
+           void* stream);
+
+/* Elapsed milliseconds between the timing events the last pr_run with
+ * PR_RECORD_EVENTS recorded (first iteration launch to last), waiting for the
+ * second event.  Divide by the iteration count for the mean per iteration. */
+int pr_plan_iteration_ms(pr_plan* plan, float* ms_host);
+
+/* Introspection for tests and benchmarks: the number of degree buckets and,
+ * per bucket, its first row-length, row count and edge count (host arrays of
+ * length at least pr_plan_num_buckets()). */
+int pr_plan_num_buckets(void);
+int pr_plan_buckets(const pr_plan* plan, int32_t* min_len_host, int32_t* rows_host,
+                    int64_t* edges_host);
+
+/* Human-readable name of a status code (static storage). */
+const char* pr_status_string(int status);
+
+/* Message of the calling thread's most recent failure (thread-local storage,
+ * valid until the next call on the same thread). */
+const char* pr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PR_H */

@@ -1,0 +1,131 @@
+"""PageRank power iteration with dangling-node redistribution on one AMD
+Instinct MI355X (gfx950).
+
+Every step runs in the HIP library ``libpr.so`` behind the C ABI in
+``include/pr.h``; ``_lib`` binds it with ctypes under the same names.  The
+helpers below only allocate device memory with torch and pass pointers:
+
+    >>> import pagerank_power_iteration_amd as prx
+    >>> g = prx.DeviceGraph.from_csr(row_ptr, col_idx)     # numpy int32 CSR
+    >>> plan = prx.Plan(g)                                 # pr_transpose + pr_plan_create
+    >>> res = plan.run(d=0.85, tol=1e-6, max_iter=100)     # pr_run
+    >>> res.x, res.iterations, res.l1_trace
+"""
+from __future__ import annotations
+
+from ._lib import (PR_ERR_ARG, PR_ERR_GRAPH, PR_ERR_HIP, PR_ERR_WORKSPACE, PR_OK,
+                   PR_RECORD_EVENTS, PR_VALIDATE, PR_X0_GIVEN, PrError, lib, pr_last_error,
+                   pr_plan_buckets, pr_plan_create, pr_plan_destroy, pr_plan_iteration_ms,
+                   pr_plan_num_buckets, pr_plan_workspace_bytes, pr_run, pr_status_string,
+                   pr_transpose, pr_transpose_workspace_bytes)
+
+__all__ = [
+    "DeviceGraph", "Plan", "RunResult", "transpose", "PrError", "lib",
+    "pr_transpose", "pr_transpose_workspace_bytes", "pr_plan_create", "pr_plan_destroy",
+    "pr_plan_workspace_bytes", "pr_run", "pr_plan_iteration_ms", "pr_plan_buckets",
+    "pr_plan_num_buckets", "pr_status_string", "pr_last_error",
+    "PR_OK", "PR_ERR_ARG", "PR_ERR_WORKSPACE", "PR_ERR_GRAPH", "PR_ERR_HIP",
+    "PR_VALIDATE", "PR_X0_GIVEN", "PR_RECORD_EVENTS",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _device_buffer(nbytes: int, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+class DeviceGraph:
+    """Out-edge CSR resident in device memory (int32)."""
+
+    def __init__(self, row_ptr, col_idx):
+        self.row_ptr = row_ptr
+        self.col_idx = col_idx
+        self.n = int(row_ptr.numel() - 1)
+        self.nnz = int(col_idx.numel())
+
+    @classmethod
+    def from_csr(cls, row_ptr, col_idx, device="cuda"):
+        torch = _torch()
+        rp = torch.as_tensor(row_ptr, dtype=torch.int32).to(device)
+        ci = torch.as_tensor(col_idx, dtype=torch.int32).to(device)
+        if ci.numel() == 0:
+            ci = torch.zeros(1, dtype=torch.int32, device=device)[:0]
+        return cls(rp, ci)
+
+
+def transpose(graph: DeviceGraph, flags: int = 0, stream=None, ws=None):
+    """In-edge CSR (in_row_ptr, in_col_idx) of `graph` via pr_transpose."""
+    torch = _torch()
+    dev = graph.row_ptr.device
+    in_rp = torch.empty(graph.n + 1, dtype=torch.int32, device=dev)
+    in_ci = torch.empty(max(graph.nnz, 1), dtype=torch.int32, device=dev)[: graph.nnz]
+    if ws is None:
+        ws = _device_buffer(pr_transpose_workspace_bytes(graph.n, graph.nnz), dev)
+    pr_transpose(graph.n, graph.nnz, graph.row_ptr, graph.col_idx, in_rp, in_ci, ws, flags, stream)
+    return in_rp, in_ci
+
+
+class RunResult:
+    __slots__ = ("x", "iterations", "l1_trace", "sum_trace")
+
+    def __init__(self, x, iterations, l1_trace, sum_trace):
+        self.x, self.iterations, self.l1_trace, self.sum_trace = x, iterations, l1_trace, sum_trace
+
+
+class Plan:
+    """A graph transposed and planned on the device, ready for pr_run.
+
+    Keeps every device buffer the C plan points into alive for its lifetime.
+    """
+
+    def __init__(self, graph: DeviceGraph, flags: int = 0, stream=None, in_csr=None):
+        self.graph = graph
+        dev = graph.row_ptr.device
+        if in_csr is None:
+            in_csr = transpose(graph, flags, stream)
+        self.in_row_ptr, self.in_col_idx = in_csr
+        self.ws = _device_buffer(pr_plan_workspace_bytes(graph.n, graph.nnz), dev)
+        self.handle = pr_plan_create(graph.n, graph.nnz, graph.row_ptr, self.in_row_ptr,
+                                     self.in_col_idx, self.ws, flags, stream)
+
+    @property
+    def n(self) -> int:
+        return self.graph.n
+
+    def buckets(self):
+        return pr_plan_buckets(self.handle)
+
+    def run(self, d: float = 0.85, tol: float = 0.0, max_iter: int = 50, x0=None,
+            record_events: bool = False, sum_trace: bool = True, stream=None, out=None):
+        torch = _torch()
+        dev = self.graph.row_ptr.device
+        x = out if out is not None else torch.empty(self.n, dtype=torch.float32, device=dev)
+        flags = 0
+        if x0 is not None:
+            x.copy_(torch.as_tensor(x0, dtype=torch.float32))
+            flags |= PR_X0_GIVEN
+        if record_events:
+            flags |= PR_RECORD_EVENTS
+        l1 = torch.full((max_iter,), float("nan"), dtype=torch.float32, device=dev)
+        st = torch.full((max_iter,), float("nan"), dtype=torch.float32, device=dev) if sum_trace else None
+        it = pr_run(self.handle, d, tol, max_iter, x, l1, st, flags, stream)
+        return RunResult(x, it, l1[:it], None if st is None else st[:it])
+
+    def iteration_ms(self) -> float:
+        return pr_plan_iteration_ms(self.handle)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            pr_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,162 @@
+"""ctypes binding of libpr.so (include/pr.h), one Python function per C entry
+point with the same name.  Argument marshalling only: tensors become device
+pointers, the stream defaults to torch's current stream, and a negative
+status becomes a PrError carrying pr_last_error().  No computation happens
+here, and there is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import functools
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB_PATH = os.path.join(PKG, "libpr.so")
+HEADER = os.path.join(ROOT, "include", "pr.h")
+
+PR_OK = 0
+PR_ERR_ARG = -1
+PR_ERR_WORKSPACE = -2
+PR_ERR_GRAPH = -3
+PR_ERR_HIP = -4
+
+PR_VALIDATE = 0x1
+PR_X0_GIVEN = 0x1
+PR_RECORD_EVENTS = 0x2
+
+
+class PrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [{status}]")
+        self.status = status
+
+
+_c = ctypes
+_vp = _c.c_void_p
+_SIGNATURES = {
+    "pr_transpose_workspace_bytes": (_c.c_size_t, [_c.c_int32, _c.c_int64]),
+    "pr_transpose": (_c.c_int, [_c.c_int32, _c.c_int64, _vp, _vp, _vp, _vp, _vp, _c.c_size_t,
+                                _c.c_uint32, _vp]),
+    "pr_plan_workspace_bytes": (_c.c_size_t, [_c.c_int32, _c.c_int64]),
+    "pr_plan_create": (_c.c_int, [_c.POINTER(_vp), _c.c_int32, _c.c_int64, _vp, _vp, _vp, _vp,
+                                  _c.c_size_t, _c.c_uint32, _vp]),
+    "pr_plan_destroy": (_c.c_int, [_vp]),
+    "pr_run": (_c.c_int, [_vp, _c.c_double, _c.c_double, _c.c_int32, _vp, _vp, _vp,
+                          _c.POINTER(_c.c_int32), _c.c_uint32, _vp]),
+    "pr_plan_iteration_ms": (_c.c_int, [_vp, _c.POINTER(_c.c_float)]),
+    "pr_plan_num_buckets": (_c.c_int, []),
+    "pr_plan_buckets": (_c.c_int, [_vp, _c.POINTER(_c.c_int32), _c.POINTER(_c.c_int32),
+                                   _c.POINTER(_c.c_int64)]),
+    "pr_status_string": (_c.c_char_p, [_c.c_int]),
+    "pr_last_error": (_c.c_char_p, []),
+}
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/pr.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pr_[a-z_0-9]+)\s*\(", text)))
+
+
+@functools.lru_cache(maxsize=1)
+def lib() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: the HIP library is not built (run __graft_entry__.build())")
+    so = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(so, name)
+        fn.restype = res
+        fn.argtypes = args
+    return so
+
+
+def _check(status: int) -> None:
+    if status != PR_OK:
+        msg = lib().pr_last_error().decode(errors="replace")
+        raise PrError(status, f"{lib().pr_status_string(status).decode()}: {msg}")
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------ entry points
+
+def pr_transpose_workspace_bytes(n: int, nnz: int) -> int:
+    return int(lib().pr_transpose_workspace_bytes(n, nnz))
+
+
+def pr_transpose(n, nnz, out_row_ptr, out_col_idx, in_row_ptr, in_col_idx, ws, flags=0,
+                 stream=None) -> None:
+    _check(lib().pr_transpose(n, nnz, _ptr(out_row_ptr), _ptr(out_col_idx), _ptr(in_row_ptr),
+                              _ptr(in_col_idx), _ptr(ws), _nbytes(ws), flags, _stream(stream)))
+
+
+def pr_plan_workspace_bytes(n: int, nnz: int) -> int:
+    return int(lib().pr_plan_workspace_bytes(n, nnz))
+
+
+def pr_plan_create(n, nnz, out_row_ptr, in_row_ptr, in_col_idx, ws, flags=0, stream=None) -> int:
+    h = _vp()
+    _check(lib().pr_plan_create(_c.byref(h), n, nnz, _ptr(out_row_ptr), _ptr(in_row_ptr),
+                                _ptr(in_col_idx), _ptr(ws), _nbytes(ws), flags, _stream(stream)))
+    return h.value
+
+
+def pr_plan_destroy(plan: int | None) -> None:
+    _check(lib().pr_plan_destroy(plan))
+
+
+def pr_run(plan, d, tol, max_iter, x, l1_trace, sum_trace=None, flags=0, stream=None) -> int:
+    it = _c.c_int32(0)
+    _check(lib().pr_run(plan, float(d), float(tol), int(max_iter), _ptr(x), _ptr(l1_trace),
+                        _ptr(sum_trace), _c.byref(it), flags, _stream(stream)))
+    return int(it.value)
+
+
+def pr_plan_iteration_ms(plan) -> float:
+    ms = _c.c_float(0.0)
+    _check(lib().pr_plan_iteration_ms(plan, _c.byref(ms)))
+    return float(ms.value)
+
+
+def pr_plan_num_buckets() -> int:
+    return int(lib().pr_plan_num_buckets())
+
+
+def pr_plan_buckets(plan) -> list[dict]:
+    nb = pr_plan_num_buckets()
+    mins = (_c.c_int32 * nb)()
+    rows = (_c.c_int32 * nb)()
+    edges = (_c.c_int64 * nb)()
+    _check(lib().pr_plan_buckets(plan, mins, rows, edges))
+    return [{"min_len": mins[b], "rows": rows[b], "edges": edges[b]} for b in range(nb)]
+
+
+def pr_status_string(status: int) -> str:
+    return lib().pr_status_string(status).decode()
+
+
+def pr_last_error() -> str:
+    return lib().pr_last_error().decode(errors="replace")

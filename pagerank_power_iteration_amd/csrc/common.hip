@@ -1,0 +1,129 @@
+// Status strings, the thread-local error message, a fill kernel and the
+// device-wide exclusive scan (the "prefix sum" step of the counting-sort
+// transpose on the Day 40 page, "One iteration, three shapes of work").
+#include <cstdarg>
+#include <cstdio>
+
+#include "common.hpp"
+
+namespace pr {
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+// ------------------------------------------------------------------- fill
+
+__global__ __launch_bounds__(kBlock) void k_fill_u32(uint32_t* __restrict__ p, uint32_t value,
+                                                     int64_t count) {
+    for (int64_t i = blockIdx.x * (int64_t)kBlock + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * kBlock)
+        p[i] = value;
+}
+
+int fill_u32(uint32_t* p, uint32_t value, int64_t count, hipStream_t stream) {
+    if (count <= 0) return PR_OK;
+    int64_t blocks = ceil_div(count, kBlock);
+    if (blocks > 4096) blocks = 4096;
+    k_fill_u32<<<dim3((unsigned)blocks), dim3(kBlock), 0, stream>>>(p, value, count);
+    PR_LAUNCHED("fill");
+    return PR_OK;
+}
+
+// ------------------------------------------------------------------- scan
+//
+// Tile = 256 lanes x 16 items.  Pass 1 sums each tile; the tile sums are
+// scanned recursively; pass 2 rescans each tile with its offset.
+
+constexpr int kScanItems = 16;
+constexpr int64_t kScanTile = (int64_t)kBlock * kScanItems;
+
+__global__ __launch_bounds__(kBlock) void k_scan_tile_sums(const uint32_t* __restrict__ in,
+                                                           int64_t N,
+                                                           uint32_t* __restrict__ sums) {
+    __shared__ uint32_t red[kWaves];
+    const int64_t base = blockIdx.x * kScanTile;
+    uint32_t s = 0;
+#pragma unroll
+    for (int r = 0; r < kScanItems; ++r) {
+        int64_t i = base + r * kBlock + threadIdx.x;
+        if (i < N) s += in[i];
+    }
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) sums[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kBlock) void k_scan_tiles(const uint32_t* __restrict__ in, int64_t N,
+                                                       const uint32_t* __restrict__ offsets,
+                                                       uint32_t* __restrict__ out) {
+    __shared__ uint32_t tmp[kWaves + 1];
+    const int64_t base = blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+    uint32_t v[kScanItems];
+    uint32_t local = 0;
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+        int64_t i = base + j;
+        v[j] = i < N ? in[i] : 0u;
+        local += v[j];
+    }
+    uint32_t total;
+    uint32_t run = block_exclusive_scan(local, &total, tmp);
+    if (offsets) run += offsets[blockIdx.x];
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+        int64_t i = base + j;
+        if (i < N) out[i] = run;
+        run += v[j];
+    }
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == kBlock - 1) out[N] = run;
+}
+
+size_t scan_workspace_bytes(int64_t N) {
+    int64_t tiles = ceil_div(N > 0 ? N : 1, kScanTile);
+    if (tiles <= 1) return 256;
+    return align_up(sizeof(uint32_t) * tiles) + align_up(sizeof(uint32_t) * (tiles + 1)) +
+           scan_workspace_bytes(tiles);
+}
+
+int scan_exclusive(const uint32_t* in, uint32_t* out, int64_t N, void* ws, hipStream_t stream) {
+    if (N <= 0) return fill_u32(out, 0u, 1, stream);
+    const int64_t tiles = ceil_div(N, kScanTile);
+    if (tiles == 1) {
+        k_scan_tiles<<<1, kBlock, 0, stream>>>(in, N, nullptr, out);
+        PR_LAUNCHED("scan");
+        return PR_OK;
+    }
+    Carver c(ws);
+    uint32_t* sums = c.take<uint32_t>(tiles);
+    uint32_t* offs = c.take<uint32_t>(tiles + 1);
+    void* rest = c.base + c.used;
+    k_scan_tile_sums<<<dim3((unsigned)tiles), kBlock, 0, stream>>>(in, N, sums);
+    PR_LAUNCHED("scan sums");
+    PR_TRY(scan_exclusive(sums, offs, tiles, rest, stream));
+    k_scan_tiles<<<dim3((unsigned)tiles), kBlock, 0, stream>>>(in, N, offs, out);
+    PR_LAUNCHED("scan tiles");
+    return PR_OK;
+}
+
+}  // namespace pr
+
+extern "C" const char* pr_status_string(int status) {
+    switch (status) {
+        case PR_OK: return "PR_OK";
+        case PR_ERR_ARG: return "PR_ERR_ARG: invalid argument";
+        case PR_ERR_WORKSPACE: return "PR_ERR_WORKSPACE: workspace too small or misaligned";
+        case PR_ERR_GRAPH: return "PR_ERR_GRAPH: malformed CSR";
+        case PR_ERR_HIP: return "PR_ERR_HIP: HIP runtime error";
+        default: return "unknown pr_status";
+    }
+}
+
+extern "C" const char* pr_last_error(void) { return pr::g_last_error; }

@@ -1,0 +1,206 @@
+// Stable least-significant-digit radix pass over (key, value) pairs, the
+// device form of the counting sort the Day 40 page ("One iteration, three
+// shapes of work") runs on the host: per 8-bit digit, a histogram of the
+// digit per tile, an exclusive scan over the digit-major histogram matrix,
+// and a scatter in which every element keeps its order among equal digits.
+//
+// Tile = 256 lanes x 16 items = 4096 elements.  Each wavefront owns 1024
+// consecutive elements and walks them as 16 rounds of 64 consecutive
+// elements, so the (round, lane) order is the element order.  The rank of an
+// element among equal digits in its round comes from eight ballots (one per
+// digit bit); a per-wavefront LDS counter per digit carries the count across
+// rounds.  Elements are then reordered in LDS by (digit, order) and written
+// out in digit runs, so global writes are contiguous within each run.
+#pragma once
+
+#include "common.hpp"
+
+namespace pr {
+
+constexpr int kRadixBits = 8;
+constexpr int kRadixDigits = 1 << kRadixBits;
+constexpr int kRadixItems = 16;
+constexpr int kRadixTile = kBlock * kRadixItems;
+constexpr int kBucketMax = 8;
+
+// Where the pass reads its pairs from.
+enum RadixMode : int {
+    // First transpose pass: key = target id out_col_idx[e]; value = the source
+    // row u that owns edge e (found by binary search in out_row_ptr).
+    kFromOutCsr = 0,
+    // Later passes: keys_in[e], vals_in[e].
+    kFromPairs = 1,
+    // Degree buckets: key = bucket of in-row v's length, value = v.
+    kFromRowLengths = 2,
+};
+
+struct RadixIn {
+    int64_t count;                 // elements
+    int32_t n;                     // vertices
+    const int32_t* keys;           // kFromOutCsr: out_col_idx; kFromPairs: keys
+    const int32_t* vals;           // kFromPairs
+    const int32_t* row_ptr;        // kFromOutCsr: out_row_ptr; kFromRowLengths: in_row_ptr
+    int32_t bucket_min[kBucketMax];  // kFromRowLengths: first length of bucket b
+    int32_t n_buckets;
+    uint32_t* error;               // set to 1 when an input index is out of range
+};
+
+// Largest r in [lo, hi] with row_ptr[r] <= e (the row owning edge e when
+// row_ptr is a valid CSR).  Clamped, so malformed input cannot index out of
+// bounds.
+__device__ __forceinline__ int32_t owner_row(const int32_t* __restrict__ rp, int64_t e, int32_t lo,
+                                             int32_t hi) {
+    while (lo < hi) {
+        int32_t mid = lo + (hi - lo + 1) / 2;
+        if ((int64_t)rp[mid] <= e)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+template <int MODE>
+__device__ __forceinline__ int32_t radix_key(const RadixIn& in, int64_t i) {
+    if (MODE == kFromOutCsr) {
+        int32_t k = in.keys[i];
+        if ((uint32_t)k >= (uint32_t)in.n) {
+            *in.error = 1u;
+            k = k < 0 ? 0 : in.n - 1;
+        }
+        return k;
+    } else if (MODE == kFromPairs) {
+        return in.keys[i];
+    } else {
+        int32_t len = in.row_ptr[i + 1] - in.row_ptr[i];
+        int32_t b = 0;
+        for (int j = 1; j < in.n_buckets; ++j) b += (len >= in.bucket_min[j]) ? 1 : 0;
+        return b;
+    }
+}
+
+// Histogram of one digit per tile, stored digit-major: hist[digit * T + tile].
+// In the first transpose pass it also counts in-degrees into indeg[n].
+template <int MODE>
+__global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, int64_t T,
+                                                       uint32_t* __restrict__ hist,
+                                                       uint32_t* __restrict__ indeg) {
+    __shared__ uint32_t h[kRadixDigits];
+    h[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t base = blockIdx.x * (int64_t)kRadixTile;
+#pragma unroll 4
+    for (int r = 0; r < kRadixItems; ++r) {
+        int64_t i = base + r * kBlock + threadIdx.x;
+        if (i < in.count) {
+            int32_t k = radix_key<MODE>(in, i);
+            atomicAdd(&h[((uint32_t)k >> shift) & (kRadixDigits - 1)], 1u);
+            if (MODE == kFromOutCsr) atomicAdd(&indeg[k], 1u);
+        }
+    }
+    __syncthreads();
+    hist[(int64_t)threadIdx.x * T + blockIdx.x] = h[threadIdx.x];
+}
+
+// Stable scatter.  `scanned` is the exclusive scan of the digit-major
+// histogram.  With LAST only values are written (keys_out unused).
+template <int MODE, bool LAST>
+__global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift, int64_t T,
+                                                          const uint32_t* __restrict__ scanned,
+                                                          int32_t* __restrict__ keys_out,
+                                                          int32_t* __restrict__ vals_out) {
+    __shared__ uint32_t wave_count[kWaves][kRadixDigits];
+    __shared__ uint32_t digit_start[kRadixDigits];
+    __shared__ uint32_t global_start[kRadixDigits];
+    __shared__ int32_t s_key[kRadixTile];
+    __shared__ int32_t s_val[kRadixTile];
+    __shared__ uint32_t scan_tmp[kWaves + 1];
+    __shared__ int32_t s_row_lo, s_row_hi;
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int64_t tile = blockIdx.x;
+    const int64_t base = tile * kRadixTile;
+    const int count = (int)((in.count - base) < kRadixTile ? (in.count - base) : kRadixTile);
+
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) wave_count[w][tid] = 0;
+    if (MODE == kFromOutCsr && tid == 0) {
+        s_row_lo = owner_row(in.row_ptr, base, 0, in.n - 1);
+        s_row_hi = owner_row(in.row_ptr, base + count - 1, s_row_lo, in.n - 1);
+    }
+    __syncthreads();
+
+    int32_t key[kRadixItems], val[kRadixItems];
+    uint32_t rank[kRadixItems];
+#pragma unroll
+    for (int r = 0; r < kRadixItems; ++r) {
+        const int idx = wave * (kWave * kRadixItems) + r * kWave + lane;
+        const bool valid = idx < count;
+        int32_t k = 0, v = 0;
+        if (valid) {
+            const int64_t g = base + idx;
+            k = radix_key<MODE>(in, g);
+            if (MODE == kFromOutCsr)
+                v = owner_row(in.row_ptr, g, s_row_lo, s_row_hi);
+            else if (MODE == kFromPairs)
+                v = in.vals[g];
+            else
+                v = (int32_t)g;
+        }
+        const uint32_t dg = ((uint32_t)k >> shift) & (kRadixDigits - 1);
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < kRadixBits; ++b) {
+            const bool bit = (dg >> b) & 1u;
+            const uint64_t votes = __ballot(bit);
+            peers &= bit ? votes : ~votes;
+        }
+        const uint32_t below = lanes_below(peers);
+        uint32_t prior = 0;
+        if (valid) prior = wave_count[wave][dg];
+        if (valid && below == 0) wave_count[wave][dg] = prior + (uint32_t)__popcll(peers);
+        key[r] = k;
+        val[r] = v;
+        rank[r] = prior + below;
+    }
+    __syncthreads();
+
+    {  // lane tid owns digit tid: per-wavefront prefixes and the tile's digit starts
+        uint32_t c[kWaves], tot = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            c[w] = wave_count[w][tid];
+            wave_count[w][tid] = tot;
+            tot += c[w];
+        }
+        uint32_t all;
+        digit_start[tid] = block_exclusive_scan(tot, &all, scan_tmp);
+        global_start[tid] = scanned[(int64_t)tid * T + tile];
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int r = 0; r < kRadixItems; ++r) {
+        const int idx = wave * (kWave * kRadixItems) + r * kWave + lane;
+        if (idx < count) {
+            const uint32_t dg = ((uint32_t)key[r] >> shift) & (kRadixDigits - 1);
+            const uint32_t pos = digit_start[dg] + wave_count[wave][dg] + rank[r];
+            s_key[pos] = key[r];
+            s_val[pos] = val[r];
+        }
+    }
+    __syncthreads();
+
+    for (int i = tid; i < count; i += kBlock) {
+        const int32_t k = s_key[i];
+        const uint32_t dg = ((uint32_t)k >> shift) & (kRadixDigits - 1);
+        const int64_t o = (int64_t)global_start[dg] + (i - (int64_t)digit_start[dg]);
+        if (!LAST) keys_out[o] = k;
+        vals_out[o] = s_val[i];
+    }
+}
+
+// Number of tiles for `count` elements.
+inline int64_t radix_tiles(int64_t count) { return ceil_div(count > 0 ? count : 1, kRadixTile); }
+
+}  // namespace pr
