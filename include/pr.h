@@ -50,7 +50,7 @@ typedef enum pr_status {
     PR_ERR_HIP = -4        /* a HIP runtime call or kernel launch failed */
 } pr_status;
 
-/* Flags for pr_transpose and pr_plan_create. */
+/* Flag for pr_transpose and pr_plan_create. */
 #define PR_VALIDATE 0x1u /* check the input CSR on the device (row_ptr[0] == 0,
                             non-decreasing, row_ptr[n] == nnz, 0 <= col < n); this
                             synchronizes `stream` once to read the verdict.  Without
@@ -70,8 +70,9 @@ size_t pr_transpose_workspace_bytes(int32_t n, int64_t nnz);
  * In-edge CSR of an out-edge CSR (Day 40, "One iteration, three shapes of
  * work": the counting-sort transpose).  Built on the device as a stable
  * least-significant-digit radix sort of the (target, source) pairs by target:
- * each 8-bit pass is a histogram, an exclusive scan and a scatter; the
- * in-degree histogram, exclusive-scanned, is in_row_ptr.
+ * each 8-bit pass is a histogram, an exclusive scan and a scatter.
+ * in_row_ptr[v] = number of edges whose target is below v (the exclusive scan
+ * of the in-degree histogram), read off the sorted targets.
  *
  *   n, nnz                     vertices and edges
  *   out_row_ptr_dev[n+1]       out-edge CSR (read only)
@@ -93,34 +94,48 @@ int pr_transpose(int32_t n, int64_t nnz, const int32_t* out_row_ptr_dev,
 /* Opaque iteration plan. */
 typedef struct pr_plan pr_plan;
 
-/* Device bytes pr_plan_create needs as workspace.  Host-only. */
+/* Device bytes the plan keeps for its lifetime (pr_plan_create's ws_dev), and
+ * the device bytes it needs only while pr_plan_create runs (scratch_dev).
+ * Host-only, no device work; 0 for invalid sizes. */
 size_t pr_plan_workspace_bytes(int32_t n, int64_t nnz);
+size_t pr_plan_scratch_bytes(int32_t n, int64_t nnz);
 
 /*
- * Build an iteration plan for one graph: the inverse out-degrees
- * (1/outdeg[u], or 0 for a dangling vertex -- Meerkat's PageRank section
- * caches the per-vertex contribution ratio for the same reason), the
- * in-rows partitioned into degree buckets (lane, sub-wave group, wavefront and
- * workgroup per row; "gpu-graph-study", PageRank T4 degree-bucketed load
- * balancing), and the per-run scratch vectors, all inside ws_dev.
+ * Build an iteration plan for one graph, all inside ws_dev:
+ *   - a renumbering of the vertices ("plan order"): rows split into degree
+ *     buckets by in-degree -- one lane, a 4- or 16-lane group, a 64-lane
+ *     wavefront or a 256-lane workgroup per row ("gpu-graph-study", PageRank
+ *     T4 degree-bucketed load balancing) -- with the longest-row bucket first,
+ *     and inside each bucket by decreasing out-degree, ties by id.  Every
+ *     bucket is a contiguous range of plan ids, and the sources read most
+ *     often sit together at the start of each range;
+ *   - inverse out-degrees: 1/outdeg[u], or 0 for a dangling vertex (Meerkat's
+ *     PageRank section caches the per-vertex ratio x[u]/out[u]; the
+ *     "gpu-graph-study" T3 tier precomputes 1/deg);
+ *   - the plan's in-edge CSR: rows and sources in plan ids, each row listing
+ *     its sources in increasing plan id, built from the out-edge CSR on the
+ *     device with the counting-sort transpose of pr_transpose;
+ *   - the work items of the iteration kernel and the per-run scratch.
  *
  *   plan_out                   receives the plan (host memory owned by the
  *                              library; release with pr_plan_destroy)
- *   out_row_ptr_dev[n+1]       out-edge CSR row pointers (out-degrees)
- *   in_row_ptr_dev[n+1]        in-edge CSR from pr_transpose
- *   in_col_idx_dev[nnz]
- *   ws_dev, ws_bytes           workspace, >= pr_plan_workspace_bytes(n, nnz); must
- *                              stay allocated and untouched while the plan lives
+ *   out_row_ptr_dev[n+1]       out-edge CSR (read only; not kept)
+ *   out_col_idx_dev[nnz]
+ *   ws_dev, ws_bytes           >= pr_plan_workspace_bytes(n, nnz); must stay
+ *                              allocated and untouched while the plan lives
+ *   scratch_dev, scratch_bytes >= pr_plan_scratch_bytes(n, nnz); free for other
+ *                              use once the call returns
  *   flags                      0 or PR_VALIDATE
  *
- * The plan keeps the three graph pointers (not copies): they must stay valid
- * and unchanged while the plan lives.  Synchronizes `stream` once (the bucket
- * sizes are read back to size the launch).  The plan belongs to the device
- * that was current when it was created.
+ * Synchronizes `stream` (the bucket sizes and the hub rows' lengths are read
+ * back to build the work list).  The plan belongs to the device current at
+ * creation.  Without PR_VALIDATE a malformed CSR cannot make the library
+ * access memory outside the buffers (targets are clamped), but the ranks are
+ * then unspecified.
  */
 int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_row_ptr_dev,
-                   const int32_t* in_row_ptr_dev, const int32_t* in_col_idx_dev, void* ws_dev,
-                   size_t ws_bytes, uint32_t flags, void* stream);
+                   const int32_t* out_col_idx_dev, void* ws_dev, size_t ws_bytes,
+                   void* scratch_dev, size_t scratch_bytes, uint32_t flags, void* stream);
 
 /* Release a plan (host state and its events); NULL is allowed.  The caller
  * must make sure no pr_run on it is still in flight. */
@@ -169,6 +184,13 @@ int pr_plan_iteration_ms(pr_plan* plan, float* ms_host);
 int pr_plan_num_buckets(void);
 int pr_plan_buckets(const pr_plan* plan, int32_t* min_len_host, int32_t* rows_host,
                     int64_t* edges_host);
+
+/* Introspection for tests: device pointers (inside the plan's workspace) to
+ * the plan's in-edge CSR (n+1 row pointers, nnz sources; rows and sources in
+ * plan ids) and to new_id[n] (the plan id of each of the caller's vertices).
+ * Any output pointer may be NULL. */
+int pr_plan_layout(const pr_plan* plan, const int32_t** in_row_ptr_dev,
+                   const int32_t** in_col_idx_dev, const int32_t** new_id_dev);
 
 /* Human-readable name of a status code (static storage). */
 const char* pr_status_string(int status);

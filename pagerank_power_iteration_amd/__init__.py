@@ -7,23 +7,25 @@ helpers below only allocate device memory with torch and pass pointers:
 
     >>> import pagerank_power_iteration_amd as prx
     >>> g = prx.DeviceGraph.from_csr(row_ptr, col_idx)     # numpy int32 CSR
-    >>> plan = prx.Plan(g)                                 # pr_transpose + pr_plan_create
+    >>> plan = prx.Plan(g)                                 # pr_plan_create
     >>> res = plan.run(d=0.85, tol=1e-6, max_iter=100)     # pr_run
     >>> res.x, res.iterations, res.l1_trace
 """
 from __future__ import annotations
 
 from ._lib import (PR_ERR_ARG, PR_ERR_GRAPH, PR_ERR_HIP, PR_ERR_WORKSPACE, PR_OK,
-                   PR_RECORD_EVENTS, PR_VALIDATE, PR_X0_GIVEN, PrError, lib, pr_last_error,
-                   pr_plan_buckets, pr_plan_create, pr_plan_destroy, pr_plan_iteration_ms,
-                   pr_plan_num_buckets, pr_plan_workspace_bytes, pr_run, pr_status_string,
+                   PR_RECORD_EVENTS, PR_VALIDATE, PR_X0_GIVEN, PrError,
+                   lib, pr_last_error, pr_plan_buckets, pr_plan_create, pr_plan_destroy,
+                   pr_plan_iteration_ms, pr_plan_layout, pr_plan_num_buckets,
+                   pr_plan_scratch_bytes, pr_plan_workspace_bytes, pr_run, pr_status_string,
                    pr_transpose, pr_transpose_workspace_bytes)
 
 __all__ = [
     "DeviceGraph", "Plan", "RunResult", "transpose", "PrError", "lib",
     "pr_transpose", "pr_transpose_workspace_bytes", "pr_plan_create", "pr_plan_destroy",
-    "pr_plan_workspace_bytes", "pr_run", "pr_plan_iteration_ms", "pr_plan_buckets",
-    "pr_plan_num_buckets", "pr_status_string", "pr_last_error",
+    "pr_plan_workspace_bytes", "pr_plan_scratch_bytes", "pr_run", "pr_plan_iteration_ms",
+    "pr_plan_buckets", "pr_plan_num_buckets", "pr_plan_layout", "pr_status_string",
+    "pr_last_error",
     "PR_OK", "PR_ERR_ARG", "PR_ERR_WORKSPACE", "PR_ERR_GRAPH", "PR_ERR_HIP",
     "PR_VALIDATE", "PR_X0_GIVEN", "PR_RECORD_EVENTS",
 ]
@@ -78,20 +80,34 @@ class RunResult:
 
 
 class Plan:
-    """A graph transposed and planned on the device, ready for pr_run.
+    """A graph planned on the device (pr_plan_create), ready for pr_run.
 
-    Keeps every device buffer the C plan points into alive for its lifetime.
+    Keeps the plan's workspace alive for its lifetime; the out-edge CSR and
+    the scratch buffer are only needed while it is built.
     """
 
-    def __init__(self, graph: DeviceGraph, flags: int = 0, stream=None, in_csr=None):
+    def __init__(self, graph: DeviceGraph, flags: int = 0, stream=None):
         self.graph = graph
         dev = graph.row_ptr.device
-        if in_csr is None:
-            in_csr = transpose(graph, flags, stream)
-        self.in_row_ptr, self.in_col_idx = in_csr
         self.ws = _device_buffer(pr_plan_workspace_bytes(graph.n, graph.nnz), dev)
-        self.handle = pr_plan_create(graph.n, graph.nnz, graph.row_ptr, self.in_row_ptr,
-                                     self.in_col_idx, self.ws, flags, stream)
+        scratch = _device_buffer(pr_plan_scratch_bytes(graph.n, graph.nnz), dev)
+        self.handle = pr_plan_create(graph.n, graph.nnz, graph.row_ptr, graph.col_idx, self.ws,
+                                     scratch, flags, stream)
+        del scratch
+
+    def layout(self):
+        """(in_row_ptr, in_col_idx, new_id) of the plan as torch tensors (views
+        of the plan's workspace): the in-edge CSR in plan ids and the plan id
+        of each of the caller's vertices."""
+        torch = _torch()
+        rp, ci, nid = pr_plan_layout(self.handle)
+        base = self.ws.data_ptr()
+        n, m = self.graph.n, self.graph.nnz
+
+        def view(addr, count):
+            off = addr - base
+            return self.ws[off:off + 4 * count].view(torch.int32)
+        return view(rp, n + 1), view(ci, m), view(nid, n)
 
     @property
     def n(self) -> int:

@@ -40,8 +40,9 @@ _SIGNATURES = {
     "pr_transpose": (_c.c_int, [_c.c_int32, _c.c_int64, _vp, _vp, _vp, _vp, _vp, _c.c_size_t,
                                 _c.c_uint32, _vp]),
     "pr_plan_workspace_bytes": (_c.c_size_t, [_c.c_int32, _c.c_int64]),
-    "pr_plan_create": (_c.c_int, [_c.POINTER(_vp), _c.c_int32, _c.c_int64, _vp, _vp, _vp, _vp,
-                                  _c.c_size_t, _c.c_uint32, _vp]),
+    "pr_plan_scratch_bytes": (_c.c_size_t, [_c.c_int32, _c.c_int64]),
+    "pr_plan_create": (_c.c_int, [_c.POINTER(_vp), _c.c_int32, _c.c_int64, _vp, _vp, _vp,
+                                  _c.c_size_t, _vp, _c.c_size_t, _c.c_uint32, _vp]),
     "pr_plan_destroy": (_c.c_int, [_vp]),
     "pr_run": (_c.c_int, [_vp, _c.c_double, _c.c_double, _c.c_int32, _vp, _vp, _vp,
                           _c.POINTER(_c.c_int32), _c.c_uint32, _vp]),
@@ -49,6 +50,7 @@ _SIGNATURES = {
     "pr_plan_num_buckets": (_c.c_int, []),
     "pr_plan_buckets": (_c.c_int, [_vp, _c.POINTER(_c.c_int32), _c.POINTER(_c.c_int32),
                                    _c.POINTER(_c.c_int64)]),
+    "pr_plan_layout": (_c.c_int, [_vp, _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_vp)]),
     "pr_status_string": (_c.c_char_p, [_c.c_int]),
     "pr_last_error": (_c.c_char_p, []),
 }
@@ -117,11 +119,23 @@ def pr_plan_workspace_bytes(n: int, nnz: int) -> int:
     return int(lib().pr_plan_workspace_bytes(n, nnz))
 
 
-def pr_plan_create(n, nnz, out_row_ptr, in_row_ptr, in_col_idx, ws, flags=0, stream=None) -> int:
+def pr_plan_scratch_bytes(n: int, nnz: int) -> int:
+    return int(lib().pr_plan_scratch_bytes(n, nnz))
+
+
+def pr_plan_create(n, nnz, out_row_ptr, out_col_idx, ws, scratch, flags=0, stream=None) -> int:
     h = _vp()
-    _check(lib().pr_plan_create(_c.byref(h), n, nnz, _ptr(out_row_ptr), _ptr(in_row_ptr),
-                                _ptr(in_col_idx), _ptr(ws), _nbytes(ws), flags, _stream(stream)))
+    _check(lib().pr_plan_create(_c.byref(h), n, nnz, _ptr(out_row_ptr), _ptr(out_col_idx),
+                                _ptr(ws), _nbytes(ws), _ptr(scratch), _nbytes(scratch), flags,
+                                _stream(stream)))
     return h.value
+
+
+def pr_plan_layout(plan) -> tuple[int, int, int | None]:
+    """Device addresses of the plan's in_row_ptr, in_col_idx and new_id."""
+    rp, ci, nid = _vp(), _vp(), _vp()
+    _check(lib().pr_plan_layout(plan, _c.byref(rp), _c.byref(ci), _c.byref(nid)))
+    return rp.value, ci.value, nid.value
 
 
 def pr_plan_destroy(plan: int | None) -> None:

@@ -46,12 +46,12 @@ int fill_u32(uint32_t* p, uint32_t value, int64_t count, hipStream_t stream) {
 constexpr int kScanItems = 16;
 constexpr int64_t kScanTile = (int64_t)kBlock * kScanItems;
 
-__global__ __launch_bounds__(kBlock) void k_scan_tile_sums(const uint32_t* __restrict__ in,
-                                                           int64_t N,
-                                                           uint32_t* __restrict__ sums) {
-    __shared__ uint32_t red[kWaves];
+template <class T>
+__global__ __launch_bounds__(kBlock) void k_scan_tile_sums(const T* __restrict__ in, int64_t N,
+                                                           T* __restrict__ sums) {
+    __shared__ T red[kWaves];
     const int64_t base = blockIdx.x * kScanTile;
-    uint32_t s = 0;
+    T s = 0;
 #pragma unroll
     for (int r = 0; r < kScanItems; ++r) {
         int64_t i = base + r * kBlock + threadIdx.x;
@@ -61,21 +61,22 @@ __global__ __launch_bounds__(kBlock) void k_scan_tile_sums(const uint32_t* __res
     if (threadIdx.x == 0) sums[blockIdx.x] = s;
 }
 
-__global__ __launch_bounds__(kBlock) void k_scan_tiles(const uint32_t* __restrict__ in, int64_t N,
-                                                       const uint32_t* __restrict__ offsets,
-                                                       uint32_t* __restrict__ out) {
-    __shared__ uint32_t tmp[kWaves + 1];
+template <class T>
+__global__ __launch_bounds__(kBlock) void k_scan_tiles(const T* __restrict__ in, int64_t N,
+                                                       const T* __restrict__ offsets,
+                                                       T* __restrict__ out) {
+    __shared__ T tmp[kWaves + 1];
     const int64_t base = blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
-    uint32_t v[kScanItems];
-    uint32_t local = 0;
+    T v[kScanItems];
+    T local = 0;
 #pragma unroll
     for (int j = 0; j < kScanItems; ++j) {
         int64_t i = base + j;
-        v[j] = i < N ? in[i] : 0u;
+        v[j] = i < N ? in[i] : (T)0;
         local += v[j];
     }
-    uint32_t total;
-    uint32_t run = block_exclusive_scan(local, &total, tmp);
+    T total;
+    T run = block_exclusive_scan(local, &total, tmp);
     if (offsets) run += offsets[blockIdx.x];
 #pragma unroll
     for (int j = 0; j < kScanItems; ++j) {
@@ -89,28 +90,43 @@ __global__ __launch_bounds__(kBlock) void k_scan_tiles(const uint32_t* __restric
 size_t scan_workspace_bytes(int64_t N) {
     int64_t tiles = ceil_div(N > 0 ? N : 1, kScanTile);
     if (tiles <= 1) return 256;
-    return align_up(sizeof(uint32_t) * tiles) + align_up(sizeof(uint32_t) * (tiles + 1)) +
+    return align_up(sizeof(uint64_t) * tiles) + align_up(sizeof(uint64_t) * (tiles + 1)) +
            scan_workspace_bytes(tiles);
 }
 
-int scan_exclusive(const uint32_t* in, uint32_t* out, int64_t N, void* ws, hipStream_t stream) {
-    if (N <= 0) return fill_u32(out, 0u, 1, stream);
+template <class T>
+int scan_impl(const T* in, T* out, int64_t N, void* ws, hipStream_t stream) {
+    if (N <= 0) {
+        k_fill_u32<<<1, kBlock, 0, stream>>>(reinterpret_cast<uint32_t*>(out), 0u,
+                                            (int64_t)(sizeof(T) / 4));
+        PR_LAUNCHED("scan fill");
+        return PR_OK;
+    }
     const int64_t tiles = ceil_div(N, kScanTile);
     if (tiles == 1) {
-        k_scan_tiles<<<1, kBlock, 0, stream>>>(in, N, nullptr, out);
+        k_scan_tiles<T><<<1, kBlock, 0, stream>>>(in, N, nullptr, out);
         PR_LAUNCHED("scan");
         return PR_OK;
     }
-    Carver c(ws);
-    uint32_t* sums = c.take<uint32_t>(tiles);
-    uint32_t* offs = c.take<uint32_t>(tiles + 1);
-    void* rest = c.base + c.used;
-    k_scan_tile_sums<<<dim3((unsigned)tiles), kBlock, 0, stream>>>(in, N, sums);
+    // workspace laid out for 8-byte items whatever T is (see scan_workspace_bytes)
+    char* base = static_cast<char*>(ws);
+    T* sums = reinterpret_cast<T*>(base);
+    T* offs = reinterpret_cast<T*>(base + align_up(sizeof(uint64_t) * tiles));
+    void* rest = base + align_up(sizeof(uint64_t) * tiles) + align_up(sizeof(uint64_t) * (tiles + 1));
+    k_scan_tile_sums<T><<<dim3((unsigned)tiles), kBlock, 0, stream>>>(in, N, sums);
     PR_LAUNCHED("scan sums");
-    PR_TRY(scan_exclusive(sums, offs, tiles, rest, stream));
-    k_scan_tiles<<<dim3((unsigned)tiles), kBlock, 0, stream>>>(in, N, offs, out);
+    PR_TRY(scan_impl<T>(sums, offs, tiles, rest, stream));
+    k_scan_tiles<T><<<dim3((unsigned)tiles), kBlock, 0, stream>>>(in, N, offs, out);
     PR_LAUNCHED("scan tiles");
     return PR_OK;
+}
+
+int scan_exclusive(const uint32_t* in, uint32_t* out, int64_t N, void* ws, hipStream_t stream) {
+    return scan_impl<uint32_t>(in, out, N, ws, stream);
+}
+
+int scan_exclusive(const uint64_t* in, uint64_t* out, int64_t N, void* ws, hipStream_t stream) {
+    return scan_impl<uint64_t>(in, out, N, ws, stream);
 }
 
 }  // namespace pr

@@ -136,10 +136,11 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
 
 // ----------------------------------------------------------- host helpers
 
-// Device-wide exclusive scan of uint32 counts: out[i] = sum in[0..i) for
-// i in [0, N]; out[N] is the total.  The total must fit in uint32.
+// Device-wide exclusive scan: out[i] = sum in[0..i) for i in [0, N]; out[N]
+// is the total.  uint32 (totals must fit) and uint64 instantiations.
 size_t scan_workspace_bytes(int64_t N);
 int scan_exclusive(const uint32_t* in, uint32_t* out, int64_t N, void* ws, hipStream_t stream);
+int scan_exclusive(const uint64_t* in, uint64_t* out, int64_t N, void* ws, hipStream_t stream);
 
 // Fill `count` 32-bit words with `value` (a kernel, so it is safe under
 // stream capture).
@@ -148,6 +149,9 @@ int fill_u32(uint32_t* p, uint32_t value, int64_t count, hipStream_t stream);
 // Copy a device error word to the host (synchronizing `stream`); PR_ERR_GRAPH
 // when it is non-zero.
 int read_error_word(const uint32_t* err_dev, hipStream_t stream, const char* what);
+
+// PR_VALIDATE check of an out-edge row-pointer array; sets *err on failure.
+int check_out_row_ptr(const int32_t* rp, int32_t n, int64_t nnz, uint32_t* err, hipStream_t stream);
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 

@@ -21,7 +21,6 @@ constexpr int kRadixBits = 8;
 constexpr int kRadixDigits = 1 << kRadixBits;
 constexpr int kRadixItems = 16;
 constexpr int kRadixTile = kBlock * kRadixItems;
-constexpr int kBucketMax = 8;
 
 // Where the pass reads its pairs from.
 enum RadixMode : int {
@@ -30,18 +29,16 @@ enum RadixMode : int {
     kFromOutCsr = 0,
     // Later passes: keys_in[e], vals_in[e].
     kFromPairs = 1,
-    // Degree buckets: key = bucket of in-row v's length, value = v.
-    kFromRowLengths = 2,
+    // Vertex keys: key = keys[i], value = i.
+    kFromKeys = 2,
 };
 
 struct RadixIn {
     int64_t count;                 // elements
     int32_t n;                     // vertices
-    const int32_t* keys;           // kFromOutCsr: out_col_idx; kFromPairs: keys
+    const int32_t* keys;           // kFromOutCsr: out_col_idx; kFromPairs, kFromKeys: keys
     const int32_t* vals;           // kFromPairs
-    const int32_t* row_ptr;        // kFromOutCsr: out_row_ptr; kFromRowLengths: in_row_ptr
-    int32_t bucket_min[kBucketMax];  // kFromRowLengths: first length of bucket b
-    int32_t n_buckets;
+    const int32_t* row_ptr;        // kFromOutCsr: out_row_ptr
     uint32_t* error;               // set to 1 when an input index is out of range
 };
 
@@ -69,22 +66,15 @@ __device__ __forceinline__ int32_t radix_key(const RadixIn& in, int64_t i) {
             k = k < 0 ? 0 : in.n - 1;
         }
         return k;
-    } else if (MODE == kFromPairs) {
-        return in.keys[i];
     } else {
-        int32_t len = in.row_ptr[i + 1] - in.row_ptr[i];
-        int32_t b = 0;
-        for (int j = 1; j < in.n_buckets; ++j) b += (len >= in.bucket_min[j]) ? 1 : 0;
-        return b;
+        return in.keys[i];
     }
 }
 
 // Histogram of one digit per tile, stored digit-major: hist[digit * T + tile].
-// In the first transpose pass it also counts in-degrees into indeg[n].
 template <int MODE>
 __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, int64_t T,
-                                                       uint32_t* __restrict__ hist,
-                                                       uint32_t* __restrict__ indeg) {
+                                                       uint32_t* __restrict__ hist) {
     __shared__ uint32_t h[kRadixDigits];
     h[threadIdx.x] = 0;
     __syncthreads();
@@ -95,7 +85,6 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, in
         if (i < in.count) {
             int32_t k = radix_key<MODE>(in, i);
             atomicAdd(&h[((uint32_t)k >> shift) & (kRadixDigits - 1)], 1u);
-            if (MODE == kFromOutCsr) atomicAdd(&indeg[k], 1u);
         }
     }
     __syncthreads();
@@ -103,8 +92,8 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, in
 }
 
 // Stable scatter.  `scanned` is the exclusive scan of the digit-major
-// histogram.  With LAST only values are written (keys_out unused).
-template <int MODE, bool LAST>
+// histogram.  Keys are written only when keys_out is not null.
+template <int MODE>
 __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift, int64_t T,
                                                           const uint32_t* __restrict__ scanned,
                                                           int32_t* __restrict__ keys_out,
@@ -145,7 +134,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
             else if (MODE == kFromPairs)
                 v = in.vals[g];
             else
-                v = (int32_t)g;
+                v = (int32_t)g;  // kFromKeys: the index itself
         }
         const uint32_t dg = ((uint32_t)k >> shift) & (kRadixDigits - 1);
         uint64_t peers = __ballot(valid);
@@ -195,12 +184,74 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
         const int32_t k = s_key[i];
         const uint32_t dg = ((uint32_t)k >> shift) & (kRadixDigits - 1);
         const int64_t o = (int64_t)global_start[dg] + (i - (int64_t)digit_start[dg]);
-        if (!LAST) keys_out[o] = k;
+        if (keys_out) keys_out[o] = k;
         vals_out[o] = s_val[i];
     }
 }
 
 // Number of tiles for `count` elements.
 inline int64_t radix_tiles(int64_t count) { return ceil_div(count > 0 ? count : 1, kRadixTile); }
+
+static_assert(kBlock == kRadixDigits, "one lane per digit in the scatter's digit phase");
+
+// Scratch for a full LSD sort of `count` pairs.
+struct RadixWs {
+    uint32_t* hist;      // [256 * T]
+    uint32_t* scanned;   // [256 * T + 1]
+    int32_t* key[2];     // [count] each, ping-pong
+    int32_t* val[2];
+    void* scan_ws;
+};
+
+inline RadixWs radix_carve(Carver& c, int64_t count) {
+    RadixWs w{};
+    const int64_t T = radix_tiles(count);
+    w.hist = c.take<uint32_t>((size_t)(kRadixDigits * T));
+    w.scanned = c.take<uint32_t>((size_t)(kRadixDigits * T + 1));
+    for (int i = 0; i < 2; ++i) {
+        w.key[i] = c.take<int32_t>((size_t)count);
+        w.val[i] = c.take<int32_t>((size_t)count);
+    }
+    // big enough for the histogram scan and for a scan over `count` items
+    const int64_t scan_n = kRadixDigits * T > count ? kRadixDigits * T : count;
+    w.scan_ws = c.base ? c.base + c.used : nullptr;
+    c.used += align_up(scan_workspace_bytes(scan_n));
+    return w;
+}
+
+// Stable LSD sort of `count` pairs by the low `bits` bits of the key (at
+// least one pass).  Pass 0 reads its pairs per MODE; later passes read the
+// previous pass's output.  The sorted values end in vals_out; the sorted keys
+// are left in *keys_sorted (one of the scratch buffers).
+template <int MODE>
+int radix_sort(RadixIn in, int bits, int32_t* vals_out, const RadixWs& w, int32_t** keys_sorted,
+               hipStream_t stream) {
+    const int64_t T = radix_tiles(in.count);
+    int passes = (bits + kRadixBits - 1) / kRadixBits;
+    if (passes < 1) passes = 1;
+    for (int p = 0; p < passes; ++p) {
+        const int shift = p * kRadixBits;
+        const bool last = p == passes - 1;
+        int32_t* kout = w.key[p & 1];
+        int32_t* vout = last ? vals_out : w.val[p & 1];
+        if (p == 0)
+            k_radix_hist<MODE><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, shift, T, w.hist);
+        else
+            k_radix_hist<kFromPairs><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, shift, T, w.hist);
+        PR_LAUNCHED("radix histogram");
+        PR_TRY(scan_exclusive(w.hist, w.scanned, kRadixDigits * T, w.scan_ws, stream));
+        if (p == 0)
+            k_radix_scatter<MODE><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, shift, T, w.scanned,
+                                                                             kout, vout);
+        else
+            k_radix_scatter<kFromPairs><<<dim3((unsigned)T), kBlock, 0, stream>>>(
+                in, shift, T, w.scanned, kout, vout);
+        PR_LAUNCHED("radix scatter");
+        in.keys = kout;
+        in.vals = vout;
+        *keys_sorted = kout;
+    }
+    return PR_OK;
+}
 
 }  // namespace pr

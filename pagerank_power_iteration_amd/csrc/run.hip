@@ -5,21 +5,27 @@
 // with contrib[u] = x[u]/outdeg[u] and D the dangling mass of x.
 //
 // The page runs five launches per iteration (scale, SpMV, two reduction
-// passes, combine).  Here one launch does all of it:
-//   * every workgroup gathers contrib over the in-rows of its degree bucket
-//     (lane, 4-lane, 16-lane, wavefront or workgroup per row);
-//   * the same lanes apply the combine to their rows, write x'[v] and the
-//     next iteration's contrib'[v] = x'[v] * inv_out[v], and accumulate
-//     |x'[v] - x[v]|, the dangling part of x' and the sum of x';
-//   * each workgroup writes those three partials once; the last workgroup to
-//     arrive reduces them (in double), appends the L1 distance to the trace,
-//     stores D' for the next launch and raises the stop flag when L1 < tol.
-// D therefore never leaves the device (the page's "Keep the dangling mass on
-// the device"), and the write budget of the reductions is one slot per
-// workgroup plus one (the page's gridDim.x + 1 rule).
+// passes, combine).  Here there are two:
+//   * k_iterate, a persistent grid that takes work items from a queue: it
+//     gathers contrib over the in-rows of each item's degree bucket (lane,
+//     4-lane, 16-lane, wavefront or workgroup per row), and the lanes that
+//     hold a row's sum apply the update on the spot: x'[v], the next
+//     iteration's contrib'[v] = x'[v] * inv_out[v], and the three running
+//     sums |x'[v] - x[v]|, the dangling part of x' and x'.  Each workgroup
+//     writes its three sums once (the page's "gridDim.x + 1" write budget);
+//   * k_finalize, one workgroup: it finishes the hub rows that were split in
+//     chunks, reduces the per-workgroup sums (in double), appends the L1
+//     distance to the trace, stores D' for the next iteration and raises the
+//     stop flag once L1 < tol.
+// D never leaves the device (the page's "Keep the dangling mass on the
+// device").  No kernel publishes data to another workgroup of the same
+// launch, so no launch needs a device-wide fence; the kernel boundary orders
+// k_iterate's stores before k_finalize's loads.
 //
-// contrib is double-buffered across iterations (rows read other rows'
-// contrib); x is updated in place (only row v's owner touches x[v]).
+// Every vector is kept in the plan's vertex order; pr_run maps the caller's
+// x in (k_init) and out (k_finish).  contrib is double-buffered across
+// iterations (rows read other rows' contrib); x is updated in place (only row
+// v's owner touches x[v]).
 #include "plan.hpp"
 
 namespace pr {
@@ -29,219 +35,275 @@ namespace {
 struct IterArgs {
     const int32_t* __restrict__ in_rp;
     const int32_t* __restrict__ in_ci;
-    const int32_t* __restrict__ rows;
     const float* __restrict__ inv_out;
     const float* __restrict__ contrib_in;
     float* __restrict__ contrib_out;
-    float* __restrict__ x;
-    float* __restrict__ partials;
+    float* __restrict__ xi;
+    const WorkItem* __restrict__ items;
+    float* __restrict__ hub_part;
+    float* __restrict__ wg_part;
     RunState* state;
-    float* __restrict__ l1_trace;
-    float* __restrict__ sum_trace;
     double d;
-    double tol;
-    int64_t nnz;
     int32_t n;
-    int32_t t;  // 1-based iteration number
-    int32_t partial_stride;
-    BucketLaunch launch[kNumBuckets];
+    int32_t n_items;
 };
 
 struct Acc {
     float l1 = 0.f, dang = 0.f, sum = 0.f;
 };
 
-// Clamp a row's edge range to [0, nnz] so a malformed in_row_ptr cannot
-// index outside in_col_idx.
-__device__ __forceinline__ void row_range(const IterArgs& a, int32_t v, int32_t& s, int32_t& e) {
-    int32_t lo = a.in_rp[v], hi = a.in_rp[v + 1];
-    const int32_t m = (int32_t)a.nnz;
-    lo = lo < 0 ? 0 : (lo > m ? m : lo);
-    hi = hi < lo ? lo : (hi > m ? m : hi);
-    s = lo;
-    e = hi;
-}
-
-// Gather of one source's contribution.  The index is clamped to [0, n) so a
-// malformed in_col_idx cannot read outside contrib.  col_idx is streamed once
-// per iteration, so it is loaded non-temporally to keep L2 for contrib.
-__device__ __forceinline__ float gather(const IterArgs& a, int32_t k) {
-    uint32_t u = (uint32_t)__builtin_nontemporal_load(a.in_ci + k);
-    const uint32_t last = (uint32_t)(a.n - 1);
-    u = u < last ? u : last;
-    return a.contrib_in[u];
-}
-
-// Sum of contrib over edges [s, e) taken by lane `gl` of a G-lane group:
-// edges s+gl, s+gl+G, ...  Four independent accumulators keep four gathers
-// in flight per lane.
-template <int G>
-__device__ __forceinline__ float strided_sum(const IterArgs& a, int32_t s, int32_t e, int gl) {
-    float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
-    int32_t k = s + gl;
-    for (; k + 3 * G < e; k += 4 * G) {
-        y0 += gather(a, k);
-        y1 += gather(a, k + G);
-        y2 += gather(a, k + 2 * G);
-        y3 += gather(a, k + 3 * G);
-    }
-    for (; k < e; k += G) y0 += gather(a, k);
-    return (y0 + y1) + (y2 + y3);
-}
-
 // Damping factor as an unevaluated float pair hi + lo (hi = d rounded to
 // float): d*y = hi*y + lo*y keeps the product at the double d to ~1e-15, so
 // the rank sum does not drift by (float(d) - d)/(1 - d) ~ 1.6e-7.
 struct Damp {
-    float hi, lo;
+    float hi, lo, base;
 };
 
-// x'[v] from the gathered sum, and the per-lane partials.
-__device__ __forceinline__ void combine(const IterArgs& a, int32_t v, float y, float base,
-                                        Damp dmp, Acc& acc) {
-    const float xo = a.x[v];
-    const float xn = fmaf(dmp.lo, y, fmaf(dmp.hi, y, base));
-    a.x[v] = xn;
-    const float io = a.inv_out[v];
-    a.contrib_out[v] = xn * io;
+__device__ __forceinline__ Damp make_damp(double d, int32_t n, double dmass) {
+    Damp k;
+    k.hi = (float)d;
+    k.lo = (float)(d - (double)k.hi);
+    k.base = (float)((1.0 - d) / (double)n + d * dmass / (double)n);
+    return k;
+}
+
+// x'[p] from the gathered sum y, and the lane's running sums.  contrib' is
+// written for every row (0 for a dangling one, whose slot is never read) so
+// the stores cover whole lines.
+__device__ __forceinline__ void update(float* __restrict__ xi, const float* __restrict__ inv_out,
+                                       float* __restrict__ contrib_out, int32_t p, float y,
+                                       const Damp& k, Acc& acc) {
+    const float xo = xi[p];
+    const float xn = fmaf(k.lo, y, fmaf(k.hi, y, k.base));
+    xi[p] = xn;
+    const float io = inv_out[p];
+    contrib_out[p] = xn * io;
     acc.l1 += fabsf(xn - xo);
     acc.dang += (io == 0.f) ? xn : 0.f;
     acc.sum += xn;
 }
 
-template <int G>
-__device__ __forceinline__ void run_bucket(const IterArgs& a, const BucketLaunch& L, int lblk,
-                                           float base, Damp dmp, Acc& acc) {
+// Sum of contrib over the edges [s, e) that lane `gl` of a G-lane group
+// takes: s+gl, s+gl+G, ...  U independent loads per step keep U gathers in
+// flight per lane.  col_idx is streamed once per iteration, so it is loaded
+// non-temporally to leave the caches to contrib.  The plan built every index
+// (in_ci holds plan ids in [0, n)), so none is re-checked here.
+template <int G, int U>
+__device__ __forceinline__ float gather_sum(const IterArgs& a, int32_t s, int32_t e, int gl) {
+    float acc[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) acc[j] = 0.f;
+    for (int32_t k = s + gl; k < e; k += U * G) {
+        int32_t u[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+            u[j] = (k + j * G < e) ? __builtin_nontemporal_load(a.in_ci + k + j * G) : -1;
+#pragma unroll
+        for (int j = 0; j < U; ++j) acc[j] += (u[j] >= 0) ? a.contrib_in[u[j]] : 0.f;
+    }
+#pragma unroll
+    for (int w = 1; w < U; w <<= 1)
+#pragma unroll
+        for (int j = 0; j + w < U; j += 2 * w) acc[j] += acc[j + w];
+    return acc[0];
+}
+
+// Rows [lo, hi) of a bucket with G lanes per row (G <= 64): group g of the
+// workgroup takes rows lo+g, lo+g+256/G, ...
+template <int G, int U>
+__device__ __forceinline__ void run_rows(const IterArgs& a, int32_t lo, int32_t hi, const Damp& k,
+                                         Acc& acc) {
     constexpr int kGroups = kBlock / G;
     const int gid = threadIdx.x / G, gl = threadIdx.x % G;
-    for (int64_t i = L.row_begin + (int64_t)lblk * kGroups + gid; i < L.row_end;
-         i += (int64_t)L.blocks * kGroups) {
-        const int32_t v = a.rows[i];
-        int32_t s, e;
-        row_range(a, v, s, e);
-        float y = strided_sum<G>(a, s, e, gl);
+    for (int32_t p = lo + gid; p < hi; p += kGroups) {
+        const int32_t s = a.in_rp[p], e = a.in_rp[p + 1];
+        float y = gather_sum<G, U>(a, s, e, gl);
         y = group_sum<G>(y);
-        if (gl == 0) combine(a, v, y, base, dmp, acc);
+        if (gl == 0) update(a.xi, a.inv_out, a.contrib_out, p, y, k, acc);
     }
 }
 
-// Hub rows: the whole workgroup on one row.
-__device__ __forceinline__ void run_hubs(const IterArgs& a, const BucketLaunch& L, int lblk,
-                                         float base, Damp dmp, Acc& acc, float* red) {
-    for (int64_t i = L.row_begin + lblk; i < L.row_end; i += L.blocks) {
-        const int32_t v = a.rows[i];
-        int32_t s, e;
-        row_range(a, v, s, e);
-        float y = strided_sum<kBlock>(a, s, e, threadIdx.x);
-        y = block_sum(y, red);
-        if (threadIdx.x == 0) combine(a, v, y, base, dmp, acc);
-    }
+// Sum over the whole workgroup of edges [s, e) (a hub row or a chunk of one).
+__device__ __forceinline__ float hub_sum(const IterArgs& a, int32_t s, int32_t e, float* red) {
+    return block_sum(gather_sum<kBlock, 8>(a, s, e, threadIdx.x), red);
 }
 
-// Write this workgroup's three partials, and if it is the last to arrive,
-// reduce all of them.  Returns true in every lane of the last workgroup,
-// with the totals in *tot.
-__device__ __forceinline__ bool arrive_and_reduce(float* __restrict__ partials, int stride,
-                                                  RunState* st, Acc acc, double tot[3]) {
-    __shared__ float redf[kWaves];
-    __shared__ double redd[kWaves];
-    __shared__ int s_last;
-    const float l1 = block_sum(acc.l1, redf);
-    const float dg = block_sum(acc.dang, redf);
-    const float sm = block_sum(acc.sum, redf);
-    if (threadIdx.x == 0) {
-        __hip_atomic_store(&partials[blockIdx.x], l1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&partials[stride + blockIdx.x], dg, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&partials[2 * stride + blockIdx.x], sm, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t prev =
-            __hip_atomic_fetch_add(&st->arrive, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == gridDim.x - 1) ? 1 : 0;
+// The next item for this workgroup: thread 0 increments queue heads, starting
+// with queue *q, until one yields an item below n_items; -1 when every queue
+// is empty.
+__device__ __forceinline__ int32_t next_item(RunState* st, int& q, int& tries, int32_t n_items,
+                                             uint32_t ticket) {
+    int32_t it = q + kQueues * (int32_t)ticket;
+    while (it >= n_items && ++tries < kQueues) {
+        q = (q + 1) % kQueues;
+        it = q + kQueues * (int32_t)atomicAdd(&st->queue[q][0], 1u);
     }
-    __syncthreads();
-    if (!s_last) return false;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    double r0 = 0.0, r1 = 0.0, r2 = 0.0;
-    for (int j = threadIdx.x; j < (int)gridDim.x; j += kBlock) {
-        r0 += (double)__hip_atomic_load(&partials[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        r1 += (double)__hip_atomic_load(&partials[stride + j], __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-        r2 += (double)__hip_atomic_load(&partials[2 * stride + j], __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    }
-    tot[0] = block_sum(r0, redd);
-    tot[1] = block_sum(r1, redd);
-    tot[2] = block_sum(r2, redd);
-    return true;
+    return it < n_items ? it : -1;
 }
 
 __global__ __launch_bounds__(kBlock) void k_iterate(IterArgs a) {
     __shared__ float red[kWaves];
+    __shared__ int32_t s_item;
     RunState* st = a.state;
     if (st->stop) return;  // an earlier iteration met the tolerance
-    const double D = st->dmass;
-    const float base = (float)((1.0 - a.d) / (double)a.n + a.d * D / (double)a.n);
-    Damp dmp;
-    dmp.hi = (float)a.d;
-    dmp.lo = (float)(a.d - (double)dmp.hi);
+    const Damp k = make_damp(a.d, a.n, st->dmass);
 
+    int q = blockIdx.x % kQueues, tries = 0;  // used by thread 0 only
+    if (threadIdx.x == 0) s_item = next_item(st, q, tries, a.n_items, atomicAdd(&st->queue[q][0], 1u));
+    __syncthreads();
+    int32_t cur = s_item;
     Acc acc;
-    const int blk = blockIdx.x;
-    if (blk < a.launch[4].block_begin + a.launch[4].blocks)
-        run_hubs(a, a.launch[4], blk - a.launch[4].block_begin, base, dmp, acc, red);
-    else if (blk < a.launch[3].block_begin + a.launch[3].blocks)
-        run_bucket<64>(a, a.launch[3], blk - a.launch[3].block_begin, base, dmp, acc);
-    else if (blk < a.launch[2].block_begin + a.launch[2].blocks)
-        run_bucket<16>(a, a.launch[2], blk - a.launch[2].block_begin, base, dmp, acc);
-    else if (blk < a.launch[1].block_begin + a.launch[1].blocks)
-        run_bucket<4>(a, a.launch[1], blk - a.launch[1].block_begin, base, dmp, acc);
-    else
-        run_bucket<1>(a, a.launch[0], blk - a.launch[0].block_begin, base, dmp, acc);
-
-    double tot[3];
-    if (!arrive_and_reduce(a.partials, a.partial_stride, st, acc, tot)) return;
-    if (threadIdx.x == 0) {
-        const int t = a.t;
-        a.l1_trace[t - 1] = (float)tot[0];
-        if (a.sum_trace) a.sum_trace[t - 1] = (float)tot[2];
-        st->dmass = tot[1];
-        if (a.tol > 0.0 && tot[0] < a.tol) {
-            st->stop = 1;
-            st->iters = t;
+    while (cur >= 0) {
+        // ask for the next item now; its answer is needed only after this one
+        uint32_t ticket = 0;
+        if (threadIdx.x == 0 && tries < kQueues) ticket = atomicAdd(&st->queue[q][0], 1u);
+        const WorkItem it = a.items[cur];
+        switch (it.kind) {
+            case 0: run_rows<1, 4>(a, it.lo, it.hi, k, acc); break;
+            case 1: run_rows<4, 4>(a, it.lo, it.hi, k, acc); break;
+            case 2: run_rows<16, 4>(a, it.lo, it.hi, k, acc); break;
+            case 3: run_rows<64, 4>(a, it.lo, it.hi, k, acc); break;
+            case kHubBucket: {
+                const float y = hub_sum(a, it.lo, it.hi, red);
+                if (threadIdx.x == 0) update(a.xi, a.inv_out, a.contrib_out, it.aux, y, k, acc);
+                break;
+            }
+            default: {  // kKindChunk
+                const float y = hub_sum(a, it.lo, it.hi, red);
+                if (threadIdx.x == 0) a.hub_part[it.aux] = y;
+                break;
+            }
         }
-        st->arrive = 0u;
+        __syncthreads();  // every lane has read s_item and finished with `red`
+        if (threadIdx.x == 0)
+            s_item = tries < kQueues ? next_item(st, q, tries, a.n_items, ticket) : -1;
+        __syncthreads();
+        cur = s_item;
+    }
+    const float l1 = block_sum(acc.l1, red);
+    const float dg = block_sum(acc.dang, red);
+    const float sm = block_sum(acc.sum, red);
+    if (threadIdx.x == 0) {
+        a.wg_part[blockIdx.x] = l1;
+        a.wg_part[kMaxGrid + blockIdx.x] = dg;
+        a.wg_part[2 * kMaxGrid + blockIdx.x] = sm;
     }
 }
 
-// Start vector (given, or 1/n), the first contrib, and its dangling mass.
-__global__ __launch_bounds__(kBlock) void k_init(const float* __restrict__ inv_out,
-                                                 float* __restrict__ x,
+constexpr int kFinalWaves = kFinalBlock / kWave;
+
+template <class T>
+__device__ __forceinline__ T final_block_sum(T v, T* scratch) {
+    v = wave_sum(v);
+    if (lane_id() == 0) scratch[threadIdx.x / kWave] = v;
+    __syncthreads();
+    T r = scratch[0];
+#pragma unroll
+    for (int w = 1; w < kFinalWaves; ++w) r += scratch[w];
+    __syncthreads();
+    return r;
+}
+
+struct FinArgs {
+    const float* __restrict__ inv_out;
+    float* __restrict__ contrib_out;
+    float* __restrict__ xi;
+    const ChunkRow* __restrict__ chunk_rows;
+    const float* __restrict__ hub_part;
+    const float* __restrict__ wg_part;
+    RunState* state;
+    float* __restrict__ l1_trace;
+    float* __restrict__ sum_trace;
+    double d;
+    double tol;
+    int32_t n;
+    int32_t n_chunk_rows;
+    int32_t parts;  // per-workgroup sums to reduce
+    int32_t t;      // iteration number; 0 after k_init
+};
+
+// One workgroup of kFinalBlock lanes.  After iteration t: finish the chunked
+// hub rows, reduce every sum, record the trace and the next D, test the
+// tolerance, and reset the work queues.  After k_init (t = 0): only D.
+__global__ __launch_bounds__(kFinalBlock) void k_finalize(FinArgs f) {
+    __shared__ double redd[kFinalWaves];
+    RunState* st = f.state;
+    if (f.t > 0 && st->stop) return;
+    Acc acc;
+    if (f.t > 0 && f.n_chunk_rows > 0) {
+        const Damp k = make_damp(f.d, f.n, st->dmass);
+        const int wave = threadIdx.x / kWave, lane = lane_id();
+        for (int32_t r = wave; r < f.n_chunk_rows; r += kFinalWaves) {
+            const ChunkRow cr = f.chunk_rows[r];
+            float y = 0.f;
+            for (int32_t j = lane; j < cr.count; j += kWave) y += f.hub_part[cr.first + j];
+            y = wave_sum(y);
+            if (lane == 0) update(f.xi, f.inv_out, f.contrib_out, cr.row, y, k, acc);
+        }
+    }
+    double r0 = acc.l1, r1 = acc.dang, r2 = acc.sum;
+    for (int j = threadIdx.x; j < f.parts; j += kFinalBlock) {
+        r0 += (double)f.wg_part[j];
+        r1 += (double)f.wg_part[kMaxGrid + j];
+        r2 += (double)f.wg_part[2 * kMaxGrid + j];
+    }
+    r0 = final_block_sum(r0, redd);
+    r1 = final_block_sum(r1, redd);
+    r2 = final_block_sum(r2, redd);
+    if (threadIdx.x < kQueues) st->queue[threadIdx.x][0] = 0u;
+    if (threadIdx.x == 0) {
+        st->dmass = r1;
+        if (f.t == 0) {
+            st->stop = 0;
+            st->iters = 0;
+        } else {
+            f.l1_trace[f.t - 1] = (float)r0;
+            if (f.sum_trace) f.sum_trace[f.t - 1] = (float)r2;
+            if (f.tol > 0.0 && r0 < f.tol) {
+                st->stop = 1;
+                st->iters = f.t;
+            }
+        }
+    }
+}
+
+// Start vector in plan order (the caller's x0, or 1/n), the first contrib,
+// and per-workgroup dangling mass and sum.
+__global__ __launch_bounds__(kBlock) void k_init(const int32_t* __restrict__ new_id,
+                                                 const float* __restrict__ inv_out,
+                                                 const float* __restrict__ x,
+                                                 float* __restrict__ xi,
                                                  float* __restrict__ contrib, int32_t n,
-                                                 int x0_given, float* __restrict__ partials,
-                                                 int stride, RunState* st) {
+                                                 int x0_given, float* __restrict__ wg_part) {
+    __shared__ float red[kWaves];
     const float uniform = (float)(1.0 / (double)n);
     Acc acc;
     for (int64_t v = blockIdx.x * (int64_t)kBlock + threadIdx.x; v < n;
          v += (int64_t)gridDim.x * kBlock) {
-        float xv = uniform;
-        if (x0_given)
-            xv = x[v];
-        else
-            x[v] = xv;
-        const float io = inv_out[v];
-        contrib[v] = xv * io;
+        const float xv = x0_given ? x[v] : uniform;
+        const int32_t p = new_id[v];
+        xi[p] = xv;
+        const float io = inv_out[p];
+        contrib[p] = xv * io;
         acc.dang += (io == 0.f) ? xv : 0.f;
         acc.sum += xv;
     }
-    double tot[3];
-    if (!arrive_and_reduce(partials, stride, st, acc, tot)) return;
+    const float dg = block_sum(acc.dang, red);
+    const float sm = block_sum(acc.sum, red);
     if (threadIdx.x == 0) {
-        st->dmass = tot[1];
-        st->stop = 0;
-        st->iters = 0;
-        st->arrive = 0u;
+        wg_part[blockIdx.x] = 0.f;
+        wg_part[kMaxGrid + blockIdx.x] = dg;
+        wg_part[2 * kMaxGrid + blockIdx.x] = sm;
     }
+}
+
+// The ranks back in the caller's order.
+__global__ __launch_bounds__(kBlock) void k_finish(const int32_t* __restrict__ new_id,
+                                                   const float* __restrict__ xi,
+                                                   float* __restrict__ x, int32_t n) {
+    for (int64_t v = blockIdx.x * (int64_t)kBlock + threadIdx.x; v < n;
+         v += (int64_t)gridDim.x * kBlock)
+        x[v] = xi[new_id[v]];
 }
 
 int chunk_size(const pr_plan* p) {
@@ -252,6 +314,14 @@ int chunk_size(const pr_plan* p) {
 }
 
 }  // namespace
+
+int iterate_blocks_per_cu() {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_iterate, kBlock, 0) != hipSuccess ||
+        blocks < 1)
+        blocks = 1;
+    return blocks;
+}
 
 }  // namespace pr
 
@@ -271,47 +341,71 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         return fail(PR_ERR_ARG, "plan belongs to device %d but device %d is current", p->device, dev);
     hipStream_t stream = as_stream(stream_v);
 
-    k_init<<<dim3((unsigned)p->init_blocks), kBlock, 0, stream>>>(
-        p->inv_out, x, p->contrib[0], p->n, (flags & PR_X0_GIVEN) ? 1 : 0, p->partials,
-        kMaxPartials, p->state);
+    k_init<<<dim3((unsigned)p->init_grid), kBlock, 0, stream>>>(
+        p->new_id, p->inv_out, x, p->xi, p->contrib[0], p->n, (flags & PR_X0_GIVEN) ? 1 : 0,
+        p->wg_part);
     PR_LAUNCHED("init");
+
+    FinArgs f{};
+    f.inv_out = p->inv_out;
+    f.xi = p->xi;
+    f.chunk_rows = p->chunk_rows;
+    f.hub_part = p->hub_part;
+    f.wg_part = p->wg_part;
+    f.state = p->state;
+    f.l1_trace = l1_trace;
+    f.sum_trace = sum_trace;
+    f.d = d;
+    f.tol = tol;
+    f.n = p->n;
+    f.n_chunk_rows = p->n_chunk_rows;
+    f.parts = p->init_grid;
+    f.t = 0;
+    k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
+    PR_LAUNCHED("init finalize");
+    f.parts = p->grid;
 
     IterArgs a{};
     a.in_rp = p->in_rp;
     a.in_ci = p->in_ci;
-    a.rows = p->rows;
     a.inv_out = p->inv_out;
-    a.x = x;
-    a.partials = p->partials;
+    a.xi = p->xi;
+    a.items = p->items;
+    a.hub_part = p->hub_part;
+    a.wg_part = p->wg_part;
     a.state = p->state;
-    a.l1_trace = l1_trace;
-    a.sum_trace = sum_trace;
     a.d = d;
-    a.tol = tol;
-    a.nnz = p->nnz;
     a.n = p->n;
-    a.partial_stride = kMaxPartials;
-    for (int b = 0; b < kNumBuckets; ++b) a.launch[b] = p->launch[b];
+    a.n_items = p->n_items;
 
     const bool record = flags & PR_RECORD_EVENTS;
     p->events_recorded = false;
     if (record) PR_HIP_TRY(hipEventRecord(p->ev_begin, stream));
 
     auto launch = [&](int32_t t) -> int {
-        a.t = t;
         a.contrib_in = p->contrib[(t - 1) & 1];
         a.contrib_out = p->contrib[t & 1];
-        k_iterate<<<dim3((unsigned)p->iter_blocks), kBlock, 0, stream>>>(a);
+        k_iterate<<<dim3((unsigned)p->grid), kBlock, 0, stream>>>(a);
         PR_LAUNCHED("iterate");
+        f.contrib_out = a.contrib_out;
+        f.t = t;
+        k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
+        PR_LAUNCHED("finalize");
+        return PR_OK;
+    };
+    auto finish = [&]() -> int {
+        if (record) {
+            PR_HIP_TRY(hipEventRecord(p->ev_end, stream));
+            p->events_recorded = true;
+        }
+        k_finish<<<dim3((unsigned)p->init_grid), kBlock, 0, stream>>>(p->new_id, p->xi, x, p->n);
+        PR_LAUNCHED("finish");
         return PR_OK;
     };
 
     if (tol <= 0.0) {
         for (int32_t t = 1; t <= max_iter; ++t) PR_TRY(launch(t));
-        if (record) {
-            PR_HIP_TRY(hipEventRecord(p->ev_end, stream));
-            p->events_recorded = true;
-        }
+        PR_TRY(finish());
         *iterations = max_iter;
         return PR_OK;
     }
@@ -336,10 +430,7 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         slot ^= 1;
         t = t_end + 1;
     }
-    if (record) {
-        PR_HIP_TRY(hipEventRecord(p->ev_end, stream));
-        p->events_recorded = true;
-    }
+    PR_TRY(finish());
     PR_HIP_TRY(hipStreamSynchronize(stream));
     const RunStatus& last = p->host_status[slot ^ 1];  // copied after every launched iteration
     *iterations = last.stop ? last.iters : max_iter;

@@ -1,0 +1,26 @@
+// Device transpose shared by pr_transpose and the plan builder.
+#pragma once
+
+#include "radix.hpp"
+
+namespace pr {
+
+struct TransposeWs {
+    RadixWs sort;
+    uint32_t* error;  // [1]
+    size_t bytes;
+};
+
+TransposeWs transpose_carve(void* base, int32_t n, int64_t nnz);
+
+// In-edge CSR of the out-edge CSR (n, nnz, out_rp, out_ci): a stable LSD
+// sort of (target, source) pairs by target; in_rp from the row boundaries of
+// the sorted targets.  Asynchronous on `stream`.  Out-of-range columns are
+// clamped and flagged in ws.error.
+int transpose_device(int32_t n, int64_t nnz, const int32_t* out_rp, const int32_t* out_ci,
+                     int32_t* in_rp, int32_t* in_ci, const TransposeWs& ws, hipStream_t stream);
+
+// Bits needed to hold every vertex id in [0, n).
+int vertex_bits(int32_t n);
+
+}  // namespace pr

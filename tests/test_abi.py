@@ -27,8 +27,9 @@ def test_workspace_queries():
     assert 0 < small < big
     # ping-pong key/value pairs for three 8-bit passes dominate: 16 bytes per edge
     assert big >= 16 * 268_435_456
-    assert prx.pr_plan_workspace_bytes(1 << 23, 268_435_456) >= 16 * (1 << 23)
-    assert prx.pr_plan_workspace_bytes(1, 0) > 0
+    assert prx.pr_plan_workspace_bytes(1 << 23, 268_435_456) >= 4 * 268_435_456 + 24 * (1 << 23)
+    assert prx.pr_plan_scratch_bytes(1 << 23, 268_435_456) >= 20 * 268_435_456
+    assert prx.pr_plan_workspace_bytes(1, 0) > 0 and prx.pr_plan_scratch_bytes(1, 0) > 0
 
 
 def test_status_strings():
@@ -48,10 +49,16 @@ def test_arguments_rejected_before_device_work():
     assert so.pr_transpose(5, 3, 256, 256, 256, 256, 256, 8, 0, None) == prx.PR_ERR_WORKSPACE
     assert so.pr_transpose(5, 3, 256, 256, 256, 256, 260, 1 << 30, 0, None) == prx.PR_ERR_WORKSPACE
     h = ctypes.c_void_p()
-    assert so.pr_plan_create(None, 5, 3, 1, 1, 1, 1, 0, 0, None) == prx.PR_ERR_ARG
-    assert so.pr_plan_create(ctypes.byref(h), 0, 3, 1, 1, 1, 1, 0, 0, None) == prx.PR_ERR_ARG
-    assert so.pr_plan_create(ctypes.byref(h), 5, 3, 256, 256, 256, 256, 4, 0, None) == \
+    assert so.pr_plan_create(None, 5, 3, 1, 1, 1, 1 << 20, 1, 1 << 20, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_plan_create(ctypes.byref(h), 0, 3, 1, 1, 1, 1 << 20, 1, 1 << 20, 0, None) == \
+        prx.PR_ERR_ARG
+    assert so.pr_plan_create(ctypes.byref(h), 5, 3, 256, 256, 256, 1 << 20, 256, 1 << 20, 0x80,
+                             None) == prx.PR_ERR_ARG
+    assert so.pr_plan_create(ctypes.byref(h), 5, 3, 256, 256, 256, 4, 256, 1 << 20, 0, None) == \
         prx.PR_ERR_WORKSPACE
+    assert so.pr_plan_create(ctypes.byref(h), 5, 3, 256, 256, 256, 1 << 20, 256, 4, 0, None) == \
+        prx.PR_ERR_WORKSPACE
+    assert so.pr_plan_layout(None, None, None, None) == prx.PR_ERR_ARG
     it = ctypes.c_int32()
     assert so.pr_run(None, 0.85, 0.0, 10, 1, 1, None, ctypes.byref(it), 0, None) == prx.PR_ERR_ARG
     assert so.pr_plan_destroy(None) == prx.PR_OK

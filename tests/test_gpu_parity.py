@@ -65,7 +65,55 @@ def test_transpose_four_radix_passes(prx):
     np.testing.assert_array_equal(_cases.to_np(in_ci), ref_ci)
 
 
-# ----------------------------------------------------------------- iteration
+# ---------------------------------------------------------------- plan layout
+
+def _expected_plan_order(g, min_len):
+    """Plan ids from their definition: hub bucket first, then decreasing
+    in-degree bucket, then decreasing out-degree saturated at 65535, ties by
+    increasing id."""
+    indeg = np.bincount(g.col_idx, minlength=g.n)
+    bucket = np.searchsorted(np.asarray(min_len), indeg, side="right") - 1
+    outdeg = np.minimum(g.out_degree(), 65535)
+    order = np.lexsort((np.arange(g.n), -outdeg, -bucket))
+    new_id = np.empty(g.n, dtype=np.int64)
+    new_id[order] = np.arange(g.n)
+    return order, new_id
+
+
+def _renumbered(g, new_id):
+    """Out-edge CSR with every vertex v renamed new_id[v]; rows keep the order
+    of their targets."""
+    src = np.repeat(np.arange(g.n), g.out_degree())
+    perm = np.argsort(new_id[src], kind="stable")
+    rp = np.zeros(g.n + 1, dtype=np.int64)
+    np.cumsum(np.bincount(new_id[src], minlength=g.n), out=rp[1:])
+    return rp.astype(np.int32), new_id[g.col_idx[perm]].astype(np.int32)
+
+
+@pytest.mark.parametrize("g", SMALL, ids=lambda g: g.name)
+def test_plan_layout(prx, g):
+    """The plan renumbers vertices as documented and holds the oracle's
+    transpose of the renumbered graph, bit for bit; every bucket is one
+    contiguous range of plan ids."""
+    dg = _cases.gpu_graph(g)
+    plan = prx.Plan(dg, flags=prx.PR_VALIDATE)
+    rp, ci, nid = (_cases.to_np(t) for t in plan.layout())
+    buckets = plan.buckets()
+    order, new_id = _expected_plan_order(g, [b["min_len"] for b in buckets])
+    np.testing.assert_array_equal(nid, new_id)
+    ref_rp, ref_ci = oracle.transpose(*_renumbered(g, new_id))
+    np.testing.assert_array_equal(rp, ref_rp)
+    np.testing.assert_array_equal(ci, ref_ci)
+    # bucket ranges: hub bucket at the lowest ids, then 3, 2, 1, 0
+    lens = np.diff(rp)
+    start = 0
+    for b in reversed(range(len(buckets))):
+        hi = buckets[b + 1]["min_len"] if b + 1 < len(buckets) else np.iinfo(np.int64).max
+        sel = lens[start:start + buckets[b]["rows"]]
+        assert np.all((sel >= buckets[b]["min_len"]) & (sel < hi))
+        start += buckets[b]["rows"]
+    assert start == g.n
+
 
 @pytest.mark.parametrize("g", SMALL, ids=lambda g: g.name)
 def test_pagerank_parity_small(prx, g):
@@ -79,6 +127,34 @@ def test_pagerank_parity_small(prx, g):
     _cases.assert_parity(_cases.to_np(res.x), _cases.to_np(res.l1_trace),
                          _cases.to_np(res.sum_trace), ref, tie_rel=tie)
     assert res.iterations == 100
+
+
+def _hubs_graph(n_leaves: int, n_hubs: int, seed: int):
+    """Every leaf links to every hub (hub in-degree n_leaves, above the
+    65,536-edge chunk), plus a seeded random graph on the leaves so that
+    leaves carry rank too; the hubs are dangling."""
+    n = n_leaves + n_hubs
+    leaves = np.arange(n_leaves, dtype=np.int64)
+    src = [np.repeat(leaves, n_hubs)]
+    dst = [np.tile(np.arange(n_leaves, n, dtype=np.int64), n_leaves)]
+    k = np.arange(2 * 4 * n_leaves, dtype=np.uint64)
+    r = (graphgen.splitmix_u64(seed, k) % np.uint64(n_leaves)).astype(np.int64)
+    src.append(r[: 4 * n_leaves])
+    dst.append(r[4 * n_leaves:])
+    return graphgen.from_edges(n, np.concatenate(src), np.concatenate(dst))
+
+
+@pytest.mark.parametrize("n_leaves,n_hubs", [(70_000, 1), (140_001, 3)])
+def test_chunked_hub_rows(prx, n_leaves, n_hubs):
+    """Hub rows longer than one work chunk are summed in pieces and finished
+    by the reduction kernel; they must match the oracle like any other row."""
+    g = _hubs_graph(n_leaves, n_hubs, seed=n_leaves)
+    plan = prx.Plan(_cases.gpu_graph(g), flags=prx.PR_VALIDATE)
+    res = plan.run(d=D, tol=0.0, max_iter=40)
+    torch.cuda.synchronize()
+    ref = oracle.pagerank(g.row_ptr, g.col_idx, d=D, max_iter=40)
+    _cases.assert_parity(_cases.to_np(res.x), _cases.to_np(res.l1_trace),
+                         _cases.to_np(res.sum_trace), ref, tie_rel=2e-6)
 
 
 @pytest.mark.parametrize("d", [0.0, 0.5, 0.99, 1.0])
@@ -207,7 +283,8 @@ def test_workload_parity(prx, name, iters):
     ref_rp, ref_ci = oracle.transpose(g.row_ptr, g.col_idx)
     assert np.array_equal(_cases.to_np(in_rp), ref_rp)
     assert np.array_equal(_cases.to_np(in_ci), ref_ci)
-    plan = prx.Plan(dg, in_csr=(in_rp, in_ci))
+    del in_rp, in_ci
+    plan = prx.Plan(dg)
     res = plan.run(d=D, max_iter=iters)
     torch.cuda.synchronize()
     ref = oracle.pagerank(g.row_ptr, g.col_idx, d=D, max_iter=iters)
@@ -230,8 +307,8 @@ def test_rmat23_parity(prx):
     ref_rp, ref_ci = oracle.transpose(g.row_ptr, g.col_idx)
     assert np.array_equal(_cases.to_np(in_rp), ref_rp)
     assert np.array_equal(_cases.to_np(in_ci), ref_ci)
-    del ref_rp, ref_ci
-    plan = prx.Plan(dg, in_csr=(in_rp, in_ci))
+    del ref_rp, ref_ci, in_rp, in_ci
+    plan = prx.Plan(dg)
     res20 = plan.run(d=D, max_iter=20)
     torch.cuda.synchronize()
     print("[rmat23] gpu done", flush=True)
