@@ -16,8 +16,8 @@
 //     lists its sources in increasing (plan) id order;
 //   * the work items of the iteration kernel: every non-hub bucket cut into
 //     row ranges of about equal cost, every hub row one item, or several
-//     fixed-size chunks when it is very long (built on the host from the hub
-//     rows' lengths).
+//     fixed-size chunks when it is long (built on the host from the hub rows'
+//     lengths).
 // The caller's x, traces and ids never change: pr_run maps x in and out.
 #include <cstdlib>
 #include <cstring>
@@ -41,8 +41,9 @@ struct PlanWs {  // lives as long as the plan
     WorkItem* items;
     ChunkRow* chunk_rows;
     float* hub_part;
-    float* wg_part;
+    float* part;
     RunState* state;
+    int64_t part_stride;
     int64_t n_items_max, n_slots_max, n_chunk_rows_max;
     size_t bytes;
 };
@@ -76,7 +77,8 @@ PlanWs carve_ws(void* base, int32_t n, int64_t nnz) {
     w.items = c.take<WorkItem>((size_t)w.n_items_max);
     w.chunk_rows = c.take<ChunkRow>((size_t)w.n_chunk_rows_max);
     w.hub_part = c.take<float>((size_t)w.n_slots_max);
-    w.wg_part = c.take<float>((size_t)(3 * kMaxGrid));
+    w.part_stride = ceil_div(w.n_items_max, kBatchItems) + kMaxGrid;
+    w.part = c.take<float>((size_t)(3 * w.part_stride));
     w.state = c.take<RunState>(1);
     w.bytes = c.used;
     return w;
@@ -271,9 +273,6 @@ int check_sizes(int32_t n, int64_t nnz) {
 
 }  // namespace
 
-// Resident workgroups of the iteration kernel per CU (run.hip).
-int iterate_blocks_per_cu();
-
 }  // namespace pr
 
 using namespace pr;
@@ -397,8 +396,8 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     int32_t items_of[kNumBuckets];
     int64_t total = (int64_t)hub_items.size();
     for (int b = 0; b < kHubBucket; ++b) {
-        const int64_t cost = (int64_t)stats[kNumBuckets + b] + kRowCost * (int64_t)stats[b];
-        items_of[b] = stats[b] ? (int32_t)ceil_div(cost, kItemCost) : 0;
+        const int64_t bc = (int64_t)stats[kNumBuckets + b] + kRowCost * (int64_t)stats[b];
+        items_of[b] = stats[b] ? (int32_t)ceil_div(bc, kItemCost) : 0;
         total += items_of[b];
     }
     if (total > w.n_items_max || n_slots > w.n_slots_max ||
@@ -422,6 +421,18 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
         }
         item0 += items_of[b];
     }
+
+    // 5. Launch shape: kIterBlocksPerCU workgroups per CU (each holds the
+    //    hot sources in LDS), fewer when there are few item batches.
+    int64_t grid = ceil_div(ceil_div(total, kBatchItems), kIterWaves);
+    if (grid > (int64_t)cus * kIterBlocksPerCU) grid = (int64_t)cus * kIterBlocksPerCU;
+    if (const char* env = std::getenv("PR_GRID"))  // tuning knob: workgroups per launch
+        if (std::atoi(env) > 0) grid = std::atoi(env);
+    if (grid > kMaxGrid / 2) grid = kMaxGrid / 2;
+    if (grid < 1) grid = 1;
+    int64_t fix_grid = ceil_div((int64_t)chunk_rows.size(), kFixBlock / kWave);
+    if (fix_grid > kMaxGrid - grid) fix_grid = kMaxGrid - grid;
+
     if (validate) PR_TRY(read_error_word(err, stream, "pr_plan_create"));
     PR_HIP_TRY(hipStreamSynchronize(stream));  // host item arrays must outlive the copies
 
@@ -442,16 +453,14 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     p->chunk_rows = w.chunk_rows;
     p->n_chunk_rows = (int32_t)chunk_rows.size();
     p->hub_part = w.hub_part;
-    p->wg_part = w.wg_part;
+    p->part = w.part;
+    p->part_stride = w.part_stride;
+    p->n_batches = (int32_t)ceil_div(total, kBatchItems);
     p->state = w.state;
+    p->grid = (int32_t)grid;
+    p->fix_grid = (int32_t)fix_grid;
     {
-        int64_t g = (int64_t)cus * iterate_blocks_per_cu();
-        const char* env = std::getenv("PR_GRID");  // tuning knob: workgroups per launch
-        if (env && std::atoi(env) > 0) g = std::atoi(env);
-        if (g > total) g = total;
-        if (g > kMaxGrid) g = kMaxGrid;
-        p->grid = (int32_t)(g > 0 ? g : 1);
-        int64_t ig = ceil_div(n, kBlock);
+        const int64_t ig = ceil_div(n, kBlock);
         p->init_grid = (int32_t)(ig < kMaxGrid ? ig : kMaxGrid);
     }
     for (int b = 0; b < kNumBuckets; ++b) {

@@ -18,19 +18,39 @@ constexpr int kBucketGroup[kNumBuckets] = {1, 4, 16, 64, 256};
 constexpr int32_t kDefaultBucketMin[kNumBuckets] = {0, 5, 17, 65, 1025};
 constexpr int32_t kMinHubLength = 257;  // lower bound for a tuned hub threshold
 
-// Work items.  A workgroup of the iteration kernel takes items from a queue
-// (one atomic increment each) until the queue is empty:
+// Work items.  Wavefronts of the iteration kernel take batches of
+// kBatchItems consecutive items from a queue (one atomic increment per
+// batch) until the queue is empty:
 //   * kind 0..3: a range of rows of one bucket whose cost (edges + kRowCost per
 //     row) is about kItemCost;
 //   * kind 4: one hub row, whole (at most kHubChunk edges);
 //   * kind 5: kHubChunk consecutive edges of a longer hub row; its gathered
-//     sum goes to a slot, and the finalize kernel adds the slots of the row,
-//     in order, and applies the update.
-// Hub items come first in the queue, so the longest work starts first.
-constexpr int64_t kItemCost = 8192;
+//     sum goes to a slot, and a second kernel adds the slots of the row, in
+//     order, and applies the update.
+// Hub items come first in the list, so the longest work starts first.
+constexpr int64_t kItemCost = 2048;
 constexpr int64_t kRowCost = 8;
-constexpr int32_t kHubChunk = 65536;
+constexpr int32_t kHubChunk = 4096;
 constexpr int kKindChunk = 5;
+constexpr int kBatchItems = 4;
+
+// The queue is split in kQueues interleaved queues: queue q holds the
+// batches q, q + kQueues, ...  A wavefront starts on queue blockIdx %
+// kQueues (workgroups are dealt to the XCDs round-robin) and moves on to the
+// others once its own is empty.  Each head sits on its own 256-byte line.
+constexpr int kQueues = 8;
+
+// The iteration kernel runs kIterBlocksPerCU workgroups of kIterBlock lanes
+// per CU; each keeps the contributions of the first kHotSources plan ids --
+// the sources with the most out-edges -- in LDS (160 KB per CU on gfx950)
+// for the whole launch.
+#ifndef PR_ITER_BLOCKS_PER_CU
+#define PR_ITER_BLOCKS_PER_CU 1
+#endif
+constexpr int kIterBlock = 1024;
+constexpr int kIterWaves = kIterBlock / kWave;
+constexpr int kIterBlocksPerCU = PR_ITER_BLOCKS_PER_CU;
+constexpr int32_t kHotSources = (163840 / kIterBlocksPerCU - 1024) / 4;
 
 struct WorkItem {
     int32_t kind;
@@ -57,23 +77,19 @@ inline int64_t max_items(int32_t n, int64_t nnz) {
     return ceil_div(nnz + kRowCost * (int64_t)n, kItemCost) + kNumBuckets + max_hub_rows(nnz) +
            max_chunk_slots(nnz);
 }
-// Workgroups of the persistent iteration kernel (and partial-sum slots).
+// Workgroups of the iteration kernels (and partial-sum slots).
 constexpr int kMaxGrid = 8192;
+constexpr int kFixBlock = 256;
 // The finalize kernel runs as one workgroup of this many lanes.
 constexpr int kFinalBlock = 1024;
 
 // Device-resident run state.  Written by the finalize and init kernels, read
-// by the next launches (kernel boundaries order the accesses).
-// The work queue is split in kQueues interleaved queues (queue q holds items
-// q, q + kQueues, ...), each head on its own 256-byte line, so the atomic
-// increments spread over kQueues addresses.  A workgroup starts on queue
-// blockIdx % kQueues (workgroups are dealt to the 8 XCDs round-robin) and
-// moves on to the others once its own is empty.
-constexpr int kQueues = 8;
+// by the next launches (kernel boundaries order the accesses); the queue
+// heads are incremented atomically by k_iterate.
 struct RunState {
-    double dmass;        // D of the vector the next iteration starts from
-    int32_t stop;        // 1 once an iteration met the tolerance
-    int32_t iters;       // that iteration's number
+    double dmass;   // D of the vector the next iteration starts from
+    int32_t stop;   // 1 once an iteration met the tolerance
+    int32_t iters;  // that iteration's number
     uint32_t pad[60];
     uint32_t queue[kQueues][64];  // queue heads at [q][0]
 };
@@ -103,9 +119,13 @@ struct pr_plan {
     const pr::ChunkRow* chunk_rows;
     int32_t n_chunk_rows;
     float* hub_part;       // chunk sums
-    float* wg_part;        // [3][kMaxGrid]: per-workgroup L1, dangling mass, sum
+    float* part;           // [3][part_stride]: L1, dangling mass and sum of x' per
+                           // item batch, then per k_hubfix workgroup
+    int64_t part_stride;
+    int32_t n_batches;
     pr::RunState* state;
     int32_t grid;          // workgroups of the iteration kernel
+    int32_t fix_grid;      // workgroups of the chunked-row kernel (0: none)
     int32_t init_grid;
     int32_t bucket_min[pr::kNumBuckets];
     int32_t row_begin[pr::kNumBuckets + 1];  // plan ids, hub bucket first

@@ -5,22 +5,29 @@
 // with contrib[u] = x[u]/outdeg[u] and D the dangling mass of x.
 //
 // The page runs five launches per iteration (scale, SpMV, two reduction
-// passes, combine).  Here there are two:
-//   * k_iterate, a persistent grid that takes work items from a queue: it
-//     gathers contrib over the in-rows of each item's degree bucket (lane,
-//     4-lane, 16-lane, wavefront or workgroup per row), and the lanes that
-//     hold a row's sum apply the update on the spot: x'[v], the next
-//     iteration's contrib'[v] = x'[v] * inv_out[v], and the three running
-//     sums |x'[v] - x[v]|, the dangling part of x' and x'.  Each workgroup
-//     writes its three sums once (the page's "gridDim.x + 1" write budget);
-//   * k_finalize, one workgroup: it finishes the hub rows that were split in
-//     chunks, reduces the per-workgroup sums (in double), appends the L1
-//     distance to the trace, stores D' for the next iteration and raises the
-//     stop flag once L1 < tol.
+// passes, combine).  Here there are two, plus one when the graph has very
+// long in-rows:
+//   * k_iterate, 1024-lane workgroups, one per CU.  A workgroup first copies
+//     the contributions of the hottest sources (the first kHotSources plan
+//     ids: the vertices with the most out-edges) into LDS, where about half of
+//     all gathers on skewed graphs then land.  Its wavefronts then take
+//     batches of work items from a queue: each gathers contrib over the
+//     in-rows of an item's degree bucket (lane, 4-lane, 16-lane group or whole
+//     wavefront per row), and the lanes that hold a row's sum apply the update
+//     on the spot: x'[v], the next iteration's contrib'[v] = x'[v] *
+//     inv_out[v], and the running sums of |x'[v] - x[v]|, of the dangling part
+//     of x' and of x'.  Each batch writes its three sums once (the page's
+//     "one partial per block" write budget), so their total does not depend
+//     on which wavefront ran which batch;
+//   * k_hubfix, only for rows longer than one chunk: adds each such row's
+//     chunk sums, in order, and applies the update;
+//   * k_finalize, one workgroup: reduces the per-workgroup sums (in double),
+//     appends the L1 distance to the trace, stores D' for the next iteration
+//     and raises the stop flag once L1 < tol.
 // D never leaves the device (the page's "Keep the dangling mass on the
 // device").  No kernel publishes data to another workgroup of the same
-// launch, so no launch needs a device-wide fence; the kernel boundary orders
-// k_iterate's stores before k_finalize's loads.
+// launch, so none needs a device-wide fence; kernel boundaries order every
+// store before the loads that depend on it.
 //
 // Every vector is kept in the plan's vertex order; pr_run maps the caller's
 // x in (k_init) and out (k_finish).  contrib is double-buffered across
@@ -41,10 +48,12 @@ struct IterArgs {
     float* __restrict__ xi;
     const WorkItem* __restrict__ items;
     float* __restrict__ hub_part;
-    float* __restrict__ wg_part;
+    float* __restrict__ part;  // [3][stride]: per-batch sums
+    int64_t stride;
     RunState* state;
     double d;
     int32_t n;
+    int32_t hot_n;  // sources held in LDS: min(n, kHotSources)
     int32_t n_items;
 };
 
@@ -83,173 +92,267 @@ __device__ __forceinline__ void update(float* __restrict__ xi, const float* __re
     acc.sum += xn;
 }
 
-// Sum of contrib over the edges [s, e) that lane `gl` of a G-lane group
-// takes: s+gl, s+gl+G, ...  U independent loads per step keep U gathers in
-// flight per lane.  col_idx is streamed once per iteration, so it is loaded
-// non-temporally to leave the caches to contrib.  The plan built every index
-// (in_ci holds plan ids in [0, n)), so none is re-checked here.
-template <int G, int U>
-__device__ __forceinline__ float gather_sum(const IterArgs& a, int32_t s, int32_t e, int gl) {
-    float acc[U];
+// One source's contribution: from the LDS copy below hot_n, else from
+// global memory.  The plan built every index (in_ci holds plan ids in
+// [0, n)), so none is re-checked here.
+__device__ __forceinline__ float contrib_of(const IterArgs& a, const float* hot, int32_t u) {
+    return u < a.hot_n ? hot[u] : a.contrib_in[u];
+}
+
+// col_idx is streamed once per iteration: load it non-temporally, leaving
+// the caches to contrib.
+__device__ __forceinline__ int32_t col(const IterArgs& a, int32_t k) {
+    return __builtin_nontemporal_load(a.in_ci + k);
+}
+
+// Rows [lo, hi) of one bucket, run by one wavefront with G lanes per row
+// (group g of the wavefront takes rows lo+g, lo+g+64/G, ...), B rows per
+// group at a time.  The first U*G edges of all B rows are loaded and gathered
+// together, B*U independent gathers per lane, which is what keeps the memory
+// system busy at this occupancy; only rows longer than U*G (none, with the
+// default bucket bounds, except in bucket 3) take a second, per-row loop.
+// Each row's edges are taken by its group's lanes at stride G and summed in a
+// fixed order, so the result does not depend on scheduling.
+template <int G, int U, int B>
+__device__ __forceinline__ void run_rows(const IterArgs& a, const float* hot, int32_t lo,
+                                         int32_t hi, const Damp& k, Acc& acc) {
+    constexpr int kGroups = kWave / G;
+    const int lane = lane_id();
+    const int gid = lane / G, gl = lane % G;
+    for (int32_t p0 = lo + gid; p0 < hi; p0 += B * kGroups) {
+        int32_t s[B], e[B];
 #pragma unroll
-    for (int j = 0; j < U; ++j) acc[j] = 0.f;
-    for (int32_t k = s + gl; k < e; k += U * G) {
+        for (int b = 0; b < B; ++b) {
+            const int32_t p = p0 + b * kGroups;
+            s[b] = p < hi ? a.in_rp[p] : 0;
+            e[b] = p < hi ? a.in_rp[p + 1] : 0;
+        }
+        int32_t u[B][U];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                const int32_t q = s[b] + gl + j * G;
+                u[b][j] = q < e[b] ? col(a, q) : -1;
+            }
+        float y[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            float c[U];
+#pragma unroll
+            for (int j = 0; j < U; ++j) c[j] = u[b][j] >= 0 ? contrib_of(a, hot, u[b][j]) : 0.f;
+#pragma unroll
+            for (int w = 1; w < U; w <<= 1)
+#pragma unroll
+                for (int j = 0; j + w < U; j += 2 * w) c[j] += c[j + w];
+            y[b] = c[0];
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            for (int32_t q = s[b] + gl + U * G; q < e[b]; q += U * G) {  // long rows only
+                float c[U];
+#pragma unroll
+                for (int j = 0; j < U; ++j) {
+                    const int32_t r = q + j * G;
+                    c[j] = r < e[b] ? contrib_of(a, hot, col(a, r)) : 0.f;
+                }
+#pragma unroll
+                for (int w = 1; w < U; w <<= 1)
+#pragma unroll
+                    for (int j = 0; j + w < U; j += 2 * w) c[j] += c[j + w];
+                y[b] += c[0];
+            }
+            y[b] = group_sum<G>(y[b]);
+            const int32_t p = p0 + b * kGroups;
+            if (gl == 0 && p < hi) update(a.xi, a.inv_out, a.contrib_out, p, y[b], k, acc);
+        }
+    }
+}
+
+// Sum of contrib over edges [s, e) by a whole wavefront (a hub row or a
+// chunk of one): lane l takes s+l, s+l+64, ..., 16 gathers in flight per
+// lane; the lanes are added by a fixed shuffle tree, so every lane gets the
+// same, schedule-independent total in y.
+__device__ __forceinline__ void run_rows_sum(const IterArgs& a, const float* hot, int32_t s,
+                                             int32_t e, int lane, float& y) {
+    constexpr int U = 16;
+    float acc = 0.f;
+    for (int32_t q = s + lane; q < e; q += U * kWave) {
         int32_t u[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j)
-            u[j] = (k + j * G < e) ? __builtin_nontemporal_load(a.in_ci + k + j * G) : -1;
+        for (int j = 0; j < U; ++j) u[j] = q + j * kWave < e ? col(a, q + j * kWave) : -1;
+        float c[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j) acc[j] += (u[j] >= 0) ? a.contrib_in[u[j]] : 0.f;
-    }
+        for (int j = 0; j < U; ++j) c[j] = u[j] >= 0 ? contrib_of(a, hot, u[j]) : 0.f;
 #pragma unroll
-    for (int w = 1; w < U; w <<= 1)
+        for (int w = 1; w < U; w <<= 1)
 #pragma unroll
-        for (int j = 0; j + w < U; j += 2 * w) acc[j] += acc[j + w];
-    return acc[0];
-}
-
-// Rows [lo, hi) of a bucket with G lanes per row (G <= 64): group g of the
-// workgroup takes rows lo+g, lo+g+256/G, ...
-template <int G, int U>
-__device__ __forceinline__ void run_rows(const IterArgs& a, int32_t lo, int32_t hi, const Damp& k,
-                                         Acc& acc) {
-    constexpr int kGroups = kBlock / G;
-    const int gid = threadIdx.x / G, gl = threadIdx.x % G;
-    for (int32_t p = lo + gid; p < hi; p += kGroups) {
-        const int32_t s = a.in_rp[p], e = a.in_rp[p + 1];
-        float y = gather_sum<G, U>(a, s, e, gl);
-        y = group_sum<G>(y);
-        if (gl == 0) update(a.xi, a.inv_out, a.contrib_out, p, y, k, acc);
+            for (int j = 0; j + w < U; j += 2 * w) c[j] += c[j + w];
+        acc += c[0];
     }
+    y = wave_sum(acc);
 }
 
-// Sum over the whole workgroup of edges [s, e) (a hub row or a chunk of one).
-__device__ __forceinline__ float hub_sum(const IterArgs& a, int32_t s, int32_t e, float* red) {
-    return block_sum(gather_sum<kBlock, 8>(a, s, e, threadIdx.x), red);
-}
-
-// The next item for this workgroup: thread 0 increments queue heads, starting
-// with queue *q, until one yields an item below n_items; -1 when every queue
-// is empty.
-__device__ __forceinline__ int32_t next_item(RunState* st, int& q, int& tries, int32_t n_items,
-                                             uint32_t ticket) {
-    int32_t it = q + kQueues * (int32_t)ticket;
-    while (it >= n_items && ++tries < kQueues) {
-        q = (q + 1) % kQueues;
-        it = q + kQueues * (int32_t)atomicAdd(&st->queue[q][0], 1u);
-    }
-    return it < n_items ? it : -1;
-}
-
-__global__ __launch_bounds__(kBlock) void k_iterate(IterArgs a) {
-    __shared__ float red[kWaves];
-    __shared__ int32_t s_item;
-    RunState* st = a.state;
-    if (st->stop) return;  // an earlier iteration met the tolerance
-    const Damp k = make_damp(a.d, a.n, st->dmass);
-
-    int q = blockIdx.x % kQueues, tries = 0;  // used by thread 0 only
-    if (threadIdx.x == 0) s_item = next_item(st, q, tries, a.n_items, atomicAdd(&st->queue[q][0], 1u));
-    __syncthreads();
-    int32_t cur = s_item;
-    Acc acc;
-    while (cur >= 0) {
-        // ask for the next item now; its answer is needed only after this one
-        uint32_t ticket = 0;
-        if (threadIdx.x == 0 && tries < kQueues) ticket = atomicAdd(&st->queue[q][0], 1u);
-        const WorkItem it = a.items[cur];
-        switch (it.kind) {
-            case 0: run_rows<1, 4>(a, it.lo, it.hi, k, acc); break;
-            case 1: run_rows<4, 4>(a, it.lo, it.hi, k, acc); break;
-            case 2: run_rows<16, 4>(a, it.lo, it.hi, k, acc); break;
-            case 3: run_rows<64, 4>(a, it.lo, it.hi, k, acc); break;
-            case kHubBucket: {
-                const float y = hub_sum(a, it.lo, it.hi, red);
-                if (threadIdx.x == 0) update(a.xi, a.inv_out, a.contrib_out, it.aux, y, k, acc);
-                break;
-            }
-            default: {  // kKindChunk
-                const float y = hub_sum(a, it.lo, it.hi, red);
-                if (threadIdx.x == 0) a.hub_part[it.aux] = y;
-                break;
-            }
-        }
-        __syncthreads();  // every lane has read s_item and finished with `red`
-        if (threadIdx.x == 0)
-            s_item = tries < kQueues ? next_item(st, q, tries, a.n_items, ticket) : -1;
-        __syncthreads();
-        cur = s_item;
-    }
-    const float l1 = block_sum(acc.l1, red);
-    const float dg = block_sum(acc.dang, red);
-    const float sm = block_sum(acc.sum, red);
-    if (threadIdx.x == 0) {
-        a.wg_part[blockIdx.x] = l1;
-        a.wg_part[kMaxGrid + blockIdx.x] = dg;
-        a.wg_part[2 * kMaxGrid + blockIdx.x] = sm;
-    }
-}
-
-constexpr int kFinalWaves = kFinalBlock / kWave;
-
-template <class T>
-__device__ __forceinline__ T final_block_sum(T v, T* scratch) {
+template <class T, int W>
+__device__ __forceinline__ T wide_block_sum(T v, T* scratch) {
     v = wave_sum(v);
     if (lane_id() == 0) scratch[threadIdx.x / kWave] = v;
     __syncthreads();
     T r = scratch[0];
 #pragma unroll
-    for (int w = 1; w < kFinalWaves; ++w) r += scratch[w];
+    for (int w = 1; w < W; ++w) r += scratch[w];
     __syncthreads();
     return r;
 }
 
-struct FinArgs {
+// A wavefront's next batch: lane 0 increments queue heads, starting with
+// queue *q, until one yields a batch that holds items; -1 when every queue is
+// empty.  `ticket` is the value the last increment of queue *q returned.
+__device__ __forceinline__ int32_t next_batch(RunState* st, int& q, int& tries, int32_t n_batches,
+                                              uint32_t ticket) {
+    int32_t b = q + kQueues * (int32_t)ticket;
+    while (b >= n_batches && ++tries < kQueues) {
+        q = (q + 1) % kQueues;
+        b = q + kQueues * (int32_t)atomicAdd(&st->queue[q][0], 1u);
+    }
+    return b < n_batches ? b : -1;
+}
+
+// With more than one workgroup per CU, the register budget must leave room
+// for all of their wavefronts.
+#if PR_ITER_BLOCKS_PER_CU > 1
+#define PR_ITER_OCCUPANCY __attribute__((amdgpu_waves_per_eu(4 * PR_ITER_BLOCKS_PER_CU)))
+#else
+#define PR_ITER_OCCUPANCY
+#endif
+
+__global__ __launch_bounds__(kIterBlock) PR_ITER_OCCUPANCY void k_iterate(IterArgs a) {
+    __shared__ float hot[kHotSources];
+    RunState* st = a.state;
+    if (st->stop) return;  // an earlier iteration met the tolerance
+    const Damp k = make_damp(a.d, a.n, st->dmass);
+    for (int32_t i = threadIdx.x; i < a.hot_n; i += kIterBlock) hot[i] = a.contrib_in[i];
+    __syncthreads();
+
+    const int lane = lane_id();
+    const int32_t n_batches = (a.n_items + kBatchItems - 1) / kBatchItems;
+    int q = blockIdx.x % kQueues, tries = 0;  // lane 0's queue state
+    int32_t batch = -1;
+    if (lane == 0) batch = next_batch(st, q, tries, n_batches, atomicAdd(&st->queue[q][0], 1u));
+    batch = __shfl(batch, 0, kWave);
+    while (batch >= 0) {
+        Acc acc;
+        // ask for the next batch now; the answer is needed only after this one
+        uint32_t ticket = 0;
+        if (lane == 0 && tries < kQueues) ticket = atomicAdd(&st->queue[q][0], 1u);
+        const int32_t i1 = (batch + 1) * kBatchItems < a.n_items ? (batch + 1) * kBatchItems
+                                                                 : a.n_items;
+        for (int32_t i = batch * kBatchItems; i < i1; ++i) {
+            const WorkItem it = a.items[i];
+            switch (it.kind) {
+                case 0: run_rows<1, 4, 4>(a, hot, it.lo, it.hi, k, acc); break;
+                case 1: run_rows<4, 4, 4>(a, hot, it.lo, it.hi, k, acc); break;
+                case 2: run_rows<16, 4, 4>(a, hot, it.lo, it.hi, k, acc); break;
+                case 3: run_rows<kWave, 8, 2>(a, hot, it.lo, it.hi, k, acc); break;
+                case kHubBucket: {
+                    float y = 0.f;
+                    run_rows_sum(a, hot, it.lo, it.hi, lane, y);
+                    if (lane == 0) update(a.xi, a.inv_out, a.contrib_out, it.aux, y, k, acc);
+                    break;
+                }
+                default: {  // kKindChunk
+                    float y = 0.f;
+                    run_rows_sum(a, hot, it.lo, it.hi, lane, y);
+                    if (lane == 0) a.hub_part[it.aux] = y;
+                    break;
+                }
+            }
+        }
+        // the batch's sums, in a fixed order whichever wavefront ran it
+        const float l1 = wave_sum(acc.l1), dg = wave_sum(acc.dang), sm = wave_sum(acc.sum);
+        if (lane == 0) {
+            a.part[batch] = l1;
+            a.part[a.stride + batch] = dg;
+            a.part[2 * a.stride + batch] = sm;
+            batch = tries < kQueues ? next_batch(st, q, tries, n_batches, ticket) : -1;
+        }
+        batch = __shfl(batch, 0, kWave);
+    }
+}
+
+struct FixArgs {
     const float* __restrict__ inv_out;
     float* __restrict__ contrib_out;
     float* __restrict__ xi;
     const ChunkRow* __restrict__ chunk_rows;
     const float* __restrict__ hub_part;
-    const float* __restrict__ wg_part;
+    float* __restrict__ part;  // this kernel's sums go to [part0, part0 + gridDim.x)
+    int64_t stride;
+    RunState* state;
+    double d;
+    int32_t n;
+    int32_t n_chunk_rows;
+    int32_t part0;
+};
+
+// Rows longer than one chunk: one wavefront per row adds the row's chunk
+// sums (lanes take slots first+lane, first+lane+64, ...; a fixed shuffle tree
+// adds the lanes) and applies the update.
+__global__ __launch_bounds__(kFixBlock) void k_hubfix(FixArgs f) {
+    __shared__ float red[kFixBlock / kWave];
+    RunState* st = f.state;
+    if (st->stop) return;
+    const Damp k = make_damp(f.d, f.n, st->dmass);
+    constexpr int kW = kFixBlock / kWave;
+    const int lane = lane_id();
+    Acc acc;
+    for (int32_t r = blockIdx.x * kW + threadIdx.x / kWave; r < f.n_chunk_rows;
+         r += gridDim.x * kW) {
+        const ChunkRow cr = f.chunk_rows[r];
+        float y = 0.f;
+        for (int32_t j = lane; j < cr.count; j += kWave) y += f.hub_part[cr.first + j];
+        y = wave_sum(y);
+        if (lane == 0) update(f.xi, f.inv_out, f.contrib_out, cr.row, y, k, acc);
+    }
+    const float l1 = wide_block_sum<float, kW>(acc.l1, red);
+    const float dg = wide_block_sum<float, kW>(acc.dang, red);
+    const float sm = wide_block_sum<float, kW>(acc.sum, red);
+    if (threadIdx.x == 0) {
+        f.part[f.part0 + blockIdx.x] = l1;
+        f.part[f.stride + f.part0 + blockIdx.x] = dg;
+        f.part[2 * f.stride + f.part0 + blockIdx.x] = sm;
+    }
+}
+
+constexpr int kFinalWaves = kFinalBlock / kWave;
+
+struct FinArgs {
+    const float* __restrict__ part;
+    int64_t stride;
     RunState* state;
     float* __restrict__ l1_trace;
     float* __restrict__ sum_trace;
-    double d;
     double tol;
-    int32_t n;
-    int32_t n_chunk_rows;
-    int32_t parts;  // per-workgroup sums to reduce
+    int32_t parts;  // sums to reduce: part[0, parts)
     int32_t t;      // iteration number; 0 after k_init
 };
 
-// One workgroup of kFinalBlock lanes.  After iteration t: finish the chunked
-// hub rows, reduce every sum, record the trace and the next D, test the
-// tolerance, and reset the work queues.  After k_init (t = 0): only D.
+// One workgroup of kFinalBlock lanes.  After iteration t: reduce every sum,
+// record the trace and the next D, test the tolerance, and reset the work
+// queues.  After k_init (t = 0): only D and the queues.
 __global__ __launch_bounds__(kFinalBlock) void k_finalize(FinArgs f) {
     __shared__ double redd[kFinalWaves];
     RunState* st = f.state;
     if (f.t > 0 && st->stop) return;
-    Acc acc;
-    if (f.t > 0 && f.n_chunk_rows > 0) {
-        const Damp k = make_damp(f.d, f.n, st->dmass);
-        const int wave = threadIdx.x / kWave, lane = lane_id();
-        for (int32_t r = wave; r < f.n_chunk_rows; r += kFinalWaves) {
-            const ChunkRow cr = f.chunk_rows[r];
-            float y = 0.f;
-            for (int32_t j = lane; j < cr.count; j += kWave) y += f.hub_part[cr.first + j];
-            y = wave_sum(y);
-            if (lane == 0) update(f.xi, f.inv_out, f.contrib_out, cr.row, y, k, acc);
-        }
-    }
-    double r0 = acc.l1, r1 = acc.dang, r2 = acc.sum;
+    double r0 = 0.0, r1 = 0.0, r2 = 0.0;
     for (int j = threadIdx.x; j < f.parts; j += kFinalBlock) {
-        r0 += (double)f.wg_part[j];
-        r1 += (double)f.wg_part[kMaxGrid + j];
-        r2 += (double)f.wg_part[2 * kMaxGrid + j];
+        r0 += (double)f.part[j];
+        r1 += (double)f.part[f.stride + j];
+        r2 += (double)f.part[2 * f.stride + j];
     }
-    r0 = final_block_sum(r0, redd);
-    r1 = final_block_sum(r1, redd);
-    r2 = final_block_sum(r2, redd);
+    r0 = wide_block_sum<double, kFinalWaves>(r0, redd);
+    r1 = wide_block_sum<double, kFinalWaves>(r1, redd);
+    r2 = wide_block_sum<double, kFinalWaves>(r2, redd);
     if (threadIdx.x < kQueues) st->queue[threadIdx.x][0] = 0u;
     if (threadIdx.x == 0) {
         st->dmass = r1;
@@ -274,7 +377,8 @@ __global__ __launch_bounds__(kBlock) void k_init(const int32_t* __restrict__ new
                                                  const float* __restrict__ x,
                                                  float* __restrict__ xi,
                                                  float* __restrict__ contrib, int32_t n,
-                                                 int x0_given, float* __restrict__ wg_part) {
+                                                 int x0_given, float* __restrict__ part,
+                                                 int64_t stride) {
     __shared__ float red[kWaves];
     const float uniform = (float)(1.0 / (double)n);
     Acc acc;
@@ -291,9 +395,9 @@ __global__ __launch_bounds__(kBlock) void k_init(const int32_t* __restrict__ new
     const float dg = block_sum(acc.dang, red);
     const float sm = block_sum(acc.sum, red);
     if (threadIdx.x == 0) {
-        wg_part[blockIdx.x] = 0.f;
-        wg_part[kMaxGrid + blockIdx.x] = dg;
-        wg_part[2 * kMaxGrid + blockIdx.x] = sm;
+        part[blockIdx.x] = 0.f;
+        part[stride + blockIdx.x] = dg;
+        part[2 * stride + blockIdx.x] = sm;
     }
 }
 
@@ -315,14 +419,6 @@ int chunk_size(const pr_plan* p) {
 
 }  // namespace
 
-int iterate_blocks_per_cu() {
-    int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_iterate, kBlock, 0) != hipSuccess ||
-        blocks < 1)
-        blocks = 1;
-    return blocks;
-}
-
 }  // namespace pr
 
 using namespace pr;
@@ -343,27 +439,21 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
 
     k_init<<<dim3((unsigned)p->init_grid), kBlock, 0, stream>>>(
         p->new_id, p->inv_out, x, p->xi, p->contrib[0], p->n, (flags & PR_X0_GIVEN) ? 1 : 0,
-        p->wg_part);
+        p->part, p->part_stride);
     PR_LAUNCHED("init");
 
     FinArgs f{};
-    f.inv_out = p->inv_out;
-    f.xi = p->xi;
-    f.chunk_rows = p->chunk_rows;
-    f.hub_part = p->hub_part;
-    f.wg_part = p->wg_part;
+    f.part = p->part;
+    f.stride = p->part_stride;
     f.state = p->state;
     f.l1_trace = l1_trace;
     f.sum_trace = sum_trace;
-    f.d = d;
     f.tol = tol;
-    f.n = p->n;
-    f.n_chunk_rows = p->n_chunk_rows;
     f.parts = p->init_grid;
     f.t = 0;
     k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
     PR_LAUNCHED("init finalize");
-    f.parts = p->grid;
+    f.parts = p->n_batches + p->fix_grid;
 
     IterArgs a{};
     a.in_rp = p->in_rp;
@@ -371,12 +461,27 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     a.inv_out = p->inv_out;
     a.xi = p->xi;
     a.items = p->items;
+    a.n_items = p->n_items;
     a.hub_part = p->hub_part;
-    a.wg_part = p->wg_part;
+    a.part = p->part;
+    a.stride = p->part_stride;
     a.state = p->state;
     a.d = d;
     a.n = p->n;
-    a.n_items = p->n_items;
+    a.hot_n = p->n < kHotSources ? p->n : kHotSources;
+
+    FixArgs fx{};
+    fx.inv_out = p->inv_out;
+    fx.xi = p->xi;
+    fx.chunk_rows = p->chunk_rows;
+    fx.hub_part = p->hub_part;
+    fx.part = p->part;
+    fx.stride = p->part_stride;
+    fx.state = p->state;
+    fx.d = d;
+    fx.n = p->n;
+    fx.n_chunk_rows = p->n_chunk_rows;
+    fx.part0 = p->n_batches;
 
     const bool record = flags & PR_RECORD_EVENTS;
     p->events_recorded = false;
@@ -385,9 +490,13 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     auto launch = [&](int32_t t) -> int {
         a.contrib_in = p->contrib[(t - 1) & 1];
         a.contrib_out = p->contrib[t & 1];
-        k_iterate<<<dim3((unsigned)p->grid), kBlock, 0, stream>>>(a);
+        k_iterate<<<dim3((unsigned)p->grid), kIterBlock, 0, stream>>>(a);
         PR_LAUNCHED("iterate");
-        f.contrib_out = a.contrib_out;
+        if (p->fix_grid > 0) {
+            fx.contrib_out = a.contrib_out;
+            k_hubfix<<<dim3((unsigned)p->fix_grid), kFixBlock, 0, stream>>>(fx);
+            PR_LAUNCHED("hub rows");
+        }
         f.t = t;
         k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
         PR_LAUNCHED("finalize");
