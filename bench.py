@@ -1,17 +1,19 @@
 """Benchmark: PageRank power iteration on one MI355X.
 
 One step = the whole path on one synthetic graph already resident in device
-memory: pr_plan_create (inverse out-degrees, sources renumbered by out-degree,
-the in-edge CSR by the device counting-sort transpose, degree buckets) and
-pr_run with 50 fixed iterations (tol = 0, the timed mode of the Day 40 page).
-The stand-alone pr_transpose of the caller's graph is timed on its own.  The default workload is R-MAT
-scale 23, edge factor 32, (a, b, c, d) = (.57, .19, .19, .05), seed 23,
-self-loops and duplicates removed.
+memory: pr_plan_create (vertices renumbered by degree bucket and out-degree,
+inverse out-degrees, the in-edge CSR by the device counting-sort transpose,
+work items) and pr_run with 50 fixed iterations (tol = 0, the timed mode of
+the Day 40 page).  The stand-alone pr_transpose of the caller's graph is
+timed on its own.  The default workload is R-MAT scale 23, edge factor 32,
+(a, b, c, d) = (.57, .19, .19, .05), seed 23, self-loops and duplicates
+removed.
 
 Printed (one JSON line): whole-step throughput in GTEPS (edges x iterations /
-step time), plus the per-iteration figures of the dominant kernel (the fused
-iteration, k_iterate) against the HBM roofline, and the CPU oracle's rate on a
-bounded sample of the same graph.
+step time); the per-iteration time and GTEPS; the gather-and-update kernel
+(k_iterate, timed launch by launch with events on the run's stream) against
+the HBM roofline, counting the bytes any pull iteration must move; and the CPU
+oracle's rate on a bounded sample of the same graph.
 
     python bench.py [--steps K] [--warmup W] [--workload rmat23] [--iters 50]
 """
@@ -142,21 +144,23 @@ def main() -> int:
         it = prx.pr_run(plan, 0.85, 0.0, args.iters, x, l1, None, prx.PR_RECORD_EVENTS, stream)
         ev[2].record(stream)
         iter_ms = prx.pr_plan_iteration_ms(plan)  # waits for the last iteration
+        kernel_ms, _ = prx.pr_plan_kernel_ms(plan)
         prx.pr_plan_destroy(plan)
-        return it, iter_ms
+        return it, iter_ms, kernel_ms
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    parts = {"plan": [], "run": [], "iter": []}
+    parts = {"plan": [], "run": [], "iter": [], "kernel": []}
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        it, iter_ms = step()
+        it, iter_ms, kernel_ms = step()
         parts["plan"].append(ev[0].elapsed_time(ev[1]))
         parts["run"].append(ev[1].elapsed_time(ev[2]))
         parts["iter"].append(iter_ms / it)
+        parts["kernel"].append(kernel_ms)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / args.steps
@@ -178,11 +182,13 @@ def main() -> int:
     med["transpose"] = statistics.median(tt)
     del ws_t, in_rp, in_ci
     iter_ms = med["iter"]
+    kernel_ms = med["kernel"]
     bytes_iter = min_bytes_per_iteration(n, m)
-    achieved = bytes_iter / (iter_ms * 1e-3) / 1e9
+    achieved = bytes_iter / (kernel_ms * 1e-3) / 1e9
     traffic, _ = traffic_from_counters(bytes_iter)
     log(f"step {ms_per_step:.3f} ms: plan {med['plan']:.3f} ms, run {med['run']:.3f} ms "
-        f"({iter_ms * 1e3:.1f} us/iteration); pr_transpose alone {med['transpose']:.3f} ms")
+        f"({iter_ms * 1e3:.1f} us/iteration, k_iterate {kernel_ms * 1e3:.1f} us/launch); "
+        f"pr_transpose alone {med['transpose']:.3f} ms")
 
     scratch = torch.empty(prx.pr_plan_scratch_bytes(n, m), dtype=torch.uint8, device="cuda")
     plan = prx.pr_plan_create(n, m, dg.row_ptr, dg.col_idx, ws_p, scratch, 0, stream)
@@ -215,12 +221,15 @@ def main() -> int:
         "config": {"workload": g.name, "n": n, "m": m, "iterations": args.iters, "d": 0.85,
                    "tol": 0.0, "index": "int32", "step": "pr_plan_create + pr_run"},
         "iteration": {"ms": round(iter_ms, 5), "gteps": round(m / (iter_ms * 1e-3) / 1e9, 2),
-                      "cv": round(iter_cv, 4), "algorithmic_bytes": bytes_iter},
+                      "gbps": round(bytes_iter / (iter_ms * 1e-3) / 1e9, 1),
+                      "cv": round(iter_cv, 4), "algorithmic_bytes": bytes_iter,
+                      "k_iterate_ms": round(kernel_ms, 5)},
         "transpose_ms": round(med["transpose"], 4),
         "plan_ms": round(med["plan"], 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "k_iterate"},
+                     "traffic": traffic, "kernel": "k_iterate",
+                     "launch_ms": round(kernel_ms, 5)},
         "copy_row_gbps": copy_gbps,
         "buckets": buckets,
         "cpu_baseline": cpu,

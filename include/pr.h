@@ -61,7 +61,8 @@ typedef enum pr_status {
 #define PR_X0_GIVEN 0x1u      /* x holds the start vector on entry (warm start, or a
                                  resume from a saved vector); otherwise 1/n */
 #define PR_RECORD_EVENTS 0x2u /* record the plan's timing events around the
-                                 iteration launches (see pr_plan_iteration_ms) */
+                                 iteration launches (see pr_plan_iteration_ms
+                                 and pr_plan_kernel_ms) */
 
 /* Device bytes pr_transpose needs as workspace.  Host-only, no device work. */
 size_t pr_transpose_workspace_bytes(int32_t n, int64_t nnz);
@@ -177,6 +178,15 @@ int pr_run(pr_plan* plan, double d, double tol, int32_t max_iter, float* x_dev,
  * PR_RECORD_EVENTS recorded (first iteration launch to last), waiting for the
  * second event.  Divide by the iteration count for the mean per iteration. */
 int pr_plan_iteration_ms(pr_plan* plan, float* ms_host);
+
+/* Mean duration in milliseconds of the iteration's gather-and-update kernel
+ * alone, over the launches the last pr_run with PR_RECORD_EVENTS timed (one
+ * event pair around each of its first 64 iterations), waiting for them.
+ * *launches_host receives the number of launches averaged.  This is the
+ * kernel that moves almost all of an iteration's bytes; the rest of the
+ * iteration is the per-iteration reduction (one workgroup) and, for graphs
+ * with in-rows longer than 4096 edges, the kernel that finishes them. */
+int pr_plan_kernel_ms(pr_plan* plan, float* mean_ms_host, int32_t* launches_host);
 
 /* Introspection for tests and benchmarks: the number of degree buckets and,
  * per bucket, its first row-length, row count and edge count (host arrays of

@@ -16,7 +16,7 @@ from __future__ import annotations
 from ._lib import (PR_ERR_ARG, PR_ERR_GRAPH, PR_ERR_HIP, PR_ERR_WORKSPACE, PR_OK,
                    PR_RECORD_EVENTS, PR_VALIDATE, PR_X0_GIVEN, PrError,
                    lib, pr_last_error, pr_plan_buckets, pr_plan_create, pr_plan_destroy,
-                   pr_plan_iteration_ms, pr_plan_layout, pr_plan_num_buckets,
+                   pr_plan_iteration_ms, pr_plan_kernel_ms, pr_plan_layout, pr_plan_num_buckets,
                    pr_plan_scratch_bytes, pr_plan_workspace_bytes, pr_run, pr_status_string,
                    pr_transpose, pr_transpose_workspace_bytes)
 
@@ -24,6 +24,7 @@ __all__ = [
     "DeviceGraph", "Plan", "RunResult", "transpose", "PrError", "lib",
     "pr_transpose", "pr_transpose_workspace_bytes", "pr_plan_create", "pr_plan_destroy",
     "pr_plan_workspace_bytes", "pr_plan_scratch_bytes", "pr_run", "pr_plan_iteration_ms",
+    "pr_plan_kernel_ms",
     "pr_plan_buckets", "pr_plan_num_buckets", "pr_plan_layout", "pr_status_string",
     "pr_last_error",
     "PR_OK", "PR_ERR_ARG", "PR_ERR_WORKSPACE", "PR_ERR_GRAPH", "PR_ERR_HIP",
@@ -134,6 +135,9 @@ class Plan:
 
     def iteration_ms(self) -> float:
         return pr_plan_iteration_ms(self.handle)
+
+    def kernel_ms(self) -> tuple[float, int]:
+        return pr_plan_kernel_ms(self.handle)
 
     def close(self) -> None:
         if getattr(self, "handle", None):

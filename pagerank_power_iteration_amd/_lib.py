@@ -47,6 +47,7 @@ _SIGNATURES = {
     "pr_run": (_c.c_int, [_vp, _c.c_double, _c.c_double, _c.c_int32, _vp, _vp, _vp,
                           _c.POINTER(_c.c_int32), _c.c_uint32, _vp]),
     "pr_plan_iteration_ms": (_c.c_int, [_vp, _c.POINTER(_c.c_float)]),
+    "pr_plan_kernel_ms": (_c.c_int, [_vp, _c.POINTER(_c.c_float), _c.POINTER(_c.c_int32)]),
     "pr_plan_num_buckets": (_c.c_int, []),
     "pr_plan_buckets": (_c.c_int, [_vp, _c.POINTER(_c.c_int32), _c.POINTER(_c.c_int32),
                                    _c.POINTER(_c.c_int64)]),
@@ -153,6 +154,14 @@ def pr_plan_iteration_ms(plan) -> float:
     ms = _c.c_float(0.0)
     _check(lib().pr_plan_iteration_ms(plan, _c.byref(ms)))
     return float(ms.value)
+
+
+def pr_plan_kernel_ms(plan) -> tuple[float, int]:
+    """(mean k_iterate launch duration in ms, number of launches averaged)."""
+    ms = _c.c_float(0.0)
+    k = _c.c_int32(0)
+    _check(lib().pr_plan_kernel_ms(plan, _c.byref(ms), _c.byref(k)))
+    return float(ms.value), int(k.value)
 
 
 def pr_plan_num_buckets() -> int:

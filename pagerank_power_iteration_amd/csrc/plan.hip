@@ -474,6 +474,8 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
 
     hipError_t e = hipEventCreate(&p->ev_begin);
     if (e == hipSuccess) e = hipEventCreate(&p->ev_end);
+    for (int i = 0; i < 2 * kTimedLaunches && e == hipSuccess; ++i)
+        e = hipEventCreate(&p->kernel_ev[i / kTimedLaunches][i % kTimedLaunches]);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->chunk_ev[0], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->chunk_ev[1], hipEventDisableTiming);
     if (e == hipSuccess)
@@ -492,6 +494,9 @@ extern "C" int pr_plan_destroy(pr_plan* p) {
     if (!p) return PR_OK;
     if (p->ev_begin) (void)hipEventDestroy(p->ev_begin);
     if (p->ev_end) (void)hipEventDestroy(p->ev_end);
+    for (int i = 0; i < 2 * kTimedLaunches; ++i)
+        if (p->kernel_ev[i / kTimedLaunches][i % kTimedLaunches])
+            (void)hipEventDestroy(p->kernel_ev[i / kTimedLaunches][i % kTimedLaunches]);
     if (p->chunk_ev[0]) (void)hipEventDestroy(p->chunk_ev[0]);
     if (p->chunk_ev[1]) (void)hipEventDestroy(p->chunk_ev[1]);
     if (p->host_status) (void)hipHostFree(p->host_status);

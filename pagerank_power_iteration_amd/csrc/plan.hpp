@@ -94,6 +94,9 @@ struct RunState {
     uint32_t queue[kQueues][64];  // queue heads at [q][0]
 };
 
+// Launches of k_iterate that PR_RECORD_EVENTS times one by one.
+constexpr int kTimedLaunches = 64;
+
 // Host copy of the fields pr_run polls.
 struct RunStatus {
     int32_t stop;
@@ -132,6 +135,8 @@ struct pr_plan {
     int64_t bucket_edges[pr::kNumBuckets];
     int32_t bucket_items[pr::kNumBuckets + 1];  // kinds 0..5
     hipEvent_t ev_begin, ev_end;
+    hipEvent_t kernel_ev[2][pr::kTimedLaunches];  // around k_iterate launches
+    int32_t kernel_timed;                         // pairs the last run recorded
     hipEvent_t chunk_ev[2];
     pr::RunStatus* host_status;  // pinned, [2]
     bool events_recorded;

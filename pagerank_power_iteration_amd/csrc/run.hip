@@ -485,13 +485,20 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
 
     const bool record = flags & PR_RECORD_EVENTS;
     p->events_recorded = false;
+    p->kernel_timed = 0;
     if (record) PR_HIP_TRY(hipEventRecord(p->ev_begin, stream));
 
     auto launch = [&](int32_t t) -> int {
         a.contrib_in = p->contrib[(t - 1) & 1];
         a.contrib_out = p->contrib[t & 1];
+        const bool timed = record && t <= kTimedLaunches;
+        if (timed) PR_HIP_TRY(hipEventRecord(p->kernel_ev[0][t - 1], stream));
         k_iterate<<<dim3((unsigned)p->grid), kIterBlock, 0, stream>>>(a);
         PR_LAUNCHED("iterate");
+        if (timed) {
+            PR_HIP_TRY(hipEventRecord(p->kernel_ev[1][t - 1], stream));
+            p->kernel_timed = t;
+        }
         if (p->fix_grid > 0) {
             fx.contrib_out = a.contrib_out;
             k_hubfix<<<dim3((unsigned)p->fix_grid), kFixBlock, 0, stream>>>(fx);
@@ -551,5 +558,21 @@ extern "C" int pr_plan_iteration_ms(pr_plan* p, float* ms) {
     if (!p->events_recorded) return fail(PR_ERR_ARG, "no pr_run with PR_RECORD_EVENTS on this plan");
     PR_HIP_TRY(hipEventSynchronize(p->ev_end));
     PR_HIP_TRY(hipEventElapsedTime(ms, p->ev_begin, p->ev_end));
+    return PR_OK;
+}
+
+extern "C" int pr_plan_kernel_ms(pr_plan* p, float* ms, int32_t* launches) {
+    if (!p || !ms) return fail(PR_ERR_ARG, "null pointer argument");
+    if (!p->events_recorded || p->kernel_timed < 1)
+        return fail(PR_ERR_ARG, "no pr_run with PR_RECORD_EVENTS on this plan");
+    double total = 0.0;
+    for (int i = 0; i < p->kernel_timed; ++i) {
+        float one = 0.f;
+        PR_HIP_TRY(hipEventSynchronize(p->kernel_ev[1][i]));
+        PR_HIP_TRY(hipEventElapsedTime(&one, p->kernel_ev[0][i], p->kernel_ev[1][i]));
+        total += one;
+    }
+    *ms = (float)(total / p->kernel_timed);
+    if (launches) *launches = p->kernel_timed;
     return PR_OK;
 }

@@ -224,6 +224,8 @@ def test_record_events_gives_a_time(prx):
     plan.run(max_iter=10, record_events=True)
     ms = plan.iteration_ms()
     assert 0.0 < ms < 10_000.0
+    kms, launches = plan.kernel_ms()
+    assert launches == 10 and 0.0 < kms * launches <= ms
 
 
 def test_buckets_cover_every_row_and_edge(prx):
