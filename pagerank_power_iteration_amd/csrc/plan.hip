@@ -49,7 +49,6 @@ struct PlanWs {  // lives as long as the plan
 };
 
 struct PlanScratch {  // needed only while pr_plan_create runs
-    uint32_t* indeg;     // [n]
     int32_t* key;        // [n]
     int32_t* old_of;     // [n]
     uint32_t* deg;       // [n]
@@ -87,7 +86,6 @@ PlanWs carve_ws(void* base, int32_t n, int64_t nnz) {
 PlanScratch carve_scratch(void* base, int32_t n, int64_t nnz) {
     PlanScratch s{};
     Carver c(base);
-    s.indeg = c.take<uint32_t>((size_t)n);
     s.key = c.take<int32_t>((size_t)n);
     s.old_of = c.take<int32_t>((size_t)n);
     s.deg = c.take<uint32_t>((size_t)n);
@@ -122,23 +120,10 @@ __device__ __forceinline__ int bucket_of(const Bounds& b, uint32_t len) {
     return k;
 }
 
-// In-degree histogram.  Targets outside [0, n) are skipped and flagged.
-__global__ __launch_bounds__(kBlock) void k_indegree(const int32_t* __restrict__ ci, int64_t nnz,
-                                                     int32_t n, uint32_t* __restrict__ indeg,
-                                                     uint32_t* __restrict__ err) {
-    GRID_STRIDE(i, nnz) {
-        const int32_t t = ci[i];
-        if ((uint32_t)t < (uint32_t)n)
-            atomicAdd(&indeg[t], 1u);
-        else
-            *err = 1u;
-    }
-}
-
 // Sort key of each vertex: hub bucket first, then decreasing bucket, then
 // decreasing out-degree (saturated at 65535); the stable sort breaks ties by
 // id.  Also rows and edges per bucket.
-__global__ __launch_bounds__(kBlock) void k_plan_keys(const uint32_t* __restrict__ indeg,
+__global__ __launch_bounds__(kBlock) void k_plan_keys(const int32_t* __restrict__ in_rp,
                                                       const int32_t* __restrict__ out_rp, int32_t n,
                                                       Bounds bounds, int32_t* __restrict__ key,
                                                       unsigned long long* __restrict__ stats) {
@@ -146,7 +131,8 @@ __global__ __launch_bounds__(kBlock) void k_plan_keys(const uint32_t* __restrict
     if (threadIdx.x < 2 * kNumBuckets) s[threadIdx.x] = 0;
     __syncthreads();
     GRID_STRIDE(v, n) {
-        const uint32_t len = indeg[v];
+        const int32_t d_in = in_rp[v + 1] - in_rp[v];
+        const uint32_t len = d_in > 0 ? (uint32_t)d_in : 0u;
         const int b = bucket_of(bounds, len);
         int32_t od = out_rp[v + 1] - out_rp[v];
         od = od < 0 ? 0 : (od > 65535 ? 65535 : od);
@@ -202,8 +188,9 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
         int64_t q = (int64_t)out_rp[old_of[j]] + (p - perm_rp[j]);
         q = q < 0 ? 0 : (q >= nnz ? nnz - 1 : q);
         const int32_t t = out_ci[q];
-        // targets were range-checked by k_indegree; clamp anyway
-        perm_ci[p] = new_id[(uint32_t)t < (uint32_t)n ? t : 0];
+        // out-of-range targets were flagged by the in-degree sort, which
+        // clamped them the same way
+        perm_ci[p] = new_id[t < 0 ? 0 : (t >= n ? n - 1 : t)];
     }
 }
 
@@ -314,21 +301,20 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     PR_TRY(fill_u32(err, 0u, 1, stream));
     PR_TRY(fill_u32(reinterpret_cast<uint32_t*>(s.stats), 0u, 4 * kNumBuckets, stream));
     PR_TRY(fill_u32(reinterpret_cast<uint32_t*>(w.state), 0u, sizeof(RunState) / 4, stream));
-    PR_TRY(fill_u32(s.indeg, 0u, n, stream));
     if (validate) {
         PR_TRY(check_out_row_ptr(out_rp, n, nnz, err, stream));
         PR_TRY(read_error_word(err, stream, "pr_plan_create"));
     }
 
-    // 1. Plan order: in-degree buckets, then decreasing out-degree.
-    if (nnz > 0) {
-        k_indegree<<<grid_for(nnz, 8192), kBlock, 0, stream>>>(out_ci, nnz, n, s.indeg, err);
-        PR_LAUNCHED("in-degree");
-    }
+    // 1. Plan order: in-degree buckets, then decreasing out-degree.  The
+    //    in-degrees are the row lengths of the transpose, whose row pointers
+    //    come from a keys-only sort of the targets (perm_rp holds them until
+    //    step 2 needs it).
+    PR_TRY(transpose_row_ptr(n, nnz, out_ci, s.perm_rp, s.tr, stream));
     if (validate) PR_TRY(read_error_word(err, stream, "pr_plan_create"));
     Bounds bounds;
     bucket_bounds(bounds.min_len);
-    k_plan_keys<<<grid_for(n, 1024), kBlock, 0, stream>>>(s.indeg, out_rp, n, bounds, s.key,
+    k_plan_keys<<<grid_for(n, 1024), kBlock, 0, stream>>>(s.perm_rp, out_rp, n, bounds, s.key,
                                                           s.stats);
     PR_LAUNCHED("plan keys");
     {

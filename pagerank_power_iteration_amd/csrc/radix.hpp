@@ -31,6 +31,8 @@ enum RadixMode : int {
     kFromPairs = 1,
     // Vertex keys: key = keys[i], value = i.
     kFromKeys = 2,
+    // Keys only, first pass: key = target id out_col_idx[i] (range-checked).
+    kFromTargets = 3,
 };
 
 struct RadixIn {
@@ -59,7 +61,7 @@ __device__ __forceinline__ int32_t owner_row(const int32_t* __restrict__ rp, int
 
 template <int MODE>
 __device__ __forceinline__ int32_t radix_key(const RadixIn& in, int64_t i) {
-    if (MODE == kFromOutCsr) {
+    if (MODE == kFromOutCsr || MODE == kFromTargets) {
         int32_t k = in.keys[i];
         if ((uint32_t)k >= (uint32_t)in.n) {
             *in.error = 1u;
@@ -92,8 +94,9 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, in
 }
 
 // Stable scatter.  `scanned` is the exclusive scan of the digit-major
-// histogram.  Keys are written only when keys_out is not null.
-template <int MODE>
+// histogram.  Keys are written only when keys_out is not null; values are
+// carried only when VALS.
+template <int MODE, bool VALS = true>
 __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift, int64_t T,
                                                           const uint32_t* __restrict__ scanned,
                                                           int32_t* __restrict__ keys_out,
@@ -129,7 +132,9 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
         if (valid) {
             const int64_t g = base + idx;
             k = radix_key<MODE>(in, g);
-            if (MODE == kFromOutCsr)
+            if (!VALS)
+                v = 0;
+            else if (MODE == kFromOutCsr)
                 v = owner_row(in.row_ptr, g, s_row_lo, s_row_hi);
             else if (MODE == kFromPairs)
                 v = in.vals[g];
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
             const uint32_t dg = ((uint32_t)key[r] >> shift) & (kRadixDigits - 1);
             const uint32_t pos = digit_start[dg] + wave_count[wave][dg] + rank[r];
             s_key[pos] = key[r];
-            s_val[pos] = val[r];
+            if (VALS) s_val[pos] = val[r];
         }
     }
     __syncthreads();
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
         const uint32_t dg = ((uint32_t)k >> shift) & (kRadixDigits - 1);
         const int64_t o = (int64_t)global_start[dg] + (i - (int64_t)digit_start[dg]);
         if (keys_out) keys_out[o] = k;
-        vals_out[o] = s_val[i];
+        if (VALS) vals_out[o] = s_val[i];
     }
 }
 
@@ -249,6 +254,36 @@ int radix_sort(RadixIn in, int bits, int32_t* vals_out, const RadixWs& w, int32_
         PR_LAUNCHED("radix scatter");
         in.keys = kout;
         in.vals = vout;
+        *keys_sorted = kout;
+    }
+    return PR_OK;
+}
+
+// Stable LSD sort of `count` keys alone by their low `bits` bits; pass 0
+// reads keys per MODE.  The sorted keys are left in *keys_sorted.
+template <int MODE>
+int radix_sort_keys(RadixIn in, int bits, const RadixWs& w, int32_t** keys_sorted,
+                    hipStream_t stream) {
+    const int64_t T = radix_tiles(in.count);
+    int passes = (bits + kRadixBits - 1) / kRadixBits;
+    if (passes < 1) passes = 1;
+    for (int p = 0; p < passes; ++p) {
+        const int shift = p * kRadixBits;
+        int32_t* kout = w.key[p & 1];
+        if (p == 0)
+            k_radix_hist<MODE><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, shift, T, w.hist);
+        else
+            k_radix_hist<kFromPairs><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, shift, T, w.hist);
+        PR_LAUNCHED("radix histogram");
+        PR_TRY(scan_exclusive(w.hist, w.scanned, kRadixDigits * T, w.scan_ws, stream));
+        if (p == 0)
+            k_radix_scatter<MODE, false><<<dim3((unsigned)T), kBlock, 0, stream>>>(
+                in, shift, T, w.scanned, kout, nullptr);
+        else
+            k_radix_scatter<kFromPairs, false><<<dim3((unsigned)T), kBlock, 0, stream>>>(
+                in, shift, T, w.scanned, kout, nullptr);
+        PR_LAUNCHED("radix scatter");
+        in.keys = kout;
         *keys_sorted = kout;
     }
     return PR_OK;

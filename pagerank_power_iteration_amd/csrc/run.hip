@@ -344,11 +344,25 @@ __global__ __launch_bounds__(kFinalBlock) void k_finalize(FinArgs f) {
     __shared__ double redd[kFinalWaves];
     RunState* st = f.state;
     if (f.t > 0 && st->stop) return;
+    // lane i adds entries i, i + 1024, ... in that order, eight loads in flight
+    constexpr int kUnroll = 8;
     double r0 = 0.0, r1 = 0.0, r2 = 0.0;
-    for (int j = threadIdx.x; j < f.parts; j += kFinalBlock) {
-        r0 += (double)f.part[j];
-        r1 += (double)f.part[f.stride + j];
-        r2 += (double)f.part[2 * f.stride + j];
+    for (int j0 = threadIdx.x; j0 < f.parts; j0 += kUnroll * kFinalBlock) {
+        float v0[kUnroll], v1[kUnroll], v2[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int j = j0 + u * kFinalBlock;
+            const bool in = j < f.parts;
+            v0[u] = in ? f.part[j] : 0.f;
+            v1[u] = in ? f.part[f.stride + j] : 0.f;
+            v2[u] = in ? f.part[2 * f.stride + j] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            r0 += (double)v0[u];
+            r1 += (double)v1[u];
+            r2 += (double)v2[u];
+        }
     }
     r0 = wide_block_sum<double, kFinalWaves>(r0, redd);
     r1 = wide_block_sum<double, kFinalWaves>(r1, redd);

@@ -93,6 +93,21 @@ int transpose_device(int32_t n, int64_t nnz, const int32_t* out_rp, const int32_
     return PR_OK;
 }
 
+int transpose_row_ptr(int32_t n, int64_t nnz, const int32_t* out_ci, int32_t* in_rp,
+                      const TransposeWs& w, hipStream_t stream) {
+    if (nnz == 0) return fill_u32(reinterpret_cast<uint32_t*>(in_rp), 0u, (int64_t)n + 1, stream);
+    RadixIn in{};
+    in.count = nnz;
+    in.n = n;
+    in.keys = out_ci;
+    in.error = w.error;
+    int32_t* sorted_keys = nullptr;
+    PR_TRY(radix_sort_keys<kFromTargets>(in, vertex_bits(n), w.sort, &sorted_keys, stream));
+    k_rows_from_sorted<<<grid_for(nnz + 1), kBlock, 0, stream>>>(sorted_keys, nnz, n, in_rp);
+    PR_LAUNCHED("row pointers");
+    return PR_OK;
+}
+
 int read_error_word(const uint32_t* err_dev, hipStream_t stream, const char* what) {
     uint32_t h = 0;
     PR_HIP_TRY(hipMemcpyAsync(&h, err_dev, sizeof h, hipMemcpyDeviceToHost, stream));

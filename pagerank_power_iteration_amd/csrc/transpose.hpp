@@ -20,6 +20,12 @@ TransposeWs transpose_carve(void* base, int32_t n, int64_t nnz);
 int transpose_device(int32_t n, int64_t nnz, const int32_t* out_rp, const int32_t* out_ci,
                      int32_t* in_rp, int32_t* in_ci, const TransposeWs& ws, hipStream_t stream);
 
+// Row pointers of the in-edge CSR alone (in_rp[v+1] - in_rp[v] = in-degree
+// of v), from a keys-only radix sort of the targets.  Out-of-range targets are
+// clamped and flagged in ws.error.  Asynchronous on `stream`.
+int transpose_row_ptr(int32_t n, int64_t nnz, const int32_t* out_ci, int32_t* in_rp,
+                      const TransposeWs& ws, hipStream_t stream);
+
 // Bits needed to hold every vertex id in [0, n).
 int vertex_bits(int32_t n);
 
