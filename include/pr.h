@@ -95,6 +95,11 @@ int pr_transpose(int32_t n, int64_t nnz, const int32_t* out_row_ptr_dev,
 /* Opaque iteration plan. */
 typedef struct pr_plan pr_plan;
 
+/* Flag for pr_plan_create: iterate with the degree-bucketed row-per-lane /
+ * group / wavefront pull kernels over the plan's in-edge CSR instead of the
+ * default tiled pull (see pr_plan_create). */
+#define PR_PLAN_BUCKETED 0x2u
+
 /* Device bytes the plan keeps for its lifetime (pr_plan_create's ws_dev), and
  * the device bytes it needs only while pr_plan_create runs (scratch_dev).
  * Host-only, no device work; 0 for invalid sizes. */
@@ -104,35 +109,45 @@ size_t pr_plan_scratch_bytes(int32_t n, int64_t nnz);
 /*
  * Build an iteration plan for one graph, all inside ws_dev:
  *   - a renumbering of the vertices ("plan order"): rows split into degree
- *     buckets by in-degree -- one lane, a 4- or 16-lane group, a 64-lane
- *     wavefront or a 256-lane workgroup per row ("gpu-graph-study", PageRank
- *     T4 degree-bucketed load balancing) -- with the longest-row bucket first,
- *     and inside each bucket by decreasing out-degree, ties by id.  Every
- *     bucket is a contiguous range of plan ids, and the sources read most
- *     often sit together at the start of each range;
+ *     buckets by in-degree ("gpu-graph-study", PageRank T4 degree-bucketed
+ *     load balancing), the longest-row bucket first, and inside each bucket
+ *     by decreasing out-degree, ties by id.  Every bucket is a contiguous
+ *     range of plan ids, and the sources read most often sit together at the
+ *     start of each range;
  *   - inverse out-degrees: 1/outdeg[u], or 0 for a dangling vertex (Meerkat's
  *     PageRank section caches the per-vertex ratio x[u]/out[u]; the
  *     "gpu-graph-study" T3 tier precomputes 1/deg);
- *   - the plan's in-edge CSR: rows and sources in plan ids, each row listing
- *     its sources in increasing plan id, built from the out-edge CSR on the
- *     device with the counting-sort transpose of pr_transpose;
- *   - the work items of the iteration kernel and the per-run scratch.
+ *   - the in-edges in one of two layouts:
+ *       default (tiled pull): each bucket cut into tiles of 2^k consecutive
+ *         rows (k per bucket, so a tile holds about 2^20 in-edges, at most
+ *         16384 rows), a tile's in-edges stored as (source, row offset) pairs
+ *         in increasing source order; the iteration streams a tile's edges in
+ *         that order and adds each contribution into the row's accumulator
+ *         (64-bit fixed point in LDS, exact and order-free);
+ *       PR_PLAN_BUCKETED: the in-edge CSR (rows and sources in plan ids, each
+ *         row listing its sources in increasing plan id), iterated with one
+ *         lane, a 4- or 16-lane group or a 64-lane wavefront per row by
+ *         bucket, hub rows split in chunks;
+ *     either built from the out-edge CSR on the device with the counting-sort
+ *     machinery of pr_transpose;
+ *   - the work list of the iteration kernel and the per-run scratch.
  *
  *   plan_out                   receives the plan (host memory owned by the
  *                              library; release with pr_plan_destroy)
  *   out_row_ptr_dev[n+1]       out-edge CSR (read only; not kept)
  *   out_col_idx_dev[nnz]
- *   ws_dev, ws_bytes           >= pr_plan_workspace_bytes(n, nnz); must stay
- *                              allocated and untouched while the plan lives
+ *   ws_dev, ws_bytes           >= pr_plan_workspace_bytes(n, nnz) (enough for
+ *                              either layout); must stay allocated and
+ *                              untouched while the plan lives
  *   scratch_dev, scratch_bytes >= pr_plan_scratch_bytes(n, nnz); free for other
  *                              use once the call returns
- *   flags                      0 or PR_VALIDATE
+ *   flags                      PR_VALIDATE | PR_PLAN_BUCKETED
  *
- * Synchronizes `stream` (the bucket sizes and the hub rows' lengths are read
- * back to build the work list).  The plan belongs to the device current at
- * creation.  Without PR_VALIDATE a malformed CSR cannot make the library
- * access memory outside the buffers (targets are clamped), but the ranks are
- * then unspecified.
+ * Synchronizes `stream` (bucket sizes and the tiles' or hub rows' edge counts
+ * are read back to build the work list).  The plan belongs to the device
+ * current at creation.  Without PR_VALIDATE a malformed CSR cannot make the
+ * library access memory outside the buffers (targets are clamped), but the
+ * ranks are then unspecified.
  */
 int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_row_ptr_dev,
                    const int32_t* out_col_idx_dev, void* ws_dev, size_t ws_bytes,
@@ -184,8 +199,9 @@ int pr_plan_iteration_ms(pr_plan* plan, float* ms_host);
  * event pair around each of its first 64 iterations), waiting for them.
  * *launches_host receives the number of launches averaged.  This is the
  * kernel that moves almost all of an iteration's bytes; the rest of the
- * iteration is the per-iteration reduction (one workgroup) and, for graphs
- * with in-rows longer than 4096 edges, the kernel that finishes them. */
+ * iteration is the per-iteration reduction (one workgroup) and, when some
+ * tiles (or, bucketed, some in-rows) are cut in pieces, the kernel that
+ * finishes their rows. */
 int pr_plan_kernel_ms(pr_plan* plan, float* mean_ms_host, int32_t* launches_host);
 
 /* Introspection for tests and benchmarks: the number of degree buckets and,
@@ -197,10 +213,20 @@ int pr_plan_buckets(const pr_plan* plan, int32_t* min_len_host, int32_t* rows_ho
 
 /* Introspection for tests: device pointers (inside the plan's workspace) to
  * the plan's in-edge CSR (n+1 row pointers, nnz sources; rows and sources in
- * plan ids) and to new_id[n] (the plan id of each of the caller's vertices).
- * Any output pointer may be NULL. */
+ * plan ids; NULL for a tiled plan) and to new_id[n] (the plan id of each of
+ * the caller's vertices).  Any output pointer may be NULL. */
 int pr_plan_layout(const pr_plan* plan, const int32_t** in_row_ptr_dev,
                    const int32_t** in_col_idx_dev, const int32_t** new_id_dev);
+
+/* Introspection for tests, tiled plans only (PR_ERR_ARG otherwise): device
+ * pointers to tile_src[nnz] (source plan id of each tile edge), tile_row[nnz]
+ * (its row's offset from the tile's first row) and tile_ptr[n_tiles+1] (the
+ * first tile edge of each tile); the tile count; and, into host arrays of
+ * n_tiles entries, each tile's first plan id and row count.  Any output may
+ * be NULL (call once with NULL arrays to learn n_tiles). */
+int pr_plan_tiles(const pr_plan* plan, const int32_t** tile_src_dev, const uint16_t** tile_row_dev,
+                  const int32_t** tile_ptr_dev, int32_t* n_tiles_host, int32_t* row0_host,
+                  int32_t* rows_host);
 
 /* Human-readable name of a status code (static storage). */
 const char* pr_status_string(int status);

@@ -14,9 +14,9 @@ helpers below only allocate device memory with torch and pass pointers:
 from __future__ import annotations
 
 from ._lib import (PR_ERR_ARG, PR_ERR_GRAPH, PR_ERR_HIP, PR_ERR_WORKSPACE, PR_OK,
-                   PR_RECORD_EVENTS, PR_VALIDATE, PR_X0_GIVEN, PrError,
+                   PR_PLAN_BUCKETED, PR_RECORD_EVENTS, PR_VALIDATE, PR_X0_GIVEN, PrError,
                    lib, pr_last_error, pr_plan_buckets, pr_plan_create, pr_plan_destroy,
-                   pr_plan_iteration_ms, pr_plan_kernel_ms, pr_plan_layout, pr_plan_num_buckets,
+                   pr_plan_iteration_ms, pr_plan_kernel_ms, pr_plan_layout, pr_plan_tiles, pr_plan_num_buckets,
                    pr_plan_scratch_bytes, pr_plan_workspace_bytes, pr_run, pr_status_string,
                    pr_transpose, pr_transpose_workspace_bytes)
 
@@ -24,11 +24,11 @@ __all__ = [
     "DeviceGraph", "Plan", "RunResult", "transpose", "PrError", "lib",
     "pr_transpose", "pr_transpose_workspace_bytes", "pr_plan_create", "pr_plan_destroy",
     "pr_plan_workspace_bytes", "pr_plan_scratch_bytes", "pr_run", "pr_plan_iteration_ms",
-    "pr_plan_kernel_ms",
+    "pr_plan_kernel_ms", "pr_plan_tiles",
     "pr_plan_buckets", "pr_plan_num_buckets", "pr_plan_layout", "pr_status_string",
     "pr_last_error",
     "PR_OK", "PR_ERR_ARG", "PR_ERR_WORKSPACE", "PR_ERR_GRAPH", "PR_ERR_HIP",
-    "PR_VALIDATE", "PR_X0_GIVEN", "PR_RECORD_EVENTS",
+    "PR_VALIDATE", "PR_PLAN_BUCKETED", "PR_X0_GIVEN", "PR_RECORD_EVENTS",
 ]
 
 
@@ -108,7 +108,23 @@ class Plan:
         def view(addr, count):
             off = addr - base
             return self.ws[off:off + 4 * count].view(torch.int32)
-        return view(rp, n + 1), view(ci, m), view(nid, n)
+        return (None if rp is None else view(rp, n + 1)), (None if ci is None else view(ci, m)), \
+            view(nid, n)
+
+    def tiles(self):
+        """Tiled plans: (tile_src int32[m], tile_row int16[m] (the row offset
+        in its tile, as unsigned 16-bit), tile_ptr int32[n_tiles+1], row0,
+        rows) -- device views and numpy arrays."""
+        torch = _torch()
+        src, row, ptr, nt, row0, rows = pr_plan_tiles(self.handle)
+        base = self.ws.data_ptr()
+        m = self.graph.nnz
+
+        def view(addr, nbytes, dtype):
+            off = addr - base
+            return self.ws[off:off + nbytes].view(dtype)
+        return (view(src, 4 * m, torch.int32), view(row, 2 * m, torch.int16),
+                view(ptr, 4 * (nt + 1), torch.int32), row0, rows)
 
     @property
     def n(self) -> int:

@@ -23,6 +23,7 @@ PR_ERR_GRAPH = -3
 PR_ERR_HIP = -4
 
 PR_VALIDATE = 0x1
+PR_PLAN_BUCKETED = 0x2
 PR_X0_GIVEN = 0x1
 PR_RECORD_EVENTS = 0x2
 
@@ -52,6 +53,8 @@ _SIGNATURES = {
     "pr_plan_buckets": (_c.c_int, [_vp, _c.POINTER(_c.c_int32), _c.POINTER(_c.c_int32),
                                    _c.POINTER(_c.c_int64)]),
     "pr_plan_layout": (_c.c_int, [_vp, _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_vp)]),
+    "pr_plan_tiles": (_c.c_int, [_vp, _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_vp),
+                                 _c.POINTER(_c.c_int32), _vp, _vp]),
     "pr_status_string": (_c.c_char_p, [_c.c_int]),
     "pr_last_error": (_c.c_char_p, []),
 }
@@ -137,6 +140,20 @@ def pr_plan_layout(plan) -> tuple[int, int, int | None]:
     rp, ci, nid = _vp(), _vp(), _vp()
     _check(lib().pr_plan_layout(plan, _c.byref(rp), _c.byref(ci), _c.byref(nid)))
     return rp.value, ci.value, nid.value
+
+
+def pr_plan_tiles(plan):
+    """Device addresses of the tiled plan's tile_src, tile_row and tile_ptr,
+    and each tile's first plan id and row count (numpy arrays)."""
+    import numpy as np
+    src, row, ptr = _vp(), _vp(), _vp()
+    nt = _c.c_int32(0)
+    _check(lib().pr_plan_tiles(plan, _c.byref(src), _c.byref(row), _c.byref(ptr), _c.byref(nt),
+                               None, None))
+    row0 = np.zeros(nt.value, dtype=np.int32)
+    rows = np.zeros(nt.value, dtype=np.int32)
+    _check(lib().pr_plan_tiles(plan, None, None, None, None, row0.ctypes.data, rows.ctypes.data))
+    return src.value, row.value, ptr.value, nt.value, row0, rows
 
 
 def pr_plan_destroy(plan: int | None) -> None:

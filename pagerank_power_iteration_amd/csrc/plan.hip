@@ -19,6 +19,7 @@
 //     fixed-size chunks when it is long (built on the host from the hub rows'
 //     lengths).
 // The caller's x, traces and ids never change: pr_run maps x in and out.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <vector>
@@ -30,21 +31,42 @@ namespace pr {
 
 namespace {
 
+// Upper bounds of the tiled layout.
+inline int64_t max_tiles(int32_t n) { return n / kTileMinRows + kNumBuckets + 1; }
+inline int64_t max_units(int32_t n, int64_t nnz) { return max_tiles(n) + nnz / kUnitEdges + 1; }
+inline int64_t max_fixes(int32_t n, int64_t nnz) {
+    const int64_t a = max_tiles(n), b = nnz / kUnitEdges + 1;
+    return a < b ? a : b;
+}
+// A tile cut into c > 1 units has more than (c-1)*kUnitEdges edges, so the
+// slots of all cut tiles hold at most 2*nnz/kUnitEdges tiles' worth of rows.
+inline int64_t max_partial(int64_t nnz) { return 2 * (nnz / kUnitEdges + 1) * kTileMaxRows; }
+
 struct PlanWs {  // lives as long as the plan
     float* inv_out;
     int32_t* new_id;
     float* xi;
     float* contrib0;
     float* contrib1;
+    float* part;
+    RunState* state;
+    int64_t part_stride;
+    // bucketed pull
     int32_t* in_rp;
     int32_t* in_ci;
     WorkItem* items;
     ChunkRow* chunk_rows;
     float* hub_part;
-    float* part;
-    RunState* state;
-    int64_t part_stride;
     int64_t n_items_max, n_slots_max, n_chunk_rows_max;
+    // tiled pull
+    int32_t* tsrc;
+    uint16_t* tdst;
+    int32_t* tile_ptr;
+    Tile* tiles;
+    TileUnit* units;
+    TileFix* fixes;
+    long long* partial;
+    int64_t n_tiles_max, n_units_max, n_fixes_max, n_partial_max;
     size_t bytes;
 };
 
@@ -54,33 +76,58 @@ struct PlanScratch {  // needed only while pr_plan_create runs
     uint32_t* deg;       // [n]
     int32_t* perm_rp;    // [n + 1]
     int32_t* perm_ci;    // [nnz]
+    int32_t* src_of;     // [nnz] source (plan id) of each edge of perm_ci
+    int32_t* order;      // [nnz] tiled: perm_ci positions sorted by tile
     unsigned long long* stats;  // [2 * kNumBuckets]: rows, edges per bucket
     RadixWs vsort;       // sort of the n vertex keys (and scans over n)
     TransposeWs tr;
     size_t bytes;
 };
 
-PlanWs carve_ws(void* base, int32_t n, int64_t nnz) {
+// The arrays both modes use come first; the rest of the workspace holds one
+// mode's arrays (the byte count is the larger of the two).
+PlanWs carve_ws(void* base, int32_t n, int64_t nnz, bool tiled) {
     PlanWs w{};
     Carver c(base);
     w.n_items_max = max_items(n, nnz);
     w.n_slots_max = max_chunk_slots(nnz);
     w.n_chunk_rows_max = max_chunk_rows(nnz);
+    w.n_tiles_max = max_tiles(n);
+    w.n_units_max = max_units(n, nnz);
+    w.n_fixes_max = max_fixes(n, nnz);
+    w.n_partial_max = max_partial(nnz);
     w.inv_out = c.take<float>((size_t)n);
     w.new_id = c.take<int32_t>((size_t)n);
     w.xi = c.take<float>((size_t)n);
     w.contrib0 = c.take<float>((size_t)n);
     w.contrib1 = c.take<float>((size_t)n);
-    w.in_rp = c.take<int32_t>((size_t)n + 1);
-    w.in_ci = c.take<int32_t>((size_t)nnz);
-    w.items = c.take<WorkItem>((size_t)w.n_items_max);
-    w.chunk_rows = c.take<ChunkRow>((size_t)w.n_chunk_rows_max);
-    w.hub_part = c.take<float>((size_t)w.n_slots_max);
-    w.part_stride = ceil_div(w.n_items_max, kBatchItems) + kMaxGrid;
+    const int64_t batches = ceil_div(w.n_items_max, kBatchItems);
+    w.part_stride = (batches > w.n_units_max ? batches : w.n_units_max) + kMaxGrid;
     w.part = c.take<float>((size_t)(3 * w.part_stride));
     w.state = c.take<RunState>(1);
+    if (!tiled) {
+        w.in_rp = c.take<int32_t>((size_t)n + 1);
+        w.in_ci = c.take<int32_t>((size_t)nnz);
+        w.items = c.take<WorkItem>((size_t)w.n_items_max);
+        w.chunk_rows = c.take<ChunkRow>((size_t)w.n_chunk_rows_max);
+        w.hub_part = c.take<float>((size_t)w.n_slots_max);
+    } else {
+        w.tsrc = c.take<int32_t>((size_t)nnz);
+        w.tdst = c.take<uint16_t>((size_t)nnz);
+        w.tile_ptr = c.take<int32_t>((size_t)w.n_tiles_max + 1);
+        w.tiles = c.take<Tile>((size_t)w.n_tiles_max);
+        w.units = c.take<TileUnit>((size_t)w.n_units_max);
+        w.fixes = c.take<TileFix>((size_t)w.n_fixes_max);
+        w.partial = c.take<long long>((size_t)w.n_partial_max);
+    }
     w.bytes = c.used;
     return w;
+}
+
+size_t ws_bytes_needed(int32_t n, int64_t nnz) {
+    const size_t a = carve_ws(nullptr, n, nnz, false).bytes;
+    const size_t b = carve_ws(nullptr, n, nnz, true).bytes;
+    return a > b ? a : b;
 }
 
 PlanScratch carve_scratch(void* base, int32_t n, int64_t nnz) {
@@ -91,6 +138,8 @@ PlanScratch carve_scratch(void* base, int32_t n, int64_t nnz) {
     s.deg = c.take<uint32_t>((size_t)n);
     s.perm_rp = c.take<int32_t>((size_t)n + 1);
     s.perm_ci = c.take<int32_t>((size_t)nnz);
+    s.src_of = c.take<int32_t>((size_t)nnz);
+    s.order = c.take<int32_t>((size_t)nnz);
     s.stats = c.take<unsigned long long>(2 * kNumBuckets);
     s.vsort = radix_carve(c, n);
     TransposeWs tw = transpose_carve(c.base ? c.base + c.used : nullptr, n, nnz);
@@ -172,7 +221,8 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
                                                          const int32_t* __restrict__ out_rp,
                                                          const int32_t* __restrict__ out_ci,
                                                          int32_t n, int64_t nnz,
-                                                         int32_t* __restrict__ perm_ci) {
+                                                         int32_t* __restrict__ perm_ci,
+                                                         int32_t* __restrict__ src_of) {
     __shared__ int32_t s_lo, s_hi;
     const int64_t base = blockIdx.x * (int64_t)(kBlock * kPermItems);
     const int64_t last = (base + kBlock * kPermItems < nnz ? base + kBlock * kPermItems : nnz) - 1;
@@ -191,6 +241,34 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
         // out-of-range targets were flagged by the in-degree sort, which
         // clamped them the same way
         perm_ci[p] = new_id[t < 0 ? 0 : (t >= n ? n - 1 : t)];
+        src_of[p] = j;
+    }
+}
+
+// First plan id of tile t.  Its segment is the last one whose first tile is
+// <= t (first tiles do not decrease; an empty segment shares its first tile
+// with the next one, which is then counted too).
+__device__ __forceinline__ int32_t tile_row0(const TileMap& m, int32_t t) {
+    int seg = 0;
+#pragma unroll
+    for (int j = 1; j < kTileSegments; ++j) seg += (t >= m.tile0[j]) ? 1 : 0;
+    return m.start[seg] + ((t - m.tile0[seg]) << m.shift[seg]);
+}
+
+// The tile edge arrays: position i of the tile-sorted order holds edge
+// order[i] of the renumbered out-edge CSR; its source and its row offset in
+// its tile (key[i]).
+__global__ __launch_bounds__(kBlock) void k_tile_edges(const int32_t* __restrict__ order,
+                                                       const int32_t* __restrict__ key,
+                                                       const int32_t* __restrict__ src_of,
+                                                       const int32_t* __restrict__ perm_ci,
+                                                       int64_t nnz, TileMap map,
+                                                       int32_t* __restrict__ tsrc,
+                                                       uint16_t* __restrict__ tdst) {
+    GRID_STRIDE(i, nnz) {
+        const int32_t e = order[i];
+        tsrc[i] = src_of[e];
+        tdst[i] = (uint16_t)(perm_ci[e] - tile_row0(map, key[i]));
     }
 }
 
@@ -251,6 +329,205 @@ void bucket_bounds(int32_t out[kNumBuckets]) {
     std::memcpy(out, tmp, sizeof(tmp));
 }
 
+
+// What a mode's builder reports back to pr_plan_create.
+struct Built {
+    int32_t n_items = 0, n_chunk_rows = 0, grid = 1, fix_grid = 0;
+    int32_t items_of[kNumBuckets + 1] = {};
+    TileMap map{};
+    int32_t n_tiles = 0, n_units = 0, n_fixes = 0, tile_grid = 1;
+    std::vector<WorkItem> hub_items;   // host arrays copied to the device
+    std::vector<ChunkRow> chunk_rows;
+    std::vector<Tile> tiles;
+    std::vector<TileUnit> units;
+    std::vector<TileFix> fixes;
+};
+
+// Bucketed pull: the plan's in-edge CSR (counting-sort transpose of the
+// renumbered out-edge CSR), hub rows whole or in chunks (from the hub rows'
+// lengths, read back), and every other bucket cut into row ranges of about
+// kItemCost.
+int build_bucketed(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
+                   const unsigned long long* stats, const int32_t* row_begin, int cus,
+                   hipStream_t stream, Built& bt) {
+    PR_TRY(transpose_device(n, nnz, s.perm_rp, s.perm_ci, w.in_rp, w.in_ci, s.tr, stream));
+    const int32_t n_hub = (int32_t)stats[kHubBucket];
+    std::vector<int32_t> hub_rp((size_t)n_hub + 1);
+    PR_HIP_TRY(hipMemcpyAsync(hub_rp.data(), w.in_rp, sizeof(int32_t) * hub_rp.size(),
+                              hipMemcpyDeviceToHost, stream));
+    PR_HIP_TRY(hipStreamSynchronize(stream));
+
+    std::vector<WorkItem>& hub_items = bt.hub_items;
+    std::vector<ChunkRow>& chunk_rows = bt.chunk_rows;
+    int32_t n_slots = 0;
+    hub_items.reserve((size_t)n_hub);
+    for (int32_t r = 0; r < n_hub; ++r) {
+        const int32_t lo = hub_rp[r], hi = hub_rp[r + 1];
+        if (hi - lo <= kHubChunk) {
+            hub_items.push_back(WorkItem{kHubBucket, lo, hi, r});
+            continue;
+        }
+        ChunkRow cr{r, n_slots, (int32_t)ceil_div(hi - lo, kHubChunk), 0};
+        for (int32_t c = 0; c < cr.count; ++c) {
+            const int32_t a = lo + c * kHubChunk;
+            const int32_t b = (hi - a) < kHubChunk ? hi : a + kHubChunk;
+            hub_items.push_back(WorkItem{kKindChunk, a, b, n_slots + c});
+        }
+        n_slots += cr.count;
+        chunk_rows.push_back(cr);
+    }
+    int64_t total = (int64_t)hub_items.size();
+    for (int b = 0; b < kHubBucket; ++b) {
+        const int64_t bc = (int64_t)stats[kNumBuckets + b] + kRowCost * (int64_t)stats[b];
+        bt.items_of[b] = stats[b] ? (int32_t)ceil_div(bc, kItemCost) : 0;
+        total += bt.items_of[b];
+    }
+    for (const WorkItem& it : hub_items) bt.items_of[it.kind] += 1;
+    if (total > w.n_items_max || n_slots > w.n_slots_max ||
+        (int64_t)chunk_rows.size() > w.n_chunk_rows_max)
+        return fail(PR_ERR_ARG, "work items (%lld) exceed the planned bound (%lld)",
+                    (long long)total, (long long)w.n_items_max);
+    if (!hub_items.empty())
+        PR_HIP_TRY(hipMemcpyAsync(w.items, hub_items.data(), sizeof(WorkItem) * hub_items.size(),
+                                  hipMemcpyHostToDevice, stream));
+    if (!chunk_rows.empty())
+        PR_HIP_TRY(hipMemcpyAsync(w.chunk_rows, chunk_rows.data(),
+                                  sizeof(ChunkRow) * chunk_rows.size(), hipMemcpyHostToDevice,
+                                  stream));
+    int32_t item0 = (int32_t)hub_items.size();
+    for (int b = kHubBucket - 1; b >= 0; --b) {
+        if (bt.items_of[b] > 0) {
+            k_bucket_items<<<grid_for(bt.items_of[b]), kBlock, 0, stream>>>(
+                w.in_rp, row_begin[b], row_begin[b] + (int32_t)stats[b], b, bt.items_of[b], item0,
+                w.items);
+            PR_LAUNCHED("bucket items");
+        }
+        item0 += bt.items_of[b];
+    }
+    bt.n_items = (int32_t)total;
+    bt.n_chunk_rows = (int32_t)chunk_rows.size();
+
+    // kIterBlocksPerCU workgroups per CU (each holds the hot sources in LDS),
+    // fewer when there are few item batches.
+    int64_t grid = ceil_div(ceil_div(total, kBatchItems), kIterWaves);
+    if (grid > (int64_t)cus * kIterBlocksPerCU) grid = (int64_t)cus * kIterBlocksPerCU;
+    if (const char* env = std::getenv("PR_GRID"))  // tuning knob: workgroups per launch
+        if (std::atoi(env) > 0) grid = std::atoi(env);
+    if (grid > kMaxGrid / 2) grid = kMaxGrid / 2;
+    if (grid < 1) grid = 1;
+    int64_t fix_grid = ceil_div((int64_t)chunk_rows.size(), kFixBlock / kWave);
+    if (fix_grid > kMaxGrid - grid) fix_grid = kMaxGrid - grid;
+    bt.grid = (int32_t)grid;
+    bt.fix_grid = (int32_t)fix_grid;
+    return PR_OK;
+}
+
+int log2_ceil(int64_t x) {
+    int k = 0;
+    while (((int64_t)1 << k) < x) ++k;
+    return k;
+}
+
+// Tiled pull: tile sizes per bucket, the renumbered edges sorted by tile
+// (stable, so each tile keeps them in increasing source order), the tile
+// edge arrays, and the units (built on the host from the tiles' edge counts,
+// read back).
+int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
+                const unsigned long long* stats, const int32_t* row_begin, int cus,
+                hipStream_t stream, Built& bt) {
+    TileMap& map = bt.map;
+    int32_t tiles = 0;
+    for (int seg = 0; seg < kTileSegments; ++seg) {
+        const int b = kHubBucket - seg;  // segment 0 = hub bucket
+        const int64_t rows = (int64_t)stats[b], edges = (int64_t)stats[kNumBuckets + b];
+        int64_t want = edges > 0 ? ceil_div(kTileTargetEdges * rows, edges) : kTileMaxRows;
+        if (want < kTileMinRows) want = kTileMinRows;
+        if (want > kTileMaxRows) want = kTileMaxRows;
+        map.start[seg] = row_begin[b];
+        map.tile0[seg] = tiles;
+        map.shift[seg] = log2_ceil(want);
+        tiles += (int32_t)ceil_div(rows, (int64_t)1 << map.shift[seg]);
+    }
+    map.start[kTileSegments] = n;
+    if (tiles > w.n_tiles_max)
+        return fail(PR_ERR_ARG, "tiles (%d) exceed the planned bound (%lld)", tiles,
+                    (long long)w.n_tiles_max);
+    bt.n_tiles = tiles;
+
+    int32_t* sorted_tiles = nullptr;
+    if (nnz > 0) {
+        RadixIn in{};
+        in.count = nnz;
+        in.n = n;
+        in.keys = s.perm_ci;
+        in.tiles = map;
+        in.error = s.tr.error;
+        PR_TRY(radix_sort<kFromTileKeys>(in, vertex_bits(tiles), s.order, s.tr.sort, &sorted_tiles,
+                                          stream));
+        k_tile_edges<<<grid_for(nnz, 8192), kBlock, 0, stream>>>(s.order, sorted_tiles, s.src_of,
+                                                                 s.perm_ci, nnz, map, w.tsrc, w.tdst);
+        PR_LAUNCHED("tile edges");
+    }
+    PR_TRY(rows_from_sorted(sorted_tiles, nnz, tiles, w.tile_ptr, stream));
+    std::vector<int32_t> tp((size_t)tiles + 1);
+    PR_HIP_TRY(hipMemcpyAsync(tp.data(), w.tile_ptr, sizeof(int32_t) * tp.size(),
+                              hipMemcpyDeviceToHost, stream));
+    PR_HIP_TRY(hipStreamSynchronize(stream));
+
+    // Tiles, units and slots.  Units of cut tiles first (the largest units),
+    // then whole tiles by decreasing edge count, so the longest work starts
+    // first.
+    bt.tiles.resize((size_t)tiles);
+    std::vector<TileUnit> whole;
+    int64_t slot = 0;
+    for (int seg = 0; seg < kTileSegments; ++seg) {
+        const int32_t end = map.start[seg + 1];
+        const int32_t last = seg + 1 < kTileSegments ? map.tile0[seg + 1] : tiles;
+        for (int32_t t = map.tile0[seg]; t < last; ++t) {
+            const int32_t row0 = map.start[seg] + ((t - map.tile0[seg]) << map.shift[seg]);
+            const int32_t rows = (end - row0) < (1 << map.shift[seg]) ? end - row0 : 1 << map.shift[seg];
+            bt.tiles[(size_t)t] = Tile{row0, rows};
+            const int32_t e0 = tp[(size_t)t], e1 = tp[(size_t)t + 1];
+            if ((int64_t)(e1 - e0) <= kUnitEdges) {
+                whole.push_back(TileUnit{t, e0, e1, -1});
+                continue;
+            }
+            const int32_t count = (int32_t)ceil_div(e1 - e0, kUnitEdges);
+            if (slot + (int64_t)count * rows > w.n_partial_max)
+                return fail(PR_ERR_ARG, "tile slots exceed the planned bound");
+            bt.fixes.push_back(TileFix{row0, rows, (int32_t)slot, count});
+            for (int32_t j = 0; j < count; ++j) {
+                const int32_t a = e0 + (int32_t)(j * kUnitEdges);
+                const int32_t b = (e1 - a) < kUnitEdges ? e1 : a + (int32_t)kUnitEdges;
+                bt.units.push_back(TileUnit{t, a, b, (int32_t)(slot + (int64_t)j * rows)});
+            }
+            slot += (int64_t)count * rows;
+        }
+    }
+    std::stable_sort(whole.begin(), whole.end(), [](const TileUnit& x, const TileUnit& y) {
+        return (x.e1 - x.e0) > (y.e1 - y.e0);
+    });
+    bt.units.insert(bt.units.end(), whole.begin(), whole.end());
+    if ((int64_t)bt.units.size() > w.n_units_max || (int64_t)bt.fixes.size() > w.n_fixes_max)
+        return fail(PR_ERR_ARG, "tile units exceed the planned bound");
+    bt.n_units = (int32_t)bt.units.size();
+    bt.n_fixes = (int32_t)bt.fixes.size();
+    PR_HIP_TRY(hipMemcpyAsync(w.tiles, bt.tiles.data(), sizeof(Tile) * bt.tiles.size(),
+                              hipMemcpyHostToDevice, stream));
+    PR_HIP_TRY(hipMemcpyAsync(w.units, bt.units.data(), sizeof(TileUnit) * bt.units.size(),
+                              hipMemcpyHostToDevice, stream));
+    if (!bt.fixes.empty())
+        PR_HIP_TRY(hipMemcpyAsync(w.fixes, bt.fixes.data(), sizeof(TileFix) * bt.fixes.size(),
+                                  hipMemcpyHostToDevice, stream));
+    int64_t grid = cus;
+    if (const char* env = std::getenv("PR_GRID"))  // tuning knob: workgroups per launch
+        if (std::atoi(env) > 0) grid = std::atoi(env);
+    if (grid > bt.n_units) grid = bt.n_units;
+    if (grid > kMaxGrid) grid = kMaxGrid;
+    bt.tile_grid = (int32_t)(grid > 0 ? grid : 1);
+    return PR_OK;
+}
+
 int check_sizes(int32_t n, int64_t nnz) {
     if (n < 1) return fail(PR_ERR_ARG, "n must be >= 1 (got %d)", n);
     if (nnz < 0 || nnz > INT32_MAX)
@@ -266,7 +543,7 @@ using namespace pr;
 
 extern "C" size_t pr_plan_workspace_bytes(int32_t n, int64_t nnz) {
     if (n < 1 || nnz < 0 || nnz > INT32_MAX) return 0;
-    return carve_ws(nullptr, n, nnz).bytes;
+    return ws_bytes_needed(n, nnz);
 }
 
 extern "C" size_t pr_plan_scratch_bytes(int32_t n, int64_t nnz) {
@@ -280,10 +557,12 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     if (!plan_out) return fail(PR_ERR_ARG, "plan_out is null");
     *plan_out = nullptr;
     PR_TRY(check_sizes(n, nnz));
-    if (flags & ~PR_VALIDATE) return fail(PR_ERR_ARG, "unknown flags 0x%x", flags);
+    if (flags & ~(PR_VALIDATE | PR_PLAN_BUCKETED))
+        return fail(PR_ERR_ARG, "unknown flags 0x%x", flags);
     if (!out_rp || !ws || !scratch || (nnz > 0 && !out_ci))
         return fail(PR_ERR_ARG, "null pointer argument");
-    PlanWs w = carve_ws(ws, n, nnz);
+    const bool tiled = !(flags & PR_PLAN_BUCKETED);
+    PlanWs w = carve_ws(ws, n, nnz, tiled);
     if (ws_bytes < w.bytes || (reinterpret_cast<uintptr_t>(ws) & 255u))
         return fail(PR_ERR_WORKSPACE, "plan workspace needs %zu bytes at 256-byte alignment (got %zu)",
                     w.bytes, ws_bytes);
@@ -329,18 +608,17 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     k_order<<<grid_for(n), kBlock, 0, stream>>>(s.old_of, out_rp, n, w.new_id, s.deg, w.inv_out);
     PR_LAUNCHED("order");
 
-    // 2. The plan's in-edge CSR: transpose of the out-edge CSR in plan order.
+    // 2. The out-edge CSR in plan order (and each edge's source).
     PR_TRY(scan_exclusive(s.deg, reinterpret_cast<uint32_t*>(s.perm_rp), n, s.vsort.scan_ws,
                           stream));
     if (nnz > 0) {
         const int64_t blocks = ceil_div(nnz, kBlock * kPermItems);
         k_permute_rows<<<dim3((unsigned)blocks), kBlock, 0, stream>>>(
-            s.perm_rp, s.old_of, w.new_id, out_rp, out_ci, n, nnz, s.perm_ci);
+            s.perm_rp, s.old_of, w.new_id, out_rp, out_ci, n, nnz, s.perm_ci, s.src_of);
         PR_LAUNCHED("permute rows");
     }
-    PR_TRY(transpose_device(n, nnz, s.perm_rp, s.perm_ci, w.in_rp, w.in_ci, s.tr, stream));
 
-    // 3. Bucket ranges (hub bucket first) and the hub rows' lengths.
+    // 3. Bucket ranges (hub bucket first).
     unsigned long long stats[2 * kNumBuckets];
     PR_HIP_TRY(hipMemcpyAsync(stats, s.stats, sizeof stats, hipMemcpyDeviceToHost, stream));
     PR_HIP_TRY(hipStreamSynchronize(stream));
@@ -353,74 +631,14 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
         }
         row_begin[kNumBuckets] = (int32_t)r;  // == n
     }
-    const int32_t n_hub = (int32_t)stats[kHubBucket];
-    std::vector<int32_t> hub_rp((size_t)n_hub + 1);
-    PR_HIP_TRY(hipMemcpyAsync(hub_rp.data(), w.in_rp, sizeof(int32_t) * hub_rp.size(),
-                              hipMemcpyDeviceToHost, stream));
-    PR_HIP_TRY(hipStreamSynchronize(stream));
 
-    // 4. Work items: hub rows (whole, or chunks with slots), then buckets 3..0.
-    std::vector<WorkItem> hub_items;
-    std::vector<ChunkRow> chunk_rows;
-    int32_t n_slots = 0;
-    hub_items.reserve((size_t)n_hub);
-    for (int32_t r = 0; r < n_hub; ++r) {
-        const int32_t lo = hub_rp[r], hi = hub_rp[r + 1];
-        if (hi - lo <= kHubChunk) {
-            hub_items.push_back(WorkItem{kHubBucket, lo, hi, r});
-            continue;
-        }
-        ChunkRow cr{r, n_slots, (int32_t)ceil_div(hi - lo, kHubChunk), 0};
-        for (int32_t c = 0; c < cr.count; ++c) {
-            const int32_t a = lo + c * kHubChunk;
-            const int32_t b = (hi - a) < kHubChunk ? hi : a + kHubChunk;
-            hub_items.push_back(WorkItem{kKindChunk, a, b, n_slots + c});
-        }
-        n_slots += cr.count;
-        chunk_rows.push_back(cr);
-    }
-    int32_t items_of[kNumBuckets];
-    int64_t total = (int64_t)hub_items.size();
-    for (int b = 0; b < kHubBucket; ++b) {
-        const int64_t bc = (int64_t)stats[kNumBuckets + b] + kRowCost * (int64_t)stats[b];
-        items_of[b] = stats[b] ? (int32_t)ceil_div(bc, kItemCost) : 0;
-        total += items_of[b];
-    }
-    if (total > w.n_items_max || n_slots > w.n_slots_max ||
-        (int64_t)chunk_rows.size() > w.n_chunk_rows_max)
-        return fail(PR_ERR_ARG, "work items (%lld) exceed the planned bound (%lld)",
-                    (long long)total, (long long)w.n_items_max);
-    if (!hub_items.empty())
-        PR_HIP_TRY(hipMemcpyAsync(w.items, hub_items.data(), sizeof(WorkItem) * hub_items.size(),
-                                  hipMemcpyHostToDevice, stream));
-    if (!chunk_rows.empty())
-        PR_HIP_TRY(hipMemcpyAsync(w.chunk_rows, chunk_rows.data(),
-                                  sizeof(ChunkRow) * chunk_rows.size(), hipMemcpyHostToDevice,
-                                  stream));
-    int32_t item0 = (int32_t)hub_items.size();
-    for (int b = kHubBucket - 1; b >= 0; --b) {
-        if (items_of[b] > 0) {
-            k_bucket_items<<<grid_for(items_of[b]), kBlock, 0, stream>>>(
-                w.in_rp, row_begin[b], row_begin[b] + (int32_t)stats[b], b, items_of[b], item0,
-                w.items);
-            PR_LAUNCHED("bucket items");
-        }
-        item0 += items_of[b];
-    }
-
-    // 5. Launch shape: kIterBlocksPerCU workgroups per CU (each holds the
-    //    hot sources in LDS), fewer when there are few item batches.
-    int64_t grid = ceil_div(ceil_div(total, kBatchItems), kIterWaves);
-    if (grid > (int64_t)cus * kIterBlocksPerCU) grid = (int64_t)cus * kIterBlocksPerCU;
-    if (const char* env = std::getenv("PR_GRID"))  // tuning knob: workgroups per launch
-        if (std::atoi(env) > 0) grid = std::atoi(env);
-    if (grid > kMaxGrid / 2) grid = kMaxGrid / 2;
-    if (grid < 1) grid = 1;
-    int64_t fix_grid = ceil_div((int64_t)chunk_rows.size(), kFixBlock / kWave);
-    if (fix_grid > kMaxGrid - grid) fix_grid = kMaxGrid - grid;
-
+    Built bt{};
+    if (tiled)
+        PR_TRY(build_tiled(w, s, n, nnz, stats, row_begin, cus, stream, bt));
+    else
+        PR_TRY(build_bucketed(w, s, n, nnz, stats, row_begin, cus, stream, bt));
     if (validate) PR_TRY(read_error_word(err, stream, "pr_plan_create"));
-    PR_HIP_TRY(hipStreamSynchronize(stream));  // host item arrays must outlive the copies
+    PR_HIP_TRY(hipStreamSynchronize(stream));  // host arrays must outlive the copies
 
     pr_plan* p = static_cast<pr_plan*>(std::calloc(1, sizeof(pr_plan)));
     if (!p) return fail(PR_ERR_ARG, "out of host memory");
@@ -429,22 +647,35 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     p->nnz = nnz;
     p->new_id = w.new_id;
     p->inv_out = w.inv_out;
+    p->tiled = tiled;
     p->in_rp = w.in_rp;
     p->in_ci = w.in_ci;
     p->xi = w.xi;
     p->contrib[0] = w.contrib0;
     p->contrib[1] = w.contrib1;
     p->items = w.items;
-    p->n_items = (int32_t)total;
+    p->n_items = bt.n_items;
     p->chunk_rows = w.chunk_rows;
-    p->n_chunk_rows = (int32_t)chunk_rows.size();
+    p->n_chunk_rows = bt.n_chunk_rows;
     p->hub_part = w.hub_part;
     p->part = w.part;
     p->part_stride = w.part_stride;
-    p->n_batches = (int32_t)ceil_div(total, kBatchItems);
+    p->n_batches = (int32_t)ceil_div(bt.n_items, kBatchItems);
     p->state = w.state;
-    p->grid = (int32_t)grid;
-    p->fix_grid = (int32_t)fix_grid;
+    p->grid = bt.grid;
+    p->fix_grid = bt.fix_grid;
+    p->tile_map = bt.map;
+    p->tsrc = w.tsrc;
+    p->tdst = w.tdst;
+    p->tile_ptr = w.tile_ptr;
+    p->tiles = w.tiles;
+    p->n_tiles = bt.n_tiles;
+    p->units = w.units;
+    p->n_units = bt.n_units;
+    p->fixes = w.fixes;
+    p->n_fixes = bt.n_fixes;
+    p->partial = w.partial;
+    p->tile_grid = bt.tile_grid;
     {
         const int64_t ig = ceil_div(n, kBlock);
         p->init_grid = (int32_t)(ig < kMaxGrid ? ig : kMaxGrid);
@@ -453,10 +684,10 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
         p->bucket_min[b] = bounds.min_len[b];
         p->row_begin[b] = row_begin[b];
         p->bucket_edges[b] = (int64_t)stats[kNumBuckets + b];
-        p->bucket_items[b] = b < kHubBucket ? items_of[b] : 0;
+        p->bucket_items[b] = bt.items_of[b];
     }
     p->row_begin[kNumBuckets] = row_begin[kNumBuckets];
-    for (const WorkItem& it : hub_items) p->bucket_items[it.kind] += 1;
+    p->bucket_items[kKindChunk] = bt.items_of[kKindChunk];
 
     hipError_t e = hipEventCreate(&p->ev_begin);
     if (e == hipSuccess) e = hipEventCreate(&p->ev_end);
@@ -509,5 +740,27 @@ extern "C" int pr_plan_layout(const pr_plan* p, const int32_t** in_row_ptr,
     if (in_row_ptr) *in_row_ptr = p->in_rp;
     if (in_col_idx) *in_col_idx = p->in_ci;
     if (new_id) *new_id = p->new_id;
+    return PR_OK;
+}
+
+extern "C" int pr_plan_tiles(const pr_plan* p, const int32_t** tile_src, const uint16_t** tile_row,
+                             const int32_t** tile_ptr, int32_t* n_tiles, int32_t* row0,
+                             int32_t* rows) {
+    if (!p) return fail(PR_ERR_ARG, "plan is null");
+    if (!p->tiled) return fail(PR_ERR_ARG, "the plan was built with PR_PLAN_BUCKETED");
+    if (tile_src) *tile_src = p->tsrc;
+    if (tile_row) *tile_row = p->tdst;
+    if (tile_ptr) *tile_ptr = p->tile_ptr;
+    if (n_tiles) *n_tiles = p->n_tiles;
+    const TileMap& m = p->tile_map;
+    for (int seg = 0; seg < kTileSegments; ++seg) {
+        const int32_t last = seg + 1 < kTileSegments ? m.tile0[seg + 1] : p->n_tiles;
+        for (int32_t t = m.tile0[seg]; t < last; ++t) {
+            const int32_t r0 = m.start[seg] + ((t - m.tile0[seg]) << m.shift[seg]);
+            const int32_t span = 1 << m.shift[seg];
+            if (row0) row0[t] = r0;
+            if (rows) rows[t] = (m.start[seg + 1] - r0) < span ? m.start[seg + 1] - r0 : span;
+        }
+    }
     return PR_OK;
 }

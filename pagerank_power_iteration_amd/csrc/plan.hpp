@@ -3,7 +3,7 @@
 // launch shape of the iteration kernels.
 #pragma once
 
-#include "common.hpp"
+#include "radix.hpp"
 
 namespace pr {
 
@@ -83,14 +83,63 @@ constexpr int kFixBlock = 256;
 // The finalize kernel runs as one workgroup of this many lanes.
 constexpr int kFinalBlock = 1024;
 
+// ------------------------------------------------------------ tiled pull
+//
+// The default iteration.  Rows are cut into tiles: blocks of consecutive plan
+// ids inside one degree bucket, 2^k rows each, k chosen per bucket so that a
+// tile holds about kTileTargetEdges in-edges (hub tiles are a few hundred
+// rows, light tiles kTileMaxRows).  A tile's in-edges are stored grouped by
+// tile and, inside a tile, by increasing source, as (source id, row offset in
+// the tile) pairs.  A workgroup streams a tile's edges in that order, so
+// consecutive lanes read neighbouring contributions (coalesced), and adds
+// each one into the row's accumulator in LDS.  Accumulators are 64-bit fixed
+// point (contribution * 2^shift, truncated): integer addition is exact and
+// order-free, so the sums do not depend on scheduling.  A tile with more than
+// kUnitEdges edges is cut into units; each unit writes its accumulators to a
+// slot of `partial`, and k_tilefix adds a tile's slots and applies the
+// update.
+constexpr int32_t kTileMaxRows = 16384;         // 128 KB of accumulators
+constexpr int32_t kTileMinRows = 64;
+constexpr int64_t kTileTargetEdges = 1 << 20;
+constexpr int64_t kUnitEdges = 1 << 18;
+constexpr int kFxShiftMax = 56;                 // 2^-56 resolution when sum|x| <= 1
+
+static_assert(kTileSegments == kNumBuckets, "one tile segment per degree bucket");
+
+struct Tile {
+    int32_t row0;
+    int32_t rows;
+};
+
+// A unit of k_tile: edges [e0, e1) of one tile.  slot < 0: the unit is the
+// whole tile and applies the update; otherwise its accumulators go to
+// partial[slot, slot + rows).
+struct TileUnit {
+    int32_t tile;
+    int32_t e0;
+    int32_t e1;
+    int32_t slot;
+};
+
+// A tile cut into units: k_tilefix adds partial[first + j*rows + r] over
+// j < count for each of its rows.
+struct TileFix {
+    int32_t row0;
+    int32_t rows;
+    int32_t first;
+    int32_t count;
+};
+
 // Device-resident run state.  Written by the finalize and init kernels, read
 // by the next launches (kernel boundaries order the accesses); the queue
-// heads are incremented atomically by k_iterate.
+// heads are incremented atomically by the iteration kernels.
 struct RunState {
-    double dmass;   // D of the vector the next iteration starts from
-    int32_t stop;   // 1 once an iteration met the tolerance
-    int32_t iters;  // that iteration's number
-    uint32_t pad[60];
+    double dmass;     // D of the vector the next iteration starts from
+    double fx_scale;  // 2^fx_shift: contribution -> fixed point (tiled pull)
+    double fx_unit;   // 2^-fx_shift
+    int32_t stop;     // 1 once an iteration met the tolerance
+    int32_t iters;    // that iteration's number
+    uint32_t pad[56];
     uint32_t queue[kQueues][64];  // queue heads at [q][0]
 };
 
@@ -109,6 +158,7 @@ struct pr_plan {
     int device;
     int32_t n;
     int64_t nnz;
+    bool tiled;            // tiled pull (default) or bucketed pull (PR_PLAN_BUCKETED)
     // plan order: vertex v of the caller sits at p = new_id[v]; rows of bucket
     // b are the plan ids [row_begin[b], row_begin[b+1]), hub rows first
     const int32_t* new_id;
@@ -134,6 +184,19 @@ struct pr_plan {
     int32_t row_begin[pr::kNumBuckets + 1];  // plan ids, hub bucket first
     int64_t bucket_edges[pr::kNumBuckets];
     int32_t bucket_items[pr::kNumBuckets + 1];  // kinds 0..5
+    // tiled pull
+    pr::TileMap tile_map;
+    const int32_t* tsrc;    // [nnz] source of each tile edge
+    const uint16_t* tdst;   // [nnz] its row offset in the tile
+    const int32_t* tile_ptr;  // [n_tiles + 1] first edge of each tile
+    const pr::Tile* tiles;
+    int32_t n_tiles;
+    const pr::TileUnit* units;
+    int32_t n_units;
+    const pr::TileFix* fixes;
+    int32_t n_fixes;
+    long long* partial;
+    int32_t tile_grid;
     hipEvent_t ev_begin, ev_end;
     hipEvent_t kernel_ev[2][pr::kTimedLaunches];  // around k_iterate launches
     int32_t kernel_timed;                         // pairs the last run recorded

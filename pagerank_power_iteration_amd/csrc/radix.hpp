@@ -33,7 +33,31 @@ enum RadixMode : int {
     kFromKeys = 2,
     // Keys only, first pass: key = target id out_col_idx[i] (range-checked).
     kFromTargets = 3,
+    // Tile of each edge: key = tile_of(keys[i]) (keys are plan ids, valid by
+    // construction), value = i.
+    kFromTileKeys = 4,
 };
+
+// Tiles of the plan: consecutive plan-id segments (one per degree bucket,
+// hub bucket first), each cut into blocks of 2^shift rows.
+constexpr int kTileSegments = 5;
+struct TileMap {
+    int32_t start[kTileSegments + 1];  // first plan id of each segment; [kTileSegments] = n
+    int32_t tile0[kTileSegments];      // first tile of each segment
+    int32_t shift[kTileSegments];      // log2 of the segment's rows per tile
+};
+
+__host__ __device__ inline int tile_segment(const TileMap& m, int32_t v) {
+    int s = 0;
+#pragma unroll
+    for (int j = 1; j < kTileSegments; ++j) s += (v >= m.start[j]) ? 1 : 0;
+    return s;
+}
+
+__host__ __device__ inline int32_t tile_of(const TileMap& m, int32_t v) {
+    const int s = tile_segment(m, v);
+    return m.tile0[s] + ((v - m.start[s]) >> m.shift[s]);
+}
 
 struct RadixIn {
     int64_t count;                 // elements
@@ -41,6 +65,7 @@ struct RadixIn {
     const int32_t* keys;           // kFromOutCsr: out_col_idx; kFromPairs, kFromKeys: keys
     const int32_t* vals;           // kFromPairs
     const int32_t* row_ptr;        // kFromOutCsr: out_row_ptr
+    TileMap tiles;                 // kFromTileKeys
     uint32_t* error;               // set to 1 when an input index is out of range
 };
 
@@ -68,6 +93,8 @@ __device__ __forceinline__ int32_t radix_key(const RadixIn& in, int64_t i) {
             k = k < 0 ? 0 : in.n - 1;
         }
         return k;
+    } else if (MODE == kFromTileKeys) {
+        return tile_of(in.tiles, in.keys[i]);
     } else {
         return in.keys[i];
     }
@@ -139,7 +166,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
             else if (MODE == kFromPairs)
                 v = in.vals[g];
             else
-                v = (int32_t)g;  // kFromKeys: the index itself
+                v = (int32_t)g;  // kFromKeys, kFromTileKeys: the index itself
         }
         const uint32_t dg = ((uint32_t)k >> shift) & (kRadixDigits - 1);
         uint64_t peers = __ballot(valid);

@@ -326,6 +326,167 @@ __global__ __launch_bounds__(kFixBlock) void k_hubfix(FixArgs f) {
 
 constexpr int kFinalWaves = kFinalBlock / kWave;
 
+// ------------------------------------------------------------ tiled pull
+
+constexpr int kTileBlock = 1024;
+constexpr int kTileWaves = kTileBlock / kWave;
+constexpr int kTileU = 8;  // edges per lane per round
+
+struct TileArgs {
+    const int32_t* __restrict__ tsrc;
+    const uint16_t* __restrict__ tdst;
+    const Tile* __restrict__ tiles;
+    const TileUnit* __restrict__ units;
+    const float* __restrict__ inv_out;
+    const float* __restrict__ contrib_in;
+    float* __restrict__ contrib_out;
+    float* __restrict__ xi;
+    long long* __restrict__ partial;
+    float* __restrict__ part;  // [3][stride]: per-unit sums
+    int64_t stride;
+    RunState* state;
+    double d;
+    int32_t n;
+    int32_t n_units;
+};
+
+// Fixed point of one contribution (truncated toward zero; the scale leaves
+// the row sums of the run well inside 64 bits).
+__device__ __forceinline__ unsigned long long to_fixed(float c, double scale) {
+    return (unsigned long long)(long long)((double)c * scale);
+}
+
+// Adds the contributions of tile edges [e0, e1) into acc[row offset].  The
+// workgroup's lanes take consecutive edges (so the sources a load
+// instruction reads are neighbours), kTileU per lane per round, and the next
+// round's edges are loaded while this round's contributions are gathered and
+// added.  The edge arrays are streamed once per iteration: non-temporal.
+__device__ __forceinline__ void accumulate(const TileArgs& a, int64_t e0, int64_t e1,
+                                           double scale, unsigned long long* acc) {
+    constexpr int64_t kStep = (int64_t)kTileBlock * kTileU;
+    int32_t sn[kTileU];
+    uint16_t dn[kTileU];
+    int64_t e = e0 + threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kTileU; ++j) {
+        const int64_t q = e + (int64_t)j * kTileBlock;
+        sn[j] = q < e1 ? __builtin_nontemporal_load(a.tsrc + q) : -1;
+        dn[j] = q < e1 ? __builtin_nontemporal_load(a.tdst + q) : (uint16_t)0;
+    }
+    for (; e < e1; e += kStep) {
+        int32_t sc[kTileU];
+        uint16_t dc[kTileU];
+#pragma unroll
+        for (int j = 0; j < kTileU; ++j) {
+            sc[j] = sn[j];
+            dc[j] = dn[j];
+        }
+#pragma unroll
+        for (int j = 0; j < kTileU; ++j) {
+            const int64_t q = e + kStep + (int64_t)j * kTileBlock;
+            sn[j] = q < e1 ? __builtin_nontemporal_load(a.tsrc + q) : -1;
+            dn[j] = q < e1 ? __builtin_nontemporal_load(a.tdst + q) : (uint16_t)0;
+        }
+        float v[kTileU];
+#pragma unroll
+        for (int j = 0; j < kTileU; ++j) v[j] = sc[j] >= 0 ? a.contrib_in[sc[j]] : 0.f;
+#pragma unroll
+        for (int j = 0; j < kTileU; ++j)
+            if (sc[j] >= 0) atomicAdd(&acc[dc[j]], to_fixed(v[j], scale));
+    }
+}
+
+// One workgroup per CU; workgroups take units from queue 0 until it is empty.
+// A whole-tile unit applies the update to its rows and writes its three sums;
+// a unit of a cut tile writes its accumulators to its slot (and zero sums).
+__global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
+    __shared__ unsigned long long acc[kTileMaxRows];
+    __shared__ float red[kTileWaves];
+    __shared__ int32_t s_unit;
+    RunState* st = a.state;
+    if (st->stop) return;  // an earlier iteration met the tolerance
+    const Damp k = make_damp(a.d, a.n, st->dmass);
+    const double scale = st->fx_scale, unit = st->fx_unit;
+    if (threadIdx.x == 0) s_unit = (int32_t)atomicAdd(&st->queue[0][0], 1u);
+    __syncthreads();
+    int32_t cur = s_unit;
+    while (cur < a.n_units) {
+        uint32_t next = 0;
+        if (threadIdx.x == 0) next = atomicAdd(&st->queue[0][0], 1u);  // answer needed at the end
+        const TileUnit u = a.units[cur];
+        const Tile t = a.tiles[u.tile];
+        for (int32_t r = threadIdx.x; r < t.rows; r += kTileBlock) acc[r] = 0ull;
+        __syncthreads();
+        accumulate(a, u.e0, u.e1, scale, acc);
+        __syncthreads();
+        Acc sums;
+        if (u.slot < 0) {
+            for (int32_t r = threadIdx.x; r < t.rows; r += kTileBlock) {
+                const float y = (float)((double)(long long)acc[r] * unit);
+                update(a.xi, a.inv_out, a.contrib_out, t.row0 + r, y, k, sums);
+            }
+        } else {
+            for (int32_t r = threadIdx.x; r < t.rows; r += kTileBlock)
+                a.partial[(int64_t)u.slot + r] = (long long)acc[r];
+        }
+        const float l1 = wide_block_sum<float, kTileWaves>(sums.l1, red);
+        const float dg = wide_block_sum<float, kTileWaves>(sums.dang, red);
+        const float sm = wide_block_sum<float, kTileWaves>(sums.sum, red);
+        if (threadIdx.x == 0) {
+            a.part[cur] = l1;
+            a.part[a.stride + cur] = dg;
+            a.part[2 * a.stride + cur] = sm;
+            s_unit = (int32_t)next;
+        }
+        __syncthreads();
+        cur = s_unit;
+    }
+}
+
+struct TileFixArgs {
+    const TileFix* __restrict__ fixes;
+    const long long* __restrict__ partial;
+    const float* __restrict__ inv_out;
+    float* __restrict__ contrib_out;
+    float* __restrict__ xi;
+    float* __restrict__ part;  // this kernel's sums go to [part0, part0 + gridDim.x)
+    int64_t stride;
+    RunState* state;
+    double d;
+    int32_t n;
+    int32_t n_fixes;
+    int32_t part0;
+};
+
+// Rows of the tiles cut into units: each row adds its slots in unit order
+// (exact integer sums) and applies the update.  Workgroup b takes fixes b,
+// b + gridDim.x, ...
+__global__ __launch_bounds__(kFixBlock) void k_tilefix(TileFixArgs f) {
+    __shared__ float red[kFixBlock / kWave];
+    RunState* st = f.state;
+    if (st->stop) return;
+    const Damp k = make_damp(f.d, f.n, st->dmass);
+    const double unit = st->fx_unit;
+    Acc sums;
+    for (int32_t i = blockIdx.x; i < f.n_fixes; i += gridDim.x) {
+        const TileFix fx = f.fixes[i];
+        for (int32_t r = threadIdx.x; r < fx.rows; r += kFixBlock) {
+            long long y = 0;
+            for (int32_t j = 0; j < fx.count; ++j)
+                y += f.partial[(int64_t)fx.first + (int64_t)j * fx.rows + r];
+            update(f.xi, f.inv_out, f.contrib_out, fx.row0 + r, (float)((double)y * unit), k, sums);
+        }
+    }
+    const float l1 = wide_block_sum<float, kFixBlock / kWave>(sums.l1, red);
+    const float dg = wide_block_sum<float, kFixBlock / kWave>(sums.dang, red);
+    const float sm = wide_block_sum<float, kFixBlock / kWave>(sums.sum, red);
+    if (threadIdx.x == 0) {
+        f.part[f.part0 + blockIdx.x] = l1;
+        f.part[f.stride + f.part0 + blockIdx.x] = dg;
+        f.part[2 * f.stride + f.part0 + blockIdx.x] = sm;
+    }
+}
+
 struct FinArgs {
     const float* __restrict__ part;
     int64_t stride;
@@ -339,7 +500,7 @@ struct FinArgs {
 
 // One workgroup of kFinalBlock lanes.  After iteration t: reduce every sum,
 // record the trace and the next D, test the tolerance, and reset the work
-// queues.  After k_init (t = 0): only D and the queues.
+// queues.  After k_init (t = 0): D, the fixed-point scale and the queues.
 __global__ __launch_bounds__(kFinalBlock) void k_finalize(FinArgs f) {
     __shared__ double redd[kFinalWaves];
     RunState* st = f.state;
@@ -373,6 +534,16 @@ __global__ __launch_bounds__(kFinalBlock) void k_finalize(FinArgs f) {
         if (f.t == 0) {
             st->stop = 0;
             st->iters = 0;
+            // Fixed-point scale of the tiled pull: every row sum of every
+            // iteration is bounded by max(1, sum |x0|) (the update does not
+            // grow the L1 norm beyond it), so 2^shift times that stays below
+            // 2^61.
+            int ex = 0;
+            (void)frexp(r0 > 1.0 ? r0 : 1.0, &ex);
+            int shift = 61 - ex;
+            shift = shift > kFxShiftMax ? kFxShiftMax : (shift < 0 ? 0 : shift);
+            st->fx_scale = ldexp(1.0, shift);
+            st->fx_unit = ldexp(1.0, -shift);
         } else {
             f.l1_trace[f.t - 1] = (float)r0;
             if (f.sum_trace) f.sum_trace[f.t - 1] = (float)r2;
@@ -385,7 +556,7 @@ __global__ __launch_bounds__(kFinalBlock) void k_finalize(FinArgs f) {
 }
 
 // Start vector in plan order (the caller's x0, or 1/n), the first contrib,
-// and per-workgroup dangling mass and sum.
+// and per-workgroup sum of |x0|, dangling mass and sum.
 __global__ __launch_bounds__(kBlock) void k_init(const int32_t* __restrict__ new_id,
                                                  const float* __restrict__ inv_out,
                                                  const float* __restrict__ x,
@@ -403,13 +574,15 @@ __global__ __launch_bounds__(kBlock) void k_init(const int32_t* __restrict__ new
         xi[p] = xv;
         const float io = inv_out[p];
         contrib[p] = xv * io;
+        acc.l1 += fabsf(xv);
         acc.dang += (io == 0.f) ? xv : 0.f;
         acc.sum += xv;
     }
+    const float l1 = block_sum(acc.l1, red);
     const float dg = block_sum(acc.dang, red);
     const float sm = block_sum(acc.sum, red);
     if (threadIdx.x == 0) {
-        part[blockIdx.x] = 0.f;
+        part[blockIdx.x] = l1;
         part[stride + blockIdx.x] = dg;
         part[2 * stride + blockIdx.x] = sm;
     }
@@ -467,7 +640,8 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     f.t = 0;
     k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
     PR_LAUNCHED("init finalize");
-    f.parts = p->n_batches + p->fix_grid;
+    const int32_t tilefix_grid = p->n_fixes < kMaxGrid ? p->n_fixes : kMaxGrid;
+    f.parts = p->tiled ? p->n_units + tilefix_grid : p->n_batches + p->fix_grid;
 
     IterArgs a{};
     a.in_rp = p->in_rp;
@@ -497,6 +671,34 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     fx.n_chunk_rows = p->n_chunk_rows;
     fx.part0 = p->n_batches;
 
+    TileArgs ta{};
+    ta.tsrc = p->tsrc;
+    ta.tdst = p->tdst;
+    ta.tiles = p->tiles;
+    ta.units = p->units;
+    ta.inv_out = p->inv_out;
+    ta.xi = p->xi;
+    ta.partial = p->partial;
+    ta.part = p->part;
+    ta.stride = p->part_stride;
+    ta.state = p->state;
+    ta.d = d;
+    ta.n = p->n;
+    ta.n_units = p->n_units;
+
+    TileFixArgs tf{};
+    tf.fixes = p->fixes;
+    tf.partial = p->partial;
+    tf.inv_out = p->inv_out;
+    tf.xi = p->xi;
+    tf.part = p->part;
+    tf.stride = p->part_stride;
+    tf.state = p->state;
+    tf.d = d;
+    tf.n = p->n;
+    tf.n_fixes = p->n_fixes;
+    tf.part0 = p->n_units;
+
     const bool record = flags & PR_RECORD_EVENTS;
     p->events_recorded = false;
     p->kernel_timed = 0;
@@ -507,13 +709,25 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         a.contrib_out = p->contrib[t & 1];
         const bool timed = record && t <= kTimedLaunches;
         if (timed) PR_HIP_TRY(hipEventRecord(p->kernel_ev[0][t - 1], stream));
-        k_iterate<<<dim3((unsigned)p->grid), kIterBlock, 0, stream>>>(a);
-        PR_LAUNCHED("iterate");
+        if (p->tiled) {
+            ta.contrib_in = a.contrib_in;
+            ta.contrib_out = a.contrib_out;
+            k_tile<<<dim3((unsigned)p->tile_grid), kTileBlock, 0, stream>>>(ta);
+            PR_LAUNCHED("tile");
+        } else {
+            k_iterate<<<dim3((unsigned)p->grid), kIterBlock, 0, stream>>>(a);
+            PR_LAUNCHED("iterate");
+        }
         if (timed) {
             PR_HIP_TRY(hipEventRecord(p->kernel_ev[1][t - 1], stream));
             p->kernel_timed = t;
         }
-        if (p->fix_grid > 0) {
+        if (p->tiled && tilefix_grid > 0) {
+            tf.contrib_out = a.contrib_out;
+            k_tilefix<<<dim3((unsigned)tilefix_grid), kFixBlock, 0, stream>>>(tf);
+            PR_LAUNCHED("tile rows");
+        }
+        if (!p->tiled && p->fix_grid > 0) {
             fx.contrib_out = a.contrib_out;
             k_hubfix<<<dim3((unsigned)p->fix_grid), kFixBlock, 0, stream>>>(fx);
             PR_LAUNCHED("hub rows");

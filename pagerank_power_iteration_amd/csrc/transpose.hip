@@ -93,6 +93,13 @@ int transpose_device(int32_t n, int64_t nnz, const int32_t* out_rp, const int32_
     return PR_OK;
 }
 
+int rows_from_sorted(const int32_t* keys, int64_t m, int32_t n, int32_t* rp, hipStream_t stream) {
+    if (m == 0) return fill_u32(reinterpret_cast<uint32_t*>(rp), 0u, (int64_t)n + 1, stream);
+    k_rows_from_sorted<<<grid_for(m + 1), kBlock, 0, stream>>>(keys, m, n, rp);
+    PR_LAUNCHED("row pointers");
+    return PR_OK;
+}
+
 int transpose_row_ptr(int32_t n, int64_t nnz, const int32_t* out_ci, int32_t* in_rp,
                       const TransposeWs& w, hipStream_t stream) {
     if (nnz == 0) return fill_u32(reinterpret_cast<uint32_t*>(in_rp), 0u, (int64_t)n + 1, stream);

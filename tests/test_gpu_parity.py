@@ -91,12 +91,12 @@ def _renumbered(g, new_id):
 
 
 @pytest.mark.parametrize("g", SMALL, ids=lambda g: g.name)
-def test_plan_layout(prx, g):
-    """The plan renumbers vertices as documented and holds the oracle's
+def test_plan_layout_bucketed(prx, g):
+    """Bucketed plans renumber vertices as documented and hold the oracle's
     transpose of the renumbered graph, bit for bit; every bucket is one
     contiguous range of plan ids."""
     dg = _cases.gpu_graph(g)
-    plan = prx.Plan(dg, flags=prx.PR_VALIDATE)
+    plan = prx.Plan(dg, flags=prx.PR_VALIDATE | prx.PR_PLAN_BUCKETED)
     rp, ci, nid = (_cases.to_np(t) for t in plan.layout())
     buckets = plan.buckets()
     order, new_id = _expected_plan_order(g, [b["min_len"] for b in buckets])
@@ -116,9 +116,50 @@ def test_plan_layout(prx, g):
 
 
 @pytest.mark.parametrize("g", SMALL, ids=lambda g: g.name)
-def test_pagerank_parity_small(prx, g):
+def test_plan_layout_tiled(prx, g):
+    """Tiled plans: the same renumbering; tiles are consecutive row blocks
+    that never straddle a bucket; and the tile edge arrays are the renumbered
+    edges sorted by tile, stably from source order, as (source, row offset)
+    pairs -- all bit for bit against that definition evaluated here."""
+    dg = _cases.gpu_graph(g)
+    plan = prx.Plan(dg, flags=prx.PR_VALIDATE)
+    assert plan.layout()[0] is None
+    nid = _cases.to_np(plan.layout()[2])
+    buckets = plan.buckets()
+    _, new_id = _expected_plan_order(g, [b["min_len"] for b in buckets])
+    np.testing.assert_array_equal(nid, new_id)
+    tsrc, trow, tptr, row0, rows = plan.tiles()
+    nt = row0.size
+    assert row0[0] == 0 and np.all(rows >= 1) and int(rows.sum()) == g.n
+    np.testing.assert_array_equal(row0[1:], (row0 + rows)[:-1])
+    bounds = np.cumsum([0] + [buckets[b]["rows"] for b in reversed(range(len(buckets)))])
+    seg_first = np.searchsorted(bounds, row0, side="right")
+    seg_last = np.searchsorted(bounds, row0 + rows - 1, side="right")
+    np.testing.assert_array_equal(seg_first, seg_last)  # inside one bucket
+    rp, ci = _renumbered(g, new_id)
+    src = np.repeat(np.arange(g.n), np.diff(rp))
+    tile_of_row = np.repeat(np.arange(nt), rows)
+    key = tile_of_row[ci]
+    o = np.argsort(key, kind="stable")
+    np.testing.assert_array_equal(_cases.to_np(tsrc), src[o])
+    np.testing.assert_array_equal(_cases.to_np(trow).astype(np.int64) & 0xFFFF,
+                                  ci[o] - row0[key[o]])
+    np.testing.assert_array_equal(_cases.to_np(tptr),
+                                  np.searchsorted(key[o], np.arange(nt + 1), side="left"))
+
+
+MODES = [0, "bucketed"]
+
+
+def _flags(prx, mode):
+    return prx.PR_PLAN_BUCKETED if mode == "bucketed" else 0
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["tiled", "bucketed"])
+@pytest.mark.parametrize("g", SMALL, ids=lambda g: g.name)
+def test_pagerank_parity_small(prx, g, mode):
     """100 fixed iterations on both sides (the Day 40 correctness protocol)."""
-    plan = prx.Plan(_cases.gpu_graph(g), flags=prx.PR_VALIDATE)
+    plan = prx.Plan(_cases.gpu_graph(g), flags=prx.PR_VALIDATE | _flags(prx, mode))
     res = plan.run(d=D, tol=0.0, max_iter=100)
     torch.cuda.synchronize()
     ref = oracle.pagerank(g.row_ptr, g.col_idx, d=D, max_iter=100)
@@ -144,12 +185,14 @@ def _hubs_graph(n_leaves: int, n_hubs: int, seed: int):
     return graphgen.from_edges(n, np.concatenate(src), np.concatenate(dst))
 
 
+@pytest.mark.parametrize("mode", MODES, ids=["tiled", "bucketed"])
 @pytest.mark.parametrize("n_leaves,n_hubs", [(70_000, 1), (140_001, 3)])
-def test_chunked_hub_rows(prx, n_leaves, n_hubs):
-    """Hub rows longer than one work chunk are summed in pieces and finished
-    by the reduction kernel; they must match the oracle like any other row."""
+def test_chunked_hub_rows(prx, n_leaves, n_hubs, mode):
+    """Rows or tiles too long for one work unit are summed in pieces and
+    finished by a second kernel (hub rows of 70K and 140K in-edges; a tile
+    of 420K edges); they must match the oracle like any other row."""
     g = _hubs_graph(n_leaves, n_hubs, seed=n_leaves)
-    plan = prx.Plan(_cases.gpu_graph(g), flags=prx.PR_VALIDATE)
+    plan = prx.Plan(_cases.gpu_graph(g), flags=prx.PR_VALIDATE | _flags(prx, mode))
     res = plan.run(d=D, tol=0.0, max_iter=40)
     torch.cuda.synchronize()
     ref = oracle.pagerank(g.row_ptr, g.col_idx, d=D, max_iter=40)
@@ -169,12 +212,13 @@ def test_damping_extremes(prx, d):
     assert abs(x.sum() - 1) <= 1e-5
 
 
-def test_tolerance_mode_citation(prx):
+@pytest.mark.parametrize("mode", MODES, ids=["tiled", "bucketed"])
+def test_tolerance_mode_citation(prx, mode):
     """Stop after the first iteration with L1 < 1e-6; the oracle with the same
     tolerance stops within one iteration of it, and the GPU vector matches
     the oracle's at the GPU's count."""
     g = _cases.workload("citation")
-    plan = prx.Plan(_cases.gpu_graph(g))
+    plan = prx.Plan(_cases.gpu_graph(g), flags=_flags(prx, mode))
     res = plan.run(d=D, tol=1e-6, max_iter=200)
     l1 = _cases.to_np(res.l1_trace)
     assert l1[-1] < 1e-6 and np.all(l1[:-1] >= 1e-6)
@@ -194,10 +238,11 @@ def test_tolerance_mode_respects_max_iter(prx):
                          _cases.to_np(res.sum_trace), ref)
 
 
-def test_warm_start_resumes(prx):
+@pytest.mark.parametrize("mode", MODES, ids=["tiled", "bucketed"])
+def test_warm_start_resumes(prx, mode):
     """x0 = the vector after 20 iterations; 30 more equal 50 from scratch."""
     g = graphgen.rmat(13)
-    plan = prx.Plan(_cases.gpu_graph(g))
+    plan = prx.Plan(_cases.gpu_graph(g), flags=_flags(prx, mode))
     first = plan.run(max_iter=20)
     x20 = first.x.clone()
     resumed = plan.run(max_iter=30, x0=x20)
@@ -210,9 +255,10 @@ def test_warm_start_resumes(prx):
     assert np.abs(_cases.to_np(resumed.l1_trace) - ref_tail.l1_trace).max() <= 2e-5
 
 
-def test_runs_are_bit_identical(prx):
+@pytest.mark.parametrize("mode", MODES, ids=["tiled", "bucketed"])
+def test_runs_are_bit_identical(prx, mode):
     g = graphgen.rmat(15)
-    plan = prx.Plan(_cases.gpu_graph(g))
+    plan = prx.Plan(_cases.gpu_graph(g), flags=_flags(prx, mode))
     a = plan.run(max_iter=25).x.clone()
     b = plan.run(max_iter=25).x.clone()
     assert torch.equal(a, b)
@@ -228,9 +274,10 @@ def test_record_events_gives_a_time(prx):
     assert launches == 10 and 0.0 < kms * launches <= ms
 
 
-def test_buckets_cover_every_row_and_edge(prx):
+@pytest.mark.parametrize("mode", MODES, ids=["tiled", "bucketed"])
+def test_buckets_cover_every_row_and_edge(prx, mode):
     g = graphgen.rmat(16)
-    plan = prx.Plan(_cases.gpu_graph(g))
+    plan = prx.Plan(_cases.gpu_graph(g), flags=_flags(prx, mode))
     b = plan.buckets()
     assert sum(x["rows"] for x in b) == g.n
     assert sum(x["edges"] for x in b) == g.m
@@ -273,11 +320,13 @@ def test_short_workspace_is_rejected(prx):
 # ------------------------------------------------- the benchmark workloads
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name,iters", [("citation", 50), ("stencil100", 50), ("rmat18", 50),
-                                        ("rmat21", 50)])
-def test_workload_parity(prx, name, iters):
-    """Full-size workloads in the benchmark's launch configuration: bit-exact
-    transpose and 50 iterations against the oracle."""
+@pytest.mark.parametrize("name,iters,mode", [("citation", 50, 0), ("stencil100", 50, 0),
+                                             ("rmat18", 50, 0), ("rmat21", 50, 0),
+                                             ("rmat21", 50, "bucketed")])
+def test_workload_parity(prx, name, iters, mode):
+    """Full-size workloads in the benchmark's launch configuration (tiled, and
+    bucketed on R-MAT 21): bit-exact transpose and 50 iterations against the
+    oracle."""
     g = _cases.workload(name)
     print(f"[{name}] n={g.n} m={g.m}", flush=True)
     dg = _cases.gpu_graph(g)
@@ -286,7 +335,7 @@ def test_workload_parity(prx, name, iters):
     assert np.array_equal(_cases.to_np(in_rp), ref_rp)
     assert np.array_equal(_cases.to_np(in_ci), ref_ci)
     del in_rp, in_ci
-    plan = prx.Plan(dg)
+    plan = prx.Plan(dg, flags=_flags(prx, mode))
     res = plan.run(d=D, max_iter=iters)
     torch.cuda.synchronize()
     ref = oracle.pagerank(g.row_ptr, g.col_idx, d=D, max_iter=iters)
