@@ -33,14 +33,14 @@ namespace {
 
 // Upper bounds of the tiled layout.
 inline int64_t max_tiles(int32_t n) { return n / kTileMinRows + kNumBuckets + 1; }
-inline int64_t max_units(int32_t n, int64_t nnz) { return max_tiles(n) + nnz / kUnitEdges + 1; }
+inline int64_t max_units(int32_t n, int64_t nnz) { return max_tiles(n) + nnz / kMinUnitEdges + 1; }
 inline int64_t max_fixes(int32_t n, int64_t nnz) {
-    const int64_t a = max_tiles(n), b = nnz / kUnitEdges + 1;
+    const int64_t a = max_tiles(n), b = nnz / kMinUnitEdges + 1;
     return a < b ? a : b;
 }
-// A tile cut into c > 1 units has more than (c-1)*kUnitEdges edges, so the
-// slots of all cut tiles hold at most 2*nnz/kUnitEdges tiles' worth of rows.
-inline int64_t max_partial(int64_t nnz) { return 2 * (nnz / kUnitEdges + 1) * kTileMaxRows; }
+// A tile cut into c > 1 units has more than (c-1)*unit edges, so the slots of
+// all cut tiles hold at most 2*nnz/unit tiles' worth of rows.
+inline int64_t max_partial(int64_t nnz) { return 2 * (nnz / kMinUnitEdges + 1) * kTileMaxRows; }
 
 struct PlanWs {  // lives as long as the plan
     float* inv_out;
@@ -65,6 +65,7 @@ struct PlanWs {  // lives as long as the plan
     Tile* tiles;
     TileUnit* units;
     TileFix* fixes;
+    int32_t* fix_rows;
     long long* partial;
     int64_t n_tiles_max, n_units_max, n_fixes_max, n_partial_max;
     size_t bytes;
@@ -118,6 +119,7 @@ PlanWs carve_ws(void* base, int32_t n, int64_t nnz, bool tiled) {
         w.tiles = c.take<Tile>((size_t)w.n_tiles_max);
         w.units = c.take<TileUnit>((size_t)w.n_units_max);
         w.fixes = c.take<TileFix>((size_t)w.n_fixes_max);
+        w.fix_rows = c.take<int32_t>((size_t)w.n_fixes_max + 1);
         w.partial = c.take<long long>((size_t)w.n_partial_max);
     }
     w.bytes = c.used;
@@ -341,6 +343,7 @@ struct Built {
     std::vector<Tile> tiles;
     std::vector<TileUnit> units;
     std::vector<TileFix> fixes;
+    std::vector<int32_t> fix_rows;
 };
 
 // Bucketed pull: the plan's in-edge CSR (counting-sort transpose of the
@@ -435,12 +438,18 @@ int log2_ceil(int64_t x) {
 int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
                 const unsigned long long* stats, const int32_t* row_begin, int cus,
                 hipStream_t stream, Built& bt) {
+    // tuning knobs: edges per tile (target) and per unit (at least kMinUnitEdges)
+    int64_t target = kTileTargetEdges, unit_edges = kUnitEdges;
+    if (const char* env = std::getenv("PR_TILE_EDGES"))
+        if (std::atoll(env) > 0) target = std::atoll(env);
+    if (const char* env = std::getenv("PR_UNIT_EDGES"))
+        if (std::atoll(env) >= kMinUnitEdges) unit_edges = std::atoll(env);
     TileMap& map = bt.map;
     int32_t tiles = 0;
     for (int seg = 0; seg < kTileSegments; ++seg) {
         const int b = kHubBucket - seg;  // segment 0 = hub bucket
         const int64_t rows = (int64_t)stats[b], edges = (int64_t)stats[kNumBuckets + b];
-        int64_t want = edges > 0 ? ceil_div(kTileTargetEdges * rows, edges) : kTileMaxRows;
+        int64_t want = edges > 0 ? ceil_div(target * rows, edges) : kTileMaxRows;
         if (want < kTileMinRows) want = kTileMinRows;
         if (want > kTileMaxRows) want = kTileMaxRows;
         map.start[seg] = row_begin[b];
@@ -488,17 +497,17 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
             const int32_t rows = (end - row0) < (1 << map.shift[seg]) ? end - row0 : 1 << map.shift[seg];
             bt.tiles[(size_t)t] = Tile{row0, rows};
             const int32_t e0 = tp[(size_t)t], e1 = tp[(size_t)t + 1];
-            if ((int64_t)(e1 - e0) <= kUnitEdges) {
+            if ((int64_t)(e1 - e0) <= unit_edges) {
                 whole.push_back(TileUnit{t, e0, e1, -1});
                 continue;
             }
-            const int32_t count = (int32_t)ceil_div(e1 - e0, kUnitEdges);
+            const int32_t count = (int32_t)ceil_div(e1 - e0, unit_edges);
             if (slot + (int64_t)count * rows > w.n_partial_max)
                 return fail(PR_ERR_ARG, "tile slots exceed the planned bound");
             bt.fixes.push_back(TileFix{row0, rows, (int32_t)slot, count});
             for (int32_t j = 0; j < count; ++j) {
-                const int32_t a = e0 + (int32_t)(j * kUnitEdges);
-                const int32_t b = (e1 - a) < kUnitEdges ? e1 : a + (int32_t)kUnitEdges;
+                const int32_t a = e0 + (int32_t)(j * unit_edges);
+                const int32_t b = (e1 - a) < unit_edges ? e1 : a + (int32_t)unit_edges;
                 bt.units.push_back(TileUnit{t, a, b, (int32_t)(slot + (int64_t)j * rows)});
             }
             slot += (int64_t)count * rows;
@@ -512,6 +521,8 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
         return fail(PR_ERR_ARG, "tile units exceed the planned bound");
     bt.n_units = (int32_t)bt.units.size();
     bt.n_fixes = (int32_t)bt.fixes.size();
+    bt.fix_rows.assign(1, 0);
+    for (const TileFix& f : bt.fixes) bt.fix_rows.push_back(bt.fix_rows.back() + f.rows);
     PR_HIP_TRY(hipMemcpyAsync(w.tiles, bt.tiles.data(), sizeof(Tile) * bt.tiles.size(),
                               hipMemcpyHostToDevice, stream));
     PR_HIP_TRY(hipMemcpyAsync(w.units, bt.units.data(), sizeof(TileUnit) * bt.units.size(),
@@ -519,6 +530,8 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
     if (!bt.fixes.empty())
         PR_HIP_TRY(hipMemcpyAsync(w.fixes, bt.fixes.data(), sizeof(TileFix) * bt.fixes.size(),
                                   hipMemcpyHostToDevice, stream));
+    PR_HIP_TRY(hipMemcpyAsync(w.fix_rows, bt.fix_rows.data(), sizeof(int32_t) * bt.fix_rows.size(),
+                              hipMemcpyHostToDevice, stream));
     int64_t grid = cus;
     if (const char* env = std::getenv("PR_GRID"))  // tuning knob: workgroups per launch
         if (std::atoi(env) > 0) grid = std::atoi(env);
@@ -673,7 +686,9 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     p->units = w.units;
     p->n_units = bt.n_units;
     p->fixes = w.fixes;
+    p->fix_rows = w.fix_rows;
     p->n_fixes = bt.n_fixes;
+    p->n_fix_rows = bt.fix_rows.empty() ? 0 : bt.fix_rows.back();
     p->partial = w.partial;
     p->tile_grid = bt.tile_grid;
     {

@@ -100,8 +100,9 @@ constexpr int kFinalBlock = 1024;
 // update.
 constexpr int32_t kTileMaxRows = 16384;         // 128 KB of accumulators
 constexpr int32_t kTileMinRows = 64;
-constexpr int64_t kTileTargetEdges = 1 << 20;
-constexpr int64_t kUnitEdges = 1 << 18;
+constexpr int64_t kTileTargetEdges = 1 << 20;  // default; PR_TILE_EDGES overrides
+constexpr int64_t kUnitEdges = 1 << 18;        // default; PR_UNIT_EDGES raises it
+constexpr int64_t kMinUnitEdges = 1 << 17;     // the workspace bounds assume units this large
 constexpr int kFxShiftMax = 56;                 // 2^-56 resolution when sum|x| <= 1
 
 static_assert(kTileSegments == kNumBuckets, "one tile segment per degree bucket");
@@ -194,7 +195,9 @@ struct pr_plan {
     const pr::TileUnit* units;
     int32_t n_units;
     const pr::TileFix* fixes;
+    const int32_t* fix_rows;  // [n_fixes + 1] rows of the cut tiles before each one
     int32_t n_fixes;
+    int32_t n_fix_rows;
     long long* partial;
     int32_t tile_grid;
     hipEvent_t ev_begin, ev_end;

@@ -350,28 +350,41 @@ struct TileArgs {
     int32_t n_units;
 };
 
-// Fixed point of one contribution (truncated toward zero; the scale leaves
-// the row sums of the run well inside 64 bits).
-__device__ __forceinline__ unsigned long long to_fixed(float c, double scale) {
-    return (unsigned long long)(long long)((double)c * scale);
+// Fixed point of one contribution: |c| * 2^shift truncated toward zero, with
+// c's sign, in two's complement.  |c| * scale is exact in fp32 (scale is a
+// power of two and the product stays below 2^61), and so is its split into
+// 32-bit halves: hi = trunc(a / 2^32) has at most 24 significant bits, so
+// a - hi * 2^32 is exact too.  The result equals truncating the exact product
+// in double precision, with single-precision instructions only.
+__device__ __forceinline__ unsigned long long to_fixed(float c, float scale) {
+    const float a = fabsf(c) * scale;
+    const uint32_t hi = (uint32_t)(a * 0x1p-32f);
+    const uint32_t lo = (uint32_t)fmaf(-(float)hi, 0x1p32f, a);
+    const unsigned long long r = ((unsigned long long)hi << 32) | lo;
+    return c < 0.f ? 0ull - r : r;
 }
 
 // Adds the contributions of tile edges [e0, e1) into acc[row offset].  The
 // workgroup's lanes take consecutive edges (so the sources a load
 // instruction reads are neighbours), kTileU per lane per round, and the next
 // round's edges are loaded while this round's contributions are gathered and
-// added.  The edge arrays are streamed once per iteration: non-temporal.
+// added.  Every load is unconditional, so the compiler issues all of a
+// round's gathers before waiting for any: a lane past e1 reads the unit's
+// last edge (a valid source and row of this tile) and adds zero.  The
+// edge arrays are streamed once per iteration: non-temporal.
 __device__ __forceinline__ void accumulate(const TileArgs& a, int64_t e0, int64_t e1,
-                                           double scale, unsigned long long* acc) {
+                                           float scale, unsigned long long* acc) {
     constexpr int64_t kStep = (int64_t)kTileBlock * kTileU;
+    const int64_t last = e1 > e0 ? e1 - 1 : e0;  // in bounds: the arrays hold >= 1 entry
     int32_t sn[kTileU];
     uint16_t dn[kTileU];
     int64_t e = e0 + threadIdx.x;
 #pragma unroll
     for (int j = 0; j < kTileU; ++j) {
         const int64_t q = e + (int64_t)j * kTileBlock;
-        sn[j] = q < e1 ? __builtin_nontemporal_load(a.tsrc + q) : -1;
-        dn[j] = q < e1 ? __builtin_nontemporal_load(a.tdst + q) : (uint16_t)0;
+        const int64_t qc = q < e1 ? q : last;
+        sn[j] = __builtin_nontemporal_load(a.tsrc + qc);
+        dn[j] = __builtin_nontemporal_load(a.tdst + qc);
     }
     for (; e < e1; e += kStep) {
         int32_t sc[kTileU];
@@ -384,15 +397,18 @@ __device__ __forceinline__ void accumulate(const TileArgs& a, int64_t e0, int64_
 #pragma unroll
         for (int j = 0; j < kTileU; ++j) {
             const int64_t q = e + kStep + (int64_t)j * kTileBlock;
-            sn[j] = q < e1 ? __builtin_nontemporal_load(a.tsrc + q) : -1;
-            dn[j] = q < e1 ? __builtin_nontemporal_load(a.tdst + q) : (uint16_t)0;
+            const int64_t qc = q < e1 ? q : last;
+            sn[j] = __builtin_nontemporal_load(a.tsrc + qc);
+            dn[j] = __builtin_nontemporal_load(a.tdst + qc);
         }
         float v[kTileU];
 #pragma unroll
-        for (int j = 0; j < kTileU; ++j) v[j] = sc[j] >= 0 ? a.contrib_in[sc[j]] : 0.f;
+        for (int j = 0; j < kTileU; ++j) v[j] = a.contrib_in[sc[j]];
 #pragma unroll
-        for (int j = 0; j < kTileU; ++j)
-            if (sc[j] >= 0) atomicAdd(&acc[dc[j]], to_fixed(v[j], scale));
+        for (int j = 0; j < kTileU; ++j) {
+            const unsigned long long f = to_fixed(v[j], scale);
+            atomicAdd(&acc[dc[j]], e + (int64_t)j * kTileBlock < e1 ? f : 0ull);
+        }
     }
 }
 
@@ -406,7 +422,8 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     RunState* st = a.state;
     if (st->stop) return;  // an earlier iteration met the tolerance
     const Damp k = make_damp(a.d, a.n, st->dmass);
-    const double scale = st->fx_scale, unit = st->fx_unit;
+    const float scale = (float)st->fx_scale;  // a power of two, exact in fp32
+    const double unit = st->fx_unit;
     if (threadIdx.x == 0) s_unit = (int32_t)atomicAdd(&st->queue[0][0], 1u);
     __syncthreads();
     int32_t cur = s_unit;
@@ -445,6 +462,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
 
 struct TileFixArgs {
     const TileFix* __restrict__ fixes;
+    const int32_t* __restrict__ fix_rows;
     const long long* __restrict__ partial;
     const float* __restrict__ inv_out;
     float* __restrict__ contrib_out;
@@ -455,12 +473,14 @@ struct TileFixArgs {
     double d;
     int32_t n;
     int32_t n_fixes;
+    int32_t n_rows;  // rows of all cut tiles
     int32_t part0;
 };
 
-// Rows of the tiles cut into units: each row adds its slots in unit order
-// (exact integer sums) and applies the update.  Workgroup b takes fixes b,
-// b + gridDim.x, ...
+// Rows of the tiles cut into units, one lane per row (the cut tiles' rows
+// numbered one after another; a binary search in fix_rows finds the tile):
+// the row adds its slots in unit order (exact integer sums) and applies the
+// update.  Lane g of workgroup b takes rows b*256 + g, then + gridDim.x*256.
 __global__ __launch_bounds__(kFixBlock) void k_tilefix(TileFixArgs f) {
     __shared__ float red[kFixBlock / kWave];
     RunState* st = f.state;
@@ -468,14 +488,22 @@ __global__ __launch_bounds__(kFixBlock) void k_tilefix(TileFixArgs f) {
     const Damp k = make_damp(f.d, f.n, st->dmass);
     const double unit = st->fx_unit;
     Acc sums;
-    for (int32_t i = blockIdx.x; i < f.n_fixes; i += gridDim.x) {
-        const TileFix fx = f.fixes[i];
-        for (int32_t r = threadIdx.x; r < fx.rows; r += kFixBlock) {
-            long long y = 0;
-            for (int32_t j = 0; j < fx.count; ++j)
-                y += f.partial[(int64_t)fx.first + (int64_t)j * fx.rows + r];
-            update(f.xi, f.inv_out, f.contrib_out, fx.row0 + r, (float)((double)y * unit), k, sums);
+    for (int32_t g = blockIdx.x * kFixBlock + threadIdx.x; g < f.n_rows;
+         g += gridDim.x * kFixBlock) {
+        int32_t lo = 0, hi = f.n_fixes - 1;  // last fix with fix_rows[i] <= g
+        while (lo < hi) {
+            const int32_t mid = (lo + hi + 1) / 2;
+            if (f.fix_rows[mid] <= g)
+                lo = mid;
+            else
+                hi = mid - 1;
         }
+        const TileFix fx = f.fixes[lo];
+        const int32_t r = g - f.fix_rows[lo];
+        long long y = 0;
+        for (int32_t j = 0; j < fx.count; ++j)
+            y += f.partial[(int64_t)fx.first + (int64_t)j * fx.rows + r];
+        update(f.xi, f.inv_out, f.contrib_out, fx.row0 + r, (float)((double)y * unit), k, sums);
     }
     const float l1 = wide_block_sum<float, kFixBlock / kWave>(sums.l1, red);
     const float dg = wide_block_sum<float, kFixBlock / kWave>(sums.dang, red);
@@ -640,7 +668,8 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     f.t = 0;
     k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
     PR_LAUNCHED("init finalize");
-    const int32_t tilefix_grid = p->n_fixes < kMaxGrid ? p->n_fixes : kMaxGrid;
+    int32_t tilefix_grid = (int32_t)((p->n_fix_rows + kFixBlock - 1) / kFixBlock);
+    if (tilefix_grid > kMaxGrid) tilefix_grid = kMaxGrid;
     f.parts = p->tiled ? p->n_units + tilefix_grid : p->n_batches + p->fix_grid;
 
     IterArgs a{};
@@ -688,6 +717,8 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
 
     TileFixArgs tf{};
     tf.fixes = p->fixes;
+    tf.fix_rows = p->fix_rows;
+    tf.n_rows = p->n_fix_rows;
     tf.partial = p->partial;
     tf.inv_out = p->inv_out;
     tf.xi = p->xi;
