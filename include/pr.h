@@ -141,7 +141,9 @@ size_t pr_plan_scratch_bytes(int32_t n, int64_t nnz);
  *                              untouched while the plan lives
  *   scratch_dev, scratch_bytes >= pr_plan_scratch_bytes(n, nnz); free for other
  *                              use once the call returns
- *   flags                      PR_VALIDATE | PR_PLAN_BUCKETED
+ *   flags                      PR_VALIDATE | PR_PLAN_BUCKETED; the default
+ *                              (tiled) layout takes n <= 2^30, PR_PLAN_BUCKETED
+ *                              any n that the sizes allow
  *
  * Synchronizes `stream` (bucket sizes and the tiles' or hub rows' edge counts
  * are read back to build the work list).  The plan belongs to the device
@@ -219,11 +221,16 @@ int pr_plan_layout(const pr_plan* plan, const int32_t** in_row_ptr_dev,
                    const int32_t** in_col_idx_dev, const int32_t** new_id_dev);
 
 /* Introspection for tests, tiled plans only (PR_ERR_ARG otherwise): device
- * pointers to tile_src[nnz] (source plan id of each tile edge), tile_row[nnz]
- * (its row's offset from the tile's first row) and tile_ptr[n_tiles+1] (the
- * first tile edge of each tile); the tile count; and, into host arrays of
- * n_tiles entries, each tile's first plan id and row count.  Any output may
- * be NULL (call once with NULL arrays to learn n_tiles). */
+ * pointers to tile_src[S] (source plan id of each tile edge slot),
+ * tile_row[S] (its row's offset from the tile's first row) and
+ * tile_ptr[n_tiles+1] (the first slot of each tile; S = tile_ptr[n_tiles]);
+ * the tile count; and, into host arrays of n_tiles entries, each tile's first
+ * plan id and row count.  Slots hold a tile's edges in increasing source
+ * order, padded to a multiple of 256 (padding slots repeat the tile's last
+ * source with row offset 16384, an accumulator that is never read), and each
+ * block of 256 is stored transposed: edge 64*i + l of a block sits at slot
+ * 4*l + i.  Any output may be NULL (call once with NULL arrays to learn
+ * n_tiles). */
 int pr_plan_tiles(const pr_plan* plan, const int32_t** tile_src_dev, const uint16_t** tile_row_dev,
                   const int32_t** tile_ptr_dev, int32_t* n_tiles_host, int32_t* row0_host,
                   int32_t* rows_host);

@@ -20,8 +20,10 @@
 //     lengths).
 // The caller's x, traces and ids never change: pr_run maps x in and out.
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "plan.hpp"
@@ -41,6 +43,8 @@ inline int64_t max_fixes(int32_t n, int64_t nnz) {
 // A tile cut into c > 1 units has more than (c-1)*unit edges, so the slots of
 // all cut tiles hold at most 2*nnz/unit tiles' worth of rows.
 inline int64_t max_partial(int64_t nnz) { return 2 * (nnz / kMinUnitEdges + 1) * kTileMaxRows; }
+// Tile edge slots: every tile padded to whole blocks.
+inline int64_t max_edge_slots(int32_t n, int64_t nnz) { return nnz + (int64_t)(kEdgeBlock - 1) * max_tiles(n); }
 
 struct PlanWs {  // lives as long as the plan
     float* inv_out;
@@ -67,7 +71,7 @@ struct PlanWs {  // lives as long as the plan
     TileFix* fixes;
     int32_t* fix_rows;
     long long* partial;
-    int64_t n_tiles_max, n_units_max, n_fixes_max, n_partial_max;
+    int64_t n_tiles_max, n_units_max, n_fixes_max, n_partial_max, n_edge_slots_max;
     size_t bytes;
 };
 
@@ -97,6 +101,7 @@ PlanWs carve_ws(void* base, int32_t n, int64_t nnz, bool tiled) {
     w.n_units_max = max_units(n, nnz);
     w.n_fixes_max = max_fixes(n, nnz);
     w.n_partial_max = max_partial(nnz);
+    w.n_edge_slots_max = max_edge_slots(n, nnz);
     w.inv_out = c.take<float>((size_t)n);
     w.new_id = c.take<int32_t>((size_t)n);
     w.xi = c.take<float>((size_t)n);
@@ -113,8 +118,8 @@ PlanWs carve_ws(void* base, int32_t n, int64_t nnz, bool tiled) {
         w.chunk_rows = c.take<ChunkRow>((size_t)w.n_chunk_rows_max);
         w.hub_part = c.take<float>((size_t)w.n_slots_max);
     } else {
-        w.tsrc = c.take<int32_t>((size_t)nnz);
-        w.tdst = c.take<uint16_t>((size_t)nnz);
+        w.tsrc = c.take<int32_t>((size_t)w.n_edge_slots_max);
+        w.tdst = c.take<uint16_t>((size_t)w.n_edge_slots_max);
         w.tile_ptr = c.take<int32_t>((size_t)w.n_tiles_max + 1);
         w.tiles = c.take<Tile>((size_t)w.n_tiles_max);
         w.units = c.take<TileUnit>((size_t)w.n_units_max);
@@ -258,19 +263,67 @@ __device__ __forceinline__ int32_t tile_row0(const TileMap& m, int32_t t) {
 }
 
 // The tile edge arrays: position i of the tile-sorted order holds edge
-// order[i] of the renumbered out-edge CSR; its source and its row offset in
-// its tile (key[i]).
+// order[i] of the renumbered out-edge CSR, edge i - first[t] of its tile t =
+// key[i]; it goes to slot slot0[t] + block_slot(i - first[t]) with its source
+// and its row offset in the tile.
 __global__ __launch_bounds__(kBlock) void k_tile_edges(const int32_t* __restrict__ order,
                                                        const int32_t* __restrict__ key,
                                                        const int32_t* __restrict__ src_of,
                                                        const int32_t* __restrict__ perm_ci,
                                                        int64_t nnz, TileMap map,
+                                                       const int32_t* __restrict__ first,
+                                                       const int32_t* __restrict__ slot0,
                                                        int32_t* __restrict__ tsrc,
                                                        uint16_t* __restrict__ tdst) {
     GRID_STRIDE(i, nnz) {
         const int32_t e = order[i];
-        tsrc[i] = src_of[e];
-        tdst[i] = (uint16_t)(perm_ci[e] - tile_row0(map, key[i]));
+        const int32_t t = key[i];
+        const int64_t q = slot0[t] + block_slot(i - first[t]);
+        tsrc[q] = src_of[e];
+        tdst[q] = (uint16_t)(perm_ci[e] - tile_row0(map, t));
+    }
+}
+
+// Padding of each tile's last block: the tile's last source and the trash
+// row (a tile without edges has no slots).
+__global__ __launch_bounds__(kBlock) void k_tile_pad(int32_t tiles, const int32_t* __restrict__ first,
+                                                     const int32_t* __restrict__ slot0,
+                                                     int32_t* __restrict__ tsrc,
+                                                     uint16_t* __restrict__ tdst) {
+    for (int32_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const int32_t count = first[t + 1] - first[t];
+        const int32_t padded = slot0[t + 1] - slot0[t];
+        if (padded == count) continue;
+        const int32_t last = tsrc[slot0[t] + block_slot(count - 1)];
+        for (int32_t k = count + threadIdx.x; k < padded; k += kBlock) {
+            const int64_t q = slot0[t] + block_slot(k);
+            tsrc[q] = last;
+            tdst[q] = (uint16_t)kTrashRow;
+        }
+    }
+}
+
+// Sector starts per chunk of kSectorChunk slots, in edge order (edge k of
+// the layout sits at slot block_slot(k)): edge k starts a sector when k == 0
+// or its source's 64-byte sector of contributions differs from edge k-1's.
+// Inside a tile the sources do not decrease (padding repeats the last), so
+// this counts the distinct sectors a range of edges gathers (a tile boundary
+// may merge one sector with the previous tile's last: a count, not an exact
+// figure).
+__global__ __launch_bounds__(kBlock) void k_sector_counts(const int32_t* __restrict__ tsrc,
+                                                          int64_t slots, int32_t chunks,
+                                                          int32_t* __restrict__ counts) {
+    __shared__ int32_t red[kBlock / kWave];
+    for (int32_t c = blockIdx.x; c < chunks; c += gridDim.x) {
+        const int64_t lo = (int64_t)c * kSectorChunk;
+        const int64_t hi = lo + kSectorChunk < slots ? lo + kSectorChunk : slots;
+        int32_t k = 0;
+        for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock) {
+            const int32_t a = tsrc[block_slot(i)] >> kSectorShift;
+            k += (i == 0 || a != (tsrc[block_slot(i - 1)] >> kSectorShift)) ? 1 : 0;
+        }
+        k = block_sum(k, red);
+        if (threadIdx.x == 0) counts[c] = k;
     }
 }
 
@@ -338,6 +391,7 @@ struct Built {
     int32_t items_of[kNumBuckets + 1] = {};
     TileMap map{};
     int32_t n_tiles = 0, n_units = 0, n_fixes = 0, tile_grid = 1;
+    int64_t n_slots = 0;
     std::vector<WorkItem> hub_items;   // host arrays copied to the device
     std::vector<ChunkRow> chunk_rows;
     std::vector<Tile> tiles;
@@ -438,12 +492,12 @@ int log2_ceil(int64_t x) {
 int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
                 const unsigned long long* stats, const int32_t* row_begin, int cus,
                 hipStream_t stream, Built& bt) {
-    // tuning knobs: edges per tile (target) and per unit (at least kMinUnitEdges)
-    int64_t target = kTileTargetEdges, unit_edges = kUnitEdges;
+    // tuning knobs: edges per tile and estimated cost per unit
+    int64_t target = kTileTargetEdges, unit_cost = kUnitCost;
     if (const char* env = std::getenv("PR_TILE_EDGES"))
         if (std::atoll(env) > 0) target = std::atoll(env);
-    if (const char* env = std::getenv("PR_UNIT_EDGES"))
-        if (std::atoll(env) >= kMinUnitEdges) unit_edges = std::atoll(env);
+    if (const char* env = std::getenv("PR_UNIT_COST"))
+        if (std::atoll(env) > 0) unit_cost = std::atoll(env);
     TileMap& map = bt.map;
     int32_t tiles = 0;
     for (int seg = 0; seg < kTileSegments; ++seg) {
@@ -473,21 +527,79 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
         in.error = s.tr.error;
         PR_TRY(radix_sort<kFromTileKeys>(in, vertex_bits(tiles), s.order, s.tr.sort, &sorted_tiles,
                                           stream));
-        k_tile_edges<<<grid_for(nnz, 8192), kBlock, 0, stream>>>(s.order, sorted_tiles, s.src_of,
-                                                                 s.perm_ci, nnz, map, w.tsrc, w.tdst);
-        PR_LAUNCHED("tile edges");
     }
-    PR_TRY(rows_from_sorted(sorted_tiles, nnz, tiles, w.tile_ptr, stream));
+    // each tile's first edge in the sorted order (s.perm_rp is free by now),
+    // then its first slot: tiles padded to whole blocks
+    int32_t* first = s.perm_rp;
+    PR_TRY(rows_from_sorted(sorted_tiles, nnz, tiles, first, stream));
     std::vector<int32_t> tp((size_t)tiles + 1);
-    PR_HIP_TRY(hipMemcpyAsync(tp.data(), w.tile_ptr, sizeof(int32_t) * tp.size(),
-                              hipMemcpyDeviceToHost, stream));
+    PR_HIP_TRY(hipMemcpyAsync(tp.data(), first, sizeof(int32_t) * tp.size(), hipMemcpyDeviceToHost,
+                              stream));
     PR_HIP_TRY(hipStreamSynchronize(stream));
+    std::vector<int32_t> sp((size_t)tiles + 1, 0);
+    {
+        int64_t q = 0;
+        for (int32_t t = 0; t < tiles; ++t) {
+            q += ceil_div((int64_t)(tp[(size_t)t + 1] - tp[(size_t)t]), kEdgeBlock) * kEdgeBlock;
+            if (q > w.n_edge_slots_max || q > INT32_MAX)
+                return fail(PR_ERR_ARG, "tile edge slots exceed the planned bound");
+            sp[(size_t)t + 1] = (int32_t)q;
+        }
+    }
+    const int64_t slots = sp[(size_t)tiles];
+    bt.n_slots = slots;
+    PR_HIP_TRY(hipMemcpyAsync(w.tile_ptr, sp.data(), sizeof(int32_t) * sp.size(),
+                              hipMemcpyHostToDevice, stream));
+    if (nnz > 0) {
+        k_tile_edges<<<grid_for(nnz, 8192), kBlock, 0, stream>>>(s.order, sorted_tiles, s.src_of,
+                                                                 s.perm_ci, nnz, map, first,
+                                                                 w.tile_ptr, w.tsrc, w.tdst);
+        PR_LAUNCHED("tile edges");
+        k_tile_pad<<<dim3((unsigned)(tiles < 8192 ? tiles : 8192)), kBlock, 0, stream>>>(
+            tiles, first, w.tile_ptr, w.tsrc, w.tdst);
+        PR_LAUNCHED("tile padding");
+    }
+    // sector starts per chunk of slots (s.order is free again)
+    const int32_t chunks = (int32_t)ceil_div(slots, kSectorChunk);
+    std::vector<int32_t> sc((size_t)chunks);
+    if (chunks > 0) {
+        k_sector_counts<<<grid_for((int64_t)chunks * kBlock, 8192), kBlock, 0, stream>>>(
+            w.tsrc, slots, chunks, s.order);
+        PR_LAUNCHED("sector counts");
+        PR_HIP_TRY(hipMemcpyAsync(sc.data(), s.order, sizeof(int32_t) * sc.size(),
+                                  hipMemcpyDeviceToHost, stream));
+    }
+    PR_HIP_TRY(hipStreamSynchronize(stream));
+    // cost prefix at chunk boundaries: slots + kSectorWeight * sectors
+    std::vector<int64_t> cp((size_t)chunks + 1, 0);
+    for (int32_t c = 0; c < chunks; ++c) {
+        const int64_t e = (c + 1 < chunks ? (int64_t)kSectorChunk : slots - (int64_t)c * kSectorChunk);
+        cp[(size_t)c + 1] = cp[(size_t)c] + e + kSectorWeight * sc[(size_t)c];
+    }
+    // cost prefix at slot e, linear inside a chunk
+    auto cost_at = [&](int64_t e) -> double {
+        if (e >= slots) return (double)cp[(size_t)chunks];
+        const int64_t c = e / kSectorChunk, r = e - c * kSectorChunk;
+        const int64_t len = (c + 1 < chunks ? (int64_t)kSectorChunk : slots - c * kSectorChunk);
+        return (double)cp[(size_t)c] + (double)(cp[(size_t)c + 1] - cp[(size_t)c]) * (double)r / (double)len;
+    };
+    // first block in [lo, hi] whose cost prefix reaches `want`
+    auto block_at = [&](int64_t lo, int64_t hi, double want) -> int64_t {
+        while (lo < hi) {
+            const int64_t mid = lo + (hi - lo) / 2;
+            if (cost_at(mid * kEdgeBlock) < want)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        return lo;
+    };
 
-    // Tiles, units and slots.  Units of cut tiles first (the largest units),
-    // then whole tiles by decreasing edge count, so the longest work starts
-    // first.
+    // Tiles, units and slots.  A tile is cut at block boundaries into
+    // min(ceil(cost / unit_cost), ceil(slots / kMinUnitEdges)) units of about
+    // equal cost; all units are then ordered by decreasing estimated cost.
     bt.tiles.resize((size_t)tiles);
-    std::vector<TileUnit> whole;
+    std::vector<std::pair<int64_t, TileUnit>> list;
     int64_t slot = 0;
     for (int seg = 0; seg < kTileSegments; ++seg) {
         const int32_t end = map.start[seg + 1];
@@ -496,27 +608,42 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
             const int32_t row0 = map.start[seg] + ((t - map.tile0[seg]) << map.shift[seg]);
             const int32_t rows = (end - row0) < (1 << map.shift[seg]) ? end - row0 : 1 << map.shift[seg];
             bt.tiles[(size_t)t] = Tile{row0, rows};
-            const int32_t e0 = tp[(size_t)t], e1 = tp[(size_t)t + 1];
-            if ((int64_t)(e1 - e0) <= unit_edges) {
-                whole.push_back(TileUnit{t, e0, e1, -1});
+            const int32_t e0 = sp[(size_t)t], e1 = sp[(size_t)t + 1];
+            const double c0 = cost_at(e0), c1 = cost_at(e1);
+            const int64_t per_unit = kUnitOverhead + kTileRowWeight * rows;
+            int64_t count = (int64_t)std::ceil((c1 - c0) / (double)unit_cost);
+            int64_t count_max = ceil_div((int64_t)(e1 - e0), kMinUnitEdges);
+            if (count_max > (e1 - e0) / kEdgeBlock) count_max = (e1 - e0) / kEdgeBlock;
+            if (count > count_max) count = count_max;
+            const int64_t count_min = ceil_div((int64_t)(e1 - e0), kMaxUnitEdges);
+            if (count < count_min) count = count_min;
+            if (count <= 1) {
+                list.push_back({(int64_t)(c1 - c0) + per_unit, TileUnit{t, e0, e1, -1, row0, rows, {0, 0}}});
                 continue;
             }
-            const int32_t count = (int32_t)ceil_div(e1 - e0, unit_edges);
-            if (slot + (int64_t)count * rows > w.n_partial_max)
+            if (slot + count * rows > w.n_partial_max)
                 return fail(PR_ERR_ARG, "tile slots exceed the planned bound");
-            bt.fixes.push_back(TileFix{row0, rows, (int32_t)slot, count});
-            for (int32_t j = 0; j < count; ++j) {
-                const int32_t a = e0 + (int32_t)(j * unit_edges);
-                const int32_t b = (e1 - a) < unit_edges ? e1 : a + (int32_t)unit_edges;
-                bt.units.push_back(TileUnit{t, a, b, (int32_t)(slot + (int64_t)j * rows)});
+            bt.fixes.push_back(TileFix{row0, rows, (int32_t)slot, (int32_t)count});
+            int64_t a = e0;
+            for (int64_t j = 0; j < count; ++j) {
+                const int64_t b =
+                    j + 1 == count ? e1
+                                   : kEdgeBlock * block_at(a / kEdgeBlock + 1,
+                                                           e1 / kEdgeBlock - (count - 1 - j),
+                                                           c0 + (c1 - c0) * (double)(j + 1) / (double)count);
+                const TileUnit u{t, (int32_t)a, (int32_t)b, (int32_t)(slot + j * rows), row0, rows, {0, 0}};
+                list.push_back({(int64_t)(cost_at(b) - cost_at(a)) + per_unit, u});
+                a = b;
             }
-            slot += (int64_t)count * rows;
+            slot += count * rows;
         }
     }
-    std::stable_sort(whole.begin(), whole.end(), [](const TileUnit& x, const TileUnit& y) {
-        return (x.e1 - x.e0) > (y.e1 - y.e0);
-    });
-    bt.units.insert(bt.units.end(), whole.begin(), whole.end());
+    std::stable_sort(list.begin(), list.end(),
+                     [](const std::pair<int64_t, TileUnit>& x, const std::pair<int64_t, TileUnit>& y) {
+                         return x.first > y.first;
+                     });
+    bt.units.clear();
+    for (const auto& u : list) bt.units.push_back(u.second);
     if ((int64_t)bt.units.size() > w.n_units_max || (int64_t)bt.fixes.size() > w.n_fixes_max)
         return fail(PR_ERR_ARG, "tile units exceed the planned bound");
     bt.n_units = (int32_t)bt.units.size();
@@ -575,6 +702,9 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     if (!out_rp || !ws || !scratch || (nnz > 0 && !out_ci))
         return fail(PR_ERR_ARG, "null pointer argument");
     const bool tiled = !(flags & PR_PLAN_BUCKETED);
+    if (tiled && n > kTiledMaxVertices)
+        return fail(PR_ERR_ARG, "a tiled plan takes n <= %d (got %d); PR_PLAN_BUCKETED takes more",
+                    kTiledMaxVertices, n);
     PlanWs w = carve_ws(ws, n, nnz, tiled);
     if (ws_bytes < w.bytes || (reinterpret_cast<uintptr_t>(ws) & 255u))
         return fail(PR_ERR_WORKSPACE, "plan workspace needs %zu bytes at 256-byte alignment (got %zu)",
@@ -681,6 +811,7 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     p->tsrc = w.tsrc;
     p->tdst = w.tdst;
     p->tile_ptr = w.tile_ptr;
+    p->n_slots = bt.n_slots;
     p->tiles = w.tiles;
     p->n_tiles = bt.n_tiles;
     p->units = w.units;

@@ -94,15 +94,46 @@ constexpr int kFinalBlock = 1024;
 // consecutive lanes read neighbouring contributions (coalesced), and adds
 // each one into the row's accumulator in LDS.  Accumulators are 64-bit fixed
 // point (contribution * 2^shift, truncated): integer addition is exact and
-// order-free, so the sums do not depend on scheduling.  A tile with more than
-// kUnitEdges edges is cut into units; each unit writes its accumulators to a
-// slot of `partial`, and k_tilefix adds a tile's slots and applies the
-// update.
+// order-free, so the sums do not depend on scheduling.  A tile whose
+// estimated cost exceeds the unit cost is cut into units of about equal
+// cost; each unit writes its accumulators to a slot of `partial`, and
+// k_tilefix adds a tile's slots and applies the update.
+//
+// Cost estimate of a range of tile edges, in edge-equivalents: its edges,
+// plus kSectorWeight per distinct 64-byte sector of contributions it gathers
+// (sources in increasing order, so a new sector starts where src >> 4
+// changes), plus, per unit, kTileRowWeight per row of the tile (clearing and
+// reading the accumulators) and kUnitOverhead.  The weights are fitted to
+// per-unit timings of k_tile on gfx950: a sector fetched from outside the CU
+// costs about six edges' worth of streaming and adding.  Units go to the
+// queue in decreasing estimated cost, so the longest start first.
 constexpr int32_t kTileMaxRows = 16384;         // 128 KB of accumulators
 constexpr int32_t kTileMinRows = 64;
 constexpr int64_t kTileTargetEdges = 1 << 20;  // default; PR_TILE_EDGES overrides
-constexpr int64_t kUnitEdges = 1 << 18;        // default; PR_UNIT_EDGES raises it
-constexpr int64_t kMinUnitEdges = 1 << 17;     // the workspace bounds assume units this large
+constexpr int64_t kUnitCost = 460000;           // default; PR_UNIT_COST overrides
+constexpr int64_t kMinUnitEdges = 1 << 17;     // a tile is cut into at most edges/this units
+constexpr int64_t kMaxUnitEdges = 1 << 26;     // and into at least edges/this units
+constexpr int32_t kTiledMaxVertices = 1 << 30; // contribution byte offsets fit 32 bits
+constexpr int kSectorShift = 4;                 // 16 fp32 contributions per 64-byte sector
+constexpr int64_t kSectorWeight = 6;
+constexpr int64_t kTileRowWeight = 1;
+constexpr int64_t kUnitOverhead = 27000;
+constexpr int32_t kSectorChunk = 4096;          // edges per sector count read back
+
+// Tile edges are stored in blocks of kEdgeBlock: each tile's edges padded to
+// a whole number of blocks, and each block transposed so that lane l of a
+// wavefront finds edges l, l + 64, l + 128 and l + 192 of the block in one
+// 16-byte load of sources and one 8-byte load of row offsets (and lane l of
+// the gather for edge l + 64*i reads next to lane l + 1's: still coalesced).
+// A padding edge repeats the tile's last source and adds into row
+// kTrashRow, an accumulator that is never read.
+constexpr int32_t kEdgeBlock = 4 * kWave;
+constexpr int32_t kTrashRow = kTileMaxRows;
+
+// Storage slot of edge k of a tile, relative to the tile's first slot.
+__host__ __device__ inline int64_t block_slot(int64_t k) {
+    return (k & ~(int64_t)(kEdgeBlock - 1)) | ((k & (kWave - 1)) << 2) | ((k >> 6) & 3);
+}
 constexpr int kFxShiftMax = 56;                 // 2^-56 resolution when sum|x| <= 1
 
 static_assert(kTileSegments == kNumBuckets, "one tile segment per degree bucket");
@@ -112,14 +143,17 @@ struct Tile {
     int32_t rows;
 };
 
-// A unit of k_tile: edges [e0, e1) of one tile.  slot < 0: the unit is the
-// whole tile and applies the update; otherwise its accumulators go to
-// partial[slot, slot + rows).
+// A unit of k_tile: edges [e0, e1) of one tile (rows [row0, row0 + rows)).
+// slot < 0: the unit is the whole tile and applies the update; otherwise its
+// accumulators go to partial[slot, slot + rows).
 struct TileUnit {
     int32_t tile;
     int32_t e0;
     int32_t e1;
     int32_t slot;
+    int32_t row0;
+    int32_t rows;
+    int32_t pad[2];
 };
 
 // A tile cut into units: k_tilefix adds partial[first + j*rows + r] over
@@ -187,9 +221,10 @@ struct pr_plan {
     int32_t bucket_items[pr::kNumBuckets + 1];  // kinds 0..5
     // tiled pull
     pr::TileMap tile_map;
-    const int32_t* tsrc;    // [nnz] source of each tile edge
-    const uint16_t* tdst;   // [nnz] its row offset in the tile
-    const int32_t* tile_ptr;  // [n_tiles + 1] first edge of each tile
+    const int32_t* tsrc;    // [n_slots] source of each tile edge slot (block layout)
+    const uint16_t* tdst;   // [n_slots] its row offset in the tile
+    const int32_t* tile_ptr;  // [n_tiles + 1] first slot of each tile (multiples of kEdgeBlock)
+    int64_t n_slots;        // tile edge slots, padding included
     const pr::Tile* tiles;
     int32_t n_tiles;
     const pr::TileUnit* units;

@@ -330,12 +330,14 @@ constexpr int kFinalWaves = kFinalBlock / kWave;
 
 constexpr int kTileBlock = 1024;
 constexpr int kTileWaves = kTileBlock / kWave;
-constexpr int kTileU = 8;  // edges per lane per round
+#ifndef PR_TILE_Q
+#define PR_TILE_Q 2
+#endif
+constexpr int kTileQ = PR_TILE_Q;  // edge blocks per wavefront per round
 
 struct TileArgs {
     const int32_t* __restrict__ tsrc;
     const uint16_t* __restrict__ tdst;
-    const Tile* __restrict__ tiles;
     const TileUnit* __restrict__ units;
     const float* __restrict__ inv_out;
     const float* __restrict__ contrib_in;
@@ -364,99 +366,165 @@ __device__ __forceinline__ unsigned long long to_fixed(float c, float scale) {
     return c < 0.f ? 0ull - r : r;
 }
 
-// Adds the contributions of tile edges [e0, e1) into acc[row offset].  The
-// workgroup's lanes take consecutive edges (so the sources a load
-// instruction reads are neighbours), kTileU per lane per round, and the next
-// round's edges are loaded while this round's contributions are gathered and
-// added.  Every load is unconditional, so the compiler issues all of a
-// round's gathers before waiting for any: a lane past e1 reads the unit's
-// last edge (a valid source and row of this tile) and adds zero.  The
-// edge arrays are streamed once per iteration: non-temporal.
-__device__ __forceinline__ void accumulate(const TileArgs& a, int64_t e0, int64_t e1,
-                                           float scale, unsigned long long* acc) {
-    constexpr int64_t kStep = (int64_t)kTileBlock * kTileU;
-    const int64_t last = e1 > e0 ? e1 - 1 : e0;  // in bounds: the arrays hold >= 1 entry
-    int32_t sn[kTileU];
-    uint16_t dn[kTileU];
-    int64_t e = e0 + threadIdx.x;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Element `index` of an array that starts at a uniform address: the byte
+// offset is 32-bit (the plan keeps units below kMaxUnitEdges slots and tiled
+// plans below kTiledMaxVertices vertices), so the load takes the base in
+// scalar registers and one 32-bit offset per lane.
+template <class T>
+__device__ __forceinline__ T load_at(const T* base, uint32_t index) {
+    return *(const T*)((const char*)base + index * (uint32_t)sizeof(T));
+}
+template <class T>
+__device__ __forceinline__ T load_nt_at(const T* base, uint32_t index) {
+    return __builtin_nontemporal_load((const T*)((const char*)base + index * (uint32_t)sizeof(T)));
+}
+
+// One round of a wavefront: blocks b + j*kTileWaves (j < kTileQ) of the
+// unit, each one 16-byte load of four sources and one 8-byte load of four
+// row offsets per lane (lane l holds edges l, l+64, l+128, l+192 of the
+// block).  Every load is unconditional, so the compiler issues all of a
+// round's loads before waiting for any: a block at or past the unit's end
+// reads its last block instead, and the caller adds zero for it.  The edge
+// arrays are streamed once per iteration: non-temporal.
+struct EdgeRound {
+    u32x4 src[kTileQ];
+    u32x2 row[kTileQ];
+};
+
+__device__ __forceinline__ void load_round(const int32_t* ts, const uint16_t* td, uint32_t b,
+                                           uint32_t nblk, uint32_t last, EdgeRound& r) {
+    const uint32_t lane = lane_id();
 #pragma unroll
-    for (int j = 0; j < kTileU; ++j) {
-        const int64_t q = e + (int64_t)j * kTileBlock;
-        const int64_t qc = q < e1 ? q : last;
-        sn[j] = __builtin_nontemporal_load(a.tsrc + qc);
-        dn[j] = __builtin_nontemporal_load(a.tdst + qc);
+    for (int j = 0; j < kTileQ; ++j) {
+        const uint32_t q = b + (uint32_t)(j * kTileWaves);
+        const uint32_t idx = (q < nblk ? q : last) * (kEdgeBlock / 4) + lane;
+        r.src[j] = load_nt_at((const u32x4*)ts, idx);
+        r.row[j] = load_nt_at((const u32x2*)td, idx);
     }
-    for (; e < e1; e += kStep) {
-        int32_t sc[kTileU];
-        uint16_t dc[kTileU];
+}
+
+// Adds the contributions of the unit's edge slots [e0, e1) (whole blocks)
+// into acc[row offset].  Wavefront w takes blocks w, w + kTileWaves, ...,
+// kTileQ per round; `next` holds its first round, loaded by the caller, and
+// each round loads the following one before gathering its own
+// contributions.  In one gather instruction lane l reads the source of edge
+// l + 64*i of a block: consecutive lanes, neighbouring sources.
+__device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_t e1, float scale,
+                                           unsigned long long* acc, EdgeRound& next) {
+    constexpr uint32_t kStep = (uint32_t)kTileWaves * kTileQ;
+    const int32_t* ts = a.tsrc + e0;
+    const uint16_t* td = a.tdst + e0;
+    const uint32_t nblk = (uint32_t)(e1 - e0) / kEdgeBlock;
+    const uint32_t last = nblk > 0 ? nblk - 1 : 0;
+    for (uint32_t b = threadIdx.x / kWave; b < nblk; b += kStep) {
+        const EdgeRound cur = next;
+        load_round(ts, td, b + kStep, nblk, last, next);
+        float v[kTileQ][4];
 #pragma unroll
-        for (int j = 0; j < kTileU; ++j) {
-            sc[j] = sn[j];
-            dc[j] = dn[j];
-        }
+        for (int j = 0; j < kTileQ; ++j)
 #pragma unroll
-        for (int j = 0; j < kTileU; ++j) {
-            const int64_t q = e + kStep + (int64_t)j * kTileBlock;
-            const int64_t qc = q < e1 ? q : last;
-            sn[j] = __builtin_nontemporal_load(a.tsrc + qc);
-            dn[j] = __builtin_nontemporal_load(a.tdst + qc);
-        }
-        float v[kTileU];
+            for (int i = 0; i < 4; ++i) v[j][i] = load_at(a.contrib_in, cur.src[j][i]);
 #pragma unroll
-        for (int j = 0; j < kTileU; ++j) v[j] = a.contrib_in[sc[j]];
+        for (int j = 0; j < kTileQ; ++j) {
+            const bool live = b + (uint32_t)(j * kTileWaves) < nblk;
 #pragma unroll
-        for (int j = 0; j < kTileU; ++j) {
-            const unsigned long long f = to_fixed(v[j], scale);
-            atomicAdd(&acc[dc[j]], e + (int64_t)j * kTileBlock < e1 ? f : 0ull);
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t row = (cur.row[j][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                const unsigned long long f = to_fixed(v[j][i], scale);
+                atomicAdd(&acc[row], live ? f : 0ull);
+            }
         }
     }
 }
 
-// One workgroup per CU; workgroups take units from queue 0 until it is empty.
-// A whole-tile unit applies the update to its rows and writes its three sums;
+// The first round of a unit's edges (nothing for an empty unit).
+__device__ __forceinline__ void first_round(const TileArgs& a, const TileUnit& u, EdgeRound& r) {
+    const uint32_t nblk = (uint32_t)(u.e1 - u.e0) / kEdgeBlock;
+    if (nblk > 0) {
+        load_round(a.tsrc + u.e0, a.tdst + u.e0, threadIdx.x / kWave, nblk, nblk - 1, r);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kTileQ; ++j) {
+            r.src[j] = u32x4{0u, 0u, 0u, 0u};
+            r.row[j] = u32x2{0u, 0u};
+        }
+    }
+}
+
+// One workgroup per CU.  Workgroup b starts with unit b, then takes units
+// gridDim.x, gridDim.x + 1, ... from queue 0 until they run out.  A
+// whole-tile unit applies the update to its rows and writes its three sums;
 // a unit of a cut tile writes its accumulators to its slot (and zero sums).
+// The accumulators are all zero between units: each unit's epilogue clears
+// the rows it read.  The next unit's descriptor and first round of edges are
+// loaded before this unit's epilogue, so their latency overlaps it.
 __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
-    __shared__ unsigned long long acc[kTileMaxRows];
-    __shared__ float red[kTileWaves];
-    __shared__ int32_t s_unit;
+    __shared__ unsigned long long acc[kTileMaxRows + 1];  // + the trash row of padding edges
+    __shared__ float red[3][kTileWaves];
+    __shared__ int32_t s_next;
     RunState* st = a.state;
     if (st->stop) return;  // an earlier iteration met the tolerance
     const Damp k = make_damp(a.d, a.n, st->dmass);
     const float scale = (float)st->fx_scale;  // a power of two, exact in fp32
     const double unit = st->fx_unit;
-    if (threadIdx.x == 0) s_unit = (int32_t)atomicAdd(&st->queue[0][0], 1u);
+    for (int32_t r = threadIdx.x; r < kTileMaxRows; r += kTileBlock) acc[r] = 0ull;
+    int32_t cur = blockIdx.x;
+    TileUnit u{};
+    EdgeRound round{};
+    if (cur < a.n_units) {
+        u = a.units[cur];
+        first_round(a, u, round);
+    }
     __syncthreads();
-    int32_t cur = s_unit;
     while (cur < a.n_units) {
-        uint32_t next = 0;
-        if (threadIdx.x == 0) next = atomicAdd(&st->queue[0][0], 1u);  // answer needed at the end
-        const TileUnit u = a.units[cur];
-        const Tile t = a.tiles[u.tile];
-        for (int32_t r = threadIdx.x; r < t.rows; r += kTileBlock) acc[r] = 0ull;
+        uint32_t ticket = 0;
+        if (threadIdx.x == 0) ticket = atomicAdd(&st->queue[0][0], 1u);  // needed at the end
+        accumulate(a, u.e0, u.e1, scale, acc, round);
+        if (threadIdx.x == 0) s_next = (int32_t)(gridDim.x + ticket);
         __syncthreads();
-        accumulate(a, u.e0, u.e1, scale, acc);
-        __syncthreads();
+        const int32_t nxt = s_next;
+        TileUnit un{};
+        if (nxt < a.n_units) {
+            un = a.units[nxt];
+            first_round(a, un, round);
+        }
         Acc sums;
         if (u.slot < 0) {
-            for (int32_t r = threadIdx.x; r < t.rows; r += kTileBlock) {
+            for (int32_t r = threadIdx.x; r < u.rows; r += kTileBlock) {
                 const float y = (float)((double)(long long)acc[r] * unit);
-                update(a.xi, a.inv_out, a.contrib_out, t.row0 + r, y, k, sums);
+                acc[r] = 0ull;
+                update(a.xi, a.inv_out, a.contrib_out, u.row0 + r, y, k, sums);
             }
         } else {
-            for (int32_t r = threadIdx.x; r < t.rows; r += kTileBlock)
+            for (int32_t r = threadIdx.x; r < u.rows; r += kTileBlock) {
                 a.partial[(int64_t)u.slot + r] = (long long)acc[r];
+                acc[r] = 0ull;
+            }
         }
-        const float l1 = wide_block_sum<float, kTileWaves>(sums.l1, red);
-        const float dg = wide_block_sum<float, kTileWaves>(sums.dang, red);
-        const float sm = wide_block_sum<float, kTileWaves>(sums.sum, red);
-        if (threadIdx.x == 0) {
-            a.part[cur] = l1;
-            a.part[a.stride + cur] = dg;
-            a.part[2 * a.stride + cur] = sm;
-            s_unit = (int32_t)next;
+        const float l1 = wave_sum(sums.l1), dg = wave_sum(sums.dang), sm = wave_sum(sums.sum);
+        if (lane_id() == 0) {
+            red[0][threadIdx.x / kWave] = l1;
+            red[1][threadIdx.x / kWave] = dg;
+            red[2][threadIdx.x / kWave] = sm;
         }
         __syncthreads();
-        cur = s_unit;
+        if (threadIdx.x == 0) {  // the next writes of red and s_next follow a barrier
+            float t0 = 0.f, t1 = 0.f, t2 = 0.f;
+#pragma unroll
+            for (int w = 0; w < kTileWaves; ++w) {
+                t0 += red[0][w];
+                t1 += red[1][w];
+                t2 += red[2][w];
+            }
+            a.part[cur] = t0;
+            a.part[a.stride + cur] = t1;
+            a.part[2 * a.stride + cur] = t2;
+        }
+        cur = nxt;
+        u = un;
     }
 }
 
@@ -703,7 +771,6 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     TileArgs ta{};
     ta.tsrc = p->tsrc;
     ta.tdst = p->tdst;
-    ta.tiles = p->tiles;
     ta.units = p->units;
     ta.inv_out = p->inv_out;
     ta.xi = p->xi;

@@ -120,7 +120,10 @@ def test_plan_layout_tiled(prx, g):
     """Tiled plans: the same renumbering; tiles are consecutive row blocks
     that never straddle a bucket; and the tile edge arrays are the renumbered
     edges sorted by tile, stably from source order, as (source, row offset)
-    pairs -- all bit for bit against that definition evaluated here."""
+    pairs, each tile padded to whole blocks of 256 edges (padding repeats the
+    tile's last source, row offset 16384) and each block stored transposed
+    (edge 64*i + l of a block at slot 4*l + i) -- all bit for bit against
+    that definition evaluated here."""
     dg = _cases.gpu_graph(g)
     plan = prx.Plan(dg, flags=prx.PR_VALIDATE)
     assert plan.layout()[0] is None
@@ -141,11 +144,24 @@ def test_plan_layout_tiled(prx, g):
     tile_of_row = np.repeat(np.arange(nt), rows)
     key = tile_of_row[ci]
     o = np.argsort(key, kind="stable")
-    np.testing.assert_array_equal(_cases.to_np(tsrc), src[o])
-    np.testing.assert_array_equal(_cases.to_np(trow).astype(np.int64) & 0xFFFF,
-                                  ci[o] - row0[key[o]])
-    np.testing.assert_array_equal(_cases.to_np(tptr),
-                                  np.searchsorted(key[o], np.arange(nt + 1), side="left"))
+    first = np.searchsorted(key[o], np.arange(nt + 1), side="left")
+    count = np.diff(first)
+    padded = -(-count // 256) * 256
+    slot0 = np.concatenate([[0], np.cumsum(padded)])
+    np.testing.assert_array_equal(_cases.to_np(tptr), slot0)
+    exp_src = np.zeros(slot0[-1], np.int64)
+    exp_row = np.full(slot0[-1], 16384, np.int64)
+    s_sorted, r_sorted = src[o], ci[o] - row0[key[o]]
+    for t in range(nt):
+        k = np.arange(padded[t])
+        slot = slot0[t] + (k & ~255) + ((k & 63) << 2) + ((k >> 6) & 3)
+        real = k < count[t]
+        exp_src[slot[real]] = s_sorted[first[t]:first[t + 1]]
+        exp_row[slot[real]] = r_sorted[first[t]:first[t + 1]]
+        if count[t] and padded[t] > count[t]:
+            exp_src[slot[~real]] = s_sorted[first[t + 1] - 1]
+    np.testing.assert_array_equal(_cases.to_np(tsrc), exp_src)
+    np.testing.assert_array_equal(_cases.to_np(trow).astype(np.int64) & 0xFFFF, exp_row)
 
 
 MODES = [0, "bucketed"]
