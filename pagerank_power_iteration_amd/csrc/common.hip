@@ -51,12 +51,15 @@ __global__ __launch_bounds__(kBlock) void k_scan_tile_sums(const T* __restrict__
                                                            T* __restrict__ sums) {
     __shared__ T red[kWaves];
     const int64_t base = blockIdx.x * kScanTile;
+    T v[kScanItems];
+#pragma unroll
+    for (int r = 0; r < kScanItems; ++r) {  // loads first, clamped: they overlap
+        const int64_t i = base + r * kBlock + threadIdx.x;
+        v[r] = in[i < N ? i : N - 1];
+    }
     T s = 0;
 #pragma unroll
-    for (int r = 0; r < kScanItems; ++r) {
-        int64_t i = base + r * kBlock + threadIdx.x;
-        if (i < N) s += in[i];
-    }
+    for (int r = 0; r < kScanItems; ++r) s += (base + r * kBlock + threadIdx.x < N) ? v[r] : (T)0;
     s = block_sum(s, red);
     if (threadIdx.x == 0) sums[blockIdx.x] = s;
 }
@@ -69,12 +72,15 @@ __global__ __launch_bounds__(kBlock) void k_scan_tiles(const T* __restrict__ in,
     const int64_t base = blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
     T v[kScanItems];
     T local = 0;
+    if (base + kScanItems <= N) {  // the lane's items are contiguous: wide loads
 #pragma unroll
-    for (int j = 0; j < kScanItems; ++j) {
-        int64_t i = base + j;
-        v[j] = i < N ? in[i] : (T)0;
-        local += v[j];
+        for (int j = 0; j < kScanItems; ++j) v[j] = in[base + j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < kScanItems; ++j) v[j] = base + j < N ? in[base + j] : (T)0;
     }
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) local += v[j];
     T total;
     T run = block_exclusive_scan(local, &total, tmp);
     if (offsets) run += offsets[blockIdx.x];

@@ -82,7 +82,8 @@ struct PlanScratch {  // needed only while pr_plan_create runs
     int32_t* perm_rp;    // [n + 1]
     int32_t* perm_ci;    // [nnz]
     int32_t* src_of;     // [nnz] source (plan id) of each edge of perm_ci
-    int32_t* order;      // [nnz] tiled: perm_ci positions sorted by tile
+    int32_t* order;      // [nnz] tiled: sources sorted by tile, then sector counts
+    int32_t* tile_first; // [max_tiles + 1] tiled: first sorted edge of each tile
     unsigned long long* stats;  // [2 * kNumBuckets]: rows, edges per bucket
     RadixWs vsort;       // sort of the n vertex keys (and scans over n)
     TransposeWs tr;
@@ -147,6 +148,7 @@ PlanScratch carve_scratch(void* base, int32_t n, int64_t nnz) {
     s.perm_ci = c.take<int32_t>((size_t)nnz);
     s.src_of = c.take<int32_t>((size_t)nnz);
     s.order = c.take<int32_t>((size_t)nnz);
+    s.tile_first = c.take<int32_t>((size_t)max_tiles(n) + 1);
     s.stats = c.take<unsigned long long>(2 * kNumBuckets);
     s.vsort = radix_carve(c, n);
     TransposeWs tw = transpose_carve(c.base ? c.base + c.used : nullptr, n, nnz);
@@ -203,10 +205,14 @@ __global__ __launch_bounds__(kBlock) void k_plan_keys(const int32_t* __restrict_
 
 // new_id[old_of[p]] = p; deg[p] = out-degree of the vertex placed at p;
 // inv_out[p] = 1/deg[p] or 0 (0 doubles as the dangling flag).
+// Also indeg[p]: the in-degree of the vertex placed at p (from in_rp, the
+// row pointers of the transpose in input ids).
 __global__ __launch_bounds__(kBlock) void k_order(const int32_t* __restrict__ old_of,
-                                                  const int32_t* __restrict__ out_rp, int32_t n,
+                                                  const int32_t* __restrict__ out_rp,
+                                                  const int32_t* __restrict__ in_rp, int32_t n,
                                                   int32_t* __restrict__ new_id,
                                                   uint32_t* __restrict__ deg,
+                                                  uint32_t* __restrict__ indeg,
                                                   float* __restrict__ inv_out) {
     GRID_STRIDE(p, n) {
         const int32_t u = old_of[p];
@@ -214,14 +220,22 @@ __global__ __launch_bounds__(kBlock) void k_order(const int32_t* __restrict__ ol
         int32_t d = out_rp[u + 1] - out_rp[u];
         d = d > 0 ? d : 0;
         deg[p] = (uint32_t)d;
+        indeg[p] = (uint32_t)(in_rp[u + 1] - in_rp[u]);
         inv_out[p] = d > 0 ? 1.0f / (float)d : 0.0f;
     }
 }
 
 // Out-edge CSR in plan order: row p of the result is row old_of[p] of the
 // input with every target renumbered.  Edge-parallel: each workgroup covers
-// 4096 positions and finds their rows by binary search.
+// kBlock * kPermItems positions.  The rows that own them, [s_lo, s_hi], are
+// found once; when there are at most kPermRows of them their output and
+// input starts are staged in LDS and each position finds its row there, so
+// a lane's loads of out_ci and then of new_id go out together for all its
+// positions.  (A window over a long run of empty rows searches perm_rp in
+// global memory instead.)
 constexpr int kPermItems = 16;
+constexpr int kPermRows = kBlock * kPermItems;
+
 __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restrict__ perm_rp,
                                                          const int32_t* __restrict__ old_of,
                                                          const int32_t* __restrict__ new_id,
@@ -230,57 +244,113 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
                                                          int32_t n, int64_t nnz,
                                                          int32_t* __restrict__ perm_ci,
                                                          int32_t* __restrict__ src_of) {
+    __shared__ int32_t s_dst[kPermRows + 1];  // perm_rp of the window's rows
+    __shared__ int32_t s_src[kPermRows];      // out_rp[old_of[row]]
     __shared__ int32_t s_lo, s_hi;
-    const int64_t base = blockIdx.x * (int64_t)(kBlock * kPermItems);
-    const int64_t last = (base + kBlock * kPermItems < nnz ? base + kBlock * kPermItems : nnz) - 1;
+    const int64_t base = blockIdx.x * (int64_t)kPermRows;
+    const int64_t last = (base + kPermRows < nnz ? base + kPermRows : nnz) - 1;
     if (threadIdx.x == 0) {
         s_lo = owner_row(perm_rp, base, 0, n - 1);
         s_hi = owner_row(perm_rp, last, s_lo, n - 1);
     }
     __syncthreads();
+    const int32_t lo = s_lo, hi = s_hi;
+    const bool staged = hi - lo + 1 <= kPermRows;
+    if (staged) {
+        for (int32_t r = threadIdx.x; r <= hi - lo; r += kBlock) {
+            s_dst[r] = perm_rp[lo + r];
+            s_src[r] = out_rp[old_of[lo + r]];
+        }
+        if (threadIdx.x == 0) s_dst[hi - lo + 1] = perm_rp[hi + 1];
+    }
+    __syncthreads();
+    int32_t row[kPermItems];
+    int64_t q[kPermItems];
+#pragma unroll
     for (int r = 0; r < kPermItems; ++r) {
-        const int64_t p = base + r * kBlock + threadIdx.x;
-        if (p > last) break;
-        const int32_t j = owner_row(perm_rp, p, s_lo, s_hi);
-        int64_t q = (int64_t)out_rp[old_of[j]] + (p - perm_rp[j]);
-        q = q < 0 ? 0 : (q >= nnz ? nnz - 1 : q);
-        const int32_t t = out_ci[q];
+        int64_t p = base + r * kBlock + threadIdx.x;
+        p = p < last ? p : last;
+        int32_t j;
+        if (staged) {
+            int32_t a = 0, b = hi - lo;  // last local row with s_dst[row] <= p
+            while (a < b) {
+                const int32_t mid = (a + b + 1) / 2;
+                if ((int64_t)s_dst[mid] <= p)
+                    a = mid;
+                else
+                    b = mid - 1;
+            }
+            j = lo + a;
+            q[r] = (int64_t)s_src[a] + (p - s_dst[a]);
+        } else {
+            j = owner_row(perm_rp, p, lo, hi);
+            q[r] = (int64_t)out_rp[old_of[j]] + (p - perm_rp[j]);
+        }
+        q[r] = q[r] < 0 ? 0 : (q[r] >= nnz ? nnz - 1 : q[r]);
+        row[r] = j;
+    }
+    int32_t t[kPermItems];
+#pragma unroll
+    for (int r = 0; r < kPermItems; ++r) {
+        t[r] = out_ci[q[r]];
         // out-of-range targets were flagged by the in-degree sort, which
         // clamped them the same way
-        perm_ci[p] = new_id[t < 0 ? 0 : (t >= n ? n - 1 : t)];
-        src_of[p] = j;
+        t[r] = t[r] < 0 ? 0 : (t[r] >= n ? n - 1 : t[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < kPermItems; ++r) t[r] = new_id[t[r]];
+#pragma unroll
+    for (int r = 0; r < kPermItems; ++r) {
+        const int64_t p = base + r * kBlock + threadIdx.x;
+        if (p <= last) {
+            perm_ci[p] = t[r];
+            src_of[p] = row[r];
+        }
     }
 }
 
-// First plan id of tile t.  Its segment is the last one whose first tile is
-// <= t (first tiles do not decrease; an empty segment shares its first tile
-// with the next one, which is then counted too).
+// First plan id of tile t: its segment is the last one whose first tile is
+// <= t (an empty segment shares its first tile with the next, which then
+// wins); picked with selects, as in tile_locate.
 __device__ __forceinline__ int32_t tile_row0(const TileMap& m, int32_t t) {
-    int seg = 0;
+    int32_t start = m.start[0], tile0 = m.tile0[0], shift = m.shift[0];
 #pragma unroll
-    for (int j = 1; j < kTileSegments; ++j) seg += (t >= m.tile0[j]) ? 1 : 0;
-    return m.start[seg] + ((t - m.tile0[seg]) << m.shift[seg]);
+    for (int j = 1; j < kTileSegments; ++j) {
+        const bool in = t >= m.tile0[j];
+        start = in ? m.start[j] : start;
+        tile0 = in ? m.tile0[j] : tile0;
+        shift = in ? m.shift[j] : shift;
+    }
+    return start + ((t - tile0) << shift);
 }
 
-// The tile edge arrays: position i of the tile-sorted order holds edge
-// order[i] of the renumbered out-edge CSR, edge i - first[t] of its tile t =
-// key[i]; it goes to slot slot0[t] + block_slot(i - first[t]) with its source
-// and its row offset in the tile.
-__global__ __launch_bounds__(kBlock) void k_tile_edges(const int32_t* __restrict__ order,
-                                                       const int32_t* __restrict__ key,
-                                                       const int32_t* __restrict__ src_of,
-                                                       const int32_t* __restrict__ perm_ci,
+// first[t] = in-edges of the rows before tile t (in_rp: the exclusive scan of
+// the in-degrees in plan order), i.e. the first position of tile t in the
+// edges sorted by tile; first[tiles] = in_rp[n].
+__global__ __launch_bounds__(kBlock) void k_tile_first(const uint32_t* __restrict__ in_rp,
+                                                       int32_t n, int32_t tiles, TileMap map,
+                                                       int32_t* __restrict__ first) {
+    GRID_STRIDE(t, (int64_t)tiles + 1) {
+        first[t] = (int32_t)in_rp[t < tiles ? tile_row0(map, (int32_t)t) : n];
+    }
+}
+
+// The tile edge arrays: sorted edge i (target targets[i], source sources[i])
+// is edge i - first[t] of its tile t and goes to slot
+// slot0[t] + block_slot(i - first[t]) with its source and its row offset in
+// the tile.
+__global__ __launch_bounds__(kBlock) void k_tile_edges(const int32_t* __restrict__ targets,
+                                                       const int32_t* __restrict__ sources,
                                                        int64_t nnz, TileMap map,
                                                        const int32_t* __restrict__ first,
                                                        const int32_t* __restrict__ slot0,
                                                        int32_t* __restrict__ tsrc,
                                                        uint16_t* __restrict__ tdst) {
     GRID_STRIDE(i, nnz) {
-        const int32_t e = order[i];
-        const int32_t t = key[i];
-        const int64_t q = slot0[t] + block_slot(i - first[t]);
-        tsrc[q] = src_of[e];
-        tdst[q] = (uint16_t)(perm_ci[e] - tile_row0(map, t));
+        const TileSpot at = tile_locate(map, targets[i]);
+        const int64_t q = slot0[at.tile] + block_slot(i - first[at.tile]);
+        tsrc[q] = sources[i];
+        tdst[q] = (uint16_t)at.offset;
     }
 }
 
@@ -517,21 +587,31 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
                     (long long)w.n_tiles_max);
     bt.n_tiles = tiles;
 
-    int32_t* sorted_tiles = nullptr;
+    // each tile's first edge: the in-edges of the rows before it (s.perm_rp
+    // is free by now and takes the scan of the in-degrees in plan order)
+    int32_t* first = s.tile_first;
+    uint32_t* in_rp_plan = reinterpret_cast<uint32_t*>(s.perm_rp);
+    PR_TRY(scan_exclusive(reinterpret_cast<const uint32_t*>(s.key), in_rp_plan, n, s.vsort.scan_ws,
+                          stream));
+    k_tile_first<<<grid_for((int64_t)tiles + 1, 1024), kBlock, 0, stream>>>(in_rp_plan, n, tiles, map,
+                                                                            first);
+    PR_LAUNCHED("tile starts");
+    // edges sorted by tile, stably (so by source inside a tile): keys are the
+    // targets, values the sources (into s.order)
+    const int32_t* sorted_targets = nullptr;
     if (nnz > 0) {
         RadixIn in{};
         in.count = nnz;
         in.n = n;
         in.keys = s.perm_ci;
+        in.vals = s.src_of;
         in.tiles = map;
         in.error = s.tr.error;
-        PR_TRY(radix_sort<kFromTileKeys>(in, vertex_bits(tiles), s.order, s.tr.sort, &sorted_tiles,
-                                          stream));
+        int32_t* keys_sorted = nullptr;
+        PR_TRY(radix_sort<kFromTileTargets>(in, vertex_bits(tiles), s.order, s.tr.sort,
+                                             &keys_sorted, stream));
+        sorted_targets = keys_sorted;
     }
-    // each tile's first edge in the sorted order (s.perm_rp is free by now),
-    // then its first slot: tiles padded to whole blocks
-    int32_t* first = s.perm_rp;
-    PR_TRY(rows_from_sorted(sorted_tiles, nnz, tiles, first, stream));
     std::vector<int32_t> tp((size_t)tiles + 1);
     PR_HIP_TRY(hipMemcpyAsync(tp.data(), first, sizeof(int32_t) * tp.size(), hipMemcpyDeviceToHost,
                               stream));
@@ -551,9 +631,8 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
     PR_HIP_TRY(hipMemcpyAsync(w.tile_ptr, sp.data(), sizeof(int32_t) * sp.size(),
                               hipMemcpyHostToDevice, stream));
     if (nnz > 0) {
-        k_tile_edges<<<grid_for(nnz, 8192), kBlock, 0, stream>>>(s.order, sorted_tiles, s.src_of,
-                                                                 s.perm_ci, nnz, map, first,
-                                                                 w.tile_ptr, w.tsrc, w.tdst);
+        k_tile_edges<<<grid_for(nnz, 8192), kBlock, 0, stream>>>(sorted_targets, s.order, nnz, map,
+                                                                 first, w.tile_ptr, w.tsrc, w.tdst);
         PR_LAUNCHED("tile edges");
         k_tile_pad<<<dim3((unsigned)(tiles < 8192 ? tiles : 8192)), kBlock, 0, stream>>>(
             tiles, first, w.tile_ptr, w.tsrc, w.tdst);
@@ -748,7 +827,9 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
         int32_t* sorted = nullptr;
         PR_TRY(radix_sort<kFromKeys>(in, 19, s.old_of, s.vsort, &sorted, stream));
     }
-    k_order<<<grid_for(n), kBlock, 0, stream>>>(s.old_of, out_rp, n, w.new_id, s.deg, w.inv_out);
+    // (s.key is free again: it holds the in-degrees in plan order from here)
+    k_order<<<grid_for(n), kBlock, 0, stream>>>(s.old_of, out_rp, s.perm_rp, n, w.new_id, s.deg,
+                                                reinterpret_cast<uint32_t*>(s.key), w.inv_out);
     PR_LAUNCHED("order");
 
     // 2. The out-edge CSR in plan order (and each edge's source).

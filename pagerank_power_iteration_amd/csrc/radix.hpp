@@ -33,9 +33,10 @@ enum RadixMode : int {
     kFromKeys = 2,
     // Keys only, first pass: key = target id out_col_idx[i] (range-checked).
     kFromTargets = 3,
-    // Tile of each edge: key = tile_of(keys[i]) (keys are plan ids, valid by
-    // construction), value = i.
-    kFromTileKeys = 4,
+    // Edges by tile: key = target plan id keys[i], value = vals[i], digit taken
+    // from tile_of(key) (targets are plan ids, valid by construction); every
+    // pass reads pairs this way, so the sorted keys are still targets.
+    kFromTileTargets = 4,
 };
 
 // Tiles of the plan: consecutive plan-id segments (one per degree bucket,
@@ -47,25 +48,37 @@ struct TileMap {
     int32_t shift[kTileSegments];      // log2 of the segment's rows per tile
 };
 
-__host__ __device__ inline int tile_segment(const TileMap& m, int32_t v) {
-    int s = 0;
+// Tile of plan id v and v's row offset in it.  The segment is the last one
+// whose start is <= v (an empty segment shares its start with the next,
+// which then wins); its fields are picked with selects rather than an index,
+// so they stay in scalar registers instead of being reloaded per lane.
+struct TileSpot {
+    int32_t tile;
+    int32_t offset;
+};
+
+__host__ __device__ inline TileSpot tile_locate(const TileMap& m, int32_t v) {
+    int32_t start = m.start[0], tile0 = m.tile0[0], shift = m.shift[0];
 #pragma unroll
-    for (int j = 1; j < kTileSegments; ++j) s += (v >= m.start[j]) ? 1 : 0;
-    return s;
+    for (int j = 1; j < kTileSegments; ++j) {
+        const bool in = v >= m.start[j];
+        start = in ? m.start[j] : start;
+        tile0 = in ? m.tile0[j] : tile0;
+        shift = in ? m.shift[j] : shift;
+    }
+    const int32_t rel = v - start;
+    return TileSpot{tile0 + (rel >> shift), rel & ((1 << shift) - 1)};
 }
 
-__host__ __device__ inline int32_t tile_of(const TileMap& m, int32_t v) {
-    const int s = tile_segment(m, v);
-    return m.tile0[s] + ((v - m.start[s]) >> m.shift[s]);
-}
+__host__ __device__ inline int32_t tile_of(const TileMap& m, int32_t v) { return tile_locate(m, v).tile; }
 
 struct RadixIn {
     int64_t count;                 // elements
     int32_t n;                     // vertices
-    const int32_t* keys;           // kFromOutCsr: out_col_idx; kFromPairs, kFromKeys: keys
-    const int32_t* vals;           // kFromPairs
+    const int32_t* keys;           // kFromOutCsr: out_col_idx; other modes: keys
+    const int32_t* vals;           // kFromPairs, kFromTileTargets
     const int32_t* row_ptr;        // kFromOutCsr: out_row_ptr
-    TileMap tiles;                 // kFromTileKeys
+    TileMap tiles;                 // kFromTileTargets
     uint32_t* error;               // set to 1 when an input index is out of range
 };
 
@@ -84,23 +97,46 @@ __device__ __forceinline__ int32_t owner_row(const int32_t* __restrict__ rp, int
     return lo;
 }
 
+// The key of element i as stored (no checks).
+__device__ __forceinline__ int32_t radix_load(const RadixIn& in, int64_t i) { return in.keys[i]; }
+
+// The key a pass uses for a loaded value k: targets read from a caller's CSR
+// are range-checked (an out-of-range one raises the error flag and is
+// clamped, so it cannot index out of bounds later).
 template <int MODE>
-__device__ __forceinline__ int32_t radix_key(const RadixIn& in, int64_t i) {
+__device__ __forceinline__ int32_t radix_check(const RadixIn& in, int32_t k) {
     if (MODE == kFromOutCsr || MODE == kFromTargets) {
-        int32_t k = in.keys[i];
         if ((uint32_t)k >= (uint32_t)in.n) {
             *in.error = 1u;
             k = k < 0 ? 0 : in.n - 1;
         }
-        return k;
-    } else if (MODE == kFromTileKeys) {
-        return tile_of(in.tiles, in.keys[i]);
-    } else {
-        return in.keys[i];
     }
+    return k;
+}
+
+// The digit a pass sorts by: of the key, or of the key's tile.
+template <int MODE>
+__device__ __forceinline__ uint32_t radix_digit(const RadixIn& in, int32_t k, int shift) {
+    const uint32_t d = MODE == kFromTileTargets ? (uint32_t)tile_of(in.tiles, k) : (uint32_t)k;
+    return (d >> shift) & (kRadixDigits - 1);
+}
+
+// Lanes of the wavefront whose digit equals this lane's (among `valid` lanes),
+// from one ballot per digit bit.
+__device__ __forceinline__ uint64_t digit_peers(uint32_t dg, bool valid) {
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < kRadixBits; ++b) {
+        const bool bit = (dg >> b) & 1u;
+        const uint64_t votes = __ballot(bit);
+        peers &= bit ? votes : ~votes;
+    }
+    return peers;
 }
 
 // Histogram of one digit per tile, stored digit-major: hist[digit * T + tile].
+// A lane loads all of its items before counting any (an index past the end
+// reloads the last element and is not counted), so the loads overlap.
 template <int MODE>
 __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, int64_t T,
                                                        uint32_t* __restrict__ hist) {
@@ -108,13 +144,17 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, in
     h[threadIdx.x] = 0;
     __syncthreads();
     const int64_t base = blockIdx.x * (int64_t)kRadixTile;
-#pragma unroll 4
+    const int64_t last = in.count - 1;
+    int32_t k[kRadixItems];
+#pragma unroll
     for (int r = 0; r < kRadixItems; ++r) {
-        int64_t i = base + r * kBlock + threadIdx.x;
-        if (i < in.count) {
-            int32_t k = radix_key<MODE>(in, i);
-            atomicAdd(&h[((uint32_t)k >> shift) & (kRadixDigits - 1)], 1u);
-        }
+        const int64_t i = base + r * kBlock + threadIdx.x;
+        k[r] = radix_load(in, i < in.count ? i : last);
+    }
+#pragma unroll
+    for (int r = 0; r < kRadixItems; ++r) {
+        const int64_t i = base + r * kBlock + threadIdx.x;
+        if (i < in.count) atomicAdd(&h[radix_digit<MODE>(in, radix_check<MODE>(in, k[r]), shift)], 1u);
     }
     __syncthreads();
     hist[(int64_t)threadIdx.x * T + blockIdx.x] = h[threadIdx.x];
@@ -151,6 +191,16 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
 
     int32_t key[kRadixItems], val[kRadixItems];
     uint32_t rank[kRadixItems];
+    // all of the lane's loads first (an index past the end reloads the last
+    // element, which is then ignored), so they overlap
+    constexpr bool kLoadVals = VALS && (MODE == kFromPairs || MODE == kFromTileTargets);
+#pragma unroll
+    for (int r = 0; r < kRadixItems; ++r) {
+        const int idx = wave * (kWave * kRadixItems) + r * kWave + lane;
+        const int64_t g = base + (idx < count ? idx : count - 1);
+        key[r] = radix_load(in, g);
+        if (kLoadVals) val[r] = in.vals[g];
+    }
 #pragma unroll
     for (int r = 0; r < kRadixItems; ++r) {
         const int idx = wave * (kWave * kRadixItems) + r * kWave + lane;
@@ -158,24 +208,18 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
         int32_t k = 0, v = 0;
         if (valid) {
             const int64_t g = base + idx;
-            k = radix_key<MODE>(in, g);
+            k = radix_check<MODE>(in, key[r]);
             if (!VALS)
                 v = 0;
             else if (MODE == kFromOutCsr)
                 v = owner_row(in.row_ptr, g, s_row_lo, s_row_hi);
-            else if (MODE == kFromPairs)
-                v = in.vals[g];
+            else if (kLoadVals)
+                v = val[r];
             else
-                v = (int32_t)g;  // kFromKeys, kFromTileKeys: the index itself
+                v = (int32_t)g;  // kFromKeys: the index itself
         }
-        const uint32_t dg = ((uint32_t)k >> shift) & (kRadixDigits - 1);
-        uint64_t peers = __ballot(valid);
-#pragma unroll
-        for (int b = 0; b < kRadixBits; ++b) {
-            const bool bit = (dg >> b) & 1u;
-            const uint64_t votes = __ballot(bit);
-            peers &= bit ? votes : ~votes;
-        }
+        const uint32_t dg = radix_digit<MODE>(in, k, shift);
+        const uint64_t peers = digit_peers(dg, valid);
         const uint32_t below = lanes_below(peers);
         uint32_t prior = 0;
         if (valid) prior = wave_count[wave][dg];
@@ -204,7 +248,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
     for (int r = 0; r < kRadixItems; ++r) {
         const int idx = wave * (kWave * kRadixItems) + r * kWave + lane;
         if (idx < count) {
-            const uint32_t dg = ((uint32_t)key[r] >> shift) & (kRadixDigits - 1);
+            const uint32_t dg = radix_digit<MODE>(in, key[r], shift);
             const uint32_t pos = digit_start[dg] + wave_count[wave][dg] + rank[r];
             s_key[pos] = key[r];
             if (VALS) s_val[pos] = val[r];
@@ -214,7 +258,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
 
     for (int i = tid; i < count; i += kBlock) {
         const int32_t k = s_key[i];
-        const uint32_t dg = ((uint32_t)k >> shift) & (kRadixDigits - 1);
+        const uint32_t dg = radix_digit<MODE>(in, k, shift);
         const int64_t o = (int64_t)global_start[dg] + (i - (int64_t)digit_start[dg]);
         if (keys_out) keys_out[o] = k;
         if (VALS) vals_out[o] = s_val[i];
@@ -251,13 +295,15 @@ inline RadixWs radix_carve(Carver& c, int64_t count) {
     return w;
 }
 
-// Stable LSD sort of `count` pairs by the low `bits` bits of the key (at
+// Stable LSD sort of `count` >= 1 pairs by the low `bits` bits of the key (at
 // least one pass).  Pass 0 reads its pairs per MODE; later passes read the
 // previous pass's output.  The sorted values end in vals_out; the sorted keys
 // are left in *keys_sorted (one of the scratch buffers).
 template <int MODE>
 int radix_sort(RadixIn in, int bits, int32_t* vals_out, const RadixWs& w, int32_t** keys_sorted,
                hipStream_t stream) {
+    constexpr int kLater = MODE == kFromTileTargets ? kFromTileTargets : kFromPairs;
+    if (in.count < 1) return fail(PR_ERR_ARG, "radix sort of %lld elements", (long long)in.count);
     const int64_t T = radix_tiles(in.count);
     int passes = (bits + kRadixBits - 1) / kRadixBits;
     if (passes < 1) passes = 1;
@@ -269,14 +315,14 @@ int radix_sort(RadixIn in, int bits, int32_t* vals_out, const RadixWs& w, int32_
         if (p == 0)
             k_radix_hist<MODE><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, shift, T, w.hist);
         else
-            k_radix_hist<kFromPairs><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, shift, T, w.hist);
+            k_radix_hist<kLater><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, shift, T, w.hist);
         PR_LAUNCHED("radix histogram");
         PR_TRY(scan_exclusive(w.hist, w.scanned, kRadixDigits * T, w.scan_ws, stream));
         if (p == 0)
             k_radix_scatter<MODE><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, shift, T, w.scanned,
                                                                              kout, vout);
         else
-            k_radix_scatter<kFromPairs><<<dim3((unsigned)T), kBlock, 0, stream>>>(
+            k_radix_scatter<kLater><<<dim3((unsigned)T), kBlock, 0, stream>>>(
                 in, shift, T, w.scanned, kout, vout);
         PR_LAUNCHED("radix scatter");
         in.keys = kout;
@@ -286,11 +332,12 @@ int radix_sort(RadixIn in, int bits, int32_t* vals_out, const RadixWs& w, int32_
     return PR_OK;
 }
 
-// Stable LSD sort of `count` keys alone by their low `bits` bits; pass 0
+// Stable LSD sort of `count` >= 1 keys alone by their low `bits` bits; pass 0
 // reads keys per MODE.  The sorted keys are left in *keys_sorted.
 template <int MODE>
 int radix_sort_keys(RadixIn in, int bits, const RadixWs& w, int32_t** keys_sorted,
                     hipStream_t stream) {
+    if (in.count < 1) return fail(PR_ERR_ARG, "radix sort of %lld elements", (long long)in.count);
     const int64_t T = radix_tiles(in.count);
     int passes = (bits + kRadixBits - 1) / kRadixBits;
     if (passes < 1) passes = 1;

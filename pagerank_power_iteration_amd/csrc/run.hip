@@ -79,17 +79,21 @@ __device__ __forceinline__ Damp make_damp(double d, int32_t n, double dmass) {
 // x'[p] from the gathered sum y, and the lane's running sums.  contrib' is
 // written for every row (0 for a dangling one, whose slot is never read) so
 // the stores cover whole lines.
-__device__ __forceinline__ void update(float* __restrict__ xi, const float* __restrict__ inv_out,
-                                       float* __restrict__ contrib_out, int32_t p, float y,
-                                       const Damp& k, Acc& acc) {
-    const float xo = xi[p];
+__device__ __forceinline__ float apply(float xo, float io, float y, const Damp& k, Acc& acc) {
     const float xn = fmaf(k.lo, y, fmaf(k.hi, y, k.base));
-    xi[p] = xn;
-    const float io = inv_out[p];
-    contrib_out[p] = xn * io;
     acc.l1 += fabsf(xn - xo);
     acc.dang += (io == 0.f) ? xn : 0.f;
     acc.sum += xn;
+    return xn;
+}
+
+__device__ __forceinline__ void update(float* __restrict__ xi, const float* __restrict__ inv_out,
+                                       float* __restrict__ contrib_out, int32_t p, float y,
+                                       const Damp& k, Acc& acc) {
+    const float io = inv_out[p];
+    const float xn = apply(xi[p], io, y, k, acc);
+    xi[p] = xn;
+    contrib_out[p] = xn * io;
 }
 
 // One source's contribution: from the LDS copy below hot_n, else from
@@ -328,10 +332,13 @@ constexpr int kFinalWaves = kFinalBlock / kWave;
 
 // ------------------------------------------------------------ tiled pull
 
-constexpr int kTileBlock = 1024;
+#ifndef PR_TILE_BLOCK
+#define PR_TILE_BLOCK 1024
+#endif
+constexpr int kTileBlock = PR_TILE_BLOCK;
 constexpr int kTileWaves = kTileBlock / kWave;
 #ifndef PR_TILE_Q
-#define PR_TILE_Q 2
+#define PR_TILE_Q 1
 #endif
 constexpr int kTileQ = PR_TILE_Q;  // edge blocks per wavefront per round
 
@@ -454,6 +461,37 @@ __device__ __forceinline__ void first_round(const TileArgs& a, const TileUnit& u
     }
 }
 
+// The update of a whole-tile unit's rows: kRowU rows per lane per step, all
+// of a step's loads issued before any is used (a lane past the last row
+// loads the last row and drops the result).  Each row's accumulator is
+// cleared after it is read.
+constexpr int kRowU = 4;
+
+__device__ __forceinline__ void update_rows(const TileArgs& a, unsigned long long* acc, int32_t row0,
+                                            int32_t rows, double unit, const Damp& k, Acc& sums) {
+    for (int32_t r = threadIdx.x; r < rows; r += kRowU * kTileBlock) {
+        float xo[kRowU], io[kRowU], y[kRowU];
+#pragma unroll
+        for (int j = 0; j < kRowU; ++j) {
+            const int32_t rj = r + j * kTileBlock;
+            const int32_t rc = rj < rows ? rj : rows - 1;
+            xo[j] = a.xi[row0 + rc];
+            io[j] = a.inv_out[row0 + rc];
+            y[j] = (float)((double)(long long)acc[rc] * unit);
+        }
+#pragma unroll
+        for (int j = 0; j < kRowU; ++j) {
+            const int32_t rj = r + j * kTileBlock;
+            if (rj < rows) {
+                acc[rj] = 0ull;
+                const float xn = apply(xo[j], io[j], y[j], k, sums);
+                a.xi[row0 + rj] = xn;
+                a.contrib_out[row0 + rj] = xn * io[j];
+            }
+        }
+    }
+}
+
 // One workgroup per CU.  Workgroup b starts with unit b, then takes units
 // gridDim.x, gridDim.x + 1, ... from queue 0 until they run out.  A
 // whole-tile unit applies the update to its rows and writes its three sums;
@@ -493,11 +531,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
         }
         Acc sums;
         if (u.slot < 0) {
-            for (int32_t r = threadIdx.x; r < u.rows; r += kTileBlock) {
-                const float y = (float)((double)(long long)acc[r] * unit);
-                acc[r] = 0ull;
-                update(a.xi, a.inv_out, a.contrib_out, u.row0 + r, y, k, sums);
-            }
+            update_rows(a, acc, u.row0, u.rows, unit, k, sums);
         } else {
             for (int32_t r = threadIdx.x; r < u.rows; r += kTileBlock) {
                 a.partial[(int64_t)u.slot + r] = (long long)acc[r];
@@ -546,40 +580,72 @@ struct TileFixArgs {
 };
 
 // Rows of the tiles cut into units, one lane per row (the cut tiles' rows
-// numbered one after another; a binary search in fix_rows finds the tile):
-// the row adds its slots in unit order (exact integer sums) and applies the
-// update.  Lane g of workgroup b takes rows b*256 + g, then + gridDim.x*256.
+// numbered one after another; fix_rows[i] is the number of rows before cut
+// tile i): the row adds its slots in unit order (exact integer sums) and
+// applies the update.  Lane g of workgroup b takes rows b*256 + g, then
+// + gridDim.x*256.  One lane finds the tile of the workgroup's first row by
+// binary search; the others step forward from it (a tile has at least 64
+// rows, so a 256-row window meets at most five tiles).
 __global__ __launch_bounds__(kFixBlock) void k_tilefix(TileFixArgs f) {
-    __shared__ float red[kFixBlock / kWave];
+    __shared__ float red[3][kFixBlock / kWave];
+    __shared__ int32_t s_fix;
     RunState* st = f.state;
     if (st->stop) return;
     const Damp k = make_damp(f.d, f.n, st->dmass);
     const double unit = st->fx_unit;
     Acc sums;
-    for (int32_t g = blockIdx.x * kFixBlock + threadIdx.x; g < f.n_rows;
-         g += gridDim.x * kFixBlock) {
-        int32_t lo = 0, hi = f.n_fixes - 1;  // last fix with fix_rows[i] <= g
-        while (lo < hi) {
-            const int32_t mid = (lo + hi + 1) / 2;
-            if (f.fix_rows[mid] <= g)
-                lo = mid;
-            else
-                hi = mid - 1;
+    for (int32_t g0 = blockIdx.x * kFixBlock; g0 < f.n_rows; g0 += gridDim.x * kFixBlock) {
+        __syncthreads();  // s_fix of the previous window has been read
+        if (threadIdx.x == 0) {
+            int32_t lo = 0, hi = f.n_fixes - 1;  // last fix with fix_rows[i] <= g0
+            while (lo < hi) {
+                const int32_t mid = (lo + hi + 1) / 2;
+                if (f.fix_rows[mid] <= g0)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            s_fix = lo;
         }
-        const TileFix fx = f.fixes[lo];
-        const int32_t r = g - f.fix_rows[lo];
-        long long y = 0;
-        for (int32_t j = 0; j < fx.count; ++j)
-            y += f.partial[(int64_t)fx.first + (int64_t)j * fx.rows + r];
-        update(f.xi, f.inv_out, f.contrib_out, fx.row0 + r, (float)((double)y * unit), k, sums);
+        __syncthreads();
+        const int32_t g = g0 + threadIdx.x;
+        if (g < f.n_rows) {
+            int32_t i = s_fix;
+            while (i + 1 < f.n_fixes && f.fix_rows[i + 1] <= g) ++i;
+            const TileFix fx = f.fixes[i];
+            const int32_t r = g - f.fix_rows[i];
+            const long long* slot = f.partial + (int64_t)fx.first + r;
+            long long y0 = 0, y1 = 0, y2 = 0, y3 = 0;
+            int32_t j = 0;
+            for (; j + 4 <= fx.count; j += 4) {
+                y0 += slot[(int64_t)j * fx.rows];
+                y1 += slot[(int64_t)(j + 1) * fx.rows];
+                y2 += slot[(int64_t)(j + 2) * fx.rows];
+                y3 += slot[(int64_t)(j + 3) * fx.rows];
+            }
+            for (; j < fx.count; ++j) y0 += slot[(int64_t)j * fx.rows];
+            const long long y = (y0 + y1) + (y2 + y3);
+            update(f.xi, f.inv_out, f.contrib_out, fx.row0 + r, (float)((double)y * unit), k, sums);
+        }
     }
-    const float l1 = wide_block_sum<float, kFixBlock / kWave>(sums.l1, red);
-    const float dg = wide_block_sum<float, kFixBlock / kWave>(sums.dang, red);
-    const float sm = wide_block_sum<float, kFixBlock / kWave>(sums.sum, red);
+    const float l1 = wave_sum(sums.l1), dg = wave_sum(sums.dang), sm = wave_sum(sums.sum);
+    if (lane_id() == 0) {
+        red[0][threadIdx.x / kWave] = l1;
+        red[1][threadIdx.x / kWave] = dg;
+        red[2][threadIdx.x / kWave] = sm;
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
-        f.part[f.part0 + blockIdx.x] = l1;
-        f.part[f.stride + f.part0 + blockIdx.x] = dg;
-        f.part[2 * f.stride + f.part0 + blockIdx.x] = sm;
+        float t0 = 0.f, t1 = 0.f, t2 = 0.f;
+#pragma unroll
+        for (int w = 0; w < kFixBlock / kWave; ++w) {
+            t0 += red[0][w];
+            t1 += red[1][w];
+            t2 += red[2][w];
+        }
+        f.part[f.part0 + blockIdx.x] = t0;
+        f.part[f.stride + f.part0 + blockIdx.x] = t1;
+        f.part[2 * f.stride + f.part0 + blockIdx.x] = t2;
     }
 }
 
