@@ -119,7 +119,7 @@ size_t pr_plan_scratch_bytes(int32_t n, int64_t nnz);
  *     "gpu-graph-study" T3 tier precomputes 1/deg);
  *   - the in-edges in one of two layouts:
  *       default (tiled pull): each bucket cut into tiles of 2^k consecutive
- *         rows (k per bucket, so a tile holds about 2^20 in-edges, at most
+ *         rows (k per bucket, so a tile holds about 2^22 in-edges, at most
  *         16384 rows), a tile's in-edges stored as (source, row offset) pairs
  *         in increasing source order; the iteration streams a tile's edges in
  *         that order and adds each contribution into the row's accumulator

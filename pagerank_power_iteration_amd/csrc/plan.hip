@@ -33,6 +33,9 @@ namespace pr {
 
 namespace {
 
+// Work list entries of the in-degree count.
+constexpr int kMaxCountChunks = 1024;
+
 // Upper bounds of the tiled layout.
 inline int64_t max_tiles(int32_t n) { return n / kTileMinRows + kNumBuckets + 1; }
 inline int64_t max_units(int32_t n, int64_t nnz) { return max_tiles(n) + nnz / kMinUnitEdges + 1; }
@@ -84,6 +87,7 @@ struct PlanScratch {  // needed only while pr_plan_create runs
     int32_t* src_of;     // [nnz] source (plan id) of each edge of perm_ci
     int32_t* order;      // [nnz] tiled: sources sorted by tile, then sector counts
     int32_t* tile_first; // [max_tiles + 1] tiled: first sorted edge of each tile
+    int32_t* count_chunks;  // [4 * kMaxCountChunks] in-degree counting work list
     unsigned long long* stats;  // [2 * kNumBuckets]: rows, edges per bucket
     RadixWs vsort;       // sort of the n vertex keys (and scans over n)
     TransposeWs tr;
@@ -149,6 +153,7 @@ PlanScratch carve_scratch(void* base, int32_t n, int64_t nnz) {
     s.src_of = c.take<int32_t>((size_t)nnz);
     s.order = c.take<int32_t>((size_t)nnz);
     s.tile_first = c.take<int32_t>((size_t)max_tiles(n) + 1);
+    s.count_chunks = c.take<int32_t>((size_t)4 * kMaxCountChunks);
     s.stats = c.take<unsigned long long>(2 * kNumBuckets);
     s.vsort = radix_carve(c, n);
     TransposeWs tw = transpose_carve(c.base ? c.base + c.used : nullptr, n, nnz);
@@ -166,6 +171,122 @@ unsigned grid_for(int64_t items, int64_t cap = 4096) {
 #define GRID_STRIDE(i, count)                                                      \
     for (int64_t i = blockIdx.x * (int64_t)kBlock + threadIdx.x; i < (count); \
          i += (int64_t)gridDim.x * kBlock)
+
+// ------------------------------------------------------------ in-degrees
+//
+// Row pointers of the transpose (the in-degrees, scanned) without a full
+// sort when vertex ids take 9..23 bits: one radix pass partitions the
+// targets by their top 8 bits, so each bucket spans at most kCountMaxSpan
+// vertices; a workgroup counts a bucket -- or a chunk of a long one -- in
+// LDS counters and stores them (adds them, when the bucket is split); a scan
+// of the counts gives the row pointers.  Other widths take the keys-only
+// radix sort of the targets.
+constexpr int kCountDigitBits = 8;
+constexpr int kCountMaxSpan = 1 << 15;  // 128 KB of LDS counters
+constexpr int kCountBlock = 1024;
+constexpr int kCountItems = 8;
+constexpr int64_t kMinCountChunk = 1 << 16;
+
+struct CountChunk {
+    int32_t bucket;
+    int32_t begin;
+    int32_t end;
+    int32_t split;  // 1: other chunks count the same bucket
+};
+
+// starts[d] = first position of digit d after the partition pass (the
+// digit-major scan of the histogram), starts[256] = the element count.
+__global__ __launch_bounds__(kBlock) void k_digit_starts(const uint32_t* __restrict__ scanned,
+                                                         int64_t T, uint32_t* __restrict__ starts) {
+    starts[threadIdx.x] = scanned[(int64_t)threadIdx.x * T];
+    if (threadIdx.x == 0) starts[kRadixDigits] = scanned[(int64_t)kRadixDigits * T];
+}
+
+__global__ __launch_bounds__(kCountBlock) void k_count_buckets(const int32_t* __restrict__ keys,
+                                                               const CountChunk* __restrict__ chunks,
+                                                               int shift, int32_t n,
+                                                               uint32_t* __restrict__ counts) {
+    __shared__ uint32_t cnt[kCountMaxSpan];
+    const CountChunk c = chunks[blockIdx.x];
+    const int32_t span = 1 << shift;
+    for (int32_t v = threadIdx.x; v < span; v += kCountBlock) cnt[v] = 0u;
+    __syncthreads();
+    const int64_t last = (int64_t)c.end - 1;
+    for (int64_t i0 = c.begin + threadIdx.x; i0 < c.end; i0 += (int64_t)kCountBlock * kCountItems) {
+        int32_t k[kCountItems];
+#pragma unroll
+        for (int j = 0; j < kCountItems; ++j) {  // loads first, clamped: they overlap
+            const int64_t i = i0 + (int64_t)j * kCountBlock;
+            k[j] = keys[i < c.end ? i : last];
+        }
+#pragma unroll
+        for (int j = 0; j < kCountItems; ++j)
+            if (i0 + (int64_t)j * kCountBlock < c.end) atomicAdd(&cnt[k[j] & (span - 1)], 1u);
+    }
+    __syncthreads();
+    const int64_t v0 = (int64_t)c.bucket << shift;
+    for (int32_t v = threadIdx.x; v < span; v += kCountBlock) {
+        if (v0 + v >= n) continue;
+        if (!c.split)
+            counts[v0 + v] = cnt[v];
+        else if (cnt[v])
+            atomicAdd(&counts[v0 + v], cnt[v]);
+    }
+}
+
+// in_rp[0..n] of the transpose of (n, nnz, out_ci).  counts: n words of
+// scratch; chunks: 4 * kMaxCountChunks words; scan_ws: a scan workspace for n
+// items.  Out-of-range targets are clamped and flagged in tr.error.
+// Synchronizes `stream` (the bucket sizes are read back).
+int indegree_row_ptr(int32_t n, int64_t nnz, const int32_t* out_ci, int32_t* in_rp,
+                     uint32_t* counts, int32_t* chunks, void* scan_ws, const TransposeWs& tr,
+                     hipStream_t stream) {
+    const int bits = vertex_bits(n);
+    if (nnz == 0 || bits <= kCountDigitBits || bits - kCountDigitBits > 15)
+        return transpose_row_ptr(n, nnz, out_ci, in_rp, tr, stream);
+    const int shift = bits - kCountDigitBits;
+    RadixIn in{};
+    in.count = nnz;
+    in.n = n;
+    in.keys = out_ci;
+    in.error = tr.error;
+    const RadixWs& w = tr.sort;
+    const int64_t T = radix_tiles(nnz);
+    k_radix_hist<kFromTargets><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, shift, T, w.hist);
+    PR_LAUNCHED("radix histogram");
+    PR_TRY(scan_exclusive(w.hist, w.scanned, kRadixDigits * T, w.scan_ws, stream));
+    k_radix_scatter<kFromTargets, false><<<dim3((unsigned)T), kBlock, 0, stream>>>(
+        in, shift, T, w.scanned, w.key[0], nullptr);
+    PR_LAUNCHED("radix scatter");
+    uint32_t* starts_dev = reinterpret_cast<uint32_t*>(chunks);
+    k_digit_starts<<<1, kBlock, 0, stream>>>(w.scanned, T, starts_dev);
+    PR_LAUNCHED("digit starts");
+    uint32_t starts[kRadixDigits + 1];
+    PR_HIP_TRY(hipMemcpyAsync(starts, starts_dev, sizeof starts, hipMemcpyDeviceToHost, stream));
+    PR_HIP_TRY(hipStreamSynchronize(stream));
+    // chunks of at least max(nnz / 256, kMinCountChunk) keys: at most 512 of them
+    int64_t size = ceil_div(nnz, kRadixDigits);
+    if (size < kMinCountChunk) size = kMinCountChunk;
+    std::vector<CountChunk> list;
+    for (int b = 0; b < kRadixDigits; ++b) {
+        const int64_t lo = starts[b], len = (int64_t)starts[b + 1] - lo;
+        if (len <= 0) continue;
+        const int64_t k = ceil_div(len, size);
+        for (int64_t j = 0; j < k; ++j)
+            list.push_back(CountChunk{b, (int32_t)(lo + len * j / k), (int32_t)(lo + len * (j + 1) / k),
+                                      k > 1 ? 1 : 0});
+    }
+    if ((int64_t)list.size() > kMaxCountChunks) return fail(PR_ERR_ARG, "in-degree chunks overflow");
+    PR_HIP_TRY(hipMemcpyAsync(chunks, list.data(), sizeof(CountChunk) * list.size(),
+                              hipMemcpyHostToDevice, stream));
+    PR_TRY(fill_u32(counts, 0u, n, stream));
+    k_count_buckets<<<dim3((unsigned)list.size()), kCountBlock, 0, stream>>>(
+        w.key[0], reinterpret_cast<const CountChunk*>(chunks), shift, n, counts);
+    PR_LAUNCHED("count buckets");
+    PR_TRY(scan_exclusive(counts, reinterpret_cast<uint32_t*>(in_rp), n, scan_ws, stream));
+    PR_HIP_TRY(hipStreamSynchronize(stream));  // `list` must outlive the copy
+    return PR_OK;
+}
 
 struct Bounds {
     int32_t min_len[kNumBuckets];
@@ -432,11 +553,12 @@ __global__ __launch_bounds__(kBlock) void k_bucket_items(const int32_t* __restri
     }
 }
 
-// Bucket lower bounds; PR_BUCKET_MIN="0,5,17,65,1025" overrides them (a
-// tuning knob).  Must start at 0, not decrease, and keep the hub bound at
-// least kMinHubLength.
-void bucket_bounds(int32_t out[kNumBuckets]) {
-    std::memcpy(out, kDefaultBucketMin, sizeof(kDefaultBucketMin));
+// Bucket lower bounds of a layout (kDefaultTileBucketMin for tiles,
+// kDefaultBucketMin for the bucketed pull); PR_BUCKET_MIN="0,5,17,65,1025"
+// overrides them (a tuning knob).  Must start at 0, not decrease, and keep
+// the hub bound at least kMinHubLength.
+void bucket_bounds(bool tiled, int32_t out[kNumBuckets]) {
+    std::memcpy(out, tiled ? kDefaultTileBucketMin : kDefaultBucketMin, sizeof(kDefaultBucketMin));
     const char* env = std::getenv("PR_BUCKET_MIN");
     if (!env) return;
     int32_t tmp[kNumBuckets];
@@ -811,10 +933,11 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     //    in-degrees are the row lengths of the transpose, whose row pointers
     //    come from a keys-only sort of the targets (perm_rp holds them until
     //    step 2 needs it).
-    PR_TRY(transpose_row_ptr(n, nnz, out_ci, s.perm_rp, s.tr, stream));
+    PR_TRY(indegree_row_ptr(n, nnz, out_ci, s.perm_rp, s.deg, s.count_chunks, s.vsort.scan_ws, s.tr,
+                            stream));
     if (validate) PR_TRY(read_error_word(err, stream, "pr_plan_create"));
     Bounds bounds;
-    bucket_bounds(bounds.min_len);
+    bucket_bounds(tiled, bounds.min_len);
     k_plan_keys<<<grid_for(n, 1024), kBlock, 0, stream>>>(s.perm_rp, out_rp, n, bounds, s.key,
                                                           s.stats);
     PR_LAUNCHED("plan keys");

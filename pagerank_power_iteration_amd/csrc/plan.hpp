@@ -16,6 +16,9 @@ constexpr int kNumBuckets = 5;
 constexpr int kHubBucket = kNumBuckets - 1;
 constexpr int kBucketGroup[kNumBuckets] = {1, 4, 16, 64, 256};
 constexpr int32_t kDefaultBucketMin[kNumBuckets] = {0, 5, 17, 65, 1025};
+// The tiled layout uses the buckets only to group rows of similar length into
+// tiles; these bounds were the fastest in sweeps on R-MAT scale 23.
+constexpr int32_t kDefaultTileBucketMin[kNumBuckets] = {0, 9, 33, 129, 2049};
 constexpr int32_t kMinHubLength = 257;  // lower bound for a tuned hub threshold
 
 // Work items.  Wavefronts of the iteration kernel take batches of
@@ -109,8 +112,8 @@ constexpr int kFinalBlock = 1024;
 // queue in decreasing estimated cost, so the longest start first.
 constexpr int32_t kTileMaxRows = 16384;         // 128 KB of accumulators
 constexpr int32_t kTileMinRows = 64;
-constexpr int64_t kTileTargetEdges = 1 << 20;  // default; PR_TILE_EDGES overrides
-constexpr int64_t kUnitCost = 460000;           // default; PR_UNIT_COST overrides
+constexpr int64_t kTileTargetEdges = 1 << 22;  // default; PR_TILE_EDGES overrides
+constexpr int64_t kUnitCost = 700000;           // default; PR_UNIT_COST overrides
 constexpr int64_t kMinUnitEdges = 1 << 17;     // a tile is cut into at most edges/this units
 constexpr int64_t kMaxUnitEdges = 1 << 26;     // and into at least edges/this units
 constexpr int32_t kTiledMaxVertices = 1 << 30; // contribution byte offsets fit 32 bits
