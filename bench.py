@@ -2,18 +2,18 @@
 
 One step = the whole path on one synthetic graph already resident in device
 memory: pr_plan_create (vertices renumbered by degree bucket and out-degree,
-inverse out-degrees, the in-edge CSR by the device counting-sort transpose,
-work items) and pr_run with 50 fixed iterations (tol = 0, the timed mode of
-the Day 40 page).  The stand-alone pr_transpose of the caller's graph is
-timed on its own.  The default workload is R-MAT scale 23, edge factor 32,
-(a, b, c, d) = (.57, .19, .19, .05), seed 23, self-loops and duplicates
-removed.
+inverse out-degrees, the in-edges sorted into tiles by the device
+counting-sort machinery, the work units) and pr_run with 50 fixed iterations
+(tol = 0, the timed mode of the Day 40 page).  The stand-alone pr_transpose of
+the caller's graph is timed on its own.  The default workload is R-MAT scale
+23, edge factor 32, (a, b, c, d) = (.57, .19, .19, .05), seed 23, self-loops
+and duplicates removed.
 
 Printed (one JSON line): whole-step throughput in GTEPS (edges x iterations /
-step time); the per-iteration time and GTEPS; the gather-and-update kernel
-(k_iterate, timed launch by launch with events on the run's stream) against
-the HBM roofline, counting the bytes any pull iteration must move; and the CPU
-oracle's rate on a bounded sample of the same graph.
+step time); the per-iteration time and GTEPS; the gather-and-accumulate
+kernel (k_tile, timed launch by launch with events on the run's stream)
+against the HBM roofline, counting the bytes any pull iteration must move;
+and the CPU oracle's rate on a bounded sample of the same graph.
 
     python bench.py [--steps K] [--warmup W] [--workload rmat23] [--iters 50]
 """
@@ -31,9 +31,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_iterate_rmat23_counters.json")
+MAIN_KERNEL = "k_tile"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_tile_rmat23_counters.json")
+# the kernel and the plan code that lays out its tiles and units
 KERNEL_SOURCES = ["pagerank_power_iteration_amd/csrc/run.hip",
+                  "pagerank_power_iteration_amd/csrc/plan.hip",
                   "pagerank_power_iteration_amd/csrc/plan.hpp",
+                  "pagerank_power_iteration_amd/csrc/radix.hpp",
                   "pagerank_power_iteration_amd/csrc/common.hpp"]
 
 
@@ -57,8 +61,8 @@ def min_bytes_per_iteration(n: int, m: int) -> int:
 
 
 def traffic_from_counters(n_launch_bytes: int):
-    """HBM bytes per k_iterate launch from the committed rocprofv3 counter
-    summary, when it was taken on the current kernel source."""
+    """HBM bytes per k_tile launch from the committed rocprofv3 counter
+    summary, when it was taken on the current kernel and plan source."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
@@ -187,7 +191,7 @@ def main() -> int:
     achieved = bytes_iter / (kernel_ms * 1e-3) / 1e9
     traffic, _ = traffic_from_counters(bytes_iter)
     log(f"step {ms_per_step:.3f} ms: plan {med['plan']:.3f} ms, run {med['run']:.3f} ms "
-        f"({iter_ms * 1e3:.1f} us/iteration, k_iterate {kernel_ms * 1e3:.1f} us/launch); "
+        f"({iter_ms * 1e3:.1f} us/iteration, {MAIN_KERNEL} {kernel_ms * 1e3:.1f} us/launch); "
         f"pr_transpose alone {med['transpose']:.3f} ms")
 
     scratch = torch.empty(prx.pr_plan_scratch_bytes(n, m), dtype=torch.uint8, device="cuda")
@@ -223,12 +227,12 @@ def main() -> int:
         "iteration": {"ms": round(iter_ms, 5), "gteps": round(m / (iter_ms * 1e-3) / 1e9, 2),
                       "gbps": round(bytes_iter / (iter_ms * 1e-3) / 1e9, 1),
                       "cv": round(iter_cv, 4), "algorithmic_bytes": bytes_iter,
-                      "k_iterate_ms": round(kernel_ms, 5)},
+                      "kernel_ms": round(kernel_ms, 5)},
         "transpose_ms": round(med["transpose"], 4),
         "plan_ms": round(med["plan"], 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "k_iterate",
+                     "traffic": traffic, "kernel": MAIN_KERNEL,
                      "launch_ms": round(kernel_ms, 5)},
         "copy_row_gbps": copy_gbps,
         "buckets": buckets,

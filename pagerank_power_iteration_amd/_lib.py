@@ -174,7 +174,8 @@ def pr_plan_iteration_ms(plan) -> float:
 
 
 def pr_plan_kernel_ms(plan) -> tuple[float, int]:
-    """(mean k_iterate launch duration in ms, number of launches averaged)."""
+    """(mean duration in ms of the main gather kernel's launches -- k_tile, or k_iterate
+    for a bucketed plan -- and the number of launches averaged)."""
     ms = _c.c_float(0.0)
     k = _c.c_int32(0)
     _check(lib().pr_plan_kernel_ms(plan, _c.byref(ms), _c.byref(k)))

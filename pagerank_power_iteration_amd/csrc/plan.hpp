@@ -181,7 +181,7 @@ struct RunState {
     uint32_t queue[kQueues][64];  // queue heads at [q][0]
 };
 
-// Launches of k_iterate that PR_RECORD_EVENTS times one by one.
+// Launches of the gather kernel that PR_RECORD_EVENTS times one by one.
 constexpr int kTimedLaunches = 64;
 
 // Host copy of the fields pr_run polls.
@@ -239,7 +239,7 @@ struct pr_plan {
     long long* partial;
     int32_t tile_grid;
     hipEvent_t ev_begin, ev_end;
-    hipEvent_t kernel_ev[2][pr::kTimedLaunches];  // around k_iterate launches
+    hipEvent_t kernel_ev[2][pr::kTimedLaunches];  // around k_tile (or k_iterate) launches
     int32_t kernel_timed;                         // pairs the last run recorded
     hipEvent_t chunk_ev[2];
     pr::RunStatus* host_status;  // pinned, [2]
