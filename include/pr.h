@@ -221,19 +221,22 @@ int pr_plan_layout(const pr_plan* plan, const int32_t** in_row_ptr_dev,
                    const int32_t** in_col_idx_dev, const int32_t** new_id_dev);
 
 /* Introspection for tests, tiled plans only (PR_ERR_ARG otherwise): device
- * pointers to tile_src[S] (source plan id of each tile edge slot),
- * tile_row[S] (its row's offset from the tile's first row) and
+ * pointers to tile_src[S], tile_row[S], tile_block[S/256] and
  * tile_ptr[n_tiles+1] (the first slot of each tile; S = tile_ptr[n_tiles]);
  * the tile count; and, into host arrays of n_tiles entries, each tile's first
  * plan id and row count.  Slots hold a tile's edges in increasing source
  * order, padded to a multiple of 256 (padding slots repeat the tile's last
  * source with row offset 16384, an accumulator that is never read), and each
  * block of 256 is stored transposed: edge 64*i + l of a block sits at slot
- * 4*l + i.  Any output may be NULL (call once with NULL arrays to learn
- * n_tiles). */
+ * 4*l + i.  Block b is narrow when its sources span less than 2^16: then
+ * tile_block[b] is its first source and slot k of the block holds
+ * (source - tile_block[b]) | row_offset << 16 in tile_src; otherwise
+ * tile_block[b] = -1, tile_src holds the source and tile_row the row offset
+ * (tile_row is not kept up to date for narrow blocks).  Any output may be
+ * NULL (call once with NULL arrays to learn n_tiles). */
 int pr_plan_tiles(const pr_plan* plan, const int32_t** tile_src_dev, const uint16_t** tile_row_dev,
-                  const int32_t** tile_ptr_dev, int32_t* n_tiles_host, int32_t* row0_host,
-                  int32_t* rows_host);
+                  const int32_t** tile_block_dev, const int32_t** tile_ptr_dev, int32_t* n_tiles_host,
+                  int32_t* row0_host, int32_t* rows_host);
 
 /* Human-readable name of a status code (static storage). */
 const char* pr_status_string(int status);

@@ -113,12 +113,14 @@ class Plan:
 
     def tiles(self):
         """Tiled plans: (tile_src int32[slots], tile_row int16[slots] (the row
-        offset in its tile, as unsigned 16-bit), tile_ptr int32[n_tiles+1],
-        row0, rows) -- device views and numpy arrays.  Tile t owns slots
+        offset in its tile, as unsigned 16-bit; wide blocks only),
+        tile_block int32[slots/256], tile_ptr int32[n_tiles+1], row0, rows)
+        -- device views and numpy arrays.  Tile t owns slots
         [tile_ptr[t], tile_ptr[t+1]), its edges padded to whole blocks of
-        256 and each block stored transposed (see pr_plan_tiles)."""
+        256, each block stored transposed and narrow blocks packed (see
+        pr_plan_tiles)."""
         torch = _torch()
-        src, row, ptr, nt, row0, rows = pr_plan_tiles(self.handle)
+        src, row, blk, ptr, nt, row0, rows = pr_plan_tiles(self.handle)
         base = self.ws.data_ptr()
 
         def view(addr, nbytes, dtype):
@@ -127,7 +129,7 @@ class Plan:
         tile_ptr = view(ptr, 4 * (nt + 1), torch.int32)
         slots = int(tile_ptr[-1].item())
         return (view(src, 4 * slots, torch.int32), view(row, 2 * slots, torch.int16),
-                tile_ptr, row0, rows)
+                view(blk, 4 * (slots // 256), torch.int32), tile_ptr, row0, rows)
 
     @property
     def n(self) -> int:

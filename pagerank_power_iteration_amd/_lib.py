@@ -54,7 +54,7 @@ _SIGNATURES = {
                                    _c.POINTER(_c.c_int64)]),
     "pr_plan_layout": (_c.c_int, [_vp, _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_vp)]),
     "pr_plan_tiles": (_c.c_int, [_vp, _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_vp),
-                                 _c.POINTER(_c.c_int32), _vp, _vp]),
+                                 _c.POINTER(_vp), _c.POINTER(_c.c_int32), _vp, _vp]),
     "pr_status_string": (_c.c_char_p, [_c.c_int]),
     "pr_last_error": (_c.c_char_p, []),
 }
@@ -143,17 +143,18 @@ def pr_plan_layout(plan) -> tuple[int, int, int | None]:
 
 
 def pr_plan_tiles(plan):
-    """Device addresses of the tiled plan's tile_src, tile_row and tile_ptr,
-    and each tile's first plan id and row count (numpy arrays)."""
+    """Device addresses of the tiled plan's tile_src, tile_row, tile_block and
+    tile_ptr, and each tile's first plan id and row count (numpy arrays)."""
     import numpy as np
-    src, row, ptr = _vp(), _vp(), _vp()
+    src, row, blk, ptr = _vp(), _vp(), _vp(), _vp()
     nt = _c.c_int32(0)
-    _check(lib().pr_plan_tiles(plan, _c.byref(src), _c.byref(row), _c.byref(ptr), _c.byref(nt),
-                               None, None))
+    _check(lib().pr_plan_tiles(plan, _c.byref(src), _c.byref(row), _c.byref(blk), _c.byref(ptr),
+                               _c.byref(nt), None, None))
     row0 = np.zeros(nt.value, dtype=np.int32)
     rows = np.zeros(nt.value, dtype=np.int32)
-    _check(lib().pr_plan_tiles(plan, None, None, None, None, row0.ctypes.data, rows.ctypes.data))
-    return src.value, row.value, ptr.value, nt.value, row0, rows
+    _check(lib().pr_plan_tiles(plan, None, None, None, None, None, row0.ctypes.data,
+                               rows.ctypes.data))
+    return src.value, row.value, blk.value, ptr.value, nt.value, row0, rows
 
 
 def pr_plan_destroy(plan: int | None) -> None:

@@ -68,6 +68,7 @@ struct PlanWs {  // lives as long as the plan
     // tiled pull
     int32_t* tsrc;
     uint16_t* tdst;
+    int32_t* tblk;
     int32_t* tile_ptr;
     Tile* tiles;
     TileUnit* units;
@@ -125,6 +126,7 @@ PlanWs carve_ws(void* base, int32_t n, int64_t nnz, bool tiled) {
     } else {
         w.tsrc = c.take<int32_t>((size_t)w.n_edge_slots_max);
         w.tdst = c.take<uint16_t>((size_t)w.n_edge_slots_max);
+        w.tblk = c.take<int32_t>((size_t)(w.n_edge_slots_max / kEdgeBlock + 1));
         w.tile_ptr = c.take<int32_t>((size_t)w.n_tiles_max + 1);
         w.tiles = c.take<Tile>((size_t)w.n_tiles_max);
         w.units = c.take<TileUnit>((size_t)w.n_units_max);
@@ -518,6 +520,34 @@ __global__ __launch_bounds__(kBlock) void k_sector_counts(const int32_t* __restr
     }
 }
 
+// Narrow blocks (see kNarrowSpan): one wavefront per block reads the
+// block's sources and rows, and a narrow block rewrites its source slots in
+// place as (source - first) | row << 16.
+__global__ __launch_bounds__(kBlock) void k_tile_pack(int64_t blocks, int32_t* __restrict__ tsrc,
+                                                      const uint16_t* __restrict__ tdst,
+                                                      int32_t* __restrict__ tblk) {
+    const int lane = lane_id();
+    for (int64_t b = blockIdx.x * (int64_t)kWaves + threadIdx.x / kWave; b < blocks;
+         b += (int64_t)gridDim.x * kWaves) {
+        int32_t* w = tsrc + b * kEdgeBlock + 4 * lane;
+        const uint16_t* r = tdst + b * kEdgeBlock + 4 * lane;
+        int32_t src[4], row[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            src[i] = w[i];
+            row[i] = r[i];
+        }
+        const int32_t first = __shfl(src[0], 0);     // edge 0 of the block: slot 0
+        const int32_t last = __shfl(src[3], kWave - 1);  // edge 255: slot 255
+        const bool narrow = last - first < kNarrowSpan;
+        if (lane == 0) tblk[b] = narrow ? first : -1;
+        if (narrow) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = (src[i] - first) | (row[i] << 16);
+        }
+    }
+}
+
 // First p in [lo, hi) with in_rp[p] + kRowCost * p >= target (hi if none).
 __device__ __forceinline__ int32_t cost_lower_bound(const int32_t* __restrict__ in_rp, int32_t lo,
                                                     int32_t hi, int64_t target) {
@@ -770,6 +800,13 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
         PR_HIP_TRY(hipMemcpyAsync(sc.data(), s.order, sizeof(int32_t) * sc.size(),
                                   hipMemcpyDeviceToHost, stream));
     }
+    if (slots > 0) {  // after the sector counts, which read the plain sources
+        const int64_t blocks = slots / kEdgeBlock;
+        const int64_t groups = ceil_div(blocks, kWaves);
+        k_tile_pack<<<dim3((unsigned)(groups < 8192 ? groups : 8192)), kBlock, 0, stream>>>(
+            blocks, w.tsrc, w.tdst, w.tblk);
+        PR_LAUNCHED("tile blocks");
+    }
     PR_HIP_TRY(hipStreamSynchronize(stream));
     // cost prefix at chunk boundaries: slots + kSectorWeight * sectors
     std::vector<int64_t> cp((size_t)chunks + 1, 0);
@@ -1014,6 +1051,7 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     p->tile_map = bt.map;
     p->tsrc = w.tsrc;
     p->tdst = w.tdst;
+    p->tblk = w.tblk;
     p->tile_ptr = w.tile_ptr;
     p->n_slots = bt.n_slots;
     p->tiles = w.tiles;
@@ -1094,12 +1132,13 @@ extern "C" int pr_plan_layout(const pr_plan* p, const int32_t** in_row_ptr,
 }
 
 extern "C" int pr_plan_tiles(const pr_plan* p, const int32_t** tile_src, const uint16_t** tile_row,
-                             const int32_t** tile_ptr, int32_t* n_tiles, int32_t* row0,
-                             int32_t* rows) {
+                             const int32_t** tile_block, const int32_t** tile_ptr, int32_t* n_tiles,
+                             int32_t* row0, int32_t* rows) {
     if (!p) return fail(PR_ERR_ARG, "plan is null");
     if (!p->tiled) return fail(PR_ERR_ARG, "the plan was built with PR_PLAN_BUCKETED");
     if (tile_src) *tile_src = p->tsrc;
     if (tile_row) *tile_row = p->tdst;
+    if (tile_block) *tile_block = p->tblk;
     if (tile_ptr) *tile_ptr = p->tile_ptr;
     if (n_tiles) *n_tiles = p->n_tiles;
     const TileMap& m = p->tile_map;

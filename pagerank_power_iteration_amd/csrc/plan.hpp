@@ -133,6 +133,14 @@ constexpr int32_t kSectorChunk = 4096;          // edges per sector count read b
 constexpr int32_t kEdgeBlock = 4 * kWave;
 constexpr int32_t kTrashRow = kTileMaxRows;
 
+// Narrow blocks.  Inside a block the sources do not decrease, so the block
+// spans [first, last] = its edges 0 and 255.  When last - first < 2^16 the
+// block is narrow: tile_block[b] = first, and each slot holds
+// (source - first) | row << 16, so one 16-byte load gives a lane four whole
+// edges.  Otherwise tile_block[b] = -1 and the slots keep the 32-bit sources,
+// with the rows in the 16-bit row array.
+constexpr int32_t kNarrowSpan = 1 << 16;
+
 // Storage slot of edge k of a tile, relative to the tile's first slot.
 __host__ __device__ inline int64_t block_slot(int64_t k) {
     return (k & ~(int64_t)(kEdgeBlock - 1)) | ((k & (kWave - 1)) << 2) | ((k >> 6) & 3);
@@ -225,7 +233,8 @@ struct pr_plan {
     // tiled pull
     pr::TileMap tile_map;
     const int32_t* tsrc;    // [n_slots] source of each tile edge slot (block layout)
-    const uint16_t* tdst;   // [n_slots] its row offset in the tile
+    const uint16_t* tdst;   // [n_slots] its row offset in the tile (read for wide blocks)
+    const int32_t* tblk;    // [n_slots / kEdgeBlock] narrow block: its first source; wide: -1
     const int32_t* tile_ptr;  // [n_tiles + 1] first slot of each tile (multiples of kEdgeBlock)
     int64_t n_slots;        // tile edge slots, padding included
     const pr::Tile* tiles;

@@ -345,6 +345,7 @@ constexpr int kTileQ = PR_TILE_Q;  // edge blocks per wavefront per round
 struct TileArgs {
     const int32_t* __restrict__ tsrc;
     const uint16_t* __restrict__ tdst;
+    const int32_t* __restrict__ tblk;
     const TileUnit* __restrict__ units;
     const float* __restrict__ inv_out;
     const float* __restrict__ contrib_in;
@@ -390,26 +391,38 @@ __device__ __forceinline__ T load_nt_at(const T* base, uint32_t index) {
 }
 
 // One round of a wavefront: blocks b + j*kTileWaves (j < kTileQ) of the
-// unit, each one 16-byte load of four sources and one 8-byte load of four
-// row offsets per lane (lane l holds edges l, l+64, l+128, l+192 of the
-// block).  Every load is unconditional, so the compiler issues all of a
-// round's loads before waiting for any: a block at or past the unit's end
-// reads its last block instead, and the caller adds zero for it.  The edge
-// arrays are streamed once per iteration: non-temporal.
+// unit, each one 16-byte load of four slots per lane (lane l holds edges l,
+// l+64, l+128, l+192 of the block) and the block's word of tblk (a scalar
+// load: the block index is the same in every lane).  Every load is
+// unconditional, so the compiler issues all of a round's loads before
+// waiting for any: a block at or past the unit's end reads its last block
+// instead, and the caller adds zero for it.  The edge arrays are streamed
+// once per iteration: non-temporal.
 struct EdgeRound {
-    u32x4 src[kTileQ];
-    u32x2 row[kTileQ];
+    u32x4 w[kTileQ];
+    int32_t first[kTileQ];  // narrow block: its first source; wide: -1
 };
 
-__device__ __forceinline__ void load_round(const int32_t* ts, const uint16_t* td, uint32_t b,
+// The block a wavefront reads for its block number q (the same in every lane:
+// readfirstlane lets the compiler keep it in a scalar register).
+__device__ __forceinline__ uint32_t block_of(uint32_t q, uint32_t nblk, uint32_t last) {
+    return __builtin_amdgcn_readfirstlane(q < nblk ? q : last);
+}
+
+// A read-only word at a wave-uniform address, through the scalar cache (the
+// constant address space lets the compiler use a scalar load).
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
+    return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
+__device__ __forceinline__ void load_round(const int32_t* ts, const int32_t* tb, uint32_t b,
                                            uint32_t nblk, uint32_t last, EdgeRound& r) {
     const uint32_t lane = lane_id();
 #pragma unroll
     for (int j = 0; j < kTileQ; ++j) {
-        const uint32_t q = b + (uint32_t)(j * kTileWaves);
-        const uint32_t idx = (q < nblk ? q : last) * (kEdgeBlock / 4) + lane;
-        r.src[j] = load_nt_at((const u32x4*)ts, idx);
-        r.row[j] = load_nt_at((const u32x2*)td, idx);
+        const uint32_t bc = block_of(b + (uint32_t)(j * kTileWaves), nblk, last);
+        r.first[j] = load_uniform(tb + bc);
+        r.w[j] = load_nt_at((const u32x4*)ts, bc * (kEdgeBlock / 4) + lane);
     }
 }
 
@@ -418,30 +431,51 @@ __device__ __forceinline__ void load_round(const int32_t* ts, const uint16_t* td
 // kTileQ per round; `next` holds its first round, loaded by the caller, and
 // each round loads the following one before gathering its own
 // contributions.  In one gather instruction lane l reads the source of edge
-// l + 64*i of a block: consecutive lanes, neighbouring sources.
+// l + 64*i of a block: consecutive lanes, neighbouring sources.  A narrow
+// block decodes its slots; a wide one (rare) loads its rows here.
 __device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_t e1, float scale,
                                            unsigned long long* acc, EdgeRound& next) {
     constexpr uint32_t kStep = (uint32_t)kTileWaves * kTileQ;
     const int32_t* ts = a.tsrc + e0;
     const uint16_t* td = a.tdst + e0;
+    const int32_t* tb = a.tblk + e0 / kEdgeBlock;
     const uint32_t nblk = (uint32_t)(e1 - e0) / kEdgeBlock;
     const uint32_t last = nblk > 0 ? nblk - 1 : 0;
-    for (uint32_t b = threadIdx.x / kWave; b < nblk; b += kStep) {
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    for (uint32_t b = wave; b < nblk; b += kStep) {
         const EdgeRound cur = next;
-        load_round(ts, td, b + kStep, nblk, last, next);
+        load_round(ts, tb, b + kStep, nblk, last, next);
+        uint32_t src[kTileQ][4], row[kTileQ][4];
+#pragma unroll
+        for (int j = 0; j < kTileQ; ++j) {
+            if (cur.first[j] >= 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    src[j][i] = (uint32_t)cur.first[j] + (cur.w[j][i] & 0xFFFFu);
+                    row[j][i] = cur.w[j][i] >> 16;
+                }
+            } else {
+                const uint32_t bc = block_of(b + (uint32_t)(j * kTileWaves), nblk, last);
+                const u32x2 r2 = load_nt_at((const u32x2*)td, bc * (kEdgeBlock / 4) + lane_id());
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    src[j][i] = cur.w[j][i];
+                    row[j][i] = (r2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                }
+            }
+        }
         float v[kTileQ][4];
 #pragma unroll
         for (int j = 0; j < kTileQ; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[j][i] = load_at(a.contrib_in, cur.src[j][i]);
+            for (int i = 0; i < 4; ++i) v[j][i] = load_at(a.contrib_in, src[j][i]);
 #pragma unroll
         for (int j = 0; j < kTileQ; ++j) {
             const bool live = b + (uint32_t)(j * kTileWaves) < nblk;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t row = (cur.row[j][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
                 const unsigned long long f = to_fixed(v[j][i], scale);
-                atomicAdd(&acc[row], live ? f : 0ull);
+                atomicAdd(&acc[row[j][i]], live ? f : 0ull);
             }
         }
     }
@@ -451,12 +485,13 @@ __device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_
 __device__ __forceinline__ void first_round(const TileArgs& a, const TileUnit& u, EdgeRound& r) {
     const uint32_t nblk = (uint32_t)(u.e1 - u.e0) / kEdgeBlock;
     if (nblk > 0) {
-        load_round(a.tsrc + u.e0, a.tdst + u.e0, threadIdx.x / kWave, nblk, nblk - 1, r);
+        load_round(a.tsrc + u.e0, a.tblk + u.e0 / kEdgeBlock,
+                   __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), nblk, nblk - 1, r);
     } else {
 #pragma unroll
         for (int j = 0; j < kTileQ; ++j) {
-            r.src[j] = u32x4{0u, 0u, 0u, 0u};
-            r.row[j] = u32x2{0u, 0u};
+            r.w[j] = u32x4{0u, 0u, 0u, 0u};
+            r.first[j] = 0;
         }
     }
 }
@@ -837,6 +872,7 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     TileArgs ta{};
     ta.tsrc = p->tsrc;
     ta.tdst = p->tdst;
+    ta.tblk = p->tblk;
     ta.units = p->units;
     ta.inv_out = p->inv_out;
     ta.xi = p->xi;

@@ -121,9 +121,10 @@ def test_plan_layout_tiled(prx, g):
     that never straddle a bucket; and the tile edge arrays are the renumbered
     edges sorted by tile, stably from source order, as (source, row offset)
     pairs, each tile padded to whole blocks of 256 edges (padding repeats the
-    tile's last source, row offset 16384) and each block stored transposed
-    (edge 64*i + l of a block at slot 4*l + i) -- all bit for bit against
-    that definition evaluated here."""
+    tile's last source, row offset 16384), each block stored transposed
+    (edge 64*i + l of a block at slot 4*l + i) and packed when its sources
+    span less than 2^16 -- all bit for bit against that definition evaluated
+    here."""
     dg = _cases.gpu_graph(g)
     plan = prx.Plan(dg, flags=prx.PR_VALIDATE)
     assert plan.layout()[0] is None
@@ -131,7 +132,7 @@ def test_plan_layout_tiled(prx, g):
     buckets = plan.buckets()
     _, new_id = _expected_plan_order(g, [b["min_len"] for b in buckets])
     np.testing.assert_array_equal(nid, new_id)
-    tsrc, trow, tptr, row0, rows = plan.tiles()
+    tsrc, trow, tblk, tptr, row0, rows = plan.tiles()
     nt = row0.size
     assert row0[0] == 0 and np.all(rows >= 1) and int(rows.sum()) == g.n
     np.testing.assert_array_equal(row0[1:], (row0 + rows)[:-1])
@@ -160,8 +161,19 @@ def test_plan_layout_tiled(prx, g):
         exp_row[slot[real]] = r_sorted[first[t]:first[t + 1]]
         if count[t] and padded[t] > count[t]:
             exp_src[slot[~real]] = s_sorted[first[t + 1] - 1]
-    np.testing.assert_array_equal(_cases.to_np(tsrc), exp_src)
-    np.testing.assert_array_equal(_cases.to_np(trow).astype(np.int64) & 0xFFFF, exp_row)
+    # block packing: narrow blocks hold (source - first) | row << 16
+    nb = slot0[-1] // 256
+    blk_src = exp_src.reshape(nb, 256)
+    first, last = blk_src[:, 0], blk_src[:, 255]
+    narrow = last - first < (1 << 16)
+    np.testing.assert_array_equal(_cases.to_np(tblk), np.where(narrow, first, -1))
+    packed = ((exp_src.reshape(nb, 256) - first[:, None]) | (exp_row.reshape(nb, 256) << 16))
+    exp_word = np.where(narrow[:, None], packed, exp_src.reshape(nb, 256)).reshape(-1)
+    np.testing.assert_array_equal(_cases.to_np(tsrc).astype(np.int64) & 0xFFFFFFFF,
+                                  exp_word & 0xFFFFFFFF)
+    wide_slots = np.repeat(~narrow, 256)
+    np.testing.assert_array_equal(_cases.to_np(trow).astype(np.int64)[wide_slots] & 0xFFFF,
+                                  exp_row[wide_slots])
 
 
 MODES = [0, "bucketed"]
