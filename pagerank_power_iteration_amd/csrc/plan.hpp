@@ -185,7 +185,8 @@ struct RunState {
     double fx_unit;   // 2^-fx_shift
     int32_t stop;     // 1 once an iteration met the tolerance
     int32_t iters;    // that iteration's number
-    uint32_t pad[56];
+    int32_t signed_contrib;  // 1 if the start vector had a negative entry
+    uint32_t pad[55];
     uint32_t queue[kQueues][64];  // queue heads at [q][0]
 };
 

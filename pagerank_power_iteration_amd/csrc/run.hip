@@ -366,12 +366,13 @@ struct TileArgs {
 // 32-bit halves: hi = trunc(a / 2^32) has at most 24 significant bits, so
 // a - hi * 2^32 is exact too.  The result equals truncating the exact product
 // in double precision, with single-precision instructions only.
+template <bool kSigned>
 __device__ __forceinline__ unsigned long long to_fixed(float c, float scale) {
-    const float a = fabsf(c) * scale;
+    const float a = (kSigned ? fabsf(c) : c) * scale;
     const uint32_t hi = (uint32_t)(a * 0x1p-32f);
     const uint32_t lo = (uint32_t)fmaf(-(float)hi, 0x1p32f, a);
     const unsigned long long r = ((unsigned long long)hi << 32) | lo;
-    return c < 0.f ? 0ull - r : r;
+    return (kSigned && c < 0.f) ? 0ull - r : r;
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -433,6 +434,7 @@ __device__ __forceinline__ void load_round(const int32_t* ts, const int32_t* tb,
 // contributions.  In one gather instruction lane l reads the source of edge
 // l + 64*i of a block: consecutive lanes, neighbouring sources.  A narrow
 // block decodes its slots; a wide one (rare) loads its rows here.
+template <bool kSigned>
 __device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_t e1, float scale,
                                            unsigned long long* acc, EdgeRound& next) {
     constexpr uint32_t kStep = (uint32_t)kTileWaves * kTileQ;
@@ -474,7 +476,7 @@ __device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_
             const bool live = b + (uint32_t)(j * kTileWaves) < nblk;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const unsigned long long f = to_fixed(v[j][i], scale);
+                const unsigned long long f = to_fixed<kSigned>(v[j][i], scale);
                 atomicAdd(&acc[row[j][i]], live ? f : 0ull);
             }
         }
@@ -543,6 +545,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     const Damp k = make_damp(a.d, a.n, st->dmass);
     const float scale = (float)st->fx_scale;  // a power of two, exact in fp32
     const double unit = st->fx_unit;
+    const bool signed_contrib = st->signed_contrib != 0;
     for (int32_t r = threadIdx.x; r < kTileMaxRows; r += kTileBlock) acc[r] = 0ull;
     int32_t cur = blockIdx.x;
     TileUnit u{};
@@ -555,7 +558,10 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     while (cur < a.n_units) {
         uint32_t ticket = 0;
         if (threadIdx.x == 0) ticket = atomicAdd(&st->queue[0][0], 1u);  // needed at the end
-        accumulate(a, u.e0, u.e1, scale, acc, round);
+        if (signed_contrib)
+            accumulate<true>(a, u.e0, u.e1, scale, acc, round);
+        else
+            accumulate<false>(a, u.e0, u.e1, scale, acc, round);
         if (threadIdx.x == 0) s_next = (int32_t)(gridDim.x + ticket);
         __syncthreads();
         const int32_t nxt = s_next;
@@ -741,6 +747,9 @@ __global__ __launch_bounds__(kFinalBlock) void k_finalize(FinArgs f) {
             shift = shift > kFxShiftMax ? kFxShiftMax : (shift < 0 ? 0 : shift);
             st->fx_scale = ldexp(1.0, shift);
             st->fx_unit = ldexp(1.0, -shift);
+            // x0 >= 0 keeps every later x and contribution >= 0 (the update
+            // only adds non-negative terms), so the tiled pull can skip signs
+            st->signed_contrib = r2 > 0.5 ? 1 : 0;
         } else {
             f.l1_trace[f.t - 1] = (float)r0;
             if (f.sum_trace) f.sum_trace[f.t - 1] = (float)r2;
@@ -753,7 +762,8 @@ __global__ __launch_bounds__(kFinalBlock) void k_finalize(FinArgs f) {
 }
 
 // Start vector in plan order (the caller's x0, or 1/n), the first contrib,
-// and per-workgroup sum of |x0|, dangling mass and sum.
+// and per workgroup: sum of |x0|, dangling mass, and the number of negative
+// entries (the third sum's slot; only the sign test of k_finalize reads it).
 __global__ __launch_bounds__(kBlock) void k_init(const int32_t* __restrict__ new_id,
                                                  const float* __restrict__ inv_out,
                                                  const float* __restrict__ x,
@@ -773,7 +783,7 @@ __global__ __launch_bounds__(kBlock) void k_init(const int32_t* __restrict__ new
         contrib[p] = xv * io;
         acc.l1 += fabsf(xv);
         acc.dang += (io == 0.f) ? xv : 0.f;
-        acc.sum += xv;
+        acc.sum += xv < 0.f ? 1.f : 0.f;
     }
     const float l1 = block_sum(acc.l1, red);
     const float dg = block_sum(acc.dang, red);

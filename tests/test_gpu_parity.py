@@ -284,6 +284,25 @@ def test_warm_start_resumes(prx, mode):
 
 
 @pytest.mark.parametrize("mode", MODES, ids=["tiled", "bucketed"])
+def test_signed_start_vector(prx, mode):
+    """A start vector with negative entries: the iteration is the same linear
+    map, so the oracle run from the same x0 must agree.  (The tiled pull
+    converts contributions with their signs only when x0 has a negative entry;
+    a non-negative x0 keeps every later contribution non-negative.)"""
+    g = graphgen.rmat(12)
+    rng = np.random.default_rng(7)
+    x0 = (rng.uniform(-1.0, 3.0, g.n) / g.n).astype(np.float32)
+    assert (x0 < 0).any()
+    plan = prx.Plan(_cases.gpu_graph(g), flags=_flags(prx, mode))
+    res = plan.run(max_iter=30, x0=torch.as_tensor(x0, device="cuda"))
+    torch.cuda.synchronize()
+    ref = oracle.pagerank(g.row_ptr, g.col_idx, max_iter=30, x0=x0.astype(np.float64))
+    x = _cases.to_np(res.x).astype(np.float64)
+    assert np.abs(x - ref.x).sum() <= 1e-5
+    assert np.abs(_cases.to_np(res.l1_trace) - ref.l1_trace).max() <= 2e-5
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["tiled", "bucketed"])
 def test_runs_are_bit_identical(prx, mode):
     g = graphgen.rmat(15)
     plan = prx.Plan(_cases.gpu_graph(g), flags=_flags(prx, mode))
