@@ -530,9 +530,10 @@ __device__ __forceinline__ void update_rows(const TileArgs& a, unsigned long lon
 }
 
 // One workgroup per CU.  Workgroup b starts with unit b, then takes units
-// gridDim.x, gridDim.x + 1, ... from queue 0 until they run out.  A
-// whole-tile unit applies the update to its rows and writes its three sums;
-// a unit of a cut tile writes its accumulators to its slot (and zero sums).
+// gridDim.x, gridDim.x + 1, ... from queue 0, one when its current unit's
+// edges are done, until they run out.  A whole-tile unit applies the update
+// to its rows and writes its three sums; a unit of a cut tile writes its
+// accumulators to its slot (and zero sums).
 // The accumulators are all zero between units: each unit's epilogue clears
 // the rows it read.  The next unit's descriptor and first round of edges are
 // loaded before this unit's epilogue, so their latency overlaps it.
@@ -556,13 +557,13 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     }
     __syncthreads();
     while (cur < a.n_units) {
-        uint32_t ticket = 0;
-        if (threadIdx.x == 0) ticket = atomicAdd(&st->queue[0][0], 1u);  // needed at the end
         if (signed_contrib)
             accumulate<true>(a, u.e0, u.e1, scale, acc, round);
         else
             accumulate<false>(a, u.e0, u.e1, scale, acc, round);
-        if (threadIdx.x == 0) s_next = (int32_t)(gridDim.x + ticket);
+        // claim the next unit only now: a claim made earlier would hold a
+        // unit back behind this one while other workgroups run out of work
+        if (threadIdx.x == 0) s_next = (int32_t)(gridDim.x + atomicAdd(&st->queue[0][0], 1u));
         __syncthreads();
         const int32_t nxt = s_next;
         TileUnit un{};
