@@ -748,26 +748,46 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
     k_tile_first<<<grid_for((int64_t)tiles + 1, 1024), kBlock, 0, stream>>>(in_rp_plan, n, tiles, map,
                                                                             first);
     PR_LAUNCHED("tile starts");
-    // edges sorted by tile, stably (so by source inside a tile): keys are the
-    // targets, values the sources (into s.order)
+    std::vector<int32_t> tp((size_t)tiles + 1);
+    PR_HIP_TRY(hipMemcpyAsync(tp.data(), first, sizeof(int32_t) * tp.size(), hipMemcpyDeviceToHost,
+                              stream));
+    PR_HIP_TRY(hipStreamSynchronize(stream));
+    // Edges sorted by tile, stably (so by source inside a tile): keys are the
+    // targets, values the sources (into s.order).  One full pass sorts by
+    // min(tile, 255); the edges of tiles 255 and up (the light tiles, which
+    // come last and hold few edges) form one range, [tp[255], nnz), which is
+    // then sorted by tile on its own.
     const int32_t* sorted_targets = nullptr;
     if (nnz > 0) {
+        constexpr int32_t kCap = kRadixDigits - 1;
         RadixIn in{};
         in.count = nnz;
         in.n = n;
         in.keys = s.perm_ci;
         in.vals = s.src_of;
         in.tiles = map;
+        in.tile_cap = kCap;
         in.error = s.tr.error;
         int32_t* keys_sorted = nullptr;
-        PR_TRY(radix_sort<kFromTileTargets>(in, vertex_bits(tiles), s.order, s.tr.sort,
-                                             &keys_sorted, stream));
+        PR_TRY(radix_sort<kFromTileTargets>(in, kRadixBits, s.order, s.tr.sort, &keys_sorted, stream));
         sorted_targets = keys_sorted;
+        const int64_t lo = tiles > kCap ? tp[(size_t)kCap] : nnz;
+        if (lo < nnz) {
+            RadixIn rest{};
+            rest.count = nnz - lo;
+            rest.n = n;
+            rest.keys = keys_sorted + lo;
+            rest.vals = s.order + lo;
+            rest.tiles = map;
+            rest.tile_base = kCap;
+            rest.error = s.tr.error;
+            // scratch: the other ping-pong pair, and the sort's inputs (free now)
+            int32_t* const sk[2] = {s.tr.sort.key[1], s.perm_ci};
+            int32_t* const sv[2] = {s.tr.sort.val[1], s.src_of};
+            PR_TRY(radix_sort_to<kFromTileTargets>(rest, vertex_bits(tiles - kCap), keys_sorted + lo,
+                                                   s.order + lo, sk, sv, s.tr.sort, stream));
+        }
     }
-    std::vector<int32_t> tp((size_t)tiles + 1);
-    PR_HIP_TRY(hipMemcpyAsync(tp.data(), first, sizeof(int32_t) * tp.size(), hipMemcpyDeviceToHost,
-                              stream));
-    PR_HIP_TRY(hipStreamSynchronize(stream));
     std::vector<int32_t> sp((size_t)tiles + 1, 0);
     {
         int64_t q = 0;

@@ -79,6 +79,8 @@ struct RadixIn {
     const int32_t* vals;           // kFromPairs, kFromTileTargets
     const int32_t* row_ptr;        // kFromOutCsr: out_row_ptr
     TileMap tiles;                 // kFromTileTargets
+    int32_t tile_base = 0;         // kFromTileTargets: the digit is
+    int32_t tile_cap = INT32_MAX;  //   min(tile_of(key) - tile_base, tile_cap)
     uint32_t* error;               // set to 1 when an input index is out of range
 };
 
@@ -117,7 +119,11 @@ __device__ __forceinline__ int32_t radix_check(const RadixIn& in, int32_t k) {
 // The digit a pass sorts by: of the key, or of the key's tile.
 template <int MODE>
 __device__ __forceinline__ uint32_t radix_digit(const RadixIn& in, int32_t k, int shift) {
-    const uint32_t d = MODE == kFromTileTargets ? (uint32_t)tile_of(in.tiles, k) : (uint32_t)k;
+    uint32_t d = (uint32_t)k;
+    if (MODE == kFromTileTargets) {
+        const int32_t t = tile_of(in.tiles, k) - in.tile_base;
+        d = (uint32_t)(t < in.tile_cap ? t : in.tile_cap);
+    }
     return (d >> shift) & (kRadixDigits - 1);
 }
 
@@ -328,6 +334,35 @@ int radix_sort(RadixIn in, int bits, int32_t* vals_out, const RadixWs& w, int32_
         in.keys = kout;
         in.vals = vout;
         *keys_sorted = kout;
+    }
+    return PR_OK;
+}
+
+// Stable LSD sort of `count` >= 1 pairs (read per MODE) by the low `bits`
+// bits of the digit, in max(2, ceil(bits / 8)) passes: pass p writes the
+// scratch pair p & 1, the last pass (keys_out, vals_out).  The input may be
+// the output range itself (the first pass writes scratch); the scratch pairs
+// must not overlap the input, the output or each other.
+template <int MODE>
+int radix_sort_to(RadixIn in, int bits, int32_t* keys_out, int32_t* vals_out,
+                  int32_t* const scratch_keys[2], int32_t* const scratch_vals[2], const RadixWs& w,
+                  hipStream_t stream) {
+    if (in.count < 1) return fail(PR_ERR_ARG, "radix sort of %lld elements", (long long)in.count);
+    const int64_t T = radix_tiles(in.count);
+    int passes = (bits + kRadixBits - 1) / kRadixBits;
+    if (passes < 2) passes = 2;
+    for (int p = 0; p < passes; ++p) {
+        const bool last = p == passes - 1;
+        int32_t* kout = last ? keys_out : scratch_keys[p & 1];
+        int32_t* vout = last ? vals_out : scratch_vals[p & 1];
+        k_radix_hist<MODE><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, p * kRadixBits, T, w.hist);
+        PR_LAUNCHED("radix histogram");
+        PR_TRY(scan_exclusive(w.hist, w.scanned, kRadixDigits * T, w.scan_ws, stream));
+        k_radix_scatter<MODE><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, p * kRadixBits, T, w.scanned,
+                                                                         kout, vout);
+        PR_LAUNCHED("radix scatter");
+        in.keys = kout;
+        in.vals = vout;
     }
     return PR_OK;
 }

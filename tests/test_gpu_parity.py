@@ -115,8 +115,7 @@ def test_plan_layout_bucketed(prx, g):
     assert start == g.n
 
 
-@pytest.mark.parametrize("g", SMALL, ids=lambda g: g.name)
-def test_plan_layout_tiled(prx, g):
+def _check_tiled_layout(prx, g):
     """Tiled plans: the same renumbering; tiles are consecutive row blocks
     that never straddle a bucket; and the tile edge arrays are the renumbered
     edges sorted by tile, stably from source order, as (source, row offset)
@@ -174,6 +173,25 @@ def test_plan_layout_tiled(prx, g):
     wide_slots = np.repeat(~narrow, 256)
     np.testing.assert_array_equal(_cases.to_np(trow).astype(np.int64)[wide_slots] & 0xFFFF,
                                   exp_row[wide_slots])
+
+
+@pytest.mark.parametrize("g", SMALL, ids=lambda g: g.name)
+def test_plan_layout_tiled(prx, g):
+    _check_tiled_layout(prx, g)
+
+
+def test_plan_layout_many_tiles(prx, monkeypatch):
+    """More than 255 tiles (small tiles forced by the tuning knob): the tile
+    sort then takes the light tiles' range in a second sort of its own."""
+    monkeypatch.setenv("PR_TILE_EDGES", "4096")
+    g = graphgen.rmat(17)  # 373 tiles
+    _check_tiled_layout(prx, g)
+    plan = prx.Plan(_cases.gpu_graph(g), flags=prx.PR_VALIDATE)
+    assert plan.tiles()[5].size > 255
+    res = plan.run(d=D, tol=0.0, max_iter=30)
+    torch.cuda.synchronize()
+    ref = oracle.pagerank(g.row_ptr, g.col_idx, d=D, max_iter=30)
+    assert np.abs(_cases.to_np(res.x).astype(np.float64) - ref.x).sum() <= 1e-5
 
 
 MODES = [0, "bucketed"]
