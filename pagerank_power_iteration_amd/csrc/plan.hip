@@ -459,27 +459,41 @@ __global__ __launch_bounds__(kBlock) void k_tile_first(const uint32_t* __restric
 }
 
 // The tile edge arrays: sorted edge i (target targets[i], source sources[i])
-// is edge i - first[t] of its tile t and goes to slot
-// slot0[t] + block_slot(i - first[t]) with its source and its row offset in
-// the tile.
+// is edge k = i - first[t] of its tile t and goes to slot
+// slot0[t] + block_slot(k).  Its block is narrow when the block's sources
+// (its first edge and its last real one; padding repeats the last) span less
+// than kNarrowSpan: the slot then holds (source - first source) | row << 16,
+// otherwise the source, with the row in tdst.  The block's first edge writes
+// its tblk word.
 __global__ __launch_bounds__(kBlock) void k_tile_edges(const int32_t* __restrict__ targets,
                                                        const int32_t* __restrict__ sources,
                                                        int64_t nnz, TileMap map,
                                                        const int32_t* __restrict__ first,
                                                        const int32_t* __restrict__ slot0,
                                                        int32_t* __restrict__ tsrc,
-                                                       uint16_t* __restrict__ tdst) {
+                                                       uint16_t* __restrict__ tdst,
+                                                       int32_t* __restrict__ tblk) {
     GRID_STRIDE(i, nnz) {
         const TileSpot at = tile_locate(map, targets[i]);
-        const int64_t q = slot0[at.tile] + block_slot(i - first[at.tile]);
-        tsrc[q] = sources[i];
-        tdst[q] = (uint16_t)at.offset;
+        const int64_t f = first[at.tile];
+        const int64_t cnt = first[at.tile + 1] - f;
+        const int64_t k = i - f;
+        const int64_t kb = k & ~(int64_t)(kEdgeBlock - 1);
+        const int64_t kl = kb + kEdgeBlock - 1 < cnt ? kb + kEdgeBlock - 1 : cnt - 1;
+        const int32_t lo = sources[f + kb], hi = sources[f + kl];
+        const bool narrow = hi - lo < kNarrowSpan;
+        const int64_t q = slot0[at.tile] + block_slot(k);
+        const int32_t src = sources[i];
+        tsrc[q] = narrow ? (src - lo) | (at.offset << 16) : src;
+        if (!narrow) tdst[q] = (uint16_t)at.offset;
+        if (k == kb) tblk[(slot0[at.tile] + kb) / kEdgeBlock] = narrow ? lo : -1;
     }
 }
 
 // Padding of each tile's last block: the tile's last source and the trash
-// row (a tile without edges has no slots).
+// row, in the block's form (a tile without edges has no slots).
 __global__ __launch_bounds__(kBlock) void k_tile_pad(int32_t tiles, const int32_t* __restrict__ first,
+                                                     const int32_t* __restrict__ sources,
                                                      const int32_t* __restrict__ slot0,
                                                      int32_t* __restrict__ tsrc,
                                                      uint16_t* __restrict__ tdst) {
@@ -487,11 +501,13 @@ __global__ __launch_bounds__(kBlock) void k_tile_pad(int32_t tiles, const int32_
         const int32_t count = first[t + 1] - first[t];
         const int32_t padded = slot0[t + 1] - slot0[t];
         if (padded == count) continue;
-        const int32_t last = tsrc[slot0[t] + block_slot(count - 1)];
+        const int32_t kb = (count - 1) & ~(kEdgeBlock - 1);
+        const int32_t lo = sources[first[t] + kb], last = sources[first[t] + count - 1];
+        const bool narrow = last - lo < kNarrowSpan;
         for (int32_t k = count + threadIdx.x; k < padded; k += kBlock) {
             const int64_t q = slot0[t] + block_slot(k);
-            tsrc[q] = last;
-            tdst[q] = (uint16_t)kTrashRow;
+            tsrc[q] = narrow ? (last - lo) | (kTrashRow << 16) : last;
+            if (!narrow) tdst[q] = (uint16_t)kTrashRow;
         }
     }
 }
@@ -503,7 +519,14 @@ __global__ __launch_bounds__(kBlock) void k_tile_pad(int32_t tiles, const int32_
 // this counts the distinct sectors a range of edges gathers (a tile boundary
 // may merge one sector with the previous tile's last: a count, not an exact
 // figure).
+__device__ __forceinline__ int32_t slot_source(const int32_t* __restrict__ tsrc,
+                                               const int32_t* __restrict__ tblk, int64_t i) {
+    const int32_t w = tsrc[block_slot(i)], b = tblk[i / kEdgeBlock];
+    return b >= 0 ? b + (w & (kNarrowSpan - 1)) : w;
+}
+
 __global__ __launch_bounds__(kBlock) void k_sector_counts(const int32_t* __restrict__ tsrc,
+                                                          const int32_t* __restrict__ tblk,
                                                           int64_t slots, int32_t chunks,
                                                           int32_t* __restrict__ counts) {
     __shared__ int32_t red[kBlock / kWave];
@@ -512,39 +535,11 @@ __global__ __launch_bounds__(kBlock) void k_sector_counts(const int32_t* __restr
         const int64_t hi = lo + kSectorChunk < slots ? lo + kSectorChunk : slots;
         int32_t k = 0;
         for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock) {
-            const int32_t a = tsrc[block_slot(i)] >> kSectorShift;
-            k += (i == 0 || a != (tsrc[block_slot(i - 1)] >> kSectorShift)) ? 1 : 0;
+            const int32_t a = slot_source(tsrc, tblk, i) >> kSectorShift;
+            k += (i == 0 || a != (slot_source(tsrc, tblk, i - 1) >> kSectorShift)) ? 1 : 0;
         }
         k = block_sum(k, red);
         if (threadIdx.x == 0) counts[c] = k;
-    }
-}
-
-// Narrow blocks (see kNarrowSpan): one wavefront per block reads the
-// block's sources and rows, and a narrow block rewrites its source slots in
-// place as (source - first) | row << 16.
-__global__ __launch_bounds__(kBlock) void k_tile_pack(int64_t blocks, int32_t* __restrict__ tsrc,
-                                                      const uint16_t* __restrict__ tdst,
-                                                      int32_t* __restrict__ tblk) {
-    const int lane = lane_id();
-    for (int64_t b = blockIdx.x * (int64_t)kWaves + threadIdx.x / kWave; b < blocks;
-         b += (int64_t)gridDim.x * kWaves) {
-        int32_t* w = tsrc + b * kEdgeBlock + 4 * lane;
-        const uint16_t* r = tdst + b * kEdgeBlock + 4 * lane;
-        int32_t src[4], row[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            src[i] = w[i];
-            row[i] = r[i];
-        }
-        const int32_t first = __shfl(src[0], 0);     // edge 0 of the block: slot 0
-        const int32_t last = __shfl(src[3], kWave - 1);  // edge 255: slot 255
-        const bool narrow = last - first < kNarrowSpan;
-        if (lane == 0) tblk[b] = narrow ? first : -1;
-        if (narrow) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = (src[i] - first) | (row[i] << 16);
-        }
     }
 }
 
@@ -804,10 +799,11 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
                               hipMemcpyHostToDevice, stream));
     if (nnz > 0) {
         k_tile_edges<<<grid_for(nnz, 8192), kBlock, 0, stream>>>(sorted_targets, s.order, nnz, map,
-                                                                 first, w.tile_ptr, w.tsrc, w.tdst);
+                                                                 first, w.tile_ptr, w.tsrc, w.tdst,
+                                                                 w.tblk);
         PR_LAUNCHED("tile edges");
         k_tile_pad<<<dim3((unsigned)(tiles < 8192 ? tiles : 8192)), kBlock, 0, stream>>>(
-            tiles, first, w.tile_ptr, w.tsrc, w.tdst);
+            tiles, first, s.order, w.tile_ptr, w.tsrc, w.tdst);
         PR_LAUNCHED("tile padding");
     }
     // sector starts per chunk of slots (s.order is free again)
@@ -815,17 +811,10 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
     std::vector<int32_t> sc((size_t)chunks);
     if (chunks > 0) {
         k_sector_counts<<<grid_for((int64_t)chunks * kBlock, 8192), kBlock, 0, stream>>>(
-            w.tsrc, slots, chunks, s.order);
+            w.tsrc, w.tblk, slots, chunks, s.order);
         PR_LAUNCHED("sector counts");
         PR_HIP_TRY(hipMemcpyAsync(sc.data(), s.order, sizeof(int32_t) * sc.size(),
                                   hipMemcpyDeviceToHost, stream));
-    }
-    if (slots > 0) {  // after the sector counts, which read the plain sources
-        const int64_t blocks = slots / kEdgeBlock;
-        const int64_t groups = ceil_div(blocks, kWaves);
-        k_tile_pack<<<dim3((unsigned)(groups < 8192 ? groups : 8192)), kBlock, 0, stream>>>(
-            blocks, w.tsrc, w.tdst, w.tblk);
-        PR_LAUNCHED("tile blocks");
     }
     PR_HIP_TRY(hipStreamSynchronize(stream));
     // cost prefix at chunk boundaries: slots + kSectorWeight * sectors
