@@ -115,7 +115,7 @@ PlanWs carve_ws(void* base, int32_t n, int64_t nnz, bool tiled) {
     w.contrib1 = c.take<float>((size_t)n);
     const int64_t batches = ceil_div(w.n_items_max, kBatchItems);
     w.part_stride = (batches > w.n_units_max ? batches : w.n_units_max) + kMaxGrid;
-    w.part = c.take<float>((size_t)(3 * w.part_stride));
+    w.part = c.take<float>((size_t)(6 * w.part_stride));  // two sets of [3][stride]
     w.state = c.take<RunState>(1);
     if (!tiled) {
         w.in_rp = c.take<int32_t>((size_t)n + 1);

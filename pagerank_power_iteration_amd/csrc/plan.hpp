@@ -186,7 +186,8 @@ struct RunState {
     int32_t stop;     // 1 once an iteration met the tolerance
     int32_t iters;    // that iteration's number
     int32_t signed_contrib;  // 1 if the start vector had a negative entry
-    uint32_t pad[55];
+    int32_t fx_shift;
+    uint32_t pad[54];
     uint32_t queue[kQueues][64];  // queue heads at [q][0]
 };
 
@@ -219,8 +220,9 @@ struct pr_plan {
     const pr::ChunkRow* chunk_rows;
     int32_t n_chunk_rows;
     float* hub_part;       // chunk sums
-    float* part;           // [3][part_stride]: L1, dangling mass and sum of x' per
-                           // item batch, then per k_hubfix workgroup
+    float* part;           // 2 x [3][part_stride]: L1, dangling mass and sum of x' per
+                           // item batch or unit, then per k_hubfix / k_tilefix
+                           // workgroup (tiled runs alternate the two sets)
     int64_t part_stride;
     int32_t n_batches;
     pr::RunState* state;

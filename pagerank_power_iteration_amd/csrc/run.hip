@@ -209,6 +209,53 @@ __device__ __forceinline__ T wide_block_sum(T v, T* scratch) {
     return r;
 }
 
+// Sums of part[0, count), part[stride + ...) and part[2*stride + ...) in
+// double: lane i adds entries i, i + kThreads, ... in that order (eight loads
+// in flight), then the workgroup adds the lanes.  The same inputs give the
+// same sums in every workgroup.  Contains barriers.
+struct Sums3 {
+    double l1, dang, sum;
+};
+
+template <int kThreads>
+__device__ __forceinline__ Sums3 sum_parts(const float* __restrict__ part, int64_t stride,
+                                           int32_t count, double* redd) {
+    constexpr int kUnroll = 8;
+    double r0 = 0.0, r1 = 0.0, r2 = 0.0;
+    for (int j0 = threadIdx.x; j0 < count; j0 += kUnroll * kThreads) {
+        float v0[kUnroll], v1[kUnroll], v2[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int j = j0 + u * kThreads;
+            const bool in = j < count;
+            v0[u] = in ? part[j] : 0.f;
+            v1[u] = in ? part[stride + j] : 0.f;
+            v2[u] = in ? part[2 * stride + j] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            r0 += (double)v0[u];
+            r1 += (double)v1[u];
+            r2 += (double)v2[u];
+        }
+    }
+    Sums3 r;
+    r.l1 = wide_block_sum<double, kThreads / kWave>(r0, redd);
+    r.dang = wide_block_sum<double, kThreads / kWave>(r1, redd);
+    r.sum = wide_block_sum<double, kThreads / kWave>(r2, redd);
+    return r;
+}
+
+// Fixed-point shift of the tiled pull: every row sum of every iteration is
+// bounded by max(1, sum |x0|) (the update does not grow the L1 norm beyond
+// it), so 2^shift times that stays below 2^61.
+__device__ __forceinline__ int fx_shift(double sum_abs_x0) {
+    int ex = 0;
+    (void)frexp(sum_abs_x0 > 1.0 ? sum_abs_x0 : 1.0, &ex);
+    const int shift = 61 - ex;
+    return shift > kFxShiftMax ? kFxShiftMax : (shift < 0 ? 0 : shift);
+}
+
 // A wavefront's next batch: lane 0 increments queue heads, starting with
 // queue *q, until one yields a batch that holds items; -1 when every queue is
 // empty.  `ticket` is the value the last increment of queue *q returned.
@@ -352,12 +399,18 @@ struct TileArgs {
     float* __restrict__ contrib_out;
     float* __restrict__ xi;
     long long* __restrict__ partial;
-    float* __restrict__ part;  // [3][stride]: per-unit sums
+    float* __restrict__ part;  // [3][stride]: this iteration's per-unit sums
+    const float* __restrict__ part_prev;  // [3][stride]: the previous iteration's
     int64_t stride;
     RunState* state;
+    float* __restrict__ l1_trace;
+    float* __restrict__ sum_trace;
     double d;
+    double tol;
     int32_t n;
     int32_t n_units;
+    int32_t parts_prev;  // sums in part_prev
+    int32_t t;           // iteration number, from 1
 };
 
 // Fixed point of one contribution: |c| * 2^shift truncated toward zero, with
@@ -541,12 +594,47 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     __shared__ unsigned long long acc[kTileMaxRows + 1];  // + the trash row of padding edges
     __shared__ float red[3][kTileWaves];
     __shared__ int32_t s_next;
+    __shared__ double redd[kTileWaves];
     RunState* st = a.state;
     if (st->stop) return;  // an earlier iteration met the tolerance
-    const Damp k = make_damp(a.d, a.n, st->dmass);
-    const float scale = (float)st->fx_scale;  // a power of two, exact in fp32
-    const double unit = st->fx_unit;
-    const bool signed_contrib = st->signed_contrib != 0;
+    // The previous iteration's (or k_init's) sums, reduced by every workgroup
+    // in the same order: its L1 distance (the stop test), its dangling mass D,
+    // and -- after k_init -- sum |x0| and the count of negative entries.
+    const Sums3 prev = sum_parts<kTileBlock>(a.part_prev, a.stride, a.parts_prev, redd);
+    if (a.t > 1 && a.tol > 0.0 && prev.l1 < a.tol) {  // iteration t - 1 met the tolerance
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            a.l1_trace[a.t - 2] = (float)prev.l1;
+            if (a.sum_trace) a.sum_trace[a.t - 2] = (float)prev.sum;
+            st->stop = 1;
+            st->iters = a.t - 1;
+        }
+        return;
+    }
+    int shift;
+    bool signed_contrib;
+    if (a.t == 1) {
+        shift = fx_shift(prev.l1);
+        signed_contrib = prev.sum > 0.5;
+    } else {
+        shift = st->fx_shift;
+        signed_contrib = st->signed_contrib != 0;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        st->dmass = prev.dang;  // for k_tilefix
+        st->queue[(a.t + 1) & 1][0] = 0u;  // the next iteration's queue
+        if (a.t == 1) {
+            st->fx_shift = shift;
+            st->fx_unit = ldexp(1.0, -shift);
+            st->signed_contrib = signed_contrib ? 1 : 0;
+        } else {
+            a.l1_trace[a.t - 2] = (float)prev.l1;
+            if (a.sum_trace) a.sum_trace[a.t - 2] = (float)prev.sum;
+        }
+    }
+    const Damp k = make_damp(a.d, a.n, prev.dang);
+    const float scale = ldexpf(1.0f, shift);  // a power of two, exact in fp32
+    const double unit = ldexp(1.0, -shift);
+    uint32_t* queue = &st->queue[a.t & 1][0];
     for (int32_t r = threadIdx.x; r < kTileMaxRows; r += kTileBlock) acc[r] = 0ull;
     int32_t cur = blockIdx.x;
     TileUnit u{};
@@ -563,7 +651,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
             accumulate<false>(a, u.e0, u.e1, scale, acc, round);
         // claim the next unit only now: a claim made earlier would hold a
         // unit back behind this one while other workgroups run out of work
-        if (threadIdx.x == 0) s_next = (int32_t)(gridDim.x + atomicAdd(&st->queue[0][0], 1u));
+        if (threadIdx.x == 0) s_next = (int32_t)(gridDim.x + atomicAdd(queue, 1u));
         __syncthreads();
         const int32_t nxt = s_next;
         TileUnit un{};
@@ -709,52 +797,24 @@ __global__ __launch_bounds__(kFinalBlock) void k_finalize(FinArgs f) {
     __shared__ double redd[kFinalWaves];
     RunState* st = f.state;
     if (f.t > 0 && st->stop) return;
-    // lane i adds entries i, i + 1024, ... in that order, eight loads in flight
-    constexpr int kUnroll = 8;
-    double r0 = 0.0, r1 = 0.0, r2 = 0.0;
-    for (int j0 = threadIdx.x; j0 < f.parts; j0 += kUnroll * kFinalBlock) {
-        float v0[kUnroll], v1[kUnroll], v2[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int j = j0 + u * kFinalBlock;
-            const bool in = j < f.parts;
-            v0[u] = in ? f.part[j] : 0.f;
-            v1[u] = in ? f.part[f.stride + j] : 0.f;
-            v2[u] = in ? f.part[2 * f.stride + j] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            r0 += (double)v0[u];
-            r1 += (double)v1[u];
-            r2 += (double)v2[u];
-        }
-    }
-    r0 = wide_block_sum<double, kFinalWaves>(r0, redd);
-    r1 = wide_block_sum<double, kFinalWaves>(r1, redd);
-    r2 = wide_block_sum<double, kFinalWaves>(r2, redd);
+    const Sums3 r = sum_parts<kFinalBlock>(f.part, f.stride, f.parts, redd);
     if (threadIdx.x < kQueues) st->queue[threadIdx.x][0] = 0u;
     if (threadIdx.x == 0) {
-        st->dmass = r1;
+        st->dmass = r.dang;
         if (f.t == 0) {
             st->stop = 0;
             st->iters = 0;
-            // Fixed-point scale of the tiled pull: every row sum of every
-            // iteration is bounded by max(1, sum |x0|) (the update does not
-            // grow the L1 norm beyond it), so 2^shift times that stays below
-            // 2^61.
-            int ex = 0;
-            (void)frexp(r0 > 1.0 ? r0 : 1.0, &ex);
-            int shift = 61 - ex;
-            shift = shift > kFxShiftMax ? kFxShiftMax : (shift < 0 ? 0 : shift);
+            const int shift = fx_shift(r.l1);
+            st->fx_shift = shift;
             st->fx_scale = ldexp(1.0, shift);
             st->fx_unit = ldexp(1.0, -shift);
             // x0 >= 0 keeps every later x and contribution >= 0 (the update
             // only adds non-negative terms), so the tiled pull can skip signs
-            st->signed_contrib = r2 > 0.5 ? 1 : 0;
+            st->signed_contrib = r.sum > 0.5 ? 1 : 0;
         } else {
-            f.l1_trace[f.t - 1] = (float)r0;
-            if (f.sum_trace) f.sum_trace[f.t - 1] = (float)r2;
-            if (f.tol > 0.0 && r0 < f.tol) {
+            f.l1_trace[f.t - 1] = (float)r.l1;
+            if (f.sum_trace) f.sum_trace[f.t - 1] = (float)r.sum;
+            if (f.tol > 0.0 && r.l1 < f.tol) {
                 st->stop = 1;
                 st->iters = f.t;
             }
@@ -771,8 +831,15 @@ __global__ __launch_bounds__(kBlock) void k_init(const int32_t* __restrict__ new
                                                  float* __restrict__ xi,
                                                  float* __restrict__ contrib, int32_t n,
                                                  int x0_given, float* __restrict__ part,
-                                                 int64_t stride) {
+                                                 int64_t stride, RunState* __restrict__ st) {
     __shared__ float red[kWaves];
+    if (blockIdx.x == 0 && threadIdx.x < kQueues) {  // a fresh run: no stop, empty queues
+        st->queue[threadIdx.x][0] = 0u;
+        if (threadIdx.x == 0) {
+            st->stop = 0;
+            st->iters = 0;
+        }
+    }
     const float uniform = (float)(1.0 / (double)n);
     Acc acc;
     for (int64_t v = blockIdx.x * (int64_t)kBlock + threadIdx.x; v < n;
@@ -832,13 +899,18 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         return fail(PR_ERR_ARG, "plan belongs to device %d but device %d is current", p->device, dev);
     hipStream_t stream = as_stream(stream_v);
 
+    // Per-iteration sums: part holds two [3][stride] sets.  A tiled run
+    // alternates them (iteration t writes set t & 1, and k_tile reduces the
+    // previous set itself: no k_finalize per iteration); a bucketed run uses
+    // set 0 and k_finalize after every iteration.
+    float* part_set[2] = {p->part, p->part + 3 * p->part_stride};
     k_init<<<dim3((unsigned)p->init_grid), kBlock, 0, stream>>>(
         p->new_id, p->inv_out, x, p->xi, p->contrib[0], p->n, (flags & PR_X0_GIVEN) ? 1 : 0,
-        p->part, p->part_stride);
+        part_set[0], p->part_stride, p->state);
     PR_LAUNCHED("init");
 
     FinArgs f{};
-    f.part = p->part;
+    f.part = part_set[0];
     f.stride = p->part_stride;
     f.state = p->state;
     f.l1_trace = l1_trace;
@@ -846,11 +918,14 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     f.tol = tol;
     f.parts = p->init_grid;
     f.t = 0;
-    k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
-    PR_LAUNCHED("init finalize");
+    if (!p->tiled) {
+        k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
+        PR_LAUNCHED("init finalize");
+    }
     int32_t tilefix_grid = (int32_t)((p->n_fix_rows + kFixBlock - 1) / kFixBlock);
     if (tilefix_grid > kMaxGrid) tilefix_grid = kMaxGrid;
-    f.parts = p->tiled ? p->n_units + tilefix_grid : p->n_batches + p->fix_grid;
+    const int32_t iter_parts = p->tiled ? p->n_units + tilefix_grid : p->n_batches + p->fix_grid;
+    f.parts = iter_parts;
 
     IterArgs a{};
     a.in_rp = p->in_rp;
@@ -888,10 +963,12 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     ta.inv_out = p->inv_out;
     ta.xi = p->xi;
     ta.partial = p->partial;
-    ta.part = p->part;
     ta.stride = p->part_stride;
     ta.state = p->state;
+    ta.l1_trace = l1_trace;
+    ta.sum_trace = sum_trace;
     ta.d = d;
+    ta.tol = tol;
     ta.n = p->n;
     ta.n_units = p->n_units;
 
@@ -923,6 +1000,10 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         if (p->tiled) {
             ta.contrib_in = a.contrib_in;
             ta.contrib_out = a.contrib_out;
+            ta.part = part_set[t & 1];
+            ta.part_prev = part_set[(t - 1) & 1];
+            ta.parts_prev = t == 1 ? p->init_grid : iter_parts;
+            ta.t = t;
             k_tile<<<dim3((unsigned)p->tile_grid), kTileBlock, 0, stream>>>(ta);
             PR_LAUNCHED("tile");
         } else {
@@ -935,6 +1016,7 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         }
         if (p->tiled && tilefix_grid > 0) {
             tf.contrib_out = a.contrib_out;
+            tf.part = part_set[t & 1];
             k_tilefix<<<dim3((unsigned)tilefix_grid), kFixBlock, 0, stream>>>(tf);
             PR_LAUNCHED("tile rows");
         }
@@ -943,9 +1025,22 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
             k_hubfix<<<dim3((unsigned)p->fix_grid), kFixBlock, 0, stream>>>(fx);
             PR_LAUNCHED("hub rows");
         }
-        f.t = t;
-        k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
-        PR_LAUNCHED("finalize");
+        if (!p->tiled) {
+            f.t = t;
+            k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
+            PR_LAUNCHED("finalize");
+        }
+        return PR_OK;
+    };
+    // A tiled run reduces its last iteration's sums here (every earlier
+    // iteration's were reduced by the next k_tile).
+    auto close = [&](int32_t t_last) -> int {
+        if (p->tiled) {
+            f.t = t_last;
+            f.part = part_set[t_last & 1];
+            k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
+            PR_LAUNCHED("finalize");
+        }
         return PR_OK;
     };
     auto finish = [&]() -> int {
@@ -960,6 +1055,7 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
 
     if (tol <= 0.0) {
         for (int32_t t = 1; t <= max_iter; ++t) PR_TRY(launch(t));
+        PR_TRY(close(max_iter));
         PR_TRY(finish());
         *iterations = max_iter;
         return PR_OK;
@@ -985,6 +1081,9 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         slot ^= 1;
         t = t_end + 1;
     }
+    PR_TRY(close(t - 1));
+    PR_HIP_TRY(hipMemcpyAsync(&p->host_status[slot ^ 1], &p->state->stop, sizeof(RunStatus),
+                              hipMemcpyDeviceToHost, stream));
     PR_TRY(finish());
     PR_HIP_TRY(hipStreamSynchronize(stream));
     const RunStatus& last = p->host_status[slot ^ 1];  // copied after every launched iteration
