@@ -102,6 +102,28 @@ def cpu_baseline(g, iters: int) -> dict:
                       f"(fp64, single thread, iteration loop only: {secs:.2f} s)"}
 
 
+def workload_rate(torch, prx, graphgen, name: str, iters: int) -> dict:
+    """Per-iteration rate of one more workload: a plan, one warm-up run, then
+    `iters` timed iterations (median of 3 runs) and the gather kernel's mean
+    launch time against the same roofline."""
+    g = graphgen.workload(name)
+    dg = prx.DeviceGraph.from_csr(g.row_ptr, g.col_idx)
+    plan = prx.Plan(dg)
+    plan.run(max_iter=3)
+    its, kms = [], []
+    for _ in range(3):
+        plan.run(max_iter=iters, record_events=True)
+        its.append(plan.iteration_ms() / iters)
+        kms.append(plan.kernel_ms()[0])
+    plan.close()
+    it, km = statistics.median(its), statistics.median(kms)
+    b = min_bytes_per_iteration(g.n, g.m)
+    return {"n": g.n, "m": g.m, "iteration_ms": round(it, 5),
+            "gteps": round(g.m / (it * 1e-3) / 1e9, 2), "kernel_ms": round(km, 5),
+            "roofline_frac": round(b / (km * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "iteration_frac": round(b / (it * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +134,9 @@ def main() -> int:
     ap.add_argument("--cpu-iters", type=int, default=8,
                     help="iterations of the CPU oracle sample (0 skips it)")
     ap.add_argument("--no-copy-row", action="store_true")
+    ap.add_argument("--workloads", default="",
+                    help="comma-separated extra workloads (e.g. citation,stencil100,rmat18,rmat21) "
+                         "whose per-iteration rate is added under 'workloads'")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -202,6 +227,11 @@ def main() -> int:
     torch.cuda.empty_cache()
     copy_gbps = None if args.no_copy_row else round(copy_row(torch), 1)
 
+    extra = {}
+    for name in [w for w in args.workloads.split(",") if w]:
+        extra[name] = workload_rate(torch, prx, graphgen, name, args.iters)
+        log(f"{name}: {extra[name]}")
+
     cpu = None
     if args.cpu_iters > 0:
         log(f"timing the CPU oracle on {args.cpu_iters} iterations ...")
@@ -238,6 +268,8 @@ def main() -> int:
         "buckets": buckets,
         "cpu_baseline": cpu,
     }
+    if extra:
+        out["workloads"] = extra
     print(json.dumps(out), flush=True)
     return 0
 

@@ -709,25 +709,44 @@ int log2_ceil(int64_t x) {
 int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
                 const unsigned long long* stats, const int32_t* row_begin, int cus,
                 hipStream_t stream, Built& bt) {
-    // tuning knobs: edges per tile and estimated cost per unit
+    // Launch width, and the tuning knobs: edges per tile and estimated cost
+    // per unit (each knob, when set, is used as given).
+    int64_t grid = cus;
+    if (const char* env = std::getenv("PR_GRID"))  // tuning knob: workgroups per launch
+        if (std::atoi(env) > 0) grid = std::atoi(env);
+    if (grid > kMaxGrid) grid = kMaxGrid;
+    if (grid < 1) grid = 1;
+    const char* tile_env = std::getenv("PR_TILE_EDGES");
+    const char* unit_env = std::getenv("PR_UNIT_COST");
     int64_t target = kTileTargetEdges, unit_cost = kUnitCost;
-    if (const char* env = std::getenv("PR_TILE_EDGES"))
-        if (std::atoll(env) > 0) target = std::atoll(env);
-    if (const char* env = std::getenv("PR_UNIT_COST"))
-        if (std::atoll(env) > 0) unit_cost = std::atoll(env);
+    if (tile_env && std::atoll(tile_env) > 0) target = std::atoll(tile_env);
+    if (unit_env && std::atoll(unit_env) > 0) unit_cost = std::atoll(unit_env);
     TileMap& map = bt.map;
-    int32_t tiles = 0;
-    for (int seg = 0; seg < kTileSegments; ++seg) {
-        const int b = kHubBucket - seg;  // segment 0 = hub bucket
-        const int64_t rows = (int64_t)stats[b], edges = (int64_t)stats[kNumBuckets + b];
-        int64_t want = edges > 0 ? ceil_div(target * rows, edges) : kTileMaxRows;
-        if (want < kTileMinRows) want = kTileMinRows;
-        if (want > kTileMaxRows) want = kTileMaxRows;
-        map.start[seg] = row_begin[b];
-        map.tile0[seg] = tiles;
-        map.shift[seg] = log2_ceil(want);
-        tiles += (int32_t)ceil_div(rows, (int64_t)1 << map.shift[seg]);
+    auto lay_out = [&](int64_t tgt) -> int32_t {  // the tile map for a target; returns the tiles
+        int32_t count = 0;
+        for (int seg = 0; seg < kTileSegments; ++seg) {
+            const int b = kHubBucket - seg;  // segment 0 = hub bucket
+            const int64_t rows = (int64_t)stats[b], edges = (int64_t)stats[kNumBuckets + b];
+            int64_t want = edges > 0 ? ceil_div(tgt * rows, edges) : kTileMaxRows;
+            if (want < kTileMinRows) want = kTileMinRows;
+            if (want > kTileMaxRows) want = kTileMaxRows;
+            map.start[seg] = row_begin[b];
+            map.tile0[seg] = count;
+            map.shift[seg] = log2_ceil(want);
+            count += (int32_t)ceil_div(rows, (int64_t)1 << map.shift[seg]);
+        }
+        return count;
+    };
+    if (!tile_env) {
+        // Smaller graphs get smaller tiles: at most 4 * nnz / grid edges each,
+        // and halved further while the tiles are fewer than the workgroups
+        // (so that every workgroup has a tile to work on).
+        int64_t cap = 4 * nnz / grid;
+        if (cap < kMinTileTarget) cap = kMinTileTarget;
+        if (target > cap) target = cap;
+        while (lay_out(target) < grid && target > kMinTileTarget) target /= 2;
     }
+    int32_t tiles = lay_out(target);
     map.start[kTileSegments] = n;
     if (tiles > w.n_tiles_max)
         return fail(PR_ERR_ARG, "tiles (%d) exceed the planned bound (%lld)", tiles,
@@ -842,6 +861,25 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
         return lo;
     };
 
+    // A smaller graph gets a smaller unit cost: when the tiles at the default
+    // cost would give fewer than two units per workgroup, the cost becomes
+    // (total cost) / (2 * grid).
+    if (!unit_env && tiles > 0) {
+        const double total = cost_at(slots) - cost_at(0);
+        int64_t units = 0;
+        for (int32_t t = 0; t < tiles; ++t) {
+            const int64_t e = sp[(size_t)t + 1] - sp[(size_t)t];
+            const int64_t c = (int64_t)std::ceil((cost_at(sp[(size_t)t + 1]) - cost_at(sp[(size_t)t])) /
+                                                 (double)unit_cost);
+            const int64_t cmax = ceil_div(e, kMinUnitEdges);
+            units += c < 1 ? 1 : (c > cmax ? cmax : c);
+        }
+        if (units < 2 * grid) {
+            const int64_t t2 = (int64_t)(total / (double)(2 * grid));
+            unit_cost = t2 > kMinUnitCost ? t2 : kMinUnitCost;
+        }
+    }
+
     // Tiles, units and slots.  A tile is cut at block boundaries into
     // min(ceil(cost / unit_cost), ceil(slots / kMinUnitEdges)) units of about
     // equal cost; all units are then ordered by decreasing estimated cost.
@@ -906,12 +944,7 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
                                   hipMemcpyHostToDevice, stream));
     PR_HIP_TRY(hipMemcpyAsync(w.fix_rows, bt.fix_rows.data(), sizeof(int32_t) * bt.fix_rows.size(),
                               hipMemcpyHostToDevice, stream));
-    int64_t grid = cus;
-    if (const char* env = std::getenv("PR_GRID"))  // tuning knob: workgroups per launch
-        if (std::atoi(env) > 0) grid = std::atoi(env);
-    if (grid > bt.n_units) grid = bt.n_units;
-    if (grid > kMaxGrid) grid = kMaxGrid;
-    bt.tile_grid = (int32_t)(grid > 0 ? grid : 1);
+    bt.tile_grid = (int32_t)(grid < bt.n_units ? grid : (bt.n_units > 0 ? bt.n_units : 1));
     return PR_OK;
 }
 

@@ -113,7 +113,9 @@ constexpr int kFinalBlock = 1024;
 constexpr int32_t kTileMaxRows = 16384;         // 128 KB of accumulators
 constexpr int32_t kTileMinRows = 64;
 constexpr int64_t kTileTargetEdges = 1 << 22;  // default; PR_TILE_EDGES overrides
+constexpr int64_t kMinTileTarget = 1 << 12;     // smaller graphs' tiles go down to this
 constexpr int64_t kUnitCost = 700000;           // default; PR_UNIT_COST overrides
+constexpr int64_t kMinUnitCost = 1 << 15;       // smaller graphs' units go down to this
 constexpr int64_t kMinUnitEdges = 1 << 17;     // a tile is cut into at most edges/this units
 constexpr int64_t kMaxUnitEdges = 1 << 26;     // and into at least edges/this units
 constexpr int32_t kTiledMaxVertices = 1 << 30; // contribution byte offsets fit 32 bits
