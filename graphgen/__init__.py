@@ -20,6 +20,17 @@ Workloads (the shapes of the pages' graphs; none of their data):
 
 Every CSR has rows sorted by target with no duplicates and no self-loops,
 except graphs built with ``from_edges(..., dedup=False)``.
+
+Valued matrices (the sparse product's inputs, class ``Matrix``):
+
+* ``stencil_matrix`` -- the 27-point stencil with its diagonal (page 2's
+  HPCCG operator shape; 100^3 gives 26,463,592 stored entries).  The page
+  does not print the values; ``values="operator"`` takes -1 for every
+  neighbour and 27 on the diagonal (diagonally dominant, and A times the
+  ones vector is 1 on interior rows), ``values="random"`` draws each entry
+  uniformly from [-1, 1).
+* ``matrix_from_lengths`` -- given row lengths, seeded uniform columns and
+  values; used for rows that straddle every length class of the product.
 """
 from __future__ import annotations
 
@@ -252,6 +263,91 @@ def dangling(n: int = 4096, n_dangling: int = 400, seed: int = 7) -> Graph:
     src, dst = g.edges()
     keep = ~np.isin(src, drop)
     return from_edges(n, src[keep], dst[keep], name="dangling")
+
+
+# --------------------------------------------------------------- valued matrices
+
+class Matrix:
+    """Valued CSR: ``row_ptr`` int32[n_rows+1], ``col_idx`` int32[nnz],
+    ``vals`` float64[nnz], columns in [0, n_cols)."""
+
+    __slots__ = ("name", "n_rows", "n_cols", "row_ptr", "col_idx", "vals")
+
+    def __init__(self, name: str, row_ptr, col_idx, vals, n_cols: int):
+        self.name = name
+        self.row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+        self.col_idx = np.ascontiguousarray(col_idx, dtype=np.int32)
+        self.vals = np.ascontiguousarray(vals, dtype=np.float64)
+        self.n_rows = int(self.row_ptr.shape[0] - 1)
+        self.n_cols = int(n_cols)
+
+    @property
+    def nnz(self) -> int:
+        return int(self.col_idx.shape[0])
+
+    def row_lengths(self) -> np.ndarray:
+        return np.diff(self.row_ptr.astype(np.int64))
+
+    def __repr__(self) -> str:
+        return f"Matrix({self.name!r}, {self.n_rows}x{self.n_cols}, nnz={self.nnz})"
+
+
+def uniform(n: int, seed: int, lo: float = -1.0, hi: float = 1.0) -> np.ndarray:
+    """n seeded draws, uniform in [lo, hi), float64 (53-bit mantissas)."""
+    u = (splitmix_u64(seed, np.arange(n, dtype=np.uint64)) >> np.uint64(11)).astype(np.float64)
+    return lo + (hi - lo) * (u * (1.0 / 9007199254740992.0))
+
+
+def small_ints(n: int, seed: int, bound: int = 8) -> np.ndarray:
+    """n seeded integers in [-bound, bound], as float64."""
+    r = splitmix_u64(seed, np.arange(n, dtype=np.uint64)) % np.uint64(2 * bound + 1)
+    return r.astype(np.float64) - bound
+
+
+def stencil_matrix(nx: int, ny: int | None = None, nz: int | None = None,
+                   values: str = "operator", seed: int = 1) -> Matrix:
+    """27-point stencil on an nx*ny*nz grid with the diagonal stored in place
+    (columns ascending in every row)."""
+    g = stencil27(nx, ny, nz)
+    n = g.n
+    deg = g.out_degree()
+    rows = np.repeat(np.arange(n, dtype=np.int64), deg)
+    after = (g.col_idx > rows).astype(np.int64)
+    e = np.arange(g.m, dtype=np.int64)
+    row_ptr = g.row_ptr.astype(np.int64) + np.arange(n + 1, dtype=np.int64)
+    col = np.empty(g.m + n, dtype=np.int32)
+    is_diag = np.ones(g.m + n, dtype=bool)
+    pos = e + rows + after
+    col[pos] = g.col_idx
+    is_diag[pos] = False
+    col[is_diag] = np.arange(n, dtype=np.int32)
+    if values == "operator":
+        vals = np.where(is_diag, 27.0, -1.0)
+    elif values == "random":
+        vals = uniform(g.m + n, seed)
+    else:
+        raise ValueError(values)
+    return Matrix(f"stencil_matrix{g.name[7:]}_{values}", row_ptr, col, vals, n)
+
+
+def matrix_from_lengths(lengths, n_cols: int, seed: int, int_values: bool = False,
+                        name: str | None = None) -> Matrix:
+    """Rows of the given lengths; columns uniform in [0, n_cols) (repeats
+    allowed, stored order unsorted), values uniform in [-1, 1) or small
+    integers."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    row_ptr = np.zeros(lengths.size + 1, dtype=np.int64)
+    np.cumsum(lengths, out=row_ptr[1:])
+    nnz = int(row_ptr[-1])
+    col = (splitmix_u64(seed, np.arange(nnz, dtype=np.uint64)) % np.uint64(max(n_cols, 1)))
+    vals = small_ints(nnz, seed + 1) if int_values else uniform(nnz, seed + 1)
+    return Matrix(name or f"rows{lengths.size}_{nnz}_{seed}", row_ptr, col.astype(np.int32),
+                  vals, n_cols)
+
+
+def matrix_of_graph(g: Graph, seed: int) -> Matrix:
+    """The graph's out-edge CSR with seeded uniform values in [-1, 1)."""
+    return Matrix(f"{g.name}_valued", g.row_ptr, g.col_idx, uniform(g.m, seed), g.n)
 
 
 def workload(name: str) -> Graph:

@@ -18,6 +18,11 @@ Parity status of each function (what pins it is in the CPU tests):
   proportionality of the broken vector, and the contraction L1_{t+1} <= d L1_t.
   On the large synthetic graphs no page prints values, so beyond these
   properties the values there are the oracle's own.
+* ``spmv`` -- pinned: exact integer products against a dense int64 matrix
+  product (square and rectangular, so a transposed operand fails), the exact
+  rational sum within the rounding bound of a k-term sum, identity and
+  diagonal matrices, empty rows, and the closed form of the 27-point stencil
+  operator (-1 per neighbour, 27 on the diagonal) applied to the ones vector.
 * ``ranking`` / ``top_k`` -- sort by (-x, id).
 """
 from __future__ import annotations
@@ -38,7 +43,8 @@ DROP_DANGLING = 1
 
 def build(verbose: bool = False) -> str:
     """Compile liboracle.so in place: plain gcc, single-threaded, -O2."""
-    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-Wall", "-o", _LIB + ".tmp", _SRC, "-lm"]
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11", "-Wall", "-o",
+           _LIB + ".tmp", _SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -59,6 +65,9 @@ def _lib() -> ctypes.CDLL:
                                  ctypes.c_double, ctypes.c_int32, f64p, ctypes.c_uint32, f64p,
                                  f64p, f64p, f64p, i32p, f64p]
     lib.pro_pagerank.restype = ctypes.c_int
+    lib.pro_spmv.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, i32p, i32p, f64p,
+                             f64p, f64p, f64p]
+    lib.pro_spmv.restype = ctypes.c_int
     return lib
 
 
@@ -128,6 +137,25 @@ def pagerank(row_ptr, col_idx, d: float = 0.85, tol: float = 0.0, max_iter: int 
     _check(rc, "pagerank")
     t = int(it[0])
     return Result(x, t, l1[:t], s[:t], dm[:t], float(secs[0]))
+
+
+def spmv(row_ptr, col_idx, vals, x, n_cols: int | None = None, timed: bool = False):
+    """y = A x for the valued CSR matrix (row_ptr, col_idx, vals); float64.
+    With timed=True returns (y, seconds of the product loop)."""
+    rp, ci = _csr(row_ptr, col_idx)
+    va = np.ascontiguousarray(vals, dtype=np.float64)
+    xa = np.ascontiguousarray(x, dtype=np.float64)
+    n_rows, nnz = rp.size - 1, ci.size
+    n_cols = xa.size if n_cols is None else int(n_cols)
+    if va.size != nnz or xa.size != n_cols:
+        raise ValueError("vals / x have the wrong length")
+    y = np.empty(max(n_rows, 1), dtype=np.float64)
+    secs = np.zeros(1, dtype=np.float64)
+    _check(_lib().pro_spmv(n_rows, n_cols, nnz, _p(rp, ctypes.c_int32), _p(ci, ctypes.c_int32),
+                           _p(va, ctypes.c_double), _p(xa, ctypes.c_double),
+                           _p(y, ctypes.c_double), _p(secs, ctypes.c_double)), "spmv")
+    y = y[:n_rows]
+    return (y, float(secs[0])) if timed else y
 
 
 def ranking(x) -> np.ndarray:

@@ -134,3 +134,28 @@ int pro_pagerank(int32_t n, int64_t m, const int32_t* out_rp, const int32_t* out
     free(in_rp); free(in_ci); free(outdeg); free(xn);
     return PRO_OK;
 }
+
+/* "A Pedagogical Introduction to Porting a Conjugate Gradient Solver to CUDA":
+ * the sparse product of its CG loop, on the flattened CSR arrays -- for every
+ * row, start from zero and add value times gathered x over the row's entries
+ * in stored order. */
+int pro_spmv(int32_t n_rows, int32_t n_cols, int64_t nnz, const int32_t* rp, const int32_t* ci,
+             const double* vals, const double* x, double* y, double* loop_seconds) {
+    if (n_rows < 0 || n_cols < 0 || nnz < 0 || nnz > INT32_MAX || !rp) return PRO_ERR_ARG;
+    if (nnz > 0 && (!ci || !vals)) return PRO_ERR_ARG;
+    if ((n_rows > 0 && !y) || (n_cols > 0 && !x)) return PRO_ERR_ARG;
+    if (rp[0] != 0 || (int64_t)rp[n_rows] != nnz) return PRO_ERR_CSR;
+    for (int32_t i = 0; i < n_rows; ++i)
+        if (rp[i + 1] < rp[i]) return PRO_ERR_CSR;
+    for (int64_t j = 0; j < nnz; ++j)
+        if (ci[j] < 0 || ci[j] >= n_cols) return PRO_ERR_CSR;
+
+    const double t0 = now_seconds();
+    for (int32_t i = 0; i < n_rows; ++i) {
+        double sum = 0.0;
+        for (int32_t j = rp[i]; j < rp[i + 1]; ++j) sum += vals[j] * x[ci[j]];
+        y[i] = sum;
+    }
+    if (loop_seconds) *loop_seconds = now_seconds() - t0;
+    return PRO_OK;
+}

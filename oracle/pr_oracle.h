@@ -17,6 +17,10 @@
  *     ranks sum to 1 after every pass;
  *     section "Exercise" (Hint 2, Solution) -- the variant with the dangling
  *     term removed, whose total obeys S' = (1-d) + d (S - D).
+ *   "A Pedagogical Introduction to Porting a Conjugate Gradient Solver to
+ *     CUDA": the CSR arrays row_offsets / cols / vals and the product
+ *     y[i] = sum over j in row i of vals[j] * x[cols[j]], in double, summed
+ *     in stored order (the thread-per-row kernel and the CPU loop it ports).
  *   "Meerkat: A Framework for Dynamic Graph Algorithms on GPUs", PageRank
  *     section -- static start 1/n, iteration i built from iteration i-1,
  *     teleport mass from the zero-out-degree vertices of iteration i-1, and
@@ -56,6 +60,17 @@ int pro_pagerank(int32_t n, int64_t m, const int32_t* out_row_ptr, const int32_t
                  double d, double tol, int32_t max_iter, const double* x0, uint32_t flags,
                  double* x, double* l1_trace, double* sum_trace, double* dmass_trace,
                  int32_t* iterations, double* loop_seconds);
+
+/* Sparse matrix-vector product y = A x of a valued CSR matrix with n_rows
+ * rows, n_cols columns and nnz stored entries: y[i] = 0.0 + the products
+ * vals[j] * x[col_idx[j]] added one at a time for j = row_ptr[i] ..
+ * row_ptr[i+1]-1.  Each product and each sum is rounded on its own (the file
+ * is built without contraction to fused multiply-adds).  Host arrays owned by
+ * the caller: row_ptr[n_rows+1], col_idx[nnz], vals[nnz], x[n_cols], y[n_rows].
+ * loop_seconds (may be NULL): wall time of the product loop. */
+int pro_spmv(int32_t n_rows, int32_t n_cols, int64_t nnz, const int32_t* row_ptr,
+             const int32_t* col_idx, const double* vals, const double* x, double* y,
+             double* loop_seconds);
 
 #ifdef __cplusplus
 }

@@ -57,6 +57,21 @@ def test_stencil_counts():
     assert small.m == (3 * 4 - 2) * (3 * 3 - 2) * (3 * 5 - 2) - 60
 
 
+def test_stencil_matrix_layout():
+    A = graphgen.stencil_matrix(6, 5, 4)
+    assert A.n_rows == A.n_cols == 120
+    assert A.nnz == (3 * 6 - 2) * (3 * 5 - 2) * (3 * 4 - 2)
+    rows = np.repeat(np.arange(A.n_rows), A.row_lengths())
+    assert np.all(np.diff(A.col_idx.astype(np.int64))[np.diff(rows) == 0] > 0)  # ascending
+    diag = A.col_idx == rows
+    assert np.array_equal(np.bincount(rows[diag], minlength=A.n_rows), np.ones(A.n_rows))
+    assert np.all(A.vals[diag] == 27.0) and np.all(A.vals[~diag] == -1.0)
+    g = graphgen.stencil27(6, 5, 4)
+    assert np.array_equal(A.col_idx[~diag], g.col_idx)  # the graph's edges, in order
+    R = graphgen.stencil_matrix(6, 5, 4, values="random", seed=3)
+    assert np.array_equal(R.col_idx, A.col_idx) and np.all(np.abs(R.vals) < 1.0)
+
+
 def test_rmat_deterministic_and_well_formed():
     a, b = graphgen.rmat(14), graphgen.rmat(14)
     np.testing.assert_array_equal(a.row_ptr, b.row_ptr)

@@ -292,3 +292,118 @@ def test_rejects_bad_arguments():
         oracle.pagerank(g.row_ptr, g.col_idx, d=1.5)
     with pytest.raises(ValueError):
         oracle.pagerank(g.row_ptr, g.col_idx, max_iter=0)
+
+
+# ------------------------------------------------------------ sparse product
+# "A Pedagogical Introduction to Porting a Conjugate Gradient Solver to CUDA":
+# y[i] = sum over the stored entries j of row i of vals[j] * x[cols[j]].
+
+U = 2.0 ** -53  # unit roundoff of binary64
+
+
+def _dense(A):
+    M = np.zeros((A.n_rows, A.n_cols), dtype=np.float64)
+    rows = np.repeat(np.arange(A.n_rows), A.row_lengths())
+    np.add.at(M, (rows, A.col_idx), A.vals)
+    return M
+
+
+@pytest.mark.parametrize("shape", [(300, 300), (257, 90), (60, 513)], ids=str)
+def test_spmv_integer_entries_match_dense_product_exactly(shape):
+    # Small integers: every product and partial sum is an integer far below
+    # 2^53, so the floating-point result is exact and must equal the int64
+    # dense product.  A rectangular shape makes A^T x impossible to confuse
+    # with A x.
+    n_rows, n_cols = shape
+    lengths = graphgen.splitmix_u64(5, np.arange(n_rows, dtype=np.uint64)) % np.uint64(41)
+    A = graphgen.matrix_from_lengths(lengths, n_cols, seed=9, int_values=True)
+    x = graphgen.small_ints(n_cols, 77)
+    dense = _dense(A).astype(np.int64) @ x.astype(np.int64)
+    y = oracle.spmv(A.row_ptr, A.col_idx, A.vals, x)
+    np.testing.assert_array_equal(y, dense.astype(np.float64))
+    assert np.count_nonzero(y) > n_rows // 2
+
+
+def test_spmv_exact_sum_within_rounding_bound():
+    # Each row's exact rational value sum_j a_j x_j; a k-term sum of rounded
+    # products differs from it by at most gamma_k * sum_j |a_j x_j| with
+    # gamma_k = k u / (1 - k u) (standard forward error bound).
+    from fractions import Fraction
+    lengths = [0, 1, 2, 3, 7, 31, 64, 65, 200]
+    A = graphgen.matrix_from_lengths(lengths, 500, seed=21)
+    x = graphgen.uniform(500, 22) * 1e3
+    y = oracle.spmv(A.row_ptr, A.col_idx, A.vals, x)
+    for i, k in enumerate(lengths):
+        s, e = A.row_ptr[i], A.row_ptr[i + 1]
+        terms = [Fraction(float(a)) * Fraction(float(x[c])) for a, c in zip(A.vals[s:e], A.col_idx[s:e])]
+        exact = sum(terms, Fraction(0))
+        mag = float(sum(abs(t) for t in terms))
+        gamma = k * U / (1 - k * U)
+        assert abs(Fraction(float(y[i])) - exact) <= Fraction(gamma * mag) + Fraction(0), (i, k)
+
+
+def test_spmv_identity_and_diagonal():
+    n = 1000
+    x = graphgen.uniform(n, 3)
+    eye = graphgen.Matrix("eye", np.arange(n + 1), np.arange(n), np.ones(n), n)
+    np.testing.assert_array_equal(oracle.spmv(eye.row_ptr, eye.col_idx, eye.vals, x), x)
+    d = graphgen.uniform(n, 4)
+    diag = graphgen.Matrix("diag", np.arange(n + 1), np.arange(n), d, n)
+    np.testing.assert_array_equal(oracle.spmv(diag.row_ptr, diag.col_idx, diag.vals, x), d * x)
+    # a permutation matrix gathers: y[i] = x[p[i]]
+    p = np.argsort(graphgen.splitmix_u64(8, np.arange(n, dtype=np.uint64)))
+    perm = graphgen.Matrix("perm", np.arange(n + 1), p, np.ones(n), n)
+    np.testing.assert_array_equal(oracle.spmv(perm.row_ptr, perm.col_idx, perm.vals, x), x[p])
+
+
+def test_spmv_empty_rows_and_empty_matrices():
+    A = graphgen.matrix_from_lengths([0, 3, 0, 0, 2, 0], 4, seed=1)
+    x = graphgen.uniform(4, 2)
+    y = oracle.spmv(A.row_ptr, A.col_idx, A.vals, x)
+    assert y[0] == 0.0 and y[2] == 0.0 and y[3] == 0.0 and y[5] == 0.0
+    assert not np.signbit(y[[0, 2, 3, 5]]).any()  # a sum that starts from +0.0
+    assert oracle.spmv(np.zeros(1, np.int32), np.zeros(0, np.int32), np.zeros(0), x).size == 0
+    z = oracle.spmv(np.zeros(6, np.int32), np.zeros(0, np.int32), np.zeros(0), x)
+    np.testing.assert_array_equal(z, np.zeros(5))
+
+
+@pytest.mark.parametrize("dims", [(5, 5, 5), (7, 4, 3), (1, 1, 9), (1, 1, 1)], ids=str)
+def test_spmv_stencil_operator_on_ones_closed_form(dims):
+    # -1 per neighbour and 27 on the diagonal: (A 1)[p] = 27 - k(p), where
+    # k(p) counts the in-grid points at Chebyshev distance 1, the product of
+    # (number of in-grid offsets -1, 0, +1) per axis minus the point itself.
+    nx, ny, nz = dims
+    A = graphgen.stencil_matrix(nx, ny, nz)
+    y = oracle.spmv(A.row_ptr, A.col_idx, A.vals, np.ones(A.n_cols))
+    zz, yy, xx = np.meshgrid(np.arange(nz), np.arange(ny), np.arange(nx), indexing="ij")
+
+    def offsets(c, size):  # in-grid offsets among -1, 0, +1 along one axis
+        return 1 + (c > 0) + (c < size - 1)
+
+    k = offsets(xx, nx) * offsets(yy, ny) * offsets(zz, nz) - 1
+    np.testing.assert_array_equal(y, (27.0 - k).ravel())
+    if min(dims) >= 3:
+        assert (y == 1.0).sum() == (nx - 2) * (ny - 2) * (nz - 2)
+
+
+def test_spmv_linearity():
+    A = graphgen.matrix_of_graph(graphgen.rmat(10), seed=5)
+    x, z = graphgen.uniform(A.n_cols, 6), graphgen.uniform(A.n_cols, 7)
+    lhs = oracle.spmv(A.row_ptr, A.col_idx, A.vals, 2.0 * x - 0.5 * z)
+    rhs = 2.0 * oracle.spmv(A.row_ptr, A.col_idx, A.vals, x) - 0.5 * oracle.spmv(
+        A.row_ptr, A.col_idx, A.vals, z)
+    scale = oracle.spmv(A.row_ptr, A.col_idx, np.abs(A.vals), 2.0 * np.abs(x) + 0.5 * np.abs(z))
+    k = A.row_lengths().max() + 2
+    assert np.all(np.abs(lhs - rhs) <= 3 * k * U * scale + 1e-300)
+
+
+def test_spmv_rejects_malformed_csr():
+    x = np.ones(3)
+    with pytest.raises(ValueError):
+        oracle.spmv(np.array([0, 2, 1]), np.array([0, 1]), np.ones(2), x)   # decreasing
+    with pytest.raises(ValueError):
+        oracle.spmv(np.array([0, 1, 2]), np.array([0, 3]), np.ones(2), x)   # column >= n_cols
+    with pytest.raises(ValueError):
+        oracle.spmv(np.array([1, 2]), np.array([0, 1]), np.ones(2), x)      # row_ptr[0] != 0
+    with pytest.raises(ValueError):
+        oracle.spmv(np.array([0, 2]), np.array([0, 1]), np.ones(3), x)      # vals length
