@@ -1,6 +1,7 @@
 /*
  * pr.h -- C ABI of libpr, PageRank power iteration with dangling-node
- * redistribution on one AMD Instinct MI355X (gfx950).
+ * redistribution on one AMD Instinct MI355X (gfx950), and the valued sparse
+ * matrix-vector product its pull iteration generalizes (pr_spmv, below).
  *
  * The method ("100 Days of GPU", Day 40 "PageRank on a real graph in CUDA",
  * section "One iteration, three shapes of work"):
@@ -237,6 +238,82 @@ int pr_plan_layout(const pr_plan* plan, const int32_t** in_row_ptr_dev,
 int pr_plan_tiles(const pr_plan* plan, const int32_t** tile_src_dev, const uint16_t** tile_row_dev,
                   const int32_t** tile_block_dev, const int32_t** tile_ptr_dev, int32_t* n_tiles_host,
                   int32_t* row0_host, int32_t* rows_host);
+
+/* ------------------------------------------------------------------------
+ * Valued sparse product y = A x in double precision ("A Pedagogical
+ * Introduction to Porting a Conjugate Gradient Solver to CUDA": the sparse
+ * product that takes most of its CG solver's time, on the CSR arrays
+ * row_offsets[n_rows+1], cols[nnz], vals[nnz]):
+ *
+ *     y[i] = sum over j in [row_ptr[i], row_ptr[i+1]) of vals[j] * x[col_idx[j]]
+ *
+ * A plan holds the row schedule of one sparsity pattern, built once on the
+ * device: rows of at most 64 entries in streamed blocks (their products are
+ * each rounded once and added in stored order from 0.0, so such rows come
+ * out bit-identical to a sequential CPU loop without fused multiply-adds),
+ * rows of 65..1024 entries one 64-lane wavefront each, longer rows in chunks
+ * of 4096 entries whose sums are added in order.  Rows longer than 64 are
+ * summed in a fixed tree order: deterministic, within the usual k-term
+ * rounding bound of the exact sum.
+ * ------------------------------------------------------------------------ */
+typedef struct pr_spmv_plan pr_spmv_plan;
+
+/* Device bytes a product plan keeps for its lifetime (ws_dev) and needs only
+ * while pr_spmv_plan_create runs (scratch_dev).  Host-only; 0 for invalid sizes. */
+size_t pr_spmv_workspace_bytes(int32_t n_rows, int64_t nnz);
+size_t pr_spmv_scratch_bytes(int32_t n_rows, int64_t nnz);
+
+/*
+ * Build the row schedule of a CSR sparsity pattern.
+ *
+ *   plan_out                 receives the plan (host memory owned by the library;
+ *                            release with pr_spmv_plan_destroy)
+ *   n_rows, n_cols, nnz      n_rows >= 0, n_cols >= 0, 0 <= nnz <= INT32_MAX;
+ *                            nnz > 0 needs n_rows >= 1 and n_cols >= 1
+ *   row_ptr_dev[n_rows+1]    the pattern; BORROWED: the plan keeps both pointers,
+ *   col_idx_dev[nnz]         and the caller keeps them allocated and unchanged
+ *                            while the plan lives
+ *   ws_dev, ws_bytes         >= pr_spmv_workspace_bytes(n_rows, nnz), 256-byte
+ *                            aligned, untouched while the plan lives
+ *   scratch_dev, scratch_bytes  >= pr_spmv_scratch_bytes(n_rows, nnz); free
+ *                            again once the call returns
+ *   flags                    0 or PR_VALIDATE (row_ptr[0] == 0, non-decreasing,
+ *                            row_ptr[n_rows] == nnz, 0 <= col < n_cols; else
+ *                            PR_ERR_GRAPH)
+ *
+ * Synchronizes `stream` (the block and row counts are read back, and the
+ * schedule is complete when the call returns).
+ * Without PR_VALIDATE a malformed pattern cannot make the product access
+ * memory outside the arrays (offsets and columns are clamped) but y is then
+ * unspecified; row pointers that describe more rows of a kind than nnz
+ * allows are rejected with PR_ERR_GRAPH.
+ */
+int pr_spmv_plan_create(pr_spmv_plan** plan_out, int32_t n_rows, int32_t n_cols, int64_t nnz,
+                        const int32_t* row_ptr_dev, const int32_t* col_idx_dev, void* ws_dev,
+                        size_t ws_bytes, void* scratch_dev, size_t scratch_bytes, uint32_t flags,
+                        void* stream);
+
+/* Release a product plan; NULL is allowed.  No pr_spmv on it may be in flight. */
+int pr_spmv_plan_destroy(pr_spmv_plan* plan);
+
+/*
+ * y = A x on `stream`, asynchronous.
+ *
+ *   vals_dev[nnz]     the values, in the order of the plan's col_idx (they may
+ *                     change between calls; the pattern may not)
+ *   x_dev[n_cols]     input vector (read only)
+ *   y_dev[n_rows]     written; must not overlap x_dev or vals_dev
+ *
+ * The plan's device must be current.  Calls on one plan must not overlap in
+ * time when it has rows longer than 1024 entries (their chunk sums share the
+ * plan's workspace); otherwise calls may run concurrently.
+ */
+int pr_spmv(const pr_spmv_plan* plan, const double* vals_dev, const double* x_dev, double* y_dev,
+            void* stream);
+
+/* Introspection for tests and benchmarks: counts_host[4] receives the number
+ * of streamed blocks, of 65..1024-entry rows, of longer rows, and of chunks. */
+int pr_spmv_plan_items(const pr_spmv_plan* plan, int32_t* counts_host);
 
 /* Human-readable name of a status code (static storage). */
 const char* pr_status_string(int status);

@@ -10,6 +10,11 @@ helpers below only allocate device memory with torch and pass pointers:
     >>> plan = prx.Plan(g)                                 # pr_plan_create
     >>> res = plan.run(d=0.85, tol=1e-6, max_iter=100)     # pr_run
     >>> res.x, res.iterations, res.l1_trace
+
+The valued sparse product y = A x (fp64 CSR, pr_spmv):
+
+    >>> A = prx.SpmvPlan.from_csr(row_ptr, col_idx, n_cols)  # pr_spmv_plan_create
+    >>> y = A.run(vals, x)                                   # pr_spmv
 """
 from __future__ import annotations
 
@@ -18,7 +23,9 @@ from ._lib import (PR_ERR_ARG, PR_ERR_GRAPH, PR_ERR_HIP, PR_ERR_WORKSPACE, PR_OK
                    lib, pr_last_error, pr_plan_buckets, pr_plan_create, pr_plan_destroy,
                    pr_plan_iteration_ms, pr_plan_kernel_ms, pr_plan_layout, pr_plan_tiles, pr_plan_num_buckets,
                    pr_plan_scratch_bytes, pr_plan_workspace_bytes, pr_run, pr_status_string,
-                   pr_transpose, pr_transpose_workspace_bytes)
+                   pr_spmv, pr_spmv_plan_create, pr_spmv_plan_destroy, pr_spmv_plan_items,
+                   pr_spmv_scratch_bytes, pr_spmv_workspace_bytes, pr_transpose,
+                   pr_transpose_workspace_bytes)
 
 __all__ = [
     "DeviceGraph", "Plan", "RunResult", "transpose", "PrError", "lib",
@@ -26,7 +33,8 @@ __all__ = [
     "pr_plan_workspace_bytes", "pr_plan_scratch_bytes", "pr_run", "pr_plan_iteration_ms",
     "pr_plan_kernel_ms", "pr_plan_tiles",
     "pr_plan_buckets", "pr_plan_num_buckets", "pr_plan_layout", "pr_status_string",
-    "pr_last_error",
+    "pr_last_error", "SpmvPlan", "pr_spmv", "pr_spmv_plan_create", "pr_spmv_plan_destroy",
+    "pr_spmv_plan_items", "pr_spmv_scratch_bytes", "pr_spmv_workspace_bytes",
     "PR_OK", "PR_ERR_ARG", "PR_ERR_WORKSPACE", "PR_ERR_GRAPH", "PR_ERR_HIP",
     "PR_VALIDATE", "PR_PLAN_BUCKETED", "PR_X0_GIVEN", "PR_RECORD_EVENTS",
 ]
@@ -163,6 +171,55 @@ class Plan:
     def close(self) -> None:
         if getattr(self, "handle", None):
             pr_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class SpmvPlan:
+    """Row schedule of a CSR sparsity pattern (pr_spmv_plan_create), ready for
+    y = A x with pr_spmv.  Keeps the pattern tensors and the plan's workspace
+    alive for its lifetime (the plan borrows row_ptr and col_idx)."""
+
+    def __init__(self, row_ptr, col_idx, n_cols: int, flags: int = 0, stream=None):
+        self.row_ptr, self.col_idx = row_ptr, col_idx
+        self.n_rows = int(row_ptr.numel() - 1)
+        self.n_cols = int(n_cols)
+        self.nnz = int(col_idx.numel())
+        dev = row_ptr.device
+        self.ws = _device_buffer(pr_spmv_workspace_bytes(self.n_rows, self.nnz), dev)
+        scratch = _device_buffer(pr_spmv_scratch_bytes(self.n_rows, self.nnz), dev)
+        self.handle = pr_spmv_plan_create(self.n_rows, self.n_cols, self.nnz, row_ptr, col_idx,
+                                          self.ws, scratch, flags, stream)
+        del scratch
+
+    @classmethod
+    def from_csr(cls, row_ptr, col_idx, n_cols: int, device="cuda", flags: int = 0):
+        g = DeviceGraph.from_csr(row_ptr, col_idx, device)
+        return cls(g.row_ptr, g.col_idx, n_cols, flags)
+
+    def items(self) -> dict:
+        return pr_spmv_plan_items(self.handle)
+
+    def run(self, vals, x, out=None, stream=None):
+        """y = A x (float64 device tensors; vals in the pattern's order)."""
+        torch = _torch()
+        y = out if out is not None else torch.empty(self.n_rows, dtype=torch.float64,
+                                                    device=self.row_ptr.device)
+        for t, n in ((vals, self.nnz), (x, self.n_cols), (y, self.n_rows)):
+            if t.dtype != torch.float64 or t.numel() != n or not t.is_contiguous():
+                raise ValueError("vals, x and y must be contiguous float64 of nnz, n_cols "
+                                 "and n_rows entries")
+        pr_spmv(self.handle, vals, x, y, stream)
+        return y
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            pr_spmv_plan_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

@@ -55,6 +55,14 @@ _SIGNATURES = {
     "pr_plan_layout": (_c.c_int, [_vp, _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_vp)]),
     "pr_plan_tiles": (_c.c_int, [_vp, _c.POINTER(_vp), _c.POINTER(_vp), _c.POINTER(_vp),
                                  _c.POINTER(_vp), _c.POINTER(_c.c_int32), _vp, _vp]),
+    "pr_spmv_workspace_bytes": (_c.c_size_t, [_c.c_int32, _c.c_int64]),
+    "pr_spmv_scratch_bytes": (_c.c_size_t, [_c.c_int32, _c.c_int64]),
+    "pr_spmv_plan_create": (_c.c_int, [_c.POINTER(_vp), _c.c_int32, _c.c_int32, _c.c_int64, _vp,
+                                       _vp, _vp, _c.c_size_t, _vp, _c.c_size_t, _c.c_uint32,
+                                       _vp]),
+    "pr_spmv_plan_destroy": (_c.c_int, [_vp]),
+    "pr_spmv": (_c.c_int, [_vp, _vp, _vp, _vp, _vp]),
+    "pr_spmv_plan_items": (_c.c_int, [_vp, _c.POINTER(_c.c_int32)]),
     "pr_status_string": (_c.c_char_p, [_c.c_int]),
     "pr_last_error": (_c.c_char_p, []),
 }
@@ -194,6 +202,38 @@ def pr_plan_buckets(plan) -> list[dict]:
     edges = (_c.c_int64 * nb)()
     _check(lib().pr_plan_buckets(plan, mins, rows, edges))
     return [{"min_len": mins[b], "rows": rows[b], "edges": edges[b]} for b in range(nb)]
+
+
+def pr_spmv_workspace_bytes(n_rows: int, nnz: int) -> int:
+    return int(lib().pr_spmv_workspace_bytes(n_rows, nnz))
+
+
+def pr_spmv_scratch_bytes(n_rows: int, nnz: int) -> int:
+    return int(lib().pr_spmv_scratch_bytes(n_rows, nnz))
+
+
+def pr_spmv_plan_create(n_rows, n_cols, nnz, row_ptr, col_idx, ws, scratch, flags=0,
+                        stream=None) -> int:
+    h = _vp()
+    _check(lib().pr_spmv_plan_create(_c.byref(h), n_rows, n_cols, nnz, _ptr(row_ptr),
+                                     _ptr(col_idx), _ptr(ws), _nbytes(ws), _ptr(scratch),
+                                     _nbytes(scratch), flags, _stream(stream)))
+    return h.value
+
+
+def pr_spmv_plan_destroy(plan: int | None) -> None:
+    _check(lib().pr_spmv_plan_destroy(plan))
+
+
+def pr_spmv(plan, vals, x, y, stream=None) -> None:
+    _check(lib().pr_spmv(plan, _ptr(vals), _ptr(x), _ptr(y), _stream(stream)))
+
+
+def pr_spmv_plan_items(plan) -> dict:
+    """Streamed blocks, 65..1024-entry rows, longer rows and their chunks."""
+    c = (_c.c_int32 * 4)()
+    _check(lib().pr_spmv_plan_items(plan, c))
+    return {"blocks": c[0], "medium_rows": c[1], "long_rows": c[2], "chunks": c[3]}
 
 
 def pr_status_string(status: int) -> str:
