@@ -102,6 +102,46 @@ def cpu_baseline(g, iters: int) -> dict:
                       f"(fp64, single thread, iteration loop only: {secs:.2f} s)"}
 
 
+def spmv_min_bytes(n_rows: int, n_cols: int, nnz: int) -> int:
+    """Bytes any CSR product y = A x in double must move: per stored entry a
+    4-byte column index and an 8-byte value; per row a row pointer and the
+    8-byte y; each x entry once; plus row_ptr[n_rows]."""
+    return 12 * nnz + 12 * n_rows + 8 * n_cols + 4
+
+
+def spmv_rate(torch, prx, graphgen, nx: int, reps: int) -> dict:
+    """The valued fp64 product of the 27-point stencil operator (diagonal
+    stored) on an nx^3 grid with seeded uniform values: plan once, one
+    warm-up product, then `reps` products timed together with events on the
+    stream they are launched on."""
+    A = graphgen.stencil_matrix(nx, values="random", seed=5)
+    x = graphgen.uniform(A.n_cols, 6)
+    plan = prx.SpmvPlan.from_csr(A.row_ptr, A.col_idx, A.n_cols)
+    vals = torch.as_tensor(A.vals, dtype=torch.float64).cuda()
+    xd = torch.as_tensor(x, dtype=torch.float64).cuda()
+    y = torch.empty(A.n_rows, dtype=torch.float64, device="cuda")
+    stream = torch.cuda.current_stream()
+    plan.run(vals, xd, y, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(3):
+        e0.record(stream)
+        for _ in range(reps):
+            plan.run(vals, xd, y, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    ms = statistics.median(times)
+    b = spmv_min_bytes(A.n_rows, A.n_cols, A.nnz)
+    items = plan.items()
+    plan.close()
+    return {"workload": A.name, "n_rows": A.n_rows, "nnz": A.nnz, "dtype": "f64",
+            "launch_ms": round(ms, 5), "gflops": round(2 * A.nnz / (ms * 1e-3) / 1e9, 1),
+            "algorithmic_bytes": b, "gbps": round(b / (ms * 1e-3) / 1e9, 1),
+            "frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "items": items}
+
+
 def workload_rate(torch, prx, graphgen, name: str, iters: int) -> dict:
     """Per-iteration rate of one more workload: a plan, one warm-up run, then
     `iters` timed iterations (median of 3 runs) and the gather kernel's mean
@@ -134,6 +174,9 @@ def main() -> int:
     ap.add_argument("--cpu-iters", type=int, default=8,
                     help="iterations of the CPU oracle sample (0 skips it)")
     ap.add_argument("--no-copy-row", action="store_true")
+    ap.add_argument("--spmv-grid", type=int, default=100,
+                    help="edge of the 27-point stencil grid of the valued fp64 product "
+                         "(0 skips it)")
     ap.add_argument("--workloads", default="",
                     help="comma-separated extra workloads (e.g. citation,stencil100,rmat18,rmat21) "
                          "whose per-iteration rate is added under 'workloads'")
@@ -232,6 +275,11 @@ def main() -> int:
         extra[name] = workload_rate(torch, prx, graphgen, name, args.iters)
         log(f"{name}: {extra[name]}")
 
+    spmv = None
+    if args.spmv_grid > 0:
+        spmv = spmv_rate(torch, prx, graphgen, args.spmv_grid, 50)
+        log(f"spmv: {spmv}")
+
     cpu = None
     if args.cpu_iters > 0:
         log(f"timing the CPU oracle on {args.cpu_iters} iterations ...")
@@ -268,6 +316,8 @@ def main() -> int:
         "buckets": buckets,
         "cpu_baseline": cpu,
     }
+    if spmv:
+        out["spmv"] = spmv
     if extra:
         out["workloads"] = extra
     print(json.dumps(out), flush=True)
