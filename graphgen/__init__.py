@@ -185,8 +185,7 @@ def from_edges(n: int, src, dst, dedup: bool = True, drop_self: bool = True,
         keep[1:] = (src[1:] != src[:-1]) | (dst[1:] != dst[:-1])
         src, dst = src[keep], dst[keep]
     row_ptr = np.zeros(n + 1, dtype=np.int64)
-    np.add.at(row_ptr, src + 1, 1)
-    row_ptr = np.cumsum(row_ptr)
+    row_ptr[1:] = np.cumsum(np.bincount(src, minlength=n))
     return Graph(name, row_ptr.astype(np.int32), dst.astype(np.int32))
 
 
@@ -226,6 +225,25 @@ def star(n: int, inward: bool = True) -> Graph:
     if inward:
         return from_edges(n, leaves, hub, name=f"star{n}_in")
     return from_edges(n, hub, leaves, name=f"star{n}_out")
+
+
+def grid2d(nx: int, ny: int | None = None) -> Graph:
+    """4-neighbour grid, both directions of every link; vertex id = x + nx*y.
+    1024 x 1024 is the high-diameter graph of the graph study's traversal
+    tables (2^20 vertices, 4,190,208 directed edges, BFS depth 2046 from a
+    corner)."""
+    ny = nx if ny is None else ny
+    x, y = np.meshgrid(np.arange(nx, dtype=np.int64), np.arange(ny, dtype=np.int64),
+                       indexing="xy")
+    x, y = x.ravel(), y.ravel()
+    v = x + nx * y
+    src, dst = [], []
+    for dx, dy in ((1, 0), (-1, 0), (0, 1), (0, -1)):
+        ok = (x + dx >= 0) & (x + dx < nx) & (y + dy >= 0) & (y + dy < ny)
+        src.append(v[ok])
+        dst.append(v[ok] + dx + nx * dy)
+    return from_edges(nx * ny, np.concatenate(src), np.concatenate(dst),
+                      name=f"grid{nx}x{ny}")
 
 
 def tiny() -> Graph:
@@ -358,6 +376,8 @@ def workload(name: str) -> Graph:
         return stencil27(100)
     if name.startswith("rmat"):
         return rmat(int(name[4:]))
+    if name == "grid1024":
+        return grid2d(1024)
     raise KeyError(name)
 
 

@@ -23,6 +23,16 @@ Parity status of each function (what pins it is in the CPU tests):
   rational sum within the rounding bound of a k-term sum, identity and
   diagonal matrices, empty rows, and the closed form of the 27-point stencil
   operator (-1 per neighbour, 27 on the diagonal) applied to the ones vector.
+* ``bfs`` -- pinned: unweighted shortest paths from scipy's csgraph routine on
+  random directed graphs, brute-force levels from powers of the boolean
+  adjacency matrix on every digraph of 3 vertices, closed forms (directed
+  chain and its reverse, cycle, both stars, the 2-D grid's Manhattan distance
+  with depth 2 (side - 1) + 1), unreachable vertices, and the edge count.
+* ``wcc`` -- pinned: scipy's weak connected components (relabelled by their
+  smallest member) on random directed graphs, the transitive closure of the
+  symmetrised adjacency on every digraph of 3 vertices, closed forms (no
+  edges, one cycle, disjoint cycles, a reversed chain, the grid), and
+  invariance under reversing every edge.
 * ``ranking`` / ``top_k`` -- sort by (-x, id).
 """
 from __future__ import annotations
@@ -68,6 +78,12 @@ def _lib() -> ctypes.CDLL:
     lib.pro_spmv.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, i32p, i32p, f64p,
                              f64p, f64p, f64p]
     lib.pro_spmv.restype = ctypes.c_int
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.pro_bfs.argtypes = [ctypes.c_int32, ctypes.c_int64, i32p, i32p, ctypes.c_int32, i32p, i32p,
+                            i64p, f64p]
+    lib.pro_bfs.restype = ctypes.c_int
+    lib.pro_wcc.argtypes = [ctypes.c_int32, ctypes.c_int64, i32p, i32p, i32p, i32p, f64p]
+    lib.pro_wcc.restype = ctypes.c_int
     return lib
 
 
@@ -156,6 +172,42 @@ def spmv(row_ptr, col_idx, vals, x, n_cols: int | None = None, timed: bool = Fal
                            _p(y, ctypes.c_double), _p(secs, ctypes.c_double)), "spmv")
     y = y[:n_rows]
     return (y, float(secs[0])) if timed else y
+
+
+class BfsResult:
+    __slots__ = ("level", "depth", "edges_scanned", "loop_seconds")
+
+    def __init__(self, level, depth, edges, secs):
+        self.level, self.depth, self.edges_scanned, self.loop_seconds = level, depth, edges, secs
+
+
+def bfs(row_ptr, col_idx, source: int) -> BfsResult:
+    """Breadth-first levels from `source` over the out-edges (-1: unreachable)."""
+    rp, ci = _csr(row_ptr, col_idx)
+    n, m = rp.size - 1, ci.size
+    level = np.empty(max(n, 1), dtype=np.int32)
+    depth = np.zeros(1, dtype=np.int32)
+    edges = np.zeros(1, dtype=np.int64)
+    secs = np.zeros(1, dtype=np.float64)
+    _check(_lib().pro_bfs(n, m, _p(rp, ctypes.c_int32), _p(ci, ctypes.c_int32), int(source),
+                          _p(level, ctypes.c_int32), _p(depth, ctypes.c_int32),
+                          _p(edges, ctypes.c_int64), _p(secs, ctypes.c_double)), "bfs")
+    return BfsResult(level[:n], int(depth[0]), int(edges[0]), float(secs[0]))
+
+
+def wcc(row_ptr, col_idx, timed: bool = False):
+    """Weakly connected components: label[v] = smallest id in v's component.
+    Returns (label, n_components), plus the search's seconds with timed=True."""
+    rp, ci = _csr(row_ptr, col_idx)
+    n, m = rp.size - 1, ci.size
+    label = np.empty(max(n, 1), dtype=np.int32)
+    comps = np.zeros(1, dtype=np.int32)
+    secs = np.zeros(1, dtype=np.float64)
+    _check(_lib().pro_wcc(n, m, _p(rp, ctypes.c_int32), _p(ci, ctypes.c_int32),
+                          _p(label, ctypes.c_int32), _p(comps, ctypes.c_int32),
+                          _p(secs, ctypes.c_double)), "wcc")
+    out = (label[:n], int(comps[0]))
+    return out + (float(secs[0]),) if timed else out
 
 
 def ranking(x) -> np.ndarray:

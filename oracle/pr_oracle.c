@@ -159,3 +159,89 @@ int pro_spmv(int32_t n_rows, int32_t n_cols, int64_t nnz, const int32_t* rp, con
     if (loop_seconds) *loop_seconds = now_seconds() - t0;
     return PRO_OK;
 }
+
+/* "gpu-graph-study", section "Traversal (BFS / WCC)": breadth-first search
+ * from one source over the out-edges.  level[v] = number of edges on a
+ * shortest directed path source -> v, -1 when no path exists.  A plain FIFO
+ * queue: every vertex enters it once, when it is first reached, with the
+ * level of the vertex that reached it plus one. */
+int pro_bfs(int32_t n, int64_t m, const int32_t* rp, const int32_t* ci, int32_t source,
+            int32_t* level, int32_t* depth, int64_t* edges_scanned, double* loop_seconds) {
+    int rc = check_csr(n, m, rp, ci);
+    if (rc) return rc;
+    if (!level || source < 0 || source >= n) return PRO_ERR_ARG;
+    int32_t* queue = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    if (!queue) return PRO_ERR_NOMEM;
+    const double t0 = now_seconds();
+    for (int32_t v = 0; v < n; ++v) level[v] = -1;
+    level[source] = 0;
+    int64_t head = 0, tail = 0, scanned = 0;
+    queue[tail++] = source;
+    int32_t deepest = 0;
+    while (head < tail) {
+        const int32_t u = queue[head++];
+        if (level[u] > deepest) deepest = level[u];
+        for (int32_t e = rp[u]; e < rp[u + 1]; ++e) {
+            const int32_t v = ci[e];
+            scanned += 1;
+            if (level[v] == -1) {
+                level[v] = level[u] + 1;
+                queue[tail++] = v;
+            }
+        }
+    }
+    if (loop_seconds) *loop_seconds = now_seconds() - t0;
+    if (depth) *depth = deepest;
+    if (edges_scanned) *edges_scanned = scanned;
+    free(queue);
+    return PRO_OK;
+}
+
+/* "gpu-graph-study", section "Traversal (BFS / WCC)": weakly connected
+ * components, the components of the graph with edge directions ignored.
+ * label[v] = the smallest vertex id in v's component (the value min-label
+ * propagation settles on).  Computed by breadth-first search over the
+ * undirected view (out-edges plus in-edges), starting a new search from each
+ * vertex, in increasing id order, that no earlier search reached: that
+ * vertex is the smallest of its component. */
+int pro_wcc(int32_t n, int64_t m, const int32_t* rp, const int32_t* ci, int32_t* label,
+            int32_t* n_components, double* loop_seconds) {
+    int rc = check_csr(n, m, rp, ci);
+    if (rc) return rc;
+    if (!label) return PRO_ERR_ARG;
+    int32_t* in_rp = (int32_t*)malloc(sizeof(int32_t) * ((size_t)n + 1));
+    int32_t* in_ci = (int32_t*)malloc(sizeof(int32_t) * (size_t)(m > 0 ? m : 1));
+    int32_t* queue = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    if (!in_rp || !in_ci || !queue) {
+        free(in_rp); free(in_ci); free(queue);
+        return PRO_ERR_NOMEM;
+    }
+    pro_transpose(n, m, rp, ci, in_rp, in_ci);
+    const double t0 = now_seconds();
+    for (int32_t v = 0; v < n; ++v) label[v] = -1;
+    int32_t comps = 0;
+    for (int32_t s = 0; s < n; ++s) {
+        if (label[s] != -1) continue;
+        comps += 1;
+        int64_t head = 0, tail = 0;
+        label[s] = s;
+        queue[tail++] = s;
+        while (head < tail) {
+            const int32_t u = queue[head++];
+            for (int32_t e = rp[u]; e < rp[u + 1]; ++e)  /* u -> v */
+                if (label[ci[e]] == -1) {
+                    label[ci[e]] = s;
+                    queue[tail++] = ci[e];
+                }
+            for (int32_t e = in_rp[u]; e < in_rp[u + 1]; ++e)  /* w -> u */
+                if (label[in_ci[e]] == -1) {
+                    label[in_ci[e]] = s;
+                    queue[tail++] = in_ci[e];
+                }
+        }
+    }
+    if (loop_seconds) *loop_seconds = now_seconds() - t0;
+    if (n_components) *n_components = comps;
+    free(in_rp); free(in_ci); free(queue);
+    return PRO_OK;
+}

@@ -21,6 +21,11 @@
  *     CUDA": the CSR arrays row_offsets / cols / vals and the product
  *     y[i] = sum over j in row i of vals[j] * x[cols[j]], in double, summed
  *     in stored order (the thread-per-row kernel and the CPU loop it ports).
+ *   "gpu-graph-study", sections "Traversal (BFS / WCC)" and "Traversal T4 --
+ *     degree-bucketed BFS / WCC": breadth-first levels from a source over the
+ *     out-edges, and weakly connected components (edge directions ignored)
+ *     labelled by label propagation, whose fixed point gives every vertex the
+ *     smallest id of its component.
  *   "Meerkat: A Framework for Dynamic Graph Algorithms on GPUs", PageRank
  *     section -- static start 1/n, iteration i built from iteration i-1,
  *     teleport mass from the zero-out-degree vertices of iteration i-1, and
@@ -71,6 +76,22 @@ int pro_pagerank(int32_t n, int64_t m, const int32_t* out_row_ptr, const int32_t
 int pro_spmv(int32_t n_rows, int32_t n_cols, int64_t nnz, const int32_t* row_ptr,
              const int32_t* col_idx, const double* vals, const double* x, double* y,
              double* loop_seconds);
+
+/* Breadth-first levels from `source` over the out-edges: level[v] = edges on a
+ * shortest directed path source -> v, or -1 if v is unreachable.  Host arrays:
+ * level[n].  Optional outputs: *depth = the largest level reached (the
+ * search's depth; 0 when only the source is reached), *edges_scanned =
+ * out-edges of the reached vertices,
+ * *loop_seconds = wall time of the search. */
+int pro_bfs(int32_t n, int64_t m, const int32_t* row_ptr, const int32_t* col_idx, int32_t source,
+            int32_t* level, int32_t* depth, int64_t* edges_scanned, double* loop_seconds);
+
+/* Weakly connected components: label[v] = smallest vertex id of the
+ * component of v in the graph with edge directions ignored.  Host arrays:
+ * label[n].  Optional: *n_components, *loop_seconds (the search alone, not
+ * the transpose it builds first). */
+int pro_wcc(int32_t n, int64_t m, const int32_t* row_ptr, const int32_t* col_idx, int32_t* label,
+            int32_t* n_components, double* loop_seconds);
 
 #ifdef __cplusplus
 }

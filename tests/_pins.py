@@ -59,3 +59,35 @@ def chain_closed_form(n: int, d: float) -> np.ndarray:
     k = (1 - d) / (n - d * (1 - d ** n) / (1 - d))
     i = np.arange(n, dtype=np.float64)
     return k * (1 - d ** (i + 1)) / (1 - d)
+
+
+def dense_adjacency(n: int, row_ptr, col_idx) -> np.ndarray:
+    """Boolean A[u, v] = there is an edge u -> v."""
+    A = np.zeros((n, n), dtype=bool)
+    for u in range(n):
+        for k in range(row_ptr[u], row_ptr[u + 1]):
+            A[u, col_idx[k]] = True
+    return A
+
+
+def brute_levels(A: np.ndarray, source: int) -> np.ndarray:
+    """Smallest k with a length-k walk source -> v, from successive boolean
+    products R_{k+1} = R_k A starting at R_0 = e_source; -1 if none."""
+    n = A.shape[0]
+    level = np.full(n, -1, dtype=np.int64)
+    reach = np.zeros(n, dtype=bool)
+    reach[source] = True
+    for k in range(n):
+        level[(level == -1) & reach] = k
+        reach = (reach.astype(np.int64) @ A.astype(np.int64)) > 0
+    return level
+
+
+def brute_weak_labels(A: np.ndarray) -> np.ndarray:
+    """Smallest vertex id connected to v once directions are ignored, from the
+    transitive closure (Warshall) of the symmetrised adjacency."""
+    n = A.shape[0]
+    C = A | A.T | np.eye(n, dtype=bool)
+    for k in range(n):
+        C = C | (C[:, k:k + 1] & C[k:k + 1, :])
+    return np.array([int(np.flatnonzero(C[v])[0]) for v in range(n)], dtype=np.int64)
