@@ -1,7 +1,9 @@
 /*
  * pr.h -- C ABI of libpr, PageRank power iteration with dangling-node
  * redistribution on one AMD Instinct MI355X (gfx950), and the valued sparse
- * matrix-vector product its pull iteration generalizes (pr_spmv, below).
+ * matrix-vector product its pull iteration generalizes (pr_spmv, below), and
+ * breadth-first search and weakly connected components on the same CSR
+ * (pr_bfs, pr_wcc).
  *
  * The method ("100 Days of GPU", Day 40 "PageRank on a real graph in CUDA",
  * section "One iteration, three shapes of work"):
@@ -314,6 +316,67 @@ int pr_spmv(const pr_spmv_plan* plan, const double* vals_dev, const double* x_de
 /* Introspection for tests and benchmarks: counts_host[4] receives the number
  * of streamed blocks, of 65..1024-entry rows, of longer rows, and of chunks. */
 int pr_spmv_plan_items(const pr_spmv_plan* plan, int32_t* counts_host);
+
+/* ---------------------------------------------------------------------------
+ * Traversals on the same out-edge CSR ("gpu-graph-study", sections
+ * "Traversal (BFS / WCC)" and "Traversal T4 -- degree-bucketed BFS / WCC"):
+ * breadth-first levels from a source, and weakly connected components.  Both
+ * schedule rows by out-degree: rows of fewer than 256 edges are walked 64 at
+ * a time by one wavefront as one flattened edge list; longer rows are cut
+ * into 2048-edge chunks dealt to whole workgroups.
+ * ------------------------------------------------------------------------ */
+
+/* Device bytes pr_bfs / pr_wcc need as workspace.  Host-only; 0 for invalid
+ * sizes (n < 1, nnz < 0 or > INT32_MAX). */
+size_t pr_bfs_workspace_bytes(int32_t n, int64_t nnz);
+size_t pr_wcc_workspace_bytes(int32_t n, int64_t nnz);
+
+/*
+ * Breadth-first search over the out-edges from `source`, level by level (a
+ * frontier expansion per level; a vertex is claimed by the first edge that
+ * reaches it, with a compare-and-swap on its level).
+ *
+ *   n, nnz                   n >= 1, 0 <= nnz <= INT32_MAX
+ *   row_ptr_dev[n+1],        out-edge CSR (read only); duplicate edges and
+ *   col_idx_dev[nnz]         self-loops are allowed
+ *   source                   0 <= source < n, else PR_ERR_ARG
+ *   level_dev[n]             out: level[v] = edges on a shortest directed path
+ *                            source -> v, -1 if v is unreachable
+ *   depth_host               out (may be NULL): the largest level reached
+ *   edges_scanned_host       out (may be NULL): out-edges of the vertices
+ *                            reached (each is expanded once)
+ *   ws_dev, ws_bytes         >= pr_bfs_workspace_bytes(n, nnz), 256-byte aligned
+ *   flags                    0 or PR_VALIDATE (as for pr_transpose)
+ *
+ * Synchronizes `stream`: levels are launched in batches (4, 8, ... up to 64)
+ * and the next frontier's size is read back once per batch.  Without
+ * PR_VALIDATE a malformed CSR cannot make a kernel leave its arrays (edge
+ * offsets and columns are clamped) but the levels are then unspecified.
+ */
+int pr_bfs(int32_t n, int64_t nnz, const int32_t* row_ptr_dev, const int32_t* col_idx_dev,
+           int32_t source, int32_t* level_dev, int32_t* depth_host, int64_t* edges_scanned_host,
+           void* ws_dev, size_t ws_bytes, uint32_t flags, void* stream);
+
+/*
+ * Weakly connected components (edge directions ignored): label_dev[v] = the
+ * smallest vertex id in v's component, which is where the page's min-label
+ * propagation settles.  Computed by linking trees in one pass over the edges
+ * (a tree's root is always its smallest vertex) and a final pass that points
+ * every vertex at its root.
+ *
+ *   n, nnz, row_ptr_dev, col_idx_dev   as for pr_bfs
+ *   label_dev[n]             out
+ *   n_components_host        out (may be NULL): number of components; when
+ *                            given, the call synchronizes `stream`
+ *   ws_dev, ws_bytes         >= pr_wcc_workspace_bytes(n, nnz), 256-byte aligned
+ *   flags                    0 or PR_VALIDATE
+ *
+ * Asynchronous unless n_components_host or PR_VALIDATE is given.  Calls that
+ * share a workspace must not overlap in time.
+ */
+int pr_wcc(int32_t n, int64_t nnz, const int32_t* row_ptr_dev, const int32_t* col_idx_dev,
+           int32_t* label_dev, int32_t* n_components_host, void* ws_dev, size_t ws_bytes,
+           uint32_t flags, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* pr_status_string(int status);

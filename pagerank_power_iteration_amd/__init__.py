@@ -20,7 +20,8 @@ from __future__ import annotations
 
 from ._lib import (PR_ERR_ARG, PR_ERR_GRAPH, PR_ERR_HIP, PR_ERR_WORKSPACE, PR_OK,
                    PR_PLAN_BUCKETED, PR_RECORD_EVENTS, PR_VALIDATE, PR_X0_GIVEN, PrError,
-                   lib, pr_last_error, pr_plan_buckets, pr_plan_create, pr_plan_destroy,
+                   lib, pr_bfs, pr_bfs_workspace_bytes, pr_last_error, pr_wcc,
+                   pr_wcc_workspace_bytes, pr_plan_buckets, pr_plan_create, pr_plan_destroy,
                    pr_plan_iteration_ms, pr_plan_kernel_ms, pr_plan_layout, pr_plan_tiles, pr_plan_num_buckets,
                    pr_plan_scratch_bytes, pr_plan_workspace_bytes, pr_run, pr_status_string,
                    pr_spmv, pr_spmv_plan_create, pr_spmv_plan_destroy, pr_spmv_plan_items,
@@ -35,6 +36,7 @@ __all__ = [
     "pr_plan_buckets", "pr_plan_num_buckets", "pr_plan_layout", "pr_status_string",
     "pr_last_error", "SpmvPlan", "pr_spmv", "pr_spmv_plan_create", "pr_spmv_plan_destroy",
     "pr_spmv_plan_items", "pr_spmv_scratch_bytes", "pr_spmv_workspace_bytes",
+    "bfs", "wcc", "pr_bfs", "pr_bfs_workspace_bytes", "pr_wcc", "pr_wcc_workspace_bytes",
     "PR_OK", "PR_ERR_ARG", "PR_ERR_WORKSPACE", "PR_ERR_GRAPH", "PR_ERR_HIP",
     "PR_VALIDATE", "PR_PLAN_BUCKETED", "PR_X0_GIVEN", "PR_RECORD_EVENTS",
 ]
@@ -79,6 +81,31 @@ def transpose(graph: DeviceGraph, flags: int = 0, stream=None, ws=None):
         ws = _device_buffer(pr_transpose_workspace_bytes(graph.n, graph.nnz), dev)
     pr_transpose(graph.n, graph.nnz, graph.row_ptr, graph.col_idx, in_rp, in_ci, ws, flags, stream)
     return in_rp, in_ci
+
+
+def bfs(graph: DeviceGraph, source: int, flags: int = 0, stream=None, ws=None, out=None):
+    """Breadth-first levels from `source` via pr_bfs: (level int32[n] on the
+    device, depth, out-edges scanned)."""
+    torch = _torch()
+    dev = graph.row_ptr.device
+    level = out if out is not None else torch.empty(graph.n, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = _device_buffer(pr_bfs_workspace_bytes(graph.n, graph.nnz), dev)
+    depth, scanned = pr_bfs(graph.n, graph.nnz, graph.row_ptr, graph.col_idx, source, level, ws,
+                            flags, stream)
+    return level, depth, scanned
+
+
+def wcc(graph: DeviceGraph, flags: int = 0, stream=None, ws=None, out=None):
+    """Weakly connected components via pr_wcc: (label int32[n] on the device,
+    number of components)."""
+    torch = _torch()
+    dev = graph.row_ptr.device
+    label = out if out is not None else torch.empty(graph.n, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = _device_buffer(pr_wcc_workspace_bytes(graph.n, graph.nnz), dev)
+    comps = pr_wcc(graph.n, graph.nnz, graph.row_ptr, graph.col_idx, label, ws, flags, stream)
+    return label, comps
 
 
 class RunResult:

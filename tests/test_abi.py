@@ -72,3 +72,32 @@ def test_binding_raises_prerror():
     with pytest.raises(prx.PrError) as e:
         _lib._check(prx.lib().pr_transpose(0, 0, None, None, None, None, None, 0, 0, None))
     assert e.value.status == prx.PR_ERR_ARG
+
+
+def test_traversal_workspace_queries_and_argument_checks():
+    so = prx.lib()
+    assert prx.pr_bfs_workspace_bytes(0, 10) == 0
+    assert prx.pr_wcc_workspace_bytes(10, -1) == 0
+    assert prx.pr_bfs_workspace_bytes(10, 1 << 31) == 0
+    n, m = 1 << 23, 268_435_456
+    # two int32 frontier queues for BFS; hub chunk descriptors for both
+    assert prx.pr_bfs_workspace_bytes(n, m) >= 8 * n + prx.pr_wcc_workspace_bytes(n, m) - 256
+    assert 0 < prx.pr_wcc_workspace_bytes(n, m) < 4 * m
+    ws = prx.pr_bfs_workspace_bytes(100, 1000)
+    # n < 1, bad source, unknown flags, null level, short / misaligned workspace:
+    # all rejected on the host, before any device work
+    assert so.pr_bfs(0, 0, 256, 256, 0, 256, None, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_bfs(100, 1000, 256, 256, 100, 256, None, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert "source" in prx.pr_last_error()
+    assert so.pr_bfs(100, 1000, 256, 256, -1, 256, None, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_bfs(100, 1000, 256, 256, 0, 256, None, None, 256, ws, 0x10, None) == prx.PR_ERR_ARG
+    assert so.pr_bfs(100, 1000, 256, 256, 0, None, None, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_bfs(100, 1000, 256, 256, 0, 256, None, None, 256, ws - 1, 0, None) == \
+        prx.PR_ERR_WORKSPACE
+    assert so.pr_bfs(100, 1000, 256, 256, 0, 256, None, None, 260, ws, 0, None) == \
+        prx.PR_ERR_WORKSPACE
+    ws = prx.pr_wcc_workspace_bytes(100, 1000)
+    assert so.pr_wcc(100, -1, 256, 256, 256, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_wcc(100, 1000, 256, None, 256, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_wcc(100, 1000, 256, 256, 256, None, 256, ws - 1, 0, None) == prx.PR_ERR_WORKSPACE
+    assert so.pr_wcc(100, 1000, 256, 256, 256, None, 256, ws, 0x4, None) == prx.PR_ERR_ARG
