@@ -92,6 +92,18 @@ def copy_row(torch, gib: float = 2.0, reps: int = 5) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def cpu_traversal_baseline(g) -> dict:
+    """The oracle's breadth-first search from vertex 0 and weak components on
+    the same graph, single-threaded, search loops only."""
+    import oracle
+    ref = oracle.bfs(g.row_ptr, g.col_idx, 0)
+    _, _, wcc_secs = oracle.wcc(g.row_ptr, g.col_idx, timed=True)
+    return {"bfs_ms": round(ref.loop_seconds * 1e3, 2),
+            "bfs_gteps": round(ref.edges_scanned / ref.loop_seconds / 1e9, 4),
+            "wcc_ms": round(wcc_secs * 1e3, 2), "wcc_gteps": round(g.m / wcc_secs / 1e9, 4),
+            "cores": 1}
+
+
 def cpu_baseline(g, iters: int) -> dict:
     import oracle
     r = oracle.pagerank(g.row_ptr, g.col_idx, d=0.85, tol=0.0, max_iter=iters)
@@ -142,6 +154,73 @@ def spmv_rate(torch, prx, graphgen, nx: int, reps: int) -> dict:
             "frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "items": items}
 
 
+def bfs_min_bytes(n: int, scanned: int, reached: int) -> int:
+    """Bytes a top-down breadth-first search must move: per scanned edge a
+    4-byte column and a 4-byte level read; per reached vertex its two row
+    pointers, its frontier-queue write and read and its level write; the level
+    array initialised once."""
+    return 8 * scanned + 20 * reached + 4 * n
+
+
+def wcc_min_bytes(n: int, m: int) -> int:
+    """Bytes a one-pass linking of weak components must move: per edge a
+    4-byte column and a 4-byte label read; per vertex the label initialised,
+    its row pointer, its own label read, and the final pass's read and write."""
+    return 8 * m + 20 * n
+
+
+def traversal_rates(torch, prx, g, dg, reps: int = 5) -> dict:
+    """BFS from vertex 0 and weak components on one resident graph, given
+    its in-edge CSR from pr_transpose (bottom-up levels, giant-tree skip) and
+    without it: median of `reps` timed calls after one warm-up, each call
+    bracketed by device synchronizations (pr_bfs synchronizes its stream
+    itself).  The transpose is built once, outside the timed calls."""
+    stream = torch.cuda.current_stream()
+    in_rp, in_ci = prx.transpose(dg)
+    level = torch.empty(g.n, dtype=torch.int32, device="cuda")
+    label = torch.empty(g.n, dtype=torch.int32, device="cuda")
+    ws_b = torch.empty(prx.pr_bfs_workspace_bytes(g.n, g.m), dtype=torch.uint8, device="cuda")
+    ws_w = torch.empty(prx.pr_wcc_workspace_bytes(g.n, g.m), dtype=torch.uint8, device="cuda")
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            out = fn()
+            torch.cuda.synchronize()
+            ts.append((time.perf_counter() - t0) * 1e3)
+        return statistics.median(ts), out
+
+    def bfs(irp, ici):
+        return prx.pr_bfs(g.n, g.m, dg.row_ptr, dg.col_idx, 0, level, ws_b, irp, ici, 0, stream)
+
+    def wcc(irp, ici):
+        return prx.pr_wcc(g.n, g.m, dg.row_ptr, dg.col_idx, label, ws_w, irp, ici, 0, stream,
+                          count_components=True)
+
+    bfs_out_ms, _ = timed(lambda: bfs(None, None))
+    wcc_out_ms, _ = timed(lambda: wcc(None, None))
+    bfs_ms, (depth, scanned) = timed(lambda: bfs(in_rp, in_ci))
+    reached = int((level >= 0).sum().item())
+    wcc_ms, comps = timed(lambda: wcc(in_rp, in_ci))
+    bb = bfs_min_bytes(g.n, scanned, reached)
+    wb = wcc_min_bytes(g.n, g.m)
+    return {
+        "bfs": {"source": 0, "ms": round(bfs_ms, 4), "depth": depth, "reached": reached,
+                "edges_scanned": scanned, "gteps": round(scanned / (bfs_ms * 1e-3) / 1e9, 2),
+                "algorithmic_bytes": bb, "gbps": round(bb / (bfs_ms * 1e-3) / 1e9, 1),
+                "frac": round(bb / (bfs_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "out_edges_only_ms": round(bfs_out_ms, 4)},
+        "wcc": {"ms": round(wcc_ms, 4), "components": comps,
+                "gteps": round(g.m / (wcc_ms * 1e-3) / 1e9, 2), "algorithmic_bytes": wb,
+                "gbps": round(wb / (wcc_ms * 1e-3) / 1e9, 1),
+                "frac": round(wb / (wcc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "out_edges_only_ms": round(wcc_out_ms, 4)},
+    }
+
+
 def workload_rate(torch, prx, graphgen, name: str, iters: int) -> dict:
     """Per-iteration rate of one more workload: a plan, one warm-up run, then
     `iters` timed iterations (median of 3 runs) and the gather kernel's mean
@@ -177,6 +256,9 @@ def main() -> int:
     ap.add_argument("--spmv-grid", type=int, default=100,
                     help="edge of the 27-point stencil grid of the valued fp64 product "
                          "(0 skips it)")
+    ap.add_argument("--traversal", default="rmat23,grid1024",
+                    help="graphs on which BFS from vertex 0 and weak components are timed "
+                         "(the main workload's graph is reused when named; empty skips)")
     ap.add_argument("--workloads", default="",
                     help="comma-separated extra workloads (e.g. citation,stencil100,rmat18,rmat21) "
                          "whose per-iteration rate is added under 'workloads'")
@@ -275,6 +357,19 @@ def main() -> int:
         extra[name] = workload_rate(torch, prx, graphgen, name, args.iters)
         log(f"{name}: {extra[name]}")
 
+    trav, trav_graphs = {}, {}
+    for name in [w for w in args.traversal.split(",") if w]:
+        if name == g.name:
+            tg, tdg = g, dg
+        else:
+            tg = graphgen.workload(name)
+            tdg = prx.DeviceGraph.from_csr(tg.row_ptr, tg.col_idx)
+        trav[name] = traversal_rates(torch, prx, tg, tdg)
+        trav_graphs[name] = tg
+        log(f"traversal {name}: {trav[name]}")
+        del tdg
+    torch.cuda.empty_cache()
+
     spmv = None
     if args.spmv_grid > 0:
         spmv = spmv_rate(torch, prx, graphgen, args.spmv_grid, 50)
@@ -284,6 +379,8 @@ def main() -> int:
     if args.cpu_iters > 0:
         log(f"timing the CPU oracle on {args.cpu_iters} iterations ...")
         cpu = cpu_baseline(g, args.cpu_iters)
+        if trav_graphs:
+            cpu["traversal"] = {k: cpu_traversal_baseline(v) for k, v in trav_graphs.items()}
 
     iter_cv = (statistics.pstdev(parts["iter"]) / statistics.mean(parts["iter"])
                if len(parts["iter"]) > 1 else 0.0)
@@ -318,6 +415,8 @@ def main() -> int:
     }
     if spmv:
         out["spmv"] = spmv
+    if trav:
+        out["traversal"] = trav
     if extra:
         out["workloads"] = extra
     print(json.dumps(out), flush=True)

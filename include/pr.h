@@ -332,21 +332,31 @@ size_t pr_bfs_workspace_bytes(int32_t n, int64_t nnz);
 size_t pr_wcc_workspace_bytes(int32_t n, int64_t nnz);
 
 /*
- * Breadth-first search over the out-edges from `source`, level by level (a
- * frontier expansion per level; a vertex is claimed by the first edge that
- * reaches it, with a compare-and-swap on its level).
+ * Breadth-first search over the out-edges from `source`, level by level.  A
+ * level is expanded top-down (each frontier vertex's out-edges; a vertex is
+ * claimed by the first edge that reaches it, with a compare-and-swap on its
+ * level) or, when the in-edge CSR is given and the frontier is large,
+ * bottom-up (each unvisited vertex looks through its in-edges for a source on
+ * the current level), by the direction-optimizing rule: bottom-up once the
+ * frontier's out-edges exceed 1/14 of the unexplored edges, top-down again
+ * once the frontier holds fewer than n/24 vertices.  The levels do not
+ * depend on the direction taken.
  *
  *   n, nnz                   n >= 1, 0 <= nnz <= INT32_MAX
  *   row_ptr_dev[n+1],        out-edge CSR (read only); duplicate edges and
  *   col_idx_dev[nnz]         self-loops are allowed
+ *   in_row_ptr_dev[n+1],     the in-edge CSR of the same graph (pr_transpose's
+ *   in_col_idx_dev[nnz]      output), or both NULL for top-down levels only
  *   source                   0 <= source < n, else PR_ERR_ARG
  *   level_dev[n]             out: level[v] = edges on a shortest directed path
  *                            source -> v, -1 if v is unreachable
  *   depth_host               out (may be NULL): the largest level reached
  *   edges_scanned_host       out (may be NULL): out-edges of the vertices
- *                            reached (each is expanded once)
+ *                            reached (the edges a top-down search scans)
  *   ws_dev, ws_bytes         >= pr_bfs_workspace_bytes(n, nnz), 256-byte aligned
- *   flags                    0 or PR_VALIDATE (as for pr_transpose)
+ *   flags                    0 or PR_VALIDATE (both CSRs checked as for
+ *                            pr_transpose; that the second is the transpose
+ *                            of the first is the caller's promise)
  *
  * Synchronizes `stream`: levels are launched in batches (4, 8, ... up to 64)
  * and the next frontier's size is read back once per batch.  Without
@@ -354,17 +364,21 @@ size_t pr_wcc_workspace_bytes(int32_t n, int64_t nnz);
  * offsets and columns are clamped) but the levels are then unspecified.
  */
 int pr_bfs(int32_t n, int64_t nnz, const int32_t* row_ptr_dev, const int32_t* col_idx_dev,
-           int32_t source, int32_t* level_dev, int32_t* depth_host, int64_t* edges_scanned_host,
-           void* ws_dev, size_t ws_bytes, uint32_t flags, void* stream);
+           const int32_t* in_row_ptr_dev, const int32_t* in_col_idx_dev, int32_t source,
+           int32_t* level_dev, int32_t* depth_host, int64_t* edges_scanned_host, void* ws_dev,
+           size_t ws_bytes, uint32_t flags, void* stream);
 
 /*
  * Weakly connected components (edge directions ignored): label_dev[v] = the
  * smallest vertex id in v's component, which is where the page's min-label
- * propagation settles.  Computed by linking trees in one pass over the edges
- * (a tree's root is always its smallest vertex) and a final pass that points
- * every vertex at its root.
+ * propagation settles.  Computed by linking trees (a tree's root is always
+ * its smallest vertex): each vertex's first two out-edges, then every other
+ * edge, then a pass that points every vertex at its root.  With the in-edge
+ * CSR, the full pass skips the vertices already in the tree most of 1024
+ * sampled vertices share and reads the in-edges of the rest instead.
  *
- *   n, nnz, row_ptr_dev, col_idx_dev   as for pr_bfs
+ *   n, nnz, row_ptr_dev, col_idx_dev, in_row_ptr_dev, in_col_idx_dev
+ *                            as for pr_bfs (the in-edge CSR may be NULL)
  *   label_dev[n]             out
  *   n_components_host        out (may be NULL): number of components; when
  *                            given, the call synchronizes `stream`
@@ -375,8 +389,9 @@ int pr_bfs(int32_t n, int64_t nnz, const int32_t* row_ptr_dev, const int32_t* co
  * share a workspace must not overlap in time.
  */
 int pr_wcc(int32_t n, int64_t nnz, const int32_t* row_ptr_dev, const int32_t* col_idx_dev,
-           int32_t* label_dev, int32_t* n_components_host, void* ws_dev, size_t ws_bytes,
-           uint32_t flags, void* stream);
+           const int32_t* in_row_ptr_dev, const int32_t* in_col_idx_dev, int32_t* label_dev,
+           int32_t* n_components_host, void* ws_dev, size_t ws_bytes, uint32_t flags,
+           void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* pr_status_string(int status);

@@ -83,28 +83,34 @@ def transpose(graph: DeviceGraph, flags: int = 0, stream=None, ws=None):
     return in_rp, in_ci
 
 
-def bfs(graph: DeviceGraph, source: int, flags: int = 0, stream=None, ws=None, out=None):
+def bfs(graph: DeviceGraph, source: int, in_csr=None, flags: int = 0, stream=None, ws=None,
+        out=None):
     """Breadth-first levels from `source` via pr_bfs: (level int32[n] on the
-    device, depth, out-edges scanned)."""
+    device, depth, out-edges scanned).  `in_csr` = (in_row_ptr, in_col_idx),
+    e.g. transpose(graph), enables bottom-up levels."""
     torch = _torch()
     dev = graph.row_ptr.device
     level = out if out is not None else torch.empty(graph.n, dtype=torch.int32, device=dev)
     if ws is None:
         ws = _device_buffer(pr_bfs_workspace_bytes(graph.n, graph.nnz), dev)
+    irp, ici = in_csr if in_csr is not None else (None, None)
     depth, scanned = pr_bfs(graph.n, graph.nnz, graph.row_ptr, graph.col_idx, source, level, ws,
-                            flags, stream)
+                            irp, ici, flags, stream)
     return level, depth, scanned
 
 
-def wcc(graph: DeviceGraph, flags: int = 0, stream=None, ws=None, out=None):
+def wcc(graph: DeviceGraph, in_csr=None, flags: int = 0, stream=None, ws=None, out=None):
     """Weakly connected components via pr_wcc: (label int32[n] on the device,
-    number of components)."""
+    number of components).  `in_csr` lets the full pass skip the giant
+    component."""
     torch = _torch()
     dev = graph.row_ptr.device
     label = out if out is not None else torch.empty(graph.n, dtype=torch.int32, device=dev)
     if ws is None:
         ws = _device_buffer(pr_wcc_workspace_bytes(graph.n, graph.nnz), dev)
-    comps = pr_wcc(graph.n, graph.nnz, graph.row_ptr, graph.col_idx, label, ws, flags, stream)
+    irp, ici = in_csr if in_csr is not None else (None, None)
+    comps = pr_wcc(graph.n, graph.nnz, graph.row_ptr, graph.col_idx, label, ws, irp, ici, flags,
+                   stream)
     return label, comps
 
 

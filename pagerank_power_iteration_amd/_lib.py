@@ -64,11 +64,11 @@ _SIGNATURES = {
     "pr_spmv": (_c.c_int, [_vp, _vp, _vp, _vp, _vp]),
     "pr_spmv_plan_items": (_c.c_int, [_vp, _c.POINTER(_c.c_int32)]),
     "pr_bfs_workspace_bytes": (_c.c_size_t, [_c.c_int32, _c.c_int64]),
-    "pr_bfs": (_c.c_int, [_c.c_int32, _c.c_int64, _vp, _vp, _c.c_int32, _vp,
+    "pr_bfs": (_c.c_int, [_c.c_int32, _c.c_int64, _vp, _vp, _vp, _vp, _c.c_int32, _vp,
                           _c.POINTER(_c.c_int32), _c.POINTER(_c.c_int64), _vp, _c.c_size_t,
                           _c.c_uint32, _vp]),
     "pr_wcc_workspace_bytes": (_c.c_size_t, [_c.c_int32, _c.c_int64]),
-    "pr_wcc": (_c.c_int, [_c.c_int32, _c.c_int64, _vp, _vp, _vp, _c.POINTER(_c.c_int32), _vp,
+    "pr_wcc": (_c.c_int, [_c.c_int32, _c.c_int64, _vp, _vp, _vp, _vp, _vp, _c.POINTER(_c.c_int32), _vp,
                           _c.c_size_t, _c.c_uint32, _vp]),
     "pr_status_string": (_c.c_char_p, [_c.c_int]),
     "pr_last_error": (_c.c_char_p, []),
@@ -247,14 +247,15 @@ def pr_bfs_workspace_bytes(n: int, nnz: int) -> int:
     return int(lib().pr_bfs_workspace_bytes(n, nnz))
 
 
-def pr_bfs(n, nnz, row_ptr, col_idx, source, level, ws, flags=0, stream=None) -> tuple[int, int]:
+def pr_bfs(n, nnz, row_ptr, col_idx, source, level, ws, in_row_ptr=None, in_col_idx=None,
+           flags=0, stream=None) -> tuple[int, int]:
     """Breadth-first levels into `level`; returns (depth, edges scanned).
-    Synchronizes the stream."""
+    Bottom-up levels need the in-edge CSR.  Synchronizes the stream."""
     depth = _c.c_int32(0)
     scanned = _c.c_int64(0)
-    _check(lib().pr_bfs(n, nnz, _ptr(row_ptr), _ptr(col_idx), int(source), _ptr(level),
-                        _c.byref(depth), _c.byref(scanned), _ptr(ws), _nbytes(ws), flags,
-                        _stream(stream)))
+    _check(lib().pr_bfs(n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(in_row_ptr),
+                        _ptr(in_col_idx), int(source), _ptr(level), _c.byref(depth),
+                        _c.byref(scanned), _ptr(ws), _nbytes(ws), flags, _stream(stream)))
     return depth.value, scanned.value
 
 
@@ -262,12 +263,13 @@ def pr_wcc_workspace_bytes(n: int, nnz: int) -> int:
     return int(lib().pr_wcc_workspace_bytes(n, nnz))
 
 
-def pr_wcc(n, nnz, row_ptr, col_idx, label, ws, flags=0, stream=None,
-           count_components: bool = True) -> int | None:
+def pr_wcc(n, nnz, row_ptr, col_idx, label, ws, in_row_ptr=None, in_col_idx=None, flags=0,
+           stream=None, count_components: bool = True) -> int | None:
     """Weak-component labels into `label`; returns the number of components
     (which synchronizes the stream) or None with count_components=False."""
     comps = _c.c_int32(0)
-    _check(lib().pr_wcc(n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(label),
+    _check(lib().pr_wcc(n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(in_row_ptr),
+                        _ptr(in_col_idx), _ptr(label),
                         _c.byref(comps) if count_components else None, _ptr(ws), _nbytes(ws),
                         flags, _stream(stream)))
     return comps.value if count_components else None

@@ -8,37 +8,51 @@
 //     label[v] = the smallest vertex id of v's component (the fixed point of
 //     the page's min-label propagation).
 //
-// Scheduling.  The page splits the vertices by degree into thread, warp and
-// block tiers, re-splitting the BFS frontier on the device every level and
-// syncing with the host to size each tier's grid.  Here, for 64-lane
+// Row scheduling.  The page splits the vertices by degree into thread, warp
+// and block tiers, re-splitting the BFS frontier on the device every level
+// and syncing with the host to size each tier's grid.  Here, for 64-lane
 // wavefronts and with no split pass and no per-level sizing sync:
-//   * a wavefront takes 64 rows (frontier vertices for BFS, every vertex for
-//     WCC).  Rows shorter than kHubMin edges are flattened: the wavefront scans
-//     their lengths and walks the concatenated edge list 256 edges a round,
-//     each lane finding its edge's row by a binary search over the scanned
-//     lengths read across lanes, so every lane stays busy whatever the mix of
-//     degrees and consecutive lanes read consecutive columns;
+//   * a wavefront takes 64 rows.  Rows shorter than kHubMin edges are
+//     flattened: the wavefront scans their lengths and walks the
+//     concatenated edge list 256 edges a round, each lane finding its edge's
+//     row by a binary search over the scanned lengths read across lanes, so
+//     every lane stays busy whatever the mix of degrees and consecutive lanes
+//     read consecutive columns;
 //   * longer rows (hubs) are cut into kHubChunk-edge chunks whose descriptors
 //     are appended to a list, and a second kernel deals the chunks to
 //     workgroups: the page's block tier, without a tail behind one hub.
 // Both kernels read their work counts from device memory, so the host
-// launches BFS levels in growing batches and reads the next frontier's size
-// once per batch.
+// launches BFS levels in growing batches and reads the frontier's size once
+// per batch.
 //
-// BFS claims a vertex with a compare-and-swap on its level, as the page's
-// kernels do with atomicCAS, and appends the claimed vertices to the next
-// frontier with one atomic add per wavefront round.
+// BFS direction.  A level is expanded top-down (the frontier's out-edges; a
+// vertex is claimed with a compare-and-swap on its level, as the page's
+// kernels do with atomicCAS) or, when the caller supplies the in-edge CSR and
+// the frontier is large, bottom-up: every unvisited vertex looks through its
+// in-edges for a parent on the current level and sets its own level, with no
+// atomic on the level array.  The choice follows the direction-optimizing
+// rule of Beamer, Asanovic and Patterson (SC 2012), which the graph study
+// names as the remedy for shallow, skewed graphs: go bottom-up when the
+// frontier's out-edges exceed 1/14 of the edges not yet explored, and back
+// top-down when the frontier holds fewer than n/24 vertices.  Every kernel of
+// a level evaluates the rule from counters the previous level left, so all
+// of them agree without a host round trip.
 //
-// WCC does not propagate labels round by round (the page's form, whose
-// round count grows with the diameter: 2046 levels on its grid).  It hooks
-// trees in one pass over the edges: every vertex starts as its own root; for
-// an edge (u, v) the roots of u and v are found by following parent links,
-// and the larger root is linked under the smaller with a compare-and-swap
-// that succeeds only while the larger is still a root, retrying from the new
-// roots otherwise.  A parent is always smaller than its child, so every tree's
-// root is its smallest vertex; after the pass every edge's ends share a tree,
-// so each component is one tree and a final pass that replaces every parent
-// by its root gives the smallest id of the component.
+// WCC does not propagate labels round by round (the page's form, whose round
+// count grows with the diameter: 2046 levels on its grid).  It links trees:
+// every vertex starts as its own root; for an edge (u, v) the roots of u and
+// v are found by following parent links, and the larger root is linked under
+// the smaller with a compare-and-swap that succeeds only while the larger is
+// still a root, retrying from the new roots otherwise.  A parent is always
+// smaller than its child, so every tree's root is its smallest vertex; once
+// every edge's ends share a tree, each component is one tree and pointing
+// every vertex at its root gives the smallest id of the component.  The
+// order follows Afforest (Sutton, Ben-Nun and Barak, IPDPS 2018): first each
+// vertex's first and second out-edges, each round followed by compression;
+// then the root most of 1024 sampled vertices share (the giant component) is
+// found, and the full pass skips every vertex already in its tree.  Skipping
+// a vertex's out-edges is only safe when its in-edges are seen from the
+// other side, so without the in-edge CSR no vertex is skipped.
 #include <algorithm>
 
 #include "common.hpp"
@@ -46,13 +60,19 @@
 namespace pr {
 namespace {
 
-constexpr int32_t kHubMin = 256;   // rows of at least this many edges go to the hub pass
+constexpr int32_t kHubMin = 256;     // rows of at least this many edges go to the hub pass
 constexpr int32_t kHubChunk = 2048;  // edges per hub chunk: 8 per lane of a workgroup
 constexpr int kPerLane = 4;          // edges per lane per round
 constexpr int kRowGrid = 2048;       // workgroups of the row and hub kernels (8 per CU)
 constexpr int kFirstBatch = 4;       // BFS levels launched before the first frontier check
 constexpr int kMaxBatch = 64;
+constexpr int kTopDown = 0, kBottomUp = 1;
+constexpr uint64_t kAlpha = 14, kBeta = 24;  // direction-switch ratios
+constexpr int32_t kSampledEdges = 2;         // WCC: out-edges linked before the full pass
+constexpr int kGiantSamples = 1024;
+constexpr uint32_t kQueueBuf = 512;  // LDS entries per wavefront staging claimed vertices
 static_assert(kHubChunk % (kBlock * kPerLane) == 0, "a hub chunk is whole rounds");
+static_assert(kGiantSamples % kBlock == 0, "giant samples are whole lane rounds");
 
 // One chunk of a hub row: edges [beg, end) of row `row`.
 struct HubChunk {
@@ -60,22 +80,29 @@ struct HubChunk {
 };
 
 struct TravState {
-    uint32_t front[3];     // BFS frontier sizes, by level mod 3
-    uint32_t err;          // PR_VALIDATE verdict
-    uint32_t chunks[2];    // hub chunks appended, by level mod 2 (WCC: slot 0)
-    uint32_t components;   // WCC: roots counted by the final pass
-    int32_t depth;         // BFS: deepest level whose frontier was non-empty
-    unsigned long long scanned;  // BFS: out-edges of the expanded vertices
-    unsigned long long pad[3];
+    uint32_t front[3];               // BFS frontier sizes, by level mod 3
+    uint32_t err;                    // PR_VALIDATE verdict
+    uint32_t chunks[2];              // hub chunks appended, by level mod 2 (WCC: by pass)
+    uint32_t components;             // WCC: roots counted by the final pass
+    int32_t depth;                   // BFS: deepest level whose frontier was non-empty
+    unsigned long long mf[3];        // BFS: out-degree sum of a level's frontier, by level mod 3
+    unsigned long long explored[2];  // BFS: out-degree sum of the levels below L, by L mod 2
+    int32_t mode[2];                 // BFS: direction of level L, by L mod 2
+    int32_t giant;                   // WCC: the root the full pass skips (-1: none)
+    int32_t pad;
 };
 
 struct TravArgs {
-    const int32_t* rp;
+    const int32_t* rp;     // the CSR a row pass walks (out-edges, or in-edges)
     const int32_t* ci;
+    const int32_t* out_rp;  // out-degrees, for the BFS frontier's edge count
+    const int32_t* in_rp;   // in-edge CSR, or null
+    const int32_t* in_ci;
     uint32_t nnz;
     uint32_t col_max;  // n - 1: columns are clamped to it
     int32_t n;
-    int32_t level;     // BFS: the level whose frontier this launch expands
+    int32_t level;     // BFS: the level this launch expands
+    int32_t skip;      // WCC: edges skipped at the start of every row
     int32_t* out;      // BFS: level[n]; WCC: label[n] (the parent links)
     const int32_t* queue;  // BFS: this level's frontier
     int32_t* next;         // BFS: the next level's frontier
@@ -84,12 +111,13 @@ struct TravArgs {
     TravState* st;
 };
 
-// Edge range of row u, clamped into [0, nnz] so that a malformed row
-// pointer cannot send a read outside col_idx.
-__device__ __forceinline__ void row_range(const TravArgs& a, int32_t u, int32_t& s, int32_t& len) {
-    const int32_t lim = (int32_t)a.nnz;
-    const int32_t b = min(max(a.rp[u], 0), lim);
-    const int32_t e = min(max(a.rp[u + 1], b), lim);
+// Edge range of row u of (rp, nnz), clamped into [0, nnz] so that a
+// malformed row pointer cannot send a read outside the column array.
+__device__ __forceinline__ void row_range(const int32_t* __restrict__ rp, uint32_t nnz, int32_t u,
+                                          int32_t& s, int32_t& len) {
+    const int32_t lim = (int32_t)nnz;
+    const int32_t b = min(max(rp[u], 0), lim);
+    const int32_t e = min(max(rp[u + 1], b), lim);
     s = b;
     len = e - b;
 }
@@ -100,12 +128,20 @@ __device__ __forceinline__ int32_t column(const TravArgs& a, int32_t e) {
     return (int32_t)min((uint32_t)a.ci[min((uint32_t)e, a.nnz - 1u)], a.col_max);
 }
 
-// Append the chunks of hub row u (edges [s, s + len)) to the chunk list of
-// `slot`.  One lane per hub.
-__device__ __forceinline__ void append_hub(const TravArgs& a, int slot, int32_t u, int32_t s,
-                                           int32_t len) {
-    const uint32_t c = (uint32_t)((len + kHubChunk - 1) / kHubChunk);
-    const uint32_t first = atomicAdd(&a.st->chunks[slot], c);
+// Append the chunks of the hub rows a wavefront holds (lane l: row u, edges
+// [s, s + len), when `hub` is set) to the chunk list of `slot`, with one
+// atomic add per wavefront: a counter that every wavefront bumps once per
+// row would serialize them.  Every lane calls this.
+__device__ __forceinline__ void append_hubs(const TravArgs& a, int slot, bool hub, int32_t u,
+                                            int32_t s, int32_t len) {
+    const uint32_t c = hub ? (uint32_t)((len + kHubChunk - 1) / kHubChunk) : 0u;
+    const uint32_t incl = wave_inclusive_scan(c);
+    const uint32_t total = __shfl(incl, kWave - 1, kWave);
+    if (total == 0) return;  // wavefront-uniform
+    uint32_t base = 0;
+    if (lane_id() == 0) base = atomicAdd(&a.st->chunks[slot], total);
+    base = __shfl(base, 0, kWave);
+    const uint32_t first = base + incl - c;
     for (uint32_t k = 0; k < c; ++k) {
         if (first + k >= a.chunk_cap) break;  // cannot happen for a well-formed CSR
         HubChunk h;
@@ -117,20 +153,131 @@ __device__ __forceinline__ void append_hub(const TravArgs& a, int slot, int32_t 
     }
 }
 
-// ------------------------------------------------------------------- BFS op
+__device__ __forceinline__ uint64_t wave_or(uint64_t v) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) v |= __shfl_xor(v, off, kWave);
+    return v;
+}
 
-struct BfsOp {
+// ------------------------------------------------------------ row walking
+
+// The flattened walk over one wavefront's rows of (a.rp, a.ci).  Lane l holds
+// its row's first edge `s`, its length `len` (0 for hubs, skipped and absent
+// rows) and the op's per-row value `aux`.  Edges of rows for which
+// op.active(lane) is false are not loaded.  Every lane of the wavefront calls
+// this, and op.edges is called by every lane.
+template <class Op>
+__device__ __forceinline__ void walk_rows(Op& op, const TravArgs& a, int32_t s, int32_t len,
+                                          int32_t aux) {
+    const int lane = lane_id();
+    const int32_t incl = wave_inclusive_scan(len);
+    const int32_t excl = incl - len;
+    const int32_t total = __shfl(incl, kWave - 1, kWave);
+    for (int32_t base = 0; base < total; base += kWave * kPerLane) {
+        int32_t e[kPerLane], ax[kPerLane], own[kPerLane];
+        bool ok[kPerLane];
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            const int32_t j = base + k * kWave + lane;
+            // largest lane i with excl_i <= j: the row that edge j of the
+            // concatenation belongs to (rows of length 0 are skipped over)
+            int i = 0;
+#pragma unroll
+            for (int step = kWave / 2; step > 0; step >>= 1) {
+                const int c = i + step;
+                if (__shfl(excl, c, kWave) <= j) i = c;
+            }
+            // cross-lane reads in converged code only: a lane masked off at a
+            // read does not supply its value to the others
+            const int32_t first = __shfl(s, i, kWave);
+            const int32_t before = __shfl(excl, i, kWave);
+            ax[k] = __shfl(aux, i, kWave);
+            own[k] = i;
+            ok[k] = j < total && op.active(i);
+            e[k] = ok[k] ? first + (j - before) : 0;
+        }
+        int32_t v[kPerLane];
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) v[k] = ok[k] ? column(a, e[k]) : 0;
+        op.edges(v, ax, own, ok);
+    }
+}
+
+// ---------------------------------------------------------------- BFS rule
+
+// Direction of level L, from what the levels before it left in the state:
+// the direction of level L-1, the size and out-degree sum of level L's
+// frontier, and the out-degree sum of the levels below L.  Every launch of
+// a level computes the same value (none of these fields changes during the
+// level).
+__device__ __forceinline__ int bfs_mode(const TravArgs& a, int L) {
+    if (!a.in_rp || L == 0) return kTopDown;
+    const TravState* st = a.st;
+    const uint64_t nf = st->front[L % 3];
+    const uint64_t mf = st->mf[L % 3];
+    const uint64_t done = st->explored[L % 2] + mf;
+    const uint64_t unexplored = (uint64_t)a.nnz > done ? (uint64_t)a.nnz - done : 0;
+    if (st->mode[(L - 1) % 2] == kTopDown) return mf * kAlpha > unexplored ? kBottomUp : kTopDown;
+    return nf * kBeta < (uint64_t)a.n ? kTopDown : kBottomUp;
+}
+
+__device__ __forceinline__ int32_t out_degree(const int32_t* __restrict__ out_rp, uint32_t nnz,
+                                              int32_t v) {
+    int32_t s, len;
+    row_range(out_rp, nnz, v, s, len);
+    return len;
+}
+
+// A wavefront's staging of claimed vertices in LDS.  The next frontier's
+// counter is bumped once per flush (every 256 or more vertices), not once per
+// round: many wavefronts adding to one address serialize.
+struct QueueWriter {
+    int32_t* buf;     // this wavefront's kQueueBuf entries of LDS
+    int32_t* next;    // the next frontier
+    uint32_t* count;  // its size
+    uint32_t fill;    // entries staged (wavefront-uniform)
+
+    // Stage v for every lane with `take`.  Every lane calls this.
+    __device__ __forceinline__ void push(bool take, int32_t v) {
+        const uint64_t m = __ballot(take);
+        if (take) buf[fill + lanes_below(m)] = v;
+        fill += (uint32_t)__popcll(m);
+    }
+
+    // Copy the staged entries out once at least `at_least` are staged.  LDS
+    // operations of one wavefront complete in order, so the lanes read what
+    // the others wrote.  Every lane calls this.
+    __device__ __forceinline__ void flush(uint32_t at_least) {
+        if (fill == 0 || fill < at_least) return;  // wavefront-uniform
+        __builtin_amdgcn_wave_barrier();
+        uint32_t base = 0;
+        if (lane_id() == 0) base = atomicAdd(count, fill);
+        base = __shfl(base, 0, kWave);
+        for (uint32_t k = lane_id(); k < fill; k += kWave) next[base + k] = buf[k];
+        __builtin_amdgcn_wave_barrier();
+        fill = 0;
+    }
+};
+
+// Top-down: claim the unvisited targets of up to kPerLane edges per lane,
+// stage them for the next frontier and add their out-degrees to this lane's
+// share of its edge count (`edges`, reduced once per workgroup).
+struct TopDownOp {
     int32_t* level;
+    const int32_t* out_rp;
+    uint32_t nnz;
     int32_t next_level;
-    int32_t* next;
-    uint32_t* next_count;
+    QueueWriter q;
+    uint64_t edges_seen;
 
-    __device__ __forceinline__ int32_t prologue(int32_t) const { return 0; }
+    __device__ __forceinline__ TopDownOp(const TravArgs& a, int L, int32_t* lds)
+        : level(a.out), out_rp(a.out_rp), nnz(a.nnz), next_level(L + 1),
+          q{lds, a.next, &a.st->front[(L + 1) % 3], 0u}, edges_seen(0) {}
 
-    // Claim the unvisited targets of up to kPerLane edges per lane and append
-    // them to the next frontier.  Called by every lane of the wavefront.
+    __device__ __forceinline__ bool active(int) const { return true; }
+
     __device__ __forceinline__ void edges(const int32_t (&v)[kPerLane], const int32_t (&)[kPerLane],
-                                          const bool (&ok)[kPerLane]) const {
+                                          const int32_t (&)[kPerLane], const bool (&ok)[kPerLane]) {
         int32_t seen[kPerLane];
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) seen[k] = ok[k] ? level[v[k]] : 0;
@@ -140,22 +287,43 @@ struct BfsOp {
             // a stale read of -1 only costs a failed compare-and-swap
             won[k] = ok[k] && seen[k] == -1 && atomicCAS(&level[v[k]], -1, next_level) == -1;
         }
-        uint64_t mask[kPerLane];
-        uint32_t count = 0;
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
-            mask[k] = __ballot(won[k]);
-            count += (uint32_t)__popcll(mask[k]);
+            q.push(won[k], v[k]);
+            if (won[k]) edges_seen += (uint64_t)out_degree(out_rp, nnz, v[k]);
         }
-        if (count == 0) return;  // wavefront-uniform
-        uint32_t base = 0;
-        if (lane_id() == 0) base = atomicAdd(next_count, count);
-        base = __shfl(base, 0, kWave);
+        q.flush(kQueueBuf - kWave * kPerLane);
+    }
+
+    // Flush what is staged and add the workgroup's edge count.  Every lane of
+    // the workgroup calls this.
+    __device__ __forceinline__ void finish(unsigned long long* next_edges, uint64_t* red) {
+        q.flush(1);
+        const uint64_t e = block_sum(edges_seen, red);
+        if (threadIdx.x == 0 && e) atomicAdd(next_edges, (unsigned long long)e);
+    }
+};
+
+// Bottom-up: the wavefront's 64 candidate vertices look through their
+// in-edges for a source on the current level; bit l of `found` is set once
+// lane l's vertex has one, and its remaining in-edges are not loaded.
+struct BottomUpOp {
+    const int32_t* level;
+    int32_t current;
+    uint64_t found;
+
+    __device__ __forceinline__ bool active(int owner) const { return !((found >> owner) & 1u); }
+
+    __device__ __forceinline__ void edges(const int32_t (&w)[kPerLane], const int32_t (&)[kPerLane],
+                                          const int32_t (&own)[kPerLane], const bool (&ok)[kPerLane]) {
+        int32_t lv[kPerLane];
 #pragma unroll
-        for (int k = 0; k < kPerLane; ++k) {
-            if (won[k]) next[base + lanes_below(mask[k])] = v[k];
-            base += (uint32_t)__popcll(mask[k]);
-        }
+        for (int k = 0; k < kPerLane; ++k) lv[k] = ok[k] ? level[w[k]] : -1;
+        uint64_t bits = 0;
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k)
+            if (lv[k] == current) bits |= 1ull << own[k];
+        found |= wave_or(bits);
     }
 };
 
@@ -192,12 +360,14 @@ __device__ __forceinline__ void hook(int32_t* label, int32_t ru, int32_t v) {
 struct WccOp {
     int32_t* label;
 
+    __device__ __forceinline__ bool active(int) const { return true; }
+
     __device__ __forceinline__ int32_t prologue(int32_t u) const {
         return u >= 0 ? find_root(label, u) : 0;
     }
 
     __device__ __forceinline__ void edges(const int32_t (&v)[kPerLane],
-                                          const int32_t (&root)[kPerLane],
+                                          const int32_t (&root)[kPerLane], const int32_t (&)[kPerLane],
                                           const bool (&ok)[kPerLane]) const {
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k)
@@ -205,141 +375,173 @@ struct WccOp {
     }
 };
 
-// ------------------------------------------------------------ row walking
-
-// The flattened walk over one wavefront's rows.  Lane l holds row `row` (or
-// -1), its first edge `s`, its length `len` (0 for hubs and absent rows) and
-// the op's per-row value `aux`.  Every lane of the wavefront calls this.
-template <class Op>
-__device__ __forceinline__ void walk_rows(const Op& op, const TravArgs& a, int32_t s, int32_t len,
-                                          int32_t aux) {
-    const int lane = lane_id();
-    const int32_t incl = wave_inclusive_scan(len);
-    const int32_t excl = incl - len;
-    const int32_t total = __shfl(incl, kWave - 1, kWave);
-    for (int32_t base = 0; base < total; base += kWave * kPerLane) {
-        int32_t e[kPerLane], ax[kPerLane];
-        bool ok[kPerLane];
-#pragma unroll
-        for (int k = 0; k < kPerLane; ++k) {
-            const int32_t j = base + k * kWave + lane;
-            // largest lane i with excl_i <= j: the row that edge j of the
-            // concatenation belongs to (rows of length 0 are skipped over)
-            int i = 0;
-#pragma unroll
-            for (int step = kWave / 2; step > 0; step >>= 1) {
-                const int c = i + step;
-                if (__shfl(excl, c, kWave) <= j) i = c;
-            }
-            // cross-lane reads in converged code only: a lane masked off at a
-            // read does not supply its value to the others
-            const int32_t first = __shfl(s, i, kWave);
-            const int32_t before = __shfl(excl, i, kWave);
-            ax[k] = __shfl(aux, i, kWave);
-            ok[k] = j < total;
-            e[k] = ok[k] ? first + (j - before) : 0;
-        }
-        int32_t v[kPerLane];
-#pragma unroll
-        for (int k = 0; k < kPerLane; ++k) v[k] = ok[k] ? column(a, e[k]) : 0;
-        op.edges(v, ax, ok);
-    }
-}
-
-// Rows [0, count): row i is rows[i], or i itself when rows is null.  Hub
-// rows go to the chunk list of `slot`.  Returns the lane's share of the
-// out-edges seen (hubs included).
-template <class Op>
-__device__ __forceinline__ uint64_t visit_rows(const Op& op, const TravArgs& a,
-                                               const int32_t* rows, uint32_t count, int slot) {
-    const int wave = threadIdx.x / kWave;
-    const int64_t waves = (int64_t)gridDim.x * kWaves;
-    uint64_t seen = 0;
-    for (int64_t t = (int64_t)blockIdx.x * kWaves + wave; t * kWave < (int64_t)count; t += waves) {
-        const int64_t i = t * kWave + lane_id();
-        int32_t u = -1, s = 0, len = 0;
-        if (i < (int64_t)count) {
-            u = rows ? rows[i] : (int32_t)i;
-            row_range(a, u, s, len);
-            seen += (uint64_t)len;
-            if (len >= kHubMin) {
-                append_hub(a, slot, u, s, len);
-                len = 0;
-            }
-        }
-        const int32_t aux = op.prologue(len > 0 ? u : -1);
-        walk_rows(op, a, s, len, aux);
-    }
-    return seen;
-}
-
-// The hub chunks of `slot`, dealt to workgroups round-robin.
-template <class Op>
-__device__ __forceinline__ void visit_hubs(const Op& op, const TravArgs& a, int slot) {
-    const uint32_t count = min(a.st->chunks[slot], a.chunk_cap);
-    for (uint32_t t = blockIdx.x; t < count; t += gridDim.x) {
-        const HubChunk h = a.chunks[t];
-        const int32_t aux = op.prologue(h.row);
-        int32_t ax[kPerLane];
-#pragma unroll
-        for (int k = 0; k < kPerLane; ++k) ax[k] = aux;
-#pragma unroll
-        for (int r = 0; r < kHubChunk / (kBlock * kPerLane); ++r) {
-            int32_t v[kPerLane];
-            bool ok[kPerLane];
-#pragma unroll
-            for (int k = 0; k < kPerLane; ++k) {
-                const int32_t e = h.beg + (r * kPerLane + k) * kBlock + (int32_t)threadIdx.x;
-                ok[k] = e < h.end;
-                v[k] = ok[k] ? column(a, e) : 0;
-            }
-            op.edges(v, ax, ok);
-        }
-    }
-}
-
 // ----------------------------------------------------------------- kernels
 
-__global__ __launch_bounds__(kBlock) void k_bfs_init(int32_t* __restrict__ level, int32_t n,
-                                                     int32_t source, int32_t* __restrict__ queue,
-                                                     TravState* __restrict__ st) {
-    for (int64_t v = blockIdx.x * (int64_t)kBlock + threadIdx.x; v < n;
+__global__ __launch_bounds__(kBlock) void k_bfs_init(TravArgs a, int32_t source) {
+    for (int64_t v = blockIdx.x * (int64_t)kBlock + threadIdx.x; v < a.n;
          v += (int64_t)gridDim.x * kBlock)
-        level[v] = v == source ? 0 : -1;
+        a.out[v] = v == source ? 0 : -1;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
-        queue[0] = source;
+        TravState* st = a.st;
+        const_cast<int32_t*>(a.queue)[0] = source;
         st->front[0] = 1;
         st->front[1] = 0;
         st->front[2] = 0;
+        st->mf[0] = (unsigned long long)out_degree(a.out_rp, a.nnz, source);
+        st->mf[1] = 0;
+        st->mf[2] = 0;
+        st->explored[0] = 0;
+        st->explored[1] = 0;
+        st->mode[0] = kTopDown;
+        st->mode[1] = kTopDown;
         st->chunks[0] = 0;
         st->chunks[1] = 0;
         st->depth = 0;
-        st->scanned = 0;
     }
 }
 
-// Expand the frontier of level a.level: short rows here, hub rows listed for
+// Level a.level: short rows here (top-down: the frontier's out-rows;
+// bottom-up: the unvisited vertices' in-rows), hub rows listed for
 // k_bfs_hubs.  A launch whose frontier is empty does nothing.
 __global__ __launch_bounds__(kBlock) void k_bfs_rows(TravArgs a) {
+    __shared__ int32_t qbuf[kWaves][kQueueBuf];
+    __shared__ uint64_t red[kWaves];
     const int L = a.level;
     const uint32_t count = min(a.st->front[L % 3], (uint32_t)a.n);
-    if (count == 0) return;
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.st->depth = L;
-    BfsOp op{a.out, L + 1, a.next, &a.st->front[(L + 1) % 3]};
-    uint64_t seen = visit_rows(op, a, a.queue, count, L % 2);
-    seen = wave_sum(seen);
-    if (lane_id() == 0 && seen) atomicAdd(&a.st->scanned, (unsigned long long)seen);
+    if (count == 0) return;  // workgroup-uniform
+    const int mode = bfs_mode(a, L);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.st->depth = L;
+        a.st->mode[L % 2] = mode;
+        a.st->explored[(L + 1) % 2] = a.st->explored[L % 2] + a.st->mf[L % 3];
+    }
+    const int wave = threadIdx.x / kWave;
+    const int64_t waves = (int64_t)gridDim.x * kWaves;
+    const int lane = lane_id();
+    int32_t* level = a.out;
+    if (mode == kTopDown) {
+        // after a bottom-up level there is no queue: scan the level array
+        const bool scan = L > 0 && a.st->mode[(L - 1) % 2] == kBottomUp;
+        const int64_t rows = scan ? (int64_t)a.n : (int64_t)count;
+        TopDownOp op(a, L, qbuf[wave]);
+        for (int64_t t = (int64_t)blockIdx.x * kWaves + wave; t * kWave < rows; t += waves) {
+            const int64_t i = t * kWave + lane;
+            int32_t u = -1, s = 0, len = 0;
+            if (i < rows) u = scan ? (level[i] == L ? (int32_t)i : -1) : a.queue[i];
+            if (u >= 0) row_range(a.rp, a.nnz, u, s, len);
+            const bool hub = len >= kHubMin;
+            append_hubs(a, L % 2, hub, u, s, len);
+            walk_rows(op, a, s, hub ? 0 : len, 0);
+        }
+        op.finish(&a.st->mf[(L + 1) % 3], red);
+    } else {
+        TravArgs b = a;  // walk the in-edge CSR
+        b.rp = a.in_rp;
+        b.ci = a.in_ci;
+        uint64_t found_n = 0, found_edges = 0;
+        for (int64_t t = (int64_t)blockIdx.x * kWaves + wave; t * kWave < (int64_t)a.n; t += waves) {
+            const int64_t i = t * kWave + lane;
+            int32_t s = 0, len = 0;
+            const bool cand = i < a.n && level[i] == -1;
+            if (cand) row_range(b.rp, b.nnz, (int32_t)i, s, len);
+            // every row's first kHubMin - 1 in-edges here; the rest of a long
+            // row only if none of those is a parent
+            const int32_t head = min(len, kHubMin - 1);
+            BottomUpOp op{level, L, 0};
+            walk_rows(op, b, s, head, 0);
+            const bool won = cand && head > 0 && ((op.found >> lane) & 1u);
+            if (won) {
+                level[i] = L + 1;
+                found_n += 1;
+                found_edges += (uint64_t)out_degree(a.out_rp, a.nnz, (int32_t)i);
+            }
+            const bool rest = cand && !won && len > head;
+            append_hubs(b, L % 2, rest, (int32_t)i, s + head, len - head);
+        }
+        const uint64_t fn = block_sum(found_n, red);
+        const uint64_t fe = block_sum(found_edges, red);
+        if (threadIdx.x == 0 && fn) {
+            atomicAdd(&a.st->front[(L + 1) % 3], (uint32_t)fn);
+            atomicAdd(&a.st->mf[(L + 1) % 3], (unsigned long long)fe);
+        }
+    }
 }
 
-// Expand the hub chunks of level a.level, then clear the counters that
-// level a.level + 1 appends to (its next frontier count and chunk count)
-// after their last reader (level a.level - 1) is done.
+// The hub chunks of level a.level, then the counters level a.level + 1
+// appends to are cleared (their last reader, level a.level - 1, is done).
 __global__ __launch_bounds__(kBlock) void k_bfs_hubs(TravArgs a) {
+    __shared__ int32_t qbuf[kWaves][kQueueBuf];
+    __shared__ uint64_t red[kWaves];
+    __shared__ int flag;
     const int L = a.level;
-    BfsOp op{a.out, L + 1, a.next, &a.st->front[(L + 1) % 3]};
-    visit_hubs(op, a, L % 2);
+    const uint32_t front = a.st->front[L % 3];
+    const uint32_t count = min(a.st->chunks[L % 2], a.chunk_cap);
+    if (front > 0 && count > 0) {  // workgroup-uniform
+        const int mode = bfs_mode(a, L);
+        int32_t* level = a.out;
+        if (mode == kTopDown) {
+            TopDownOp op(a, L, qbuf[threadIdx.x / kWave]);
+            const int32_t none[kPerLane] = {};
+            for (uint32_t t = blockIdx.x; t < count; t += gridDim.x) {
+                const HubChunk h = a.chunks[t];
+#pragma unroll
+                for (int r = 0; r < kHubChunk / (kBlock * kPerLane); ++r) {
+                    int32_t v[kPerLane];
+                    bool ok[kPerLane];
+#pragma unroll
+                    for (int k = 0; k < kPerLane; ++k) {
+                        const int32_t e = h.beg + (r * kPerLane + k) * kBlock + (int32_t)threadIdx.x;
+                        ok[k] = e < h.end;
+                        v[k] = ok[k] ? column(a, e) : 0;
+                    }
+                    op.edges(v, none, none, ok);
+                }
+            }
+            op.finish(&a.st->mf[(L + 1) % 3], red);
+        } else {
+            TravArgs b = a;
+            b.ci = a.in_ci;
+            uint64_t found_n = 0, found_edges = 0;
+            for (uint32_t t = blockIdx.x; t < count; t += gridDim.x) {  // workgroup-uniform
+                const HubChunk h = a.chunks[t];
+                // one read of the row's level decides for the whole workgroup
+                // whether another chunk has already found it a parent
+                if (threadIdx.x == 0) flag = level[h.row] == -1 ? 0 : 2;
+                __syncthreads();
+                const int state = flag;
+                bool hit = false;
+                if (state == 0) {
+                    int32_t w[kHubChunk / kBlock];
+#pragma unroll
+                    for (int r = 0; r < kHubChunk / kBlock; ++r) {
+                        const int32_t e = h.beg + r * kBlock + (int32_t)threadIdx.x;
+                        w[r] = e < h.end ? column(b, e) : -1;
+                    }
+#pragma unroll
+                    for (int r = 0; r < kHubChunk / kBlock; ++r)
+                        if (w[r] >= 0 && level[w[r]] == L) hit = true;
+                }
+                __syncthreads();  // every lane has read `flag`
+                if (hit) flag = 1;
+                __syncthreads();
+                if (threadIdx.x == 0 && state == 0 && flag == 1 &&
+                    atomicCAS(&level[h.row], -1, L + 1) == -1) {
+                    found_n += 1;
+                    found_edges += (uint64_t)out_degree(a.out_rp, a.nnz, h.row);
+                }
+                __syncthreads();  // before `flag` is written again
+            }
+            const uint64_t fn = block_sum(found_n, red);
+            const uint64_t fe = block_sum(found_edges, red);
+            if (threadIdx.x == 0 && fn) {
+                atomicAdd(&a.st->front[(L + 1) % 3], (uint32_t)fn);
+                atomicAdd(&a.st->mf[(L + 1) % 3], (unsigned long long)fe);
+            }
+        }
+    }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         a.st->front[(L + 2) % 3] = 0;
+        a.st->mf[(L + 2) % 3] = 0;
         a.st->chunks[(L + 1) % 2] = 0;
     }
 }
@@ -351,24 +553,26 @@ __global__ __launch_bounds__(kBlock) void k_wcc_init(int32_t* __restrict__ label
         label[v] = (int32_t)v;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         st->chunks[0] = 0;
+        st->chunks[1] = 0;
         st->components = 0;
+        st->giant = -1;
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_wcc_rows(TravArgs a) {
-    WccOp op{a.out};
-    visit_rows(op, a, nullptr, (uint32_t)a.n, 0);
+// Link every vertex with its r-th out-neighbour (if it has one).
+__global__ __launch_bounds__(kBlock) void k_wcc_sample(TravArgs a, int32_t r) {
+    for (int64_t u = blockIdx.x * (int64_t)kBlock + threadIdx.x; u < a.n;
+         u += (int64_t)gridDim.x * kBlock) {
+        int32_t s, len;
+        row_range(a.rp, a.nnz, (int32_t)u, s, len);
+        if (len > r) hook(a.out, find_root(a.out, (int32_t)u), column(a, s + r));
+    }
 }
 
-__global__ __launch_bounds__(kBlock) void k_wcc_hubs(TravArgs a) {
-    WccOp op{a.out};
-    visit_hubs(op, a, 0);
-}
-
-// Replace every link by its root and count the roots.  Concurrent writers
-// only ever store roots, so every read is an ancestor.
+// Point every vertex at its root; with `count`, also count the roots.
+// Concurrent writers only ever store roots, so every read is an ancestor.
 __global__ __launch_bounds__(kBlock) void k_wcc_compress(int32_t* __restrict__ label, int32_t n,
-                                                         TravState* __restrict__ st) {
+                                                         TravState* __restrict__ st, int count) {
     __shared__ uint32_t red[kWaves];
     uint32_t roots = 0;
     for (int64_t v = blockIdx.x * (int64_t)kBlock + threadIdx.x; v < n;
@@ -382,8 +586,92 @@ __global__ __launch_bounds__(kBlock) void k_wcc_compress(int32_t* __restrict__ l
         label[v] = x;
         roots += x == (int32_t)v ? 1u : 0u;
     }
+    if (!count) return;
     roots = block_sum(roots, red);
     if (threadIdx.x == 0 && roots) atomicAdd(&st->components, roots);
+}
+
+// The root shared by most of kGiantSamples vertices drawn by a fixed
+// multiplicative hash (ties: the smaller root).  One workgroup.
+__global__ __launch_bounds__(kBlock) void k_wcc_giant(const int32_t* __restrict__ label, int32_t n,
+                                                      TravState* __restrict__ st) {
+    __shared__ int32_t smp[kGiantSamples];
+    __shared__ uint64_t best[kWaves];
+    for (int i = threadIdx.x; i < kGiantSamples; i += kBlock) {
+        const uint64_t h = (uint64_t)(i + 1) * 0x9E3779B97F4A7C15ull;
+        smp[i] = label[(int64_t)((h >> 32) % (uint64_t)n)];
+    }
+    __syncthreads();
+    // key = count << 32 | (INT32_MAX - root): the largest key is the most
+    // frequent root, the smaller one on a tie
+    uint64_t key = 0;
+    for (int j = threadIdx.x; j < kGiantSamples; j += kBlock) {
+        uint32_t c = 0;
+        for (int i = 0; i < kGiantSamples; ++i) c += smp[i] == smp[j] ? 1u : 0u;
+        const uint64_t k = (uint64_t)c << 32 | (uint32_t)(INT32_MAX - smp[j]);
+        key = k > key ? k : key;
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const uint64_t o = __shfl_xor(key, off, kWave);
+        key = o > key ? o : key;
+    }
+    if (lane_id() == 0) best[threadIdx.x / kWave] = key;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t b = best[0];
+        for (int w = 1; w < kWaves; ++w) b = best[w] > b ? best[w] : b;
+        st->giant = INT32_MAX - (int32_t)(uint32_t)b;
+    }
+}
+
+// The full linking pass over the rows of (a.rp, a.ci), from edge a.skip of
+// every row, skipping the rows of vertices already in the giant tree.
+__global__ __launch_bounds__(kBlock) void k_wcc_rows(TravArgs a, int slot) {
+    const int32_t giant = a.st->giant;
+    const int wave = threadIdx.x / kWave;
+    const int64_t waves = (int64_t)gridDim.x * kWaves;
+    WccOp op{a.out};
+    for (int64_t t = (int64_t)blockIdx.x * kWaves + wave; t * kWave < (int64_t)a.n; t += waves) {
+        const int64_t i = t * kWave + lane_id();
+        int32_t s = 0, len = 0, root = 0;
+        if (i < a.n && (giant < 0 || a.out[i] != giant)) {
+            row_range(a.rp, a.nnz, (int32_t)i, s, len);
+            const int32_t k = min(len, a.skip);
+            s += k;
+            len -= k;
+        }
+        const bool hub = len >= kHubMin;
+        append_hubs(a, slot, hub, (int32_t)i, s, len);
+        if (hub) len = 0;
+        if (len > 0) root = op.prologue((int32_t)i);
+        walk_rows(op, a, s, len, root);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_wcc_hubs(TravArgs a, int slot) {
+    WccOp op{a.out};
+    const uint32_t count = min(a.st->chunks[slot], a.chunk_cap);
+    const int32_t none[kPerLane] = {};
+    for (uint32_t t = blockIdx.x; t < count; t += gridDim.x) {
+        const HubChunk h = a.chunks[t];
+        const int32_t root = op.prologue(h.row);
+        int32_t roots[kPerLane];
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) roots[k] = root;
+#pragma unroll
+        for (int r = 0; r < kHubChunk / (kBlock * kPerLane); ++r) {
+            int32_t v[kPerLane];
+            bool ok[kPerLane];
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k) {
+                const int32_t e = h.beg + (r * kPerLane + k) * kBlock + (int32_t)threadIdx.x;
+                ok[k] = e < h.end;
+                v[k] = ok[k] ? column(a, e) : 0;
+            }
+            op.edges(v, roots, none, ok);
+        }
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void k_trav_check_cols(const int32_t* __restrict__ ci,
@@ -427,11 +715,14 @@ TravWs carve(void* base, int32_t n, int64_t nnz, bool queues) {
     return w;
 }
 
-int check_graph(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* ci) {
+int check_graph(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* ci,
+                const int32_t* in_rp, const int32_t* in_ci) {
     if (n < 1) return fail(PR_ERR_ARG, "n must be >= 1 (got %d)", n);
     if (nnz < 0 || nnz > INT32_MAX)
         return fail(PR_ERR_ARG, "nnz must be in [0, INT32_MAX] (got %lld)", (long long)nnz);
     if (!rp || (nnz > 0 && !ci)) return fail(PR_ERR_ARG, "null pointer argument");
+    if ((in_ci && !in_rp) || (in_rp && nnz > 0 && !in_ci))
+        return fail(PR_ERR_ARG, "in_row_ptr and in_col_idx are given together or not at all");
     return PR_OK;
 }
 
@@ -443,27 +734,38 @@ int check_ws(const TravWs& w, void* ws, size_t ws_bytes, const char* what) {
     return PR_OK;
 }
 
-int validate(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* ci, TravState* st,
-             hipStream_t stream, const char* what) {
+// PR_VALIDATE: the out-edge CSR, and the in-edge CSR when given (as a CSR of
+// the same size; that it is the transpose is the caller's promise).
+int validate(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* ci, const int32_t* in_rp,
+             const int32_t* in_ci, TravState* st, hipStream_t stream, const char* what) {
     uint32_t* err = &st->err;
     PR_TRY(fill_u32(err, 0u, 1, stream));
     PR_TRY(check_out_row_ptr(rp, n, nnz, err, stream));
+    if (in_rp) PR_TRY(check_out_row_ptr(in_rp, n, nnz, err, stream));
     if (nnz > 0) {
         k_trav_check_cols<<<vertex_grid(nnz), kBlock, 0, stream>>>(ci, nnz, n, err);
         PR_LAUNCHED("check columns");
+        if (in_ci) {
+            k_trav_check_cols<<<vertex_grid(nnz), kBlock, 0, stream>>>(in_ci, nnz, n, err);
+            PR_LAUNCHED("check columns");
+        }
     }
     return read_error_word(err, stream, what);
 }
 
-TravArgs make_args(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* ci, int32_t* out,
-                   const TravWs& w) {
+TravArgs make_args(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* ci,
+                   const int32_t* in_rp, const int32_t* in_ci, int32_t* out, const TravWs& w) {
     TravArgs a{};
     a.rp = rp;
     a.ci = ci;
+    a.out_rp = rp;
+    a.in_rp = in_rp;
+    a.in_ci = in_ci;
     a.nnz = (uint32_t)nnz;
     a.col_max = (uint32_t)(n - 1);
     a.n = n;
     a.out = out;
+    a.queue = w.queue[0];
     a.chunks = w.chunks;
     a.chunk_cap = chunk_capacity(nnz);
     a.st = w.st;
@@ -485,10 +787,11 @@ extern "C" size_t pr_wcc_workspace_bytes(int32_t n, int64_t nnz) {
     return carve(nullptr, n, nnz, false).bytes;
 }
 
-extern "C" int pr_bfs(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* ci, int32_t source,
-                      int32_t* level, int32_t* depth_host, int64_t* edges_scanned_host, void* ws,
-                      size_t ws_bytes, uint32_t flags, void* stream_v) {
-    PR_TRY(check_graph(n, nnz, rp, ci));
+extern "C" int pr_bfs(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* ci,
+                      const int32_t* in_rp, const int32_t* in_ci, int32_t source, int32_t* level,
+                      int32_t* depth_host, int64_t* edges_scanned_host, void* ws, size_t ws_bytes,
+                      uint32_t flags, void* stream_v) {
+    PR_TRY(check_graph(n, nnz, rp, ci, in_rp, in_ci));
     if (!level) return fail(PR_ERR_ARG, "level is null");
     if (source < 0 || source >= n)
         return fail(PR_ERR_ARG, "source %d is not a vertex of a %d-vertex graph", source, n);
@@ -496,11 +799,12 @@ extern "C" int pr_bfs(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* 
     const TravWs w = carve(ws, n, nnz, true);
     PR_TRY(check_ws(w, ws, ws_bytes, "pr_bfs"));
     hipStream_t stream = as_stream(stream_v);
-    if (flags & PR_VALIDATE) PR_TRY(validate(n, nnz, rp, ci, w.st, stream, "pr_bfs"));
+    if (flags & PR_VALIDATE)
+        PR_TRY(validate(n, nnz, rp, ci, in_rp, in_ci, w.st, stream, "pr_bfs"));
 
-    k_bfs_init<<<vertex_grid(n), kBlock, 0, stream>>>(level, n, source, w.queue[0], w.st);
+    TravArgs a = make_args(n, nnz, rp, ci, in_rp, in_ci, level, w);
+    k_bfs_init<<<vertex_grid(n), kBlock, 0, stream>>>(a, source);
     PR_LAUNCHED("bfs init");
-    TravArgs a = make_args(n, nnz, rp, ci, level, w);
     TravState h{};
     int32_t L = 0;
     int batch = kFirstBatch;
@@ -521,29 +825,57 @@ extern "C" int pr_bfs(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* 
         batch = std::min(batch * 2, kMaxBatch);
     }
     if (depth_host) *depth_host = h.depth;
-    if (edges_scanned_host) *edges_scanned_host = (int64_t)h.scanned;
+    // the out-degree sum of every non-empty level, recorded by the level after
+    // the deepest one
+    if (edges_scanned_host) *edges_scanned_host = (int64_t)h.explored[(h.depth + 1) % 2];
     return PR_OK;
 }
 
-extern "C" int pr_wcc(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* ci, int32_t* label,
+extern "C" int pr_wcc(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* ci,
+                      const int32_t* in_rp, const int32_t* in_ci, int32_t* label,
                       int32_t* n_components_host, void* ws, size_t ws_bytes, uint32_t flags,
                       void* stream_v) {
-    PR_TRY(check_graph(n, nnz, rp, ci));
+    PR_TRY(check_graph(n, nnz, rp, ci, in_rp, in_ci));
     if (!label) return fail(PR_ERR_ARG, "label is null");
     if (flags & ~PR_VALIDATE) return fail(PR_ERR_ARG, "unknown flags 0x%x", flags);
     const TravWs w = carve(ws, n, nnz, false);
     PR_TRY(check_ws(w, ws, ws_bytes, "pr_wcc"));
     hipStream_t stream = as_stream(stream_v);
-    if (flags & PR_VALIDATE) PR_TRY(validate(n, nnz, rp, ci, w.st, stream, "pr_wcc"));
+    if (flags & PR_VALIDATE)
+        PR_TRY(validate(n, nnz, rp, ci, in_rp, in_ci, w.st, stream, "pr_wcc"));
 
-    k_wcc_init<<<vertex_grid(n), kBlock, 0, stream>>>(label, n, w.st);
+    const unsigned vg = vertex_grid(n);
+    k_wcc_init<<<vg, kBlock, 0, stream>>>(label, n, w.st);
     PR_LAUNCHED("wcc init");
-    const TravArgs a = make_args(n, nnz, rp, ci, label, w);
-    k_wcc_rows<<<kRowGrid, kBlock, 0, stream>>>(a);
-    PR_LAUNCHED("wcc rows");
-    k_wcc_hubs<<<kRowGrid, kBlock, 0, stream>>>(a);
-    PR_LAUNCHED("wcc hubs");
-    k_wcc_compress<<<vertex_grid(n), kBlock, 0, stream>>>(label, n, w.st);
+    TravArgs a = make_args(n, nnz, rp, ci, in_rp, in_ci, label, w);
+    if (nnz > 0) {
+        for (int32_t r = 0; r < kSampledEdges; ++r) {
+            k_wcc_sample<<<vg, kBlock, 0, stream>>>(a, r);
+            PR_LAUNCHED("wcc sample");
+            k_wcc_compress<<<vg, kBlock, 0, stream>>>(label, n, w.st, 0);
+            PR_LAUNCHED("wcc compress");
+        }
+        if (in_rp) {
+            k_wcc_giant<<<1, kBlock, 0, stream>>>(label, n, w.st);
+            PR_LAUNCHED("wcc giant");
+        }
+        a.skip = kSampledEdges;
+        k_wcc_rows<<<kRowGrid, kBlock, 0, stream>>>(a, 0);
+        PR_LAUNCHED("wcc rows");
+        k_wcc_hubs<<<kRowGrid, kBlock, 0, stream>>>(a, 0);
+        PR_LAUNCHED("wcc hubs");
+        if (in_rp) {  // the in-edges of the vertices outside the giant tree
+            TravArgs b = a;
+            b.rp = in_rp;
+            b.ci = in_ci;
+            b.skip = 0;
+            k_wcc_rows<<<kRowGrid, kBlock, 0, stream>>>(b, 1);
+            PR_LAUNCHED("wcc in-rows");
+            k_wcc_hubs<<<kRowGrid, kBlock, 0, stream>>>(b, 1);
+            PR_LAUNCHED("wcc in-hubs");
+        }
+    }
+    k_wcc_compress<<<vg, kBlock, 0, stream>>>(label, n, w.st, 1);
     PR_LAUNCHED("wcc compress");
     if (n_components_host) {
         uint32_t c = 0;

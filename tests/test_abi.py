@@ -86,18 +86,22 @@ def test_traversal_workspace_queries_and_argument_checks():
     ws = prx.pr_bfs_workspace_bytes(100, 1000)
     # n < 1, bad source, unknown flags, null level, short / misaligned workspace:
     # all rejected on the host, before any device work
-    assert so.pr_bfs(0, 0, 256, 256, 0, 256, None, None, 256, ws, 0, None) == prx.PR_ERR_ARG
-    assert so.pr_bfs(100, 1000, 256, 256, 100, 256, None, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_bfs(0, 0, 256, 256, None, None, 0, 256, None, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_bfs(100, 1000, 256, 256, None, None, 100, 256, None, None, 256, ws, 0, None) == prx.PR_ERR_ARG
     assert "source" in prx.pr_last_error()
-    assert so.pr_bfs(100, 1000, 256, 256, -1, 256, None, None, 256, ws, 0, None) == prx.PR_ERR_ARG
-    assert so.pr_bfs(100, 1000, 256, 256, 0, 256, None, None, 256, ws, 0x10, None) == prx.PR_ERR_ARG
-    assert so.pr_bfs(100, 1000, 256, 256, 0, None, None, None, 256, ws, 0, None) == prx.PR_ERR_ARG
-    assert so.pr_bfs(100, 1000, 256, 256, 0, 256, None, None, 256, ws - 1, 0, None) == \
+    assert so.pr_bfs(100, 1000, 256, 256, None, None, -1, 256, None, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_bfs(100, 1000, 256, 256, None, None, 0, 256, None, None, 256, ws, 0x10, None) == prx.PR_ERR_ARG
+    assert so.pr_bfs(100, 1000, 256, 256, None, None, 0, None, None, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_bfs(100, 1000, 256, 256, None, None, 0, 256, None, None, 256, ws - 1, 0, None) == \
         prx.PR_ERR_WORKSPACE
-    assert so.pr_bfs(100, 1000, 256, 256, 0, 256, None, None, 260, ws, 0, None) == \
+    assert so.pr_bfs(100, 1000, 256, 256, None, None, 0, 256, None, None, 260, ws, 0, None) == \
         prx.PR_ERR_WORKSPACE
     ws = prx.pr_wcc_workspace_bytes(100, 1000)
-    assert so.pr_wcc(100, -1, 256, 256, 256, None, 256, ws, 0, None) == prx.PR_ERR_ARG
-    assert so.pr_wcc(100, 1000, 256, None, 256, None, 256, ws, 0, None) == prx.PR_ERR_ARG
-    assert so.pr_wcc(100, 1000, 256, 256, 256, None, 256, ws - 1, 0, None) == prx.PR_ERR_WORKSPACE
-    assert so.pr_wcc(100, 1000, 256, 256, 256, None, 256, ws, 0x4, None) == prx.PR_ERR_ARG
+    assert so.pr_wcc(100, -1, 256, 256, None, None, 256, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_wcc(100, 1000, 256, None, None, None, 256, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_wcc(100, 1000, 256, 256, None, None, 256, None, 256, ws - 1, 0, None) == prx.PR_ERR_WORKSPACE
+    assert so.pr_wcc(100, 1000, 256, 256, None, None, 256, None, 256, ws, 0x4, None) == prx.PR_ERR_ARG
+    # an in-edge CSR needs both arrays
+    assert so.pr_wcc(100, 1000, 256, 256, 256, None, 256, None, 256, ws, 0, None) == prx.PR_ERR_ARG
+    assert so.pr_bfs(100, 1000, 256, 256, None, 256, 0, 256, None, None, 256,
+                     prx.pr_bfs_workspace_bytes(100, 1000), 0, None) == prx.PR_ERR_ARG
