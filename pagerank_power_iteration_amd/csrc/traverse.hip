@@ -70,9 +70,10 @@ constexpr int kTopDown = 0, kBottomUp = 1;
 constexpr uint64_t kAlpha = 14, kBeta = 24;  // direction-switch ratios
 constexpr int32_t kSampledEdges = 2;         // WCC: out-edges linked before the full pass
 constexpr int kGiantSamples = 1024;
-constexpr uint32_t kQueueBuf = 512;  // LDS entries per wavefront staging claimed vertices
+constexpr uint32_t kQueueBuf = 512;
+constexpr int32_t kProbe = 4;  // in-edges each lane checks itself before a bottom-up walk  // LDS entries per wavefront staging claimed vertices
 static_assert(kHubChunk % (kBlock * kPerLane) == 0, "a hub chunk is whole rounds");
-static_assert(kGiantSamples % kBlock == 0, "giant samples are whole lane rounds");
+static_assert(kGiantSamples <= 1024 && kGiantSamples % kWave == 0, "one sample per lane");
 
 // One chunk of a hub row: edges [beg, end) of row `row`.
 struct HubChunk {
@@ -444,18 +445,28 @@ __global__ __launch_bounds__(kBlock) void k_bfs_rows(TravArgs a) {
             int32_t s = 0, len = 0;
             const bool cand = i < a.n && level[i] == -1;
             if (cand) row_range(b.rp, b.nnz, (int32_t)i, s, len);
-            // every row's first kHubMin - 1 in-edges here; the rest of a long
-            // row only if none of those is a parent
+            // A parent, when there is one, is nearly always among a row's
+            // first few in-edges: each lane first probes its own row's first
+            // kProbe in-edges, two at a time; then the rows still without a
+            // parent walk the rest of their first kHubMin - 1 in-edges
+            // together, and the rest of a long row goes to the hub pass.
+            bool hit = false;
+            const int32_t probe = min(len, kProbe);
+            for (int32_t p = 0; p < probe && !hit; p += 2) {
+                const int32_t w0 = column(b, s + p);
+                const int32_t w1 = p + 1 < probe ? column(b, s + p + 1) : w0;
+                hit = level[w0] == L || level[w1] == L;
+            }
             const int32_t head = min(len, kHubMin - 1);
             BottomUpOp op{level, L, 0};
-            walk_rows(op, b, s, head, 0);
-            const bool won = cand && head > 0 && ((op.found >> lane) & 1u);
+            walk_rows(op, b, s + probe, hit ? 0 : head - probe, 0);
+            const bool won = cand && (hit || ((op.found >> lane) & 1u));
             if (won) {
                 level[i] = L + 1;
                 found_n += 1;
                 found_edges += (uint64_t)out_degree(a.out_rp, a.nnz, (int32_t)i);
             }
-            const bool rest = cand && !won && len > head;
+            const bool rest = cand && !won && len > head;  // (then head > kProbe)
             append_hubs(b, L % 2, rest, (int32_t)i, s + head, len - head);
         }
         const uint64_t fn = block_sum(found_n, red);
@@ -592,35 +603,32 @@ __global__ __launch_bounds__(kBlock) void k_wcc_compress(int32_t* __restrict__ l
 }
 
 // The root shared by most of kGiantSamples vertices drawn by a fixed
-// multiplicative hash (ties: the smaller root).  One workgroup.
-__global__ __launch_bounds__(kBlock) void k_wcc_giant(const int32_t* __restrict__ label, int32_t n,
-                                                      TravState* __restrict__ st) {
+// multiplicative hash (ties: the smaller root).  One workgroup of
+// kGiantSamples lanes, one sample each.
+__global__ __launch_bounds__(kGiantSamples) void k_wcc_giant(const int32_t* __restrict__ label,
+                                                             int32_t n, TravState* __restrict__ st) {
     __shared__ int32_t smp[kGiantSamples];
-    __shared__ uint64_t best[kWaves];
-    for (int i = threadIdx.x; i < kGiantSamples; i += kBlock) {
-        const uint64_t h = (uint64_t)(i + 1) * 0x9E3779B97F4A7C15ull;
-        smp[i] = label[(int64_t)((h >> 32) % (uint64_t)n)];
-    }
+    __shared__ uint64_t best[kGiantSamples / kWave];
+    const int j = threadIdx.x;
+    const uint64_t h = (uint64_t)(j + 1) * 0x9E3779B97F4A7C15ull;
+    smp[j] = label[(int64_t)((h >> 32) % (uint64_t)n)];
     __syncthreads();
     // key = count << 32 | (INT32_MAX - root): the largest key is the most
     // frequent root, the smaller one on a tie
-    uint64_t key = 0;
-    for (int j = threadIdx.x; j < kGiantSamples; j += kBlock) {
-        uint32_t c = 0;
-        for (int i = 0; i < kGiantSamples; ++i) c += smp[i] == smp[j] ? 1u : 0u;
-        const uint64_t k = (uint64_t)c << 32 | (uint32_t)(INT32_MAX - smp[j]);
-        key = k > key ? k : key;
-    }
+    const int32_t mine = smp[j];
+    uint32_t c = 0;
+    for (int i = 0; i < kGiantSamples; ++i) c += smp[i] == mine ? 1u : 0u;
+    uint64_t key = (uint64_t)c << 32 | (uint32_t)(INT32_MAX - mine);
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) {
         const uint64_t o = __shfl_xor(key, off, kWave);
         key = o > key ? o : key;
     }
-    if (lane_id() == 0) best[threadIdx.x / kWave] = key;
+    if (lane_id() == 0) best[j / kWave] = key;
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (j == 0) {
         uint64_t b = best[0];
-        for (int w = 1; w < kWaves; ++w) b = best[w] > b ? best[w] : b;
+        for (int w = 1; w < kGiantSamples / kWave; ++w) b = best[w] > b ? best[w] : b;
         st->giant = INT32_MAX - (int32_t)(uint32_t)b;
     }
 }
@@ -856,7 +864,7 @@ extern "C" int pr_wcc(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* 
             PR_LAUNCHED("wcc compress");
         }
         if (in_rp) {
-            k_wcc_giant<<<1, kBlock, 0, stream>>>(label, n, w.st);
+            k_wcc_giant<<<1, kGiantSamples, 0, stream>>>(label, n, w.st);
             PR_LAUNCHED("wcc giant");
         }
         a.skip = kSampledEdges;
@@ -875,7 +883,9 @@ extern "C" int pr_wcc(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* 
             PR_LAUNCHED("wcc in-hubs");
         }
     }
-    k_wcc_compress<<<vg, kBlock, 0, stream>>>(label, n, w.st, 1);
+    // the counting pass adds one value per workgroup to a single counter:
+    // keep the workgroups few
+    k_wcc_compress<<<std::min(vg, 512u), kBlock, 0, stream>>>(label, n, w.st, 1);
     PR_LAUNCHED("wcc compress");
     if (n_components_host) {
         uint32_t c = 0;
