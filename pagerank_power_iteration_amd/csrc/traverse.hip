@@ -47,10 +47,13 @@
 // smaller than its child, so every tree's root is its smallest vertex; once
 // every edge's ends share a tree, each component is one tree and pointing
 // every vertex at its root gives the smallest id of the component.  The
-// order follows Afforest (Sutton, Ben-Nun and Barak, IPDPS 2018): first each
-// vertex's first and second out-edges, each round followed by compression;
-// then the root most of 1024 sampled vertices share (the giant component) is
-// found, and the full pass skips every vertex already in its tree.  Skipping
+// order follows Afforest (Sutton, Ben-Nun and Barak, IPDPS 2018): first one
+// neighbour per vertex (its first out-edge; with the in-edge CSR, the smaller
+// of its first out- and in-neighbour, linked without an atomic because each
+// vertex writes only its own link), then its second out-edge, each round
+// followed by compression; then the root most of 1024 sampled vertices share
+// (the giant component) is found, and the full pass skips every vertex
+// already in its tree.  Skipping
 // a vertex's out-edges is only safe when its in-edges are seen from the
 // other side, so without the in-edge CSR no vertex is skipped.
 #include <algorithm>
@@ -64,7 +67,7 @@ constexpr int32_t kHubMin = 256;     // rows of at least this many edges go to t
 constexpr int32_t kHubChunk = 2048;  // edges per hub chunk: 8 per lane of a workgroup
 constexpr int kPerLane = 4;          // edges per lane per round
 constexpr int kRowGrid = 2048;       // workgroups of the row and hub kernels (8 per CU)
-constexpr int kFirstBatch = 4;       // BFS levels launched before the first frontier check
+constexpr int kFirstBatch = 8;       // BFS levels launched before the first frontier check
 constexpr int kMaxBatch = 64;
 constexpr int kTopDown = 0, kBottomUp = 1;
 constexpr uint64_t kAlpha = 14, kBeta = 24;  // direction-switch ratios
@@ -570,6 +573,24 @@ __global__ __launch_bounds__(kBlock) void k_wcc_init(int32_t* __restrict__ label
     }
 }
 
+// Point every vertex at the smaller of its first out-neighbour and its first
+// in-neighbour when that is below its own id.  Only the vertex's own lane
+// writes its link, so no atomic is needed; the links point to smaller ids,
+// so they form trees.  (Used with the in-edge CSR: the full pass then walks
+// every edge of the vertices outside the giant tree, these included.)
+__global__ __launch_bounds__(kBlock) void k_wcc_link_first(TravArgs a) {
+    for (int64_t u = blockIdx.x * (int64_t)kBlock + threadIdx.x; u < a.n;
+         u += (int64_t)gridDim.x * kBlock) {
+        int32_t s, len, is, ilen;
+        row_range(a.rp, a.nnz, (int32_t)u, s, len);
+        row_range(a.in_rp, a.nnz, (int32_t)u, is, ilen);
+        int32_t c = INT32_MAX;
+        if (len > 0) c = column(a, s);
+        if (ilen > 0) c = min(c, (int32_t)min((uint32_t)a.in_ci[min((uint32_t)is, a.nnz - 1u)], a.col_max));
+        if (c < (int32_t)u) a.out[u] = c;
+    }
+}
+
 // Link every vertex with its r-th out-neighbour (if it has one).
 __global__ __launch_bounds__(kBlock) void k_wcc_sample(TravArgs a, int32_t r) {
     for (int64_t u = blockIdx.x * (int64_t)kBlock + threadIdx.x; u < a.n;
@@ -857,8 +878,14 @@ extern "C" int pr_wcc(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* 
     PR_LAUNCHED("wcc init");
     TravArgs a = make_args(n, nnz, rp, ci, in_rp, in_ci, label, w);
     if (nnz > 0) {
-        for (int32_t r = 0; r < kSampledEdges; ++r) {
-            k_wcc_sample<<<vg, kBlock, 0, stream>>>(a, r);
+        // with the in-edge CSR one round already puts nearly every vertex of
+        // the giant component in its tree
+        const int32_t rounds = in_rp ? 1 : kSampledEdges;
+        for (int32_t r = 0; r < rounds; ++r) {
+            if (r == 0 && in_rp)
+                k_wcc_link_first<<<vg, kBlock, 0, stream>>>(a);
+            else
+                k_wcc_sample<<<vg, kBlock, 0, stream>>>(a, r);
             PR_LAUNCHED("wcc sample");
             k_wcc_compress<<<vg, kBlock, 0, stream>>>(label, n, w.st, 0);
             PR_LAUNCHED("wcc compress");
@@ -867,7 +894,12 @@ extern "C" int pr_wcc(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* 
             k_wcc_giant<<<1, kGiantSamples, 0, stream>>>(label, n, w.st);
             PR_LAUNCHED("wcc giant");
         }
-        a.skip = kSampledEdges;
+        // Without the in-edge CSR every vertex's out-row is walked, and the
+        // two sampled out-edges are already linked.  With it only the rows
+        // outside the giant tree are walked, each from its first edge (the
+        // first sampling round linked one edge per vertex, not necessarily
+        // an out-edge).
+        a.skip = in_rp ? 0 : kSampledEdges;
         k_wcc_rows<<<kRowGrid, kBlock, 0, stream>>>(a, 0);
         PR_LAUNCHED("wcc rows");
         k_wcc_hubs<<<kRowGrid, kBlock, 0, stream>>>(a, 0);
