@@ -458,88 +458,102 @@ __global__ __launch_bounds__(kBlock) void k_tile_first(const uint32_t* __restric
     }
 }
 
-// The tile edge arrays: sorted edge i (target targets[i], source sources[i])
-// is edge k = i - first[t] of its tile t and goes to slot
-// slot0[t] + block_slot(k).  Its block is narrow when the block's sources
-// (its first edge and its last real one; padding repeats the last) span less
-// than kNarrowSpan: the slot then holds (source - first source) | row << 16,
-// otherwise the source, with the row in tdst.  The block's first edge writes
-// its tblk word.
-__global__ __launch_bounds__(kBlock) void k_tile_edges(const int32_t* __restrict__ targets,
-                                                       const int32_t* __restrict__ sources,
-                                                       int64_t nnz, TileMap map,
-                                                       const int32_t* __restrict__ first,
-                                                       const int32_t* __restrict__ slot0,
-                                                       int32_t* __restrict__ tsrc,
-                                                       uint16_t* __restrict__ tdst,
-                                                       int32_t* __restrict__ tblk) {
-    GRID_STRIDE(i, nnz) {
-        const TileSpot at = tile_locate(map, targets[i]);
-        const int64_t f = first[at.tile];
-        const int64_t cnt = first[at.tile + 1] - f;
-        const int64_t k = i - f;
-        const int64_t kb = k & ~(int64_t)(kEdgeBlock - 1);
-        const int64_t kl = kb + kEdgeBlock - 1 < cnt ? kb + kEdgeBlock - 1 : cnt - 1;
-        const int32_t lo = sources[f + kb], hi = sources[f + kl];
+// The tile edge arrays, one kEdgeBlock-slot block at a time per wavefront.
+// Sorted edge f + k of tile t (f = first[t]; target targets[f + k], source
+// sources[f + k]) goes to slot slot0[t] + block_slot(k): lane l of the
+// wavefront holds edges k0 + 64 i + l (i = 0..3) of the block starting at k0
+// and writes its four slots 4 l .. 4 l + 3 with one 16-byte store.  Slots
+// past the tile's last edge are padding: the tile's last source and the
+// trash row.  A block is narrow when its sources (its first edge and its
+// last real one) span less than kNarrowSpan: its slots then hold
+// (source - first source) | row << 16 and tblk its first source, otherwise
+// the source, with the row in tdst and -1 in tblk.
+// The same pass counts, per kSectorChunk slots, the slots whose source's
+// 64-byte sector of contributions differs from the previous slot's (in edge
+// order; the previous slot of a tile's first is the previous tile's last),
+// into sector_counts (zeroed beforehand).
+// Each wavefront takes a contiguous range of blocks and finds each block's
+// tile by walking forward from the tile of its first block.
+__global__ __launch_bounds__(kBlock) void k_tile_blocks(const int32_t* __restrict__ targets,
+                                                        const int32_t* __restrict__ sources,
+                                                        TileMap map, const int32_t* __restrict__ first,
+                                                        const int32_t* __restrict__ slot0,
+                                                        int32_t tiles, int64_t n_blocks,
+                                                        int32_t* __restrict__ tsrc,
+                                                        uint16_t* __restrict__ tdst,
+                                                        int32_t* __restrict__ tblk,
+                                                        int32_t* __restrict__ sector_counts) {
+    const int lane = lane_id();
+    const int64_t waves = (int64_t)gridDim.x * kWaves;
+    const int64_t wave = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+    const int64_t per = (n_blocks + waves - 1) / waves;
+    int64_t b = wave * per;
+    const int64_t b_end = b + per < n_blocks ? b + per : n_blocks;
+    if (b >= b_end) return;
+    // last tile whose first slot is at or before this block (it is not empty)
+    int32_t t = 0;
+    {
+        int32_t lo = 0, hi = tiles - 1;
+        const int64_t slot = b * kEdgeBlock;
+        while (lo < hi) {
+            const int32_t mid = (lo + hi + 1) / 2;
+            if ((int64_t)slot0[mid] <= slot)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        t = lo;
+    }
+    for (; b < b_end; ++b) {
+        const int64_t slot = b * kEdgeBlock;
+        while ((int64_t)slot0[t + 1] <= slot) ++t;  // skips empty tiles
+        const int32_t k0 = (int32_t)(slot - slot0[t]);
+        const int32_t f = first[t];
+        const int32_t cnt = first[t + 1] - f;
+        int32_t src[4], row[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int32_t k = k0 + i * kWave + lane;
+            const bool real = k < cnt;
+            const int32_t e = f + (real ? k : cnt - 1);
+            src[i] = sources[e];
+            row[i] = real ? tile_locate(map, targets[e]).offset : kTrashRow;
+        }
+        const int32_t lo = sources[f + k0];
+        const int32_t hi = sources[f + (k0 + kEdgeBlock - 1 < cnt ? k0 + kEdgeBlock - 1 : cnt - 1)];
         const bool narrow = hi - lo < kNarrowSpan;
-        const int64_t q = slot0[at.tile] + block_slot(k);
-        const int32_t src = sources[i];
-        tsrc[q] = narrow ? (src - lo) | (at.offset << 16) : src;
-        if (!narrow) tdst[q] = (uint16_t)at.offset;
-        if (k == kb) tblk[(slot0[at.tile] + kb) / kEdgeBlock] = narrow ? lo : -1;
-    }
-}
-
-// Padding of each tile's last block: the tile's last source and the trash
-// row, in the block's form (a tile without edges has no slots).
-__global__ __launch_bounds__(kBlock) void k_tile_pad(int32_t tiles, const int32_t* __restrict__ first,
-                                                     const int32_t* __restrict__ sources,
-                                                     const int32_t* __restrict__ slot0,
-                                                     int32_t* __restrict__ tsrc,
-                                                     uint16_t* __restrict__ tdst) {
-    for (int32_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-        const int32_t count = first[t + 1] - first[t];
-        const int32_t padded = slot0[t + 1] - slot0[t];
-        if (padded == count) continue;
-        const int32_t kb = (count - 1) & ~(kEdgeBlock - 1);
-        const int32_t lo = sources[first[t] + kb], last = sources[first[t] + count - 1];
-        const bool narrow = last - lo < kNarrowSpan;
-        for (int32_t k = count + threadIdx.x; k < padded; k += kBlock) {
-            const int64_t q = slot0[t] + block_slot(k);
-            tsrc[q] = narrow ? (last - lo) | (kTrashRow << 16) : last;
-            if (!narrow) tdst[q] = (uint16_t)kTrashRow;
+        int4 w;
+        w.x = narrow ? (src[0] - lo) | (row[0] << 16) : src[0];
+        w.y = narrow ? (src[1] - lo) | (row[1] << 16) : src[1];
+        w.z = narrow ? (src[2] - lo) | (row[2] << 16) : src[2];
+        w.w = narrow ? (src[3] - lo) | (row[3] << 16) : src[3];
+        *reinterpret_cast<int4*>(tsrc + slot + 4 * lane) = w;
+        if (!narrow) {
+            ushort4 d;
+            d.x = (uint16_t)row[0];
+            d.y = (uint16_t)row[1];
+            d.z = (uint16_t)row[2];
+            d.w = (uint16_t)row[3];
+            *reinterpret_cast<ushort4*>(tdst + slot + 4 * lane) = d;
         }
-    }
-}
-
-// Sector starts per chunk of kSectorChunk slots, in edge order (edge k of
-// the layout sits at slot block_slot(k)): edge k starts a sector when k == 0
-// or its source's 64-byte sector of contributions differs from edge k-1's.
-// Inside a tile the sources do not decrease (padding repeats the last), so
-// this counts the distinct sectors a range of edges gathers (a tile boundary
-// may merge one sector with the previous tile's last: a count, not an exact
-// figure).
-__device__ __forceinline__ int32_t slot_source(const int32_t* __restrict__ tsrc,
-                                               const int32_t* __restrict__ tblk, int64_t i) {
-    const int32_t w = tsrc[block_slot(i)], b = tblk[i / kEdgeBlock];
-    return b >= 0 ? b + (w & (kNarrowSpan - 1)) : w;
-}
-
-__global__ __launch_bounds__(kBlock) void k_sector_counts(const int32_t* __restrict__ tsrc,
-                                                          const int32_t* __restrict__ tblk,
-                                                          int64_t slots, int32_t chunks,
-                                                          int32_t* __restrict__ counts) {
-    __shared__ int32_t red[kBlock / kWave];
-    for (int32_t c = blockIdx.x; c < chunks; c += gridDim.x) {
-        const int64_t lo = (int64_t)c * kSectorChunk;
-        const int64_t hi = lo + kSectorChunk < slots ? lo + kSectorChunk : slots;
-        int32_t k = 0;
-        for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock) {
-            const int32_t a = slot_source(tsrc, tblk, i) >> kSectorShift;
-            k += (i == 0 || a != (slot_source(tsrc, tblk, i - 1) >> kSectorShift)) ? 1 : 0;
+        if (lane == 0) tblk[b] = narrow ? lo : -1;
+        // sector starts: edge 64 i + l follows edge 64 i + l - 1 (lane l - 1,
+        // or lane 63 of round i - 1); edge 0 follows the slot before the block
+        int32_t before;
+        if (k0 > 0)
+            before = sources[f + (k0 - 1 < cnt ? k0 - 1 : cnt - 1)];
+        else
+            before = f > 0 ? sources[f - 1] : -1;
+        int32_t starts = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int32_t up = __shfl_up(src[i], 1, kWave);
+            const int32_t last_of_round = __shfl(src[i > 0 ? i - 1 : 0], kWave - 1, kWave);
+            const int32_t prev = lane > 0 ? up : (i > 0 ? last_of_round : before);
+            starts += (prev < 0 || (src[i] >> kSectorShift) != (prev >> kSectorShift)) ? 1 : 0;
         }
-        k = block_sum(k, red);
-        if (threadIdx.x == 0) counts[c] = k;
+        starts = wave_sum(starts);
+        if (lane == 0) atomicAdd(&sector_counts[slot / kSectorChunk], starts);
     }
 }
 
@@ -816,23 +830,19 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
     bt.n_slots = slots;
     PR_HIP_TRY(hipMemcpyAsync(w.tile_ptr, sp.data(), sizeof(int32_t) * sp.size(),
                               hipMemcpyHostToDevice, stream));
-    if (nnz > 0) {
-        k_tile_edges<<<grid_for(nnz, 8192), kBlock, 0, stream>>>(sorted_targets, s.order, nnz, map,
-                                                                 first, w.tile_ptr, w.tsrc, w.tdst,
-                                                                 w.tblk);
-        PR_LAUNCHED("tile edges");
-        k_tile_pad<<<dim3((unsigned)(tiles < 8192 ? tiles : 8192)), kBlock, 0, stream>>>(
-            tiles, first, s.order, w.tile_ptr, w.tsrc, w.tdst);
-        PR_LAUNCHED("tile padding");
-    }
-    // sector starts per chunk of slots (s.order is free again)
+    // tile slots and sector starts per chunk of slots (s.perm_ci, scratch of
+    // the sort, is free again and takes the counts)
     const int32_t chunks = (int32_t)ceil_div(slots, kSectorChunk);
     std::vector<int32_t> sc((size_t)chunks);
-    if (chunks > 0) {
-        k_sector_counts<<<grid_for((int64_t)chunks * kBlock, 8192), kBlock, 0, stream>>>(
-            w.tsrc, w.tblk, slots, chunks, s.order);
-        PR_LAUNCHED("sector counts");
-        PR_HIP_TRY(hipMemcpyAsync(sc.data(), s.order, sizeof(int32_t) * sc.size(),
+    if (nnz > 0) {
+        int32_t* counts = s.perm_ci;
+        PR_TRY(fill_u32(reinterpret_cast<uint32_t*>(counts), 0u, chunks, stream));
+        const int64_t n_blocks = slots / kEdgeBlock;
+        k_tile_blocks<<<grid_for(n_blocks * kWave, 2048), kBlock, 0, stream>>>(
+            sorted_targets, s.order, map, first, w.tile_ptr, tiles, n_blocks, w.tsrc, w.tdst,
+            w.tblk, counts);
+        PR_LAUNCHED("tile blocks");
+        PR_HIP_TRY(hipMemcpyAsync(sc.data(), counts, sizeof(int32_t) * sc.size(),
                                   hipMemcpyDeviceToHost, stream));
     }
     PR_HIP_TRY(hipStreamSynchronize(stream));
