@@ -474,6 +474,66 @@ __global__ __launch_bounds__(kBlock) void k_tile_first(const uint32_t* __restric
 // into sector_counts (zeroed beforehand).
 // Each wavefront takes a contiguous range of blocks and finds each block's
 // tile by walking forward from the tile of its first block.
+// One block's slots (see k_tile_blocks): loads first, then the writes.
+struct TileBlockIn {
+    int64_t slot;
+    int32_t k0, cnt;
+    int32_t src[4], row[4];
+    int32_t lo, hi, before;
+};
+
+__device__ __forceinline__ void tile_block_load(TileBlockIn& in, const int32_t* __restrict__ targets,
+                                                const int32_t* __restrict__ sources,
+                                                const TileMap& map, int32_t f, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int32_t k = in.k0 + i * kWave + lane;
+        const bool real = k < in.cnt;
+        const int32_t e = f + (real ? k : in.cnt - 1);
+        in.src[i] = sources[e];
+        in.row[i] = real ? tile_locate(map, targets[e]).offset : kTrashRow;
+    }
+    in.lo = sources[f + in.k0];
+    in.hi = sources[f + (in.k0 + kEdgeBlock - 1 < in.cnt ? in.k0 + kEdgeBlock - 1 : in.cnt - 1)];
+    // the slot before the block: the previous edge of the tile, or the last
+    // edge of the previous non-empty tile
+    in.before = in.k0 > 0 ? sources[f + in.k0 - 1] : (f > 0 ? sources[f - 1] : -1);
+}
+
+__device__ __forceinline__ void tile_block_store(const TileBlockIn& in, int32_t* __restrict__ tsrc,
+                                                 uint16_t* __restrict__ tdst,
+                                                 int32_t* __restrict__ tblk,
+                                                 int32_t* __restrict__ sector_counts, int lane) {
+    const bool narrow = in.hi - in.lo < kNarrowSpan;
+    int4 w;
+    w.x = narrow ? (in.src[0] - in.lo) | (in.row[0] << 16) : in.src[0];
+    w.y = narrow ? (in.src[1] - in.lo) | (in.row[1] << 16) : in.src[1];
+    w.z = narrow ? (in.src[2] - in.lo) | (in.row[2] << 16) : in.src[2];
+    w.w = narrow ? (in.src[3] - in.lo) | (in.row[3] << 16) : in.src[3];
+    *reinterpret_cast<int4*>(tsrc + in.slot + 4 * lane) = w;
+    if (!narrow) {
+        ushort4 d;
+        d.x = (uint16_t)in.row[0];
+        d.y = (uint16_t)in.row[1];
+        d.z = (uint16_t)in.row[2];
+        d.w = (uint16_t)in.row[3];
+        *reinterpret_cast<ushort4*>(tdst + in.slot + 4 * lane) = d;
+    }
+    if (lane == 0) tblk[in.slot / kEdgeBlock] = narrow ? in.lo : -1;
+    // sector starts: edge 64 i + l follows edge 64 i + l - 1 (lane l - 1, or
+    // lane 63 of round i - 1); edge 0 follows the slot before the block
+    int32_t starts = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int32_t up = __shfl_up(in.src[i], 1, kWave);
+        const int32_t last_of_round = __shfl(in.src[i > 0 ? i - 1 : 0], kWave - 1, kWave);
+        const int32_t prev = lane > 0 ? up : (i > 0 ? last_of_round : in.before);
+        starts += (prev < 0 || (in.src[i] >> kSectorShift) != (prev >> kSectorShift)) ? 1 : 0;
+    }
+    starts = wave_sum(starts);
+    if (lane == 0) atomicAdd(&sector_counts[in.slot / kSectorChunk], starts);
+}
+
 __global__ __launch_bounds__(kBlock) void k_tile_blocks(const int32_t* __restrict__ targets,
                                                         const int32_t* __restrict__ sources,
                                                         TileMap map, const int32_t* __restrict__ first,
@@ -504,56 +564,23 @@ __global__ __launch_bounds__(kBlock) void k_tile_blocks(const int32_t* __restric
         }
         t = lo;
     }
-    for (; b < b_end; ++b) {
-        const int64_t slot = b * kEdgeBlock;
-        while ((int64_t)slot0[t + 1] <= slot) ++t;  // skips empty tiles
-        const int32_t k0 = (int32_t)(slot - slot0[t]);
-        const int32_t f = first[t];
-        const int32_t cnt = first[t + 1] - f;
-        int32_t src[4], row[4];
+    // two blocks per step, all of their loads issued before either is written
+    for (; b < b_end; b += 2) {
+        TileBlockIn in[2];
+        int32_t f[2];
+        const int nb = b + 1 < b_end ? 2 : 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int32_t k = k0 + i * kWave + lane;
-            const bool real = k < cnt;
-            const int32_t e = f + (real ? k : cnt - 1);
-            src[i] = sources[e];
-            row[i] = real ? tile_locate(map, targets[e]).offset : kTrashRow;
+        for (int j = 0; j < 2; ++j) {
+            in[j].slot = (b + (j < nb ? j : 0)) * kEdgeBlock;
+            while ((int64_t)slot0[t + 1] <= in[j].slot) ++t;  // skips empty tiles
+            in[j].k0 = (int32_t)(in[j].slot - slot0[t]);
+            f[j] = first[t];
+            in[j].cnt = first[t + 1] - f[j];
         }
-        const int32_t lo = sources[f + k0];
-        const int32_t hi = sources[f + (k0 + kEdgeBlock - 1 < cnt ? k0 + kEdgeBlock - 1 : cnt - 1)];
-        const bool narrow = hi - lo < kNarrowSpan;
-        int4 w;
-        w.x = narrow ? (src[0] - lo) | (row[0] << 16) : src[0];
-        w.y = narrow ? (src[1] - lo) | (row[1] << 16) : src[1];
-        w.z = narrow ? (src[2] - lo) | (row[2] << 16) : src[2];
-        w.w = narrow ? (src[3] - lo) | (row[3] << 16) : src[3];
-        *reinterpret_cast<int4*>(tsrc + slot + 4 * lane) = w;
-        if (!narrow) {
-            ushort4 d;
-            d.x = (uint16_t)row[0];
-            d.y = (uint16_t)row[1];
-            d.z = (uint16_t)row[2];
-            d.w = (uint16_t)row[3];
-            *reinterpret_cast<ushort4*>(tdst + slot + 4 * lane) = d;
-        }
-        if (lane == 0) tblk[b] = narrow ? lo : -1;
-        // sector starts: edge 64 i + l follows edge 64 i + l - 1 (lane l - 1,
-        // or lane 63 of round i - 1); edge 0 follows the slot before the block
-        int32_t before;
-        if (k0 > 0)
-            before = sources[f + (k0 - 1 < cnt ? k0 - 1 : cnt - 1)];
-        else
-            before = f > 0 ? sources[f - 1] : -1;
-        int32_t starts = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int32_t up = __shfl_up(src[i], 1, kWave);
-            const int32_t last_of_round = __shfl(src[i > 0 ? i - 1 : 0], kWave - 1, kWave);
-            const int32_t prev = lane > 0 ? up : (i > 0 ? last_of_round : before);
-            starts += (prev < 0 || (src[i] >> kSectorShift) != (prev >> kSectorShift)) ? 1 : 0;
-        }
-        starts = wave_sum(starts);
-        if (lane == 0) atomicAdd(&sector_counts[slot / kSectorChunk], starts);
+        for (int j = 0; j < 2; ++j) tile_block_load(in[j], targets, sources, map, f[j], lane);
+        tile_block_store(in[0], tsrc, tdst, tblk, sector_counts, lane);
+        if (nb == 2) tile_block_store(in[1], tsrc, tdst, tblk, sector_counts, lane);
     }
 }
 
