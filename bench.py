@@ -347,6 +347,19 @@ def main() -> int:
     scratch = torch.empty(prx.pr_plan_scratch_bytes(n, m), dtype=torch.uint8, device="cuda")
     plan = prx.pr_plan_create(n, m, dg.row_ptr, dg.col_idx, ws_p, scratch, 0, stream)
     buckets = prx.pr_plan_buckets(plan)
+    # the convergence run of the same configuration: stop at the first
+    # iteration whose L1 distance is below 1e-6 (at most 200 iterations)
+    tol_l1 = torch.empty(200, dtype=torch.float32, device="cuda")
+    prx.pr_run(plan, 0.85, 1e-6, 200, x, tol_l1, None, 0, stream)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tol_it = prx.pr_run(plan, 0.85, 1e-6, 200, x, tol_l1, None, 0, stream)
+    torch.cuda.synchronize()
+    tol_ms = (time.perf_counter() - t0) * 1e3
+    tol_run = {"tol": 1e-6, "iterations": tol_it, "ms": round(tol_ms, 3),
+               "final_l1": float(tol_l1[tol_it - 1].item()),
+               "gteps": round(m * tol_it / (tol_ms * 1e-3) / 1e9, 2)}
+    log(f"tolerance run: {tol_run}")
     prx.pr_plan_destroy(plan)
     del scratch, ws_p
     torch.cuda.empty_cache()
@@ -404,6 +417,7 @@ def main() -> int:
                       "cv": round(iter_cv, 4), "algorithmic_bytes": bytes_iter,
                       "kernel_ms": round(kernel_ms, 5)},
         "transpose_ms": round(med["transpose"], 4),
+        "tol_run": tol_run,
         "plan_ms": round(med["plan"], 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -1,7 +1,7 @@
 // Internal helpers shared by the libpr translation units: status handling,
 // workspace carving, and the wavefront/workgroup primitives every kernel uses.
-// gfx950 runs 64-lane wavefronts; every kernel here is launched with 256-lane
-// workgroups (4 wavefronts).
+// gfx950 runs 64-lane wavefronts; kernels are launched with 256-lane
+// workgroups (4 wavefronts) unless their launch bounds say otherwise.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -95,10 +95,11 @@ __device__ __forceinline__ T wave_inclusive_scan(T v) {
     return v;
 }
 
-// Workgroup-wide exclusive scan of one value per lane; `scratch` holds at
-// least kWaves + 1 entries of LDS.  Returns the exclusive prefix and stores
-// the workgroup total in *total.  Contains barriers: call from every lane.
-template <class T>
+// Workgroup-wide exclusive scan of one value per lane, for workgroups of W
+// wavefronts; `scratch` holds at least W + 1 entries of LDS.  Returns the
+// exclusive prefix and stores the workgroup total in *total.  Contains
+// barriers: call from every lane.
+template <class T, int W = kWaves>
 __device__ __forceinline__ T block_exclusive_scan(T v, T* total, T* scratch) {
     const int wave = threadIdx.x / kWave;
     T incl = wave_inclusive_scan(v);
@@ -106,30 +107,30 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* total, T* scratch) {
     __syncthreads();
     if (threadIdx.x == 0) {
         T run = 0;
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < W; ++w) {
             T c = scratch[w];
             scratch[w] = run;
             run += c;
         }
-        scratch[kWaves] = run;
+        scratch[W] = run;
     }
     __syncthreads();
     T out = scratch[wave] + incl - v;
-    *total = scratch[kWaves];
+    *total = scratch[W];
     __syncthreads();
     return out;
 }
 
-// Workgroup sum; the result is valid in every lane.  `scratch` holds at least
-// kWaves entries of LDS.  Contains barriers.
-template <class T>
+// Workgroup sum for workgroups of W wavefronts; the result is valid in every
+// lane.  `scratch` holds at least W entries of LDS.  Contains barriers.
+template <class T, int W = kWaves>
 __device__ __forceinline__ T block_sum(T v, T* scratch) {
     v = wave_sum(v);
     if (lane_id() == 0) scratch[threadIdx.x / kWave] = v;
     __syncthreads();
     T r = scratch[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r += scratch[w];
+    for (int w = 1; w < W; ++w) r += scratch[w];
     __syncthreads();
     return r;
 }

@@ -74,7 +74,10 @@ constexpr uint64_t kAlpha = 14, kBeta = 24;  // direction-switch ratios
 constexpr int32_t kSampledEdges = 2;         // WCC: out-edges linked before the full pass
 constexpr int kGiantSamples = 1024;
 constexpr uint32_t kQueueBuf = 512;
-constexpr int32_t kProbe = 4;  // in-edges each lane checks itself before a bottom-up walk  // LDS entries per wavefront staging claimed vertices
+constexpr int32_t kProbe = 4;  // in-edges each lane checks itself before a bottom-up walk
+constexpr int kSmallBlock = 1024;             // lanes of the small-frontier kernel
+constexpr int32_t kSmallCap = 2048;           // frontier vertices it keeps in LDS
+constexpr uint64_t kSmallEdges = 65536;       // frontier out-edges it takes per level  // LDS entries per wavefront staging claimed vertices
 static_assert(kHubChunk % (kBlock * kPerLane) == 0, "a hub chunk is whole rounds");
 static_assert(kGiantSamples <= 1024 && kGiantSamples % kWave == 0, "one sample per lane");
 
@@ -93,7 +96,7 @@ struct TravState {
     unsigned long long explored[2];  // BFS: out-degree sum of the levels below L, by L mod 2
     int32_t mode[2];                 // BFS: direction of level L, by L mod 2
     int32_t giant;                   // WCC: the root the full pass skips (-1: none)
-    int32_t pad;
+    int32_t small_next;              // BFS: the level a small-frontier run stopped at
 };
 
 struct TravArgs {
@@ -560,6 +563,107 @@ __global__ __launch_bounds__(kBlock) void k_bfs_hubs(TravArgs a) {
     }
 }
 
+// Small frontiers, level after level in one launch of one workgroup (the
+// grid-wide kernels pay two launches per level, which is all a search of
+// thousands of narrow levels costs).  Entered at level a.level with the
+// frontier in a.queue (at most kSmallCap vertices, at most kSmallEdges
+// out-edges).  Each level: the frontier's rows and the prefix sums of their
+// lengths sit in LDS; every lane takes edges j, j + 1024, ... of their
+// concatenation, finds its row by binary search, and claims the target with
+// a compare-and-swap on its level; claimed vertices get LDS slots from an
+// LDS counter and are also written to the global queue of their level.  It
+// stops after a level whose frontier is empty, or larger than it takes, and
+// leaves the state as the grid-wide kernels of the next level expect it
+// (counts of that level, the counters it appends to cleared, the queue in
+// place), with that level in small_next.
+__global__ __launch_bounds__(kSmallBlock) void k_bfs_small(TravArgs a, int32_t* q0, int32_t* q1) {
+    __shared__ int32_t fv[2][kSmallCap];  // frontier vertices
+    __shared__ int32_t fs[2][kSmallCap];  // their first out-edges
+    __shared__ int32_t fl[2][kSmallCap];  // their out-degrees
+    __shared__ int32_t pre[kSmallCap + 1];
+    __shared__ uint32_t claimed;
+    __shared__ uint64_t red[kSmallBlock / kWave];
+    __shared__ uint32_t scan_tmp[kSmallBlock / kWave + 1];
+    TravState* st = a.st;
+    int32_t* level = a.out;
+    const int tid = threadIdx.x;
+    int L = a.level;
+    int cur = 0;
+    uint32_t F = st->front[L % 3];
+    uint64_t M = st->mf[L % 3];
+    for (uint32_t i = tid; i < F; i += kSmallBlock) {
+        const int32_t v = (L % 2 ? q1 : q0)[i];
+        int32_t s0, len;
+        row_range(a.rp, a.nnz, v, s0, len);
+        fv[0][i] = v;
+        fs[0][i] = s0;
+        fl[0][i] = len;
+    }
+    while (true) {
+        // level L: prefix sums of the frontier's row lengths (two per lane)
+        __syncthreads();
+        const uint32_t i0 = 2 * tid, i1 = 2 * tid + 1;
+        const uint32_t l0 = i0 < F ? (uint32_t)fl[cur][i0] : 0u;
+        const uint32_t l1 = i1 < F ? (uint32_t)fl[cur][i1] : 0u;
+        uint32_t total;
+        const uint32_t ex =
+            block_exclusive_scan<uint32_t, kSmallBlock / kWave>(l0 + l1, &total, scan_tmp);
+        if (i0 <= F) pre[i0] = (int32_t)ex;
+        if (i1 <= F) pre[i1] = (int32_t)(ex + l0);
+        if (tid == 0) claimed = 0;
+        __syncthreads();
+        int32_t* next_q = (L + 1) % 2 ? q1 : q0;
+        const int nxt = cur ^ 1;
+        uint64_t edges = 0;
+        for (uint32_t j = tid; j < total; j += kSmallBlock) {
+            int32_t lo = 0, hi = (int32_t)F - 1;  // last row with pre[row] <= j
+            while (lo < hi) {
+                const int32_t mid = (lo + hi + 1) / 2;
+                if ((uint32_t)pre[mid] <= j)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            const int32_t v = column(a, fs[cur][lo] + (int32_t)(j - (uint32_t)pre[lo]));
+            if (atomicCAS(&level[v], -1, L + 1) == -1) {
+                const uint32_t pos = atomicAdd(&claimed, 1u);
+                next_q[pos] = v;  // each vertex is claimed once: pos < n
+                int32_t s0, len;
+                row_range(a.rp, a.nnz, v, s0, len);
+                edges += (uint64_t)len;
+                if (pos < (uint32_t)kSmallCap) {
+                    fv[nxt][pos] = v;
+                    fs[nxt][pos] = s0;
+                    fl[nxt][pos] = len;
+                }
+            }
+        }
+        // (the sum's barriers also publish `claimed`)
+        const uint64_t M_next = block_sum<uint64_t, kSmallBlock / kWave>(edges, red);
+        const uint32_t F_next = claimed;
+        if (tid == 0) {
+            st->depth = L;
+            st->mode[L % 2] = kTopDown;
+            st->explored[(L + 1) % 2] = st->explored[L % 2] + M;
+        }
+        ++L;
+        if (F_next == 0 || F_next > (uint32_t)kSmallCap || M_next > kSmallEdges) {
+            if (tid == 0) {
+                st->front[L % 3] = F_next;
+                st->mf[L % 3] = M_next;
+                st->front[(L + 1) % 3] = 0;
+                st->mf[(L + 1) % 3] = 0;
+                st->chunks[L % 2] = 0;
+                st->small_next = L;
+            }
+            return;
+        }
+        F = F_next;
+        M = M_next;
+        cur = nxt;
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void k_wcc_init(int32_t* __restrict__ label, int32_t n,
                                                      TravState* __restrict__ st) {
     for (int64_t v = blockIdx.x * (int64_t)kBlock + threadIdx.x; v < n;
@@ -835,10 +939,27 @@ extern "C" int pr_bfs(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* 
     k_bfs_init<<<vertex_grid(n), kBlock, 0, stream>>>(a, source);
     PR_LAUNCHED("bfs init");
     TravState h{};
+    auto read_state = [&]() -> int {
+        PR_HIP_TRY(hipMemcpyAsync(&h, w.st, sizeof h, hipMemcpyDeviceToHost, stream));
+        PR_HIP_TRY(hipStreamSynchronize(stream));
+        return PR_OK;
+    };
+    PR_TRY(read_state());
     int32_t L = 0;
     int batch = kFirstBatch;
     // A frontier holds at least one vertex, so at most n levels are non-empty.
-    while (L <= n) {
+    while (L <= n && h.front[L % 3] != 0) {
+        a.level = L;
+        a.queue = w.queue[L % 2];
+        a.next = w.queue[(L + 1) % 2];
+        if (h.front[L % 3] <= (uint32_t)kSmallCap && h.mf[L % 3] <= kSmallEdges) {
+            // narrow levels: one launch runs them until the frontier grows
+            k_bfs_small<<<1, kSmallBlock, 0, stream>>>(a, w.queue[0], w.queue[1]);
+            PR_LAUNCHED("bfs small levels");
+            PR_TRY(read_state());
+            L = h.small_next;
+            continue;
+        }
         for (int k = 0; k < batch; ++k, ++L) {
             a.level = L;
             a.queue = w.queue[L % 2];
@@ -848,9 +969,7 @@ extern "C" int pr_bfs(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* 
             k_bfs_hubs<<<kRowGrid, kBlock, 0, stream>>>(a);
             PR_LAUNCHED("bfs hubs");
         }
-        PR_HIP_TRY(hipMemcpyAsync(&h, w.st, sizeof h, hipMemcpyDeviceToHost, stream));
-        PR_HIP_TRY(hipStreamSynchronize(stream));
-        if (h.front[L % 3] == 0) break;  // the frontier of level L is empty
+        PR_TRY(read_state());  // then h.front[L % 3]: the frontier of level L
         batch = std::min(batch * 2, kMaxBatch);
     }
     if (depth_host) *depth_host = h.depth;
