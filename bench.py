@@ -104,6 +104,16 @@ def cpu_traversal_baseline(g) -> dict:
             "cores": 1}
 
 
+def cpu_spmv_baseline(graphgen, nx: int) -> dict:
+    """The oracle's product loop on the same seeded stencil matrix as the
+    GPU leg, single-threaded."""
+    import oracle
+    A = graphgen.stencil_matrix(nx, values="random", seed=5)
+    x = graphgen.uniform(A.n_cols, 6)
+    _, secs = oracle.spmv(A.row_ptr, A.col_idx, A.vals, x, A.n_cols, timed=True)
+    return {"ms": round(secs * 1e3, 2), "gflops": round(2 * A.nnz / secs / 1e9, 3), "cores": 1}
+
+
 def cpu_baseline(g, iters: int) -> dict:
     import oracle
     r = oracle.pagerank(g.row_ptr, g.col_idx, d=0.85, tol=0.0, max_iter=iters)
@@ -394,6 +404,8 @@ def main() -> int:
         cpu = cpu_baseline(g, args.cpu_iters)
         if trav_graphs:
             cpu["traversal"] = {k: cpu_traversal_baseline(v) for k, v in trav_graphs.items()}
+        if args.spmv_grid > 0:
+            cpu["spmv"] = cpu_spmv_baseline(graphgen, args.spmv_grid)
 
     iter_cv = (statistics.pstdev(parts["iter"]) / statistics.mean(parts["iter"])
                if len(parts["iter"]) > 1 else 0.0)
