@@ -429,6 +429,12 @@ def main() -> int:
                       "cv": round(iter_cv, 4), "algorithmic_bytes": bytes_iter,
                       "kernel_ms": round(kernel_ms, 5)},
         "transpose_ms": round(med["transpose"], 4),
+        "transpose": {"ms": round(med["transpose"], 4),
+                      "algorithmic_bytes": 8 * m + 8 * (n + 1),
+                      "frac": round((8 * m + 8 * (n + 1)) / (med["transpose"] * 1e-3) / 1e9
+                                    / HBM_PEAK_GBPS, 4),
+                      "note": "bytes any transpose must move: read the out-edge CSR, write the "
+                              "in-edge CSR"},
         "tol_run": tol_run,
         "plan_ms": round(med["plan"], 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
