@@ -23,7 +23,10 @@
 //     workgroups: the page's block tier, without a tail behind one hub.
 // Both kernels read their work counts from device memory, so the host
 // launches BFS levels in growing batches and reads the frontier's size once
-// per batch.
+// per batch.  A run of narrow levels (a frontier of at most 2048 vertices and
+// 65,536 out-edges) runs instead in one launch of one workgroup, level after
+// level, until the frontier grows or empties: on a high-diameter graph the
+// two launches per level would be all the time spent.
 //
 // BFS direction.  A level is expanded top-down (the frontier's out-edges; a
 // vertex is claimed with a compare-and-swap on its level, as the page's
@@ -32,7 +35,8 @@
 // in-edges for a parent on the current level and sets its own level, with no
 // atomic on the level array.  The choice follows the direction-optimizing
 // rule of Beamer, Asanovic and Patterson (SC 2012), which the graph study
-// names as the remedy for shallow, skewed graphs: go bottom-up when the
+// mentions, beside CPU/GPU hybrids, as the known answer where its own tiers
+// lose to the CPU: go bottom-up when the
 // frontier's out-edges exceed 1/14 of the edges not yet explored, and back
 // top-down when the frontier holds fewer than n/24 vertices.  Every kernel of
 // a level evaluates the rule from counters the previous level left, so all
@@ -71,13 +75,13 @@ constexpr int kFirstBatch = 8;       // BFS levels launched before the first fro
 constexpr int kMaxBatch = 64;
 constexpr int kTopDown = 0, kBottomUp = 1;
 constexpr uint64_t kAlpha = 14, kBeta = 24;  // direction-switch ratios
-constexpr int32_t kSampledEdges = 2;         // WCC: out-edges linked before the full pass
-constexpr int kGiantSamples = 1024;
-constexpr uint32_t kQueueBuf = 512;
-constexpr int32_t kProbe = 4;  // in-edges each lane checks itself before a bottom-up walk
-constexpr int kSmallBlock = 1024;             // lanes of the small-frontier kernel
-constexpr int32_t kSmallCap = 2048;           // frontier vertices it keeps in LDS
-constexpr uint64_t kSmallEdges = 65536;       // frontier out-edges it takes per level  // LDS entries per wavefront staging claimed vertices
+constexpr int32_t kSampledEdges = 2;         // WCC without in-edges: out-edges linked first
+constexpr int kGiantSamples = 1024;          // WCC: vertices sampled for the giant root
+constexpr uint32_t kQueueBuf = 512;          // LDS entries per wavefront staging claimed vertices
+constexpr int32_t kProbe = 4;                // in-edges a lane checks itself before a bottom-up walk
+constexpr int kSmallBlock = 1024;            // lanes of the small-frontier kernel
+constexpr int32_t kSmallCap = 2048;          // frontier vertices it keeps in LDS
+constexpr uint64_t kSmallEdges = 65536;      // frontier out-edges it takes per level
 static_assert(kHubChunk % (kBlock * kPerLane) == 0, "a hub chunk is whole rounds");
 static_assert(kGiantSamples <= 1024 && kGiantSamples % kWave == 0, "one sample per lane");
 
