@@ -74,6 +74,7 @@ struct PlanWs {  // lives as long as the plan
     TileUnit* units;
     TileFix* fixes;
     int32_t* fix_rows;
+    int32_t* fix_win;  // [n / kFixBlock + 1] the cut tile holding each 256-row window's first row
     long long* partial;
     int64_t n_tiles_max, n_units_max, n_fixes_max, n_partial_max, n_edge_slots_max;
     size_t bytes;
@@ -132,6 +133,7 @@ PlanWs carve_ws(void* base, int32_t n, int64_t nnz, bool tiled) {
         w.units = c.take<TileUnit>((size_t)w.n_units_max);
         w.fixes = c.take<TileFix>((size_t)w.n_fixes_max);
         w.fix_rows = c.take<int32_t>((size_t)w.n_fixes_max + 1);
+        w.fix_win = c.take<int32_t>((size_t)ceil_div(n, kFixBlock) + 1);
         w.partial = c.take<long long>((size_t)w.n_partial_max);
     }
     w.bytes = c.used;
@@ -656,6 +658,7 @@ struct Built {
     std::vector<TileUnit> units;
     std::vector<TileFix> fixes;
     std::vector<int32_t> fix_rows;
+    std::vector<int32_t> fix_win;
 };
 
 // Bucketed pull: the plan's in-edge CSR (counting-sort transpose of the
@@ -972,6 +975,18 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
     bt.n_fixes = (int32_t)bt.fixes.size();
     bt.fix_rows.assign(1, 0);
     for (const TileFix& f : bt.fixes) bt.fix_rows.push_back(bt.fix_rows.back() + f.rows);
+    // for k_tilefix: the last cut tile whose rows start at or before row
+    // w * kFixBlock of the cut tiles' rows, for every window w
+    bt.fix_win.clear();
+    {
+        const int32_t total = bt.fix_rows.back();
+        int32_t i = 0;
+        for (int32_t g0 = 0; g0 < total; g0 += kFixBlock) {
+            while (i + 1 < bt.n_fixes && bt.fix_rows[(size_t)i + 1] <= g0) ++i;
+            bt.fix_win.push_back(i);
+        }
+        if (bt.fix_win.empty()) bt.fix_win.push_back(0);
+    }
     PR_HIP_TRY(hipMemcpyAsync(w.tiles, bt.tiles.data(), sizeof(Tile) * bt.tiles.size(),
                               hipMemcpyHostToDevice, stream));
     PR_HIP_TRY(hipMemcpyAsync(w.units, bt.units.data(), sizeof(TileUnit) * bt.units.size(),
@@ -980,6 +995,8 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
         PR_HIP_TRY(hipMemcpyAsync(w.fixes, bt.fixes.data(), sizeof(TileFix) * bt.fixes.size(),
                                   hipMemcpyHostToDevice, stream));
     PR_HIP_TRY(hipMemcpyAsync(w.fix_rows, bt.fix_rows.data(), sizeof(int32_t) * bt.fix_rows.size(),
+                              hipMemcpyHostToDevice, stream));
+    PR_HIP_TRY(hipMemcpyAsync(w.fix_win, bt.fix_win.data(), sizeof(int32_t) * bt.fix_win.size(),
                               hipMemcpyHostToDevice, stream));
     bt.tile_grid = (int32_t)(grid < bt.n_units ? grid : (bt.n_units > 0 ? bt.n_units : 1));
     return PR_OK;
@@ -1139,6 +1156,7 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     p->n_units = bt.n_units;
     p->fixes = w.fixes;
     p->fix_rows = w.fix_rows;
+    p->fix_win = w.fix_win;
     p->n_fixes = bt.n_fixes;
     p->n_fix_rows = bt.fix_rows.empty() ? 0 : bt.fix_rows.back();
     p->partial = w.partial;

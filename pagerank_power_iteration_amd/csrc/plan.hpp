@@ -248,6 +248,7 @@ struct pr_plan {
     int32_t n_units;
     const pr::TileFix* fixes;
     const int32_t* fix_rows;  // [n_fixes + 1] rows of the cut tiles before each one
+    const int32_t* fix_win;   // per 256-row window of those rows: the cut tile of its first row
     int32_t n_fixes;
     int32_t n_fix_rows;
     long long* partial;

@@ -695,6 +695,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
 struct TileFixArgs {
     const TileFix* __restrict__ fixes;
     const int32_t* __restrict__ fix_rows;
+    const int32_t* __restrict__ fix_win;
     const long long* __restrict__ partial;
     const float* __restrict__ inv_out;
     float* __restrict__ contrib_out;
@@ -713,34 +714,20 @@ struct TileFixArgs {
 // numbered one after another; fix_rows[i] is the number of rows before cut
 // tile i): the row adds its slots in unit order (exact integer sums) and
 // applies the update.  Lane g of workgroup b takes rows b*256 + g, then
-// + gridDim.x*256.  One lane finds the tile of the workgroup's first row by
-// binary search; the others step forward from it (a tile has at least 64
-// rows, so a 256-row window meets at most five tiles).
+// + gridDim.x*256.  The plan lists the cut tile of every 256-row window's
+// first row (fix_win); each lane steps forward from it (a tile has at least
+// 64 rows, so a window meets at most five tiles).
 __global__ __launch_bounds__(kFixBlock) void k_tilefix(TileFixArgs f) {
     __shared__ float red[3][kFixBlock / kWave];
-    __shared__ int32_t s_fix;
     RunState* st = f.state;
     if (st->stop) return;
     const Damp k = make_damp(f.d, f.n, st->dmass);
     const double unit = st->fx_unit;
     Acc sums;
     for (int32_t g0 = blockIdx.x * kFixBlock; g0 < f.n_rows; g0 += gridDim.x * kFixBlock) {
-        __syncthreads();  // s_fix of the previous window has been read
-        if (threadIdx.x == 0) {
-            int32_t lo = 0, hi = f.n_fixes - 1;  // last fix with fix_rows[i] <= g0
-            while (lo < hi) {
-                const int32_t mid = (lo + hi + 1) / 2;
-                if (f.fix_rows[mid] <= g0)
-                    lo = mid;
-                else
-                    hi = mid - 1;
-            }
-            s_fix = lo;
-        }
-        __syncthreads();
         const int32_t g = g0 + threadIdx.x;
         if (g < f.n_rows) {
-            int32_t i = s_fix;
+            int32_t i = f.fix_win[g0 / kFixBlock];
             while (i + 1 < f.n_fixes && f.fix_rows[i + 1] <= g) ++i;
             const TileFix fx = f.fixes[i];
             const int32_t r = g - f.fix_rows[i];
@@ -975,6 +962,7 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     TileFixArgs tf{};
     tf.fixes = p->fixes;
     tf.fix_rows = p->fix_rows;
+    tf.fix_win = p->fix_win;
     tf.n_rows = p->n_fix_rows;
     tf.partial = p->partial;
     tf.inv_out = p->inv_out;
