@@ -157,10 +157,29 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, in
         const int64_t i = base + r * kBlock + threadIdx.x;
         k[r] = radix_load(in, i < in.count ? i : last);
     }
+    // Graph keys are skewed: many lanes of a round often hold digit 0 (the
+    // low ids of a power-law graph), and LDS adds to one address serialize.
+    // Digits below kRegDigits are counted in registers and added once per
+    // wavefront.
+    constexpr int kRegDigits = 4;
+    uint32_t reg[kRegDigits] = {};
 #pragma unroll
     for (int r = 0; r < kRadixItems; ++r) {
         const int64_t i = base + r * kBlock + threadIdx.x;
-        if (i < in.count) atomicAdd(&h[radix_digit<MODE>(in, radix_check<MODE>(in, k[r]), shift)], 1u);
+        if (i < in.count) {
+            const uint32_t dg = radix_digit<MODE>(in, radix_check<MODE>(in, k[r]), shift);
+            if (dg < (uint32_t)kRegDigits) {
+#pragma unroll
+                for (int j = 0; j < kRegDigits; ++j) reg[j] += dg == (uint32_t)j ? 1u : 0u;
+            } else {
+                atomicAdd(&h[dg], 1u);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kRegDigits; ++j) {
+        const uint32_t c = wave_sum(reg[j]);
+        if (lane_id() == 0 && c) atomicAdd(&h[j], c);
     }
     __syncthreads();
     hist[(int64_t)threadIdx.x * T + blockIdx.x] = h[threadIdx.x];
