@@ -352,8 +352,8 @@ __global__ __launch_bounds__(kBlock) void k_order(const int32_t* __restrict__ ol
 
 // Out-edge CSR in plan order: row p of the result is row old_of[p] of the
 // input with every target renumbered.  Edge-parallel: each workgroup covers
-// kBlock * kPermItems positions.  The rows that own them, [s_lo, s_hi], are
-// found once; when there are at most kPermRows of them their output and
+// kBlock * kPermItems positions.  The rows that own them, [lo, hi], are
+// found once, by the whole workgroup; when there are at most kPermRows of them their output and
 // input starts are staged in LDS and each position finds its row there, so
 // a lane's loads of out_ci and then of new_id go out together for all its
 // positions.  (A window over a long run of empty rows searches perm_rp in
@@ -371,15 +371,11 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
                                                          int32_t* __restrict__ src_of) {
     __shared__ int32_t s_dst[kPermRows + 1];  // perm_rp of the window's rows
     __shared__ int32_t s_src[kPermRows];      // out_rp[old_of[row]]
-    __shared__ int32_t s_lo, s_hi;
     const int64_t base = blockIdx.x * (int64_t)kPermRows;
     const int64_t last = (base + kPermRows < nnz ? base + kPermRows : nnz) - 1;
-    if (threadIdx.x == 0) {
-        s_lo = owner_row(perm_rp, base, 0, n - 1);
-        s_hi = owner_row(perm_rp, last, s_lo, n - 1);
-    }
-    __syncthreads();
-    const int32_t lo = s_lo, hi = s_hi;
+    int32_t lo, hi;
+    block_owner_rows(perm_rp, base, last, n, (uint32_t*)s_src, lo, hi);
+    __syncthreads();  // s_src held the search's counts
     const bool staged = hi - lo + 1 <= kPermRows;
     if (staged) {
         for (int32_t r = threadIdx.x; r <= hi - lo; r += kBlock) {

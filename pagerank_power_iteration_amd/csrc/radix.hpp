@@ -99,6 +99,47 @@ __device__ __forceinline__ int32_t owner_row(const int32_t* __restrict__ rp, int
     return lo;
 }
 
+// The owners of edges e0 <= e1 (largest r in [0, n-1] with row_ptr[r] <= e),
+// found by the whole workgroup at once.  Each half of the workgroup searches
+// for one of them; every round each of its lanes probes one row of the
+// half's interval, the rows evenly spaced, and the count of probes at or
+// below the edge picks the sub-interval: 2^23 rows take four rounds of
+// parallel loads instead of 23 dependent ones.  Assumes row_ptr[0] <= e0
+// (the first probe counts as a hit); with a malformed row_ptr the intervals
+// still shrink every round and stay inside [0, n-1].  `cnt` is 2 * kWaves
+// words of LDS.  Contains barriers: call from every lane; every lane
+// receives both rows.
+__device__ __forceinline__ void block_owner_rows(const int32_t* __restrict__ rp, int64_t e0,
+                                                 int64_t e1, int32_t n, uint32_t* cnt,
+                                                 int32_t& r0, int32_t& r1) {
+    constexpr int kProbes = kBlock / 2;
+    const int half = threadIdx.x / kProbes, k = threadIdx.x % kProbes, wave = threadIdx.x / kWave;
+    const int64_t e = half ? e1 : e0;
+    int32_t lo[2] = {0, 0}, hi[2] = {n - 1, n - 1};
+    for (int round = 0; hi[0] > lo[0] || hi[1] > lo[1]; ++round) {
+        const int32_t step[2] = {(hi[0] - lo[0]) / kProbes + 1, (hi[1] - lo[1]) / kProbes + 1};
+        const int64_t r = lo[half] + (int64_t)k * step[half];
+        const bool hit = k == 0 || (r <= hi[half] && (int64_t)rp[r] <= e);
+        const uint64_t votes = __ballot(hit);
+        uint32_t* c = cnt + (round & 1) * kWaves;  // alternate slots: one barrier a round
+        if (lane_id() == 0) c[wave] = (uint32_t)__popcll(votes);
+        __syncthreads();
+        constexpr int kHalfWaves = kWaves / 2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t hits = 0;
+#pragma unroll
+            for (int w = 0; w < kHalfWaves; ++w) hits += c[h * kHalfWaves + w];
+            const int64_t nlo = lo[h] + (int64_t)(hits - 1) * step[h];
+            const int64_t nhi = nlo + step[h] - 1;
+            lo[h] = (int32_t)nlo;
+            hi[h] = (int32_t)(nhi < hi[h] ? nhi : hi[h]);
+        }
+    }
+    r0 = lo[0];
+    r1 = lo[1];
+}
+
 // The key of element i as stored (no checks).
 __device__ __forceinline__ int32_t radix_load(const RadixIn& in, int64_t i) { return in.keys[i]; }
 
@@ -185,6 +226,61 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, in
     hist[(int64_t)threadIdx.x * T + blockIdx.x] = h[threadIdx.x];
 }
 
+// Workgroups are dealt to the eight XCDs in turn (workgroup b to XCD b mod 8)
+// and every XCD has an L2 of its own.  Tiles t and t + 1 write neighbouring
+// pieces of each digit's output run, often parts of one cache line, so the
+// scatter gives each XCD a contiguous range of tiles, taken in order: the
+// pieces of a line then meet in one L2 instead of leaving two partial lines.
+// A bijection of [0, T): XCD x gets floor(T / 8) tiles, plus one if x < T mod 8.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
+    const int64_t x = b % kXcds, j = b / kXcds, q = T / kXcds, r = T % kXcds;
+    return x * q + (x < r ? x : r) + j;
+}
+
+// Owner rows of a first-pass tile, when the rows it touches are at most
+// kRadixTile: own[i] = the row of edge base + i, for i < count.  Each row
+// that starts inside the tile marks its first slot (of rows that start at
+// the same slot, the last one wins: the others are empty), and an inclusive
+// max-scan carries the marks forward; slot 0 belongs to `lo`, the owner of
+// the tile's first edge.  Contains barriers: call from every lane.
+__device__ __forceinline__ void stage_owner_rows(const int32_t* __restrict__ rp, int64_t base,
+                                                 int count, int32_t lo, int32_t hi, int32_t* own,
+                                                 int32_t* wave_max) {
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    for (int i = tid; i < count; i += kBlock) own[i] = i == 0 ? lo : -1;
+    __syncthreads();
+    for (int32_t r = lo + 1 + tid; r <= hi; r += kBlock) {
+        const int64_t p = (int64_t)rp[r] - base;
+        if (p > 0 && p < count) atomicMax(&own[p], r);  // in range for a valid row_ptr
+    }
+    __syncthreads();
+    // wavefront w scans slots [w * 1024, (w + 1) * 1024) in rounds of 64
+    constexpr int kSpan = kRadixTile / kWaves;
+    int32_t carry = -1;
+    for (int r = 0; r < kSpan / kWave; ++r) {
+        const int i = wave * kSpan + r * kWave + lane;
+        int32_t v = i < count ? own[i] : -1;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int32_t t = __shfl_up(v, off, kWave);
+            if (lane >= off) v = v > t ? v : t;
+        }
+        v = v > carry ? v : carry;
+        if (i < count) own[i] = v;
+        carry = __shfl(v, kWave - 1, kWave);
+    }
+    if (lane == 0) wave_max[wave] = carry;
+    __syncthreads();
+    int32_t before = -1;
+    for (int w = 0; w < wave; ++w) before = before > wave_max[w] ? before : wave_max[w];
+    for (int r = 0; r < kSpan / kWave; ++r) {
+        const int i = wave * kSpan + r * kWave + lane;
+        if (i < count && own[i] < before) own[i] = before;
+    }
+    __syncthreads();
+}
+
 // Stable scatter.  `scanned` is the exclusive scan of the digit-major
 // histogram.  Keys are written only when keys_out is not null; values are
 // carried only when VALS.
@@ -199,20 +295,25 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
     __shared__ int32_t s_key[kRadixTile];
     __shared__ int32_t s_val[kRadixTile];
     __shared__ uint32_t scan_tmp[kWaves + 1];
-    __shared__ int32_t s_row_lo, s_row_hi;
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-    const int64_t tile = blockIdx.x;
+    const int64_t tile = xcd_tile(blockIdx.x, T);
     const int64_t base = tile * kRadixTile;
     const int count = (int)((in.count - base) < kRadixTile ? (in.count - base) : kRadixTile);
 
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) wave_count[w][tid] = 0;
-    if (MODE == kFromOutCsr && tid == 0) {
-        s_row_lo = owner_row(in.row_ptr, base, 0, in.n - 1);
-        s_row_hi = owner_row(in.row_ptr, base + count - 1, s_row_lo, in.n - 1);
-    }
+    // First pass: the rows that own the tile's edges, [row_lo, row_hi].  Their
+    // owner rows come from LDS when there are few enough of them (a tile
+    // inside a long run of empty rows searches row_ptr per edge instead).
+    // s_val is free until the reorder below.
+    int32_t row_lo = 0, row_hi = 0;
+    if (MODE == kFromOutCsr)
+        block_owner_rows(in.row_ptr, base, base + count - 1, in.n, (uint32_t*)s_key, row_lo, row_hi);
     __syncthreads();
+    const bool staged_rows = MODE == kFromOutCsr && VALS && row_hi - row_lo < kRadixTile;
+    if (staged_rows)
+        stage_owner_rows(in.row_ptr, base, count, row_lo, row_hi, s_val, (int32_t*)scan_tmp);
 
     int32_t key[kRadixItems], val[kRadixItems];
     uint32_t rank[kRadixItems];
@@ -237,7 +338,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
             if (!VALS)
                 v = 0;
             else if (MODE == kFromOutCsr)
-                v = owner_row(in.row_ptr, g, s_row_lo, s_row_hi);
+                v = staged_rows ? s_val[idx] : owner_row(in.row_ptr, g, row_lo, row_hi);
             else if (kLoadVals)
                 v = val[r];
             else

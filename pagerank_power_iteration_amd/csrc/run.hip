@@ -385,7 +385,7 @@ constexpr int kFinalWaves = kFinalBlock / kWave;
 constexpr int kTileBlock = PR_TILE_BLOCK;
 constexpr int kTileWaves = kTileBlock / kWave;
 #ifndef PR_TILE_Q
-#define PR_TILE_Q 1
+#define PR_TILE_Q 2
 #endif
 constexpr int kTileQ = PR_TILE_Q;  // edge blocks per wavefront per round
 

@@ -38,15 +38,38 @@ namespace {
 
 // in_rp[v] = first i with keys[i] >= v, for v in [0, n]; keys sorted.  Element
 // i writes the vertices in (keys[i-1], keys[i]] (with keys[-1] = -1 and
-// keys[m] = n), so every v is written exactly once.
+// keys[m] = n), so every v is written exactly once.  A lane takes kRowsRun
+// consecutive elements with two 16-byte loads (keys is 256-byte aligned
+// scratch) plus the key before them, so a wavefront keeps 2 KiB of reads in
+// flight; the lane holding the end of the array takes its elements one by
+// one.
+constexpr int kRowsRun = 8;
+
 __global__ __launch_bounds__(kBlock) void k_rows_from_sorted(const int32_t* __restrict__ keys,
                                                              int64_t m, int32_t n,
                                                              int32_t* __restrict__ in_rp) {
-    for (int64_t i = blockIdx.x * (int64_t)kBlock + threadIdx.x; i <= m;
-         i += (int64_t)gridDim.x * kBlock) {
-        const int32_t lo = (i == 0) ? 0 : keys[i - 1] + 1;
-        const int32_t hi = (i == m) ? n : keys[i];
-        for (int32_t v = lo; v <= hi; ++v) in_rp[v] = (int32_t)i;
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    const int64_t runs = m / kRowsRun + 1;  // the last run holds element m
+    for (int64_t c = blockIdx.x * (int64_t)kBlock + threadIdx.x; c < runs;
+         c += (int64_t)gridDim.x * kBlock) {
+        const int64_t i0 = c * kRowsRun;
+        int32_t prev = i0 == 0 ? -1 : keys[i0 - 1];
+        if (i0 + kRowsRun <= m) {
+            const i32x4 a = *(const i32x4*)(keys + i0);
+            const i32x4 b = *(const i32x4*)(keys + i0 + 4);
+            const int32_t k[kRowsRun] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int j = 0; j < kRowsRun; ++j) {
+                for (int32_t v = prev + 1; v <= k[j]; ++v) in_rp[v] = (int32_t)(i0 + j);
+                prev = k[j];
+            }
+        } else {
+            for (int64_t i = i0; i <= m; ++i) {
+                const int32_t hi = i == m ? n : keys[i];
+                for (int32_t v = prev + 1; v <= hi; ++v) in_rp[v] = (int32_t)i;
+                prev = hi;
+            }
+        }
     }
 }
 
@@ -88,14 +111,7 @@ int transpose_device(int32_t n, int64_t nnz, const int32_t* out_rp, const int32_
     in.error = w.error;
     int32_t* sorted_keys = nullptr;
     PR_TRY(radix_sort<kFromOutCsr>(in, vertex_bits(n), in_ci, w.sort, &sorted_keys, stream));
-    k_rows_from_sorted<<<grid_for(nnz + 1), kBlock, 0, stream>>>(sorted_keys, nnz, n, in_rp);
-    PR_LAUNCHED("row pointers");
-    return PR_OK;
-}
-
-int rows_from_sorted(const int32_t* keys, int64_t m, int32_t n, int32_t* rp, hipStream_t stream) {
-    if (m == 0) return fill_u32(reinterpret_cast<uint32_t*>(rp), 0u, (int64_t)n + 1, stream);
-    k_rows_from_sorted<<<grid_for(m + 1), kBlock, 0, stream>>>(keys, m, n, rp);
+    k_rows_from_sorted<<<grid_for(nnz / kRowsRun + 1), kBlock, 0, stream>>>(sorted_keys, nnz, n, in_rp);
     PR_LAUNCHED("row pointers");
     return PR_OK;
 }
@@ -110,7 +126,7 @@ int transpose_row_ptr(int32_t n, int64_t nnz, const int32_t* out_ci, int32_t* in
     in.error = w.error;
     int32_t* sorted_keys = nullptr;
     PR_TRY(radix_sort_keys<kFromTargets>(in, vertex_bits(n), w.sort, &sorted_keys, stream));
-    k_rows_from_sorted<<<grid_for(nnz + 1), kBlock, 0, stream>>>(sorted_keys, nnz, n, in_rp);
+    k_rows_from_sorted<<<grid_for(nnz / kRowsRun + 1), kBlock, 0, stream>>>(sorted_keys, nnz, n, in_rp);
     PR_LAUNCHED("row pointers");
     return PR_OK;
 }

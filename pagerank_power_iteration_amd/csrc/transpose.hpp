@@ -26,10 +26,6 @@ int transpose_device(int32_t n, int64_t nnz, const int32_t* out_rp, const int32_
 int transpose_row_ptr(int32_t n, int64_t nnz, const int32_t* out_ci, int32_t* in_rp,
                       const TransposeWs& ws, hipStream_t stream);
 
-// rp[v] = first position i with keys[i] >= v, for v in [0, n]; keys sorted,
-// each in [0, n).
-int rows_from_sorted(const int32_t* keys, int64_t m, int32_t n, int32_t* rp, hipStream_t stream);
-
 // Bits needed to hold every vertex id in [0, n).
 int vertex_bits(int32_t n);
 
