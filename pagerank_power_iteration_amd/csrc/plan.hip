@@ -34,7 +34,8 @@ namespace pr {
 namespace {
 
 // Work list entries of the in-degree count.
-constexpr int kMaxCountChunks = 1024;
+// (chunks hold at least nnz / 256 keys, so 256 buckets make at most 512)
+constexpr int kMaxCountChunks = 512;
 
 // Upper bounds of the tiled layout.
 inline int64_t max_tiles(int32_t n) { return n / kTileMinRows + kNumBuckets + 1; }
@@ -89,7 +90,7 @@ struct PlanScratch {  // needed only while pr_plan_create runs
     int32_t* src_of;     // [nnz] source (plan id) of each edge of perm_ci
     int32_t* order;      // [nnz] tiled: sources sorted by tile, then sector counts
     int32_t* tile_first; // [max_tiles + 1] tiled: first sorted edge of each tile
-    int32_t* count_chunks;  // [4 * kMaxCountChunks] in-degree counting work list
+    int32_t* count_chunks;  // [4 * kMaxCountChunks + 1] in-degree counting work list, its length last
     unsigned long long* stats;  // [2 * kNumBuckets]: rows, edges per bucket
     RadixWs vsort;       // sort of the n vertex keys (and scans over n)
     TransposeWs tr;
@@ -157,7 +158,7 @@ PlanScratch carve_scratch(void* base, int32_t n, int64_t nnz) {
     s.src_of = c.take<int32_t>((size_t)nnz);
     s.order = c.take<int32_t>((size_t)nnz);
     s.tile_first = c.take<int32_t>((size_t)max_tiles(n) + 1);
-    s.count_chunks = c.take<int32_t>((size_t)4 * kMaxCountChunks);
+    s.count_chunks = c.take<int32_t>((size_t)4 * kMaxCountChunks + 1);
     s.stats = c.take<unsigned long long>(2 * kNumBuckets);
     s.vsort = radix_carve(c, n);
     TransposeWs tw = transpose_carve(c.base ? c.base + c.used : nullptr, n, nnz);
@@ -198,26 +199,41 @@ struct CountChunk {
     int32_t split;  // 1: other chunks count the same bucket
 };
 
-// starts[d] = first position of digit d after the partition pass (the
-// digit-major scan of the histogram), starts[256] = the element count.
-__global__ __launch_bounds__(kBlock) void k_digit_starts(const uint32_t* __restrict__ scanned,
-                                                         int64_t T, uint32_t* __restrict__ starts) {
-    starts[threadIdx.x] = scanned[(int64_t)threadIdx.x * T];
-    if (threadIdx.x == 0) starts[kRadixDigits] = scanned[(int64_t)kRadixDigits * T];
+// The count's work list, from the partition pass's digit-major histogram
+// scan (digit d's keys start at scanned[d * T]; scanned[256 * T] = nnz): the
+// keys of bucket d cut into ceil(len / size) chunks of about equal length,
+// in bucket order.  One lane per bucket; the list's length goes to
+// chunks[4 * kMaxCountChunks].  With size >= nnz / 256 there are at most
+// 256 + nnz / size <= kMaxCountChunks chunks.
+__global__ __launch_bounds__(kBlock) void k_count_chunks(const uint32_t* __restrict__ scanned,
+                                                         int64_t T, int64_t size,
+                                                         int32_t* __restrict__ chunks) {
+    __shared__ uint32_t scan_tmp[kWaves + 1];
+    const int b = threadIdx.x;
+    const int64_t lo = scanned[(int64_t)b * T], len = (int64_t)scanned[(int64_t)(b + 1) * T] - lo;
+    const int64_t k = len > 0 ? (len + size - 1) / size : 0;
+    uint32_t total;
+    const uint32_t base = block_exclusive_scan((uint32_t)k, &total, scan_tmp);
+    CountChunk* list = reinterpret_cast<CountChunk*>(chunks);
+    for (int64_t j = 0; j < k; ++j)
+        list[base + j] = CountChunk{b, (int32_t)(lo + len * j / k), (int32_t)(lo + len * (j + 1) / k),
+                                    k > 1 ? 1 : 0};
+    if (b == 0) chunks[4 * kMaxCountChunks] = (int32_t)total;
 }
 
-__global__ __launch_bounds__(kCountBlock) void k_count_buckets(const int32_t* __restrict__ keys,
-                                                               const CountChunk* __restrict__ chunks,
+__global__ __launch_bounds__(kCountBlock) void k_count_buckets(const uint16_t* __restrict__ keys,
+                                                               const int32_t* __restrict__ chunks,
                                                                int shift, int32_t n,
                                                                uint32_t* __restrict__ counts) {
     __shared__ uint32_t cnt[kCountMaxSpan];
-    const CountChunk c = chunks[blockIdx.x];
+    if ((int32_t)blockIdx.x >= chunks[4 * kMaxCountChunks]) return;  // the grid covers the bound
+    const CountChunk c = reinterpret_cast<const CountChunk*>(chunks)[blockIdx.x];
     const int32_t span = 1 << shift;
     for (int32_t v = threadIdx.x; v < span; v += kCountBlock) cnt[v] = 0u;
     __syncthreads();
     const int64_t last = (int64_t)c.end - 1;
     for (int64_t i0 = c.begin + threadIdx.x; i0 < c.end; i0 += (int64_t)kCountBlock * kCountItems) {
-        int32_t k[kCountItems];
+        uint32_t k[kCountItems];
 #pragma unroll
         for (int j = 0; j < kCountItems; ++j) {  // loads first, clamped: they overlap
             const int64_t i = i0 + (int64_t)j * kCountBlock;
@@ -239,9 +255,9 @@ __global__ __launch_bounds__(kCountBlock) void k_count_buckets(const int32_t* __
 }
 
 // in_rp[0..n] of the transpose of (n, nnz, out_ci).  counts: n words of
-// scratch; chunks: 4 * kMaxCountChunks words; scan_ws: a scan workspace for n
-// items.  Out-of-range targets are clamped and flagged in tr.error.
-// Synchronizes `stream` (the bucket sizes are read back).
+// scratch; chunks: 4 * kMaxCountChunks + 1 words; scan_ws: a scan workspace
+// for n items.  Out-of-range targets are clamped and flagged in tr.error.
+// Asynchronous on `stream`.
 int indegree_row_ptr(int32_t n, int64_t nnz, const int32_t* out_ci, int32_t* in_rp,
                      uint32_t* counts, int32_t* chunks, void* scan_ws, const TransposeWs& tr,
                      hipStream_t stream) {
@@ -259,36 +275,20 @@ int indegree_row_ptr(int32_t n, int64_t nnz, const int32_t* out_ci, int32_t* in_
     k_radix_hist<kFromTargets><<<dim3((unsigned)T), kBlock, 0, stream>>>(in, shift, T, w.hist);
     PR_LAUNCHED("radix histogram");
     PR_TRY(scan_exclusive(w.hist, w.scanned, kRadixDigits * T, w.scan_ws, stream));
-    k_radix_scatter<kFromTargets, false><<<dim3((unsigned)T), kBlock, 0, stream>>>(
+    // the keys' low 16 bits are enough: a bucket spans at most 2^15 vertices
+    k_radix_scatter<kFromTargets, false, true><<<dim3((unsigned)T), kBlock, 0, stream>>>(
         in, shift, T, w.scanned, w.key[0], nullptr);
     PR_LAUNCHED("radix scatter");
-    uint32_t* starts_dev = reinterpret_cast<uint32_t*>(chunks);
-    k_digit_starts<<<1, kBlock, 0, stream>>>(w.scanned, T, starts_dev);
-    PR_LAUNCHED("digit starts");
-    uint32_t starts[kRadixDigits + 1];
-    PR_HIP_TRY(hipMemcpyAsync(starts, starts_dev, sizeof starts, hipMemcpyDeviceToHost, stream));
-    PR_HIP_TRY(hipStreamSynchronize(stream));
-    // chunks of at least max(nnz / 256, kMinCountChunk) keys: at most 512 of them
+    // chunks of at least max(nnz / 256, kMinCountChunk) keys, listed on the device
     int64_t size = ceil_div(nnz, kRadixDigits);
     if (size < kMinCountChunk) size = kMinCountChunk;
-    std::vector<CountChunk> list;
-    for (int b = 0; b < kRadixDigits; ++b) {
-        const int64_t lo = starts[b], len = (int64_t)starts[b + 1] - lo;
-        if (len <= 0) continue;
-        const int64_t k = ceil_div(len, size);
-        for (int64_t j = 0; j < k; ++j)
-            list.push_back(CountChunk{b, (int32_t)(lo + len * j / k), (int32_t)(lo + len * (j + 1) / k),
-                                      k > 1 ? 1 : 0});
-    }
-    if ((int64_t)list.size() > kMaxCountChunks) return fail(PR_ERR_ARG, "in-degree chunks overflow");
-    PR_HIP_TRY(hipMemcpyAsync(chunks, list.data(), sizeof(CountChunk) * list.size(),
-                              hipMemcpyHostToDevice, stream));
+    k_count_chunks<<<1, kBlock, 0, stream>>>(w.scanned, T, size, chunks);
+    PR_LAUNCHED("count chunks");
     PR_TRY(fill_u32(counts, 0u, n, stream));
-    k_count_buckets<<<dim3((unsigned)list.size()), kCountBlock, 0, stream>>>(
-        w.key[0], reinterpret_cast<const CountChunk*>(chunks), shift, n, counts);
+    k_count_buckets<<<dim3((unsigned)kMaxCountChunks), kCountBlock, 0, stream>>>(
+        reinterpret_cast<const uint16_t*>(w.key[0]), chunks, shift, n, counts);
     PR_LAUNCHED("count buckets");
     PR_TRY(scan_exclusive(counts, reinterpret_cast<uint32_t*>(in_rp), n, scan_ws, stream));
-    PR_HIP_TRY(hipStreamSynchronize(stream));  // `list` must outlive the copy
     return PR_OK;
 }
 
@@ -353,13 +353,18 @@ __global__ __launch_bounds__(kBlock) void k_order(const int32_t* __restrict__ ol
 // Out-edge CSR in plan order: row p of the result is row old_of[p] of the
 // input with every target renumbered.  Edge-parallel: each workgroup covers
 // kBlock * kPermItems positions.  The rows that own them, [lo, hi], are
-// found once, by the whole workgroup; when there are at most kPermRows of them their output and
-// input starts are staged in LDS and each position finds its row there, so
-// a lane's loads of out_ci and then of new_id go out together for all its
-// positions.  (A window over a long run of empty rows searches perm_rp in
-// global memory instead.)
+// found once, by the whole workgroup; when there are at most kPermRows of
+// them, their output and input starts are staged in LDS and each position
+// finds its row there, so a lane's loads of out_ci and then of new_id go out
+// together for all its positions.  (A window over a long run of empty rows
+// searches perm_rp in global memory instead.)  A tiled plan also gets the
+// first pass of the sort by tile here: when `hist` is set, the workgroup's
+// histogram of min(tile of the renamed target, 255), stored digit-major as
+// the radix histogram of a pass over the same 4096-edge tiles
+// (hist[digit * T + workgroup]).
 constexpr int kPermItems = 16;
 constexpr int kPermRows = kBlock * kPermItems;
+static_assert(kPermRows == kRadixTile, "the permutation's windows are the sort's tiles");
 
 __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restrict__ perm_rp,
                                                          const int32_t* __restrict__ old_of,
@@ -368,9 +373,13 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
                                                          const int32_t* __restrict__ out_ci,
                                                          int32_t n, int64_t nnz,
                                                          int32_t* __restrict__ perm_ci,
-                                                         int32_t* __restrict__ src_of) {
+                                                         int32_t* __restrict__ src_of,
+                                                         TileMap map, uint32_t* __restrict__ hist,
+                                                         int64_t T) {
     __shared__ int32_t s_dst[kPermRows + 1];  // perm_rp of the window's rows
     __shared__ int32_t s_src[kPermRows];      // out_rp[old_of[row]]
+    __shared__ uint32_t s_hist[kRadixDigits];
+    if (hist) s_hist[threadIdx.x] = 0u;
     const int64_t base = blockIdx.x * (int64_t)kPermRows;
     const int64_t last = (base + kPermRows < nnz ? base + kPermRows : nnz) - 1;
     int32_t lo, hi;
@@ -386,12 +395,13 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
     }
     __syncthreads();
     int32_t row[kPermItems];
-    int64_t q[kPermItems];
+    int32_t q[kPermItems];  // input positions, clamped into [0, nnz): they fit 32 bits
 #pragma unroll
     for (int r = 0; r < kPermItems; ++r) {
         int64_t p = base + r * kBlock + threadIdx.x;
         p = p < last ? p : last;
         int32_t j;
+        int64_t qr;
         if (staged) {
             int32_t a = 0, b = hi - lo;  // last local row with s_dst[row] <= p
             while (a < b) {
@@ -402,12 +412,12 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
                     b = mid - 1;
             }
             j = lo + a;
-            q[r] = (int64_t)s_src[a] + (p - s_dst[a]);
+            qr = (int64_t)s_src[a] + (p - s_dst[a]);
         } else {
             j = owner_row(perm_rp, p, lo, hi);
-            q[r] = (int64_t)out_rp[old_of[j]] + (p - perm_rp[j]);
+            qr = (int64_t)out_rp[old_of[j]] + (p - perm_rp[j]);
         }
-        q[r] = q[r] < 0 ? 0 : (q[r] >= nnz ? nnz - 1 : q[r]);
+        q[r] = (int32_t)(qr < 0 ? 0 : (qr >= nnz ? nnz - 1 : qr));
         row[r] = j;
     }
     int32_t t[kPermItems];
@@ -427,6 +437,25 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
             perm_ci[p] = t[r];
             src_of[p] = row[r];
         }
+    }
+    if (hist) {
+        // The targets go through LDS (s_src is free once every lane is past
+        // the row search), so that the count starts with no per-item
+        // registers live: counting from them directly costs occupancy.
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kPermItems; ++r) s_src[r * kBlock + threadIdx.x] = t[r];
+        __syncthreads();
+        DigitCounter dc;
+        for (int r = 0; r < kPermItems; ++r) {
+            const int i = r * kBlock + threadIdx.x;
+            if (base + i > last) break;
+            const int32_t tile = tile_of(map, s_src[i]);
+            dc.add((uint32_t)(tile < kRadixDigits - 1 ? tile : kRadixDigits - 1), s_hist);
+        }
+        dc.flush(s_hist);
+        __syncthreads();
+        hist[(int64_t)threadIdx.x * T + blockIdx.x] = s_hist[threadIdx.x];
     }
 }
 
@@ -644,6 +673,7 @@ void bucket_bounds(bool tiled, int32_t out[kNumBuckets]) {
 // What a mode's builder reports back to pr_plan_create.
 struct Built {
     int32_t n_items = 0, n_chunk_rows = 0, grid = 1, fix_grid = 0;
+    int64_t tile_launch = 1, unit_cost = 0;  // tiled: workgroups per launch, cost per unit
     int32_t items_of[kNumBuckets + 1] = {};
     TileMap map{};
     int32_t n_tiles = 0, n_units = 0, n_fixes = 0, tile_grid = 1;
@@ -742,13 +772,10 @@ int log2_ceil(int64_t x) {
     return k;
 }
 
-// Tiled pull: tile sizes per bucket, the renumbered edges sorted by tile
-// (stable, so each tile keeps them in increasing source order), the tile
-// edge arrays, and the units (built on the host from the tiles' edge counts,
-// read back).
-int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
-                const unsigned long long* stats, const int32_t* row_begin, int cus,
-                hipStream_t stream, Built& bt) {
+// Tiled pull, before the permutation: tile sizes per bucket, from the bucket
+// sizes (host only).  The permutation counts the edges per tile with the map.
+int lay_out_tiles(const PlanWs& w, int64_t nnz, const unsigned long long* stats,
+                  const int32_t* row_begin, int32_t n, int cus, Built& bt) {
     // Launch width, and the tuning knobs: edges per tile and estimated cost
     // per unit (each knob, when set, is used as given).
     int64_t grid = cus;
@@ -792,6 +819,22 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
         return fail(PR_ERR_ARG, "tiles (%d) exceed the planned bound (%lld)", tiles,
                     (long long)w.n_tiles_max);
     bt.n_tiles = tiles;
+    bt.tile_launch = grid;
+    bt.unit_cost = unit_env ? unit_cost : 0;  // 0: chosen from the costs once they are known
+    return PR_OK;
+}
+
+// Tiled pull, after the permutation (which wrote the first sort pass's
+// histogram): the renumbered edges sorted by tile (stable, so each tile
+// keeps them in increasing source order), the tile edge arrays, and the
+// units (built on the host from the tiles' edge counts, read back).
+int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, hipStream_t stream,
+                Built& bt) {
+    const int64_t grid = bt.tile_launch;
+    const bool unit_env = bt.unit_cost > 0;
+    int64_t unit_cost = unit_env ? bt.unit_cost : kUnitCost;
+    const TileMap& map = bt.map;
+    const int32_t tiles = bt.n_tiles;
 
     // each tile's first edge: the in-edges of the rows before it (s.perm_rp
     // is free by now and takes the scan of the in-degrees in plan order)
@@ -802,18 +845,14 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
     k_tile_first<<<grid_for((int64_t)tiles + 1, 1024), kBlock, 0, stream>>>(in_rp_plan, n, tiles, map,
                                                                             first);
     PR_LAUNCHED("tile starts");
-    std::vector<int32_t> tp((size_t)tiles + 1);
-    PR_HIP_TRY(hipMemcpyAsync(tp.data(), first, sizeof(int32_t) * tp.size(), hipMemcpyDeviceToHost,
-                              stream));
-    PR_HIP_TRY(hipStreamSynchronize(stream));
     // Edges sorted by tile, stably (so by source inside a tile): keys are the
     // targets, values the sources (into s.order).  One full pass sorts by
-    // min(tile, 255); the edges of tiles 255 and up (the light tiles, which
-    // come last and hold few edges) form one range, [tp[255], nnz), which is
-    // then sorted by tile on its own.
+    // min(tile, 255), from the histogram the permutation counted; the edges of
+    // tiles 255 and up (the light tiles, which come last and hold few edges)
+    // form one range, [tp[255], nnz), which is then sorted by tile on its own.
     const int32_t* sorted_targets = nullptr;
+    constexpr int32_t kCap = kRadixDigits - 1;
     if (nnz > 0) {
-        constexpr int32_t kCap = kRadixDigits - 1;
         RadixIn in{};
         in.count = nnz;
         in.n = n;
@@ -822,15 +861,25 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
         in.tiles = map;
         in.tile_cap = kCap;
         in.error = s.tr.error;
-        int32_t* keys_sorted = nullptr;
-        PR_TRY(radix_sort<kFromTileTargets>(in, kRadixBits, s.order, s.tr.sort, &keys_sorted, stream));
-        sorted_targets = keys_sorted;
+        const RadixWs& rw = s.tr.sort;
+        const int64_t T = radix_tiles(nnz);
+        PR_TRY(scan_exclusive(rw.hist, rw.scanned, kRadixDigits * T, rw.scan_ws, stream));
+        k_radix_scatter<kFromTileTargets><<<dim3((unsigned)T), kBlock, 0, stream>>>(
+            in, 0, T, rw.scanned, rw.key[0], s.order);
+        PR_LAUNCHED("radix scatter");
+        sorted_targets = rw.key[0];
+    }
+    std::vector<int32_t> tp((size_t)tiles + 1);
+    PR_HIP_TRY(hipMemcpyAsync(tp.data(), first, sizeof(int32_t) * tp.size(), hipMemcpyDeviceToHost,
+                              stream));
+    PR_HIP_TRY(hipStreamSynchronize(stream));
+    if (nnz > 0) {
         const int64_t lo = tiles > kCap ? tp[(size_t)kCap] : nnz;
         if (lo < nnz) {
             RadixIn rest{};
             rest.count = nnz - lo;
             rest.n = n;
-            rest.keys = keys_sorted + lo;
+            rest.keys = s.tr.sort.key[0] + lo;
             rest.vals = s.order + lo;
             rest.tiles = map;
             rest.tile_base = kCap;
@@ -838,7 +887,7 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
             // scratch: the other ping-pong pair, and the sort's inputs (free now)
             int32_t* const sk[2] = {s.tr.sort.key[1], s.perm_ci};
             int32_t* const sv[2] = {s.tr.sort.val[1], s.src_of};
-            PR_TRY(radix_sort_to<kFromTileTargets>(rest, vertex_bits(tiles - kCap), keys_sorted + lo,
+            PR_TRY(radix_sort_to<kFromTileTargets>(rest, vertex_bits(tiles - kCap), s.tr.sort.key[0] + lo,
                                                    s.order + lo, sk, sv, s.tr.sort, stream));
         }
     }
@@ -1070,6 +1119,23 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     k_plan_keys<<<grid_for(n, 1024), kBlock, 0, stream>>>(s.perm_rp, out_rp, n, bounds, s.key,
                                                           s.stats);
     PR_LAUNCHED("plan keys");
+
+    // Bucket ranges (hub bucket first), read back now: a tiled plan lays out
+    // its tiles before the permutation, which counts the edges per tile.
+    unsigned long long stats[2 * kNumBuckets];
+    PR_HIP_TRY(hipMemcpyAsync(stats, s.stats, sizeof stats, hipMemcpyDeviceToHost, stream));
+    PR_HIP_TRY(hipStreamSynchronize(stream));
+    int32_t row_begin[kNumBuckets + 1];  // indexed by bucket; hub rows start at 0
+    {
+        int64_t r = 0;
+        for (int b = kHubBucket; b >= 0; --b) {
+            row_begin[b] = (int32_t)r;
+            r += (int64_t)stats[b];
+        }
+        row_begin[kNumBuckets] = (int32_t)r;  // == n
+    }
+    Built bt{};
+    if (tiled) PR_TRY(lay_out_tiles(w, nnz, stats, row_begin, n, cus, bt));
     {
         RadixIn in{};
         in.count = n;
@@ -1090,27 +1156,14 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     if (nnz > 0) {
         const int64_t blocks = ceil_div(nnz, kBlock * kPermItems);
         k_permute_rows<<<dim3((unsigned)blocks), kBlock, 0, stream>>>(
-            s.perm_rp, s.old_of, w.new_id, out_rp, out_ci, n, nnz, s.perm_ci, s.src_of);
+            s.perm_rp, s.old_of, w.new_id, out_rp, out_ci, n, nnz, s.perm_ci, s.src_of, bt.map,
+            tiled ? s.tr.sort.hist : nullptr, blocks);
         PR_LAUNCHED("permute rows");
     }
 
-    // 3. Bucket ranges (hub bucket first).
-    unsigned long long stats[2 * kNumBuckets];
-    PR_HIP_TRY(hipMemcpyAsync(stats, s.stats, sizeof stats, hipMemcpyDeviceToHost, stream));
-    PR_HIP_TRY(hipStreamSynchronize(stream));
-    int32_t row_begin[kNumBuckets + 1];  // indexed by bucket; hub rows start at 0
-    {
-        int64_t r = 0;
-        for (int b = kHubBucket; b >= 0; --b) {
-            row_begin[b] = (int32_t)r;
-            r += (int64_t)stats[b];
-        }
-        row_begin[kNumBuckets] = (int32_t)r;  // == n
-    }
-
-    Built bt{};
+    // 3. The layout's work items.
     if (tiled)
-        PR_TRY(build_tiled(w, s, n, nnz, stats, row_begin, cus, stream, bt));
+        PR_TRY(build_tiled(w, s, n, nnz, stream, bt));
     else
         PR_TRY(build_bucketed(w, s, n, nnz, stats, row_begin, cus, stream, bt));
     if (validate) PR_TRY(read_error_word(err, stream, "pr_plan_create"));

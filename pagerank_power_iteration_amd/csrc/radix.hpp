@@ -181,6 +181,45 @@ __device__ __forceinline__ uint64_t digit_peers(uint32_t dg, bool valid) {
     return peers;
 }
 
+// Workgroups are dealt to the eight XCDs in turn (workgroup b to XCD b mod 8)
+// and every XCD has an L2 of its own.  Tiles t and t + 1 write neighbouring
+// pieces of each digit's output run, often parts of one cache line, so the
+// scatter gives each XCD a contiguous range of tiles, taken in order: the
+// pieces of a line then meet in one L2 instead of leaving two partial lines.
+// (The read-mostly passes keep the dealt order: given contiguous ranges,
+// the histograms of skewed keys and the permutation ran slower.)
+// A bijection of [0, T): XCD x gets floor(T / 8) tiles, plus one if x < T mod 8.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
+    const int64_t x = b % kXcds, j = b / kXcds, q = T / kXcds, r = T % kXcds;
+    return x * q + (x < r ? x : r) + j;
+}
+
+// Counts digits into the LDS histogram h, one item at a time.  Graph keys
+// are skewed: many lanes of a round often hold digit 0 (the low ids of a
+// power-law graph, or the hub tiles), and LDS adds to one address
+// serialize, so digits below kRegDigits are counted in registers and added
+// once per wavefront by flush(), which every lane calls.
+struct DigitCounter {
+    static constexpr int kRegDigits = 4;
+    uint32_t reg[kRegDigits] = {};
+    __device__ __forceinline__ void add(uint32_t dg, uint32_t* h) {
+        if (dg < (uint32_t)kRegDigits) {
+#pragma unroll
+            for (int j = 0; j < kRegDigits; ++j) reg[j] += dg == (uint32_t)j ? 1u : 0u;
+        } else {
+            atomicAdd(&h[dg], 1u);
+        }
+    }
+    __device__ __forceinline__ void flush(uint32_t* h) {
+#pragma unroll
+        for (int j = 0; j < kRegDigits; ++j) {
+            const uint32_t c = wave_sum(reg[j]);
+            if (lane_id() == 0 && c) atomicAdd(&h[j], c);
+        }
+    }
+};
+
 // Histogram of one digit per tile, stored digit-major: hist[digit * T + tile].
 // A lane loads all of its items before counting any (an index past the end
 // reloads the last element and is not counted), so the loads overlap.
@@ -198,44 +237,14 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, in
         const int64_t i = base + r * kBlock + threadIdx.x;
         k[r] = radix_load(in, i < in.count ? i : last);
     }
-    // Graph keys are skewed: many lanes of a round often hold digit 0 (the
-    // low ids of a power-law graph), and LDS adds to one address serialize.
-    // Digits below kRegDigits are counted in registers and added once per
-    // wavefront.
-    constexpr int kRegDigits = 4;
-    uint32_t reg[kRegDigits] = {};
+    DigitCounter dc;
 #pragma unroll
-    for (int r = 0; r < kRadixItems; ++r) {
-        const int64_t i = base + r * kBlock + threadIdx.x;
-        if (i < in.count) {
-            const uint32_t dg = radix_digit<MODE>(in, radix_check<MODE>(in, k[r]), shift);
-            if (dg < (uint32_t)kRegDigits) {
-#pragma unroll
-                for (int j = 0; j < kRegDigits; ++j) reg[j] += dg == (uint32_t)j ? 1u : 0u;
-            } else {
-                atomicAdd(&h[dg], 1u);
-            }
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < kRegDigits; ++j) {
-        const uint32_t c = wave_sum(reg[j]);
-        if (lane_id() == 0 && c) atomicAdd(&h[j], c);
-    }
+    for (int r = 0; r < kRadixItems; ++r)
+        if (base + r * kBlock + threadIdx.x < in.count)
+            dc.add(radix_digit<MODE>(in, radix_check<MODE>(in, k[r]), shift), h);
+    dc.flush(h);
     __syncthreads();
     hist[(int64_t)threadIdx.x * T + blockIdx.x] = h[threadIdx.x];
-}
-
-// Workgroups are dealt to the eight XCDs in turn (workgroup b to XCD b mod 8)
-// and every XCD has an L2 of its own.  Tiles t and t + 1 write neighbouring
-// pieces of each digit's output run, often parts of one cache line, so the
-// scatter gives each XCD a contiguous range of tiles, taken in order: the
-// pieces of a line then meet in one L2 instead of leaving two partial lines.
-// A bijection of [0, T): XCD x gets floor(T / 8) tiles, plus one if x < T mod 8.
-constexpr int kXcds = 8;
-__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
-    const int64_t x = b % kXcds, j = b / kXcds, q = T / kXcds, r = T % kXcds;
-    return x * q + (x < r ? x : r) + j;
 }
 
 // Owner rows of a first-pass tile, when the rows it touches are at most
@@ -282,9 +291,10 @@ __device__ __forceinline__ void stage_owner_rows(const int32_t* __restrict__ rp,
 }
 
 // Stable scatter.  `scanned` is the exclusive scan of the digit-major
-// histogram.  Keys are written only when keys_out is not null; values are
-// carried only when VALS.
-template <int MODE, bool VALS = true>
+// histogram.  Keys are written only when keys_out is not null (with KEY16,
+// as uint16 words holding each key's low 16 bits); values are carried only
+// when VALS.
+template <int MODE, bool VALS = true, bool KEY16 = false>
 __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift, int64_t T,
                                                           const uint32_t* __restrict__ scanned,
                                                           int32_t* __restrict__ keys_out,
@@ -386,7 +396,10 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
         const int32_t k = s_key[i];
         const uint32_t dg = radix_digit<MODE>(in, k, shift);
         const int64_t o = (int64_t)global_start[dg] + (i - (int64_t)digit_start[dg]);
-        if (keys_out) keys_out[o] = k;
+        if (KEY16)
+            reinterpret_cast<uint16_t*>(keys_out)[o] = (uint16_t)k;
+        else if (keys_out)
+            keys_out[o] = k;
         if (VALS) vals_out[o] = s_val[i];
     }
 }
