@@ -78,6 +78,7 @@ struct RadixIn {
     const int32_t* keys;           // kFromOutCsr: out_col_idx; other modes: keys
     const int32_t* vals;           // kFromPairs, kFromTileTargets
     const int32_t* row_ptr;        // kFromOutCsr: out_row_ptr
+    const int32_t* tile_row;       // kFromOutCsr: [T + 1] from k_tile_rows
     TileMap tiles;                 // kFromTileTargets
     int32_t tile_base = 0;         // kFromTileTargets: the digit is
     int32_t tile_cap = INT32_MAX;  //   min(tile_of(key) - tile_base, tile_cap)
@@ -252,7 +253,12 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, in
 // that starts inside the tile marks its first slot (of rows that start at
 // the same slot, the last one wins: the others are empty), and an inclusive
 // max-scan carries the marks forward; slot 0 belongs to `lo`, the owner of
-// the tile's first edge.  Contains barriers: call from every lane.
+// the tile's first edge.  The scan: every lane takes the maximum of its
+// kRadixItems consecutive slots, a workgroup-wide exclusive max-scan of
+// those gives each lane its carry, and the lane sweeps its slots again from
+// it.  (Sixteen 64-slot rounds per wavefront, each waiting for the last
+// one's carry, cost about four times as much.)  `wave_max` is kWaves words
+// of LDS.  Contains barriers: call from every lane.
 __device__ __forceinline__ void stage_owner_rows(const int32_t* __restrict__ rp, int64_t base,
                                                  int count, int32_t lo, int32_t hi, int32_t* own,
                                                  int32_t* wave_max) {
@@ -264,28 +270,29 @@ __device__ __forceinline__ void stage_owner_rows(const int32_t* __restrict__ rp,
         if (p > 0 && p < count) atomicMax(&own[p], r);  // in range for a valid row_ptr
     }
     __syncthreads();
-    // wavefront w scans slots [w * 1024, (w + 1) * 1024) in rounds of 64
-    constexpr int kSpan = kRadixTile / kWaves;
-    int32_t carry = -1;
-    for (int r = 0; r < kSpan / kWave; ++r) {
-        const int i = wave * kSpan + r * kWave + lane;
-        int32_t v = i < count ? own[i] : -1;
+    const int i0 = tid * kRadixItems;
+    int32_t m = -1;
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int32_t t = __shfl_up(v, off, kWave);
-            if (lane >= off) v = v > t ? v : t;
-        }
-        v = v > carry ? v : carry;
-        if (i < count) own[i] = v;
-        carry = __shfl(v, kWave - 1, kWave);
+    for (int j = 0; j < kRadixItems; ++j)
+        if (i0 + j < count) m = max(m, own[i0 + j]);
+    // exclusive max-scan of the lanes' maxima, in lane order
+    int32_t incl = m;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t t = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl = max(incl, t);
     }
-    if (lane == 0) wave_max[wave] = carry;
+    int32_t carry = __shfl_up(incl, 1, kWave);
+    if (lane == 0) carry = -1;
+    if (lane == kWave - 1) wave_max[wave] = incl;
     __syncthreads();
-    int32_t before = -1;
-    for (int w = 0; w < wave; ++w) before = before > wave_max[w] ? before : wave_max[w];
-    for (int r = 0; r < kSpan / kWave; ++r) {
-        const int i = wave * kSpan + r * kWave + lane;
-        if (i < count && own[i] < before) own[i] = before;
+    for (int w = 0; w < wave; ++w) carry = max(carry, wave_max[w]);
+#pragma unroll
+    for (int j = 0; j < kRadixItems; ++j) {
+        if (i0 + j < count) {
+            carry = max(carry, own[i0 + j]);
+            own[i0 + j] = carry;
+        }
     }
     __syncthreads();
 }
@@ -313,17 +320,6 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
 
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) wave_count[w][tid] = 0;
-    // First pass: the rows that own the tile's edges, [row_lo, row_hi].  Their
-    // owner rows come from LDS when there are few enough of them (a tile
-    // inside a long run of empty rows searches row_ptr per edge instead).
-    // s_val is free until the reorder below.
-    int32_t row_lo = 0, row_hi = 0;
-    if (MODE == kFromOutCsr)
-        block_owner_rows(in.row_ptr, base, base + count - 1, in.n, (uint32_t*)s_key, row_lo, row_hi);
-    __syncthreads();
-    const bool staged_rows = MODE == kFromOutCsr && VALS && row_hi - row_lo < kRadixTile;
-    if (staged_rows)
-        stage_owner_rows(in.row_ptr, base, count, row_lo, row_hi, s_val, (int32_t*)scan_tmp);
 
     int32_t key[kRadixItems], val[kRadixItems];
     uint32_t rank[kRadixItems];
@@ -337,6 +333,23 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
         key[r] = radix_load(in, g);
         if (kLoadVals) val[r] = in.vals[g];
     }
+    // First pass: the rows that own the tile's edges lie in [row_lo, row_hi]
+    // (clamped, so a malformed row_ptr cannot index out of bounds).  Their
+    // owner rows come from LDS when there are few enough of them (a tile
+    // inside a long run of empty rows searches row_ptr per edge instead).
+    // s_val is free until the reorder below.  The loads above stay in flight
+    // meanwhile: the barriers here wait for LDS only.
+    int32_t row_lo = 0, row_hi = 0;
+    if (MODE == kFromOutCsr) {
+        row_lo = min(max(in.tile_row[tile], 0), in.n - 1);
+        row_hi = min(max(in.tile_row[tile + 1], row_lo), in.n - 1);
+    }
+    const bool staged_rows = MODE == kFromOutCsr && VALS && row_hi - row_lo < kRadixTile;
+    if (staged_rows)
+        stage_owner_rows(in.row_ptr, base, count, row_lo, row_hi, s_val, (int32_t*)scan_tmp);
+    else
+        __syncthreads();  // the wave counters' clearing
+
 #pragma unroll
     for (int r = 0; r < kRadixItems; ++r) {
         const int idx = wave * (kWave * kRadixItems) + r * kWave + lane;

@@ -29,6 +29,7 @@ TransposeWs transpose_carve(void* base, int32_t n, int64_t nnz) {
     TransposeWs w{};
     Carver c(base);
     w.sort = radix_carve(c, nnz);
+    w.tile_row = c.take<int32_t>((size_t)radix_tiles(nnz) + 1);
     w.error = c.take<uint32_t>(1);
     w.bytes = c.used;
     return w;
@@ -73,6 +74,18 @@ __global__ __launch_bounds__(kBlock) void k_rows_from_sorted(const int32_t* __re
     }
 }
 
+// tile_row[t] = the row that owns edge t * kRadixTile (the first edge of tile
+// t), for t < T, and tile_row[T] = n - 1: the first pass's row range of tile
+// t is then [tile_row[t], tile_row[t + 1]] (a bound on the owner of its last
+// edge).  One lane per tile, each a binary search: the searches run side by
+// side here instead of in series at the start of every tile of the pass.
+__global__ __launch_bounds__(kBlock) void k_tile_rows(const int32_t* __restrict__ rp, int32_t n,
+                                                      int64_t T, int32_t* __restrict__ tile_row) {
+    const int64_t t = blockIdx.x * (int64_t)kBlock + threadIdx.x;
+    if (t < T) tile_row[t] = owner_row(rp, t * kRadixTile, 0, n - 1);
+    if (t == T) tile_row[T] = n - 1;
+}
+
 // Checks of an out-edge CSR for PR_VALIDATE: row_ptr[0] == 0, non-decreasing,
 // row_ptr[n] == nnz.  (Columns are range-checked by the first sort pass.)
 __global__ __launch_bounds__(kBlock) void k_check_row_ptr(const int32_t* __restrict__ rp, int32_t n,
@@ -108,7 +121,11 @@ int transpose_device(int32_t n, int64_t nnz, const int32_t* out_rp, const int32_
     in.n = n;
     in.keys = out_ci;
     in.row_ptr = out_rp;
+    in.tile_row = w.tile_row;
     in.error = w.error;
+    const int64_t T = radix_tiles(nnz);
+    k_tile_rows<<<grid_for(T + 1, INT32_MAX), kBlock, 0, stream>>>(out_rp, n, T, w.tile_row);
+    PR_LAUNCHED("tile rows");
     int32_t* sorted_keys = nullptr;
     PR_TRY(radix_sort<kFromOutCsr>(in, vertex_bits(n), in_ci, w.sort, &sorted_keys, stream));
     k_rows_from_sorted<<<grid_for(nnz / kRowsRun + 1), kBlock, 0, stream>>>(sorted_keys, nnz, n, in_rp);

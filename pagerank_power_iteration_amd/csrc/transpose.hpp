@@ -7,7 +7,8 @@ namespace pr {
 
 struct TransposeWs {
     RadixWs sort;
-    uint32_t* error;  // [1]
+    int32_t* tile_row;  // [radix_tiles(nnz) + 1] the first pass's row range per tile
+    uint32_t* error;    // [1]
     size_t bytes;
 };
 
