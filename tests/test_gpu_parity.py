@@ -53,6 +53,28 @@ def test_transpose_is_deterministic(prx):
     assert torch.equal(a_rp, b_rp) and torch.equal(a_ci, b_ci)
 
 
+def test_transpose_tiles_over_empty_rows(prx):
+    """The first sort pass finds each edge's source row from the row starts
+    inside its 4096-edge tile, and searches row_ptr instead when the tile
+    spans more than 4096 rows.  Here rows with edges are 7001 apart (so every
+    tile spans thousands of empty rows), except for a dense run of short rows
+    at the end (tiles of few rows, some starting mid-row)."""
+    n = 60_000
+    src, dst = [], []
+    for u in range(0, 49_007, 7001):
+        t = (np.arange(1500, dtype=np.int64) * 7919 + u * 31 + 3) % n
+        src.append(np.full(t.size, u))
+        dst.append(t)
+    dense = np.arange(50_000, n, dtype=np.int64)
+    src.append(np.repeat(dense, 3))
+    dst.append((np.repeat(dense, 3) * 13 + np.tile([1, 2, 5], dense.size)) % n)
+    g = graphgen.from_edges(n, np.concatenate(src), np.concatenate(dst), name="sparse_rows")
+    _, in_rp, in_ci = _transpose_gpu(prx, g)
+    ref_rp, ref_ci = oracle.transpose(g.row_ptr, g.col_idx)
+    np.testing.assert_array_equal(_cases.to_np(in_rp), ref_rp)
+    np.testing.assert_array_equal(_cases.to_np(in_ci), ref_ci)
+
+
 def test_transpose_four_radix_passes(prx):
     """n > 2^24 needs a fourth 8-bit pass."""
     n = (1 << 24) + 37
