@@ -189,7 +189,7 @@ unsigned grid_for(int64_t items, int64_t cap = 4096) {
 constexpr int kCountDigitBits = 8;
 constexpr int kCountMaxSpan = 1 << 15;  // 128 KB of LDS counters
 constexpr int kCountBlock = 1024;
-constexpr int kCountItems = 8;
+constexpr int kCountGroups = 4;  // 16-byte groups of keys per lane per round
 constexpr int64_t kMinCountChunk = 1 << 16;
 
 struct CountChunk {
@@ -231,17 +231,35 @@ __global__ __launch_bounds__(kCountBlock) void k_count_buckets(const uint16_t* _
     const int32_t span = 1 << shift;
     for (int32_t v = threadIdx.x; v < span; v += kCountBlock) cnt[v] = 0u;
     __syncthreads();
-    const int64_t last = (int64_t)c.end - 1;
-    for (int64_t i0 = c.begin + threadIdx.x; i0 < c.end; i0 += (int64_t)kCountBlock * kCountItems) {
-        uint32_t k[kCountItems];
+    // The chunk's 8-aligned middle in 16-byte groups of 8 keys, kCountGroups
+    // groups per lane per round (loads first, clamped: they overlap), so a
+    // workgroup keeps 64 KB of reads in flight; the unaligned ends one key
+    // per lane.
+    const int64_t a0 = ((int64_t)c.begin + 7) & ~(int64_t)7;
+    const int64_t a1 = ((int64_t)c.end & ~(int64_t)7) > a0 ? ((int64_t)c.end & ~(int64_t)7) : a0;
+    for (int64_t i = c.begin + threadIdx.x; i < c.end && i < a0; i += kCountBlock)
+        atomicAdd(&cnt[keys[i] & (span - 1)], 1u);
+    for (int64_t i = a1 + threadIdx.x; i < c.end; i += kCountBlock)
+        atomicAdd(&cnt[keys[i] & (span - 1)], 1u);
+    const uint4* groups = reinterpret_cast<const uint4*>(keys + a0);  // keys: 256-byte aligned
+    const int64_t ng = (a1 - a0) / 8;
+    for (int64_t g0 = threadIdx.x; g0 < ng; g0 += (int64_t)kCountBlock * kCountGroups) {
+        uint4 w[kCountGroups];
 #pragma unroll
-        for (int j = 0; j < kCountItems; ++j) {  // loads first, clamped: they overlap
-            const int64_t i = i0 + (int64_t)j * kCountBlock;
-            k[j] = keys[i < c.end ? i : last];
+        for (int j = 0; j < kCountGroups; ++j) {
+            const int64_t g = g0 + (int64_t)j * kCountBlock;
+            w[j] = groups[g < ng ? g : ng - 1];
         }
 #pragma unroll
-        for (int j = 0; j < kCountItems; ++j)
-            if (i0 + (int64_t)j * kCountBlock < c.end) atomicAdd(&cnt[k[j] & (span - 1)], 1u);
+        for (int j = 0; j < kCountGroups; ++j) {
+            if (g0 + (int64_t)j * kCountBlock >= ng) break;
+            const uint32_t h[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                atomicAdd(&cnt[(h[q] & 0xFFFFu) & (span - 1)], 1u);
+                atomicAdd(&cnt[(h[q] >> 16) & (span - 1)], 1u);
+            }
+        }
     }
     __syncthreads();
     const int64_t v0 = (int64_t)c.bucket << shift;

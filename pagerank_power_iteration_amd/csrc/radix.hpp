@@ -184,11 +184,13 @@ __device__ __forceinline__ uint64_t digit_peers(uint32_t dg, bool valid) {
 
 // Workgroups are dealt to the eight XCDs in turn (workgroup b to XCD b mod 8)
 // and every XCD has an L2 of its own.  Tiles t and t + 1 write neighbouring
-// pieces of each digit's output run, often parts of one cache line, so the
-// scatter gives each XCD a contiguous range of tiles, taken in order: the
-// pieces of a line then meet in one L2 instead of leaving two partial lines.
-// (The read-mostly passes keep the dealt order: given contiguous ranges,
-// the histograms of skewed keys and the permutation ran slower.)
+// words of every histogram row and neighbouring pieces of each digit's
+// output run, often parts of one cache line, so the histogram and scatter
+// passes give each XCD a contiguous range of tiles, taken in order: the
+// pieces of a line then meet in one L2 instead of leaving partial lines in
+// several.  (On RMAT-23: the later scatter passes 1.41 -> 1.04 ms, the
+// histograms 0.30 -> 0.25 ms.  k_permute_rows keeps the dealt order: given
+// contiguous ranges it ran slower.)
 // A bijection of [0, T): XCD x gets floor(T / 8) tiles, plus one if x < T mod 8.
 constexpr int kXcds = 8;
 __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
@@ -204,12 +206,12 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
 struct DigitCounter {
     static constexpr int kRegDigits = 4;
     uint32_t reg[kRegDigits] = {};
-    __device__ __forceinline__ void add(uint32_t dg, uint32_t* h) {
+    __device__ __forceinline__ void add(uint32_t dg, uint32_t* h, uint32_t c = 1u) {
         if (dg < (uint32_t)kRegDigits) {
 #pragma unroll
-            for (int j = 0; j < kRegDigits; ++j) reg[j] += dg == (uint32_t)j ? 1u : 0u;
+            for (int j = 0; j < kRegDigits; ++j) reg[j] += dg == (uint32_t)j ? c : 0u;
         } else {
-            atomicAdd(&h[dg], 1u);
+            atomicAdd(&h[dg], c);
         }
     }
     __device__ __forceinline__ void flush(uint32_t* h) {
@@ -222,30 +224,53 @@ struct DigitCounter {
 };
 
 // Histogram of one digit per tile, stored digit-major: hist[digit * T + tile].
-// A lane loads all of its items before counting any (an index past the end
-// reloads the last element and is not counted), so the loads overlap.
+// A lane takes kRadixItems consecutive keys (four 16-byte loads) and adds
+// each run of equal digits once: a CSR's rows hold their targets in
+// increasing order, so neighbouring keys often share their high digits, and
+// lanes adding one at a time to the same LDS counter serialize.
 template <int MODE>
 __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, int64_t T,
                                                        uint32_t* __restrict__ hist) {
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
     __shared__ uint32_t h[kRadixDigits];
     h[threadIdx.x] = 0;
     __syncthreads();
-    const int64_t base = blockIdx.x * (int64_t)kRadixTile;
-    const int64_t last = in.count - 1;
+    const int64_t tile = xcd_tile(blockIdx.x, T);
+    const int64_t i0 = tile * kRadixTile + threadIdx.x * kRadixItems;
+    const int64_t left = in.count - i0;  // keys of this lane: min(left, kRadixItems)
     int32_t k[kRadixItems];
+    // (16-byte loads when the keys are 16-byte aligned: scratch always is, a
+    // caller's CSR or a sub-range of scratch need not be)
+    if (left >= kRadixItems && (reinterpret_cast<uintptr_t>(in.keys) & 15u) == 0) {
 #pragma unroll
-    for (int r = 0; r < kRadixItems; ++r) {
-        const int64_t i = base + r * kBlock + threadIdx.x;
-        k[r] = radix_load(in, i < in.count ? i : last);
+        for (int q = 0; q < kRadixItems / 4; ++q) {
+            const i32x4 v = *(const i32x4*)(in.keys + i0 + 4 * q);
+            k[4 * q] = v.x;
+            k[4 * q + 1] = v.y;
+            k[4 * q + 2] = v.z;
+            k[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < kRadixItems; ++r) k[r] = r < left ? radix_load(in, i0 + r) : 0;
     }
     DigitCounter dc;
+    uint32_t cur = 0, run = 0;
 #pragma unroll
-    for (int r = 0; r < kRadixItems; ++r)
-        if (base + r * kBlock + threadIdx.x < in.count)
-            dc.add(radix_digit<MODE>(in, radix_check<MODE>(in, k[r]), shift), h);
+    for (int r = 0; r < kRadixItems; ++r) {
+        if (r >= left) break;
+        const uint32_t dg = radix_digit<MODE>(in, radix_check<MODE>(in, k[r]), shift);
+        if (run > 0 && dg != cur) {
+            dc.add(cur, h, run);
+            run = 0;
+        }
+        cur = dg;
+        ++run;
+    }
+    if (run > 0) dc.add(cur, h, run);
     dc.flush(h);
     __syncthreads();
-    hist[(int64_t)threadIdx.x * T + blockIdx.x] = h[threadIdx.x];
+    hist[(int64_t)threadIdx.x * T + tile] = h[threadIdx.x];
 }
 
 // Owner rows of a first-pass tile, when the rows it touches are at most
