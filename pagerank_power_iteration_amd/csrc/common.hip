@@ -69,12 +69,19 @@ __global__ __launch_bounds__(kBlock) void k_scan_tiles(const T* __restrict__ in,
                                                        const T* __restrict__ offsets,
                                                        T* __restrict__ out) {
     __shared__ T tmp[kWaves + 1];
+    // A lane's items are contiguous: with both arrays 16-byte aligned (all of
+    // the library's scratch is), a full lane moves them as 16-byte vectors.
+    constexpr int kVec = kScanItems * (int)sizeof(T) / 16;
     const int64_t base = blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+    const bool wide = base + kScanItems <= N &&
+                      ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15u) == 0;
     T v[kScanItems];
     T local = 0;
-    if (base + kScanItems <= N) {  // the lane's items are contiguous: wide loads
+    if (wide) {
+        uint4 q[kVec];
 #pragma unroll
-        for (int j = 0; j < kScanItems; ++j) v[j] = in[base + j];
+        for (int j = 0; j < kVec; ++j) q[j] = reinterpret_cast<const uint4*>(in + base)[j];
+        __builtin_memcpy(v, q, sizeof v);
     } else {
 #pragma unroll
         for (int j = 0; j < kScanItems; ++j) v[j] = base + j < N ? in[base + j] : (T)0;
@@ -84,11 +91,21 @@ __global__ __launch_bounds__(kBlock) void k_scan_tiles(const T* __restrict__ in,
     T total;
     T run = block_exclusive_scan(local, &total, tmp);
     if (offsets) run += offsets[blockIdx.x];
+    T o[kScanItems];
 #pragma unroll
     for (int j = 0; j < kScanItems; ++j) {
-        int64_t i = base + j;
-        if (i < N) out[i] = run;
+        o[j] = run;
         run += v[j];
+    }
+    if (wide) {
+        uint4 q[kVec];
+        __builtin_memcpy(q, o, sizeof q);
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) reinterpret_cast<uint4*>(out + base)[j] = q[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < kScanItems; ++j)
+            if (base + j < N) out[base + j] = o[j];
     }
     if (blockIdx.x == gridDim.x - 1 && threadIdx.x == kBlock - 1) out[N] = run;
 }
