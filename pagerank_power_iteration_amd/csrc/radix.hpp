@@ -145,17 +145,23 @@ __device__ __forceinline__ void block_owner_rows(const int32_t* __restrict__ rp,
 __device__ __forceinline__ int32_t radix_load(const RadixIn& in, int64_t i) { return in.keys[i]; }
 
 // The key a pass uses for a loaded value k: targets read from a caller's CSR
-// are range-checked (an out-of-range one raises the error flag and is
-// clamped, so it cannot index out of bounds later).
+// are range-checked (an out-of-range one is clamped, so it cannot index out
+// of bounds later, and sets `bad`).  The caller raises the error flag once,
+// with report_bad: a store in the per-item loop would make the compiler
+// reload the kernel's arguments after every item.
 template <int MODE>
-__device__ __forceinline__ int32_t radix_check(const RadixIn& in, int32_t k) {
+__device__ __forceinline__ int32_t radix_check(const RadixIn& in, int32_t k, bool& bad) {
     if (MODE == kFromOutCsr || MODE == kFromTargets) {
-        if ((uint32_t)k >= (uint32_t)in.n) {
-            *in.error = 1u;
-            k = k < 0 ? 0 : in.n - 1;
-        }
+        const bool out = (uint32_t)k >= (uint32_t)in.n;
+        bad |= out;
+        k = out ? (k < 0 ? 0 : in.n - 1) : k;
     }
     return k;
+}
+
+template <int MODE>
+__device__ __forceinline__ void report_bad(const RadixIn& in, bool bad) {
+    if ((MODE == kFromOutCsr || MODE == kFromTargets) && bad) *in.error = 1u;
 }
 
 // The digit a pass sorts by: of the key, or of the key's tile.
@@ -256,10 +262,11 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, in
     }
     DigitCounter dc;
     uint32_t cur = 0, run = 0;
+    bool bad = false;
 #pragma unroll
     for (int r = 0; r < kRadixItems; ++r) {
         if (r >= left) break;
-        const uint32_t dg = radix_digit<MODE>(in, radix_check<MODE>(in, k[r]), shift);
+        const uint32_t dg = radix_digit<MODE>(in, radix_check<MODE>(in, k[r], bad), shift);
         if (run > 0 && dg != cur) {
             dc.add(cur, h, run);
             run = 0;
@@ -268,6 +275,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, in
         ++run;
     }
     if (run > 0) dc.add(cur, h, run);
+    report_bad<MODE>(in, bad);
     dc.flush(h);
     __syncthreads();
     hist[(int64_t)threadIdx.x * T + tile] = h[threadIdx.x];
@@ -375,6 +383,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
     else
         __syncthreads();  // the wave counters' clearing
 
+    bool bad = false;
 #pragma unroll
     for (int r = 0; r < kRadixItems; ++r) {
         const int idx = wave * (kWave * kRadixItems) + r * kWave + lane;
@@ -382,7 +391,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
         int32_t k = 0, v = 0;
         if (valid) {
             const int64_t g = base + idx;
-            k = radix_check<MODE>(in, key[r]);
+            k = radix_check<MODE>(in, key[r], bad);
             if (!VALS)
                 v = 0;
             else if (MODE == kFromOutCsr)
@@ -402,6 +411,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
         val[r] = v;
         rank[r] = prior + below;
     }
+    report_bad<MODE>(in, bad);
     __syncthreads();
 
     {  // lane tid owns digit tid: per-wavefront prefixes and the tile's digit starts
