@@ -25,7 +25,8 @@ constexpr int kRadixTile = kBlock * kRadixItems;
 // Where the pass reads its pairs from.
 enum RadixMode : int {
     // First transpose pass: key = target id out_col_idx[e]; value = the source
-    // row u that owns edge e (found by binary search in out_row_ptr).
+    // row u that owns edge e (from the row starts inside e's tile, within the
+    // tile's row range from k_tile_rows; see stage_owner_rows).
     kFromOutCsr = 0,
     // Later passes: keys_in[e], vals_in[e].
     kFromPairs = 1,
