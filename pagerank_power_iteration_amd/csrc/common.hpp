@@ -105,7 +105,16 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* total, T* scratch) {
     T incl = wave_inclusive_scan(v);
     if (lane_id() == kWave - 1) scratch[wave] = incl;
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if constexpr (W > 8) {  // many wavefronts: wavefront 0 scans their totals
+        static_assert(W <= kWave, "one lane per wavefront total");
+        if (wave == 0) {
+            const int l = lane_id();
+            const T c = l < W ? scratch[l] : (T)0;
+            const T in = wave_inclusive_scan(c);
+            if (l < W) scratch[l] = in - c;
+            if (l == W - 1) scratch[W] = in;
+        }
+    } else if (threadIdx.x == 0) {
         T run = 0;
         for (int w = 0; w < W; ++w) {
             T c = scratch[w];

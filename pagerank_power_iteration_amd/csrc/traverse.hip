@@ -595,6 +595,10 @@ __global__ __launch_bounds__(kSmallBlock) void k_bfs_small(TravArgs a, int32_t* 
     int cur = 0;
     uint32_t F = st->front[L % 3];
     uint64_t M = st->mf[L % 3];
+    // out-degree sum of the levels below L, carried in a register: a
+    // read-modify-write of the state per level would hold every level's
+    // closing barrier for a global load
+    uint64_t explored = st->explored[L % 2];
     for (uint32_t i = tid; i < F; i += kSmallBlock) {
         const int32_t v = (L % 2 ? q1 : q0)[i];
         int32_t s0, len;
@@ -629,11 +633,15 @@ __global__ __launch_bounds__(kSmallBlock) void k_bfs_small(TravArgs a, int32_t* 
                     hi = mid - 1;
             }
             const int32_t v = column(a, fs[cur][lo] + (int32_t)(j - (uint32_t)pre[lo]));
+            // v's row bounds are loaded before the claim resolves (wasted when
+            // it fails): a narrow level is a chain of memory latencies
+            // (column, claim, row bounds), and this runs the last two side by
+            // side.
+            int32_t s0, len;
+            row_range(a.rp, a.nnz, v, s0, len);
             if (atomicCAS(&level[v], -1, L + 1) == -1) {
                 const uint32_t pos = atomicAdd(&claimed, 1u);
                 next_q[pos] = v;  // each vertex is claimed once: pos < n
-                int32_t s0, len;
-                row_range(a.rp, a.nnz, v, s0, len);
                 edges += (uint64_t)len;
                 if (pos < (uint32_t)kSmallCap) {
                     fv[nxt][pos] = v;
@@ -645,10 +653,11 @@ __global__ __launch_bounds__(kSmallBlock) void k_bfs_small(TravArgs a, int32_t* 
         // (the sum's barriers also publish `claimed`)
         const uint64_t M_next = block_sum<uint64_t, kSmallBlock / kWave>(edges, red);
         const uint32_t F_next = claimed;
+        explored += M;
         if (tid == 0) {
             st->depth = L;
             st->mode[L % 2] = kTopDown;
-            st->explored[(L + 1) % 2] = st->explored[L % 2] + M;
+            st->explored[(L + 1) % 2] = explored;
         }
         ++L;
         if (F_next == 0 || F_next > (uint32_t)kSmallCap || M_next > kSmallEdges) {
