@@ -292,23 +292,29 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, in
 // those gives each lane its carry, and the lane sweeps its slots again from
 // it.  (Sixteen 64-slot rounds per wavefront, each waiting for the last
 // one's carry, cost about four times as much.)  `wave_max` is kWaves words
-// of LDS.  Contains barriers: call from every lane.
+// of LDS.  Slot i lives at own[owner_slot(i)], a bijection of [0, 4096) that
+// keeps the lane-strided sweeps (lane t: slots 16t..16t+15) and the
+// consecutive reads of the ranking loop in 64 distinct LDS banks: unswizzled,
+// a strided sweep put a wavefront's reads in four.  Contains barriers: call
+// from every lane.
+__device__ __forceinline__ int owner_slot(int i) { return i ^ ((i >> 4) & 63); }
+
 __device__ __forceinline__ void stage_owner_rows(const int32_t* __restrict__ rp, int64_t base,
                                                  int count, int32_t lo, int32_t hi, int32_t* own,
                                                  int32_t* wave_max) {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-    for (int i = tid; i < count; i += kBlock) own[i] = i == 0 ? lo : -1;
+    for (int i = tid; i < count; i += kBlock) own[owner_slot(i)] = i == 0 ? lo : -1;
     __syncthreads();
     for (int32_t r = lo + 1 + tid; r <= hi; r += kBlock) {
         const int64_t p = (int64_t)rp[r] - base;
-        if (p > 0 && p < count) atomicMax(&own[p], r);  // in range for a valid row_ptr
+        if (p > 0 && p < count) atomicMax(&own[owner_slot((int)p)], r);  // in range for a valid row_ptr
     }
     __syncthreads();
     const int i0 = tid * kRadixItems;
     int32_t m = -1;
 #pragma unroll
     for (int j = 0; j < kRadixItems; ++j)
-        if (i0 + j < count) m = max(m, own[i0 + j]);
+        if (i0 + j < count) m = max(m, own[owner_slot(i0 + j)]);
     // exclusive max-scan of the lanes' maxima, in lane order
     int32_t incl = m;
 #pragma unroll
@@ -324,8 +330,8 @@ __device__ __forceinline__ void stage_owner_rows(const int32_t* __restrict__ rp,
 #pragma unroll
     for (int j = 0; j < kRadixItems; ++j) {
         if (i0 + j < count) {
-            carry = max(carry, own[i0 + j]);
-            own[i0 + j] = carry;
+            carry = max(carry, own[owner_slot(i0 + j)]);
+            own[owner_slot(i0 + j)] = carry;
         }
     }
     __syncthreads();
@@ -396,7 +402,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
             if (!VALS)
                 v = 0;
             else if (MODE == kFromOutCsr)
-                v = staged_rows ? s_val[idx] : owner_row(in.row_ptr, g, row_lo, row_hi);
+                v = staged_rows ? s_val[owner_slot(idx)] : owner_row(in.row_ptr, g, row_lo, row_hi);
             else if (kLoadVals)
                 v = val[r];
             else
