@@ -384,10 +384,12 @@ constexpr int kFinalWaves = kFinalBlock / kWave;
 #endif
 constexpr int kTileBlock = PR_TILE_BLOCK;
 constexpr int kTileWaves = kTileBlock / kWave;
-#ifndef PR_TILE_Q
-#define PR_TILE_Q 2
-#endif
-constexpr int kTileQ = PR_TILE_Q;  // edge blocks per wavefront per round
+// Edge blocks per wavefront per round: two keep more contribution gathers in
+// flight; one wastes fewer loads when units are a few blocks long (a block
+// past a unit's end is loaded and dropped).  pr_run picks per plan.
+constexpr int kTileQWide = 2;
+constexpr int kTileQNarrow = 1;
+constexpr int64_t kWideUnitSlots = 4096;  // mean slots per unit from which kTileQWide runs
 
 struct TileArgs {
     const int32_t* __restrict__ tsrc;
@@ -444,7 +446,7 @@ __device__ __forceinline__ T load_nt_at(const T* base, uint32_t index) {
     return __builtin_nontemporal_load((const T*)((const char*)base + index * (uint32_t)sizeof(T)));
 }
 
-// One round of a wavefront: blocks b + j*kTileWaves (j < kTileQ) of the
+// One round of a wavefront: blocks b + j*kTileWaves (j < Q) of the
 // unit, each one 16-byte load of four slots per lane (lane l holds edges l,
 // l+64, l+128, l+192 of the block) and the block's word of tblk (a scalar
 // load: the block index is the same in every lane).  Every load is
@@ -452,9 +454,10 @@ __device__ __forceinline__ T load_nt_at(const T* base, uint32_t index) {
 // waiting for any: a block at or past the unit's end reads its last block
 // instead, and the caller adds zero for it.  The edge arrays are streamed
 // once per iteration: non-temporal.
+template <int Q>
 struct EdgeRound {
-    u32x4 w[kTileQ];
-    int32_t first[kTileQ];  // narrow block: its first source; wide: -1
+    u32x4 w[Q];
+    int32_t first[Q];  // narrow block: its first source; wide: -1
 };
 
 // The block a wavefront reads for its block number q (the same in every lane:
@@ -469,11 +472,12 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
     return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
+template <int Q>
 __device__ __forceinline__ void load_round(const int32_t* ts, const int32_t* tb, uint32_t b,
-                                           uint32_t nblk, uint32_t last, EdgeRound& r) {
+                                           uint32_t nblk, uint32_t last, EdgeRound<Q>& r) {
     const uint32_t lane = lane_id();
 #pragma unroll
-    for (int j = 0; j < kTileQ; ++j) {
+    for (int j = 0; j < Q; ++j) {
         const uint32_t bc = block_of(b + (uint32_t)(j * kTileWaves), nblk, last);
         r.first[j] = load_uniform(tb + bc);
         r.w[j] = load_nt_at((const u32x4*)ts, bc * (kEdgeBlock / 4) + lane);
@@ -482,15 +486,15 @@ __device__ __forceinline__ void load_round(const int32_t* ts, const int32_t* tb,
 
 // Adds the contributions of the unit's edge slots [e0, e1) (whole blocks)
 // into acc[row offset].  Wavefront w takes blocks w, w + kTileWaves, ...,
-// kTileQ per round; `next` holds its first round, loaded by the caller, and
+// Q per round; `next` holds its first round, loaded by the caller, and
 // each round loads the following one before gathering its own
 // contributions.  In one gather instruction lane l reads the source of edge
 // l + 64*i of a block: consecutive lanes, neighbouring sources.  A narrow
 // block decodes its slots; a wide one (rare) loads its rows here.
-template <bool kSigned>
+template <bool kSigned, int Q>
 __device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_t e1, float scale,
-                                           unsigned long long* acc, EdgeRound& next) {
-    constexpr uint32_t kStep = (uint32_t)kTileWaves * kTileQ;
+                                           unsigned long long* acc, EdgeRound<Q>& next) {
+    constexpr uint32_t kStep = (uint32_t)kTileWaves * Q;
     const int32_t* ts = a.tsrc + e0;
     const uint16_t* td = a.tdst + e0;
     const int32_t* tb = a.tblk + e0 / kEdgeBlock;
@@ -498,11 +502,11 @@ __device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_
     const uint32_t last = nblk > 0 ? nblk - 1 : 0;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     for (uint32_t b = wave; b < nblk; b += kStep) {
-        const EdgeRound cur = next;
+        const EdgeRound<Q> cur = next;
         load_round(ts, tb, b + kStep, nblk, last, next);
-        uint32_t src[kTileQ][4], row[kTileQ][4];
+        uint32_t src[Q][4], row[Q][4];
 #pragma unroll
-        for (int j = 0; j < kTileQ; ++j) {
+        for (int j = 0; j < Q; ++j) {
             if (cur.first[j] >= 0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -519,13 +523,13 @@ __device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_
                 }
             }
         }
-        float v[kTileQ][4];
+        float v[Q][4];
 #pragma unroll
-        for (int j = 0; j < kTileQ; ++j)
+        for (int j = 0; j < Q; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[j][i] = load_at(a.contrib_in, src[j][i]);
 #pragma unroll
-        for (int j = 0; j < kTileQ; ++j) {
+        for (int j = 0; j < Q; ++j) {
             const bool live = b + (uint32_t)(j * kTileWaves) < nblk;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -537,14 +541,15 @@ __device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_
 }
 
 // The first round of a unit's edges (nothing for an empty unit).
-__device__ __forceinline__ void first_round(const TileArgs& a, const TileUnit& u, EdgeRound& r) {
+template <int Q>
+__device__ __forceinline__ void first_round(const TileArgs& a, const TileUnit& u, EdgeRound<Q>& r) {
     const uint32_t nblk = (uint32_t)(u.e1 - u.e0) / kEdgeBlock;
     if (nblk > 0) {
         load_round(a.tsrc + u.e0, a.tblk + u.e0 / kEdgeBlock,
                    __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), nblk, nblk - 1, r);
     } else {
 #pragma unroll
-        for (int j = 0; j < kTileQ; ++j) {
+        for (int j = 0; j < Q; ++j) {
             r.w[j] = u32x4{0u, 0u, 0u, 0u};
             r.first[j] = 0;
         }
@@ -590,6 +595,7 @@ __device__ __forceinline__ void update_rows(const TileArgs& a, unsigned long lon
 // The accumulators are all zero between units: each unit's epilogue clears
 // the rows it read.  The next unit's descriptor and first round of edges are
 // loaded before this unit's epilogue, so their latency overlaps it.
+template <int Q>
 __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     __shared__ unsigned long long acc[kTileMaxRows + 1];  // + the trash row of padding edges
     __shared__ float red[3][kTileWaves];
@@ -638,7 +644,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     for (int32_t r = threadIdx.x; r < kTileMaxRows; r += kTileBlock) acc[r] = 0ull;
     int32_t cur = blockIdx.x;
     TileUnit u{};
-    EdgeRound round{};
+    EdgeRound<Q> round{};
     if (cur < a.n_units) {
         u = a.units[cur];
         first_round(a, u, round);
@@ -646,9 +652,9 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     __syncthreads();
     while (cur < a.n_units) {
         if (signed_contrib)
-            accumulate<true>(a, u.e0, u.e1, scale, acc, round);
+            accumulate<true, Q>(a, u.e0, u.e1, scale, acc, round);
         else
-            accumulate<false>(a, u.e0, u.e1, scale, acc, round);
+            accumulate<false, Q>(a, u.e0, u.e1, scale, acc, round);
         // claim the next unit only now: a claim made earlier would hold a
         // unit back behind this one while other workgroups run out of work
         if (threadIdx.x == 0) s_next = (int32_t)(gridDim.x + atomicAdd(queue, 1u));
@@ -910,6 +916,7 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         PR_LAUNCHED("init finalize");
     }
     int32_t tilefix_grid = (int32_t)((p->n_fix_rows + kFixBlock - 1) / kFixBlock);
+    const bool wide_rounds = p->n_units > 0 && p->n_slots >= kWideUnitSlots * (int64_t)p->n_units;
     if (tilefix_grid > kMaxGrid) tilefix_grid = kMaxGrid;
     const int32_t iter_parts = p->tiled ? p->n_units + tilefix_grid : p->n_batches + p->fix_grid;
     f.parts = iter_parts;
@@ -992,7 +999,10 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
             ta.part_prev = part_set[(t - 1) & 1];
             ta.parts_prev = t == 1 ? p->init_grid : iter_parts;
             ta.t = t;
-            k_tile<<<dim3((unsigned)p->tile_grid), kTileBlock, 0, stream>>>(ta);
+            if (wide_rounds)
+                k_tile<kTileQWide><<<dim3((unsigned)p->tile_grid), kTileBlock, 0, stream>>>(ta);
+            else
+                k_tile<kTileQNarrow><<<dim3((unsigned)p->tile_grid), kTileBlock, 0, stream>>>(ta);
             PR_LAUNCHED("tile");
         } else {
             k_iterate<<<dim3((unsigned)p->grid), kIterBlock, 0, stream>>>(a);
