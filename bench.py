@@ -275,8 +275,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see the sharding paragraph of DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path. "
+              "Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
