@@ -95,6 +95,28 @@ int pr_transpose(int32_t n, int64_t nnz, const int32_t* out_row_ptr_dev,
                  int32_t* in_col_idx_dev, void* ws_dev, size_t ws_bytes, uint32_t flags,
                  void* stream);
 
+/*
+ * pr_transpose without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, output and errors as
+ * pr_transpose; the workspace is instead a device array inside the library,
+ * PR_NOALLOC_SCRATCH_BYTES bytes, of which every GPU the library runs on
+ * holds one copy until the process ends.  The call allocates nothing (no
+ * hipMalloc, no hipFree, no allocating library routine).
+ *
+ * Limit: graphs whose pr_transpose_workspace_bytes(n, nnz) exceeds
+ * PR_NOALLOC_SCRATCH_BYTES (about 8 million edges) are rejected with
+ * PR_ERR_WORKSPACE before any device work.
+ * Calls on one GPU share its array: calls that overlap in time on the same
+ * GPU (on different streams, or from different threads) race and give
+ * unspecified output.  Every array entry a call reads is written earlier in
+ * the same call, so nothing carries over from one call to the next.
+ */
+#define PR_NOALLOC_SCRATCH_BYTES (128u << 20)
+int pr_transpose_noalloc(int32_t n, int64_t nnz, const int32_t* out_row_ptr_dev,
+                         const int32_t* out_col_idx_dev, int32_t* in_row_ptr_dev,
+                         int32_t* in_col_idx_dev, uint32_t flags, void* stream);
+
 /* Opaque iteration plan. */
 typedef struct pr_plan pr_plan;
 

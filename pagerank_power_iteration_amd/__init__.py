@@ -26,11 +26,13 @@ from ._lib import (PR_ERR_ARG, PR_ERR_GRAPH, PR_ERR_HIP, PR_ERR_WORKSPACE, PR_OK
                    pr_plan_scratch_bytes, pr_plan_workspace_bytes, pr_run, pr_status_string,
                    pr_spmv, pr_spmv_plan_create, pr_spmv_plan_destroy, pr_spmv_plan_items,
                    pr_spmv_scratch_bytes, pr_spmv_workspace_bytes, pr_transpose,
-                   pr_transpose_workspace_bytes)
+                   pr_transpose_noalloc, pr_transpose_workspace_bytes,
+                   PR_NOALLOC_SCRATCH_BYTES)
 
 __all__ = [
     "DeviceGraph", "Plan", "RunResult", "transpose", "PrError", "lib",
-    "pr_transpose", "pr_transpose_workspace_bytes", "pr_plan_create", "pr_plan_destroy",
+    "pr_transpose", "pr_transpose_workspace_bytes", "pr_transpose_noalloc",
+    "PR_NOALLOC_SCRATCH_BYTES", "pr_plan_create", "pr_plan_destroy",
     "pr_plan_workspace_bytes", "pr_plan_scratch_bytes", "pr_run", "pr_plan_iteration_ms",
     "pr_plan_kernel_ms", "pr_plan_tiles",
     "pr_plan_buckets", "pr_plan_num_buckets", "pr_plan_layout", "pr_status_string",

@@ -26,6 +26,7 @@ PR_VALIDATE = 0x1
 PR_PLAN_BUCKETED = 0x2
 PR_X0_GIVEN = 0x1
 PR_RECORD_EVENTS = 0x2
+PR_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class PrError(RuntimeError):
@@ -40,6 +41,8 @@ _SIGNATURES = {
     "pr_transpose_workspace_bytes": (_c.c_size_t, [_c.c_int32, _c.c_int64]),
     "pr_transpose": (_c.c_int, [_c.c_int32, _c.c_int64, _vp, _vp, _vp, _vp, _vp, _c.c_size_t,
                                 _c.c_uint32, _vp]),
+    "pr_transpose_noalloc": (_c.c_int, [_c.c_int32, _c.c_int64, _vp, _vp, _vp, _vp, _c.c_uint32,
+                                        _vp]),
     "pr_plan_workspace_bytes": (_c.c_size_t, [_c.c_int32, _c.c_int64]),
     "pr_plan_scratch_bytes": (_c.c_size_t, [_c.c_int32, _c.c_int64]),
     "pr_plan_create": (_c.c_int, [_c.POINTER(_vp), _c.c_int32, _c.c_int64, _vp, _vp, _vp,
@@ -132,6 +135,13 @@ def pr_transpose(n, nnz, out_row_ptr, out_col_idx, in_row_ptr, in_col_idx, ws, f
                  stream=None) -> None:
     _check(lib().pr_transpose(n, nnz, _ptr(out_row_ptr), _ptr(out_col_idx), _ptr(in_row_ptr),
                               _ptr(in_col_idx), _ptr(ws), _nbytes(ws), flags, _stream(stream)))
+
+
+def pr_transpose_noalloc(n, nnz, out_row_ptr, out_col_idx, in_row_ptr, in_col_idx, flags=0,
+                         stream=None) -> None:
+    _check(lib().pr_transpose_noalloc(n, nnz, _ptr(out_row_ptr), _ptr(out_col_idx),
+                                      _ptr(in_row_ptr), _ptr(in_col_idx), flags,
+                                      _stream(stream)))
 
 
 def pr_plan_workspace_bytes(n: int, nnz: int) -> int:

@@ -10,6 +10,9 @@
 // first position whose sorted target is >= v, read off the boundaries of the
 // sorted targets (a per-vertex histogram with atomics would serialize on the
 // hub vertices).
+#include <atomic>
+#include <mutex>
+
 #include "transpose.hpp"
 
 namespace pr {
@@ -191,4 +194,63 @@ extern "C" int pr_transpose(int32_t n, int64_t nnz, const int32_t* out_row_ptr,
     PR_TRY(transpose_device(n, nnz, out_row_ptr, out_col_idx, in_row_ptr, in_col_idx, w, stream));
     if (validate) PR_TRY(read_error_word(w.error, stream, "pr_transpose"));
     return PR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// pr_transpose_noalloc: pr_transpose with its workspace in a device array of
+// the library's own, for callers that cannot allocate.
+//
+// `scratch` is a file-scope device array: every device the library runs on
+// holds its own copy until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in, not a device
+// address); the device address comes from hipGetSymbolAddress, once per
+// device, with that device current, and is kept per device.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[PR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The current device's copy of `scratch` (its address looked up on the first
+// call on that device).
+int scratch_on_current_device(void** out) {
+    int dev = -1;
+    PR_HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PR_ERR_ARG, "device %d is beyond the %d devices the library tracks", dev,
+                    kMaxDevices);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            PR_HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+            if (!p) return fail(PR_ERR_HIP, "no device address for the library's scratch array");
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return PR_OK;
+}
+
+}  // namespace
+
+extern "C" int pr_transpose_noalloc(int32_t n, int64_t nnz, const int32_t* out_row_ptr,
+                                    const int32_t* out_col_idx, int32_t* in_row_ptr,
+                                    int32_t* in_col_idx, uint32_t flags, void* stream) {
+    if (n < 1) return fail(PR_ERR_ARG, "n must be >= 1 (got %d)", n);
+    if (nnz < 0 || nnz > INT32_MAX)
+        return fail(PR_ERR_ARG, "nnz must be in [0, INT32_MAX] (got %lld)", (long long)nnz);
+    const size_t need = transpose_carve(nullptr, n, nnz).bytes;
+    if (need > (size_t)PR_NOALLOC_SCRATCH_BYTES)
+        return fail(PR_ERR_WORKSPACE,
+                    "pr_transpose_noalloc: n = %d, nnz = %lld need %zu bytes of workspace, more "
+                    "than the library's %zu-byte scratch array (use pr_transpose)",
+                    n, (long long)nnz, need, (size_t)PR_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    PR_TRY(scratch_on_current_device(&ws));
+    return pr_transpose(n, nnz, out_row_ptr, out_col_idx, in_row_ptr, in_col_idx, ws,
+                        (size_t)PR_NOALLOC_SCRATCH_BYTES, flags, stream);
 }
