@@ -12,8 +12,12 @@ and duplicates removed.
 Printed (one JSON line): whole-step throughput in GTEPS (edges x iterations /
 step time); the per-iteration time and GTEPS; the gather-and-accumulate
 kernel (k_tile, timed launch by launch with events on the run's stream)
-against the HBM roofline, counting the bytes any pull iteration must move;
-and the CPU oracle's rate on a bounded sample of the same graph.
+against the HBM roofline, counting the bytes any pull iteration must move,
+beside the counter-measured traffic and Day 40's own byte model; the
+L1 < 1e-6 run; the other workloads (citation-like, 27-point stencil, R-MAT
+18 and 21, and R-MAT 23 with shuffled ids); the rerun after an edge batch;
+and the CPU oracle's rate on a bounded sample of the same graph, on one
+pinned core, with the host's CPU model and core count.
 
     python bench.py [--steps K] [--warmup W] [--workload rmat23] [--iters 50]
 """
@@ -60,6 +64,13 @@ def min_bytes_per_iteration(n: int, m: int) -> int:
     return 8 * m + 20 * n + 4
 
 
+def day40_hand_bytes(n: int, m: int) -> int:
+    """Day 40's own byte count of one iteration of its hand-written kernels
+    ("Results"): scale 12n, SpMV 8m + 8n + 4, dangling 5n, residual 8n,
+    combine 8n, i.e. 33n + 8m + 4 (3,437,470 bytes on its citation graph)."""
+    return 33 * n + 8 * m + 4
+
+
 def traffic_from_counters(n_launch_bytes: int):
     """HBM bytes per k_tile launch from the committed rocprofv3 counter
     summary, when it was taken on the current kernel and plan source."""
@@ -96,8 +107,9 @@ def cpu_traversal_baseline(g) -> dict:
     """The oracle's breadth-first search from vertex 0 and weak components on
     the same graph, single-threaded, search loops only."""
     import oracle
-    ref = oracle.bfs(g.row_ptr, g.col_idx, 0)
-    _, _, wcc_secs = oracle.wcc(g.row_ptr, g.col_idx, timed=True)
+    with pinned_to_one_core():
+        ref = oracle.bfs(g.row_ptr, g.col_idx, 0)
+        _, _, wcc_secs = oracle.wcc(g.row_ptr, g.col_idx, timed=True)
     return {"bfs_ms": round(ref.loop_seconds * 1e3, 2),
             "bfs_gteps": round(ref.edges_scanned / ref.loop_seconds / 1e9, 4),
             "wcc_ms": round(wcc_secs * 1e3, 2), "wcc_gteps": round(g.m / wcc_secs / 1e9, 4),
@@ -110,18 +122,75 @@ def cpu_spmv_baseline(graphgen, nx: int) -> dict:
     import oracle
     A = graphgen.stencil_matrix(nx, values="random", seed=5)
     x = graphgen.uniform(A.n_cols, 6)
-    _, secs = oracle.spmv(A.row_ptr, A.col_idx, A.vals, x, A.n_cols, timed=True)
+    with pinned_to_one_core():
+        _, secs = oracle.spmv(A.row_ptr, A.col_idx, A.vals, x, A.n_cols, timed=True)
     return {"ms": round(secs * 1e3, 2), "gflops": round(2 * A.nnz / secs / 1e9, 3), "cores": 1}
+
+
+def host_info() -> dict:
+    """The host the CPU baseline runs on: CPU model, logical CPUs, and the
+    CPUs this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = sorted(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = []
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": _ranges(allowed)}
+
+
+def _ranges(cpus) -> str:
+    out, i = [], 0
+    while i < len(cpus):
+        j = i
+        while j + 1 < len(cpus) and cpus[j + 1] == cpus[j] + 1:
+            j += 1
+        out.append(f"{cpus[i]}" if i == j else f"{cpus[i]}-{cpus[j]}")
+        i = j + 1
+    return ",".join(out)
+
+
+class pinned_to_one_core:
+    """Run the calling thread on one CPU (the last one it may use), then
+    restore its affinity.  The oracle runs in this thread through ctypes, so
+    it is pinned too."""
+
+    def __enter__(self):
+        self.before = None
+        self.core = None
+        try:
+            self.before = os.sched_getaffinity(0)
+            self.core = max(self.before)
+            os.sched_setaffinity(0, {self.core})
+        except (AttributeError, OSError):
+            pass
+        return self
+
+    def __exit__(self, *exc):
+        if self.before is not None:
+            os.sched_setaffinity(0, self.before)
+        return False
 
 
 def cpu_baseline(g, iters: int) -> dict:
     import oracle
-    r = oracle.pagerank(g.row_ptr, g.col_idx, d=0.85, tol=0.0, max_iter=iters)
+    with pinned_to_one_core() as pin:
+        r = oracle.pagerank(g.row_ptr, g.col_idx, d=0.85, tol=0.0, max_iter=iters)
     secs = r.loop_seconds
     return {"value": round(g.m * iters / secs / 1e9, 4), "unit": "GTEPS", "cores": 1,
             "kind": "oracle",
             "sample": f"{iters} of the 50 iterations on the same {g.name} graph "
-                      f"(fp64, single thread, iteration loop only: {secs:.2f} s)"}
+                      f"(fp64, single thread pinned to CPU {pin.core}, iteration loop only: "
+                      f"{secs:.2f} s)",
+            "ms_per_iteration": round(secs * 1e3 / iters, 2), "pinned_cpu": pin.core,
+            "host": host_info()}
 
 
 def spmv_min_bytes(n_rows: int, n_cols: int, nnz: int) -> int:
@@ -232,12 +301,22 @@ def traversal_rates(torch, prx, g, dg, reps: int = 5) -> dict:
 
 
 def workload_rate(torch, prx, graphgen, name: str, iters: int) -> dict:
-    """Per-iteration rate of one more workload: a plan, one warm-up run, then
-    `iters` timed iterations (median of 3 runs) and the gather kernel's mean
-    launch time against the same roofline."""
+    """Per-iteration rate of one more workload: a plan (timed), one warm-up
+    run, then `iters` timed iterations (median of 3 runs) and the gather
+    kernel's mean launch time against the same roofline."""
+    t0 = time.time()
     g = graphgen.workload(name)
+    log(f"{name}: n={g.n} m={g.m} generated in {time.time() - t0:.1f}s")
     dg = prx.DeviceGraph.from_csr(g.row_ptr, g.col_idx)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    prx.Plan(dg).close()  # warm-up plan
+    torch.cuda.synchronize()
+    e0.record(stream)
     plan = prx.Plan(dg)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    plan_ms = e0.elapsed_time(e1)
     plan.run(max_iter=3)
     its, kms = [], []
     for _ in range(3):
@@ -247,10 +326,69 @@ def workload_rate(torch, prx, graphgen, name: str, iters: int) -> dict:
     plan.close()
     it, km = statistics.median(its), statistics.median(kms)
     b = min_bytes_per_iteration(g.n, g.m)
-    return {"n": g.n, "m": g.m, "iteration_ms": round(it, 5),
+    hb = day40_hand_bytes(g.n, g.m)
+    cached = b < 256e6
+    return {"n": g.n, "m": g.m, "plan_ms": round(plan_ms, 4), "iteration_ms": round(it, 5),
             "gteps": round(g.m / (it * 1e-3) / 1e9, 2), "kernel_ms": round(km, 5),
             "roofline_frac": round(b / (km * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "iteration_frac": round(b / (it * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            "iteration_frac": round(b / (it * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "day40_model_frac": round(hb / (it * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "note": ("working set fits the 256 MB Infinity Cache: not an HBM point" if cached
+                     else "working set exceeds the Infinity Cache")}
+
+
+def incremental_rate(torch, prx, graphgen, g, dg, iters_cap: int = 200, tol: float = 1e-6) -> dict:
+    """The rerun after an edge batch (Meerkat's incremental/decremental
+    PageRank): ranks of G to tol, then a seeded batch (m/256 deletions of
+    existing edges and m/256 R-MAT insertion draws) gives G', which is
+    re-planned and iterated to tol twice: from G's ranks (warm) and from 1/n
+    (cold).  The batch is applied on the host and G' uploaded before anything
+    is timed."""
+    stream = torch.cuda.current_stream()
+    plan = prx.Plan(dg)
+    before = plan.run(tol=tol, max_iter=iters_cap)
+    x_g = before.x.clone()
+    plan.close()
+    del plan
+    t0 = time.time()
+    dele, u, v = graphgen.edge_batch(g, g.m // 256, g.m // 256, seed=256)
+    g2 = graphgen.apply_batch(g, dele, u, v)
+    log(f"edge batch: -{dele.size} / +{u.size} draws, m {g.m} -> {g2.m} ({time.time() - t0:.1f}s)")
+    dg2 = prx.DeviceGraph.from_csr(g2.row_ptr, g2.col_idx)
+    ws = torch.empty(prx.pr_plan_workspace_bytes(g2.n, g2.m), dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(prx.pr_plan_scratch_bytes(g2.n, g2.m), dtype=torch.uint8, device="cuda")
+    x = torch.empty(g2.n, dtype=torch.float32, device="cuda")
+    l1 = torch.empty(iters_cap, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    replans = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        h = prx.pr_plan_create(g2.n, g2.m, dg2.row_ptr, dg2.col_idx, ws, scratch, 0, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        replans.append(e0.elapsed_time(e1))
+        prx.pr_plan_destroy(h)
+    h = prx.pr_plan_create(g2.n, g2.m, dg2.row_ptr, dg2.col_idx, ws, scratch, 0, stream)
+
+    def run(warm: bool):
+        if warm:
+            x.copy_(x_g)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        it = prx.pr_run(h, 0.85, tol, iters_cap, x, l1, None,
+                        prx.PR_X0_GIVEN if warm else 0, stream)
+        torch.cuda.synchronize()
+        return it, (time.perf_counter() - t) * 1e3
+
+    run(True)
+    it_warm, ms_warm = run(True)
+    it_cold, ms_cold = run(False)
+    prx.pr_plan_destroy(h)
+    return {"graph": g.name, "batch_delete": int(dele.size), "batch_insert_draws": int(u.size),
+            "m_before": g.m, "m_after": g2.m, "tol": tol, "iters_before": before.iterations,
+            "replan_ms": round(statistics.median(replans), 4), "iters_warm": it_warm,
+            "warm_ms": round(ms_warm, 3), "iters_cold": it_cold, "cold_ms": round(ms_cold, 3)}
 
 
 def main() -> int:
@@ -260,7 +398,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="rmat23")
     ap.add_argument("--iters", type=int, default=50)
-    ap.add_argument("--cpu-iters", type=int, default=8,
+    ap.add_argument("--cpu-iters", type=int, default=12,
                     help="iterations of the CPU oracle sample (0 skips it)")
     ap.add_argument("--no-copy-row", action="store_true")
     ap.add_argument("--spmv-grid", type=int, default=100,
@@ -269,9 +407,12 @@ def main() -> int:
     ap.add_argument("--traversal", default="rmat23,grid1024",
                     help="graphs on which BFS from vertex 0 and weak components are timed "
                          "(the main workload's graph is reused when named; empty skips)")
-    ap.add_argument("--workloads", default="",
-                    help="comma-separated extra workloads (e.g. citation,stencil100,rmat18,rmat21) "
-                         "whose per-iteration rate is added under 'workloads'")
+    ap.add_argument("--workloads", default="citation,stencil100,rmat18,rmat21,rmat23r",
+                    help="comma-separated extra workloads whose plan time and per-iteration "
+                         "rate are added under 'workloads' (rmat23r: R-MAT 23 with seeded "
+                         "shuffled ids; empty skips)")
+    ap.add_argument("--no-incremental", action="store_true",
+                    help="skip the rerun after an edge batch")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -375,6 +516,12 @@ def main() -> int:
     torch.cuda.empty_cache()
     copy_gbps = None if args.no_copy_row else round(copy_row(torch), 1)
 
+    incremental = None
+    if not args.no_incremental:
+        incremental = incremental_rate(torch, prx, graphgen, g, dg)
+        log(f"incremental: {incremental}")
+        torch.cuda.empty_cache()
+
     extra = {}
     for name in [w for w in args.workloads.split(",") if w]:
         extra[name] = workload_rate(torch, prx, graphgen, name, args.iters)
@@ -440,7 +587,24 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": MAIN_KERNEL,
-                     "launch_ms": round(kernel_ms, 5)},
+                     "launch_ms": round(kernel_ms, 5),
+                     "achieved_basis": "algorithmic: B_min = 8m + 20n + 4 bytes (what any pull "
+                                       "iteration must move) per launch / launch time",
+                     "counter_gbps": (round(traffic / (kernel_ms * 1e-3) / 1e9, 1)
+                                      if traffic else None),
+                     "counter_frac": (round(traffic / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+                                      if traffic else None),
+                     "iteration_frac": round(bytes_iter / (iter_ms * 1e-3) / 1e9
+                                             / HBM_PEAK_GBPS, 4)},
+        "byte_models": {"b_min": bytes_iter, "b_min_frac_iteration":
+                        round(bytes_iter / (iter_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "day40_hand_model": day40_hand_bytes(n, m),
+                        "day40_hand_model_frac_iteration":
+                        round(day40_hand_bytes(n, m) / (iter_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "note": "Day 40 counts 33n + 8m + 4 bytes per iteration of its "
+                                "five-kernel design; B_min = 8m + 20n + 4 is the pull "
+                                "minimum; counter traffic is what the L2s exchanged with "
+                                "the fabric per gather launch"},
         "copy_row_gbps": copy_gbps,
         "buckets": buckets,
         "cpu_baseline": cpu,
@@ -451,6 +615,8 @@ def main() -> int:
         out["traversal"] = trav
     if extra:
         out["workloads"] = extra
+    if incremental:
+        out["incremental"] = incremental
     print(json.dumps(out), flush=True)
     return 0
 

@@ -73,6 +73,14 @@ def _lib() -> ctypes.CDLL:
                                 p32, p32, pm]
     for f in (lib.gg_rmat, lib.gg_stencil27, lib.gg_citation):
         f.restype = ctypes.c_int
+    i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    lib.gg_rmat_edges.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                  ctypes.c_uint64, ctypes.c_int64, ctypes.c_int64, i32p, i32p]
+    lib.gg_relabel.argtypes = [ctypes.c_int32, i32p, i32p, i32p, p32, p32, pm]
+    lib.gg_edit.argtypes = [ctypes.c_int32, i32p, i32p, ctypes.c_int64, i64p, ctypes.c_int64,
+                            i32p, i32p, p32, p32, pm]
+    for f in (lib.gg_rmat_edges, lib.gg_relabel, lib.gg_edit):
+        f.restype = ctypes.c_int
     lib.gg_free.argtypes = [ctypes.c_void_p]
     lib.gg_free.restype = None
     lib.gg_draw_u64.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
@@ -368,8 +376,87 @@ def matrix_of_graph(g: Graph, seed: int) -> Matrix:
     return Matrix(f"{g.name}_valued", g.row_ptr, g.col_idx, uniform(g.m, seed), g.n)
 
 
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def relabel(g: Graph, seed: int, name: str | None = None) -> Graph:
+    """The same graph with its vertex ids shuffled by a seeded permutation:
+    vertex v becomes perm[v], where perm sorts the vertices by their
+    SplitMix64 draw (ties by id).  Kills whatever locality the generator's
+    ids carry (R-MAT's hot vertices sit at ids with few one bits)."""
+    perm = relabel_permutation(g.n, seed)
+    rp, ci, m = (ctypes.POINTER(ctypes.c_int32)(), ctypes.POINTER(ctypes.c_int32)(),
+                 ctypes.c_int64())
+    rc = _lib().gg_relabel(g.n, _i32p(g.row_ptr), _i32p(g.col_idx), _i32p(perm),
+                           ctypes.byref(rp), ctypes.byref(ci), ctypes.byref(m))
+    return _take(name or f"{g.name}_relabelled", rc, rp, ci, m, g.n)
+
+
+def relabel_permutation(n: int, seed: int) -> np.ndarray:
+    keys = splitmix_u64(seed, np.arange(n, dtype=np.uint64))
+    order = np.lexsort((np.arange(n), keys))
+    perm = np.empty(n, dtype=np.int32)
+    perm[order] = np.arange(n, dtype=np.int32)
+    return perm
+
+
+def edge_batch(g: Graph, n_delete: int, n_insert: int, seed: int):
+    """A seeded batch of edge deletions and insertions: the indices (into
+    g.col_idx, ascending) of n_delete distinct existing edges, drawn
+    uniformly, and n_insert new (u, v) draws -- R-MAT draws with the
+    workload's parameters when n is a power of two, uniform pairs otherwise
+    (self-loops and edges already present are dropped when applied)."""
+    m = g.m
+    n_delete = min(n_delete, m)
+    k, picked = 0, np.zeros(0, dtype=np.int64)
+    while picked.size < n_delete:
+        want = 2 * (n_delete - picked.size) + 16
+        cand = (splitmix_u64(seed, np.arange(k, k + want, dtype=np.uint64)) %
+                np.uint64(m)).astype(np.int64)
+        k += want
+        _, first = np.unique(np.concatenate([picked, cand]), return_index=True)
+        merged = np.concatenate([picked, cand])[np.sort(first)]
+        picked = merged[:n_delete]
+    dele = np.sort(picked)
+    scale = g.n.bit_length() - 1
+    u = np.empty(n_insert, dtype=np.int32)
+    v = np.empty(n_insert, dtype=np.int32)
+    if g.n == 1 << scale and scale >= 1:
+        rc = _lib().gg_rmat_edges(scale, RMAT_ABC[0], RMAT_ABC[1], RMAT_ABC[2], seed + 1, 0,
+                                  n_insert, _i32p(u), _i32p(v))
+        if rc != 0:
+            raise ValueError(f"gg_rmat_edges failed with code {rc}")
+    else:
+        r = splitmix_u64(seed + 1, np.arange(2 * n_insert, dtype=np.uint64)) % np.uint64(g.n)
+        u[:], v[:] = r[:n_insert], r[n_insert:]
+    return dele, u, v
+
+
+def apply_batch(g: Graph, dele: np.ndarray, ins_u: np.ndarray, ins_v: np.ndarray,
+                name: str | None = None) -> Graph:
+    """g with the edges at indices `dele` (ascending) removed and the edges
+    (ins_u[i], ins_v[i]) added (no self-loops, no duplicates)."""
+    dele = np.ascontiguousarray(dele, dtype=np.int64)
+    ins_u = np.ascontiguousarray(ins_u, dtype=np.int32)
+    ins_v = np.ascontiguousarray(ins_v, dtype=np.int32)
+    rp, ci, m = (ctypes.POINTER(ctypes.c_int32)(), ctypes.POINTER(ctypes.c_int32)(),
+                 ctypes.c_int64())
+    rc = _lib().gg_edit(g.n, _i32p(g.row_ptr), _i32p(g.col_idx), dele.size,
+                        dele.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ins_u.size,
+                        _i32p(ins_u), _i32p(ins_v), ctypes.byref(rp), ctypes.byref(ci),
+                        ctypes.byref(m))
+    return _take(name or f"{g.name}_edited", rc, rp, ci, m, g.n)
+
+
+RELABEL_SEED = 2323
+
+
 def workload(name: str) -> Graph:
-    """The named benchmark workloads."""
+    """The named benchmark workloads ("rmat23r": R-MAT 23 with its vertex ids
+    shuffled by a seeded permutation)."""
+    if name.endswith("r") and name.startswith("rmat"):
+        return relabel(rmat(int(name[4:-1])), RELABEL_SEED, name=name)
     if name == "citation":
         return citation()
     if name == "stencil100":

@@ -349,3 +349,91 @@ int gg_citation(int32_t n, int32_t n_dangling, double mean_outdeg, uint64_t seed
     return GG_OK;
 }
 
+
+/* Raw R-MAT draws k0 .. k0+count-1 of stream `seed` (the same per-edge draw
+ * as gg_rmat, self-loops included): the edges of a seeded insertion batch. */
+int gg_rmat_edges(int scale, double a, double b, double c, uint64_t seed, int64_t k0,
+                  int64_t count, int32_t* u_out, int32_t* v_out) {
+    if (scale < 1 || scale > 30 || k0 < 0 || count < 0 || a < 0 || b < 0 || c < 0 ||
+        a + b + c > 1.0)
+        return GG_ERR_ARG;
+    const uint64_t key = mix64(seed);
+    const uint64_t A = threshold53(a), AB = threshold53(a + b), ABC = threshold53(a + b + c);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        rmat_edge(key, scale, (uint64_t)(k0 + i), A, AB, ABC, &u_out[i], &v_out[i]);
+    return GG_OK;
+}
+
+/* The graph with every vertex v renamed perm[v] (perm a permutation of
+ * [0, n)): row perm[u] holds perm[v] for every edge (u, v), sorted. */
+int gg_relabel(int32_t n, const int32_t* rp, const int32_t* ci, const int32_t* perm,
+               int32_t** rp_out, int32_t** ci_out, int64_t* m_out) {
+    if (n < 1) return GG_ERR_ARG;
+    int64_t* raw_rp = (int64_t*)malloc(sizeof(int64_t) * ((size_t)n + 1));
+    int32_t* inv = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    const int64_t m = rp[n];
+    int32_t* raw_ci = (int32_t*)malloc(sizeof(int32_t) * (size_t)(m > 0 ? m : 1));
+    if (!raw_rp || !inv || !raw_ci) { free(raw_rp); free(inv); free(raw_ci); return GG_ERR_NOMEM; }
+    for (int32_t u = 0; u < n; ++u) {
+        if (perm[u] < 0 || perm[u] >= n) { free(raw_rp); free(inv); free(raw_ci); return GG_ERR_ARG; }
+        inv[perm[u]] = u;
+    }
+    int64_t acc = 0;
+    for (int32_t p = 0; p < n; ++p) {
+        raw_rp[p] = acc;
+        acc += rp[inv[p] + 1] - rp[inv[p]];
+    }
+    raw_rp[n] = acc;
+#pragma omp parallel for schedule(dynamic, 1024)
+    for (int32_t p = 0; p < n; ++p) {
+        const int32_t u = inv[p];
+        for (int64_t j = rp[u]; j < rp[u + 1]; ++j) raw_ci[raw_rp[p] + (j - rp[u])] = perm[ci[j]];
+    }
+    free(inv);
+    return finish_csr(n, raw_rp, raw_ci, rp_out, ci_out, m_out);
+}
+
+/* The graph after an edge batch: the edges whose indices are listed in
+ * del_idx (ascending, each in [0, m)) removed, then the n_ins edges
+ * (ins_u[i], ins_v[i]) added; self-loops and edges already present are not
+ * added twice.  Rows come out sorted. */
+int gg_edit(int32_t n, const int32_t* rp, const int32_t* ci, int64_t n_del, const int64_t* del_idx,
+            int64_t n_ins, const int32_t* ins_u, const int32_t* ins_v, int32_t** rp_out,
+            int32_t** ci_out, int64_t* m_out) {
+    if (n < 1 || n_del < 0 || n_ins < 0) return GG_ERR_ARG;
+    const int64_t m = rp[n];
+    for (int64_t i = 0; i < n_del; ++i)
+        if (del_idx[i] < 0 || del_idx[i] >= m || (i > 0 && del_idx[i] <= del_idx[i - 1]))
+            return GG_ERR_ARG;
+    for (int64_t i = 0; i < n_ins; ++i)
+        if (ins_u[i] < 0 || ins_u[i] >= n || ins_v[i] < 0 || ins_v[i] >= n) return GG_ERR_ARG;
+    int64_t* raw_rp = (int64_t*)calloc((size_t)n + 1, sizeof(int64_t));
+    int64_t* cur = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
+    if (!raw_rp || !cur) { free(raw_rp); free(cur); return GG_ERR_NOMEM; }
+    /* kept out-degrees plus inserted ones */
+    int64_t d = 0;
+    for (int32_t u = 0; u < n; ++u) {
+        int64_t keep = rp[u + 1] - rp[u];
+        while (d < n_del && del_idx[d] < rp[u + 1]) { --keep; ++d; }
+        raw_rp[u + 1] = keep;
+    }
+    for (int64_t i = 0; i < n_ins; ++i)
+        if (ins_u[i] != ins_v[i]) raw_rp[ins_u[i] + 1]++;
+    for (int32_t u = 0; u < n; ++u) raw_rp[u + 1] += raw_rp[u];
+    const int64_t raw_m = raw_rp[n];
+    int32_t* raw_ci = (int32_t*)malloc(sizeof(int32_t) * (size_t)(raw_m > 0 ? raw_m : 1));
+    if (!raw_ci) { free(raw_rp); free(cur); return GG_ERR_NOMEM; }
+    d = 0;
+    for (int32_t u = 0; u < n; ++u) {
+        cur[u] = raw_rp[u];
+        for (int64_t j = rp[u]; j < rp[u + 1]; ++j) {
+            if (d < n_del && del_idx[d] == j) { ++d; continue; }
+            raw_ci[cur[u]++] = ci[j];
+        }
+    }
+    for (int64_t i = 0; i < n_ins; ++i)
+        if (ins_u[i] != ins_v[i]) raw_ci[cur[ins_u[i]]++] = ins_v[i];
+    free(cur);
+    return finish_csr(n, raw_rp, raw_ci, rp_out, ci_out, m_out);
+}

@@ -33,6 +33,8 @@
 // x in (k_init) and out (k_finish).  contrib is double-buffered across
 // iterations (rows read other rows' contrib); x is updated in place (only row
 // v's owner touches x[v]).
+#include <cstdlib>
+
 #include "plan.hpp"
 
 namespace pr {
@@ -916,7 +918,11 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         PR_LAUNCHED("init finalize");
     }
     int32_t tilefix_grid = (int32_t)((p->n_fix_rows + kFixBlock - 1) / kFixBlock);
-    const bool wide_rounds = p->n_units > 0 && p->n_slots >= kWideUnitSlots * (int64_t)p->n_units;
+    bool wide_rounds = p->n_units > 0 && p->n_slots >= kWideUnitSlots * (int64_t)p->n_units;
+    if (const char* env = std::getenv("PR_TILE_Q")) {  // tuning knob: edge blocks per round
+        if (std::atoi(env) == 1) wide_rounds = false;
+        if (std::atoi(env) == 2) wide_rounds = true;
+    }
     if (tilefix_grid > kMaxGrid) tilefix_grid = kMaxGrid;
     const int32_t iter_parts = p->tiled ? p->n_units + tilefix_grid : p->n_batches + p->fix_grid;
     f.parts = iter_parts;

@@ -111,3 +111,40 @@ def test_from_edges_dedup_and_order():
     assert g.col_idx.tolist() == [1, 2, 0, 1]
     with pytest.raises(ValueError):
         graphgen.from_edges(2, [0], [2])
+
+
+def test_relabel_is_the_same_graph_under_the_permutation():
+    g = graphgen.rmat(11)
+    r = graphgen.relabel(g, 31)
+    perm = graphgen.relabel_permutation(g.n, 31)
+    assert sorted(perm.tolist()) == list(range(g.n))
+    src, dst = g.edges()
+    s2, d2 = r.edges()
+    assert r.m == g.m
+    assert set(zip(perm[src].tolist(), perm[dst].tolist())) == set(zip(s2.tolist(), d2.tolist()))
+    # rows sorted, no duplicates
+    for u in range(r.n):
+        row = r.col_idx[r.row_ptr[u]:r.row_ptr[u + 1]]
+        assert np.all(np.diff(row) > 0)
+
+
+def test_edge_batch_applies_deletions_and_insertions():
+    g = graphgen.rmat(10)
+    dele, u, v = graphgen.edge_batch(g, 300, 500, seed=4)
+    assert dele.size == 300 and np.all(np.diff(dele) > 0) and dele.max() < g.m
+    assert u.size == 500 and u.max() < g.n and v.max() < g.n
+    h = graphgen.apply_batch(g, dele, u, v)
+    src, dst = g.edges()
+    keep = np.ones(g.m, bool)
+    keep[dele] = False
+    want = set(zip(src[keep].tolist(), dst[keep].tolist()))
+    want |= {(a, b) for a, b in zip(u.tolist(), v.tolist()) if a != b}
+    s2, d2 = h.edges()
+    assert set(zip(s2.tolist(), d2.tolist())) == want and h.m == len(want)
+    # deterministic
+    d_again, u_again, v_again = graphgen.edge_batch(g, 300, 500, seed=4)
+    assert np.array_equal(dele, d_again) and np.array_equal(u, u_again)
+    # a batch with nothing in it leaves the graph as it was
+    same = graphgen.apply_batch(g, np.zeros(0, np.int64), np.zeros(0, np.int32),
+                                np.zeros(0, np.int32))
+    assert np.array_equal(same.row_ptr, g.row_ptr) and np.array_equal(same.col_idx, g.col_idx)
