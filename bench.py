@@ -450,6 +450,7 @@ def main() -> int:
         ev[2].record(stream)
         iter_ms = prx.pr_plan_iteration_ms(plan)  # waits for the last iteration
         kernel_ms, _ = prx.pr_plan_kernel_ms(plan)
+        ev[2].synchronize()  # the step ends when its ranks are back in the caller's order
         prx.pr_plan_destroy(plan)
         return it, iter_ms, kernel_ms
 

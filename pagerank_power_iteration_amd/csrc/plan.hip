@@ -23,13 +23,91 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <utility>
 #include <vector>
 
 #include "plan.hpp"
 #include "transpose.hpp"
 
+
 namespace pr {
+
+// ------------------------------------------------------- host resources
+//
+// One pool of PlanHost records per process, each record tied to the device it
+// was made on.  Records are created on demand and never freed: there are at
+// most as many as plans that were alive at the same time.
+namespace {
+std::mutex g_pool_mutex;
+PlanHost* g_pool = nullptr;
+constexpr size_t kStageInitial = 1u << 20;
+}  // namespace
+
+int host_stage(PlanHost* h, size_t bytes) {
+    if (h->stage_bytes >= bytes) return PR_OK;
+    size_t cap = h->stage_bytes ? h->stage_bytes : kStageInitial;
+    while (cap < bytes) cap *= 2;
+    if (h->stage) PR_HIP_TRY(hipHostFree(h->stage));
+    h->stage = nullptr;
+    h->stage_bytes = 0;
+    // non-coherent: cached on the host side, which reads the read-backs many
+    // times (every copy through it is waited for before the host touches it)
+    PR_HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&h->stage), cap, hipHostMallocNonCoherent));
+    h->stage_bytes = cap;
+    return PR_OK;
+}
+
+int host_take(PlanHost** out) {
+    *out = nullptr;
+    int dev = 0;
+    PR_HIP_TRY(hipGetDevice(&dev));
+    {
+        std::lock_guard<std::mutex> lock(g_pool_mutex);
+        for (PlanHost** pp = &g_pool; *pp; pp = &(*pp)->next) {
+            if ((*pp)->device == dev) {
+                *out = *pp;
+                *pp = (*pp)->next;
+                (*out)->next = nullptr;
+                return PR_OK;
+            }
+        }
+    }
+    PlanHost* h = static_cast<PlanHost*>(std::calloc(1, sizeof(PlanHost)));
+    if (!h) return fail(PR_ERR_ARG, "out of host memory");
+    h->device = dev;
+    hipError_t e = hipEventCreate(&h->ev_begin);
+    if (e == hipSuccess) e = hipEventCreate(&h->ev_end);
+    for (int i = 0; i < 2 * kTimedLaunches && e == hipSuccess; ++i)
+        e = hipEventCreate(&h->kernel_ev[i / kTimedLaunches][i % kTimedLaunches]);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->chunk_ev[0], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->chunk_ev[1], hipEventDisableTiming);
+    if (e == hipSuccess)
+        e = hipHostMalloc(reinterpret_cast<void**>(&h->status), 2 * sizeof(RunStatus),
+                          hipHostMallocDefault);
+    if (e != hipSuccess) {
+        const int rc = fail(PR_ERR_HIP, "plan events / pinned status: %s", hipGetErrorString(e));
+        if (h->ev_begin) (void)hipEventDestroy(h->ev_begin);
+        if (h->ev_end) (void)hipEventDestroy(h->ev_end);
+        for (int i = 0; i < 2 * kTimedLaunches; ++i)
+            if (h->kernel_ev[i / kTimedLaunches][i % kTimedLaunches])
+                (void)hipEventDestroy(h->kernel_ev[i / kTimedLaunches][i % kTimedLaunches]);
+        for (int i = 0; i < 2; ++i)
+            if (h->chunk_ev[i]) (void)hipEventDestroy(h->chunk_ev[i]);
+        if (h->status) (void)hipHostFree(h->status);
+        std::free(h);
+        return rc;
+    }
+    *out = h;
+    return host_stage(h, kStageInitial);
+}
+
+void host_give(PlanHost* h) {
+    if (!h) return;
+    std::lock_guard<std::mutex> lock(g_pool_mutex);
+    h->next = g_pool;
+    g_pool = h;
+}
 
 namespace {
 
@@ -88,7 +166,8 @@ struct PlanScratch {  // needed only while pr_plan_create runs
     int32_t* perm_rp;    // [n + 1]
     int32_t* perm_ci;    // [nnz]
     int32_t* src_of;     // [nnz] source (plan id) of each edge of perm_ci
-    int32_t* order;      // [nnz] tiled: sources sorted by tile, then sector counts
+    uint32_t* in_rp_plan;  // [n + 1] tiled: in-degrees in plan order, scanned
+    int32_t* order;      // [nnz] tiled: sources sorted by tile
     int32_t* tile_first; // [max_tiles + 1] tiled: first sorted edge of each tile
     int32_t* count_chunks;  // [4 * kMaxCountChunks + 1] in-degree counting work list, its length last
     unsigned long long* stats;  // [2 * kNumBuckets]: rows, edges per bucket
@@ -156,6 +235,7 @@ PlanScratch carve_scratch(void* base, int32_t n, int64_t nnz) {
     s.perm_rp = c.take<int32_t>((size_t)n + 1);
     s.perm_ci = c.take<int32_t>((size_t)nnz);
     s.src_of = c.take<int32_t>((size_t)nnz);
+    s.in_rp_plan = c.take<uint32_t>((size_t)n + 1);
     s.order = c.take<int32_t>((size_t)nnz);
     s.tile_first = c.take<int32_t>((size_t)max_tiles(n) + 1);
     s.count_chunks = c.take<int32_t>((size_t)4 * kMaxCountChunks + 1);
@@ -272,6 +352,106 @@ __global__ __launch_bounds__(kCountBlock) void k_count_buckets(const uint16_t* _
     }
 }
 
+// The partition of the targets by their top 8 bits for the count: only the
+// number of keys per target matters, so the order inside a digit's range is
+// free.  A 1024-lane workgroup takes kPartTiles consecutive histogram tiles
+// (16,384 keys, 16 consecutive keys per lane) and writes each digit's keys of
+// all of them as one run, starting where the scanned histogram puts the
+// first tile's: runs four times longer than a stable pass over single tiles
+// writes, so whole cache lines go out.  A lane adds each run of equal
+// digits among its keys once (a CSR row lists its targets in increasing
+// order, so neighbouring keys share their top bits): first to count, then,
+// with the returned offset, to place the run in LDS.  Keys are written as
+// their low 16 bits.  Out-of-range targets are clamped and flagged as the
+// histogram pass does.
+constexpr int kPartBlock = 1024;
+constexpr int kPartItems = 16;
+constexpr int kPartTiles = kPartBlock * kPartItems / kRadixTile;
+static_assert(kPartTiles * kRadixTile == kPartBlock * kPartItems, "whole histogram tiles");
+
+__global__ __launch_bounds__(kPartBlock) void k_count_partition(RadixIn in, int shift, int64_t T,
+                                                                const uint32_t* __restrict__ scanned,
+                                                                uint16_t* __restrict__ out) {
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+    __shared__ uint32_t cnt[kRadixDigits];
+    __shared__ uint32_t start[kRadixDigits + 1];
+    __shared__ uint32_t cursor[kRadixDigits];
+    __shared__ uint32_t gstart[kRadixDigits];
+    __shared__ int32_t stage[kPartBlock * kPartItems];
+    __shared__ uint32_t scan_tmp[kPartBlock / kWave + 1];
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * kPartTiles;
+    const int64_t base = t0 * kRadixTile;
+    const int count = (int)((in.count - base) < kPartBlock * kPartItems ? (in.count - base)
+                                                                         : kPartBlock * kPartItems);
+    if (tid < kRadixDigits) {
+        cnt[tid] = 0u;
+        cursor[tid] = 0u;
+        // digit tid's keys of tiles [t0, t0 + kPartTiles) start here
+        gstart[tid] = scanned[(int64_t)tid * T + t0];
+    }
+    const int i0 = tid * kPartItems;
+    const int left = count - i0;
+    int32_t k[kPartItems];
+    if (left >= kPartItems && (reinterpret_cast<uintptr_t>(in.keys) & 15u) == 0) {
+#pragma unroll
+        for (int q = 0; q < kPartItems / 4; ++q) {
+            const i32x4 v = *(const i32x4*)(in.keys + base + i0 + 4 * q);
+            k[4 * q] = v.x;
+            k[4 * q + 1] = v.y;
+            k[4 * q + 2] = v.z;
+            k[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < kPartItems; ++r) k[r] = r < left ? in.keys[base + i0 + r] : 0;
+    }
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < kPartItems; ++r)
+        if (r < left) k[r] = radix_check<kFromTargets>(in, k[r], bad);
+    report_bad<kFromTargets>(in, bad);
+    // each key's digit (a key past the end gets a digit of its own, so no
+    // run reaches it) and the length of the run of equal digits from it on
+    uint32_t dg[kPartItems], len[kPartItems];
+#pragma unroll
+    for (int r = 0; r < kPartItems; ++r)
+        dg[r] = r < left ? ((uint32_t)k[r] >> shift) & (kRadixDigits - 1) : kRadixDigits + r;
+#pragma unroll
+    for (int r = kPartItems - 1; r >= 0; --r)
+        len[r] = (r + 1 < kPartItems && dg[r + 1] == dg[r]) ? len[r + 1] + 1 : 1u;
+    __syncthreads();  // counters cleared
+#pragma unroll
+    for (int r = 0; r < kPartItems; ++r)
+        if (r < left && (r == 0 || dg[r - 1] != dg[r])) atomicAdd(&cnt[dg[r]], len[r]);
+    __syncthreads();
+    {  // digit starts inside the workgroup's keys
+        uint32_t total;
+        const uint32_t c = tid < kRadixDigits ? cnt[tid] : 0u;
+        const uint32_t e = block_exclusive_scan<uint32_t, kPartBlock / kWave>(c, &total, scan_tmp);
+        if (tid < kRadixDigits) start[tid] = e;
+        if (tid == 0) start[kRadixDigits] = total;
+    }
+    __syncthreads();
+    {  // the head of each run takes the run's places at once
+        uint32_t pos = 0;
+#pragma unroll
+        for (int r = 0; r < kPartItems; ++r) {
+            if (r < left) {
+                const bool head = r == 0 || dg[r - 1] != dg[r];
+                pos = head ? start[dg[r]] + atomicAdd(&cursor[dg[r]], len[r]) : pos + 1;
+                stage[pos] = k[r];
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < count; i += kPartBlock) {
+        const int32_t key = stage[i];
+        const uint32_t dg = ((uint32_t)key >> shift) & (kRadixDigits - 1);
+        out[(int64_t)gstart[dg] + (i - start[dg])] = (uint16_t)key;
+    }
+}
+
 // in_rp[0..n] of the transpose of (n, nnz, out_ci).  counts: n words of
 // scratch; chunks: 4 * kMaxCountChunks + 1 words; scan_ws: a scan workspace
 // for n items.  Out-of-range targets are clamped and flagged in tr.error.
@@ -294,9 +474,9 @@ int indegree_row_ptr(int32_t n, int64_t nnz, const int32_t* out_ci, int32_t* in_
     PR_LAUNCHED("radix histogram");
     PR_TRY(scan_exclusive(w.hist, w.scanned, kRadixDigits * T, w.scan_ws, stream));
     // the keys' low 16 bits are enough: a bucket spans at most 2^15 vertices
-    k_radix_scatter<kFromTargets, false, true><<<dim3((unsigned)T), kBlock, 0, stream>>>(
-        in, shift, T, w.scanned, w.key[0], nullptr);
-    PR_LAUNCHED("radix scatter");
+    k_count_partition<<<dim3((unsigned)ceil_div(T, kPartTiles)), kPartBlock, 0, stream>>>(
+        in, shift, T, w.scanned, reinterpret_cast<uint16_t*>(w.key[0]));
+    PR_LAUNCHED("count partition");
     // chunks of at least max(nnz / 256, kMinCountChunk) keys, listed on the device
     int64_t size = ceil_div(nnz, kRadixDigits);
     if (size < kMinCountChunk) size = kMinCountChunk;
@@ -629,6 +809,17 @@ __global__ __launch_bounds__(kBlock) void k_tile_blocks(const int32_t* __restric
     }
 }
 
+// Estimated cost of each kSectorChunk-slot chunk of the tile slots: its slots
+// plus kSectorWeight per sector start counted in it (cost[c], c < chunks).
+__global__ __launch_bounds__(kBlock) void k_chunk_costs(const int32_t* __restrict__ sectors,
+                                                        int64_t slots, int32_t chunks,
+                                                        uint64_t* __restrict__ cost) {
+    GRID_STRIDE(c, chunks) {
+        const int64_t len = c + 1 < chunks ? (int64_t)kSectorChunk : slots - c * (int64_t)kSectorChunk;
+        cost[c] = (uint64_t)(len + kSectorWeight * (int64_t)sectors[c]);
+    }
+}
+
 // First p in [lo, hi) with in_rp[p] + kRowCost * p >= target (hi if none).
 __device__ __forceinline__ int32_t cost_lower_bound(const int32_t* __restrict__ in_rp, int32_t lo,
                                                     int32_t hi, int64_t target) {
@@ -688,6 +879,17 @@ void bucket_bounds(bool tiled, int32_t out[kNumBuckets]) {
 }
 
 
+// Copies `bytes` of device memory to host array `dst` through the pinned
+// stage, synchronizing `stream` (no copy may be using the stage).
+int read_back(PlanHost* h, void* dst, const void* src, size_t bytes, hipStream_t stream) {
+    if (bytes == 0) return PR_OK;
+    PR_TRY(host_stage(h, bytes));
+    PR_HIP_TRY(hipMemcpyAsync(h->stage, src, bytes, hipMemcpyDeviceToHost, stream));
+    PR_HIP_TRY(hipStreamSynchronize(stream));
+    std::memcpy(dst, h->stage, bytes);
+    return PR_OK;
+}
+
 // What a mode's builder reports back to pr_plan_create.
 struct Built {
     int32_t n_items = 0, n_chunk_rows = 0, grid = 1, fix_grid = 0;
@@ -703,21 +905,25 @@ struct Built {
     std::vector<TileFix> fixes;
     std::vector<int32_t> fix_rows;
     std::vector<int32_t> fix_win;
+    // tiled: where the work lists were uploaded
+    const Tile* dev_tiles = nullptr;
+    const TileUnit* dev_units = nullptr;
+    const TileFix* dev_fixes = nullptr;
+    const int32_t* dev_fix_rows = nullptr;
+    const int32_t* dev_fix_win = nullptr;
 };
 
 // Bucketed pull: the plan's in-edge CSR (counting-sort transpose of the
 // renumbered out-edge CSR), hub rows whole or in chunks (from the hub rows'
 // lengths, read back), and every other bucket cut into row ranges of about
 // kItemCost.
-int build_bucketed(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz,
+int build_bucketed(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, PlanHost* host,
                    const unsigned long long* stats, const int32_t* row_begin, int cus,
                    hipStream_t stream, Built& bt) {
     PR_TRY(transpose_device(n, nnz, s.perm_rp, s.perm_ci, w.in_rp, w.in_ci, s.tr, stream));
     const int32_t n_hub = (int32_t)stats[kHubBucket];
     std::vector<int32_t> hub_rp((size_t)n_hub + 1);
-    PR_HIP_TRY(hipMemcpyAsync(hub_rp.data(), w.in_rp, sizeof(int32_t) * hub_rp.size(),
-                              hipMemcpyDeviceToHost, stream));
-    PR_HIP_TRY(hipStreamSynchronize(stream));
+    PR_TRY(read_back(host, hub_rp.data(), w.in_rp, sizeof(int32_t) * hub_rp.size(), stream));
 
     std::vector<WorkItem>& hub_items = bt.hub_items;
     std::vector<ChunkRow>& chunk_rows = bt.chunk_rows;
@@ -846,18 +1052,17 @@ int lay_out_tiles(const PlanWs& w, int64_t nnz, const unsigned long long* stats,
 // histogram): the renumbered edges sorted by tile (stable, so each tile
 // keeps them in increasing source order), the tile edge arrays, and the
 // units (built on the host from the tiles' edge counts, read back).
-int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, hipStream_t stream,
-                Built& bt) {
+int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, PlanHost* host,
+                hipStream_t stream, Built& bt) {
     const int64_t grid = bt.tile_launch;
     const bool unit_env = bt.unit_cost > 0;
     int64_t unit_cost = unit_env ? bt.unit_cost : kUnitCost;
     const TileMap& map = bt.map;
     const int32_t tiles = bt.n_tiles;
 
-    // each tile's first edge: the in-edges of the rows before it (s.perm_rp
-    // is free by now and takes the scan of the in-degrees in plan order)
+    // each tile's first edge: the in-edges of the rows before it
     int32_t* first = s.tile_first;
-    uint32_t* in_rp_plan = reinterpret_cast<uint32_t*>(s.perm_rp);
+    uint32_t* in_rp_plan = s.in_rp_plan;
     PR_TRY(scan_exclusive(reinterpret_cast<const uint32_t*>(s.key), in_rp_plan, n, s.vsort.scan_ws,
                           stream));
     k_tile_first<<<grid_for((int64_t)tiles + 1, 1024), kBlock, 0, stream>>>(in_rp_plan, n, tiles, map,
@@ -888,9 +1093,7 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, h
         sorted_targets = rw.key[0];
     }
     std::vector<int32_t> tp((size_t)tiles + 1);
-    PR_HIP_TRY(hipMemcpyAsync(tp.data(), first, sizeof(int32_t) * tp.size(), hipMemcpyDeviceToHost,
-                              stream));
-    PR_HIP_TRY(hipStreamSynchronize(stream));
+    PR_TRY(read_back(host, tp.data(), first, sizeof(int32_t) * tp.size(), stream));
     if (nnz > 0) {
         const int64_t lo = tiles > kCap ? tp[(size_t)kCap] : nnz;
         if (lo < nnz) {
@@ -921,30 +1124,39 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, h
     }
     const int64_t slots = sp[(size_t)tiles];
     bt.n_slots = slots;
-    PR_HIP_TRY(hipMemcpyAsync(w.tile_ptr, sp.data(), sizeof(int32_t) * sp.size(),
-                              hipMemcpyHostToDevice, stream));
     // tile slots and sector starts per chunk of slots (s.perm_ci, scratch of
-    // the sort, is free again and takes the counts)
+    // the sort, is free again and takes the counts), then the chunks' cost
+    // prefix, scanned on the device into s.src_of (free too) and read back
+    // through the pinned stage, which first carries the slot starts up
     const int32_t chunks = (int32_t)ceil_div(slots, kSectorChunk);
-    std::vector<int32_t> sc((size_t)chunks);
+    const size_t sp_bytes = align_up(sizeof(int32_t) * sp.size());
+    PR_TRY(host_stage(host, sp_bytes + sizeof(uint64_t) * ((size_t)chunks + 1)));
+    std::memcpy(host->stage, sp.data(), sizeof(int32_t) * sp.size());
+    PR_HIP_TRY(hipMemcpyAsync(w.tile_ptr, host->stage, sizeof(int32_t) * sp.size(),
+                              hipMemcpyHostToDevice, stream));
+    const int64_t* cp = reinterpret_cast<const int64_t*>(host->stage + sp_bytes);
     if (nnz > 0) {
         int32_t* counts = s.perm_ci;
+        // chunks <= nnz / 16 + 1 (a non-empty tile pads at most 255 slots per
+        // edge), so both arrays fit the nnz words of s.src_of
+        uint64_t* cost = reinterpret_cast<uint64_t*>(s.src_of);
+        uint64_t* prefix = cost + chunks + 1;
         PR_TRY(fill_u32(reinterpret_cast<uint32_t*>(counts), 0u, chunks, stream));
         const int64_t n_blocks = slots / kEdgeBlock;
         k_tile_blocks<<<grid_for(n_blocks * kWave, 2048), kBlock, 0, stream>>>(
             sorted_targets, s.order, map, first, w.tile_ptr, tiles, n_blocks, w.tsrc, w.tdst,
             w.tblk, counts);
         PR_LAUNCHED("tile blocks");
-        PR_HIP_TRY(hipMemcpyAsync(sc.data(), counts, sizeof(int32_t) * sc.size(),
-                                  hipMemcpyDeviceToHost, stream));
+        k_chunk_costs<<<grid_for(chunks, 1024), kBlock, 0, stream>>>(counts, slots, chunks, cost);
+        PR_LAUNCHED("chunk costs");
+        PR_TRY(scan_exclusive(cost, prefix, chunks, s.tr.sort.scan_ws, stream));
+        PR_HIP_TRY(hipMemcpyAsync(host->stage + sp_bytes, prefix,
+                                  sizeof(uint64_t) * ((size_t)chunks + 1), hipMemcpyDeviceToHost,
+                                  stream));
+    } else {
+        std::memset(host->stage + sp_bytes, 0, sizeof(uint64_t));
     }
     PR_HIP_TRY(hipStreamSynchronize(stream));
-    // cost prefix at chunk boundaries: slots + kSectorWeight * sectors
-    std::vector<int64_t> cp((size_t)chunks + 1, 0);
-    for (int32_t c = 0; c < chunks; ++c) {
-        const int64_t e = (c + 1 < chunks ? (int64_t)kSectorChunk : slots - (int64_t)c * kSectorChunk);
-        cp[(size_t)c + 1] = cp[(size_t)c] + e + kSectorWeight * sc[(size_t)c];
-    }
     // cost prefix at slot e, linear inside a chunk
     auto cost_at = [&](int64_t e) -> double {
         if (e >= slots) return (double)cp[(size_t)chunks];
@@ -952,15 +1164,38 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, h
         const int64_t len = (c + 1 < chunks ? (int64_t)kSectorChunk : slots - c * kSectorChunk);
         return (double)cp[(size_t)c] + (double)(cp[(size_t)c + 1] - cp[(size_t)c]) * (double)r / (double)len;
     };
-    // first block in [lo, hi] whose cost prefix reaches `want`
+    // first block in [lo, hi] whose cost prefix reaches `want` (hi if none).
+    // The prefix does not decrease, so the search first narrows [lo, hi] by
+    // whole chunks, using the prefix at chunk starts (where cost_at is
+    // exactly cp), then steps through the at most kBlocksPerChunk blocks left.
+    constexpr int64_t kBlocksPerChunk = kSectorChunk / kEdgeBlock;
     auto block_at = [&](int64_t lo, int64_t hi, double want) -> int64_t {
-        while (lo < hi) {
-            const int64_t mid = lo + (hi - lo) / 2;
-            if (cost_at(mid * kEdgeBlock) < want)
-                lo = mid + 1;
-            else
-                hi = mid;
+        int64_t c_lo = ceil_div(lo, kBlocksPerChunk), c_hi = hi / kBlocksPerChunk;
+        if (c_lo <= c_hi && (double)cp[(size_t)c_lo] < want) {
+            // last chunk start in [c_lo, c_hi] below want
+            while (c_lo < c_hi) {
+                const int64_t mid = c_lo + (c_hi - c_lo + 1) / 2;
+                if ((double)cp[(size_t)mid] < want)
+                    c_lo = mid;
+                else
+                    c_hi = mid - 1;
+            }
+            lo = c_lo * kBlocksPerChunk;  // cost_at(lo) < want: the answer is later
+            // inside chunk c_lo the prefix is linear: jump to one block before
+            // where it reaches want, then step
+            const double c0 = (double)cp[(size_t)c_lo];
+            const double dc = (double)(cp[(size_t)c_lo + 1] - cp[(size_t)c_lo]);
+            if (dc > 0.0) {
+                const int64_t len = (c_lo + 1 < chunks ? (int64_t)kSectorChunk
+                                                       : slots - c_lo * (int64_t)kSectorChunk);
+                const int64_t k = (int64_t)((want - c0) * (double)len / (dc * kEdgeBlock)) - 1;
+                if (k > 0) lo += k < kBlocksPerChunk ? k : kBlocksPerChunk - 1;
+                if (lo > hi) lo = hi;
+                while (lo > 0 && lo > c_lo * kBlocksPerChunk && cost_at(lo * kEdgeBlock) >= want) --lo;
+            }
         }
+        for (; lo < hi; ++lo)
+            if (cost_at(lo * kEdgeBlock) >= want) break;
         return lo;
     };
 
@@ -1050,17 +1285,35 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, h
         }
         if (bt.fix_win.empty()) bt.fix_win.push_back(0);
     }
-    PR_HIP_TRY(hipMemcpyAsync(w.tiles, bt.tiles.data(), sizeof(Tile) * bt.tiles.size(),
-                              hipMemcpyHostToDevice, stream));
-    PR_HIP_TRY(hipMemcpyAsync(w.units, bt.units.data(), sizeof(TileUnit) * bt.units.size(),
-                              hipMemcpyHostToDevice, stream));
-    if (!bt.fixes.empty())
-        PR_HIP_TRY(hipMemcpyAsync(w.fixes, bt.fixes.data(), sizeof(TileFix) * bt.fixes.size(),
-                                  hipMemcpyHostToDevice, stream));
-    PR_HIP_TRY(hipMemcpyAsync(w.fix_rows, bt.fix_rows.data(), sizeof(int32_t) * bt.fix_rows.size(),
-                              hipMemcpyHostToDevice, stream));
-    PR_HIP_TRY(hipMemcpyAsync(w.fix_win, bt.fix_win.data(), sizeof(int32_t) * bt.fix_win.size(),
-                              hipMemcpyHostToDevice, stream));
+    // The work lists go up in one copy: packed one after another from the
+    // start of their workspace region (which holds each at its largest), from
+    // the pinned stage (nothing uses it now: the read-back above was waited
+    // for).
+    {
+        const void* src[5] = {bt.tiles.data(), bt.units.data(), bt.fixes.data(),
+                              bt.fix_rows.data(), bt.fix_win.data()};
+        const size_t bytes[5] = {sizeof(Tile) * bt.tiles.size(), sizeof(TileUnit) * bt.units.size(),
+                                 sizeof(TileFix) * bt.fixes.size(),
+                                 sizeof(int32_t) * bt.fix_rows.size(),
+                                 sizeof(int32_t) * bt.fix_win.size()};
+        size_t off[5], total = 0;
+        for (int i = 0; i < 5; ++i) {
+            off[i] = total;
+            total += align_up(bytes[i]);
+        }
+        char* region = reinterpret_cast<char*>(w.tiles);
+        if (total > (size_t)(reinterpret_cast<char*>(w.partial) - region))
+            return fail(PR_ERR_ARG, "work lists exceed their workspace region");
+        PR_TRY(host_stage(host, total));
+        for (int i = 0; i < 5; ++i)
+            if (bytes[i]) std::memcpy(host->stage + off[i], src[i], bytes[i]);
+        PR_HIP_TRY(hipMemcpyAsync(region, host->stage, total, hipMemcpyHostToDevice, stream));
+        bt.dev_tiles = reinterpret_cast<const Tile*>(region + off[0]);
+        bt.dev_units = reinterpret_cast<const TileUnit*>(region + off[1]);
+        bt.dev_fixes = reinterpret_cast<const TileFix*>(region + off[2]);
+        bt.dev_fix_rows = reinterpret_cast<const int32_t*>(region + off[3]);
+        bt.dev_fix_win = reinterpret_cast<const int32_t*>(region + off[4]);
+    }
     bt.tile_grid = (int32_t)(grid < bt.n_units ? grid : (bt.n_units > 0 ? bt.n_units : 1));
     return PR_OK;
 }
@@ -1088,6 +1341,14 @@ extern "C" size_t pr_plan_scratch_bytes(int32_t n, int64_t nnz) {
     return carve_scratch(nullptr, n, nnz).bytes;
 }
 
+namespace pr {
+namespace {
+int plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_rp,
+                const int32_t* out_ci, const PlanWs& w, const PlanScratch& s, uint32_t flags,
+                int dev, int cus, PlanHost* host, hipStream_t stream);
+}  // namespace
+}  // namespace pr
+
 extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_rp,
                               const int32_t* out_ci, void* ws, size_t ws_bytes, void* scratch,
                               size_t scratch_bytes, uint32_t flags, void* stream_v) {
@@ -1114,6 +1375,20 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     PR_HIP_TRY(hipGetDevice(&dev));
     PR_HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     hipStream_t stream = as_stream(stream_v);
+    PlanHost* host = nullptr;
+    PR_TRY(host_take(&host));
+    const int rc = plan_create(plan_out, n, nnz, out_rp, out_ci, w, s, flags, dev, cus, host, stream);
+    if (rc != PR_OK) host_give(host);
+    return rc;
+}
+
+namespace pr {
+namespace {
+
+int plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_rp,
+                const int32_t* out_ci, const PlanWs& w, const PlanScratch& s, uint32_t flags,
+                int dev, int cus, PlanHost* host, hipStream_t stream) {
+    const bool tiled = !(flags & PR_PLAN_BUCKETED);
     const bool validate = flags & PR_VALIDATE;
     uint32_t* err = s.tr.error;
 
@@ -1141,8 +1416,9 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     // Bucket ranges (hub bucket first), read back now: a tiled plan lays out
     // its tiles before the permutation, which counts the edges per tile.
     unsigned long long stats[2 * kNumBuckets];
-    PR_HIP_TRY(hipMemcpyAsync(stats, s.stats, sizeof stats, hipMemcpyDeviceToHost, stream));
+    PR_HIP_TRY(hipMemcpyAsync(host->stage, s.stats, sizeof stats, hipMemcpyDeviceToHost, stream));
     PR_HIP_TRY(hipStreamSynchronize(stream));
+    std::memcpy(stats, host->stage, sizeof stats);
     int32_t row_begin[kNumBuckets + 1];  // indexed by bucket; hub rows start at 0
     {
         int64_t r = 0;
@@ -1168,7 +1444,7 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
                                                 reinterpret_cast<uint32_t*>(s.key), w.inv_out);
     PR_LAUNCHED("order");
 
-    // 2. The out-edge CSR in plan order (and each edge's source).
+    // 2. The out-edge CSR in plan order.
     PR_TRY(scan_exclusive(s.deg, reinterpret_cast<uint32_t*>(s.perm_rp), n, s.vsort.scan_ws,
                           stream));
     if (nnz > 0) {
@@ -1181,9 +1457,9 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
 
     // 3. The layout's work items.
     if (tiled)
-        PR_TRY(build_tiled(w, s, n, nnz, stream, bt));
+        PR_TRY(build_tiled(w, s, n, nnz, host, stream, bt));
     else
-        PR_TRY(build_bucketed(w, s, n, nnz, stats, row_begin, cus, stream, bt));
+        PR_TRY(build_bucketed(w, s, n, nnz, host, stats, row_begin, cus, stream, bt));
     if (validate) PR_TRY(read_error_word(err, stream, "pr_plan_create"));
     PR_HIP_TRY(hipStreamSynchronize(stream));  // host arrays must outlive the copies
 
@@ -1217,13 +1493,13 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     p->tblk = w.tblk;
     p->tile_ptr = w.tile_ptr;
     p->n_slots = bt.n_slots;
-    p->tiles = w.tiles;
+    p->tiles = bt.dev_tiles;
     p->n_tiles = bt.n_tiles;
-    p->units = w.units;
+    p->units = bt.dev_units;
     p->n_units = bt.n_units;
-    p->fixes = w.fixes;
-    p->fix_rows = w.fix_rows;
-    p->fix_win = w.fix_win;
+    p->fixes = bt.dev_fixes;
+    p->fix_rows = bt.dev_fix_rows;
+    p->fix_win = bt.dev_fix_win;
     p->n_fixes = bt.n_fixes;
     p->n_fix_rows = bt.fix_rows.empty() ? 0 : bt.fix_rows.back();
     p->partial = w.partial;
@@ -1241,34 +1517,17 @@ extern "C" int pr_plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const 
     p->row_begin[kNumBuckets] = row_begin[kNumBuckets];
     p->bucket_items[kKindChunk] = bt.items_of[kKindChunk];
 
-    hipError_t e = hipEventCreate(&p->ev_begin);
-    if (e == hipSuccess) e = hipEventCreate(&p->ev_end);
-    for (int i = 0; i < 2 * kTimedLaunches && e == hipSuccess; ++i)
-        e = hipEventCreate(&p->kernel_ev[i / kTimedLaunches][i % kTimedLaunches]);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->chunk_ev[0], hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->chunk_ev[1], hipEventDisableTiming);
-    if (e == hipSuccess)
-        e = hipHostMalloc(reinterpret_cast<void**>(&p->host_status), 2 * sizeof(RunStatus),
-                          hipHostMallocDefault);
-    if (e != hipSuccess) {
-        int rc = fail(PR_ERR_HIP, "plan events / pinned status: %s", hipGetErrorString(e));
-        pr_plan_destroy(p);
-        return rc;
-    }
+    p->host = host;
     *plan_out = p;
     return PR_OK;
 }
 
+}  // namespace
+}  // namespace pr
+
 extern "C" int pr_plan_destroy(pr_plan* p) {
     if (!p) return PR_OK;
-    if (p->ev_begin) (void)hipEventDestroy(p->ev_begin);
-    if (p->ev_end) (void)hipEventDestroy(p->ev_end);
-    for (int i = 0; i < 2 * kTimedLaunches; ++i)
-        if (p->kernel_ev[i / kTimedLaunches][i % kTimedLaunches])
-            (void)hipEventDestroy(p->kernel_ev[i / kTimedLaunches][i % kTimedLaunches]);
-    if (p->chunk_ev[0]) (void)hipEventDestroy(p->chunk_ev[0]);
-    if (p->chunk_ev[1]) (void)hipEventDestroy(p->chunk_ev[1]);
-    if (p->host_status) (void)hipHostFree(p->host_status);
+    host_give(p->host);
     std::free(p);
     return PR_OK;
 }

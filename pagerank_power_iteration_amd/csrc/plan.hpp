@@ -202,6 +202,29 @@ struct RunStatus {
     int32_t iters;
 };
 
+// A plan's host-side resources: timing events, the pinned status pair pr_run
+// polls, and a pinned staging buffer for the plan builder's read-backs and
+// uploads.  They outlive plans: pr_plan_destroy returns them to a pool of the
+// device, and the next pr_plan_create takes them from there, so building a
+// plan creates no events and allocates no host memory once the pool holds
+// enough for it.
+struct PlanHost {
+    int device;
+    hipEvent_t ev_begin, ev_end;
+    hipEvent_t kernel_ev[2][kTimedLaunches];  // around k_tile (or k_iterate) launches
+    hipEvent_t chunk_ev[2];
+    RunStatus* status;  // pinned, [2]
+    char* stage;        // pinned staging buffer of stage_bytes
+    size_t stage_bytes;
+    PlanHost* next;     // pool link
+};
+
+// A PlanHost of the current device (from the pool, or new), and back.
+int host_take(PlanHost** out);
+void host_give(PlanHost* h);
+// Makes h->stage hold at least `bytes` (its contents are not kept).
+int host_stage(PlanHost* h, size_t bytes);
+
 }  // namespace pr
 
 struct pr_plan {
@@ -253,10 +276,7 @@ struct pr_plan {
     int32_t n_fix_rows;
     long long* partial;
     int32_t tile_grid;
-    hipEvent_t ev_begin, ev_end;
-    hipEvent_t kernel_ev[2][pr::kTimedLaunches];  // around k_tile (or k_iterate) launches
-    int32_t kernel_timed;                         // pairs the last run recorded
-    hipEvent_t chunk_ev[2];
-    pr::RunStatus* host_status;  // pinned, [2]
+    pr::PlanHost* host;    // events, pinned status and staging (pooled)
+    int32_t kernel_timed;  // event pairs around launches the last run recorded
     bool events_recorded;
 };

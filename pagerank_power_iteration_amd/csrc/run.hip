@@ -991,13 +991,13 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     const bool record = flags & PR_RECORD_EVENTS;
     p->events_recorded = false;
     p->kernel_timed = 0;
-    if (record) PR_HIP_TRY(hipEventRecord(p->ev_begin, stream));
+    if (record) PR_HIP_TRY(hipEventRecord(p->host->ev_begin, stream));
 
     auto launch = [&](int32_t t) -> int {
         a.contrib_in = p->contrib[(t - 1) & 1];
         a.contrib_out = p->contrib[t & 1];
         const bool timed = record && t <= kTimedLaunches;
-        if (timed) PR_HIP_TRY(hipEventRecord(p->kernel_ev[0][t - 1], stream));
+        if (timed) PR_HIP_TRY(hipEventRecord(p->host->kernel_ev[0][t - 1], stream));
         if (p->tiled) {
             ta.contrib_in = a.contrib_in;
             ta.contrib_out = a.contrib_out;
@@ -1015,7 +1015,7 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
             PR_LAUNCHED("iterate");
         }
         if (timed) {
-            PR_HIP_TRY(hipEventRecord(p->kernel_ev[1][t - 1], stream));
+            PR_HIP_TRY(hipEventRecord(p->host->kernel_ev[1][t - 1], stream));
             p->kernel_timed = t;
         }
         if (p->tiled && tilefix_grid > 0) {
@@ -1049,7 +1049,7 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     };
     auto finish = [&]() -> int {
         if (record) {
-            PR_HIP_TRY(hipEventRecord(p->ev_end, stream));
+            PR_HIP_TRY(hipEventRecord(p->host->ev_end, stream));
             p->events_recorded = true;
         }
         k_finish<<<dim3((unsigned)p->init_grid), kBlock, 0, stream>>>(p->new_id, p->xi, x, p->n);
@@ -1074,23 +1074,23 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     while (t <= max_iter && !stopped) {
         const int32_t t_end = (max_iter - t + 1) < chunk ? max_iter : t + chunk - 1;
         for (int32_t tt = t; tt <= t_end; ++tt) PR_TRY(launch(tt));
-        PR_HIP_TRY(hipMemcpyAsync(&p->host_status[slot], &p->state->stop, sizeof(RunStatus),
+        PR_HIP_TRY(hipMemcpyAsync(&p->host->status[slot], &p->state->stop, sizeof(RunStatus),
                                   hipMemcpyDeviceToHost, stream));
-        PR_HIP_TRY(hipEventRecord(p->chunk_ev[slot], stream));
+        PR_HIP_TRY(hipEventRecord(p->host->chunk_ev[slot], stream));
         if (have_prev) {
-            PR_HIP_TRY(hipEventSynchronize(p->chunk_ev[slot ^ 1]));
-            if (p->host_status[slot ^ 1].stop) stopped = true;
+            PR_HIP_TRY(hipEventSynchronize(p->host->chunk_ev[slot ^ 1]));
+            if (p->host->status[slot ^ 1].stop) stopped = true;
         }
         have_prev = true;
         slot ^= 1;
         t = t_end + 1;
     }
     PR_TRY(close(t - 1));
-    PR_HIP_TRY(hipMemcpyAsync(&p->host_status[slot ^ 1], &p->state->stop, sizeof(RunStatus),
+    PR_HIP_TRY(hipMemcpyAsync(&p->host->status[slot ^ 1], &p->state->stop, sizeof(RunStatus),
                               hipMemcpyDeviceToHost, stream));
     PR_TRY(finish());
     PR_HIP_TRY(hipStreamSynchronize(stream));
-    const RunStatus& last = p->host_status[slot ^ 1];  // copied after every launched iteration
+    const RunStatus& last = p->host->status[slot ^ 1];  // copied after every launched iteration
     *iterations = last.stop ? last.iters : max_iter;
     return PR_OK;
 }
@@ -1098,8 +1098,8 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
 extern "C" int pr_plan_iteration_ms(pr_plan* p, float* ms) {
     if (!p || !ms) return fail(PR_ERR_ARG, "null pointer argument");
     if (!p->events_recorded) return fail(PR_ERR_ARG, "no pr_run with PR_RECORD_EVENTS on this plan");
-    PR_HIP_TRY(hipEventSynchronize(p->ev_end));
-    PR_HIP_TRY(hipEventElapsedTime(ms, p->ev_begin, p->ev_end));
+    PR_HIP_TRY(hipEventSynchronize(p->host->ev_end));
+    PR_HIP_TRY(hipEventElapsedTime(ms, p->host->ev_begin, p->host->ev_end));
     return PR_OK;
 }
 
@@ -1110,8 +1110,8 @@ extern "C" int pr_plan_kernel_ms(pr_plan* p, float* ms, int32_t* launches) {
     double total = 0.0;
     for (int i = 0; i < p->kernel_timed; ++i) {
         float one = 0.f;
-        PR_HIP_TRY(hipEventSynchronize(p->kernel_ev[1][i]));
-        PR_HIP_TRY(hipEventElapsedTime(&one, p->kernel_ev[0][i], p->kernel_ev[1][i]));
+        PR_HIP_TRY(hipEventSynchronize(p->host->kernel_ev[1][i]));
+        PR_HIP_TRY(hipEventElapsedTime(&one, p->host->kernel_ev[0][i], p->host->kernel_ev[1][i]));
         total += one;
     }
     *ms = (float)(total / p->kernel_timed);
