@@ -241,10 +241,27 @@ __device__ __forceinline__ Sums3 sum_parts(const float* __restrict__ part, int64
             r2 += (double)v2[u];
         }
     }
-    Sums3 r;
-    r.l1 = wide_block_sum<double, kThreads / kWave>(r0, redd);
-    r.dang = wide_block_sum<double, kThreads / kWave>(r1, redd);
-    r.sum = wide_block_sum<double, kThreads / kWave>(r2, redd);
+    // the three sums of the workgroup at once: one exchange through LDS
+    // (`redd` holds 3 * kThreads / kWave doubles), every lane adding the
+    // wavefronts' sums in the same order
+    constexpr int W = kThreads / kWave;
+    r0 = wave_sum(r0);
+    r1 = wave_sum(r1);
+    r2 = wave_sum(r2);
+    if (lane_id() == 0) {
+        redd[threadIdx.x / kWave] = r0;
+        redd[W + threadIdx.x / kWave] = r1;
+        redd[2 * W + threadIdx.x / kWave] = r2;
+    }
+    __syncthreads();
+    Sums3 r{redd[0], redd[W], redd[2 * W]};
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+        r.l1 += redd[w];
+        r.dang += redd[W + w];
+        r.sum += redd[2 * W + w];
+    }
+    __syncthreads();
     return r;
 }
 
@@ -602,7 +619,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     __shared__ unsigned long long acc[kTileMaxRows + 1];  // + the trash row of padding edges
     __shared__ float red[3][kTileWaves];
     __shared__ int32_t s_next;
-    __shared__ double redd[kTileWaves];
+    __shared__ double redd[3 * kTileWaves];
     RunState* st = a.state;
     if (st->stop) return;  // an earlier iteration met the tolerance
     // The previous iteration's (or k_init's) sums, reduced by every workgroup
@@ -659,7 +676,10 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
             accumulate<false, Q>(a, u.e0, u.e1, scale, acc, round);
         // claim the next unit only now: a claim made earlier would hold a
         // unit back behind this one while other workgroups run out of work
-        if (threadIdx.x == 0) s_next = (int32_t)(gridDim.x + atomicAdd(queue, 1u));
+        // (with no more units than workgroups there is none to claim)
+        if (threadIdx.x == 0)
+            s_next = (int32_t)gridDim.x >= a.n_units ? a.n_units
+                                                     : (int32_t)(gridDim.x + atomicAdd(queue, 1u));
         __syncthreads();
         const int32_t nxt = s_next;
         TileUnit un{};
@@ -789,7 +809,7 @@ struct FinArgs {
 // record the trace and the next D, test the tolerance, and reset the work
 // queues.  After k_init (t = 0): D, the fixed-point scale and the queues.
 __global__ __launch_bounds__(kFinalBlock) void k_finalize(FinArgs f) {
-    __shared__ double redd[kFinalWaves];
+    __shared__ double redd[3 * kFinalWaves];
     RunState* st = f.state;
     if (f.t > 0 && st->stop) return;
     const Sums3 r = sum_parts<kFinalBlock>(f.part, f.stride, f.parts, redd);
