@@ -80,8 +80,13 @@ constexpr int kGiantSamples = 1024;          // WCC: vertices sampled for the gi
 constexpr uint32_t kQueueBuf = 512;          // LDS entries per wavefront staging claimed vertices
 constexpr int32_t kProbe = 4;                // in-edges a lane checks itself before a bottom-up walk
 constexpr int kSmallBlock = 1024;            // lanes of the small-frontier kernel
-constexpr int32_t kSmallCap = 2048;          // frontier vertices it keeps in LDS
+constexpr int32_t kSmallCap = 2048;          // frontier rows it keeps in LDS
 constexpr uint64_t kSmallEdges = 65536;      // frontier out-edges it takes per level
+// Graphs of at most kBitVerts vertices run narrow levels with a visited
+// bitmap in LDS (128 KB) and a frontier of at most kSmallBitCap rows.
+constexpr int32_t kBitVerts = 1 << 20;
+constexpr int32_t kSmallBitCap = 1536;
+constexpr int kSmallBatch = 4;               // consecutive edges a lane takes
 static_assert(kHubChunk % (kBlock * kPerLane) == 0, "a hub chunk is whole rounds");
 static_assert(kGiantSamples <= 1024 && kGiantSamples % kWave == 0, "one sample per lane");
 
@@ -567,103 +572,138 @@ __global__ __launch_bounds__(kBlock) void k_bfs_hubs(TravArgs a) {
     }
 }
 
+// Inclusive prefix sum over a wavefront from DPP row shifts (1, 2, 4, 8
+// within each row of 16 lanes) and the two row broadcasts (lane 15 into rows
+// 1 and 3, lane 31 into rows 2 and 3): register moves, where a scan from lane
+// shuffles takes an LDS round trip per step.  Lanes whose source is outside
+// the row, or whose row is masked off, add 0.
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
 // Small frontiers, level after level in one launch of one workgroup (the
 // grid-wide kernels pay two launches per level, which is all a search of
 // thousands of narrow levels costs).  Entered at level a.level with the
 // frontier in a.queue (at most kSmallCap vertices, at most kSmallEdges
-// out-edges).  Each level: the frontier's rows and the prefix sums of their
-// lengths sit in LDS; every lane takes edges j, j + 1024, ... of their
-// concatenation, finds its row by binary search, and claims the target with
-// a compare-and-swap on its level; claimed vertices get LDS slots from an
-// LDS counter and are also written to the global queue of their level.  It
-// stops after a level whose frontier is empty, or larger than it takes, and
+// out-edges).  Each level: the frontier's rows that have out-edges sit in
+// LDS (first out-edge, and the offset of the row's edges in the
+// concatenation of the rows, in any row order); lane t takes the kSmallBatch
+// consecutive edges from kSmallBatch * t on (then the next 4096, ...), finds
+// the first one's row by binary search and the others' rows among the next
+// three (no row is empty), and claims each target.  Claimed vertices go to
+// the global queue of their level, and those with out-edges also to LDS
+// rows of the next level, whose slots and edge offsets come from one atomic
+// add per wavefront on a packed (rows, edges) counter: slot order and offset
+// order agree, so the offsets need no scan.  It stops after a level whose
+// frontier is empty, or larger than it takes (in rows or out-edges), and
 // leaves the state as the grid-wide kernels of the next level expect it
 // (counts of that level, the counters it appends to cleared, the queue in
 // place), with that level in small_next.
+//
+// A narrow level is a chain of latencies: LDS for the row search, memory for
+// the column, then the claim (LDS or memory) alongside the target's row
+// bounds (memory), then the slot counters (LDS).  So a lane issues the loads
+// of all its edges together, in straight-line code (a load under a branch is
+// waited for where the branch ends), and stores only after its last load (a
+// store ahead of a load holds that load's wait until the store completes).
+// One barrier per level; the counters of levels L, L + 1 and L + 2 are
+// three slots, and level L clears the slot of L + 2.
+//
+// kBits: the graph has at most kBitVerts vertices, and the workgroup keeps a
+// bitmap of the visited vertices in LDS, built from the level array at entry.
+// A vertex is then claimed by an LDS atomic OR on its bit and its level is a
+// plain store, in place of a compare-and-swap on its level.  The frontier
+// then holds at most kSmallBitCap rows.
+template <bool kBits>
 __global__ __launch_bounds__(kSmallBlock) void k_bfs_small(TravArgs a, int32_t* q0, int32_t* q1) {
-    __shared__ int32_t fv[2][kSmallCap];  // frontier vertices
-    __shared__ int32_t fs[2][kSmallCap];  // their first out-edges
-    __shared__ int32_t fl[2][kSmallCap];  // their out-degrees
-    __shared__ int32_t pre[kSmallCap + 1];
-    __shared__ uint32_t claimed;
-    __shared__ uint64_t red[kSmallBlock / kWave];
-    __shared__ uint32_t scan_tmp[kSmallBlock / kWave + 1];
+    constexpr int32_t kCap = kBits ? kSmallBitCap : kSmallCap;
+    __shared__ int32_t fs[2][kCap];   // frontier rows' first out-edges
+    __shared__ int32_t pre[2][kCap];  // and their offsets (increasing)
+    __shared__ uint32_t seen[kBits ? kBitVerts / 32 : 1];
+    __shared__ uint32_t nq[3];             // a level's claims (its queue length)
+    __shared__ unsigned long long nre[3];  // its rows << 32 | their out-edges
+    __shared__ uint32_t nlong[3];          // non-zero: a row has > kSmallBatch edges
+    __shared__ uint32_t sink[kWave];       // targets of unused slots' claims
     TravState* st = a.st;
     int32_t* level = a.out;
     const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid / kWave);
     int L = a.level;
     int cur = 0;
-    uint32_t F = st->front[L % 3];
-    uint64_t M = st->mf[L % 3];
+    if (kBits) {
+        // bit v of `seen`: level[v] != -1.  A lane builds whole words, from
+        // eight 16-byte loads issued together when the level array is
+        // 16-byte aligned (word w's levels start at byte 128 w), else and in
+        // the last, partial word one level at a time.  Words past the last
+        // vertex are never read.
+        const int32_t words = (a.n + 31) / 32;
+        const bool vec = ((uintptr_t)level & 15u) == 0;
+        for (int32_t w = tid; w < words; w += kSmallBlock) {
+            const int32_t v0 = w * 32;
+            uint32_t bits = 0;
+            if (vec && v0 + 32 <= a.n) {
+                const int4* p = reinterpret_cast<const int4*>(level + v0);
+                int4 q[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) q[k] = p[k];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    bits |= (uint32_t)(q[k].x != -1) << (4 * k) |
+                            (uint32_t)(q[k].y != -1) << (4 * k + 1) |
+                            (uint32_t)(q[k].z != -1) << (4 * k + 2) |
+                            (uint32_t)(q[k].w != -1) << (4 * k + 3);
+            } else {
+                for (int k = 0; k < 32 && v0 + k < a.n; ++k)
+                    bits |= (uint32_t)(level[v0 + k] != -1) << k;
+            }
+            seen[w] = bits;
+        }
+    }
     // out-degree sum of the levels below L, carried in a register: a
     // read-modify-write of the state per level would hold every level's
     // closing barrier for a global load
     uint64_t explored = st->explored[L % 2];
-    for (uint32_t i = tid; i < F; i += kSmallBlock) {
-        const int32_t v = (L % 2 ? q1 : q0)[i];
-        int32_t s0, len;
-        row_range(a.rp, a.nnz, v, s0, len);
-        fv[0][i] = v;
-        fs[0][i] = s0;
-        fl[0][i] = len;
+    const uint32_t Fq0 = st->front[L % 3];  // level L's vertices, in its queue
+    if (tid == 0) {
+        nq[L % 3] = Fq0;
+        nre[L % 3] = 0;
+        nlong[L % 3] = 0;
+        nq[(L + 1) % 3] = 0;
+        nre[(L + 1) % 3] = 0;
+        nlong[(L + 1) % 3] = 0;
     }
+    __syncthreads();
+    // the entry frontier's rows with out-edges (Fq0 <= kCap)
+    for (uint32_t i = tid; i < Fq0; i += kSmallBlock) {
+        int32_t s0, len;
+        row_range(a.rp, a.nnz, (L % 2 ? q1 : q0)[i], s0, len);
+        if (len > 0) {
+            const unsigned long long o = atomicAdd(&nre[L % 3], 1ull << 32 | (uint32_t)len);
+            fs[0][o >> 32] = s0;
+            pre[0][o >> 32] = (int32_t)(uint32_t)o;
+            if (len > kSmallBatch) nlong[L % 3] = 1;
+        }
+    }
+    __syncthreads();
     while (true) {
-        // level L: prefix sums of the frontier's row lengths (two per lane)
-        __syncthreads();
-        const uint32_t i0 = 2 * tid, i1 = 2 * tid + 1;
-        const uint32_t l0 = i0 < F ? (uint32_t)fl[cur][i0] : 0u;
-        const uint32_t l1 = i1 < F ? (uint32_t)fl[cur][i1] : 0u;
-        uint32_t total;
-        const uint32_t ex =
-            block_exclusive_scan<uint32_t, kSmallBlock / kWave>(l0 + l1, &total, scan_tmp);
-        if (i0 <= F) pre[i0] = (int32_t)ex;
-        if (i1 <= F) pre[i1] = (int32_t)(ex + l0);
-        if (tid == 0) claimed = 0;
-        __syncthreads();
-        int32_t* next_q = (L + 1) % 2 ? q1 : q0;
-        const int nxt = cur ^ 1;
-        uint64_t edges = 0;
-        for (uint32_t j = tid; j < total; j += kSmallBlock) {
-            int32_t lo = 0, hi = (int32_t)F - 1;  // last row with pre[row] <= j
-            while (lo < hi) {
-                const int32_t mid = (lo + hi + 1) / 2;
-                if ((uint32_t)pre[mid] <= j)
-                    lo = mid;
-                else
-                    hi = mid - 1;
-            }
-            const int32_t v = column(a, fs[cur][lo] + (int32_t)(j - (uint32_t)pre[lo]));
-            // v's row bounds are loaded before the claim resolves (wasted when
-            // it fails): a narrow level is a chain of memory latencies
-            // (column, claim, row bounds), and this runs the last two side by
-            // side.
-            int32_t s0, len;
-            row_range(a.rp, a.nnz, v, s0, len);
-            if (atomicCAS(&level[v], -1, L + 1) == -1) {
-                const uint32_t pos = atomicAdd(&claimed, 1u);
-                next_q[pos] = v;  // each vertex is claimed once: pos < n
-                edges += (uint64_t)len;
-                if (pos < (uint32_t)kSmallCap) {
-                    fv[nxt][pos] = v;
-                    fs[nxt][pos] = s0;
-                    fl[nxt][pos] = len;
-                }
-            }
-        }
-        // (the sum's barriers also publish `claimed`)
-        const uint64_t M_next = block_sum<uint64_t, kSmallBlock / kWave>(edges, red);
-        const uint32_t F_next = claimed;
-        explored += M;
-        if (tid == 0) {
-            st->depth = L;
-            st->mode[L % 2] = kTopDown;
-            st->explored[(L + 1) % 2] = explored;
-        }
-        ++L;
-        if (F_next == 0 || F_next > (uint32_t)kSmallCap || M_next > kSmallEdges) {
+        // level L: Fq vertices, Fr rows in fs/pre[cur], total out-edges
+        const int b = L % 3;
+        const uint32_t Fq = nq[b];
+        const unsigned long long re = nre[b];
+        const uint32_t Fr = (uint32_t)(re >> 32), total = (uint32_t)re;
+        if (Fq == 0 || Fr > (uint32_t)kCap || total > kSmallEdges) {
+            // an empty level, or one the workgroup does not take: hand it
+            // to the grid-wide kernels (uniform: every lane read the same)
             if (tid == 0) {
-                st->front[L % 3] = F_next;
-                st->mf[L % 3] = M_next;
+                st->front[L % 3] = Fq;
+                st->mf[L % 3] = total;
                 st->front[(L + 1) % 3] = 0;
                 st->mf[(L + 1) % 3] = 0;
                 st->chunks[L % 2] = 0;
@@ -671,8 +711,163 @@ __global__ __launch_bounds__(kSmallBlock) void k_bfs_small(TravArgs a, int32_t* 
             }
             return;
         }
-        F = F_next;
-        M = M_next;
+        // level L + 2's counters, which level L + 1 fills after the barrier
+        // that ends level L (the slot of level L - 1, which every lane read
+        // before the barrier that ended it)
+        if (tid == 0) {
+            nq[(L + 2) % 3] = 0;
+            nre[(L + 2) % 3] = 0;
+            nlong[(L + 2) % 3] = 0;
+        }
+        int32_t* next_q = (L + 1) % 2 ? q1 : q0;
+        const int nxt = cur ^ 1;
+        // direct: no row has more than kSmallBatch edges, so slots are rows
+        // (kSmallBatch per row, the unused ones idle) and nothing is
+        // searched; else slots are edges, kSmallBatch consecutive ones per
+        // lane and pass
+        const bool direct = nlong[b] == 0;
+        const uint32_t span = direct ? Fr * kSmallBatch : total;
+        // binary search steps: powers of two from the largest below Fr
+        const int32_t top = Fr > 1 ? 1 << (31 - __builtin_clz(Fr - 1)) : 0;
+        for (uint32_t p0 = 0; p0 < span; p0 += (uint32_t)(kSmallBlock * kSmallBatch)) {
+            // a wavefront whose first slot is past the end has none (uniform)
+            if (p0 + (uint32_t)wave_u * (kWave * kSmallBatch) >= span) continue;
+            const uint32_t j0 = p0 + (uint32_t)tid * kSmallBatch;
+            bool won[kSmallBatch];
+            int32_t v[kSmallBatch], s0[kSmallBatch], len[kSmallBatch];
+            uint32_t cnt = 0, esum = 0;
+#pragma unroll
+            for (int k = 0; k < kSmallBatch; ++k) {
+                won[k] = false;
+                v[k] = 0;
+                s0[k] = 0;
+                len[k] = 0;
+            }
+            if (j0 < span) {
+                // offset of row r, with row Fr at `total` (above every edge)
+                auto off = [&](int32_t r) -> uint32_t {
+                    const uint32_t x = (uint32_t)pre[cur][min(r, (int32_t)Fr - 1)];
+                    return r >= (int32_t)Fr ? total : x;
+                };
+                bool ok[kSmallBatch];
+                int32_t e[kSmallBatch];
+                if (direct) {
+                    // row t < Fr: its first edge and length
+                    const int32_t t = (int32_t)(j0 / kSmallBatch);
+                    const int32_t sr = fs[cur][t];
+                    const uint32_t len0 = off(t + 1) - off(t);
+#pragma unroll
+                    for (int k = 0; k < kSmallBatch; ++k) {
+                        ok[k] = (uint32_t)k < len0;
+                        e[k] = ok[k] ? sr + k : 0;
+                    }
+                } else {
+                    int32_t lo = 0;  // the last row whose offset is <= j0
+                    for (int32_t step = top; step > 0; step >>= 1)
+                        if (off(lo + step) <= j0) lo += step;
+                    // rows lo .. lo + 3 hold edges j0 .. j0 + 3 (no row is
+                    // empty)
+                    uint32_t P[4];
+                    int32_t S[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        P[i] = off(lo + i);
+                        S[i] = fs[cur][min(lo + i, (int32_t)Fr - 1)];
+                    }
+#pragma unroll
+                    for (int k = 0; k < kSmallBatch; ++k) {
+                        const uint32_t j = j0 + (uint32_t)k;
+                        int32_t sr = S[0];
+                        uint32_t pr = P[0];
+#pragma unroll
+                        for (int i = 1; i < 4; ++i) {
+                            if (P[i] <= j) {
+                                sr = S[i];
+                                pr = P[i];
+                            }
+                        }
+                        ok[k] = j < total;
+                        e[k] = ok[k] ? sr + (int32_t)(j - pr) : 0;
+                    }
+                }
+                // total > 0, so nnz > 0 and column() is defined; unused
+                // slots (edge 0) claim nothing
+#pragma unroll
+                for (int k = 0; k < kSmallBatch; ++k) v[k] = column(a, e[k]);
+                int32_t old[kSmallBatch];
+#pragma unroll
+                for (int k = 0; k < kSmallBatch; ++k) {
+                    // an unused slot takes a word of its own lane and
+                    // changes nothing
+                    if (kBits) {
+                        const uint32_t bit = ok[k] ? 1u << (v[k] & 31) : 0u;
+                        const uint32_t prev =
+                            atomicOr(ok[k] ? &seen[v[k] >> 5] : &sink[lane], bit);
+                        won[k] = ok[k] && !(prev & bit);
+                    } else {
+                        // (no level holds INT32_MIN)
+                        old[k] = atomicCAS(&level[ok[k] ? v[k] : min(tid, a.n - 1)],
+                                           ok[k] ? -1 : INT32_MIN, L + 1);
+                    }
+                }
+                // kBits: the rows of claimed vertices (the others read row 0's
+                // bounds, unused); else every target's, loaded while the
+                // compare-and-swap is in flight
+#pragma unroll
+                for (int k = 0; k < kSmallBatch; ++k)
+                    row_range(a.rp, a.nnz, kBits ? (won[k] ? v[k] : 0) : v[k], s0[k], len[k]);
+#pragma unroll
+                for (int k = 0; k < kSmallBatch; ++k) {
+                    if (!kBits) won[k] = ok[k] && old[k] == -1;
+                    // claims in the low half, rows with out-edges in the high
+                    cnt += won[k] ? (len[k] > 0 ? 0x10001u : 1u) : 0u;
+                    esum += won[k] ? (uint32_t)len[k] : 0u;
+                    if (won[k] && len[k] > kSmallBatch) nlong[(L + 1) % 3] = 1;
+                }
+            }
+            // one pair of LDS atomics per wavefront; its lanes take slots in
+            // lane order (a wavefront's claims stay below 2^16, and the
+            // out-edges of claimed vertices below nnz < 2^31)
+            const uint32_t cincl = wave_scan_dpp(cnt);
+            const uint32_t eincl = wave_scan_dpp(esum);
+            const uint32_t wc = (uint32_t)__builtin_amdgcn_readlane((int)cincl, kWave - 1);
+            const uint32_t we = (uint32_t)__builtin_amdgcn_readlane((int)eincl, kWave - 1);
+            uint32_t bq = 0;
+            unsigned long long bre = 0;
+            if (lane == kWave - 1 && wc) {
+                bq = atomicAdd(&nq[(L + 1) % 3], wc & 0xffffu);
+                bre = atomicAdd(&nre[(L + 1) % 3],
+                                (unsigned long long)(wc >> 16) << 32 | we);
+            }
+            const uint32_t cex = cincl - cnt;
+            uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)bq, kWave - 1) + (cex & 0xffffu);
+            uint32_t rpos =
+                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bre >> 32), kWave - 1) + (cex >> 16);
+            uint32_t epos = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bre, kWave - 1) +
+                            (eincl - esum);
+#pragma unroll
+            for (int k = 0; k < kSmallBatch; ++k) {
+                if (!won[k]) continue;
+                if (kBits) level[v[k]] = L + 1;
+                next_q[pos++] = v[k];  // each vertex is claimed once: pos < n
+                if (len[k] > 0) {
+                    if (rpos < (uint32_t)kCap) {
+                        fs[nxt][rpos] = s0[k];
+                        pre[nxt][rpos] = (int32_t)epos;
+                    }
+                    ++rpos;
+                    epos += (uint32_t)len[k];
+                }
+            }
+        }
+        __syncthreads();
+        explored += total;
+        if (tid == 0) {
+            st->depth = L;
+            st->mode[L % 2] = kTopDown;
+            st->explored[(L + 1) % 2] = explored;
+        }
+        ++L;
         cur = nxt;
     }
 }
@@ -967,7 +1162,10 @@ extern "C" int pr_bfs(int32_t n, int64_t nnz, const int32_t* rp, const int32_t* 
         a.next = w.queue[(L + 1) % 2];
         if (h.front[L % 3] <= (uint32_t)kSmallCap && h.mf[L % 3] <= kSmallEdges) {
             // narrow levels: one launch runs them until the frontier grows
-            k_bfs_small<<<1, kSmallBlock, 0, stream>>>(a, w.queue[0], w.queue[1]);
+            if (n <= kBitVerts && h.front[L % 3] <= (uint32_t)kSmallBitCap)
+                k_bfs_small<true><<<1, kSmallBlock, 0, stream>>>(a, w.queue[0], w.queue[1]);
+            else
+                k_bfs_small<false><<<1, kSmallBlock, 0, stream>>>(a, w.queue[0], w.queue[1]);
             PR_LAUNCHED("bfs small levels");
             PR_TRY(read_state());
             L = h.small_next;

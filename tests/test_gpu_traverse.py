@@ -158,6 +158,29 @@ def test_bfs_grid_is_2046_levels_deep(prx, mode):
     assert comps == 1 and not _cases.to_np(label).any()
 
 
+@pytest.mark.parametrize("nx, ny, sx, sy", [
+    # frontiers of up to 1,536 vertices (more than one per lane of the
+    # single-workgroup levels): the centre-left source of the 1024 x 1024 grid
+    (1024, 1024, 256, 512),
+    # more vertices than the visited bitmap in LDS covers (2^20): those
+    # levels claim by compare-and-swap on the level array
+    (1100, 1000, 0, 0),
+    (1100, 1000, 550, 500),
+])
+def test_bfs_grid_levels_are_manhattan_distances(prx, nx, ny, sx, sy):
+    """On a 4-neighbour grid the BFS level of (x, y) is |x - sx| + |y - sy|
+    (closed form), the depth is the largest such distance and every one of
+    the grid's out-edges is scanned once."""
+    g = graphgen.grid2d(nx, ny)
+    print(f"[bfs grid] {g.name} source ({sx}, {sy})", flush=True)
+    dg = _cases.gpu_graph(g)
+    level, depth, scanned = prx.bfs(dg, sx + nx * sy)
+    v = np.arange(g.n)
+    want = np.abs(v % nx - sx) + np.abs(v // nx - sy)
+    np.testing.assert_array_equal(_cases.to_np(level), want)
+    assert depth == want.max() and scanned == g.m
+
+
 def test_reused_workspace_and_repeats(prx):
     """Calls reuse one workspace; a second search from another source and a
     rerun give the oracle's results again (no state leaks between calls)."""
