@@ -117,14 +117,17 @@ constexpr int kMaxCountChunks = 512;
 
 // Upper bounds of the tiled layout.
 inline int64_t max_tiles(int32_t n) { return n / kTileMinRows + kNumBuckets + 1; }
-inline int64_t max_units(int32_t n, int64_t nnz) { return max_tiles(n) + nnz / kMinUnitEdges + 1; }
+// A tile of e edges and r rows is cut into c <= ceil(e / min_unit_edges(r))
+// units, each of at least kMinUnitEdgesFloor edges when c > 1: so at most
+// tiles + nnz / kMinUnitEdgesFloor units, at most nnz / kMinUnitEdgesFloor
+// cut tiles, and c * r < r * e / min_unit_edges(r) + r <= e / 8 + r partial
+// slots per cut tile, nnz / 8 + n over all of them.
+inline int64_t max_units(int32_t n, int64_t nnz) { return max_tiles(n) + nnz / kMinUnitEdgesFloor + 1; }
 inline int64_t max_fixes(int32_t n, int64_t nnz) {
-    const int64_t a = max_tiles(n), b = nnz / kMinUnitEdges + 1;
+    const int64_t a = max_tiles(n), b = nnz / kMinUnitEdgesFloor + 1;
     return a < b ? a : b;
 }
-// A tile cut into c > 1 units has more than (c-1)*unit edges, so the slots of
-// all cut tiles hold at most 2*nnz/unit tiles' worth of rows.
-inline int64_t max_partial(int64_t nnz) { return 2 * (nnz / kMinUnitEdges + 1) * kTileMaxRows; }
+inline int64_t max_partial(int32_t n, int64_t nnz) { return nnz / 8 + n + 1; }
 // Tile edge slots: every tile padded to whole blocks.
 inline int64_t max_edge_slots(int32_t n, int64_t nnz) { return nnz + (int64_t)(kEdgeBlock - 1) * max_tiles(n); }
 
@@ -187,7 +190,7 @@ PlanWs carve_ws(void* base, int32_t n, int64_t nnz, bool tiled) {
     w.n_tiles_max = max_tiles(n);
     w.n_units_max = max_units(n, nnz);
     w.n_fixes_max = max_fixes(n, nnz);
-    w.n_partial_max = max_partial(nnz);
+    w.n_partial_max = max_partial(n, nnz);
     w.n_edge_slots_max = max_edge_slots(n, nnz);
     w.inv_out = c.take<float>((size_t)n);
     w.new_id = c.take<int32_t>((size_t)n);
@@ -1012,6 +1015,11 @@ int lay_out_tiles(const PlanWs& w, int64_t nnz, const unsigned long long* stats,
     int64_t target = kTileTargetEdges, unit_cost = kUnitCost;
     if (tile_env && std::atoll(tile_env) > 0) target = std::atoll(tile_env);
     if (unit_env && std::atoll(unit_env) > 0) unit_cost = std::atoll(unit_env);
+    const int64_t wg_edges = nnz / grid;
+    int64_t max_rows = wg_edges < kWgEdgesMid ? kTileRowsFew
+                       : wg_edges < kWgEdgesMany ? kTileRowsMid : kTileMaxRows;
+    if (const char* env = std::getenv("PR_TILE_ROWS"))  // tuning knob: rows per tile at most
+        if (std::atoll(env) >= kTileMinRows && std::atoll(env) <= kTileMaxRows) max_rows = std::atoll(env);
     TileMap& map = bt.map;
     auto lay_out = [&](int64_t tgt) -> int32_t {  // the tile map for a target; returns the tiles
         int32_t count = 0;
@@ -1019,8 +1027,8 @@ int lay_out_tiles(const PlanWs& w, int64_t nnz, const unsigned long long* stats,
             const int b = kHubBucket - seg;  // segment 0 = hub bucket
             const int64_t rows = (int64_t)stats[b], edges = (int64_t)stats[kNumBuckets + b];
             int64_t want = edges > 0 ? ceil_div(tgt * rows, edges) : kTileMaxRows;
+            if (want > max_rows) want = max_rows;
             if (want < kTileMinRows) want = kTileMinRows;
-            if (want > kTileMaxRows) want = kTileMaxRows;
             map.start[seg] = row_begin[b];
             map.tile0[seg] = count;
             map.shift[seg] = log2_ceil(want);
@@ -1201,7 +1209,11 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
 
     // A smaller graph gets a smaller unit cost: when the tiles at the default
     // cost would give fewer than two units per workgroup, the cost becomes
-    // (total cost) / (2 * grid).
+    // (total cost) / (2 * grid), and a tile of few rows may then be cut
+    // into units down to min_unit_edges(rows) edges (kMinUnitEdges
+    // otherwise): the hubs' tiles of such a graph would else be its longest
+    // units.
+    bool fine_cuts = false;
     if (!unit_env && tiles > 0) {
         const double total = cost_at(slots) - cost_at(0);
         int64_t units = 0;
@@ -1215,11 +1227,12 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
         if (units < 2 * grid) {
             const int64_t t2 = (int64_t)(total / (double)(2 * grid));
             unit_cost = t2 > kMinUnitCost ? t2 : kMinUnitCost;
+            fine_cuts = true;
         }
     }
 
     // Tiles, units and slots.  A tile is cut at block boundaries into
-    // min(ceil(cost / unit_cost), ceil(slots / kMinUnitEdges)) units of about
+    // min(ceil(cost / unit_cost), ceil(slots / that minimum)) units of about
     // equal cost; all units are then ordered by decreasing estimated cost.
     bt.tiles.resize((size_t)tiles);
     std::vector<std::pair<int64_t, TileUnit>> list;
@@ -1235,7 +1248,8 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
             const double c0 = cost_at(e0), c1 = cost_at(e1);
             const int64_t per_unit = kUnitOverhead + kTileRowWeight * rows;
             int64_t count = (int64_t)std::ceil((c1 - c0) / (double)unit_cost);
-            int64_t count_max = ceil_div((int64_t)(e1 - e0), kMinUnitEdges);
+            int64_t count_max =
+                ceil_div((int64_t)(e1 - e0), fine_cuts ? min_unit_edges(rows) : kMinUnitEdges);
             if (count_max > (e1 - e0) / kEdgeBlock) count_max = (e1 - e0) / kEdgeBlock;
             if (count > count_max) count = count_max;
             const int64_t count_min = ceil_div((int64_t)(e1 - e0), kMaxUnitEdges);

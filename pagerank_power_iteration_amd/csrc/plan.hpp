@@ -112,17 +112,38 @@ constexpr int kFinalBlock = 1024;
 // queue in decreasing estimated cost, so the longest start first.
 constexpr int32_t kTileMaxRows = 16384;         // 128 KB of accumulators
 constexpr int32_t kTileMinRows = 64;
+// Rows per tile at most, by edges per workgroup of the launch: a tile's
+// unit clears, reads and updates every row of the tile, so on a graph with
+// little work per workgroup the tiles of the light rows (many rows, few
+// edges each) would be the longest units.  Measured on gfx950 (R-MAT 18,
+// 21, 23, the 27-point stencil): 4096 rows below 2^16 edges per workgroup,
+// 8192 below 2^19, else kTileMaxRows.
+constexpr int32_t kTileRowsFew = 4096;
+constexpr int32_t kTileRowsMid = 8192;
+constexpr int64_t kWgEdgesMid = 1 << 16;
+constexpr int64_t kWgEdgesMany = 1 << 19;
 constexpr int64_t kTileTargetEdges = 1 << 22;  // default; PR_TILE_EDGES overrides
 constexpr int64_t kMinTileTarget = 1 << 12;     // smaller graphs' tiles go down to this
 constexpr int64_t kUnitCost = 700000;           // default; PR_UNIT_COST overrides
 constexpr int64_t kMinUnitCost = 1 << 15;       // smaller graphs' units go down to this
-constexpr int64_t kMinUnitEdges = 1 << 17;     // a tile is cut into at most edges/this units
-constexpr int64_t kMaxUnitEdges = 1 << 26;     // and into at least edges/this units
+constexpr int64_t kMinUnitEdges = 1 << 17;     // a unit of a cut tile has at least
+constexpr int64_t kMinUnitEdgesFloor = 1 << 12; //   min(kMinUnitEdges, max(this,
+constexpr int64_t kUnitEdgesPerRow = 64;        //   this * rows)) edges (min_unit_edges)
+constexpr int64_t kMaxUnitEdges = 1 << 26;     // and at most this many
 constexpr int32_t kTiledMaxVertices = 1 << 30; // contribution byte offsets fit 32 bits
 constexpr int kSectorShift = 4;                 // 16 fp32 contributions per 64-byte sector
 constexpr int64_t kSectorWeight = 6;
 constexpr int64_t kTileRowWeight = 1;
 constexpr int64_t kUnitOverhead = 27000;
+
+// The fewest edges a unit of a cut tile of `rows` rows may have: a unit
+// writes one partial slot per row, so a tile of few rows (the hubs') can be
+// cut finely and one of many rows only coarsely.  rows / min_unit_edges(rows)
+// is at most max(1 / kUnitEdgesPerRow, kTileMaxRows / kMinUnitEdges) = 1/8.
+inline int64_t min_unit_edges(int64_t rows) {
+    const int64_t e = kUnitEdgesPerRow * rows;
+    return e < kMinUnitEdgesFloor ? kMinUnitEdgesFloor : (e > kMinUnitEdges ? kMinUnitEdges : e);
+}
 constexpr int32_t kSectorChunk = 4096;          // edges per sector count read back
 
 // Tile edges are stored in blocks of kEdgeBlock: each tile's edges padded to
