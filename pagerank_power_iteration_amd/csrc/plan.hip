@@ -815,11 +815,11 @@ __global__ __launch_bounds__(kBlock) void k_tile_blocks(const int32_t* __restric
 // Estimated cost of each kSectorChunk-slot chunk of the tile slots: its slots
 // plus kSectorWeight per sector start counted in it (cost[c], c < chunks).
 __global__ __launch_bounds__(kBlock) void k_chunk_costs(const int32_t* __restrict__ sectors,
-                                                        int64_t slots, int32_t chunks,
+                                                        int64_t slots, int32_t chunks, int64_t weight,
                                                         uint64_t* __restrict__ cost) {
     GRID_STRIDE(c, chunks) {
         const int64_t len = c + 1 < chunks ? (int64_t)kSectorChunk : slots - c * (int64_t)kSectorChunk;
-        cost[c] = (uint64_t)(len + kSectorWeight * (int64_t)sectors[c]);
+        cost[c] = (uint64_t)(len + weight * (int64_t)sectors[c]);
     }
 }
 
@@ -1020,6 +1020,11 @@ int lay_out_tiles(const PlanWs& w, int64_t nnz, const unsigned long long* stats,
                        : wg_edges < kWgEdgesMany ? kTileRowsMid : kTileMaxRows;
     if (const char* env = std::getenv("PR_TILE_ROWS"))  // tuning knob: rows per tile at most
         if (std::atoll(env) >= kTileMinRows && std::atoll(env) <= kTileMaxRows) max_rows = std::atoll(env);
+    int64_t light_rows = kTileRowsLight, light_deg = kLightDeg;
+    if (const char* env = std::getenv("PR_LIGHT_ROWS"))  // tuning knob: rows per light tile
+        if (std::atoll(env) >= kTileMinRows && std::atoll(env) <= kTileMaxRows) light_rows = std::atoll(env);
+    if (const char* env = std::getenv("PR_LIGHT_DEG"))  // tuning knob: in-edges per row of a light segment
+        if (std::atoll(env) >= 0) light_deg = std::atoll(env);
     TileMap& map = bt.map;
     auto lay_out = [&](int64_t tgt) -> int32_t {  // the tile map for a target; returns the tiles
         int32_t count = 0;
@@ -1028,6 +1033,7 @@ int lay_out_tiles(const PlanWs& w, int64_t nnz, const unsigned long long* stats,
             const int64_t rows = (int64_t)stats[b], edges = (int64_t)stats[kNumBuckets + b];
             int64_t want = edges > 0 ? ceil_div(tgt * rows, edges) : kTileMaxRows;
             if (want > max_rows) want = max_rows;
+            if (edges < light_deg * rows && want > light_rows) want = light_rows;
             if (want < kTileMinRows) want = kTileMinRows;
             map.start[seg] = row_begin[b];
             map.tile0[seg] = count;
@@ -1155,7 +1161,10 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
             sorted_targets, s.order, map, first, w.tile_ptr, tiles, n_blocks, w.tsrc, w.tdst,
             w.tblk, counts);
         PR_LAUNCHED("tile blocks");
-        k_chunk_costs<<<grid_for(chunks, 1024), kBlock, 0, stream>>>(counts, slots, chunks, cost);
+        int64_t weight = nnz / grid < kWgEdgesMid ? kSectorWeightFew : kSectorWeight;
+        if (const char* env = std::getenv("PR_SECTOR_WEIGHT"))  // tuning knob: cost per sector
+            if (std::atoll(env) >= 0) weight = std::atoll(env);
+        k_chunk_costs<<<grid_for(chunks, 1024), kBlock, 0, stream>>>(counts, slots, chunks, weight, cost);
         PR_LAUNCHED("chunk costs");
         PR_TRY(scan_exclusive(cost, prefix, chunks, s.tr.sort.scan_ws, stream));
         PR_HIP_TRY(hipMemcpyAsync(host->stage + sp_bytes, prefix,

@@ -106,10 +106,16 @@ constexpr int kFinalBlock = 1024;
 // plus kSectorWeight per distinct 64-byte sector of contributions it gathers
 // (sources in increasing order, so a new sector starts where src >> 4
 // changes), plus, per unit, kTileRowWeight per row of the tile (clearing and
-// reading the accumulators) and kUnitOverhead.  The weights are fitted to
-// per-unit timings of k_tile on gfx950: a sector fetched from outside the CU
-// costs about six edges' worth of streaming and adding.  Units go to the
-// queue in decreasing estimated cost, so the longest start first.
+// reading the accumulators) and kUnitOverhead.  The row and unit weights
+// are fitted to per-unit timings of k_tile on gfx950.  The sector weight and
+// the unit cost were then re-tuned together by sweeping the whole launch
+// (R-MAT 23, original and shuffled ids: weight 6-14, cost 0.7-1.0 M): a
+// sector fetched from outside the CU costs about ten edges' worth of
+// streaming and adding, and at weight 6 the sparse-source units ran up to 60%
+// longer than units of the same estimate, ending the launch late.  Graphs
+// with little work per workgroup (R-MAT 18) keep weight 6, their best.
+// Units go to the queue in decreasing estimated cost, so the longest start
+// first.
 constexpr int32_t kTileMaxRows = 16384;         // 128 KB of accumulators
 constexpr int32_t kTileMinRows = 64;
 // Rows per tile at most, by edges per workgroup of the launch: a tile's
@@ -122,9 +128,14 @@ constexpr int32_t kTileRowsFew = 4096;
 constexpr int32_t kTileRowsMid = 8192;
 constexpr int64_t kWgEdgesMid = 1 << 16;
 constexpr int64_t kWgEdgesMany = 1 << 19;
+// Tiles of a light segment (fewer than kLightDeg in-edges per row: one gather
+// per edge, no source reuse to lose) hold at most kTileRowsLight rows, so the
+// last units of the schedule are short (R-MAT 23: 319 -> 318 us).
+constexpr int32_t kTileRowsLight = 8192;
+constexpr int64_t kLightDeg = 9;
 constexpr int64_t kTileTargetEdges = 1 << 22;  // default; PR_TILE_EDGES overrides
 constexpr int64_t kMinTileTarget = 1 << 12;     // smaller graphs' tiles go down to this
-constexpr int64_t kUnitCost = 700000;           // default; PR_UNIT_COST overrides
+constexpr int64_t kUnitCost = 900000;           // default; PR_UNIT_COST overrides
 constexpr int64_t kMinUnitCost = 1 << 15;       // smaller graphs' units go down to this
 constexpr int64_t kMinUnitEdges = 1 << 17;     // a unit of a cut tile has at least
 constexpr int64_t kMinUnitEdgesFloor = 1 << 12; //   min(kMinUnitEdges, max(this,
@@ -132,7 +143,8 @@ constexpr int64_t kUnitEdgesPerRow = 64;        //   this * rows)) edges (min_un
 constexpr int64_t kMaxUnitEdges = 1 << 26;     // and at most this many
 constexpr int32_t kTiledMaxVertices = 1 << 30; // contribution byte offsets fit 32 bits
 constexpr int kSectorShift = 4;                 // 16 fp32 contributions per 64-byte sector
-constexpr int64_t kSectorWeight = 6;
+constexpr int64_t kSectorWeight = 10;           // default; PR_SECTOR_WEIGHT overrides
+constexpr int64_t kSectorWeightFew = 6;         // below kWgEdgesMid edges per workgroup
 constexpr int64_t kTileRowWeight = 1;
 constexpr int64_t kUnitOverhead = 27000;
 
