@@ -621,11 +621,16 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     __shared__ int32_t s_next;
     __shared__ double redd[3 * kTileWaves];
     RunState* st = a.state;
-    if (st->stop) return;  // an earlier iteration met the tolerance
+    // An earlier iteration met the tolerance: nothing to do.  The flag is
+    // tested after the reduction below, so that its load and the reduction's
+    // loads are in flight together (a stopped launch reduces stale sums and
+    // drops them).
+    const bool stopped = st->stop != 0;
     // The previous iteration's (or k_init's) sums, reduced by every workgroup
     // in the same order: its L1 distance (the stop test), its dangling mass D,
     // and -- after k_init -- sum |x0| and the count of negative entries.
     const Sums3 prev = sum_parts<kTileBlock>(a.part_prev, a.stride, a.parts_prev, redd);
+    if (stopped) return;
     if (a.t > 1 && a.tol > 0.0 && prev.l1 < a.tol) {  // iteration t - 1 met the tolerance
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             a.l1_trace[a.t - 2] = (float)prev.l1;
