@@ -553,12 +553,15 @@ __global__ __launch_bounds__(kBlock) void k_order(const int32_t* __restrict__ ol
 
 // Out-edge CSR in plan order: row p of the result is row old_of[p] of the
 // input with every target renumbered.  Edge-parallel: each workgroup covers
-// kBlock * kPermItems positions.  The rows that own them, [lo, hi], are
-// found once, by the whole workgroup; when there are at most kPermRows of
-// them, their output and input starts are staged in LDS and each position
-// finds its row there, so a lane's loads of out_ci and then of new_id go out
-// together for all its positions.  (A window over a long run of empty rows
-// searches perm_rp in global memory instead.)  A tiled plan also gets the
+// kBlock * kPermItems positions.  The rows that own them lie in [lo, hi] =
+// [win_row[w], win_row[w + 1]] (k_tile_rows over perm_rp, every window's
+// search side by side before this kernel).  When there are at most
+// kPermRows of them, each row marks its first position in an LDS array and
+// keeps the distance from its output start to its input start; a max-scan
+// carries the marks forward (owner_max_scan), so a position finds its row
+// and its input position with two LDS reads, and a lane's loads of out_ci
+// and then of new_id go out together for all its positions.  (A window over
+// a long run of empty rows searches perm_rp in global memory instead.)  A tiled plan also gets the
 // first pass of the sort by tile here: when `hist` is set, the workgroup's
 // histogram of min(tile of the renamed target, 255), stored digit-major as
 // the radix histogram of a pass over the same 4096-edge tiles
@@ -566,8 +569,12 @@ __global__ __launch_bounds__(kBlock) void k_order(const int32_t* __restrict__ ol
 constexpr int kPermItems = 16;
 constexpr int kPermRows = kBlock * kPermItems;
 static_assert(kPermRows == kRadixTile, "the permutation's windows are the sort's tiles");
+// Rows a window stages: four fewer than its positions, so that the kernel's
+// LDS is 32 KB and five workgroups fit a CU.
+constexpr int kPermStaged = kPermRows - 4;
 
 __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restrict__ perm_rp,
+                                                         const int32_t* __restrict__ win_row,
                                                          const int32_t* __restrict__ old_of,
                                                          const int32_t* __restrict__ new_id,
                                                          const int32_t* __restrict__ out_rp,
@@ -577,24 +584,38 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
                                                          int32_t* __restrict__ src_of,
                                                          TileMap map, uint32_t* __restrict__ hist,
                                                          int64_t T) {
-    __shared__ int32_t s_dst[kPermRows + 1];  // perm_rp of the window's rows
-    __shared__ int32_t s_src[kPermRows];      // out_rp[old_of[row]]
-    __shared__ uint32_t s_hist[kRadixDigits];
-    if (hist) s_hist[threadIdx.x] = 0u;
+    __shared__ int32_t s_own[kPermRows];      // slot owner_slot(i): local row of position base + i
+    __shared__ int32_t s_delta[kPermStaged];  // per local row: input start - output start
+    __shared__ int32_t s_wave[kWaves];
     const int64_t base = blockIdx.x * (int64_t)kPermRows;
     const int64_t last = (base + kPermRows < nnz ? base + kPermRows : nnz) - 1;
-    int32_t lo, hi;
-    block_owner_rows(perm_rp, base, last, n, (uint32_t*)s_src, lo, hi);
-    __syncthreads();  // s_src held the search's counts
-    const bool staged = hi - lo + 1 <= kPermRows;
-    if (staged) {
-        for (int32_t r = threadIdx.x; r <= hi - lo; r += kBlock) {
-            s_dst[r] = perm_rp[lo + r];
-            s_src[r] = out_rp[old_of[lo + r]];
-        }
-        if (threadIdx.x == 0) s_dst[hi - lo + 1] = perm_rp[hi + 1];
+    const int count = (int)(last - base + 1);
+    const int32_t lo = min(max(win_row[blockIdx.x], 0), n - 1);
+    int32_t hi = min(max(win_row[blockIdx.x + 1], lo), n - 1);
+    // rows lo .. hi are staged when they fit, or when the rows past the
+    // first kPermStaged all start after the window (hi owns the next
+    // window's first position, so a window of one-edge rows has one too
+    // many); the same in every lane
+    bool staged = hi - lo + 1 <= kPermStaged;
+    if (!staged && perm_rp[lo + kPermStaged] > last) {
+        hi = lo + kPermStaged - 1;
+        staged = true;
     }
-    __syncthreads();
+    if (staged) {
+        // position base belongs to row lo (local 0); a later row marks its
+        // first position (of rows starting at one position the last wins:
+        // the others are empty)
+        for (int i = threadIdx.x; i < count; i += kBlock) s_own[owner_slot(i)] = i == 0 ? 0 : -1;
+        __syncthreads();
+        for (int32_t r = threadIdx.x; r <= hi - lo; r += kBlock) {
+            const int32_t d = perm_rp[lo + r];
+            s_delta[r] = out_rp[old_of[lo + r]] - d;
+            const int64_t pos = (int64_t)d - base;
+            if (r > 0 && pos > 0 && pos < count) atomicMax(&s_own[owner_slot((int)pos)], r);
+        }
+        __syncthreads();
+        owner_max_scan(count, s_own, s_wave);
+    }
     int32_t row[kPermItems];
     int32_t q[kPermItems];  // input positions, clamped into [0, nnz): they fit 32 bits
 #pragma unroll
@@ -604,16 +625,9 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
         int32_t j;
         int64_t qr;
         if (staged) {
-            int32_t a = 0, b = hi - lo;  // last local row with s_dst[row] <= p
-            while (a < b) {
-                const int32_t mid = (a + b + 1) / 2;
-                if ((int64_t)s_dst[mid] <= p)
-                    a = mid;
-                else
-                    b = mid - 1;
-            }
+            const int32_t a = max(s_own[owner_slot((int)(p - base))], 0);
             j = lo + a;
-            qr = (int64_t)s_src[a] + (p - s_dst[a]);
+            qr = p + s_delta[a];
         } else {
             j = owner_row(perm_rp, p, lo, hi);
             qr = (int64_t)out_rp[old_of[j]] + (p - perm_rp[j]);
@@ -640,18 +654,21 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
         }
     }
     if (hist) {
-        // The targets go through LDS (s_src is free once every lane is past
-        // the row search), so that the count starts with no per-item
-        // registers live: counting from them directly costs occupancy.
+        // The targets go through LDS (s_own, and s_delta for the counts, are
+        // free once every lane has found its rows), so that the count starts
+        // with no per-item registers live: counting from them directly costs
+        // occupancy.
+        uint32_t* s_hist = reinterpret_cast<uint32_t*>(s_delta);
         __syncthreads();
+        s_hist[threadIdx.x] = 0u;
 #pragma unroll
-        for (int r = 0; r < kPermItems; ++r) s_src[r * kBlock + threadIdx.x] = t[r];
+        for (int r = 0; r < kPermItems; ++r) s_own[r * kBlock + threadIdx.x] = t[r];
         __syncthreads();
         DigitCounter dc;
         for (int r = 0; r < kPermItems; ++r) {
             const int i = r * kBlock + threadIdx.x;
             if (base + i > last) break;
-            const int32_t tile = tile_of(map, s_src[i]);
+            const int32_t tile = tile_of(map, s_own[i]);
             dc.add((uint32_t)(tile < kRadixDigits - 1 ? tile : kRadixDigits - 1), s_hist);
         }
         dc.flush(s_hist);
@@ -1472,9 +1489,12 @@ int plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_r
                           stream));
     if (nnz > 0) {
         const int64_t blocks = ceil_div(nnz, kBlock * kPermItems);
+        // (the transpose's tile_row scratch is free until a bucketed plan's
+        // transpose, after this)
+        PR_TRY(window_rows(s.perm_rp, n, blocks, s.tr.tile_row, stream));
         k_permute_rows<<<dim3((unsigned)blocks), kBlock, 0, stream>>>(
-            s.perm_rp, s.old_of, w.new_id, out_rp, out_ci, n, nnz, s.perm_ci, s.src_of, bt.map,
-            tiled ? s.tr.sort.hist : nullptr, blocks);
+            s.perm_rp, s.tr.tile_row, s.old_of, w.new_id, out_rp, out_ci, n, nnz, s.perm_ci,
+            s.src_of, bt.map, tiled ? s.tr.sort.hist : nullptr, blocks);
         PR_LAUNCHED("permute rows");
     }
 

@@ -299,17 +299,11 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(RadixIn in, int shift, in
 // from every lane.
 __device__ __forceinline__ int owner_slot(int i) { return i ^ ((i >> 4) & 63); }
 
-__device__ __forceinline__ void stage_owner_rows(const int32_t* __restrict__ rp, int64_t base,
-                                                 int count, int32_t lo, int32_t hi, int32_t* own,
-                                                 int32_t* wave_max) {
+// The scan half of stage_owner_rows: own[owner_slot(i)], i < count, holds a
+// mark (a row) or -1; afterwards every slot holds the largest mark at or
+// before it.  Contains barriers: call from every lane.
+__device__ __forceinline__ void owner_max_scan(int count, int32_t* own, int32_t* wave_max) {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-    for (int i = tid; i < count; i += kBlock) own[owner_slot(i)] = i == 0 ? lo : -1;
-    __syncthreads();
-    for (int32_t r = lo + 1 + tid; r <= hi; r += kBlock) {
-        const int64_t p = (int64_t)rp[r] - base;
-        if (p > 0 && p < count) atomicMax(&own[owner_slot((int)p)], r);  // in range for a valid row_ptr
-    }
-    __syncthreads();
     const int i0 = tid * kRadixItems;
     int32_t m = -1;
 #pragma unroll
@@ -335,6 +329,20 @@ __device__ __forceinline__ void stage_owner_rows(const int32_t* __restrict__ rp,
         }
     }
     __syncthreads();
+}
+
+__device__ __forceinline__ void stage_owner_rows(const int32_t* __restrict__ rp, int64_t base,
+                                                 int count, int32_t lo, int32_t hi, int32_t* own,
+                                                 int32_t* wave_max) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < count; i += kBlock) own[owner_slot(i)] = i == 0 ? lo : -1;
+    __syncthreads();
+    for (int32_t r = lo + 1 + tid; r <= hi; r += kBlock) {
+        const int64_t p = (int64_t)rp[r] - base;
+        if (p > 0 && p < count) atomicMax(&own[owner_slot((int)p)], r);  // in range for a valid row_ptr
+    }
+    __syncthreads();
+    owner_max_scan(count, own, wave_max);
 }
 
 // Stable scatter.  `scanned` is the exclusive scan of the digit-major

@@ -116,6 +116,12 @@ int check_out_row_ptr(const int32_t* rp, int32_t n, int64_t nnz, uint32_t* err, 
     return PR_OK;
 }
 
+int window_rows(const int32_t* rp, int32_t n, int64_t T, int32_t* win_row, hipStream_t stream) {
+    k_tile_rows<<<grid_for(T + 1, INT32_MAX), kBlock, 0, stream>>>(rp, n, T, win_row);
+    PR_LAUNCHED("window rows");
+    return PR_OK;
+}
+
 int transpose_device(int32_t n, int64_t nnz, const int32_t* out_rp, const int32_t* out_ci,
                      int32_t* in_rp, int32_t* in_ci, const TransposeWs& w, hipStream_t stream) {
     if (nnz == 0) return fill_u32(reinterpret_cast<uint32_t*>(in_rp), 0u, (int64_t)n + 1, stream);

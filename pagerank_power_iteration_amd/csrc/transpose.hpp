@@ -27,6 +27,12 @@ int transpose_device(int32_t n, int64_t nnz, const int32_t* out_rp, const int32_
 int transpose_row_ptr(int32_t n, int64_t nnz, const int32_t* out_ci, int32_t* in_rp,
                       const TransposeWs& ws, hipStream_t stream);
 
+// win_row[t] = the row of the CSR row pointers rp[0..n] that owns position
+// t * kRadixTile, for t < T, and win_row[T] = n - 1: rows [win_row[t],
+// win_row[t + 1]] hold every position of window t.  One binary search per
+// window, all side by side.  Asynchronous on `stream`.
+int window_rows(const int32_t* rp, int32_t n, int64_t T, int32_t* win_row, hipStream_t stream);
+
 // Bits needed to hold every vertex id in [0, n).
 int vertex_bits(int32_t n);
 
