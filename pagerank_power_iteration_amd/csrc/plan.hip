@@ -82,6 +82,7 @@ int host_take(PlanHost** out) {
         e = hipEventCreate(&h->kernel_ev[i / kTimedLaunches][i % kTimedLaunches]);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&h->chunk_ev[0], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&h->chunk_ev[1], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->stage_ev, hipEventDisableTiming);
     if (e == hipSuccess)
         e = hipHostMalloc(reinterpret_cast<void**>(&h->status), 2 * sizeof(RunStatus),
                           hipHostMallocDefault);
@@ -94,6 +95,7 @@ int host_take(PlanHost** out) {
                 (void)hipEventDestroy(h->kernel_ev[i / kTimedLaunches][i % kTimedLaunches]);
         for (int i = 0; i < 2; ++i)
             if (h->chunk_ev[i]) (void)hipEventDestroy(h->chunk_ev[i]);
+        if (h->stage_ev) (void)hipEventDestroy(h->stage_ev);
         if (h->status) (void)hipHostFree(h->status);
         std::free(h);
         return rc;
@@ -1453,23 +1455,15 @@ int plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_r
                                                           s.stats);
     PR_LAUNCHED("plan keys");
 
-    // Bucket ranges (hub bucket first), read back now: a tiled plan lays out
-    // its tiles before the permutation, which counts the edges per tile.
+    // Bucket ranges (hub bucket first), read back: a tiled plan lays out its
+    // tiles before the permutation, which counts the edges per tile.  The
+    // host waits for the copy alone, after queueing the work that does not
+    // need it (the sort by plan key, the order, the permuted row pointers and
+    // their windows), so the device runs that work while the host lays out
+    // the tiles, with no gaps between its short kernels.
     unsigned long long stats[2 * kNumBuckets];
     PR_HIP_TRY(hipMemcpyAsync(host->stage, s.stats, sizeof stats, hipMemcpyDeviceToHost, stream));
-    PR_HIP_TRY(hipStreamSynchronize(stream));
-    std::memcpy(stats, host->stage, sizeof stats);
-    int32_t row_begin[kNumBuckets + 1];  // indexed by bucket; hub rows start at 0
-    {
-        int64_t r = 0;
-        for (int b = kHubBucket; b >= 0; --b) {
-            row_begin[b] = (int32_t)r;
-            r += (int64_t)stats[b];
-        }
-        row_begin[kNumBuckets] = (int32_t)r;  // == n
-    }
-    Built bt{};
-    if (tiled) PR_TRY(lay_out_tiles(w, nnz, stats, row_begin, n, cus, bt));
+    PR_HIP_TRY(hipEventRecord(host->stage_ev, stream));
     {
         RadixIn in{};
         in.count = n;
@@ -1483,18 +1477,32 @@ int plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_r
     k_order<<<grid_for(n), kBlock, 0, stream>>>(s.old_of, out_rp, s.perm_rp, n, w.new_id, s.deg,
                                                 reinterpret_cast<uint32_t*>(s.key), w.inv_out);
     PR_LAUNCHED("order");
-
-    // 2. The out-edge CSR in plan order.
+    // row pointers of the out-edge CSR in plan order, and the permutation's
+    // windows (the transpose's tile_row scratch is free until a bucketed
+    // plan's transpose, after the permutation)
     PR_TRY(scan_exclusive(s.deg, reinterpret_cast<uint32_t*>(s.perm_rp), n, s.vsort.scan_ws,
                           stream));
+    const int64_t perm_blocks = ceil_div(nnz, kBlock * kPermItems);
+    if (nnz > 0) PR_TRY(window_rows(s.perm_rp, n, perm_blocks, s.tr.tile_row, stream));
+    PR_HIP_TRY(hipEventSynchronize(host->stage_ev));
+    std::memcpy(stats, host->stage, sizeof stats);
+    int32_t row_begin[kNumBuckets + 1];  // indexed by bucket; hub rows start at 0
+    {
+        int64_t r = 0;
+        for (int b = kHubBucket; b >= 0; --b) {
+            row_begin[b] = (int32_t)r;
+            r += (int64_t)stats[b];
+        }
+        row_begin[kNumBuckets] = (int32_t)r;  // == n
+    }
+    Built bt{};
+    if (tiled) PR_TRY(lay_out_tiles(w, nnz, stats, row_begin, n, cus, bt));
+
+    // 2. The out-edge CSR in plan order.
     if (nnz > 0) {
-        const int64_t blocks = ceil_div(nnz, kBlock * kPermItems);
-        // (the transpose's tile_row scratch is free until a bucketed plan's
-        // transpose, after this)
-        PR_TRY(window_rows(s.perm_rp, n, blocks, s.tr.tile_row, stream));
-        k_permute_rows<<<dim3((unsigned)blocks), kBlock, 0, stream>>>(
+        k_permute_rows<<<dim3((unsigned)perm_blocks), kBlock, 0, stream>>>(
             s.perm_rp, s.tr.tile_row, s.old_of, w.new_id, out_rp, out_ci, n, nnz, s.perm_ci,
-            s.src_of, bt.map, tiled ? s.tr.sort.hist : nullptr, blocks);
+            s.src_of, bt.map, tiled ? s.tr.sort.hist : nullptr, perm_blocks);
         PR_LAUNCHED("permute rows");
     }
 

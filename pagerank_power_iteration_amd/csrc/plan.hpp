@@ -246,7 +246,8 @@ struct PlanHost {
     hipEvent_t ev_begin, ev_end;
     hipEvent_t kernel_ev[2][kTimedLaunches];  // around k_tile (or k_iterate) launches
     hipEvent_t chunk_ev[2];
-    RunStatus* status;  // pinned, [2]
+    hipEvent_t stage_ev;  // a plan's read-back into `stage` is done
+    RunStatus* status;    // pinned, [2]
     char* stage;        // pinned staging buffer of stage_bytes
     size_t stage_bytes;
     PlanHost* next;     // pool link
