@@ -571,9 +571,6 @@ __global__ __launch_bounds__(kBlock) void k_order(const int32_t* __restrict__ ol
 constexpr int kPermItems = 16;
 constexpr int kPermRows = kBlock * kPermItems;
 static_assert(kPermRows == kRadixTile, "the permutation's windows are the sort's tiles");
-// Rows a window stages: four fewer than its positions, so that the kernel's
-// LDS is 32 KB and five workgroups fit a CU.
-constexpr int kPermStaged = kPermRows - 4;
 
 __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restrict__ perm_rp,
                                                          const int32_t* __restrict__ win_row,
@@ -587,7 +584,7 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
                                                          TileMap map, uint32_t* __restrict__ hist,
                                                          int64_t T) {
     __shared__ int32_t s_own[kPermRows];      // slot owner_slot(i): local row of position base + i
-    __shared__ int32_t s_delta[kPermStaged];  // per local row: input start - output start
+    __shared__ int32_t s_delta[kPermRows];  // per local row: input start - output start
     __shared__ int32_t s_wave[kWaves];
     const int64_t base = blockIdx.x * (int64_t)kPermRows;
     const int64_t last = (base + kPermRows < nnz ? base + kPermRows : nnz) - 1;
@@ -595,12 +592,12 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
     const int32_t lo = min(max(win_row[blockIdx.x], 0), n - 1);
     int32_t hi = min(max(win_row[blockIdx.x + 1], lo), n - 1);
     // rows lo .. hi are staged when they fit, or when the rows past the
-    // first kPermStaged all start after the window (hi owns the next
-    // window's first position, so a window of one-edge rows has one too
-    // many); the same in every lane
-    bool staged = hi - lo + 1 <= kPermStaged;
-    if (!staged && perm_rp[lo + kPermStaged] > last) {
-        hi = lo + kPermStaged - 1;
+    // first kPermRows all start after the window (hi owns the next window's
+    // first position, so a window of one-edge rows has one too many); the
+    // same in every lane
+    bool staged = hi - lo + 1 <= kPermRows;
+    if (!staged && perm_rp[lo + kPermRows] > last) {
+        hi = lo + kPermRows - 1;
         staged = true;
     }
     if (staged) {

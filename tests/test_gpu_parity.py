@@ -223,6 +223,38 @@ def test_plan_layout_tiled(prx, g):
     _check_tiled_layout(prx, g)
 
 
+def _empty_run_graph():
+    """15,000 vertices with exactly 12 in-edges each (one in-degree bucket),
+    of which only the first 5,000 have an out-edge, and 20,000 vertices with
+    nine out-edges and at most one in-edge: in plan order the first bucket's
+    10,000 empty rows sit between positions, so a 4096-edge window of the
+    out-edge CSR in plan order meets more rows than it can stage."""
+    heavy, light = 15_000, 20_000
+    v = np.repeat(np.arange(heavy, dtype=np.int64), 12)
+    k = np.arange(heavy * 12, dtype=np.int64)
+    src = np.concatenate([heavy + k % light, np.arange(5_000)])
+    dst = np.concatenate([v, heavy + np.arange(5_000) % light])
+    return graphgen.from_edges(heavy + light, src, dst, name="emptyrun35000")
+
+
+@pytest.mark.parametrize("g", [_empty_run_graph(), graphgen.chain(20_000)], ids=lambda g: g.name)
+def test_plan_layout_permutation_windows(prx, g):
+    """The permutation into plan order takes 4096-edge windows: a window of
+    one-edge rows (the chain) spans one row more than its edges, and the
+    empty-run graph's windows meet thousands of empty rows.  Both layouts
+    must still match their definitions bit for bit."""
+    print(f"[windows] {g.name} n={g.n} m={g.m}", flush=True)
+    _check_tiled_layout(prx, g)
+    dg = _cases.gpu_graph(g)
+    plan = prx.Plan(dg, flags=prx.PR_VALIDATE | prx.PR_PLAN_BUCKETED)
+    rp, ci, nid = (_cases.to_np(t) for t in plan.layout())
+    _, new_id = _expected_plan_order(g, [b["min_len"] for b in plan.buckets()])
+    np.testing.assert_array_equal(nid, new_id)
+    ref_rp, ref_ci = oracle.transpose(*_renumbered(g, new_id))
+    np.testing.assert_array_equal(rp, ref_rp)
+    np.testing.assert_array_equal(ci, ref_ci)
+
+
 def test_plan_layout_many_tiles(prx, monkeypatch):
     """More than 255 tiles (small tiles forced by the tuning knob): the tile
     sort then takes the light tiles' range in a second sort of its own."""
