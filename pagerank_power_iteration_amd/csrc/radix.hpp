@@ -101,47 +101,6 @@ __device__ __forceinline__ int32_t owner_row(const int32_t* __restrict__ rp, int
     return lo;
 }
 
-// The owners of edges e0 <= e1 (largest r in [0, n-1] with row_ptr[r] <= e),
-// found by the whole workgroup at once.  Each half of the workgroup searches
-// for one of them; every round each of its lanes probes one row of the
-// half's interval, the rows evenly spaced, and the count of probes at or
-// below the edge picks the sub-interval: 2^23 rows take four rounds of
-// parallel loads instead of 23 dependent ones.  Assumes row_ptr[0] <= e0
-// (the first probe counts as a hit); with a malformed row_ptr the intervals
-// still shrink every round and stay inside [0, n-1].  `cnt` is 2 * kWaves
-// words of LDS.  Contains barriers: call from every lane; every lane
-// receives both rows.
-__device__ __forceinline__ void block_owner_rows(const int32_t* __restrict__ rp, int64_t e0,
-                                                 int64_t e1, int32_t n, uint32_t* cnt,
-                                                 int32_t& r0, int32_t& r1) {
-    constexpr int kProbes = kBlock / 2;
-    const int half = threadIdx.x / kProbes, k = threadIdx.x % kProbes, wave = threadIdx.x / kWave;
-    const int64_t e = half ? e1 : e0;
-    int32_t lo[2] = {0, 0}, hi[2] = {n - 1, n - 1};
-    for (int round = 0; hi[0] > lo[0] || hi[1] > lo[1]; ++round) {
-        const int32_t step[2] = {(hi[0] - lo[0]) / kProbes + 1, (hi[1] - lo[1]) / kProbes + 1};
-        const int64_t r = lo[half] + (int64_t)k * step[half];
-        const bool hit = k == 0 || (r <= hi[half] && (int64_t)rp[r] <= e);
-        const uint64_t votes = __ballot(hit);
-        uint32_t* c = cnt + (round & 1) * kWaves;  // alternate slots: one barrier a round
-        if (lane_id() == 0) c[wave] = (uint32_t)__popcll(votes);
-        __syncthreads();
-        constexpr int kHalfWaves = kWaves / 2;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint32_t hits = 0;
-#pragma unroll
-            for (int w = 0; w < kHalfWaves; ++w) hits += c[h * kHalfWaves + w];
-            const int64_t nlo = lo[h] + (int64_t)(hits - 1) * step[h];
-            const int64_t nhi = nlo + step[h] - 1;
-            lo[h] = (int32_t)nlo;
-            hi[h] = (int32_t)(nhi < hi[h] ? nhi : hi[h]);
-        }
-    }
-    r0 = lo[0];
-    r1 = lo[1];
-}
-
 // The key of element i as stored (no checks).
 __device__ __forceinline__ int32_t radix_load(const RadixIn& in, int64_t i) { return in.keys[i]; }
 
