@@ -219,27 +219,89 @@ struct Sums3 {
     double l1, dang, sum;
 };
 
+constexpr int kPartUnroll = 8;
+
+// One round of the three sums' loads: entries j0 + u * kThreads, u <
+// kPartUnroll (0 past count).
+struct PartRound {
+    float v0[kPartUnroll], v1[kPartUnroll], v2[kPartUnroll];
+};
+
+// Every load is unconditional (an entry past count reads the last one, or
+// entry 0, and is dropped): a load under a branch is waited for where the
+// branch ends, which would make the round's loads one chain of latencies.
+// (The part arrays hold at least `stride` entries.)
+template <int kThreads, int R>
+__device__ __forceinline__ void parts_load_r(const float* __restrict__ part, int64_t stride,
+                                             int32_t count, int start, PartRound& p) {
+    const int last = count > 0 ? count - 1 : 0;
+#pragma unroll
+    for (int u = 0; u < kPartUnroll; ++u) {
+        if (u < R) {
+            const int j = start + (int)threadIdx.x + u * kThreads;
+            const int jc = j < last ? j : last;
+            p.v0[u] = part[jc];
+            p.v1[u] = part[stride + jc];
+            p.v2[u] = part[2 * stride + jc];
+        } else {
+            p.v0[u] = p.v1[u] = p.v2[u] = 0.f;
+        }
+    }
+}
+
+// The first round of the sums holds kPartFirst entries per lane (2048 for
+// 1024 lanes: every workload's units fit), the later ones kPartUnroll.
+constexpr int kPartFirst = 2;
+
+// Loads entries start + i + u * kThreads (u < R) of the three sums into lane
+// i's round, unconditionally: an entry at or past count reads the last one
+// (or entry 0) and add_round drops it.  No load sits under a branch (one
+// would be waited for where the branch ends), and no value is used here, so
+// a caller can issue other loads before the round's first use.  (The part
+// arrays hold at least `stride` entries.)
+template <int kThreads, int R>
+__device__ __forceinline__ void parts_load(const float* __restrict__ part, int64_t stride,
+                                           int32_t count, int start, PartRound& p) {
+    const int last = count > 0 ? count - 1 : 0;
+#pragma unroll
+    for (int u = 0; u < kPartUnroll; ++u) {
+        if (u < R) {
+            const int j = start + (int)threadIdx.x + u * kThreads;
+            const int jc = j < last ? j : last;
+            p.v0[u] = part[jc];
+            p.v1[u] = part[stride + jc];
+            p.v2[u] = part[2 * stride + jc];
+        } else {
+            p.v0[u] = p.v1[u] = p.v2[u] = 0.f;
+        }
+    }
+}
+
+// Adds a round's entries below count to the lane's three sums, in order.
 template <int kThreads>
-__device__ __forceinline__ Sums3 sum_parts(const float* __restrict__ part, int64_t stride,
-                                           int32_t count, double* redd) {
-    constexpr int kUnroll = 8;
+__device__ __forceinline__ void add_round(const PartRound& p, int start, int32_t count, double& r0,
+                                          double& r1, double& r2) {
+#pragma unroll
+    for (int u = 0; u < kPartUnroll; ++u) {
+        const bool in = start + (int)threadIdx.x + u * kThreads < count;
+        r0 += in ? (double)p.v0[u] : 0.0;
+        r1 += in ? (double)p.v1[u] : 0.0;
+        r2 += in ? (double)p.v2[u] : 0.0;
+    }
+}
+
+// The sums, given the first round's loads (parts_load<kThreads, kPartFirst>
+// at start 0), so that a caller can issue them before other loads and add
+// them later.
+template <int kThreads>
+__device__ __forceinline__ Sums3 sum_parts_from(const PartRound& first, const float* __restrict__ part,
+                                                int64_t stride, int32_t count, double* redd) {
     double r0 = 0.0, r1 = 0.0, r2 = 0.0;
-    for (int j0 = threadIdx.x; j0 < count; j0 += kUnroll * kThreads) {
-        float v0[kUnroll], v1[kUnroll], v2[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int j = j0 + u * kThreads;
-            const bool in = j < count;
-            v0[u] = in ? part[j] : 0.f;
-            v1[u] = in ? part[stride + j] : 0.f;
-            v2[u] = in ? part[2 * stride + j] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            r0 += (double)v0[u];
-            r1 += (double)v1[u];
-            r2 += (double)v2[u];
-        }
+    add_round<kThreads>(first, 0, count, r0, r1, r2);
+    for (int start = kPartFirst * kThreads; start < count; start += kPartUnroll * kThreads) {
+        PartRound p;
+        parts_load<kThreads, kPartUnroll>(part, stride, count, start, p);
+        add_round<kThreads>(p, start, count, r0, r1, r2);
     }
     // the three sums of the workgroup at once: one exchange through LDS
     // (`redd` holds 3 * kThreads / kWave doubles), every lane adding the
@@ -263,6 +325,14 @@ __device__ __forceinline__ Sums3 sum_parts(const float* __restrict__ part, int64
     }
     __syncthreads();
     return r;
+}
+
+template <int kThreads>
+__device__ __forceinline__ Sums3 sum_parts(const float* __restrict__ part, int64_t stride,
+                                           int32_t count, double* redd) {
+    PartRound first;
+    parts_load<kThreads, kPartFirst>(part, stride, count, 0, first);
+    return sum_parts_from<kThreads>(first, part, stride, count, redd);
 }
 
 // Fixed-point shift of the tiled pull: every row sum of every iteration is
@@ -559,20 +629,18 @@ __device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_
     }
 }
 
-// The first round of a unit's edges (nothing for an empty unit).
+// The first round of a unit's edges.  An empty unit reads block 0 of the
+// slot arrays instead (the plan's workspace always holds it; the values go
+// unused), so every unit issues the same loads with no branch: a load under
+// a branch is waited for where the branch ends, and a path with fewer loads
+// in flight makes the waits after the join count too few.
 template <int Q>
 __device__ __forceinline__ void first_round(const TileArgs& a, const TileUnit& u, EdgeRound<Q>& r) {
     const uint32_t nblk = (uint32_t)(u.e1 - u.e0) / kEdgeBlock;
-    if (nblk > 0) {
-        load_round(a.tsrc + u.e0, a.tblk + u.e0 / kEdgeBlock,
-                   __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), nblk, nblk - 1, r);
-    } else {
-#pragma unroll
-        for (int j = 0; j < Q; ++j) {
-            r.w[j] = u32x4{0u, 0u, 0u, 0u};
-            r.first[j] = 0;
-        }
-    }
+    const int32_t e0 = nblk > 0 ? u.e0 : 0;
+    const uint32_t nb = nblk > 0 ? nblk : 1u;
+    load_round(a.tsrc + e0, a.tblk + e0 / kEdgeBlock,
+               __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), nb, nb - 1, r);
 }
 
 // The update of a whole-tile unit's rows: kRowU rows per lane per step, all
@@ -626,10 +694,21 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     // loads are in flight together (a stopped launch reduces stale sums and
     // drops them).
     const bool stopped = st->stop != 0;
+    // Loads in this order: the first round of the previous iteration's sums,
+    // then the first unit's descriptor and first round of edges (which do not
+    // depend on the sums), so that the reduction waits for its own loads only
+    // and the unit's are in flight meanwhile.
+    // (Every workgroup has a first unit: the launch is at most n_units wide.)
+    PartRound pr0;
+    parts_load<kTileBlock, kPartFirst>(a.part_prev, a.stride, a.parts_prev, 0, pr0);
+    int32_t cur = blockIdx.x;
+    TileUnit u = a.units[cur];
+    EdgeRound<Q> round;
+    first_round(a, u, round);
     // The previous iteration's (or k_init's) sums, reduced by every workgroup
     // in the same order: its L1 distance (the stop test), its dangling mass D,
     // and -- after k_init -- sum |x0| and the count of negative entries.
-    const Sums3 prev = sum_parts<kTileBlock>(a.part_prev, a.stride, a.parts_prev, redd);
+    const Sums3 prev = sum_parts_from<kTileBlock>(pr0, a.part_prev, a.stride, a.parts_prev, redd);
     if (stopped) return;
     if (a.t > 1 && a.tol > 0.0 && prev.l1 < a.tol) {  // iteration t - 1 met the tolerance
         if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -666,13 +745,6 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     const double unit = ldexp(1.0, -shift);
     uint32_t* queue = &st->queue[a.t & 1][0];
     for (int32_t r = threadIdx.x; r < kTileMaxRows; r += kTileBlock) acc[r] = 0ull;
-    int32_t cur = blockIdx.x;
-    TileUnit u{};
-    EdgeRound<Q> round{};
-    if (cur < a.n_units) {
-        u = a.units[cur];
-        first_round(a, u, round);
-    }
     __syncthreads();
     while (cur < a.n_units) {
         if (signed_contrib)
@@ -917,6 +989,11 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     PR_HIP_TRY(hipGetDevice(&dev));
     if (dev != p->device)
         return fail(PR_ERR_ARG, "plan belongs to device %d but device %d is current", p->device, dev);
+    // k_tile starts every workgroup on unit blockIdx.x without a check: a
+    // tiled plan has a unit per tile at least, and launches at most one
+    // workgroup per unit
+    if (p->tiled && (p->n_units < 1 || p->tile_grid > p->n_units))
+        return fail(PR_ERR_ARG, "tiled plan with %d units for %d workgroups", p->n_units, p->tile_grid);
     hipStream_t stream = as_stream(stream_v);
 
     // Per-iteration sums: part holds two [3][stride] sets.  A tiled run
