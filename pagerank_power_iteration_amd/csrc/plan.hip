@@ -158,7 +158,8 @@ struct PlanWs {  // lives as long as the plan
     TileUnit* units;
     TileFix* fixes;
     int32_t* fix_rows;
-    int32_t* fix_win;  // [n / kFixBlock + 1] the cut tile holding each 256-row window's first row
+    int32_t* fix_win;    // [n / kFixBlock + 1] the cut tile holding each 256-row window's first row
+    uint32_t* fix_done;  // [n_fixes_max]
     long long* partial;
     int64_t n_tiles_max, n_units_max, n_fixes_max, n_partial_max, n_edge_slots_max;
     size_t bytes;
@@ -200,7 +201,10 @@ PlanWs carve_ws(void* base, int32_t n, int64_t nnz, bool tiled) {
     w.contrib0 = c.take<float>((size_t)n);
     w.contrib1 = c.take<float>((size_t)n);
     const int64_t batches = ceil_div(w.n_items_max, kBatchItems);
-    w.part_stride = (batches > w.n_units_max ? batches : w.n_units_max) + kMaxGrid;
+    // bucketed: batches + k_hubfix workgroups; tiled: units + cut tiles (or
+    // + k_tilefix workgroups)
+    const int64_t tiled_parts = w.n_units_max + w.n_fixes_max;
+    w.part_stride = (batches > tiled_parts ? batches : tiled_parts) + kMaxGrid;
     w.part = c.take<float>((size_t)(6 * w.part_stride));  // two sets of [3][stride]
     w.state = c.take<RunState>(1);
     if (!tiled) {
@@ -219,6 +223,7 @@ PlanWs carve_ws(void* base, int32_t n, int64_t nnz, bool tiled) {
         w.fixes = c.take<TileFix>((size_t)w.n_fixes_max);
         w.fix_rows = c.take<int32_t>((size_t)w.n_fixes_max + 1);
         w.fix_win = c.take<int32_t>((size_t)ceil_div(n, kFixBlock) + 1);
+        w.fix_done = c.take<uint32_t>((size_t)w.n_fixes_max);
         w.partial = c.take<long long>((size_t)w.n_partial_max);
     }
     w.bytes = c.used;
@@ -924,6 +929,7 @@ struct Built {
     std::vector<TileFix> fixes;
     std::vector<int32_t> fix_rows;
     std::vector<int32_t> fix_win;
+    bool fused = false;
     // tiled: where the work lists were uploaded
     const Tile* dev_tiles = nullptr;
     const TileUnit* dev_units = nullptr;
@@ -1280,11 +1286,12 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
             const int64_t count_min = ceil_div((int64_t)(e1 - e0), kMaxUnitEdges);
             if (count < count_min) count = count_min;
             if (count <= 1) {
-                list.push_back({(int64_t)(c1 - c0) + per_unit, TileUnit{t, e0, e1, -1, row0, rows, {0, 0}}});
+                list.push_back({(int64_t)(c1 - c0) + per_unit, TileUnit{t, e0, e1, -1, row0, rows, -1, 1}});
                 continue;
             }
             if (slot + count * rows > w.n_partial_max)
                 return fail(PR_ERR_ARG, "tile slots exceed the planned bound");
+            const int32_t fix = (int32_t)bt.fixes.size();
             bt.fixes.push_back(TileFix{row0, rows, (int32_t)slot, (int32_t)count});
             int64_t a = e0;
             for (int64_t j = 0; j < count; ++j) {
@@ -1293,7 +1300,8 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
                                    : kEdgeBlock * block_at(a / kEdgeBlock + 1,
                                                            e1 / kEdgeBlock - (count - 1 - j),
                                                            c0 + (c1 - c0) * (double)(j + 1) / (double)count);
-                const TileUnit u{t, (int32_t)a, (int32_t)b, (int32_t)(slot + j * rows), row0, rows, {0, 0}};
+                const TileUnit u{t, (int32_t)a, (int32_t)b, (int32_t)(slot + j * rows), row0, rows, fix,
+                                  (int32_t)count};
                 list.push_back({(int64_t)(cost_at(b) - cost_at(a)) + per_unit, u});
                 a = b;
             }
@@ -1310,20 +1318,29 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
         return fail(PR_ERR_ARG, "tile units exceed the planned bound");
     bt.n_units = (int32_t)bt.units.size();
     bt.n_fixes = (int32_t)bt.fixes.size();
+    // Finish the cut tiles in k_tile when there are some and no tile's finish
+    // is long (its last unit adds (count - 1) * rows slot entries).
+    bt.fused = bt.n_fixes > 0;
+    for (const TileFix& f : bt.fixes)
+        if ((int64_t)(f.count - 1) * f.rows > kFuseSlots) bt.fused = false;
+    if (const char* env = std::getenv("PR_TILE_FUSE"))  // tuning knob: 0 k_tilefix, 1 k_tile
+        bt.fused = std::atoi(env) != 0;
+    if (!bt.fused)
+        for (TileUnit& u : bt.units) u.fix = -1;
     bt.fix_rows.assign(1, 0);
-    for (const TileFix& f : bt.fixes) bt.fix_rows.push_back(bt.fix_rows.back() + f.rows);
-    // for k_tilefix: the last cut tile whose rows start at or before row
-    // w * kFixBlock of the cut tiles' rows, for every window w
     bt.fix_win.clear();
-    {
+    if (!bt.fused) {
+        for (const TileFix& f : bt.fixes) bt.fix_rows.push_back(bt.fix_rows.back() + f.rows);
+        // for k_tilefix: the last cut tile whose rows start at or before row
+        // w * kFixBlock of the cut tiles' rows, for every window w
         const int32_t total = bt.fix_rows.back();
         int32_t i = 0;
         for (int32_t g0 = 0; g0 < total; g0 += kFixBlock) {
             while (i + 1 < bt.n_fixes && bt.fix_rows[(size_t)i + 1] <= g0) ++i;
             bt.fix_win.push_back(i);
         }
-        if (bt.fix_win.empty()) bt.fix_win.push_back(0);
     }
+    if (bt.fix_win.empty()) bt.fix_win.push_back(0);
     // The work lists go up in one copy: packed one after another from the
     // start of their workspace region (which holds each at its largest), from
     // the pinned stage (nothing uses it now: the read-back above was waited
@@ -1341,7 +1358,7 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
             total += align_up(bytes[i]);
         }
         char* region = reinterpret_cast<char*>(w.tiles);
-        if (total > (size_t)(reinterpret_cast<char*>(w.partial) - region))
+        if (total > (size_t)(reinterpret_cast<char*>(w.fix_done) - region))
             return fail(PR_ERR_ARG, "work lists exceed their workspace region");
         PR_TRY(host_stage(host, total));
         for (int i = 0; i < 5; ++i)
@@ -1353,6 +1370,9 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
         bt.dev_fix_rows = reinterpret_cast<const int32_t*>(region + off[3]);
         bt.dev_fix_win = reinterpret_cast<const int32_t*>(region + off[4]);
     }
+    // every cut tile's count of finished units starts at zero (the unit that
+    // finishes a tile sets it back to zero)
+    if (bt.fused) PR_TRY(fill_u32(w.fix_done, 0u, bt.n_fixes, stream));
     bt.tile_grid = (int32_t)(grid < bt.n_units ? grid : (bt.n_units > 0 ? bt.n_units : 1));
     return PR_OK;
 }
@@ -1546,6 +1566,8 @@ int plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_r
     p->units = bt.dev_units;
     p->n_units = bt.n_units;
     p->fixes = bt.dev_fixes;
+    p->fused = bt.fused;
+    p->fix_done = w.fix_done;
     p->fix_rows = bt.dev_fix_rows;
     p->fix_win = bt.dev_fix_win;
     p->n_fixes = bt.n_fixes;

@@ -99,8 +99,12 @@ constexpr int kFinalBlock = 1024;
 // point (contribution * 2^shift, truncated): integer addition is exact and
 // order-free, so the sums do not depend on scheduling.  A tile whose
 // estimated cost exceeds the unit cost is cut into units of about equal
-// cost; each unit writes its accumulators to a slot of `partial`, and
-// k_tilefix adds a tile's slots and applies the update.
+// cost; each unit writes its accumulators to a slot of `partial`.  When no
+// cut tile has more than kFuseSlots slot entries besides one unit's own, the
+// unit that finishes a tile last adds the other slots and applies the
+// update, which spares a launch; otherwise k_tilefix finishes every cut tile
+// after k_tile, because one workgroup adding that many entries holds the
+// launch's end back.
 //
 // Cost estimate of a range of tile edges, in edge-equivalents: its edges,
 // plus kSectorWeight per distinct 64-byte sector of contributions it gathers
@@ -141,6 +145,11 @@ constexpr int64_t kMinUnitEdges = 1 << 17;     // a unit of a cut tile has at le
 constexpr int64_t kMinUnitEdgesFloor = 1 << 12; //   min(kMinUnitEdges, max(this,
 constexpr int64_t kUnitEdgesPerRow = 64;        //   this * rows)) edges (min_unit_edges)
 constexpr int64_t kMaxUnitEdges = 1 << 26;     // and at most this many
+// Cut tiles are finished in k_tile when (count - 1) * rows <= kFuseSlots for
+// each.  Measured on gfx950 (iteration time, finish in k_tile against
+// k_tilefix): R-MAT 18, largest 896: 22.1 against 25.5 us; R-MAT 21,
+// 184,320: 85.5 against 87.0 us; R-MAT 23, 491,520: 311.5 against 304.1 us.
+constexpr int64_t kFuseSlots = 1 << 18;
 constexpr int32_t kTiledMaxVertices = 1 << 30; // contribution byte offsets fit 32 bits
 constexpr int kSectorShift = 4;                 // 16 fp32 contributions per 64-byte sector
 constexpr int64_t kSectorWeight = 10;           // default; PR_SECTOR_WEIGHT overrides
@@ -190,7 +199,8 @@ struct Tile {
 };
 
 // A unit of k_tile: edges [e0, e1) of one tile (rows [row0, row0 + rows)).
-// slot < 0: the unit is the whole tile and applies the update; otherwise its
+// slot < 0: the unit is the whole tile and applies the update; otherwise the
+// tile is cut tile `fix`, cut into `count` units, and the unit's
 // accumulators go to partial[slot, slot + rows).
 struct TileUnit {
     int32_t tile;
@@ -199,11 +209,15 @@ struct TileUnit {
     int32_t slot;
     int32_t row0;
     int32_t rows;
-    int32_t pad[2];
+    int32_t fix;    // -1 for a whole tile
+    int32_t count;  // 1 for a whole tile
 };
 
-// A tile cut into units: k_tilefix adds partial[first + j*rows + r] over
-// j < count for each of its rows.
+// A tile cut into `count` units: unit j's accumulators sit at
+// partial[first + j*rows, + rows).  In a plan that finishes cut tiles in
+// k_tile, the unit that finishes last adds the others' slots to its own
+// accumulators and applies the update; otherwise k_tilefix does, after
+// k_tile.
 struct TileFix {
     int32_t row0;
     int32_t rows;
@@ -280,8 +294,9 @@ struct pr_plan {
     int32_t n_chunk_rows;
     float* hub_part;       // chunk sums
     float* part;           // 2 x [3][part_stride]: L1, dangling mass and sum of x' per
-                           // item batch or unit, then per k_hubfix / k_tilefix
-                           // workgroup (tiled runs alternate the two sets)
+                           // item batch, then per k_hubfix workgroup; or per
+                           // unit, then per cut tile (tiled runs alternate the
+                           // two sets)
     int64_t part_stride;
     int32_t n_batches;
     pr::RunState* state;
@@ -304,8 +319,10 @@ struct pr_plan {
     const pr::TileUnit* units;
     int32_t n_units;
     const pr::TileFix* fixes;
-    const int32_t* fix_rows;  // [n_fixes + 1] rows of the cut tiles before each one
-    const int32_t* fix_win;   // per 256-row window of those rows: the cut tile of its first row
+    bool fused;             // cut tiles finished in k_tile (else by k_tilefix)
+    uint32_t* fix_done;     // fused: [n_fixes] units of each cut tile done in this launch (0 between launches)
+    const int32_t* fix_rows;  // k_tilefix: [n_fixes + 1] rows of the cut tiles before each one
+    const int32_t* fix_win;   // k_tilefix: per 256-row window of those rows, the cut tile of its first row
     int32_t n_fixes;
     int32_t n_fix_rows;
     long long* partial;

@@ -490,7 +490,9 @@ struct TileArgs {
     float* __restrict__ contrib_out;
     float* __restrict__ xi;
     long long* __restrict__ partial;
-    float* __restrict__ part;  // [3][stride]: this iteration's per-unit sums
+    const TileFix* __restrict__ fixes;
+    uint32_t* __restrict__ fix_done;
+    float* __restrict__ part;  // [3][stride]: this iteration's sums, per unit then per cut tile
     const float* __restrict__ part_prev;  // [3][stride]: the previous iteration's
     int64_t stride;
     RunState* state;
@@ -674,19 +676,72 @@ __device__ __forceinline__ void update_rows(const TileArgs& a, unsigned long lon
     }
 }
 
+// A cut tile's units run on workgroups of any XCD, and an XCD's L2 does not
+// see another's.  So a unit's slot goes out with device-scope stores, which
+// write through to the level every XCD reads, and the unit that finishes the
+// tile reads the other slots with device-scope loads.
+__device__ __forceinline__ void store_device(long long* p, long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ long long load_device(long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this lane's vector memory operations are done: s_waitcnt with
+// vmcnt 0 (bits 3:0 and 15:14) and the other counters at their maximum
+// (expcnt 7 in bits 6:4, lgkmcnt 15 in bits 11:8).  A device-scope store is
+// done once the level every XCD reads holds it.
+__device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// The unit that finishes cut tile fx (its own slot is own_slot, its
+// accumulators still in acc) adds the other units' slots into acc: entries
+// [first, first + count*rows) minus its own, kFixU per lane with their loads
+// issued together, added with LDS atomics (a step may meet a row twice when
+// the tile has fewer rows than the workgroup has lanes).  The integer sums
+// are exact, so the order of the additions does not matter.
+constexpr int kFixU = 16;
+
+__device__ __forceinline__ void gather_slots(const TileArgs& a, unsigned long long* acc,
+                                             const TileFix& fx, int32_t own_slot) {
+    const uint32_t rows = (uint32_t)fx.rows;
+    const uint32_t own = (uint32_t)(own_slot - fx.first);
+    const uint32_t total = (uint32_t)(fx.count - 1) * rows;
+    long long* base = a.partial + fx.first;
+    for (uint32_t e0 = threadIdx.x; e0 < total; e0 += kFixU * kTileBlock) {
+        long long v[kFixU];
+        uint32_t r[kFixU];
+#pragma unroll
+        for (int i = 0; i < kFixU; ++i) {
+            const uint32_t e = e0 + (uint32_t)(i * kTileBlock);
+            const uint32_t ec = e < total ? e : total - 1;
+            const uint32_t o = ec < own ? ec : ec + rows;  // skip the own slot
+            r[i] = o % rows;
+            v[i] = load_device(base + o);
+        }
+#pragma unroll
+        for (int i = 0; i < kFixU; ++i)
+            if (e0 + (uint32_t)(i * kTileBlock) < total) atomicAdd(&acc[r[i]], (unsigned long long)v[i]);
+    }
+}
+
 // One workgroup per CU.  Workgroup b starts with unit b, then takes units
 // gridDim.x, gridDim.x + 1, ... from queue 0, one when its current unit's
 // edges are done, until they run out.  A whole-tile unit applies the update
 // to its rows and writes its three sums; a unit of a cut tile writes its
-// accumulators to its slot (and zero sums).
+// accumulators to its slot (and zero sums) and counts itself done on the
+// tile; the tile's last unit adds the other slots to its accumulators,
+// applies the update and writes the tile's sums to the tile's own entry
+// (after the units'), so where they land does not depend on which unit was
+// last.  In a plan that leaves the cut tiles to k_tilefix (kFused false), a
+// unit of a cut tile only writes its slot.
 // The accumulators are all zero between units: each unit's epilogue clears
 // the rows it read.  The next unit's descriptor and first round of edges are
 // loaded before this unit's epilogue, so their latency overlaps it.
-template <int Q>
+template <int Q, bool kFused>
 __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     __shared__ unsigned long long acc[kTileMaxRows + 1];  // + the trash row of padding edges
     __shared__ float red[3][kTileWaves];
     __shared__ int32_t s_next;
+    __shared__ int32_t s_last;
     __shared__ double redd[3 * kTileWaves];
     RunState* st = a.state;
     // An earlier iteration met the tolerance: nothing to do.  The flag is
@@ -751,12 +806,28 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
             accumulate<true, Q>(a, u.e0, u.e1, scale, acc, round);
         else
             accumulate<false, Q>(a, u.e0, u.e1, scale, acc, round);
+        // A unit of a cut tile finished here sends its slot out (once every
+        // wavefront's additions are in) before the claim, so that the stores
+        // and the claim are in flight together.
+        const bool cut = u.slot >= 0;
+        const bool fused = kFused && cut;
+        if (fused) {
+            __syncthreads();
+            for (int32_t r = threadIdx.x; r < u.rows; r += kTileBlock)
+                store_device(a.partial + (int64_t)u.slot + r, (long long)acc[r]);
+        }
         // claim the next unit only now: a claim made earlier would hold a
         // unit back behind this one while other workgroups run out of work
         // (with no more units than workgroups there is none to claim)
         if (threadIdx.x == 0)
             s_next = (int32_t)gridDim.x >= a.n_units ? a.n_units
                                                      : (int32_t)(gridDim.x + atomicAdd(queue, 1u));
+        if (fused) {
+            wait_vector_memory();  // this lane's slot stores are done ...
+            __syncthreads();       // ... and every lane's, before the count
+            if (threadIdx.x == 0)
+                s_last = atomicAdd(&a.fix_done[u.fix], 1u) + 1u == (uint32_t)u.count ? 1 : 0;
+        }
         __syncthreads();
         const int32_t nxt = s_next;
         TileUnit un{};
@@ -765,13 +836,24 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
             first_round(a, un, round);
         }
         Acc sums;
-        if (u.slot < 0) {
+        int32_t sum_at = cur;
+        if (!cut) {
             update_rows(a, acc, u.row0, u.rows, unit, k, sums);
-        } else {
+        } else if (!kFused) {  // k_tilefix finishes the tile
             for (int32_t r = threadIdx.x; r < u.rows; r += kTileBlock) {
                 a.partial[(int64_t)u.slot + r] = (long long)acc[r];
                 acc[r] = 0ull;
             }
+        } else if (s_last) {  // every other unit's slot is out: finish the tile
+            const TileFix fx = a.fixes[u.fix];
+            gather_slots(a, acc, fx, u.slot);
+            if (threadIdx.x == 0)  // no unit of this launch counts on it again
+                __hip_atomic_store(&a.fix_done[u.fix], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            update_rows(a, acc, u.row0, u.rows, unit, k, sums);
+            sum_at = a.n_units + u.fix;
+        } else {
+            for (int32_t r = threadIdx.x; r < u.rows; r += kTileBlock) acc[r] = 0ull;
         }
         const float l1 = wave_sum(sums.l1), dg = wave_sum(sums.dang), sm = wave_sum(sums.sum);
         if (lane_id() == 0) {
@@ -788,9 +870,14 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
                 t1 += red[1][w];
                 t2 += red[2][w];
             }
-            a.part[cur] = t0;
-            a.part[a.stride + cur] = t1;
-            a.part[2 * a.stride + cur] = t2;
+            a.part[sum_at] = t0;
+            a.part[a.stride + sum_at] = t1;
+            a.part[2 * a.stride + sum_at] = t2;
+            if (sum_at != cur) {  // a cut tile's units hold zero sums
+                a.part[cur] = 0.f;
+                a.part[a.stride + cur] = 0.f;
+                a.part[2 * a.stride + cur] = 0.f;
+            }
         }
         cur = nxt;
         u = un;
@@ -1019,14 +1106,17 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
         PR_LAUNCHED("init finalize");
     }
-    int32_t tilefix_grid = (int32_t)((p->n_fix_rows + kFixBlock - 1) / kFixBlock);
     bool wide_rounds = p->n_units > 0 && p->n_slots >= kWideUnitSlots * (int64_t)p->n_units;
     if (const char* env = std::getenv("PR_TILE_Q")) {  // tuning knob: edge blocks per round
         if (std::atoi(env) == 1) wide_rounds = false;
         if (std::atoi(env) == 2) wide_rounds = true;
     }
+    int32_t tilefix_grid = p->fused ? 0 : (int32_t)((p->n_fix_rows + kFixBlock - 1) / kFixBlock);
     if (tilefix_grid > kMaxGrid) tilefix_grid = kMaxGrid;
-    const int32_t iter_parts = p->tiled ? p->n_units + tilefix_grid : p->n_batches + p->fix_grid;
+    // a tiled run's sums: per unit, then per cut tile (finished in k_tile) or
+    // per k_tilefix workgroup
+    const int32_t iter_parts = p->tiled ? p->n_units + (p->fused ? p->n_fixes : tilefix_grid)
+                                        : p->n_batches + p->fix_grid;
     f.parts = iter_parts;
 
     IterArgs a{};
@@ -1065,6 +1155,8 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     ta.inv_out = p->inv_out;
     ta.xi = p->xi;
     ta.partial = p->partial;
+    ta.fixes = p->fixes;
+    ta.fix_done = p->fix_done;
     ta.stride = p->part_stride;
     ta.state = p->state;
     ta.l1_trace = l1_trace;
@@ -1107,10 +1199,15 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
             ta.part_prev = part_set[(t - 1) & 1];
             ta.parts_prev = t == 1 ? p->init_grid : iter_parts;
             ta.t = t;
-            if (wide_rounds)
-                k_tile<kTileQWide><<<dim3((unsigned)p->tile_grid), kTileBlock, 0, stream>>>(ta);
+            const dim3 grid((unsigned)p->tile_grid);
+            if (wide_rounds && p->fused)
+                k_tile<kTileQWide, true><<<grid, kTileBlock, 0, stream>>>(ta);
+            else if (wide_rounds)
+                k_tile<kTileQWide, false><<<grid, kTileBlock, 0, stream>>>(ta);
+            else if (p->fused)
+                k_tile<kTileQNarrow, true><<<grid, kTileBlock, 0, stream>>>(ta);
             else
-                k_tile<kTileQNarrow><<<dim3((unsigned)p->tile_grid), kTileBlock, 0, stream>>>(ta);
+                k_tile<kTileQNarrow, false><<<grid, kTileBlock, 0, stream>>>(ta);
             PR_LAUNCHED("tile");
         } else {
             k_iterate<<<dim3((unsigned)p->grid), kIterBlock, 0, stream>>>(a);

@@ -421,6 +421,34 @@ def test_edge_blocks_per_round_agree(prx, make, monkeypatch):
     _cases.assert_parity(_cases.to_np(xs["2"][0]), _cases.to_np(xs["2"][1]), None, ref)
 
 
+@pytest.mark.parametrize("make", [lambda: graphgen.rmat(15), lambda: graphgen.rmat(18),
+                                  lambda: _hubs_graph(70_000, 1, 7),
+                                  lambda: _hubs_graph(140_001, 3, 5)],
+                         ids=["rmat15", "rmat18", "hub70000", "hub140001"])
+def test_cut_tiles_finished_either_way(prx, make, monkeypatch):
+    """A tile cut into units is finished either inside the gather kernel, by
+    the unit that completes it last (which one that is varies from run to
+    run), or by a second kernel after it; the plan picks one (PR_TILE_FUSE
+    forces either).  Both must match the oracle, and the in-kernel finish
+    must give the same ranks on every run.  The hub graphs' tiles are cut
+    into many units, so the finishing unit adds slots over several rounds,
+    and several of its lanes meet the same row in a round (tiles of fewer
+    rows than the workgroup has lanes)."""
+    g = make()
+    ref = oracle.pagerank(g.row_ptr, g.col_idx, d=D, max_iter=25)
+    dg = _cases.gpu_graph(g)
+    for fuse in ("0", "1"):
+        monkeypatch.setenv("PR_TILE_FUSE", fuse)
+        plan = prx.Plan(dg)
+        a = plan.run(d=D, max_iter=25)
+        xa, la = a.x.clone(), a.l1_trace.clone()
+        b = plan.run(d=D, max_iter=25)
+        torch.cuda.synchronize()
+        assert torch.equal(xa, b.x) and torch.equal(la, b.l1_trace), fuse
+        _cases.assert_parity(_cases.to_np(xa), _cases.to_np(la), None, ref)
+        plan.close()
+
+
 @pytest.mark.parametrize("q", ["1", "2"])
 def test_signed_start_vector_both_rounds(prx, q, monkeypatch):
     """The signed fixed-point conversion under one and under two edge blocks
