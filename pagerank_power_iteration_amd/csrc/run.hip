@@ -563,38 +563,50 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
     return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
+// Blocks b, b + stride, ..., Q of them.
 template <int Q>
 __device__ __forceinline__ void load_round(const int32_t* ts, const int32_t* tb, uint32_t b,
-                                           uint32_t nblk, uint32_t last, EdgeRound<Q>& r) {
+                                           uint32_t stride, uint32_t nblk, uint32_t last,
+                                           EdgeRound<Q>& r) {
     const uint32_t lane = lane_id();
 #pragma unroll
     for (int j = 0; j < Q; ++j) {
-        const uint32_t bc = block_of(b + (uint32_t)(j * kTileWaves), nblk, last);
+        const uint32_t bc = block_of(b + (uint32_t)j * stride, nblk, last);
         r.first[j] = load_uniform(tb + bc);
         r.w[j] = load_nt_at((const u32x4*)ts, bc * (kEdgeBlock / 4) + lane);
     }
 }
 
 // Adds the contributions of the unit's edge slots [e0, e1) (whole blocks)
-// into acc[row offset].  Wavefront w takes blocks w, w + kTileWaves, ...,
-// Q per round; `next` holds its first round, loaded by the caller, and
-// each round loads the following one before gathering its own
-// contributions.  In one gather instruction lane l reads the source of edge
+// into acc[row offset].  A round of a wavefront is Q blocks: its first round
+// is blocks w, w + kTileWaves, ... (wavefront w; `next` holds it, loaded by
+// the caller), and each later one the next Q blocks of the unit's counter
+// *s_blk (kTileWaves * Q at the start), claimed by lane 0 when the round
+// before starts.  Each round loads the following one before gathering its
+// own contributions.  Wavefronts of a workgroup progress at different rates
+// (the oldest are served first), so with a fixed share each the first
+// finished a unit of 10^5 edges at about half its time on R-MAT 23, and the
+// unit's last blocks ran on a few wavefronts; the counter keeps them all
+// busy to the end.  In one gather instruction lane l reads the source of edge
 // l + 64*i of a block: consecutive lanes, neighbouring sources.  A narrow
 // block decodes its slots; a wide one (rare) loads its rows here.
 template <bool kSigned, int Q>
 __device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_t e1, float scale,
-                                           unsigned long long* acc, EdgeRound<Q>& next) {
-    constexpr uint32_t kStep = (uint32_t)kTileWaves * Q;
+                                           unsigned long long* acc, uint32_t* s_blk,
+                                           EdgeRound<Q>& next) {
     const int32_t* ts = a.tsrc + e0;
     const uint16_t* td = a.tdst + e0;
     const int32_t* tb = a.tblk + e0 / kEdgeBlock;
     const uint32_t nblk = (uint32_t)(e1 - e0) / kEdgeBlock;
     const uint32_t last = nblk > 0 ? nblk - 1 : 0;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    for (uint32_t b = wave; b < nblk; b += kStep) {
+    uint32_t b = wave, stride = kTileWaves;  // this round: blocks b + j * stride
+    while (b < nblk) {
         const EdgeRound<Q> cur = next;
-        load_round(ts, tb, b + kStep, nblk, last, next);
+        uint32_t nb = 0;
+        if (lane_id() == 0) nb = atomicAdd(s_blk, (uint32_t)Q);
+        nb = __builtin_amdgcn_readlane(nb, 0);
+        load_round(ts, tb, nb, 1u, nblk, last, next);
         uint32_t src[Q][4], row[Q][4];
 #pragma unroll
         for (int j = 0; j < Q; ++j) {
@@ -605,7 +617,7 @@ __device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_
                     row[j][i] = cur.w[j][i] >> 16;
                 }
             } else {
-                const uint32_t bc = block_of(b + (uint32_t)(j * kTileWaves), nblk, last);
+                const uint32_t bc = block_of(b + (uint32_t)j * stride, nblk, last);
                 const u32x2 r2 = load_nt_at((const u32x2*)td, bc * (kEdgeBlock / 4) + lane_id());
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -621,13 +633,15 @@ __device__ __forceinline__ void accumulate(const TileArgs& a, int32_t e0, int32_
             for (int i = 0; i < 4; ++i) v[j][i] = load_at(a.contrib_in, src[j][i]);
 #pragma unroll
         for (int j = 0; j < Q; ++j) {
-            const bool live = b + (uint32_t)(j * kTileWaves) < nblk;
+            const bool live = b + (uint32_t)j * stride < nblk;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const unsigned long long f = to_fixed<kSigned>(v[j][i], scale);
                 atomicAdd(&acc[row[j][i]], live ? f : 0ull);
             }
         }
+        b = nb;
+        stride = 1;
     }
 }
 
@@ -642,7 +656,7 @@ __device__ __forceinline__ void first_round(const TileArgs& a, const TileUnit& u
     const int32_t e0 = nblk > 0 ? u.e0 : 0;
     const uint32_t nb = nblk > 0 ? nblk : 1u;
     load_round(a.tsrc + e0, a.tblk + e0 / kEdgeBlock,
-               __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), nb, nb - 1, r);
+               __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), (uint32_t)kTileWaves, nb, nb - 1, r);
 }
 
 // The update of a whole-tile unit's rows: kRowU rows per lane per step, all
@@ -742,6 +756,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     __shared__ float red[3][kTileWaves];
     __shared__ int32_t s_next;
     __shared__ int32_t s_last;
+    __shared__ uint32_t s_blk;  // the current unit's next unclaimed edge block
     __shared__ double redd[3 * kTileWaves];
     RunState* st = a.state;
     // An earlier iteration met the tolerance: nothing to do.  The flag is
@@ -800,12 +815,13 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     const double unit = ldexp(1.0, -shift);
     uint32_t* queue = &st->queue[a.t & 1][0];
     for (int32_t r = threadIdx.x; r < kTileMaxRows; r += kTileBlock) acc[r] = 0ull;
+    if (threadIdx.x == 0) s_blk = (uint32_t)(kTileWaves * Q);
     __syncthreads();
     while (cur < a.n_units) {
         if (signed_contrib)
-            accumulate<true, Q>(a, u.e0, u.e1, scale, acc, round);
+            accumulate<true, Q>(a, u.e0, u.e1, scale, acc, &s_blk, round);
         else
-            accumulate<false, Q>(a, u.e0, u.e1, scale, acc, round);
+            accumulate<false, Q>(a, u.e0, u.e1, scale, acc, &s_blk, round);
         // A unit of a cut tile finished here sends its slot out (once every
         // wavefront's additions are in) before the claim, so that the stores
         // and the claim are in flight together.
@@ -829,6 +845,9 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
                 s_last = atomicAdd(&a.fix_done[u.fix], 1u) + 1u == (uint32_t)u.count ? 1 : 0;
         }
         __syncthreads();
+        // every wavefront is past its last claim: the next unit's counter
+        // (the next write of s_blk's readers follows the barrier below)
+        if (threadIdx.x == 0) s_blk = (uint32_t)(kTileWaves * Q);
         const int32_t nxt = s_next;
         TileUnit un{};
         if (nxt < a.n_units) {
