@@ -1238,12 +1238,12 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
         return lo;
     };
 
-    // A smaller graph gets a smaller unit cost: when the tiles at the default
-    // cost would give fewer than two units per workgroup, the cost becomes
-    // (total cost) / (2 * grid), and a tile of few rows may then be cut
-    // into units down to min_unit_edges(rows) edges (kMinUnitEdges
-    // otherwise): the hubs' tiles of such a graph would else be its longest
-    // units.
+    // The unit cost from the total: when the tiles at kUnitCost would give
+    // fewer than two units per workgroup, the cost is (total cost) /
+    // (2 * grid), and a tile of few rows may then be cut into units down to
+    // min_unit_edges(rows) edges (kMinUnitEdges otherwise): the hubs' tiles
+    // of such a graph would else be its longest units.  Otherwise it is
+    // kUnitShare * (total cost) / grid.
     bool fine_cuts = false;
     if (!unit_env && tiles > 0) {
         const double total = cost_at(slots) - cost_at(0);
@@ -1259,6 +1259,9 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
             const int64_t t2 = (int64_t)(total / (double)(2 * grid));
             unit_cost = t2 > kMinUnitCost ? t2 : kMinUnitCost;
             fine_cuts = true;
+        } else {
+            const int64_t t1 = (int64_t)(kUnitShare * total / (double)grid);
+            unit_cost = t1 > kMinUnitCost ? t1 : kMinUnitCost;
         }
     }
 

@@ -119,7 +119,15 @@ constexpr int kFinalBlock = 1024;
 // longer than units of the same estimate, ending the launch late.  Graphs
 // with little work per workgroup (R-MAT 18) keep weight 6, their best.
 // Units go to the queue in decreasing estimated cost, so the longest start
-// first.
+// first.  A unit costs kUnitShare of one workgroup's share of the total
+// (graphs with at least two units per workgroup at kUnitCost; smaller ones
+// get half a share, see build_tiled): fewer, longer units cut fewer tiles
+// (less partial traffic, fewer accumulator passes) while the longest still
+// ends with the rest.  Swept on gfx950 with every workgroup's wavefronts
+// sharing a unit's blocks (R-MAT 22, 23, 24; shares 0.6-1.1 of a
+// workgroup's): 0.95 was best or within 2% of best on each (R-MAT 23 287 ->
+// 274 us, R-MAT 22 158 -> 149 us, R-MAT 24 734 -> 651 us against the fixed
+// cost of 900K before).
 constexpr int32_t kTileMaxRows = 16384;         // 128 KB of accumulators
 constexpr int32_t kTileMinRows = 64;
 // Rows per tile at most, by edges per workgroup of the launch: a tile's
@@ -139,7 +147,8 @@ constexpr int32_t kTileRowsLight = 8192;
 constexpr int64_t kLightDeg = 9;
 constexpr int64_t kTileTargetEdges = 1 << 22;  // default; PR_TILE_EDGES overrides
 constexpr int64_t kMinTileTarget = 1 << 12;     // smaller graphs' tiles go down to this
-constexpr int64_t kUnitCost = 900000;           // default; PR_UNIT_COST overrides
+constexpr int64_t kUnitCost = 900000;           // sets which graphs are small; PR_UNIT_COST overrides
+constexpr double kUnitShare = 0.95;
 constexpr int64_t kMinUnitCost = 1 << 15;       // smaller graphs' units go down to this
 constexpr int64_t kMinUnitEdges = 1 << 17;     // a unit of a cut tile has at least
 constexpr int64_t kMinUnitEdgesFloor = 1 << 12; //   min(kMinUnitEdges, max(this,
