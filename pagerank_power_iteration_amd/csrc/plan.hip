@@ -171,7 +171,7 @@ struct PlanScratch {  // needed only while pr_plan_create runs
     uint32_t* deg;       // [n]
     int32_t* perm_rp;    // [n + 1]
     int32_t* perm_ci;    // [nnz]
-    int32_t* src_of;     // [nnz] source (plan id) of each edge of perm_ci
+    int32_t* src_of;     // [nnz] scratch of the tiled layout (sort buffers, chunk costs)
     uint32_t* in_rp_plan;  // [n + 1] tiled: in-degrees in plan order, scanned
     int32_t* order;      // [nnz] tiled: sources sorted by tile
     int32_t* tile_first; // [max_tiles + 1] tiled: first sorted edge of each tile
@@ -585,7 +585,6 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
                                                          const int32_t* __restrict__ out_ci,
                                                          int32_t n, int64_t nnz,
                                                          int32_t* __restrict__ perm_ci,
-                                                         int32_t* __restrict__ src_of,
                                                          TileMap map, uint32_t* __restrict__ hist,
                                                          int64_t T) {
     __shared__ int32_t s_own[kPermRows];      // slot owner_slot(i): local row of position base + i
@@ -620,24 +619,20 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
         __syncthreads();
         owner_max_scan(count, s_own, s_wave);
     }
-    int32_t row[kPermItems];
     int32_t q[kPermItems];  // input positions, clamped into [0, nnz): they fit 32 bits
 #pragma unroll
     for (int r = 0; r < kPermItems; ++r) {
         int64_t p = base + r * kBlock + threadIdx.x;
         p = p < last ? p : last;
-        int32_t j;
         int64_t qr;
         if (staged) {
             const int32_t a = max(s_own[owner_slot((int)(p - base))], 0);
-            j = lo + a;
             qr = p + s_delta[a];
         } else {
-            j = owner_row(perm_rp, p, lo, hi);
+            const int32_t j = owner_row(perm_rp, p, lo, hi);
             qr = (int64_t)out_rp[old_of[j]] + (p - perm_rp[j]);
         }
         q[r] = (int32_t)(qr < 0 ? 0 : (qr >= nnz ? nnz - 1 : qr));
-        row[r] = j;
     }
     int32_t t[kPermItems];
 #pragma unroll
@@ -654,7 +649,6 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
         const int64_t p = base + r * kBlock + threadIdx.x;
         if (p <= last) {
             perm_ci[p] = t[r];
-            src_of[p] = row[r];
         }
     }
     if (hist) {
@@ -1106,7 +1100,9 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
     PR_LAUNCHED("tile starts");
     // Edges sorted by tile, stably (so by source inside a tile): keys are the
     // targets, values the sources (into s.order).  One full pass sorts by
-    // min(tile, 255), from the histogram the permutation counted; the edges of
+    // min(tile, 255), from the histogram the permutation counted, taking each
+    // edge's source from the plan-order row pointers (the permutation's row
+    // windows are the pass's tiles); the edges of
     // tiles 255 and up (the light tiles, which come last and hold few edges)
     // form one range, [tp[255], nnz), which is then sorted by tile on its own.
     const int32_t* sorted_targets = nullptr;
@@ -1116,14 +1112,15 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
         in.count = nnz;
         in.n = n;
         in.keys = s.perm_ci;
-        in.vals = s.src_of;
+        in.row_ptr = s.perm_rp;
+        in.tile_row = s.tr.tile_row;
         in.tiles = map;
         in.tile_cap = kCap;
         in.error = s.tr.error;
         const RadixWs& rw = s.tr.sort;
         const int64_t T = radix_tiles(nnz);
         PR_TRY(scan_exclusive(rw.hist, rw.scanned, kRadixDigits * T, rw.scan_ws, stream));
-        k_radix_scatter<kFromTileTargets><<<dim3((unsigned)T), kBlock, 0, stream>>>(
+        k_radix_scatter<kFromTileCsr><<<dim3((unsigned)T), kBlock, 0, stream>>>(
             in, 0, T, rw.scanned, rw.key[0], s.order);
         PR_LAUNCHED("radix scatter");
         sorted_targets = rw.key[0];
@@ -1522,7 +1519,7 @@ int plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_r
     if (nnz > 0) {
         k_permute_rows<<<dim3((unsigned)perm_blocks), kBlock, 0, stream>>>(
             s.perm_rp, s.tr.tile_row, s.old_of, w.new_id, out_rp, out_ci, n, nnz, s.perm_ci,
-            s.src_of, bt.map, tiled ? s.tr.sort.hist : nullptr, perm_blocks);
+            bt.map, tiled ? s.tr.sort.hist : nullptr, perm_blocks);
         PR_LAUNCHED("permute rows");
     }
 

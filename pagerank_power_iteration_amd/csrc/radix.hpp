@@ -38,6 +38,10 @@ enum RadixMode : int {
     // from tile_of(key) (targets are plan ids, valid by construction); every
     // pass reads pairs this way, so the sorted keys are still targets.
     kFromTileTargets = 4,
+    // Edges by tile, first pass over a CSR in plan order: key = target plan
+    // id keys[i] (the column array), digit from tile_of(key); value = the row
+    // that owns edge i, found from row_ptr as in kFromOutCsr.
+    kFromTileCsr = 5,
 };
 
 // Tiles of the plan: consecutive plan-id segments (one per degree bucket,
@@ -78,10 +82,10 @@ struct RadixIn {
     int32_t n;                     // vertices
     const int32_t* keys;           // kFromOutCsr: out_col_idx; other modes: keys
     const int32_t* vals;           // kFromPairs, kFromTileTargets
-    const int32_t* row_ptr;        // kFromOutCsr: out_row_ptr
-    const int32_t* tile_row;       // kFromOutCsr: [T + 1] from k_tile_rows
-    TileMap tiles;                 // kFromTileTargets
-    int32_t tile_base = 0;         // kFromTileTargets: the digit is
+    const int32_t* row_ptr;        // kFromOutCsr, kFromTileCsr: the row pointers
+    const int32_t* tile_row;       // kFromOutCsr, kFromTileCsr: [T + 1] from k_tile_rows
+    TileMap tiles;                 // kFromTileTargets, kFromTileCsr
+    int32_t tile_base = 0;         // kFromTileTargets, kFromTileCsr: the digit is
     int32_t tile_cap = INT32_MAX;  //   min(tile_of(key) - tile_base, tile_cap)
     uint32_t* error;               // set to 1 when an input index is out of range
 };
@@ -128,7 +132,7 @@ __device__ __forceinline__ void report_bad(const RadixIn& in, bool bad) {
 template <int MODE>
 __device__ __forceinline__ uint32_t radix_digit(const RadixIn& in, int32_t k, int shift) {
     uint32_t d = (uint32_t)k;
-    if (MODE == kFromTileTargets) {
+    if (MODE == kFromTileTargets || MODE == kFromTileCsr) {
         const int32_t t = tile_of(in.tiles, k) - in.tile_base;
         d = (uint32_t)(t < in.tile_cap ? t : in.tile_cap);
     }
@@ -346,12 +350,13 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
     // inside a long run of empty rows searches row_ptr per edge instead).
     // s_val is free until the reorder below.  The loads above stay in flight
     // meanwhile: the barriers here wait for LDS only.
+    constexpr bool kRows = MODE == kFromOutCsr || MODE == kFromTileCsr;  // values: owner rows
     int32_t row_lo = 0, row_hi = 0;
-    if (MODE == kFromOutCsr) {
+    if (kRows) {
         row_lo = min(max(in.tile_row[tile], 0), in.n - 1);
         row_hi = min(max(in.tile_row[tile + 1], row_lo), in.n - 1);
     }
-    const bool staged_rows = MODE == kFromOutCsr && VALS && row_hi - row_lo < kRadixTile;
+    const bool staged_rows = kRows && VALS && row_hi - row_lo < kRadixTile;
     if (staged_rows)
         stage_owner_rows(in.row_ptr, base, count, row_lo, row_hi, s_val, (int32_t*)scan_tmp);
     else
@@ -368,7 +373,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
             k = radix_check<MODE>(in, key[r], bad);
             if (!VALS)
                 v = 0;
-            else if (MODE == kFromOutCsr)
+            else if (kRows)
                 v = staged_rows ? s_val[owner_slot(idx)] : owner_row(in.row_ptr, g, row_lo, row_hi);
             else if (kLoadVals)
                 v = val[r];
