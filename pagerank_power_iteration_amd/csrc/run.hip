@@ -712,7 +712,7 @@ __device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcn
 // issued together, added with LDS atomics (a step may meet a row twice when
 // the tile has fewer rows than the workgroup has lanes).  The integer sums
 // are exact, so the order of the additions does not matter.
-constexpr int kFixU = 16;
+constexpr int kFixU = 8;
 
 __device__ __forceinline__ void gather_slots(const TileArgs& a, unsigned long long* acc,
                                              const TileFix& fx, int32_t own_slot) {
@@ -923,11 +923,13 @@ struct TileFixArgs {
 
 // Rows of the tiles cut into units, one lane per row (the cut tiles' rows
 // numbered one after another; fix_rows[i] is the number of rows before cut
-// tile i): the row adds its slots in unit order (exact integer sums) and
-// applies the update.  Lane g of workgroup b takes rows b*256 + g, then
+// tile i): the row adds its slots (exact integer sums, so in any order),
+// kFixSlots loads at a time, and applies the update.  Lane g of workgroup b takes rows b*256 + g, then
 // + gridDim.x*256.  The plan lists the cut tile of every 256-row window's
 // first row (fix_win); each lane steps forward from it (a tile has at least
 // 64 rows, so a window meets at most five tiles).
+constexpr int kFixSlots = 8;
+
 __global__ __launch_bounds__(kFixBlock) void k_tilefix(TileFixArgs f) {
     __shared__ float red[3][kFixBlock / kWave];
     RunState* st = f.state;
@@ -942,18 +944,28 @@ __global__ __launch_bounds__(kFixBlock) void k_tilefix(TileFixArgs f) {
             while (i + 1 < f.n_fixes && f.fix_rows[i + 1] <= g) ++i;
             const TileFix fx = f.fixes[i];
             const int32_t r = g - f.fix_rows[i];
+            const int32_t p = fx.row0 + r;
+            // the row's own loads first, then its slots kFixSlots at a time
+            // (the last step's extra slots reload the last one and add 0),
+            // each step's loads issued together
+            const float xo = f.xi[p], io = f.inv_out[p];
             const long long* slot = f.partial + (int64_t)fx.first + r;
-            long long y0 = 0, y1 = 0, y2 = 0, y3 = 0;
-            int32_t j = 0;
-            for (; j + 4 <= fx.count; j += 4) {
-                y0 += slot[(int64_t)j * fx.rows];
-                y1 += slot[(int64_t)(j + 1) * fx.rows];
-                y2 += slot[(int64_t)(j + 2) * fx.rows];
-                y3 += slot[(int64_t)(j + 3) * fx.rows];
+            long long y[kFixSlots] = {};
+            for (int32_t j = 0; j < fx.count; j += kFixSlots) {
+                long long v[kFixSlots];
+#pragma unroll
+                for (int u = 0; u < kFixSlots; ++u) {
+                    const int32_t jj = j + u < fx.count ? j + u : fx.count - 1;
+                    v[u] = slot[(int64_t)jj * fx.rows];
+                }
+#pragma unroll
+                for (int u = 0; u < kFixSlots; ++u) y[u] += j + u < fx.count ? v[u] : 0ll;
             }
-            for (; j < fx.count; ++j) y0 += slot[(int64_t)j * fx.rows];
-            const long long y = (y0 + y1) + (y2 + y3);
-            update(f.xi, f.inv_out, f.contrib_out, fx.row0 + r, (float)((double)y * unit), k, sums);
+#pragma unroll
+            for (int u = 1; u < kFixSlots; ++u) y[0] += y[u];
+            const float xn = apply(xo, io, (float)((double)y[0] * unit), k, sums);
+            f.xi[p] = xn;
+            f.contrib_out[p] = xn * io;
         }
     }
     const float l1 = wave_sum(sums.l1), dg = wave_sum(sums.dang), sm = wave_sum(sums.sum);
