@@ -123,13 +123,17 @@ inline int64_t max_tiles(int32_t n) { return n / kTileMinRows + kNumBuckets + 1;
 // units, each of at least kMinUnitEdgesFloor edges when c > 1: so at most
 // tiles + nnz / kMinUnitEdgesFloor units, at most nnz / kMinUnitEdgesFloor
 // cut tiles, and c * r < r * e / min_unit_edges(r) + r <= e / 8 + r partial
-// slots per cut tile, nnz / 8 + n over all of them.
+// slots per cut tile, nnz / 8 + n over all of them (plus the padding that
+// starts each cut tile's slots on a 128-byte line: kSlotAlign - 1 at most).
 inline int64_t max_units(int32_t n, int64_t nnz) { return max_tiles(n) + nnz / kMinUnitEdgesFloor + 1; }
 inline int64_t max_fixes(int32_t n, int64_t nnz) {
     const int64_t a = max_tiles(n), b = nnz / kMinUnitEdgesFloor + 1;
     return a < b ? a : b;
 }
-inline int64_t max_partial(int32_t n, int64_t nnz) { return nnz / 8 + n + 1; }
+constexpr int64_t kSlotAlign = 16;  // slots of 8 bytes: a 128-byte line
+inline int64_t max_partial(int32_t n, int64_t nnz) {
+    return nnz / 8 + n + 1 + (kSlotAlign - 1) * max_fixes(n, nnz);
+}
 // Tile edge slots: every tile padded to whole blocks.
 inline int64_t max_edge_slots(int32_t n, int64_t nnz) { return nnz + (int64_t)(kEdgeBlock - 1) * max_tiles(n); }
 
@@ -1289,6 +1293,12 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
                 list.push_back({(int64_t)(c1 - c0) + per_unit, TileUnit{t, e0, e1, -1, row0, rows, -1, 1}});
                 continue;
             }
+            // No 128-byte line holds slots of two cut tiles, so the unit
+            // that finishes a tile reads no line that another tile's finish
+            // (maybe on the same XCD, earlier in the launch) has read: what
+            // its device-scope loads return never depends on whether an L2
+            // kept such a line.
+            slot = ceil_div(slot, kSlotAlign) * kSlotAlign;
             if (slot + count * rows > w.n_partial_max)
                 return fail(PR_ERR_ARG, "tile slots exceed the planned bound");
             const int32_t fix = (int32_t)bt.fixes.size();
