@@ -139,17 +139,43 @@ __device__ __forceinline__ uint32_t radix_digit(const RadixIn& in, int32_t k, in
     return (d >> shift) & (kRadixDigits - 1);
 }
 
+// The digit of a tile-keyed pass, with the tile map staged in LDS: seg[j] =
+// {start, first tile - tile_base, shift} of segment j.  The segment is the
+// number of segment starts after the first that are <= k (an empty segment
+// shares its start with the next, which then counts too), so one LDS read
+// replaces the chain of selects in tile_of, each of which costs two vector
+// instructions when its operands are kernel arguments (an instruction may
+// read one scalar register besides the condition).
+struct SegRow {
+    int32_t start, tile0, shift, pad;
+};
+__device__ __forceinline__ uint32_t tile_digit(const SegRow* seg, const RadixIn& in, int32_t k,
+                                               int shift) {
+    int32_t j = 0;
+#pragma unroll
+    for (int i = 1; i < kTileSegments; ++i) j += k >= in.tiles.start[i] ? 1 : 0;
+    const SegRow r = seg[j];
+    const int32_t t = r.tile0 + ((k - r.start) >> r.shift);
+    return ((uint32_t)(t < in.tile_cap ? t : in.tile_cap) >> shift) & (kRadixDigits - 1);
+}
+
 // Lanes of the wavefront whose digit equals this lane's (among `valid` lanes),
-// from one ballot per digit bit.
+// from one ballot per digit bit: with m the bit as a lane mask (0 or all
+// ones), peers &= ~(ballot(m) ^ m), one three-input bitwise instruction per
+// 32-bit half (truth table 0x90 over (peers, votes, m): peers and votes equal
+// to m).  Four vector instructions per bit; the two-way select it replaces
+// took nine.
 __device__ __forceinline__ uint64_t digit_peers(uint32_t dg, bool valid) {
-    uint64_t peers = __ballot(valid);
+    const uint64_t all = __ballot(valid);
+    uint32_t lo = (uint32_t)all, hi = (uint32_t)(all >> 32);
 #pragma unroll
     for (int b = 0; b < kRadixBits; ++b) {
-        const bool bit = (dg >> b) & 1u;
-        const uint64_t votes = __ballot(bit);
-        peers &= bit ? votes : ~votes;
+        const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int32_t)dg, b, 1);
+        const uint64_t votes = __builtin_amdgcn_uicmp(m, 0u, 33);  // 33: not equal
+        lo = __builtin_amdgcn_bitop3_b32(lo, (uint32_t)votes, m, 0x90);
+        hi = __builtin_amdgcn_bitop3_b32(hi, (uint32_t)(votes >> 32), m, 0x90);
     }
-    return peers;
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // Workgroups are dealt to the eight XCDs in turn (workgroup b to XCD b mod 8)
@@ -323,8 +349,19 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
     __shared__ int32_t s_key[kRadixTile];
     __shared__ int32_t s_val[kRadixTile];
     __shared__ uint32_t scan_tmp[kWaves + 1];
+    __shared__ SegRow seg[kTileSegments];
+    constexpr bool kTileKeys = MODE == kFromTileTargets || MODE == kFromTileCsr;
+    // the digit of key k (after the first barrier below)
+    auto digit = [&](int32_t k) -> uint32_t {
+        if constexpr (kTileKeys)
+            return tile_digit(seg, in, k, shift);
+        else
+            return radix_digit<MODE>(in, k, shift);
+    };
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    if (kTileKeys && tid < kTileSegments)
+        seg[tid] = SegRow{in.tiles.start[tid], in.tiles.tile0[tid] - in.tile_base, in.tiles.shift[tid], 0};
     const int64_t tile = xcd_tile(blockIdx.x, T);
     const int64_t base = tile * kRadixTile;
     const int count = (int)((in.count - base) < kRadixTile ? (in.count - base) : kRadixTile);
@@ -380,7 +417,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
             else
                 v = (int32_t)g;  // kFromKeys: the index itself
         }
-        const uint32_t dg = radix_digit<MODE>(in, k, shift);
+        const uint32_t dg = digit(k);
         const uint64_t peers = digit_peers(dg, valid);
         const uint32_t below = lanes_below(peers);
         uint32_t prior = 0;
@@ -411,7 +448,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
     for (int r = 0; r < kRadixItems; ++r) {
         const int idx = wave * (kWave * kRadixItems) + r * kWave + lane;
         if (idx < count) {
-            const uint32_t dg = radix_digit<MODE>(in, key[r], shift);
+            const uint32_t dg = digit(key[r]);
             const uint32_t pos = digit_start[dg] + wave_count[wave][dg] + rank[r];
             s_key[pos] = key[r];
             if (VALS) s_val[pos] = val[r];
@@ -421,7 +458,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
 
     for (int i = tid; i < count; i += kBlock) {
         const int32_t k = s_key[i];
-        const uint32_t dg = radix_digit<MODE>(in, k, shift);
+        const uint32_t dg = digit(k);
         const int64_t o = (int64_t)global_start[dg] + (i - (int64_t)digit_start[dg]);
         if (KEY16)
             reinterpret_cast<uint16_t*>(keys_out)[o] = (uint16_t)k;
