@@ -730,15 +730,15 @@ struct TileBlockIn {
 };
 
 __device__ __forceinline__ void tile_block_load(TileBlockIn& in, const int32_t* __restrict__ targets,
-                                                const int32_t* __restrict__ sources,
-                                                const TileMap& map, int32_t f, int lane) {
+                                                const int32_t* __restrict__ sources, int32_t row0,
+                                                int32_t f, int lane) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int32_t k = in.k0 + i * kWave + lane;
         const bool real = k < in.cnt;
         const int32_t e = f + (real ? k : in.cnt - 1);
         in.src[i] = sources[e];
-        in.row[i] = real ? tile_locate(map, targets[e]).offset : kTrashRow;
+        in.row[i] = real ? targets[e] - row0 : kTrashRow;  // a tile's edges target its rows
     }
     in.lo = sources[f + in.k0];
     in.hi = sources[f + (in.k0 + kEdgeBlock - 1 < in.cnt ? in.k0 + kEdgeBlock - 1 : in.cnt - 1)];
@@ -814,7 +814,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_blocks(const int32_t* __restric
     // two blocks per step, all of their loads issued before either is written
     for (; b < b_end; b += 2) {
         TileBlockIn in[2];
-        int32_t f[2];
+        int32_t f[2], row0[2];
         const int nb = b + 1 < b_end ? 2 : 1;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -823,9 +823,10 @@ __global__ __launch_bounds__(kBlock) void k_tile_blocks(const int32_t* __restric
             in[j].k0 = (int32_t)(in[j].slot - slot0[t]);
             f[j] = first[t];
             in[j].cnt = first[t + 1] - f[j];
+            row0[j] = tile_row0(map, t);
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) tile_block_load(in[j], targets, sources, map, f[j], lane);
+        for (int j = 0; j < 2; ++j) tile_block_load(in[j], targets, sources, row0[j], f[j], lane);
         tile_block_store(in[0], tsrc, tdst, tblk, sector_counts, lane);
         if (nb == 2) tile_block_store(in[1], tsrc, tdst, tblk, sector_counts, lane);
     }

@@ -149,13 +149,23 @@ __device__ __forceinline__ uint32_t radix_digit(const RadixIn& in, int32_t k, in
 struct SegRow {
     int32_t start, tile0, shift, pad;
 };
-__device__ __forceinline__ uint32_t tile_digit(const SegRow* seg, const RadixIn& in, int32_t k,
-                                               int shift) {
+// seg[j] = {start[j], tile0[j] - tile_base, shift[j]}, from the first
+// kTileSegments lanes; read after a barrier
+__device__ __forceinline__ void stage_segments(SegRow* seg, const TileMap& m, int32_t tile_base) {
+    if (threadIdx.x < kTileSegments)
+        seg[threadIdx.x] = SegRow{m.start[threadIdx.x], m.tile0[threadIdx.x] - tile_base,
+                                  m.shift[threadIdx.x], 0};
+}
+__device__ __forceinline__ int32_t seg_tile(const SegRow* seg, const TileMap& m, int32_t k) {
     int32_t j = 0;
 #pragma unroll
-    for (int i = 1; i < kTileSegments; ++i) j += k >= in.tiles.start[i] ? 1 : 0;
+    for (int i = 1; i < kTileSegments; ++i) j += k >= m.start[i] ? 1 : 0;
     const SegRow r = seg[j];
-    const int32_t t = r.tile0 + ((k - r.start) >> r.shift);
+    return r.tile0 + ((k - r.start) >> r.shift);
+}
+__device__ __forceinline__ uint32_t tile_digit(const SegRow* seg, const RadixIn& in, int32_t k,
+                                               int shift) {
+    const int32_t t = seg_tile(seg, in.tiles, k);
     return ((uint32_t)(t < in.tile_cap ? t : in.tile_cap) >> shift) & (kRadixDigits - 1);
 }
 
@@ -360,8 +370,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
     };
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-    if (kTileKeys && tid < kTileSegments)
-        seg[tid] = SegRow{in.tiles.start[tid], in.tiles.tile0[tid] - in.tile_base, in.tiles.shift[tid], 0};
+    if (kTileKeys) stage_segments(seg, in.tiles, in.tile_base);
     const int64_t tile = xcd_tile(blockIdx.x, T);
     const int64_t base = tile * kRadixTile;
     const int count = (int)((in.count - base) < kRadixTile ? (in.count - base) : kRadixTile);
