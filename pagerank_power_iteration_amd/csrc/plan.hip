@@ -1103,6 +1103,13 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
     k_tile_first<<<grid_for((int64_t)tiles + 1, 1024), kBlock, 0, stream>>>(in_rp_plan, n, tiles, map,
                                                                             first);
     PR_LAUNCHED("tile starts");
+    // The tile starts go to the host ahead of the sort's full pass: the host
+    // waits for that copy alone and queues the work that needs them (the
+    // light tiles' sort, the slot layout) while the pass runs.
+    const size_t tp_bytes = sizeof(int32_t) * ((size_t)tiles + 1);
+    PR_TRY(host_stage(host, tp_bytes));
+    PR_HIP_TRY(hipMemcpyAsync(host->stage, first, tp_bytes, hipMemcpyDeviceToHost, stream));
+    PR_HIP_TRY(hipEventRecord(host->stage_ev, stream));
     // Edges sorted by tile, stably (so by source inside a tile): keys are the
     // targets, values the sources (into s.order).  One full pass sorts by
     // min(tile, 255), from the histogram the permutation counted, taking each
@@ -1131,7 +1138,8 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
         sorted_targets = rw.key[0];
     }
     std::vector<int32_t> tp((size_t)tiles + 1);
-    PR_TRY(read_back(host, tp.data(), first, sizeof(int32_t) * tp.size(), stream));
+    PR_HIP_TRY(hipEventSynchronize(host->stage_ev));
+    std::memcpy(tp.data(), host->stage, tp_bytes);
     if (nnz > 0) {
         const int64_t lo = tiles > kCap ? tp[(size_t)kCap] : nnz;
         if (lo < nnz) {
@@ -1463,8 +1471,6 @@ int plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_r
     uint32_t* err = s.tr.error;
 
     PR_TRY(fill_u32(err, 0u, 1, stream));
-    PR_TRY(fill_u32(reinterpret_cast<uint32_t*>(s.stats), 0u, 4 * kNumBuckets, stream));
-    PR_TRY(fill_u32(reinterpret_cast<uint32_t*>(w.state), 0u, sizeof(RunState) / 4, stream));
     if (validate) {
         PR_TRY(check_out_row_ptr(out_rp, n, nnz, err, stream));
         PR_TRY(read_error_word(err, stream, "pr_plan_create"));
@@ -1477,6 +1483,10 @@ int plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_r
     PR_TRY(indegree_row_ptr(n, nnz, out_ci, s.perm_rp, s.deg, s.count_chunks, s.vsort.scan_ws, s.tr,
                             stream));
     if (validate) PR_TRY(read_error_word(err, stream, "pr_plan_create"));
+    // (cleared once the long in-degree kernels are queued: their launches'
+    // host time then overlaps them)
+    PR_TRY(fill_u32(reinterpret_cast<uint32_t*>(s.stats), 0u, 4 * kNumBuckets, stream));
+    PR_TRY(fill_u32(reinterpret_cast<uint32_t*>(w.state), 0u, sizeof(RunState) / 4, stream));
     Bounds bounds;
     bucket_bounds(tiled, bounds.min_len);
     k_plan_keys<<<grid_for(n, 1024), kBlock, 0, stream>>>(s.perm_rp, out_rp, n, bounds, s.key,
