@@ -928,7 +928,7 @@ struct Built {
     std::vector<TileFix> fixes;
     std::vector<int32_t> fix_rows;
     std::vector<int32_t> fix_win;
-    bool fused = false;
+    int32_t n_fused = 0;  // cut tiles finished in k_tile: the first n_fused of `fixes`
     // tiled: where the work lists were uploaded
     const Tile* dev_tiles = nullptr;
     const TileUnit* dev_units = nullptr;
@@ -1337,25 +1337,42 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
         return fail(PR_ERR_ARG, "tile units exceed the planned bound");
     bt.n_units = (int32_t)bt.units.size();
     bt.n_fixes = (int32_t)bt.fixes.size();
-    // Finish the cut tiles in k_tile when there are some and no tile's finish
-    // is long (its last unit adds (count - 1) * rows slot entries).
-    bt.fused = bt.n_fixes > 0;
-    for (const TileFix& f : bt.fixes)
-        if ((int64_t)(f.count - 1) * f.rows > kFuseSlots) bt.fused = false;
-    if (const char* env = std::getenv("PR_TILE_FUSE"))  // tuning knob: 0 k_tilefix, 1 k_tile
-        bt.fused = std::atoi(env) != 0;
-    if (!bt.fused)
-        for (TileUnit& u : bt.units) u.fix = -1;
+    // A cut tile is finished inside k_tile, by whichever of its units
+    // completes it last, when that finish is short: its last unit adds the
+    // other (count - 1) * rows slot entries, at most kFuseSlots.  A longer
+    // finish would hold the launch's end back; k_tilefix does those tiles
+    // after k_tile.  The tiles finished inside come first in the list (a
+    // unit's fix indexes them; -1 for a unit of a tile left to k_tilefix).
+    {
+        int mode = -1;  // per tile
+        if (const char* env = std::getenv("PR_TILE_FUSE"))  // tuning knob: 0 all k_tilefix, 1 all k_tile
+            mode = std::atoi(env) != 0 ? 1 : 0;
+        std::vector<TileFix> inside, outside;
+        std::vector<int32_t> remap(bt.fixes.size());
+        for (size_t i = 0; i < bt.fixes.size(); ++i) {
+            const TileFix& f = bt.fixes[i];
+            const bool in = mode < 0 ? (int64_t)(f.count - 1) * f.rows <= kFuseSlots : mode == 1;
+            remap[i] = in ? (int32_t)inside.size() : -1;
+            (in ? inside : outside).push_back(f);
+        }
+        bt.n_fused = (int32_t)inside.size();
+        bt.fixes = inside;
+        bt.fixes.insert(bt.fixes.end(), outside.begin(), outside.end());
+        for (TileUnit& u : bt.units)
+            if (u.fix >= 0) u.fix = remap[(size_t)u.fix];
+    }
     bt.fix_rows.assign(1, 0);
     bt.fix_win.clear();
-    if (!bt.fused) {
-        for (const TileFix& f : bt.fixes) bt.fix_rows.push_back(bt.fix_rows.back() + f.rows);
-        // for k_tilefix: the last cut tile whose rows start at or before row
-        // w * kFixBlock of the cut tiles' rows, for every window w
+    {
+        const int32_t n_out = bt.n_fixes - bt.n_fused;
+        for (int32_t i = 0; i < n_out; ++i)
+            bt.fix_rows.push_back(bt.fix_rows.back() + bt.fixes[(size_t)(bt.n_fused + i)].rows);
+        // for k_tilefix: the last of its cut tiles whose rows start at or
+        // before row w * kFixBlock of those tiles' rows, for every window w
         const int32_t total = bt.fix_rows.back();
         int32_t i = 0;
         for (int32_t g0 = 0; g0 < total; g0 += kFixBlock) {
-            while (i + 1 < bt.n_fixes && bt.fix_rows[(size_t)i + 1] <= g0) ++i;
+            while (i + 1 < n_out && bt.fix_rows[(size_t)i + 1] <= g0) ++i;
             bt.fix_win.push_back(i);
         }
     }
@@ -1391,7 +1408,7 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
     }
     // every cut tile's count of finished units starts at zero (the unit that
     // finishes a tile sets it back to zero)
-    if (bt.fused) PR_TRY(fill_u32(w.fix_done, 0u, bt.n_fixes, stream));
+    if (bt.n_fused > 0) PR_TRY(fill_u32(w.fix_done, 0u, bt.n_fused, stream));
     bt.tile_grid = (int32_t)(grid < bt.n_units ? grid : (bt.n_units > 0 ? bt.n_units : 1));
     return PR_OK;
 }
@@ -1587,7 +1604,7 @@ int plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_r
     p->units = bt.dev_units;
     p->n_units = bt.n_units;
     p->fixes = bt.dev_fixes;
-    p->fused = bt.fused;
+    p->n_fused = bt.n_fused;
     p->fix_done = w.fix_done;
     p->fix_rows = bt.dev_fix_rows;
     p->fix_win = bt.dev_fix_win;

@@ -328,12 +328,12 @@ struct pr_plan {
     const pr::TileUnit* units;
     int32_t n_units;
     const pr::TileFix* fixes;
-    bool fused;             // cut tiles finished in k_tile (else by k_tilefix)
-    uint32_t* fix_done;     // fused: [n_fixes] units of each cut tile done in this launch (0 between launches)
-    const int32_t* fix_rows;  // k_tilefix: [n_fixes + 1] rows of the cut tiles before each one
+    int32_t n_fused;        // cut tiles [0, n_fused) are finished in k_tile, the rest by k_tilefix
+    uint32_t* fix_done;     // [n_fused] units of each of those tiles done in this launch (0 between launches)
+    const int32_t* fix_rows;  // k_tilefix: [n_fixes - n_fused + 1] rows of its cut tiles before each one
     const int32_t* fix_win;   // k_tilefix: per 256-row window of those rows, the cut tile of its first row
     int32_t n_fixes;
-    int32_t n_fix_rows;
+    int32_t n_fix_rows;       // rows of k_tilefix's cut tiles
     long long* partial;
     int32_t tile_grid;
     pr::PlanHost* host;    // events, pinned status and staging (pooled)

@@ -745,8 +745,8 @@ __device__ __forceinline__ void gather_slots(const TileArgs& a, unsigned long lo
 // tile; the tile's last unit adds the other slots to its accumulators,
 // applies the update and writes the tile's sums to the tile's own entry
 // (after the units'), so where they land does not depend on which unit was
-// last.  In a plan that leaves the cut tiles to k_tilefix (kFused false), a
-// unit of a cut tile only writes its slot.
+// last.  A unit of a cut tile that the plan leaves to k_tilefix (fix -1;
+// every cut tile when kFused is false) only writes its slot.
 // The accumulators are all zero between units: each unit's epilogue clears
 // the rows it read.  The next unit's descriptor and first round of edges are
 // loaded before this unit's epilogue, so their latency overlaps it.
@@ -826,7 +826,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
         // wavefront's additions are in) before the claim, so that the stores
         // and the claim are in flight together.
         const bool cut = u.slot >= 0;
-        const bool fused = kFused && cut;
+        const bool fused = kFused && cut && u.fix >= 0;
         if (fused) {
             __syncthreads();
             for (int32_t r = threadIdx.x; r < u.rows; r += kTileBlock)
@@ -858,7 +858,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
         int32_t sum_at = cur;
         if (!cut) {
             update_rows(a, acc, u.row0, u.rows, unit, k, sums);
-        } else if (!kFused) {  // k_tilefix finishes the tile
+        } else if (!fused) {  // k_tilefix finishes the tile
             for (int32_t r = threadIdx.x; r < u.rows; r += kTileBlock) {
                 a.partial[(int64_t)u.slot + r] = (long long)acc[r];
                 acc[r] = 0ull;
@@ -1142,11 +1142,11 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         if (std::atoi(env) == 1) wide_rounds = false;
         if (std::atoi(env) == 2) wide_rounds = true;
     }
-    int32_t tilefix_grid = p->fused ? 0 : (int32_t)((p->n_fix_rows + kFixBlock - 1) / kFixBlock);
+    int32_t tilefix_grid = (int32_t)((p->n_fix_rows + kFixBlock - 1) / kFixBlock);
     if (tilefix_grid > kMaxGrid) tilefix_grid = kMaxGrid;
-    // a tiled run's sums: per unit, then per cut tile (finished in k_tile) or
+    // a tiled run's sums: per unit, then per cut tile finished in k_tile, then
     // per k_tilefix workgroup
-    const int32_t iter_parts = p->tiled ? p->n_units + (p->fused ? p->n_fixes : tilefix_grid)
+    const int32_t iter_parts = p->tiled ? p->n_units + p->n_fused + tilefix_grid
                                         : p->n_batches + p->fix_grid;
     f.parts = iter_parts;
 
@@ -1198,7 +1198,7 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     ta.n_units = p->n_units;
 
     TileFixArgs tf{};
-    tf.fixes = p->fixes;
+    tf.fixes = p->fixes + p->n_fused;  // the cut tiles k_tile leaves to it
     tf.fix_rows = p->fix_rows;
     tf.fix_win = p->fix_win;
     tf.n_rows = p->n_fix_rows;
@@ -1210,8 +1210,8 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     tf.state = p->state;
     tf.d = d;
     tf.n = p->n;
-    tf.n_fixes = p->n_fixes;
-    tf.part0 = p->n_units;
+    tf.n_fixes = p->n_fixes - p->n_fused;
+    tf.part0 = p->n_units + p->n_fused;
 
     const bool record = flags & PR_RECORD_EVENTS;
     p->events_recorded = false;
@@ -1231,11 +1231,11 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
             ta.parts_prev = t == 1 ? p->init_grid : iter_parts;
             ta.t = t;
             const dim3 grid((unsigned)p->tile_grid);
-            if (wide_rounds && p->fused)
+            if (wide_rounds && p->n_fused > 0)
                 k_tile<kTileQWide, true><<<grid, kTileBlock, 0, stream>>>(ta);
             else if (wide_rounds)
                 k_tile<kTileQWide, false><<<grid, kTileBlock, 0, stream>>>(ta);
-            else if (p->fused)
+            else if (p->n_fused > 0)
                 k_tile<kTileQNarrow, true><<<grid, kTileBlock, 0, stream>>>(ta);
             else
                 k_tile<kTileQNarrow, false><<<grid, kTileBlock, 0, stream>>>(ta);

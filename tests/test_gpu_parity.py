@@ -428,17 +428,21 @@ def test_edge_blocks_per_round_agree(prx, make, monkeypatch):
 def test_cut_tiles_finished_either_way(prx, make, monkeypatch):
     """A tile cut into units is finished either inside the gather kernel, by
     the unit that completes it last (which one that is varies from run to
-    run), or by a second kernel after it; the plan picks one (PR_TILE_FUSE
-    forces either).  Both must match the oracle, and the in-kernel finish
-    must give the same ranks on every run.  The hub graphs' tiles are cut
-    into many units, so the finishing unit adds slots over several rounds,
-    and several of its lanes meet the same row in a round (tiles of fewer
-    rows than the workgroup has lanes)."""
+    run), or by a second kernel after it; the plan picks per tile (a short
+    finish inside), and PR_TILE_FUSE forces either for every tile.  Each
+    must match the oracle, and the in-kernel finish must give the same ranks
+    on every run.  The hub graphs' tiles are cut into many units, so the
+    finishing unit adds slots over several rounds, and several of its lanes
+    meet the same row in a round (tiles of fewer rows than the workgroup has
+    lanes)."""
     g = make()
     ref = oracle.pagerank(g.row_ptr, g.col_idx, d=D, max_iter=25)
     dg = _cases.gpu_graph(g)
-    for fuse in ("0", "1"):
-        monkeypatch.setenv("PR_TILE_FUSE", fuse)
+    for fuse in (None, "0", "1"):
+        if fuse is None:
+            monkeypatch.delenv("PR_TILE_FUSE", raising=False)
+        else:
+            monkeypatch.setenv("PR_TILE_FUSE", fuse)
         plan = prx.Plan(dg)
         a = plan.run(d=D, max_iter=25)
         xa, la = a.x.clone(), a.l1_trace.clone()
