@@ -1347,11 +1347,14 @@ int build_tiled(const PlanWs& w, const PlanScratch& s, int32_t n, int64_t nnz, P
         int mode = -1;  // per tile
         if (const char* env = std::getenv("PR_TILE_FUSE"))  // tuning knob: 0 all k_tilefix, 1 all k_tile
             mode = std::atoi(env) != 0 ? 1 : 0;
+        int64_t fuse_slots = kFuseSlots;
+        if (const char* env = std::getenv("PR_FUSE_SLOTS"))  // tuning knob: the per-tile limit
+            if (std::atoll(env) >= 0) fuse_slots = std::atoll(env);
         std::vector<TileFix> inside, outside;
         std::vector<int32_t> remap(bt.fixes.size());
         for (size_t i = 0; i < bt.fixes.size(); ++i) {
             const TileFix& f = bt.fixes[i];
-            const bool in = mode < 0 ? (int64_t)(f.count - 1) * f.rows <= kFuseSlots : mode == 1;
+            const bool in = mode < 0 ? (int64_t)(f.count - 1) * f.rows <= fuse_slots : mode == 1;
             remap[i] = in ? (int32_t)inside.size() : -1;
             (in ? inside : outside).push_back(f);
         }

@@ -99,12 +99,12 @@ constexpr int kFinalBlock = 1024;
 // point (contribution * 2^shift, truncated): integer addition is exact and
 // order-free, so the sums do not depend on scheduling.  A tile whose
 // estimated cost exceeds the unit cost is cut into units of about equal
-// cost; each unit writes its accumulators to a slot of `partial`.  When no
-// cut tile has more than kFuseSlots slot entries besides one unit's own, the
-// unit that finishes a tile last adds the other slots and applies the
-// update, which spares a launch; otherwise k_tilefix finishes every cut tile
-// after k_tile, because one workgroup adding that many entries holds the
-// launch's end back.
+// cost; each unit writes its accumulators to a slot of `partial`.  When a
+// cut tile has at most kFuseSlots slot entries besides one unit's own, the
+// unit that finishes it last adds the other slots and applies the update;
+// k_tilefix finishes the other cut tiles after k_tile (and is not launched
+// when there are none), because one workgroup adding that many entries
+// holds the launch's end back.
 //
 // Cost estimate of a range of tile edges, in edge-equivalents: its edges,
 // plus kSectorWeight per distinct 64-byte sector of contributions it gathers
@@ -154,10 +154,15 @@ constexpr int64_t kMinUnitEdges = 1 << 17;     // a unit of a cut tile has at le
 constexpr int64_t kMinUnitEdgesFloor = 1 << 12; //   min(kMinUnitEdges, max(this,
 constexpr int64_t kUnitEdgesPerRow = 64;        //   this * rows)) edges (min_unit_edges)
 constexpr int64_t kMaxUnitEdges = 1 << 26;     // and at most this many
-// Cut tiles are finished in k_tile when (count - 1) * rows <= kFuseSlots for
-// each.  Measured on gfx950 (iteration time, finish in k_tile against
-// k_tilefix): R-MAT 18, largest 896: 22.1 against 25.5 us; R-MAT 21,
-// 184,320: 85.5 against 87.0 us; R-MAT 23, 491,520: 311.5 against 304.1 us.
+// A cut tile is finished in k_tile when (count - 1) * rows <= kFuseSlots
+// (PR_FUSE_SLOTS overrides).  Measured on gfx950 when one rule held for a
+// whole plan (iteration time, finish in k_tile against k_tilefix): R-MAT 18,
+// largest 896: 22.1 against 25.5 us; R-MAT 21, 184,320: 85.5 against
+// 87.0 us; R-MAT 23, 491,520: 311.5 against 304.1 us.  Per tile, R-MAT 23
+// finishes all but its most-cut tiles inside: 274.3 -> 270.7 us.  Limits
+// from 0 to 2^22: R-MAT 23 271 us from 2^16 to 2^18, 296 us from 2^19 (its
+// most-cut tile then finishes inside); R-MAT 21 82-84 us below 2^18, 78 us
+// from 2^18.
 constexpr int64_t kFuseSlots = 1 << 18;
 constexpr int32_t kTiledMaxVertices = 1 << 30; // contribution byte offsets fit 32 bits
 constexpr int kSectorShift = 4;                 // 16 fp32 contributions per 64-byte sector
