@@ -369,6 +369,12 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
             return radix_digit<MODE>(in, k, shift);
     };
 
+    // A tile-keyed pass with keys below 2^24 (plan ids of a graph with at
+    // most that many vertices) keeps each key's digit in its top byte in LDS,
+    // so the write-out does not look the tile up again.
+    constexpr int kPackShift = 32 - kRadixBits;
+    const bool packed = kTileKeys && in.n <= (1 << kPackShift);
+
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     if (kTileKeys) stage_segments(seg, in.tiles, in.tile_base);
     const int64_t tile = xcd_tile(blockIdx.x, T);
@@ -459,15 +465,21 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(RadixIn in, int shift,
         if (idx < count) {
             const uint32_t dg = digit(key[r]);
             const uint32_t pos = digit_start[dg] + wave_count[wave][dg] + rank[r];
-            s_key[pos] = key[r];
+            s_key[pos] = packed ? (int32_t)((uint32_t)key[r] | (dg << kPackShift)) : key[r];
             if (VALS) s_val[pos] = val[r];
         }
     }
     __syncthreads();
 
     for (int i = tid; i < count; i += kBlock) {
-        const int32_t k = s_key[i];
-        const uint32_t dg = digit(k);
+        int32_t k = s_key[i];
+        uint32_t dg;
+        if (packed) {
+            dg = (uint32_t)k >> kPackShift;
+            k &= (1 << kPackShift) - 1;
+        } else {
+            dg = digit(k);
+        }
         const int64_t o = (int64_t)global_start[dg] + (i - (int64_t)digit_start[dg]);
         if (KEY16)
             reinterpret_cast<uint16_t*>(keys_out)[o] = (uint16_t)k;
