@@ -756,6 +756,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     __shared__ float red[3][kTileWaves];
     __shared__ int32_t s_next;
     __shared__ int32_t s_last;
+    __shared__ int32_t s_late;  // a tile's finishing unit's claim, made after the finish
     __shared__ uint32_t s_blk;  // the current unit's next unclaimed edge block
     __shared__ double redd[3 * kTileWaves];
     RunState* st = a.state;
@@ -834,21 +835,30 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
         }
         // claim the next unit only now: a claim made earlier would hold a
         // unit back behind this one while other workgroups run out of work
-        // (with no more units than workgroups there is none to claim)
-        if (threadIdx.x == 0)
-            s_next = (int32_t)gridDim.x >= a.n_units ? a.n_units
-                                                     : (int32_t)(gridDim.x + atomicAdd(queue, 1u));
+        // (with no more units than workgroups there is none to claim).  A
+        // unit that may complete its tile counts itself done first, and the
+        // one that does claims only after finishing the tile (up to 20 us on
+        // R-MAT 23, at the end of the launch), so no unit waits behind it.
+        auto claim = [&]() -> int32_t {
+            return (int32_t)gridDim.x >= a.n_units ? a.n_units
+                                                   : (int32_t)(gridDim.x + atomicAdd(queue, 1u));
+        };
+        if (!fused && threadIdx.x == 0) s_next = claim();
         if (fused) {
             wait_vector_memory();  // this lane's slot stores are done ...
             __syncthreads();       // ... and every lane's, before the count
-            if (threadIdx.x == 0)
-                s_last = atomicAdd(&a.fix_done[u.fix], 1u) + 1u == (uint32_t)u.count ? 1 : 0;
+            if (threadIdx.x == 0) {
+                const bool last = atomicAdd(&a.fix_done[u.fix], 1u) + 1u == (uint32_t)u.count;
+                s_last = last ? 1 : 0;
+                if (!last) s_next = claim();
+            }
         }
         __syncthreads();
         // every wavefront is past its last claim: the next unit's counter
         // (the next write of s_blk's readers follows the barrier below)
         if (threadIdx.x == 0) s_blk = (uint32_t)(kTileWaves * Q);
-        const int32_t nxt = s_next;
+        const bool finisher = fused && s_last;
+        int32_t nxt = finisher ? a.n_units : s_next;
         TileUnit un{};
         if (nxt < a.n_units) {
             un = a.units[nxt];
@@ -871,6 +881,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
             __syncthreads();
             update_rows(a, acc, u.row0, u.rows, unit, k, sums);
             sum_at = a.n_units + u.fix;
+            if (threadIdx.x == 0) s_late = claim();  // read after the barrier below
         } else {
             for (int32_t r = threadIdx.x; r < u.rows; r += kTileBlock) acc[r] = 0ull;
         }
@@ -896,6 +907,13 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
                 a.part[cur] = 0.f;
                 a.part[a.stride + cur] = 0.f;
                 a.part[2 * a.stride + cur] = 0.f;
+            }
+        }
+        if (finisher) {  // (s_late is written again only after a later finish's barriers)
+            nxt = s_late;
+            if (nxt < a.n_units) {
+                un = a.units[nxt];
+                first_round(a, un, round);
             }
         }
         cur = nxt;

@@ -255,6 +255,18 @@ def test_plan_layout_permutation_windows(prx, g):
     np.testing.assert_array_equal(ci, ref_ci)
 
 
+def test_plan_layout_wide_ids(prx):
+    """More than 2^24 vertices: the sort by tile can no longer carry each
+    key's digit in the key's top byte between its ranking and its write-out,
+    and looks the tile up again (both sorts: the full pass and the light
+    tiles' own, over more than 1000 tiles here)."""
+    n = (1 << 24) + 37
+    k = np.arange(200_003, dtype=np.uint64)
+    r = graphgen.splitmix_u64(7, k) % np.uint64(n)
+    g = graphgen.from_edges(n, r[:100_001].astype(np.int64), r[100_001:200_002].astype(np.int64))
+    _check_tiled_layout(prx, g)
+
+
 def test_plan_layout_many_tiles(prx, monkeypatch):
     """More than 255 tiles (small tiles forced by the tuning knob): the tile
     sort then takes the light tiles' range in a second sort of its own."""
