@@ -206,11 +206,11 @@ PlanWs carve_ws(void* base, int32_t n, int64_t nnz, bool tiled) {
     w.contrib0 = c.take<float>((size_t)n);
     w.contrib1 = c.take<float>((size_t)n);
     const int64_t batches = ceil_div(w.n_items_max, kBatchItems);
-    // bucketed: batches + k_hubfix workgroups; tiled: units + cut tiles (or
-    // + k_tilefix workgroups)
-    const int64_t tiled_parts = w.n_units_max + w.n_fixes_max;
-    w.part_stride = (batches > tiled_parts ? batches : tiled_parts) + kMaxGrid;
-    w.part = c.take<float>((size_t)(6 * w.part_stride));  // two sets of [3][stride]
+    // per-workgroup sums: k_init's workgroups, or a bucketed iteration's
+    // batches and k_hubfix workgroups (a tiled iteration adds its sums into
+    // RunState::tsum)
+    w.part_stride = (tiled ? 0 : batches) + kMaxGrid;
+    w.part = c.take<float>((size_t)(3 * w.part_stride));  // [3][stride]
     w.state = c.take<RunState>(1);
     if (!tiled) {
         w.in_rp = c.take<int32_t>((size_t)n + 1);

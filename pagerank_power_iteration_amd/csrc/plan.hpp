@@ -239,6 +239,8 @@ struct TileFix {
     int32_t count;
 };
 
+constexpr int kSumSlots = 4;  // RunState::tsum lines per iteration
+
 // Device-resident run state.  Written by the finalize and init kernels, read
 // by the next launches (kernel boundaries order the accesses); the queue
 // heads are incremented atomically by the iteration kernels.
@@ -252,6 +254,13 @@ struct RunState {
     int32_t fx_shift;
     uint32_t pad[54];
     uint32_t queue[kQueues][64];  // queue heads at [q][0]
+    // Tiled pull: iteration t adds its L1 distance, dangling mass and sum of
+    // x' into tsum[t % 3][s][0..2] in fixed point (times 2^fx_shift), exact
+    // and in any order, workgroup b into line s = b % kSumSlots (one line
+    // each: the workgroups finish together, and adds to one address
+    // serialize); iteration t + 1 adds the lines up and clears
+    // tsum[(t + 2) % 3].
+    long long tsum[3][kSumSlots][16];
 };
 
 // Launches of the gather kernel that PR_RECORD_EVENTS times one by one.
@@ -307,10 +316,10 @@ struct pr_plan {
     const pr::ChunkRow* chunk_rows;
     int32_t n_chunk_rows;
     float* hub_part;       // chunk sums
-    float* part;           // 2 x [3][part_stride]: L1, dangling mass and sum of x' per
-                           // item batch, then per k_hubfix workgroup; or per
-                           // unit, then per cut tile (tiled runs alternate the
-                           // two sets)
+    float* part;           // [3][part_stride]: L1, dangling mass and sum of x' per
+                           // k_init workgroup, or per item batch and then per
+                           // k_hubfix workgroup (a tiled iteration's go to
+                           // RunState::tsum)
     int64_t part_stride;
     int32_t n_batches;
     pr::RunState* state;

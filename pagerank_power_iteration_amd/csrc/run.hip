@@ -345,6 +345,32 @@ __device__ __forceinline__ int fx_shift(double sum_abs_x0) {
     return shift > kFxShiftMax ? kFxShiftMax : (shift < 0 ? 0 : shift);
 }
 
+// An iteration's three sums (L1 distance, dangling mass, sum of x') are
+// totals in fixed point, times 2^shift with each workgroup's part rounded:
+// integer adds, exact in any order, so the totals do not depend on which
+// workgroup adds first.  The shift keeps them below 2^62 (every |x'| sum is
+// at most max(1, sum |x0|)).  A workgroup adds its parts up in registers and
+// then into its line of RunState::tsum once; a reader adds the lines.
+__device__ __forceinline__ long long to_sum(float v, double scale) {
+    return (long long)llrint((double)v * scale);
+}
+__device__ __forceinline__ void add_sums(long long (*ts)[16], const long long (&v)[3]) {
+    long long* line = ts[blockIdx.x % kSumSlots];
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+        if (v[j] != 0) atomicAdd(reinterpret_cast<unsigned long long*>(line + j), (unsigned long long)v[j]);
+}
+// An iteration's three totals, times 2^-shift (the same in every lane).
+__device__ __forceinline__ Sums3 read_sums(const long long (*ts)[16], int shift) {
+    long long v[3] = {0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < kSumSlots; ++s)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) v[j] += ts[s][j];
+    const double un = ldexp(1.0, -shift);
+    return Sums3{(double)v[0] * un, (double)v[1] * un, (double)v[2] * un};
+}
+
 // A wavefront's next batch: lane 0 increments queue heads, starting with
 // queue *q, until one yields a batch that holds items; -1 when every queue is
 // empty.  `ticket` is the value the last increment of queue *q returned.
@@ -492,8 +518,7 @@ struct TileArgs {
     long long* __restrict__ partial;
     const TileFix* __restrict__ fixes;
     uint32_t* __restrict__ fix_done;
-    float* __restrict__ part;  // [3][stride]: this iteration's sums, per unit then per cut tile
-    const float* __restrict__ part_prev;  // [3][stride]: the previous iteration's
+    const float* __restrict__ part_prev;  // [3][stride]: k_init's sums (read by iteration 1)
     int64_t stride;
     RunState* state;
     float* __restrict__ l1_trace;
@@ -765,21 +790,33 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     // loads are in flight together (a stopped launch reduces stale sums and
     // drops them).
     const bool stopped = st->stop != 0;
-    // Loads in this order: the first round of the previous iteration's sums,
-    // then the first unit's descriptor and first round of edges (which do not
-    // depend on the sums), so that the reduction waits for its own loads only
-    // and the unit's are in flight meanwhile.
+    // Loads in this order: the previous iteration's sums, then the first
+    // unit's descriptor and first round of edges (which do not depend on
+    // them), so that the sums wait for their own loads only and the unit's
+    // are in flight meanwhile.  After iteration 1 the sums are three exact
+    // fixed-point totals (RunState::tsum); after k_init (any start vector,
+    // whose sums need not fit that scale) every workgroup reduces k_init's
+    // per-workgroup sums in the same order.
     // (Every workgroup has a first unit: the launch is at most n_units wide.)
+    const bool after_init = a.t == 1;
     PartRound pr0;
-    parts_load<kTileBlock, kPartFirst>(a.part_prev, a.stride, a.parts_prev, 0, pr0);
+    Sums3 ps{0.0, 0.0, 0.0};
+    int pshift = 0;
+    if (after_init) {
+        parts_load<kTileBlock, kPartFirst>(a.part_prev, a.stride, a.parts_prev, 0, pr0);
+    } else {
+        pshift = st->fx_shift;
+        ps = read_sums(st->tsum[(a.t - 1) % 3], pshift);
+    }
     int32_t cur = blockIdx.x;
     TileUnit u = a.units[cur];
     EdgeRound<Q> round;
     first_round(a, u, round);
-    // The previous iteration's (or k_init's) sums, reduced by every workgroup
-    // in the same order: its L1 distance (the stop test), its dangling mass D,
-    // and -- after k_init -- sum |x0| and the count of negative entries.
-    const Sums3 prev = sum_parts_from<kTileBlock>(pr0, a.part_prev, a.stride, a.parts_prev, redd);
+    // The previous iteration's L1 distance (the stop test), its dangling mass
+    // D and its sum of x' -- after k_init: sum |x0|, D and the count of
+    // negative entries.
+    const Sums3 prev =
+        after_init ? sum_parts_from<kTileBlock>(pr0, a.part_prev, a.stride, a.parts_prev, redd) : ps;
     if (stopped) return;
     if (a.t > 1 && a.tol > 0.0 && prev.l1 < a.tol) {  // iteration t - 1 met the tolerance
         if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -796,9 +833,11 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
         shift = fx_shift(prev.l1);
         signed_contrib = prev.sum > 0.5;
     } else {
-        shift = st->fx_shift;
+        shift = pshift;
         signed_contrib = st->signed_contrib != 0;
     }
+    if (blockIdx.x == 0 && threadIdx.x < kSumSlots * 3)  // the next iteration's sums
+        st->tsum[(a.t + 1) % 3][threadIdx.x / 3][threadIdx.x % 3] = 0;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         st->dmass = prev.dang;  // for k_tilefix
         st->queue[(a.t + 1) & 1][0] = 0u;  // the next iteration's queue
@@ -814,6 +853,8 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     const Damp k = make_damp(a.d, a.n, prev.dang);
     const float scale = ldexpf(1.0f, shift);  // a power of two, exact in fp32
     const double unit = ldexp(1.0, -shift);
+    const double sum_scale = ldexp(1.0, shift);
+    long long wsum[3] = {0, 0, 0};  // this workgroup's sums (lane 0)
     uint32_t* queue = &st->queue[a.t & 1][0];
     for (int32_t r = threadIdx.x; r < kTileMaxRows; r += kTileBlock) acc[r] = 0ull;
     if (threadIdx.x == 0) s_blk = (uint32_t)(kTileWaves * Q);
@@ -865,7 +906,6 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
             first_round(a, un, round);
         }
         Acc sums;
-        int32_t sum_at = cur;
         if (!cut) {
             update_rows(a, acc, u.row0, u.rows, unit, k, sums);
         } else if (!fused) {  // k_tilefix finishes the tile
@@ -880,7 +920,6 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
                 __hip_atomic_store(&a.fix_done[u.fix], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
             update_rows(a, acc, u.row0, u.rows, unit, k, sums);
-            sum_at = a.n_units + u.fix;
             if (threadIdx.x == 0) s_late = claim();  // read after the barrier below
         } else {
             for (int32_t r = threadIdx.x; r < u.rows; r += kTileBlock) acc[r] = 0ull;
@@ -900,14 +939,9 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
                 t1 += red[1][w];
                 t2 += red[2][w];
             }
-            a.part[sum_at] = t0;
-            a.part[a.stride + sum_at] = t1;
-            a.part[2 * a.stride + sum_at] = t2;
-            if (sum_at != cur) {  // a cut tile's units hold zero sums
-                a.part[cur] = 0.f;
-                a.part[a.stride + cur] = 0.f;
-                a.part[2 * a.stride + cur] = 0.f;
-            }
+            wsum[0] += to_sum(t0, sum_scale);  // (a cut tile's other units: zeros)
+            wsum[1] += to_sum(t1, sum_scale);
+            wsum[2] += to_sum(t2, sum_scale);
         }
         if (finisher) {  // (s_late is written again only after a later finish's barriers)
             nxt = s_late;
@@ -919,6 +953,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
         cur = nxt;
         u = un;
     }
+    if (threadIdx.x == 0) add_sums(st->tsum[a.t % 3], wsum);
 }
 
 struct TileFixArgs {
@@ -929,14 +964,12 @@ struct TileFixArgs {
     const float* __restrict__ inv_out;
     float* __restrict__ contrib_out;
     float* __restrict__ xi;
-    float* __restrict__ part;  // this kernel's sums go to [part0, part0 + gridDim.x)
-    int64_t stride;
-    RunState* state;
+    RunState* state;  // the sums go to state->tsum[t % 3]
     double d;
     int32_t n;
     int32_t n_fixes;
     int32_t n_rows;  // rows of all cut tiles
-    int32_t part0;
+    int32_t t;
 };
 
 // Rows of the tiles cut into units, one lane per row (the cut tiles' rows
@@ -1001,9 +1034,9 @@ __global__ __launch_bounds__(kFixBlock) void k_tilefix(TileFixArgs f) {
             t1 += red[1][w];
             t2 += red[2][w];
         }
-        f.part[f.part0 + blockIdx.x] = t0;
-        f.part[f.stride + f.part0 + blockIdx.x] = t1;
-        f.part[2 * f.stride + f.part0 + blockIdx.x] = t2;
+        const double sc = ldexp(1.0, st->fx_shift);
+        const long long v[3] = {to_sum(t0, sc), to_sum(t1, sc), to_sum(t2, sc)};
+        add_sums(st->tsum[f.t % 3], v);
     }
 }
 
@@ -1016,6 +1049,7 @@ struct FinArgs {
     double tol;
     int32_t parts;  // sums to reduce: part[0, parts)
     int32_t t;      // iteration number; 0 after k_init
+    int32_t tiled;  // t >= 1: the sums are RunState::tsum[t % 3], not part
 };
 
 // One workgroup of kFinalBlock lanes.  After iteration t: reduce every sum,
@@ -1025,7 +1059,12 @@ __global__ __launch_bounds__(kFinalBlock) void k_finalize(FinArgs f) {
     __shared__ double redd[3 * kFinalWaves];
     RunState* st = f.state;
     if (f.t > 0 && st->stop) return;
-    const Sums3 r = sum_parts<kFinalBlock>(f.part, f.stride, f.parts, redd);
+    Sums3 r;
+    if (f.tiled && f.t > 0) {
+        r = read_sums(st->tsum[f.t % 3], st->fx_shift);
+    } else {
+        r = sum_parts<kFinalBlock>(f.part, f.stride, f.parts, redd);
+    }
     if (threadIdx.x < kQueues) st->queue[threadIdx.x][0] = 0u;
     if (threadIdx.x == 0) {
         st->dmass = r.dang;
@@ -1061,6 +1100,9 @@ __global__ __launch_bounds__(kBlock) void k_init(const int32_t* __restrict__ new
                                                  int x0_given, float* __restrict__ part,
                                                  int64_t stride, RunState* __restrict__ st) {
     __shared__ float red[kWaves];
+    if (blockIdx.x == 0)  // no sums yet
+        for (int i = threadIdx.x; i < 3 * kSumSlots * 3; i += kBlock)
+            st->tsum[i / (kSumSlots * 3)][(i / 3) % kSumSlots][i % 3] = 0;
     if (blockIdx.x == 0 && threadIdx.x < kQueues) {  // a fresh run: no stop, empty queues
         st->queue[threadIdx.x][0] = 0u;
         if (threadIdx.x == 0) {
@@ -1132,18 +1174,18 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         return fail(PR_ERR_ARG, "tiled plan with %d units for %d workgroups", p->n_units, p->tile_grid);
     hipStream_t stream = as_stream(stream_v);
 
-    // Per-iteration sums: part holds two [3][stride] sets.  A tiled run
-    // alternates them (iteration t writes set t & 1, and k_tile reduces the
-    // previous set itself: no k_finalize per iteration); a bucketed run uses
+    // Per-workgroup sums: k_init writes its own to part set 0 (sum |x0|, D0,
+    // negative entries), reduced by the first k_tile (tiled) or k_finalize
+    // (bucketed).  A tiled iteration adds its sums into RunState::tsum, read
+    // by the next k_tile: no k_finalize per iteration; a bucketed run uses
     // set 0 and k_finalize after every iteration.
-    float* part_set[2] = {p->part, p->part + 3 * p->part_stride};
     k_init<<<dim3((unsigned)p->init_grid), kBlock, 0, stream>>>(
         p->new_id, p->inv_out, x, p->xi, p->contrib[0], p->n, (flags & PR_X0_GIVEN) ? 1 : 0,
-        part_set[0], p->part_stride, p->state);
+        p->part, p->part_stride, p->state);
     PR_LAUNCHED("init");
 
     FinArgs f{};
-    f.part = part_set[0];
+    f.part = p->part;
     f.stride = p->part_stride;
     f.state = p->state;
     f.l1_trace = l1_trace;
@@ -1162,10 +1204,8 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     }
     int32_t tilefix_grid = (int32_t)((p->n_fix_rows + kFixBlock - 1) / kFixBlock);
     if (tilefix_grid > kMaxGrid) tilefix_grid = kMaxGrid;
-    // a tiled run's sums: per unit, then per cut tile finished in k_tile, then
-    // per k_tilefix workgroup
-    const int32_t iter_parts = p->tiled ? p->n_units + p->n_fused + tilefix_grid
-                                        : p->n_batches + p->fix_grid;
+    // a bucketed run's sums: per batch, then per k_hubfix workgroup
+    const int32_t iter_parts = p->n_batches + p->fix_grid;
     f.parts = iter_parts;
 
     IterArgs a{};
@@ -1223,13 +1263,10 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     tf.partial = p->partial;
     tf.inv_out = p->inv_out;
     tf.xi = p->xi;
-    tf.part = p->part;
-    tf.stride = p->part_stride;
     tf.state = p->state;
     tf.d = d;
     tf.n = p->n;
     tf.n_fixes = p->n_fixes - p->n_fused;
-    tf.part0 = p->n_units + p->n_fused;
 
     const bool record = flags & PR_RECORD_EVENTS;
     p->events_recorded = false;
@@ -1244,9 +1281,8 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         if (p->tiled) {
             ta.contrib_in = a.contrib_in;
             ta.contrib_out = a.contrib_out;
-            ta.part = part_set[t & 1];
-            ta.part_prev = part_set[(t - 1) & 1];
-            ta.parts_prev = t == 1 ? p->init_grid : iter_parts;
+            ta.part_prev = p->part;  // iteration 1 reduces k_init's sums
+            ta.parts_prev = p->init_grid;
             ta.t = t;
             const dim3 grid((unsigned)p->tile_grid);
             if (wide_rounds && p->n_fused > 0)
@@ -1268,7 +1304,7 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
         }
         if (p->tiled && tilefix_grid > 0) {
             tf.contrib_out = a.contrib_out;
-            tf.part = part_set[t & 1];
+            tf.t = t;
             k_tilefix<<<dim3((unsigned)tilefix_grid), kFixBlock, 0, stream>>>(tf);
             PR_LAUNCHED("tile rows");
         }
@@ -1289,7 +1325,7 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     auto close = [&](int32_t t_last) -> int {
         if (p->tiled) {
             f.t = t_last;
-            f.part = part_set[t_last & 1];
+            f.tiled = 1;
             k_finalize<<<1, kFinalBlock, 0, stream>>>(f);
             PR_LAUNCHED("finalize");
         }
