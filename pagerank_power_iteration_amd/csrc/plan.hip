@@ -1614,6 +1614,8 @@ int plan_create(pr_plan** plan_out, int32_t n, int64_t nnz, const int32_t* out_r
     p->n_slots = bt.n_slots;
     p->tiles = bt.dev_tiles;
     p->n_tiles = bt.n_tiles;
+    p->max_tile_rows = 0;
+    for (const Tile& tl : bt.tiles) p->max_tile_rows = tl.rows > p->max_tile_rows ? tl.rows : p->max_tile_rows;
     p->units = bt.dev_units;
     p->n_units = bt.n_units;
     p->fixes = bt.dev_fixes;

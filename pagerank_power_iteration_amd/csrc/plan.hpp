@@ -339,6 +339,7 @@ struct pr_plan {
     int64_t n_slots;        // tile edge slots, padding included
     const pr::Tile* tiles;
     int32_t n_tiles;
+    int32_t max_tile_rows;  // rows of the largest tile (k_tile clears that many accumulators)
     const pr::TileUnit* units;
     int32_t n_units;
     const pr::TileFix* fixes;

@@ -527,6 +527,7 @@ struct TileArgs {
     double tol;
     int32_t n;
     int32_t n_units;
+    int32_t max_rows;    // rows of the largest tile: the accumulators any unit touches
     int32_t parts_prev;  // sums in part_prev
     int32_t t;           // iteration number, from 1
 };
@@ -856,7 +857,7 @@ __global__ __launch_bounds__(kTileBlock) void k_tile(TileArgs a) {
     const double sum_scale = ldexp(1.0, shift);
     long long wsum[3] = {0, 0, 0};  // this workgroup's sums (lane 0)
     uint32_t* queue = &st->queue[a.t & 1][0];
-    for (int32_t r = threadIdx.x; r < kTileMaxRows; r += kTileBlock) acc[r] = 0ull;
+    for (int32_t r = threadIdx.x; r < a.max_rows; r += kTileBlock) acc[r] = 0ull;  // (not the trash row)
     if (threadIdx.x == 0) s_blk = (uint32_t)(kTileWaves * Q);
     __syncthreads();
     while (cur < a.n_units) {
@@ -1254,6 +1255,7 @@ extern "C" int pr_run(pr_plan* p, double d, double tol, int32_t max_iter, float*
     ta.tol = tol;
     ta.n = p->n;
     ta.n_units = p->n_units;
+    ta.max_rows = p->max_tile_rows;
 
     TileFixArgs tf{};
     tf.fixes = p->fixes + p->n_fused;  // the cut tiles k_tile leaves to it
