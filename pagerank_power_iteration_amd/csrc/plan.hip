@@ -642,7 +642,7 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
     int32_t t[kPermItems];
 #pragma unroll
     for (int r = 0; r < kPermItems; ++r) {
-        t[r] = out_ci[q[r]];
+        t[r] = __builtin_nontemporal_load(out_ci + q[r]);  // streamed: leave L2 to new_id
         // out-of-range targets were flagged by the in-degree sort, which
         // clamped them the same way
         t[r] = t[r] < 0 ? 0 : (t[r] >= n ? n - 1 : t[r]);
@@ -653,7 +653,7 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const int32_t* __restri
     for (int r = 0; r < kPermItems; ++r) {
         const int64_t p = base + r * kBlock + threadIdx.x;
         if (p <= last) {
-            perm_ci[p] = t[r];
+            __builtin_nontemporal_store(t[r], perm_ci + p);
         }
     }
     if (hist) {
