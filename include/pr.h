@@ -226,9 +226,9 @@ int pr_plan_iteration_ms(pr_plan* plan, float* ms_host);
  * event pair around each of its first 64 iterations), waiting for them.
  * *launches_host receives the number of launches averaged.  This is the
  * kernel that moves almost all of an iteration's bytes; the rest of the
- * iteration is the per-iteration reduction (one workgroup) and, when some
- * tiles (or, bucketed, some in-rows) are cut in pieces, the kernel that
- * finishes their rows. */
+ * iteration is, when some tiles (or, bucketed, some in-rows) are cut into
+ * pieces too many to finish inside it, the kernel that finishes their rows,
+ * and in the bucketed layout the per-iteration reduction (one workgroup). */
 int pr_plan_kernel_ms(pr_plan* plan, float* mean_ms_host, int32_t* launches_host);
 
 /* Introspection for tests and benchmarks: the number of degree buckets and,
