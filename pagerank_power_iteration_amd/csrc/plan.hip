@@ -369,17 +369,19 @@ __global__ __launch_bounds__(kCountBlock) void k_count_buckets(const uint16_t* _
 
 // The partition of the targets by their top 8 bits for the count: only the
 // number of keys per target matters, so the order inside a digit's range is
-// free.  A 1024-lane workgroup takes kPartTiles consecutive histogram tiles
-// (16,384 keys, 16 consecutive keys per lane) and writes each digit's keys of
-// all of them as one run, starting where the scanned histogram puts the
-// first tile's: runs four times longer than a stable pass over single tiles
-// writes, so whole cache lines go out.  A lane adds each run of equal
+// free.  A 512-lane workgroup takes kPartTiles consecutive histogram tiles
+// (8192 keys, 16 consecutive keys per lane) and writes each digit's keys of
+// both as one run, starting where the scanned histogram puts the first
+// tile's: runs twice as long as a stable pass over single tiles writes.
+// (1024 lanes over four tiles, with runs twice as long again, hold 64 KB of
+// LDS and fit two workgroups per CU instead of four: R-MAT 23's plan was
+// 0.1-0.15 ms slower; 256 lanes over one tile in between.)  A lane adds each run of equal
 // digits among its keys once (a CSR row lists its targets in increasing
 // order, so neighbouring keys share their top bits): first to count, then,
 // with the returned offset, to place the run in LDS.  Keys are written as
 // their low 16 bits.  Out-of-range targets are clamped and flagged as the
 // histogram pass does.
-constexpr int kPartBlock = 1024;
+constexpr int kPartBlock = 512;
 constexpr int kPartItems = 16;
 constexpr int kPartTiles = kPartBlock * kPartItems / kRadixTile;
 static_assert(kPartTiles * kRadixTile == kPartBlock * kPartItems, "whole histogram tiles");
