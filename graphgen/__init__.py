@@ -7,25 +7,26 @@ here with numpy.
 
 Workloads (the shapes of the pages' graphs; none of their data):
 
-* ``citation``   -- 28,042 papers, 2,204 of which cite nothing (page 1, "100
-  Days of GPU" Day 40, the real citation graph's counts); the others cite a
+* ``citation``   -- 28,042 papers, 2,204 of which cite nothing ("100 Days of
+  GPU" Day 40, the real citation graph's counts); the others cite a
   geometric number of papers with mean 12, each target drawn with probability
   proportional to in-degree + 1.  Stands in for the page's citation graph,
   which is not available here.
-* ``stencil100`` -- 27-point stencil on a 100^3 grid (page 2, the HPCCG
+* ``stencil100`` -- 27-point stencil on a 100^3 grid ("A Pedagogical
+  Introduction to Porting a Conjugate Gradient Solver to CUDA", the HPCCG
   problem's 100^3 size): n = 10^6, m = 298^3 - 10^6 = 25,463,592.
 * ``rmatS``      -- R-MAT scale S, edge factor 32, (a, b, c, d) =
   (0.57, 0.19, 0.19, 0.05), seed S, self-loops and duplicates removed
-  (page 4, "gpu-graph-study", scale study over 2^18 .. 2^23 vertices).
+  ("gpu-graph-study", scale study over 2^18 .. 2^23 vertices).
 
 Every CSR has rows sorted by target with no duplicates and no self-loops,
 except graphs built with ``from_edges(..., dedup=False)``.
 
 Valued matrices (the sparse product's inputs, class ``Matrix``):
 
-* ``stencil_matrix`` -- the 27-point stencil with its diagonal (page 2's
-  HPCCG operator shape; 100^3 gives 26,463,592 stored entries).  The page
-  does not print the values; ``values="operator"`` takes -1 for every
+* ``stencil_matrix`` -- the 27-point stencil with its diagonal (the HPCCG
+  operator's shape in the conjugate-gradient porting article; 100^3 gives
+  26,463,592 stored entries).  The article does not print the values; ``values="operator"`` takes -1 for every
   neighbour and 27 on the diagonal (diagonally dominant, and A times the
   ones vector is 1 on interior rows), ``values="random"`` draws each entry
   uniformly from [-1, 1).
